@@ -1,0 +1,36 @@
+"""CPU oracle of the CSA decode path — TEST INFRASTRUCTURE, not product code.
+
+A plain, slow float64 NumPy restatement of what the pages define for the five
+steps (compressor reduce, lightning-indexer score, top-k, gather, sparse
+attention with a sink) and their composition into one decode step.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
+``cpu_baseline`` leg may import it.  The HIP library and its Python binding
+never do, and the two share no code.  Parity pins: ``tests/test_oracle_pins.py``.
+"""
+
+from . import numfmt
+from .csa import (
+    LayerState,
+    SwaRing,
+    compress,
+    decode_step,
+    gather,
+    index_score,
+    kv_norm,
+    sparse_attn,
+    topk,
+)
+
+__all__ = [
+    "numfmt",
+    "compress",
+    "kv_norm",
+    "index_score",
+    "topk",
+    "gather",
+    "sparse_attn",
+    "SwaRing",
+    "LayerState",
+    "decode_step",
+]

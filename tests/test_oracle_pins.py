@@ -1,0 +1,617 @@
+"""Pins for the CPU oracle: every oracle function checked against something
+other than itself — hand-derived closed forms (tests/golden/), invariants the
+mathematics fixes, special cases that reduce to a textbook formula, and brute
+force on tiny inputs.  Each pin is chosen so a plausible mistake (a dropped
+term, a wrong sign or index, the wrong softmax axis, the bias leaking into C)
+fails it; the ``test_mutation_*`` tests plant such mistakes in wrapped copies
+of the oracle and check that the pins reject them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import numfmt
+from tests.conftest import GOLDEN
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _num(x):
+    if isinstance(x, str):
+        return float(x)  # "-inf", "-0.0"
+    if isinstance(x, list):
+        return [_num(v) for v in x]
+    return x
+
+
+def _g(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def test_bf16_decode_known_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x7F7F, 0x0001, 0x3FC0, 0x7F80, 0xFF80],
+                    dtype=np.uint16)
+    v = numfmt.bf16_bits_to_f64(bits)
+    exp = [1.0, -2.0, 0.0, -0.0, (2 - 2 ** -7) * 2.0 ** 127, 2.0 ** -133, 1.5, math.inf, -math.inf]
+    assert list(v) == exp
+    assert math.copysign(1.0, v[3]) == -1.0
+
+
+def test_bf16_decode_matches_torch():
+    import torch
+    bits = _g(1).integers(0, 1 << 16, size=4096, dtype=np.uint16)
+    exp_mask = (bits >> 7) & 0xFF
+    bits = bits[exp_mask != 0xFF]  # drop inf/NaN patterns
+    ours = numfmt.bf16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_f32_to_bf16_matches_torch_rne():
+    import torch
+    g = _g(2)
+    x = np.concatenate([g.standard_normal(4096).astype(np.float32) * 10,
+                        # exact halfway cases: 1 + 2^-8 (tie -> even 1.0), 1 + 3*2^-8 (tie -> up)
+                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8)], dtype=np.float32)])
+    ours = numfmt.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    assert numfmt.bf16_bits_to_f64(ours[-3:]).tolist() == [1.0, 1 + 2 ** -6, -1.0]
+
+
+def test_f64_to_bf16_single_rounding():
+    # just above a bf16 halfway point, below float32 resolution: one rounding
+    # from float64 goes up; a float32 detour would land on the tie and go to even
+    x = 1.0 + 2.0 ** -8 + 2.0 ** -30
+    assert numfmt.bf16_round_f64(np.array([x]))[0] == 1.0 + 2.0 ** -7
+    assert numfmt.bf16_round_f64(np.array([1.0 + 2.0 ** -8]))[0] == 1.0          # tie -> even
+    assert numfmt.bf16_round_f64(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+    assert numfmt.bf16_round_f64(np.array([2.0 ** -134 * 1.5]))[0] == 2.0 ** -133  # subnormal
+    assert numfmt.bf16_round_f64(np.array([3.0e38 * 1.2]))[0] == math.inf
+    b = numfmt.f64_to_bf16_bits(np.array([1.0, -2.0]))
+    assert b.tolist() == [0x3F80, 0xC000]
+
+
+# ---------------------------------------------------------------------------
+# (1) compressor reduce
+# ---------------------------------------------------------------------------
+
+def _check_compress_golden(fn):
+    for c in _load("compress_hand.json")["cases"]:
+        y = fn(np.array(c["Z"]), np.array(c["C"]), np.array(c["B"]), c["m"], overlap=c["overlap"])
+        np.testing.assert_allclose(y, np.array(c["expect"]), rtol=0, atol=1e-13, err_msg=c["name"])
+
+
+def _check_compress_weights(fn, m=4, D=6, seed=3):
+    """Extract the softmax weights through one-hot C and check the closed form."""
+    g = _g(seed)
+    Z = g.standard_normal((m, D)) * 3
+    B = g.standard_normal((m, D)) * 0.5
+    w = np.empty((m, D))
+    for t in range(m):
+        C = np.zeros((m, D))
+        C[t] = 1.0
+        w[t] = fn(Z, C, B, m)[0]
+    np.testing.assert_allclose(w.sum(axis=0), 1.0, rtol=0, atol=1e-15)
+    for c in range(D):
+        for t in range(1, m):
+            # p_t / p_0 = exp(l_t - l_0) with l = Z + B (bias on the logits)
+            r = w[t, c] / w[0, c]
+            e = math.exp((Z[t, c] + B[t, c]) - (Z[0, c] + B[0, c]))
+            assert abs(r - e) <= 1e-12 * e
+
+
+def _check_compress_bias_leak(fn, m=4, D=8, seed=4):
+    """C constant per channel => output is that constant, whatever Z and B."""
+    g = _g(seed)
+    Z = g.standard_normal((3 * m, D)) * 4
+    B = g.standard_normal((m, D)) * 2
+    const = g.standard_normal(D)
+    C = np.tile(const, (3 * m, 1))
+    np.testing.assert_allclose(fn(Z, C, B, m), np.tile(const, (3, 1)), rtol=0, atol=1e-14)
+
+
+def test_compress_golden():
+    _check_compress_golden(oracle.compress)
+
+
+def test_compress_weights_are_softmax_of_z_plus_b():
+    _check_compress_weights(oracle.compress)
+
+
+def test_compress_bias_never_reaches_c():
+    _check_compress_bias_leak(oracle.compress)
+
+
+def test_compress_shift_invariance():
+    g = _g(5)
+    m, D = 4, 16
+    Z = g.standard_normal((2 * m, D))
+    C = g.standard_normal((2 * m, D))
+    B = g.standard_normal((m, D)) * 0.1
+    y0 = oracle.compress(Z, C, B, m)
+    sz = g.standard_normal(D) * 7
+    sb = g.standard_normal(D) * 7
+    np.testing.assert_allclose(oracle.compress(Z + sz, C, B, m), y0, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(oracle.compress(Z, C, B + sb, m), y0, rtol=0, atol=1e-13)
+    # a per-row shift is NOT an invariance: it changes the weights
+    shifted = Z.copy()
+    shifted[0] += 1.0
+    assert np.abs(oracle.compress(shifted, C, B, m) - y0).max() > 1e-3
+
+
+def test_compress_special_cases():
+    g = _g(6)
+    D = 10
+    # m = 1: the softmax over one row is 1, so the output is C itself
+    Z, C, B = g.standard_normal((5, D)), g.standard_normal((5, D)), g.standard_normal((1, D))
+    np.testing.assert_allclose(oracle.compress(Z, C, B, 1), C, rtol=0, atol=0)
+    # equal logits and zero bias: the block mean
+    C = g.standard_normal((4, D))
+    np.testing.assert_allclose(oracle.compress(np.ones((4, D)) * 0.3, C, np.zeros((4, D)), 4),
+                               C.mean(axis=0, keepdims=True), rtol=0, atol=1e-15)
+    # one logit 50 above the rest takes (almost) all the weight
+    Z = np.zeros((4, D))
+    Z[2] = 50.0
+    y = oracle.compress(Z, C, np.zeros((4, D)), 4)
+    np.testing.assert_allclose(y[0], C[2], rtol=0, atol=8 * math.exp(-50) * np.abs(C).max())
+    # huge logits stay finite (max subtraction)
+    Z = g.standard_normal((4, D)) + 900.0
+    y = oracle.compress(Z, C, np.zeros((4, D)), 4)
+    np.testing.assert_allclose(y, oracle.compress(Z - 900.0, C, np.zeros((4, D)), 4), rtol=1e-12, atol=1e-12)
+
+
+def test_compress_tail_rows_ignored():
+    g = _g(7)
+    Z, C = g.standard_normal((11, 4)), g.standard_normal((11, 4))
+    B = g.standard_normal((4, 4))
+    y = oracle.compress(Z, C, B, 4)
+    assert y.shape == (2, 4)
+    Z2, C2 = Z.copy(), C.copy()
+    Z2[8:] += 100.0
+    C2[8:] -= 100.0
+    np.testing.assert_array_equal(oracle.compress(Z2, C2, B, 4), y)
+
+
+def test_compress_overlap_reduces_to_plain_blocks():
+    """Overlapped block 0 is the plain reduce of the b half; block i>0 is the plain
+    reduce (ratio 2m) of [a half of block i-1 ; b half of block i]."""
+    g = _g(8)
+    m, D, nb = 4, 6, 4
+    Z = g.standard_normal((nb * m, 2 * D))
+    C = g.standard_normal((nb * m, 2 * D))
+    B = g.standard_normal((m, 2 * D)) * 0.3
+    y = oracle.compress(Z, C, B, m, overlap=True)
+    a, b = slice(0, D), slice(D, 2 * D)
+    np.testing.assert_allclose(y[0], oracle.compress(Z[:m, b], C[:m, b], B[:, b], m)[0], rtol=0, atol=1e-15)
+    for i in range(1, nb):
+        Zi = np.concatenate([Z[(i - 1) * m:i * m, a], Z[i * m:(i + 1) * m, b]])
+        Ci = np.concatenate([C[(i - 1) * m:i * m, a], C[i * m:(i + 1) * m, b]])
+        Bi = np.concatenate([B[:, a], B[:, b]])
+        np.testing.assert_allclose(y[i], oracle.compress(Zi, Ci, Bi, 2 * m)[0], rtol=0, atol=1e-15)
+    # the a half of the last block is never used
+    Z2, C2 = Z.copy(), C.copy()
+    Z2[(nb - 1) * m:, a] = 77.0
+    C2[(nb - 1) * m:, a] = -77.0
+    np.testing.assert_array_equal(oracle.compress(Z2, C2, B, m, overlap=True), y)
+
+
+def test_kv_norm_closed_forms():
+    w = np.array([1.0, 2.0, -1.0, 0.5])
+    a = 3.0
+    y = oracle.kv_norm(np.full((1, 4), a), w)
+    np.testing.assert_allclose(y[0], a / math.sqrt(a * a + 1e-6) * w, rtol=1e-15)
+    g = _g(9)
+    x = g.standard_normal((3, 64))
+    y1 = oracle.kv_norm(x, np.ones(64))
+    ms = (y1 ** 2).mean(axis=1)
+    np.testing.assert_allclose(ms, (x ** 2).mean(axis=1) / ((x ** 2).mean(axis=1) + 1e-6), rtol=1e-14)
+
+
+def test_mutation_compress_pins_catch_planted_mistakes():
+    def bias_on_c(Z, C, B, m, overlap=False):  # the bug the pages fixed
+        reps = np.asarray(Z).shape[0] // m
+        Cb = np.asarray(C, dtype=float).copy()
+        Cb[:reps * m] += np.tile(B, (reps, 1))
+        return oracle.compress(Z, Cb, B, m, overlap)
+
+    def wrong_axis(Z, C, B, m, overlap=False):  # softmax across channels, not rows
+        Z, C = np.asarray(Z, float), np.asarray(C, float)
+        out = []
+        for i in range(Z.shape[0] // m):
+            L = Z[i * m:(i + 1) * m] + B
+            p = np.exp(L - L.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            out.append((p * C[i * m:(i + 1) * m]).sum(axis=0))
+        return np.array(out)
+
+    def no_bias(Z, C, B, m, overlap=False):
+        return oracle.compress(Z, C, np.zeros_like(np.asarray(B, dtype=float)), m, overlap)
+
+    with pytest.raises(AssertionError):
+        _check_compress_bias_leak(bias_on_c)
+    with pytest.raises(AssertionError):
+        _check_compress_golden(bias_on_c)
+    with pytest.raises(AssertionError):
+        _check_compress_weights(wrong_axis, m=4, D=6)
+    with pytest.raises(AssertionError):
+        _check_compress_weights(no_bias)
+
+
+# ---------------------------------------------------------------------------
+# (2) lightning-indexer score
+# ---------------------------------------------------------------------------
+
+def _check_index_golden(fn):
+    for c in _load("index_score_hand.json")["cases"]:
+        got = fn(np.array(c["q"]), np.array(c["w"]), np.array(c["K"]),
+                 q_pos=c.get("q_pos"))
+        np.testing.assert_array_equal(got, np.array(_num(c["expect"])), err_msg=c["name"])
+
+
+def test_index_score_golden():
+    _check_index_golden(oracle.index_score)
+
+
+def test_index_score_single_head_is_relu_matvec():
+    g = _g(10)
+    q = g.standard_normal((1, 1, 7))
+    K = g.standard_normal((9, 7))
+    got = oracle.index_score(q, np.ones((1, 1)), K)[0]
+    for s in range(9):
+        dot = 0.0
+        for d in range(7):
+            dot += q[0, 0, d] * K[s, d]
+        assert abs(got[s] - max(dot, 0.0)) <= 1e-14
+
+
+def test_index_score_linear_in_w_and_relu_split():
+    g = _g(11)
+    T, H, d, N = 2, 8, 16, 30
+    q = g.standard_normal((T, H, d))
+    K = g.standard_normal((N, d))
+    w1, w2 = g.standard_normal((T, H)), g.standard_normal((T, H))
+    I1, I2 = oracle.index_score(q, w1, K), oracle.index_score(q, w2, K)
+    np.testing.assert_allclose(oracle.index_score(q, 2 * w1 - 3 * w2, K), 2 * I1 - 3 * I2, rtol=1e-12, atol=1e-12)
+    # ReLU(x) - ReLU(-x) = x  =>  I(q) - I(-q) = K @ (sum_h w_h q_h)
+    lin = np.einsum("th,thd->td", w1, q) @ K.T
+    np.testing.assert_allclose(I1 - oracle.index_score(-q, w1, K), lin, rtol=1e-12, atol=1e-12)
+    # non-negative weights give non-negative scores
+    assert (oracle.index_score(q, np.abs(w1), K) >= 0).all()
+
+
+def test_index_score_key_is_shared_across_heads():
+    """F3: the stored key is [N, d_I]; a per-head [N, H, d_I] key is rejected."""
+    g = _g(12)
+    q = g.standard_normal((1, 4, 8))
+    with pytest.raises(ValueError):
+        oracle.index_score(q, np.ones((1, 4)), g.standard_normal((5, 4, 8)))
+
+
+def test_index_score_causal_visible_counts():
+    q = np.ones((1, 1, 1))
+    K = np.ones((40, 1))
+    for p in range(0, 150, 7):
+        row = oracle.index_score(q, np.ones((1, 1)), K, q_pos=[p])[0]
+        visible = int(np.isfinite(row).sum())
+        assert visible == min(40, (p + 1) // 4)
+        assert np.isfinite(row[:visible]).all() and not np.isfinite(row[visible:]).any()
+
+
+def test_mutation_index_pins_catch_planted_mistakes():
+    def no_relu(q, w, K, q_pos=None, ratio=4):
+        q = np.asarray(q, float)
+        return np.einsum("th,thn->tn", np.asarray(w, float), q @ np.asarray(K, float).T)
+
+    def off_by_one_mask(q, w, K, q_pos=None, ratio=4):
+        out = oracle.index_score(q, w, K)
+        if q_pos is not None:
+            ends = ratio * np.arange(out.shape[1]) + ratio - 1
+            out[(ends - 1)[None, :] > np.asarray(q_pos)[:, None]] = -np.inf
+        return out
+
+    with pytest.raises(AssertionError):
+        _check_index_golden(no_relu)
+    with pytest.raises(AssertionError):
+        _check_index_golden(off_by_one_mask)
+
+
+# ---------------------------------------------------------------------------
+# (3) top-k
+# ---------------------------------------------------------------------------
+
+def _check_topk_golden(fn):
+    for c in _load("topk_hand.json")["cases"]:
+        idx, cnt = fn(np.array([_num(c["scores"])]), c["k"])
+        assert idx[0].tolist() == c["expect_idx"], c
+        assert int(cnt[0]) == c["expect_count"], c
+
+
+def test_topk_golden():
+    _check_topk_golden(oracle.topk)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_topk_brute_force(seed):
+    g = _g(100 + seed)
+    N = int(g.integers(1, 48))
+    k = int(g.integers(1, 60))
+    s = g.integers(-3, 4, size=N).astype(float)  # many ties
+    s[g.random(N) < 0.2] = -np.inf
+    idx, cnt = oracle.topk(s[None], k)
+    valid = [i for i in range(N) if s[i] != -np.inf]
+    ranked = sorted(valid, key=lambda i: (-s[i], i))[:k]
+    assert idx[0, :len(ranked)].tolist() == ranked
+    assert (idx[0, len(ranked):] == -1).all()
+    assert cnt[0] == min(k, len(valid))
+
+
+def test_topk_invariants_large():
+    g = _g(13)
+    s = g.standard_normal((3, 5000))
+    k = 300
+    idx, cnt = oracle.topk(s, k)
+    for t in range(3):
+        sel = idx[t]
+        assert len(set(sel.tolist())) == k and cnt[t] == k
+        mask = np.zeros(5000, bool)
+        mask[sel] = True
+        assert s[t, mask].min() >= s[t, ~mask].max()
+        assert (np.diff(s[t, sel]) <= 0).all()
+
+
+def test_mutation_topk_pins_catch_planted_mistakes():
+    def higher_index_wins(scores, k):
+        s = np.asarray(scores, float)
+        idx, cnt = oracle.topk(s[:, ::-1], k)
+        N = s.shape[1]
+        return np.where(idx >= 0, N - 1 - idx, -1), cnt
+
+    def signed_zero_order(scores, k):
+        s = np.asarray(scores, float)
+        s = np.where((s == 0) & np.signbit(s), -1e-300, s)
+        return oracle.topk(s, k)
+
+    with pytest.raises(AssertionError):
+        _check_topk_golden(higher_index_wins)
+    with pytest.raises(AssertionError):
+        _check_topk_golden(signed_zero_order)
+
+
+# ---------------------------------------------------------------------------
+# (4) gather
+# ---------------------------------------------------------------------------
+
+def test_gather_golden():
+    for c in _load("gather_hand.json")["cases"]:
+        rows, nv = oracle.gather(np.array(c["comp_kv"]), np.array(c["idx"]), c["count"],
+                                 np.array(c["swa"]), c["swa_head"], c["swa_len"])
+        assert rows.tolist() == c["expect_rows"] and nv == c["expect_n_valid"]
+
+
+def test_gather_wrap_is_chronological():
+    W, D = 8, 3
+    g = _g(14)
+    ring = oracle.SwaRing(np.zeros((W, D)))
+    history = []
+    for p in range(29):  # wraps three times and ends with head = 29 % 8 = 5
+        row = g.standard_normal(D)
+        ring.append(row)
+        history.append(row)
+    assert ring.head == 29 % W and ring.length == W
+    rows, nv = oracle.gather(np.zeros((1, D)), np.array([-1]), 0, ring.rows, ring.head, ring.length)
+    np.testing.assert_array_equal(rows, np.stack(history[-W:]))
+    assert nv == W
+
+
+# ---------------------------------------------------------------------------
+# (5) sparse attention with a sink
+# ---------------------------------------------------------------------------
+
+def _check_attn_golden(fn):
+    for c in _load("attn_hand.json")["cases"]:
+        q = np.array(c["q"], dtype=float)
+        kv = np.array(c["kv"], dtype=float).reshape(-1, q.shape[1])
+        out, lse = fn(q, kv, None if c["sink"] is None else np.array(c["sink"]), c["scale"])
+        np.testing.assert_allclose(out, np.array(c["expect_out"]), rtol=1e-14, atol=1e-15, err_msg=c["name"])
+        np.testing.assert_allclose(lse, np.array(c["expect_lse"]), rtol=1e-14, err_msg=c["name"])
+
+
+def test_attn_golden():
+    _check_attn_golden(oracle.sparse_attn)
+
+
+def test_attn_sink_to_minus_inf_is_plain_softmax():
+    g = _g(15)
+    q, kv = g.standard_normal((4, 16)), g.standard_normal((9, 16))
+    o1, l1 = oracle.sparse_attn(q, kv, np.full(4, -np.inf))
+    o2, l2 = oracle.sparse_attn(q, kv, None)
+    np.testing.assert_array_equal(o1, o2)
+    # plain softmax attention, written as the textbook formula
+    s = q @ kv.T / 4.0
+    p = np.exp(s - s.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    np.testing.assert_allclose(o2, p @ kv, rtol=1e-13, atol=1e-14)
+
+
+def test_attn_one_row_closed_form():
+    g = _g(16)
+    D = 8
+    q, v = g.standard_normal((3, D)), g.standard_normal((1, D))
+    sink = g.standard_normal(3)
+    out, lse = oracle.sparse_attn(q, v, sink)
+    s = q @ v[0] / math.sqrt(D)
+    sig = 1.0 / (1.0 + np.exp(-(s - sink)))
+    np.testing.assert_allclose(out, sig[:, None] * v, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lse, np.log(np.exp(s) + np.exp(sink)), rtol=1e-13)
+
+
+def test_attn_identical_rows_closed_form():
+    g = _g(17)
+    D, n = 8, 5
+    q, v = g.standard_normal((2, D)), g.standard_normal(D)
+    sink = np.array([0.3, -1.2])
+    out, _ = oracle.sparse_attn(q, np.tile(v, (n, 1)), sink)
+    s = q @ v / math.sqrt(D)
+    np.testing.assert_allclose(out, (n / (n + np.exp(sink - s)))[:, None] * v, rtol=1e-13, atol=1e-15)
+
+
+def test_attn_permutation_invariance_and_weights():
+    g = _g(18)
+    q, kv = g.standard_normal((4, 32)), g.standard_normal((20, 32))
+    sink = g.standard_normal(4)
+    o1, l1, w, ws = oracle.sparse_attn(q, kv, sink, return_weights=True)
+    perm = g.permutation(20)
+    o2, l2 = oracle.sparse_attn(q, kv[perm], sink)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=1e-14)
+    np.testing.assert_allclose(w.sum(1) + ws, 1.0, rtol=0, atol=1e-14)
+    s = q @ kv.T / math.sqrt(32)
+    np.testing.assert_allclose(w[:, 3] / w[:, 7], np.exp(s[:, 3] - s[:, 7]), rtol=1e-12)
+    np.testing.assert_allclose(ws / w[:, 0], np.exp(sink - s[:, 0]), rtol=1e-12)
+
+
+def test_attn_large_logits_stable():
+    q = np.full((1, 4), 30.0)
+    kv = np.array([[30.0] * 4, [29.0] * 4])
+    out, lse = oracle.sparse_attn(q, kv, np.array([0.0]))
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def test_mutation_attn_pins_catch_planted_mistakes():
+    def sink_in_numerator(q, kv, sink=None, scale=None):  # sink given a value row of ones
+        if sink is None or len(kv) == 0:
+            return oracle.sparse_attn(q, kv, sink, scale)
+        out, lse, w, ws = oracle.sparse_attn(q, kv, sink, scale, return_weights=True)
+        return out + ws[:, None], lse
+
+    def sink_scaled_again(q, kv, sink=None, scale=None):
+        sc = 1.0 / math.sqrt(np.asarray(q).shape[1]) if scale is None else scale
+        return oracle.sparse_attn(q, kv, None if sink is None else np.asarray(sink) * sc + 0.5, scale)
+
+    with pytest.raises(AssertionError):
+        _check_attn_golden(sink_in_numerator)
+    with pytest.raises(AssertionError):
+        _check_attn_golden(sink_scaled_again)
+
+
+# ---------------------------------------------------------------------------
+# (6) decode step
+# ---------------------------------------------------------------------------
+
+def _empty_state(g, D=16, di=8, H=4, W=8, max_comp=64, m=4):
+    return oracle.LayerState(
+        comp_kv=np.zeros((max_comp, D)), idx_keys=np.zeros((max_comp, di)), n_comp=0,
+        swa=oracle.SwaRing(np.zeros((W, D))), main_bias=g.standard_normal((m, D)) * 0.1,
+        idx_bias=g.standard_normal((m, di)) * 0.1, sink=g.standard_normal(H), m=m)
+
+
+def _step_inputs(g, D=16, di=8, H=4, Hi=4, m=4):
+    return dict(q=g.standard_normal((H, D)), q_idx=g.standard_normal((Hi, di)),
+                w_idx=g.standard_normal(Hi), kv_new=g.standard_normal(D),
+                z_main=g.standard_normal((m, D)), c_main=g.standard_normal((m, D)),
+                z_idx=g.standard_normal((m, di)), c_idx=g.standard_normal((m, di)))
+
+
+def test_decode_step_state_advances():
+    g = _g(19)
+    L = _empty_state(g)
+    for pos in range(23):
+        r = oracle.decode_step(L, pos=pos, top_k=3, **_step_inputs(g))
+        assert L.n_comp == (pos + 1) // 4
+        assert L.swa.length == min(pos + 1, 8) and L.swa.head == (pos + 1) % 8
+        assert r["count"] == min(3, L.n_comp)
+        assert r["n_valid"] == r["count"] + L.swa.length
+        assert (r["new_entry"] is not None) == (pos % 4 == 3)
+
+
+def test_decode_step_sees_new_token_and_new_block():
+    g = _g(20)
+    L = _empty_state(g)
+    L.sink = None
+    inp = _step_inputs(g)
+    r = oracle.decode_step(L, pos=0, top_k=2, **inp)
+    # one SWA row, nothing compressed, no sink: attention returns that row
+    np.testing.assert_allclose(r["out"], np.tile(inp["kv_new"], (4, 1)), rtol=1e-15)
+    for pos in (1, 2):
+        oracle.decode_step(L, pos=pos, top_k=2, **_step_inputs(g))
+    inp = _step_inputs(g)
+    r = oracle.decode_step(L, pos=3, top_k=2, **inp)
+    assert L.n_comp == 1 and r["count"] == 1 and r["idx"].tolist() == [0, -1]
+    np.testing.assert_allclose(r["rows"][0], oracle.compress(inp["z_main"], inp["c_main"], L.main_bias, 4)[0])
+
+
+def test_decode_step_sparse_equals_dense_when_k_covers_all():
+    """top_k >= n_comp: sparse attention equals dense attention over [comp_kv; SWA]."""
+    g = _g(21)
+    L = _empty_state(g)
+    for pos in range(30):
+        oracle.decode_step(L, pos=pos, top_k=64, **_step_inputs(g))
+    inp = _step_inputs(_g(999))
+    q = inp["q"]
+    r = oracle.decode_step(L, pos=30, top_k=64, **inp)
+    dense_rows = np.concatenate([L.comp_kv[:L.n_comp],
+                                 np.stack([L.swa.rows[(L.swa.head - L.swa.length + j) % 8]
+                                           for j in range(L.swa.length)])])
+    out_d, lse_d = oracle.sparse_attn(q, dense_rows, L.sink)
+    np.testing.assert_allclose(r["out"], out_d, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(r["lse"], lse_d, rtol=1e-13)
+
+
+def test_decode_step_cache_rounding_applies():
+    g = _g(22)
+    L = _empty_state(g)
+    L.round_cache = numfmt.bf16_round_f64
+    inp = _step_inputs(g)
+    for pos in range(3):
+        oracle.decode_step(L, pos=pos, top_k=2, **_step_inputs(g))
+    oracle.decode_step(L, pos=3, top_k=2, **inp)
+    exact = oracle.compress(inp["z_main"], inp["c_main"], L.main_bias, 4)[0]
+    np.testing.assert_array_equal(L.comp_kv[0], numfmt.bf16_round_f64(exact))
+
+
+# ---------------------------------------------------------------------------
+# workload shapes against the pages' printed sizes
+# ---------------------------------------------------------------------------
+
+def test_workload_shapes_match_printed_sizes():
+    import synth
+    ps = _load("page_sizes.json")
+    s = synth.SHAPES["ctx1m"]
+    assert s.d_i == ps["indexer_key_width"] and s.h_i == ps["indexer_heads"]
+    assert s.d_i * 2 == ps["indexer_bytes_per_block"]
+    assert s.ctx // s.m == ps["blocks_at_1m"] == s.n_comp
+    assert s.n_comp * s.d_i * 2 == ps["indexer_bytes_per_layer_at_1m"]
+    assert s.n_comp * s.d * 2 == ps["main_bytes_per_layer_at_1m"]
+    assert s.w * s.d * 2 == ps["swa_bytes_per_layer"] and s.w == ps["swa_window"]
+    assert s.top_k + s.w == ps["gather_buf_rows"]
+    assert 2 * s.d_i == ps["indexer_compressor_kv_dim"] and 2 * s.d == ps["main_compressor_kv_dim"]
+    assert [s.m, 2 * s.d_i] == ps["indexer_position_bias_shape"]
+
+
+def test_synth_inputs_deterministic_and_shaped():
+    import synth
+    sh = synth.SHAPES["tiny"]
+    a = synth.make_decode_inputs(sh, 1001)
+    b = synth.make_decode_inputs(sh, 1001)
+    for k in a:
+        np.testing.assert_array_equal(np.asarray(a[k]), np.asarray(b[k]))
+    assert a["idx_keys"].shape == (1, 256, 128) and a["comp_kv"].shape == (1, 256, 128)
+    assert a["n_comp"] == 255 and a["swa_head"] == 1023 % 128 and a["swa_len"] == 128
+    sh2 = synth.SHAPES["ctx8k"]
+    c = synth.make_decode_inputs(synth.with_(sh2, n_comp=64, ctx=256), 5)
+    assert c["comp_kv"].dtype == np.uint16 and c["q"].shape == (1, 64, 512)
