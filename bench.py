@@ -1,0 +1,269 @@
+"""Benchmark: CSA decode steps/s at 1M context (n_comp 250,000) on one MI355X.
+
+One step = one new token through 30 independent CSA layers (each with its own
+seeded 64 MB indexer-key cache and 256 MB compressed-KV cache), i.e. 30 calls
+of csa_decode_step on one stream: SWA append, compression of the block the
+token completes, indexer scan over 250,000 keys, top-512, gather of 640 rows,
+attention of 64 heads x 512 with a sink.  The 30-layer step is captured once
+in a HIP graph and replayed; every replay redoes all the work (same token
+position, so each replay rewrites the same cache slots with the same values).
+
+Prints one JSON line.  `roofline` is for the dominant kernel (the indexer
+scan), timed with HIP events on its launch stream; `cpu_baseline` is the
+float64 CPU oracle timed on the host over a bounded sample of the same step.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+
+
+def algorithmic_bytes(shape) -> dict:
+    """Bytes each step of one layer must move at minimum (bf16 caches)."""
+    N, di, hi, D, H, K, W, m = (shape.n_comp, shape.d_i, shape.h_i, shape.d, shape.h, shape.top_k,
+                                shape.w, shape.m)
+    scan = N * di * 2 + hi * di * 2 + hi * 4            # keys + q_idx + head weights
+    topk = K * 4 + 4                                    # indices + count
+    gather = 2 * (K + W) * D * 2                        # read + write rows
+    attn = (K + W) * D * 2 + H * D * 2 + H * 4 + H * D * 2 + H * 4  # rows, q, sink, out, lse
+    compress = (2 * m * D * 4 + m * D * 4 + D * 2) + (2 * m * di * 4 + m * di * 4 + di * 2)
+    swa = 2 * D * 2
+    per_layer = scan + topk + gather + attn + compress + swa
+    return {"scan": scan, "topk": topk, "gather": gather, "attn": attn, "compress": compress,
+            "swa": swa, "per_layer": per_layer}
+
+
+def build_layers(csa, shape, dev):
+    import torch
+    import synth
+
+    layers = []
+    for x in synth.make_decode_inputs_torch(shape, seed=None, device=dev):
+        B, K, W, D = shape.batch, shape.top_k, shape.w, shape.d
+        L = csa.make_layer_desc(comp_kv=x["comp_kv"], idx_keys=x["idx_keys"], swa=x["swa"],
+                                main_bias=x["main_bias"], idx_bias=x["idx_bias"], sink=x["sink"],
+                                n_comp=x["n_comp"], swa_head=x["swa_head"], swa_len=x["swa_len"],
+                                h=shape.h, h_i=shape.h_i, m=shape.m, top_k=K)
+        outs = dict(scores=torch.empty(B, shape.max_comp, device=dev),
+                    topk_idx=torch.empty(B, K, dtype=torch.int32, device=dev),
+                    topk_count=torch.empty(B, dtype=torch.int32, device=dev),
+                    gather_buf=torch.zeros(B, K + W, D, dtype=torch.bfloat16, device=dev),
+                    n_valid=torch.empty(B, dtype=torch.int32, device=dev),
+                    out=torch.empty(B, shape.h, D, dtype=torch.bfloat16, device=dev),
+                    lse=torch.empty(B, shape.h, device=dev))
+        io = csa.make_step_io(pos=x["pos"], q=x["q"], q_idx=x["q_idx"], w_idx=x["w_idx"],
+                              kv_new=x["kv_new"], z_main=x["z_main"], c_main=x["c_main"],
+                              z_idx=x["z_idx"], c_idx=x["c_idx"], **outs)
+        ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=dev)
+        layers.append({"x": x, "L": L, "io": io, "outs": outs, "ws": ws})
+    return layers
+
+
+def run_step(csa, layers):
+    for ly in layers:
+        csa.csa_decode_step(ly["L"], ly["io"], ly["ws"])
+
+
+def time_scan_kernel(csa, layers, shape, reps: int):
+    """Average duration of one indexer-scan launch (HIP events on its stream)."""
+    import torch
+
+    pairs = []
+    stream = torch.cuda.current_stream()
+    for _ in range(reps):
+        for ly in layers:
+            x, o = ly["x"], ly["outs"]
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            csa.csa_index_score(x["q_idx"][:, None], x["w_idx"][:, None], x["idx_keys"],
+                                o["scores"][:, None], n=shape.n_comp, stream=stream)
+            e1.record(stream)
+            pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in pairs]
+    return sum(ms) / len(ms), min(ms)
+
+
+def cpu_baseline(layers, shape, budget_s: float):
+    """The float64 oracle on the host, layer by layer, until the budget is spent."""
+    import numpy as np
+    import oracle
+    from oracle import numfmt
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    cores = len(os.sched_getaffinity(0))
+
+    def f64(t):
+        import torch
+        if t.dtype == torch.bfloat16:
+            return numfmt.bf16_bits_to_f64(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+        return t.cpu().numpy().astype(np.float64)
+
+    times = []
+    for ly in layers:
+        x = ly["x"]
+        st = oracle.LayerState(comp_kv=f64(x["comp_kv"][0]), idx_keys=f64(x["idx_keys"][0]),
+                               n_comp=x["n_comp"] - 0, swa=oracle.SwaRing(f64(x["swa"][0]), x["swa_head"],
+                                                                        x["swa_len"]),
+                               main_bias=f64(x["main_bias"]), idx_bias=f64(x["idx_bias"]),
+                               sink=f64(x["sink"]), round_cache=numfmt.bf16_round_f64)
+        # the GPU step already wrote this step's block into the caches; the
+        # oracle recomputes it into the same slot
+        st.n_comp = x["n_comp"]
+        args = dict(q=f64(x["q"][0]), q_idx=f64(x["q_idx"][0]), w_idx=f64(x["w_idx"][0]),
+                    kv_new=f64(x["kv_new"][0]), pos=x["pos"], top_k=shape.top_k,
+                    z_main=f64(x["z_main"][0]), c_main=f64(x["c_main"][0]), z_idx=f64(x["z_idx"][0]),
+                    c_idx=f64(x["c_idx"][0]), scale=1.0 / np.sqrt(shape.d))
+        t0 = time.perf_counter()
+        oracle.decode_step(st, **args)
+        times.append(time.perf_counter() - t0)
+        del st
+        if sum(times) > budget_s:
+            break
+    per_layer = sum(times) / len(times)
+    return {"value": 1.0 / (per_layer * shape.layers), "unit": "steps/s", "cores": min(threads, cores),
+            "kind": "oracle",
+            "sample": f"{len(times)} of {shape.layers} layers of one decode step at n_comp={shape.n_comp} "
+                      f"(float64 numpy oracle, mean {per_layer:.3f} s/layer; steps/s = 1/(30 x mean))"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--scan-reps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs the "
+              "path on a single MI355X)", file=sys.stderr)
+        return 2
+
+    import torch
+    import compressed_sparse_attention_reduce_amd as csa
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shape = synth.SHAPES["ctx1m"]
+    csa.lib()
+    layers = build_layers(csa, shape, dev)
+    torch.cuda.synchronize()
+
+    # eager warm-up, then a reference copy of layer 0's output
+    for _ in range(max(1, args.warmup // 4)):
+        run_step(csa, layers)
+    torch.cuda.synchronize()
+    ref_out = layers[0]["outs"]["out"].clone()
+    ref_idx = layers[0]["outs"]["topk_idx"].clone()
+
+    # eager timing (host launch overhead included)
+    n_eager = max(3, min(20, args.steps // 10))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_eager):
+        run_step(csa, layers)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / n_eager
+
+    graph = None
+    if args.mode == "graph":
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_step(csa, layers)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        # every replay must reproduce the eager result
+        assert torch.equal(layers[0]["outs"]["out"], ref_out), "graph replay differs from eager"
+        assert torch.equal(layers[0]["outs"]["topk_idx"], ref_idx), "graph replay differs from eager"
+
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            run_step(csa, layers)
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    assert torch.equal(layers[0]["outs"]["out"], ref_out), "timed replays differ from eager"
+
+    scan_ms, scan_min_ms = time_scan_kernel(csa, layers, shape, args.scan_reps)
+    ab = algorithmic_bytes(shape)
+    scan_gbs = ab["scan"] / (scan_ms * 1e-3) / 1e9
+    step_bytes = ab["per_layer"] * shape.layers
+    step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(layers, shape, args.cpu_budget)
+
+    res = {
+        "metric": "CSA decode steps/s and indexer-scan HBM GB/s at 1M ctx (250K comp entries)",
+        "value": round(1e3 / ms_per_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "ctx1m: one decode token through 30 CSA layers, context 1,000,000 "
+                        "(n_comp 250,000, SWA 128 with wrap), batch 1, indexer 64x128 bf16, "
+                        "top_k 512, main attention 64 heads x 512 bf16 with sink",
+            "layers": shape.layers, "n_comp": shape.n_comp, "top_k": shape.top_k,
+            "swa": shape.w, "batch": shape.batch, "mode": args.mode,
+        },
+        "scan_gbps": round(scan_gbs, 1),
+        "step_gbps": round(step_gbs, 1),
+        "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "eager_ms_per_step": round(eager_ms, 4),
+        "wall_ms_timed": round(wall_ms, 2),
+        "roofline": {
+            "kernel": "k_index_score_bf16",
+            "bound": "hbm",
+            "achieved": round(scan_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "alg_bytes_per_launch": ab["scan"],
+            "avg_launch_us": round(scan_ms * 1e3, 3),
+            "min_launch_us": round(scan_min_ms * 1e3, 3),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,28 @@
+"""MI355X-native compressed-sparse-attention (CSA) decode path.
+
+The compute lives in ``libcsa.so`` (hand-written HIP kernels for gfx950
+behind the C ABI of ``include/csa.h``); this package is its thin Python
+binding.  Build the library with ``compressed_sparse_attention_reduce_amd.build.build()``.
+"""
+
+from .binding import (  # noqa: F401
+    CSA_BF16,
+    CSA_F32,
+    CsaError,
+    LayerDesc,
+    StepIO,
+    csa_compress,
+    csa_decode_step,
+    csa_decode_step_workspace_size,
+    csa_gather,
+    csa_index_score,
+    csa_last_error,
+    csa_layer_advance,
+    csa_sparse_attn,
+    csa_sparse_attn_workspace_size,
+    csa_topk,
+    csa_topk_workspace_size,
+    lib,
+    make_layer_desc,
+    make_step_io,
+)

@@ -1,0 +1,267 @@
+"""Thin ctypes binding of libcsa.so (include/csa.h), same names as the C ABI.
+
+Argument marshalling only: tensors become device pointers, batch strides and
+sizes are read from tensor shapes, the stream is torch's current stream.
+Every step of the path runs in the HIP library; there is no fallback.  If the
+library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcsa.so")
+
+CSA_OK = 0
+CSA_ERR_INVALID_ARG = -1
+CSA_ERR_UNSUPPORTED = -2
+CSA_ERR_LAUNCH = -3
+CSA_ERR_WORKSPACE = -4
+CSA_F32 = 0
+CSA_BF16 = 1
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_ll = ctypes.c_longlong
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+class CsaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"CSA error {code}: {msg}")
+        self.code = code
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", _i), ("h", _i), ("d", _i), ("h_i", _i), ("d_i", _i), ("m", _i), ("w", _i),
+        ("top_k", _i), ("overlap", _i), ("dtype", _i), ("out_dtype", _i),
+        ("comp_kv", _vp), ("comp_kv_stride_b", _ll),
+        ("idx_keys", _vp), ("idx_keys_stride_b", _ll),
+        ("swa", _vp), ("swa_stride_b", _ll),
+        ("max_comp", _i),
+        ("main_bias", _vp), ("idx_bias", _vp), ("main_norm", _vp), ("idx_norm", _vp), ("sink", _vp),
+        ("scale", _f),
+        ("n_comp", _i), ("swa_head", _i), ("swa_len", _i),
+    ]
+
+
+class StepIO(ctypes.Structure):
+    _fields_ = [
+        ("pos", _i),
+        ("q", _vp), ("q_stride_b", _ll),
+        ("q_idx", _vp), ("q_idx_stride_b", _ll),
+        ("w_idx", _vp), ("w_stride_b", _ll),
+        ("kv_new", _vp), ("kv_new_stride_b", _ll),
+        ("z_main", _vp), ("c_main", _vp), ("zc_main_stride_b", _ll),
+        ("z_idx", _vp), ("c_idx", _vp), ("zc_idx_stride_b", _ll),
+        ("scores", _vp), ("scores_stride_b", _ll),
+        ("topk_idx", _vp), ("topk_count", _vp),
+        ("gather_buf", _vp), ("gather_stride_b", _ll),
+        ("n_valid", _vp),
+        ("out", _vp), ("out_stride_b", _ll),
+        ("lse", _vp),
+    ]
+
+
+_SIGS = {
+    "csa_last_error": (ctypes.c_char_p, []),
+    "csa_compress": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _ll, _ll, _vp]),
+    "csa_index_score": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _ll, _ll, _ll,
+                             _ll, _ll, _vp]),
+    "csa_topk_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "csa_topk": (_i, [_vp, _i, _i, _i, _ll, _ll, _i, _vp, _vp, _vp, _sz, _vp]),
+    "csa_gather": (_i, [_vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _i, _i, _i, _ll, _ll,
+                        _ll, _vp]),
+    "csa_sparse_attn_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "csa_sparse_attn": (_i, [_vp, _vp, _vp, _vp, _f, _vp, _vp, _i, _i, _i, _i, _i, _i, _ll, _ll,
+                             _ll, _vp, _sz, _vp]),
+    "csa_decode_step_workspace_size": (_sz, [ctypes.POINTER(LayerDesc)]),
+    "csa_decode_step": (_i, [ctypes.POINTER(LayerDesc), ctypes.POINTER(StepIO), _vp, _sz, _vp]),
+    "csa_layer_advance": (_i, [ctypes.POINTER(LayerDesc), _i]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -c "
+                               "'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != CSA_OK:
+        raise CsaError(rc, lib().csa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _inner_contig(t: torch.Tensor, name: str) -> None:
+    # every dim but the batch dim must be dense row-major
+    exp = 1
+    for size, st in zip(reversed(t.shape[1:]), reversed(t.stride()[1:])):
+        if size != 1 and st != exp:
+            raise ValueError(f"{name}: inner dims must be contiguous (stride {t.stride()})")
+        exp *= size
+
+
+def csa_last_error() -> str:
+    return lib().csa_last_error().decode()
+
+
+def csa_compress(z, c, bias, out, m: int, overlap: int = 0, first_block: int = 0, norm_w=None,
+                 n_blocks: Optional[int] = None, stream=None) -> None:
+    """z, c: [B, rows, d or 2d] float32; bias [m, d or 2d]; out [B, n_blocks, d]."""
+    for t, nm in ((z, "z"), (c, "c"), (out, "out")):
+        _inner_contig(t, nm)
+    B, nb, d = out.shape
+    nb = nb if n_blocks is None else n_blocks
+    _check(lib().csa_compress(_ptr(z), _ptr(c), _ptr(bias), _ptr(norm_w), _ptr(out), _dt(out), B, nb,
+                              m, d, overlap, first_block, z.stride(0), out.stride(0), _stream(stream)))
+
+
+def csa_index_score(q, w, k, scores, q_pos=None, ratio: int = 4, n: Optional[int] = None,
+                    stream=None) -> None:
+    """q [B, t, h_i, d_i]; w [B, t, h_i] float32; k [B, N, d_i]; scores [B, t, ld] float32."""
+    for t_, nm in ((q, "q"), (w, "w"), (k, "k"), (scores, "scores")):
+        _inner_contig(t_, nm)
+    B, t, h_i, d_i = q.shape
+    n = k.shape[1] if n is None else n
+    _check(lib().csa_index_score(_ptr(q), _ptr(w), _ptr(k), _ptr(scores), _dt(q), B, t, h_i, d_i, n,
+                                 _ptr(q_pos), ratio, q.stride(0), w.stride(0),
+                                 k.stride(0) if k.shape[0] > 1 else 0, scores.stride(0),
+                                 scores.shape[2], _stream(stream)))
+
+
+def csa_topk_workspace_size(batch: int, t: int, n: int, k: int) -> int:
+    return int(lib().csa_topk_workspace_size(batch, t, n, k))
+
+
+def csa_topk(scores, k: int, idx, count, ws, n: Optional[int] = None, stream=None) -> None:
+    """scores [B, t, ld] float32 (first n columns); idx [B, t, k] int32; count [B, t] int32."""
+    _inner_contig(scores, "scores")
+    B, t, ld = scores.shape
+    n = ld if n is None else n
+    _check(lib().csa_topk(_ptr(scores), B, t, n, ld, scores.stride(0), k, _ptr(idx), _ptr(count),
+                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def csa_gather(comp_kv, idx, count, swa, swa_head: int, swa_len: int, gather_buf, n_valid,
+               n_comp: Optional[int] = None, stream=None) -> None:
+    """comp_kv [B, >=n_comp, d]; idx [B, k]; count [B]; swa [B, W, d]; gather_buf [B, k+W, d]."""
+    for t_, nm in ((comp_kv, "comp_kv"), (swa, "swa"), (gather_buf, "gather_buf")):
+        _inner_contig(t_, nm)
+    B, _, d = gather_buf.shape
+    k = idx.shape[1]
+    W = swa.shape[1]
+    n_comp = comp_kv.shape[1] if n_comp is None else n_comp
+    _check(lib().csa_gather(_ptr(comp_kv), n_comp, _ptr(idx), _ptr(count), k, _ptr(swa), swa_head,
+                            swa_len, W, _ptr(gather_buf), _ptr(n_valid), _dt(gather_buf), B, d,
+                            comp_kv.stride(0), swa.stride(0), gather_buf.stride(0), _stream(stream)))
+
+
+def csa_sparse_attn_workspace_size(batch: int, h: int, d: int, n_max: int) -> int:
+    return int(lib().csa_sparse_attn_workspace_size(batch, h, d, n_max))
+
+
+def csa_sparse_attn(q, kv, n_valid, sink, scale: float, out, lse=None, ws=None, stream=None) -> None:
+    """q [B, h, d]; kv [B, n_max, d]; n_valid [B] int32; sink [h] or None; out [B, h, d]."""
+    for t_, nm in ((q, "q"), (kv, "kv"), (out, "out")):
+        _inner_contig(t_, nm)
+    B, h, d = q.shape
+    n_max = kv.shape[1]
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().csa_sparse_attn(_ptr(q), _ptr(kv), _ptr(n_valid), _ptr(sink), scale, _ptr(out),
+                                 _ptr(lse), _dt(q), _dt(out), B, h, d, n_max, q.stride(0),
+                                 kv.stride(0), out.stride(0), _ptr(ws), wsb, _stream(stream)))
+
+
+def csa_decode_step_workspace_size(layer: LayerDesc) -> int:
+    return int(lib().csa_decode_step_workspace_size(ctypes.byref(layer)))
+
+
+def csa_decode_step(layer: LayerDesc, io: StepIO, ws, stream=None) -> None:
+    _check(lib().csa_decode_step(ctypes.byref(layer), ctypes.byref(io), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def csa_layer_advance(layer: LayerDesc, pos: int) -> None:
+    _check(lib().csa_layer_advance(ctypes.byref(layer), pos))
+
+
+def make_layer_desc(*, comp_kv, idx_keys, swa, main_bias, idx_bias, sink, n_comp: int,
+                    swa_head: int, swa_len: int, h: int, h_i: int, m: int = 4, top_k: int,
+                    overlap: int = 0, out_dtype=None, scale: Optional[float] = None,
+                    main_norm=None, idx_norm=None) -> LayerDesc:
+    """Fill a LayerDesc from cache tensors: comp_kv [B, max_comp, d], idx_keys
+    [B, max_comp, d_i], swa [B, W, d]."""
+    B, max_comp, d = comp_kv.shape
+    L = LayerDesc()
+    L.batch, L.h, L.d, L.h_i, L.d_i = B, h, d, h_i, idx_keys.shape[2]
+    L.m, L.w, L.top_k, L.overlap = m, swa.shape[1], top_k, overlap
+    L.dtype = _dt(comp_kv)
+    L.out_dtype = _dt(comp_kv) if out_dtype is None else (CSA_BF16 if out_dtype == torch.bfloat16 else CSA_F32)
+    L.comp_kv, L.comp_kv_stride_b = comp_kv.data_ptr(), comp_kv.stride(0)
+    L.idx_keys, L.idx_keys_stride_b = idx_keys.data_ptr(), idx_keys.stride(0)
+    L.swa, L.swa_stride_b = swa.data_ptr(), swa.stride(0)
+    L.max_comp = max_comp
+    L.main_bias, L.idx_bias = main_bias.data_ptr(), idx_bias.data_ptr()
+    L.main_norm, L.idx_norm = _ptr(main_norm), _ptr(idx_norm)
+    L.sink = _ptr(sink)
+    L.scale = (1.0 / d ** 0.5) if scale is None else scale
+    L.n_comp, L.swa_head, L.swa_len = n_comp, swa_head, swa_len
+    return L
+
+
+def make_step_io(*, pos: int, q, q_idx, w_idx, kv_new, z_main, c_main, z_idx, c_idx, scores,
+                 topk_idx, topk_count, gather_buf, n_valid, out, lse=None) -> StepIO:
+    """q [B, h, d]; q_idx [B, h_i, d_i]; w_idx [B, h_i]; kv_new [B, d]; z/c [B, rows, width];
+    scores [B, >=N]; topk_idx [B, k]; topk_count [B]; gather_buf [B, k+W, d]; out [B, h, d]."""
+    io = StepIO()
+    io.pos = pos
+    io.q, io.q_stride_b = q.data_ptr(), q.stride(0)
+    io.q_idx, io.q_idx_stride_b = q_idx.data_ptr(), q_idx.stride(0)
+    io.w_idx, io.w_stride_b = w_idx.data_ptr(), w_idx.stride(0)
+    io.kv_new, io.kv_new_stride_b = kv_new.data_ptr(), kv_new.stride(0)
+    io.z_main, io.c_main, io.zc_main_stride_b = z_main.data_ptr(), c_main.data_ptr(), z_main.stride(0)
+    io.z_idx, io.c_idx, io.zc_idx_stride_b = z_idx.data_ptr(), c_idx.data_ptr(), z_idx.stride(0)
+    io.scores, io.scores_stride_b = scores.data_ptr(), scores.stride(0)
+    io.topk_idx, io.topk_count = topk_idx.data_ptr(), topk_count.data_ptr()
+    io.gather_buf, io.gather_stride_b = gather_buf.data_ptr(), gather_buf.stride(0)
+    io.n_valid = n_valid.data_ptr()
+    io.out, io.out_stride_b = out.data_ptr(), out.stride(0)
+    io.lse = _ptr(lse)
+    return io

@@ -1,0 +1,343 @@
+// C ABI of the CSA decode path (declared in include/csa.h).
+//
+// This layer validates host-known arguments, sizes workspaces and enqueues
+// the kernels of compress.hip, index_score.hip, topk.hip, gather.hip and
+// attn.hip on the caller's stream.  It never synchronises, never reads device
+// memory and never allocates.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+
+#include "../../include/csa.h"
+#include "kernels.h"
+
+namespace csa {
+
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (dev >= 0 && dev < 64) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+}  // namespace csa
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return CSA_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(CSA_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+#define CHECK(cond, ...)                                            \
+    do {                                                            \
+        if (!(cond)) return fail(CSA_ERR_INVALID_ARG, __VA_ARGS__); \
+    } while (0)
+
+int elem_size(csa_dtype dt) { return dt == CSA_BF16 ? 2 : 4; }
+bool dtype_ok(int dt) { return dt == CSA_F32 || dt == CSA_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_last_error(void) { return g_err; }
+
+int csa_compress(const float* z, const float* c, const float* bias, const float* norm_w, void* out,
+                 csa_dtype out_dtype, int batch, int n_blocks, int m, int d, int overlap,
+                 int first_block, long long zc_stride_b, long long out_stride_b, csa_stream stream) {
+    CHECK(z && c && bias && out, "csa_compress: null pointer argument");
+    CHECK(dtype_ok(out_dtype), "csa_compress: bad out_dtype %d", (int)out_dtype);
+    CHECK(batch >= 1 && n_blocks >= 0, "csa_compress: batch %d / n_blocks %d", batch, n_blocks);
+    CHECK(m >= 1 && m <= 1024, "csa_compress: m=%d out of 1..1024", m);
+    CHECK(d >= 1 && d <= 4096, "csa_compress: d=%d out of 1..4096", d);
+    CHECK(overlap == 0 || overlap == 1, "csa_compress: overlap must be 0 or 1");
+    CHECK(first_block >= 0, "csa_compress: first_block < 0");
+    CHECK(zc_stride_b >= 0 && out_stride_b >= 0, "csa_compress: negative stride");
+    CHECK(batch == 1 || (zc_stride_b > 0 && out_stride_b > 0), "csa_compress: zero batch stride");
+    return launched(csa::launch_compress(z, c, bias, norm_w, out, out_dtype == CSA_BF16, batch,
+                                         n_blocks, m, d, overlap != 0, first_block, zc_stride_b,
+                                         out_stride_b, static_cast<hipStream_t>(stream)),
+                    "csa_compress");
+}
+
+static int check_score_args(const void* q, const float* w, const void* k, float* scores,
+                            csa_dtype dtype, int batch, int t, int h_i, int d_i, int n, int ratio,
+                            long long q_stride_b, long long w_stride_b, long long k_stride_b,
+                            long long s_stride_b, long long ld_s, const char* who) {
+    CHECK(q && w && k && scores, "%s: null pointer argument", who);
+    CHECK(dtype_ok(dtype), "%s: bad dtype %d", who, (int)dtype);
+    CHECK(batch >= 1 && t >= 1 && n >= 0, "%s: batch %d t %d n %d", who, batch, t, n);
+    CHECK(batch * static_cast<long long>(t) <= 65535, "%s: batch*t above 65535", who);
+    CHECK(ratio >= 1, "%s: ratio %d", who, ratio);
+    CHECK(ld_s >= n && q_stride_b >= 0 && w_stride_b >= 0 && k_stride_b >= 0 && s_stride_b >= 0,
+          "%s: bad strides", who);
+    if (dtype == CSA_BF16) {
+        if (h_i != 64 || d_i != 128)
+            return fail(CSA_ERR_UNSUPPORTED, "%s: bf16 path needs h_i=64, d_i=128 (got %d, %d)", who, h_i, d_i);
+        CHECK(aligned16(q) && aligned16(k) && aligned16(w), "%s: q, k, w must be 16-byte aligned", who);
+        CHECK(q_stride_b % 8 == 0 && k_stride_b % 8 == 0 && w_stride_b % 4 == 0,
+              "%s: batch strides must keep 16-byte alignment", who);
+    } else {
+        if (h_i < 1 || h_i > 64 || d_i < 1 || d_i > 256 || h_i * d_i > 8192)
+            return fail(CSA_ERR_UNSUPPORTED, "%s: f32 path needs 1<=h_i<=64, 1<=d_i<=256, h_i*d_i<=8192", who);
+    }
+    return CSA_OK;
+}
+
+int csa_index_score(const void* q, const float* w, const void* k, float* scores, csa_dtype dtype,
+                    int batch, int t, int h_i, int d_i, int n, const int* q_pos, int ratio,
+                    long long q_stride_b, long long w_stride_b, long long k_stride_b,
+                    long long s_stride_b, long long ld_s, csa_stream stream) {
+    const int rc = check_score_args(q, w, k, scores, dtype, batch, t, h_i, d_i, n, ratio, q_stride_b,
+                                    w_stride_b, k_stride_b, s_stride_b, ld_s, "csa_index_score");
+    if (rc != CSA_OK) return rc;
+    csa::ScoreArgs a{q, w, k, scores, batch, t, h_i, d_i, n, q_pos, ratio,
+                     q_stride_b, w_stride_b, k_stride_b, s_stride_b, ld_s, nullptr};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    return launched(dtype == CSA_BF16 ? csa::launch_index_score_bf16(a, s)
+                                      : csa::launch_index_score_f32(a, s),
+                    "csa_index_score");
+}
+
+size_t csa_topk_workspace_size(int batch, int t, int n, int k) {
+    if (batch < 1 || t < 1 || n < 0 || k < 1) return 0;
+    return csa::topk_workspace_bytes(batch * t, n, k);
+}
+
+int csa_topk(const float* scores, int batch, int t, int n, long long ld_s, long long s_stride_b,
+             int k, int* idx, int* count, void* ws, size_t ws_bytes, csa_stream stream) {
+    CHECK(idx && ws && (scores || n == 0), "csa_topk: null pointer argument");
+    CHECK(batch >= 1 && t >= 1 && n >= 0, "csa_topk: batch %d t %d n %d", batch, t, n);
+    CHECK(batch * static_cast<long long>(t) <= 65535, "csa_topk: batch*t above 65535");
+    CHECK(k >= 1 && k <= csa::kTopkMaxK, "csa_topk: k=%d out of 1..%d", k, csa::kTopkMaxK);
+    CHECK(ld_s >= n && s_stride_b >= 0, "csa_topk: bad strides");
+    CHECK(aligned16(ws), "csa_topk: workspace must be 16-byte aligned");
+    if (ws_bytes < csa_topk_workspace_size(batch, t, n, k))
+        return fail(CSA_ERR_WORKSPACE, "csa_topk: workspace %zu < %zu bytes", ws_bytes,
+                    csa_topk_workspace_size(batch, t, n, k));
+    csa::TopkArgs a{scores, batch, t, n, ld_s, s_stride_b, k, idx, count, ws};
+    return launched(csa::launch_topk(a, false, static_cast<hipStream_t>(stream)), "csa_topk");
+}
+
+int csa_gather(const void* comp_kv, int n_comp, const int* idx, const int* count, int k,
+               const void* swa, int swa_head, int swa_len, int w, void* gather_buf, int* n_valid,
+               csa_dtype dtype, int batch, int d, long long kv_stride_b, long long swa_stride_b,
+               long long buf_stride_b, csa_stream stream) {
+    CHECK(gather_buf && (idx || k == 0) && (comp_kv || n_comp == 0) && (swa || swa_len == 0),
+          "csa_gather: null pointer argument");
+    CHECK(dtype_ok(dtype), "csa_gather: bad dtype");
+    CHECK(batch >= 1 && d >= 1 && k >= 0 && n_comp >= 0, "csa_gather: bad sizes");
+    CHECK(w >= 1 && swa_head >= 0 && swa_head < w && swa_len >= 0 && swa_len <= w,
+          "csa_gather: bad window (w %d head %d len %d)", w, swa_head, swa_len);
+    CHECK((static_cast<long long>(d) * elem_size(dtype)) % 16 == 0, "csa_gather: row bytes must be a multiple of 16");
+    CHECK(aligned16(gather_buf) && (!comp_kv || aligned16(comp_kv)) && (!swa || aligned16(swa)),
+          "csa_gather: buffers must be 16-byte aligned");
+    CHECK(kv_stride_b >= 0 && swa_stride_b >= 0 && buf_stride_b >= 0, "csa_gather: negative stride");
+    const int es = elem_size(dtype);
+    CHECK((kv_stride_b * es) % 16 == 0 && (swa_stride_b * es) % 16 == 0 && (buf_stride_b * es) % 16 == 0,
+          "csa_gather: batch strides must keep 16-byte alignment");
+    return launched(csa::launch_gather(comp_kv, n_comp, idx, count, k, swa, swa_head, swa_len, w,
+                                       gather_buf, n_valid, es, batch, d, kv_stride_b, swa_stride_b,
+                                       buf_stride_b, static_cast<hipStream_t>(stream)),
+                    "csa_gather");
+}
+
+size_t csa_sparse_attn_workspace_size(int batch, int h, int d, int n_max) {
+    if (batch < 1 || h < 1 || d < 1 || n_max < 0) return 0;
+    const size_t s = csa::attn_workspace_bytes(true, batch, h, d, n_max);
+    return s > 0 ? s : 16;
+}
+
+static int check_attn(const void* q, const void* kv, const int* n_valid, void* out,
+                      csa_dtype dtype, csa_dtype out_dtype, int batch, int h, int d, int n_max,
+                      long long q_stride_b, long long kv_stride_b, long long out_stride_b,
+                      const char* who) {
+    CHECK(q && kv && n_valid && out, "%s: null pointer argument", who);
+    CHECK(dtype_ok(dtype) && dtype_ok(out_dtype), "%s: bad dtype", who);
+    CHECK(batch >= 1 && h >= 1 && d >= 1 && n_max >= 0, "%s: bad sizes", who);
+    CHECK(q_stride_b >= 0 && kv_stride_b >= 0 && out_stride_b >= 0, "%s: negative stride", who);
+    if (dtype == CSA_BF16) {
+        if (h % 16 != 0 || d % 32 != 0 || d > 512)
+            return fail(CSA_ERR_UNSUPPORTED, "%s: bf16 path needs h%%16==0, d%%32==0, d<=512", who);
+        CHECK(aligned16(q) && aligned16(kv), "%s: q, kv must be 16-byte aligned", who);
+        CHECK(q_stride_b % 8 == 0 && kv_stride_b % 8 == 0, "%s: batch strides must keep 16-byte alignment", who);
+        CHECK(batch <= 65535 && h / 16 <= 65535, "%s: grid too large", who);
+    } else {
+        if (d > 1024 || n_max > 8192)
+            return fail(CSA_ERR_UNSUPPORTED, "%s: f32 path needs d<=1024, n_max<=8192", who);
+    }
+    return CSA_OK;
+}
+
+int csa_sparse_attn(const void* q, const void* kv, const int* n_valid, const float* sink, float scale,
+                    void* out, float* lse, csa_dtype dtype, csa_dtype out_dtype, int batch, int h,
+                    int d, int n_max, long long q_stride_b, long long kv_stride_b,
+                    long long out_stride_b, void* ws, size_t ws_bytes, csa_stream stream) {
+    const int rc = check_attn(q, kv, n_valid, out, dtype, out_dtype, batch, h, d, n_max, q_stride_b,
+                              kv_stride_b, out_stride_b, "csa_sparse_attn");
+    if (rc != CSA_OK) return rc;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == CSA_BF16) {
+        CHECK(ws && aligned16(ws), "csa_sparse_attn: workspace missing or misaligned");
+        const size_t need = csa::attn_workspace_bytes(true, batch, h, d, n_max);
+        if (ws_bytes < need)
+            return fail(CSA_ERR_WORKSPACE, "csa_sparse_attn: workspace %zu < %zu bytes", ws_bytes, need);
+        return launched(csa::launch_attn_bf16(q, kv, n_valid, sink, scale, out, out_dtype == CSA_BF16,
+                                              lse, batch, h, d, n_max, q_stride_b, kv_stride_b,
+                                              out_stride_b, ws, s),
+                        "csa_sparse_attn");
+    }
+    return launched(csa::launch_attn_f32(q, kv, n_valid, sink, scale, out, out_dtype == CSA_BF16, lse,
+                                         batch, h, d, n_max, q_stride_b, kv_stride_b, out_stride_b, s),
+                    "csa_sparse_attn");
+}
+
+// ---- fused decode step ------------------------------------------------------------
+
+static size_t step_topk_bytes(const csa_layer_desc* L) {
+    return align256(csa::topk_workspace_bytes(L->batch, L->max_comp, L->top_k));
+}
+
+size_t csa_decode_step_workspace_size(const csa_layer_desc* L) {
+    if (!L || L->batch < 1 || L->max_comp < 0 || L->top_k < 1) return 0;
+    return step_topk_bytes(L) +
+           align256(csa::attn_workspace_bytes(L->dtype == CSA_BF16, L->batch, L->h, L->d, L->top_k + L->w)) +
+           256;
+}
+
+int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes,
+                    csa_stream stream) {
+    CHECK(L && io, "csa_decode_step: null layer or io");
+    CHECK(dtype_ok(L->dtype) && dtype_ok(L->out_dtype), "csa_decode_step: bad dtype");
+    CHECK(L->batch >= 1 && L->m >= 1 && L->w >= 1 && L->top_k >= 1 && L->top_k <= csa::kTopkMaxK,
+          "csa_decode_step: bad batch/m/w/top_k");
+    CHECK(L->overlap == 0 || L->overlap == 1, "csa_decode_step: overlap must be 0 or 1");
+    CHECK(L->comp_kv && L->idx_keys && L->swa && L->main_bias && L->idx_bias,
+          "csa_decode_step: null cache or bias pointer");
+    CHECK(io->q && io->q_idx && io->w_idx && io->kv_new && io->scores && io->topk_idx &&
+              io->topk_count && io->gather_buf && io->n_valid && io->out,
+          "csa_decode_step: null io pointer");
+    CHECK(io->pos >= 0, "csa_decode_step: pos < 0");
+    CHECK(L->n_comp >= 0 && L->n_comp <= L->max_comp, "csa_decode_step: n_comp %d outside 0..max_comp %d",
+          L->n_comp, L->max_comp);
+    CHECK(L->swa_head >= 0 && L->swa_head < L->w && L->swa_len >= 0 && L->swa_len <= L->w,
+          "csa_decode_step: bad SWA state");
+    const bool completes = io->pos % L->m == L->m - 1;
+    if (completes) {
+        CHECK(io->z_main && io->c_main && io->z_idx && io->c_idx, "csa_decode_step: block rows missing");
+        CHECK(L->n_comp < L->max_comp, "csa_decode_step: compressed cache full (max_comp %d)", L->max_comp);
+    }
+    if (!aligned16(ws)) return fail(CSA_ERR_INVALID_ARG, "csa_decode_step: workspace must be 16-byte aligned");
+    if (ws_bytes < csa_decode_step_workspace_size(L))
+        return fail(CSA_ERR_WORKSPACE, "csa_decode_step: workspace %zu < %zu bytes", ws_bytes,
+                    csa_decode_step_workspace_size(L));
+    const int N = L->n_comp + (completes ? 1 : 0);
+    const int rc_s = check_score_args(io->q_idx, io->w_idx, L->idx_keys, io->scores, L->dtype, L->batch,
+                                      1, L->h_i, L->d_i, N, L->m, io->q_idx_stride_b, io->w_stride_b,
+                                      L->idx_keys_stride_b, io->scores_stride_b, N, "csa_decode_step");
+    if (rc_s != CSA_OK) return rc_s;
+    const int n_max = L->top_k + L->w;
+    const int rc_a = check_attn(io->q, io->gather_buf, io->n_valid, io->out, L->dtype, L->out_dtype,
+                                L->batch, L->h, L->d, n_max, io->q_stride_b, io->gather_stride_b,
+                                io->out_stride_b, "csa_decode_step");
+    if (rc_a != CSA_OK) return rc_a;
+    const int es = elem_size(L->dtype);
+    CHECK((static_cast<long long>(L->d) * es) % 16 == 0, "csa_decode_step: row bytes must be a multiple of 16");
+
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf = L->dtype == CSA_BF16;
+    hipError_t e;
+
+    // a. new token -> SWA ring
+    e = csa::launch_swa_append(io->kv_new, L->swa, L->swa_head, es, L->batch, L->d,
+                               io->kv_new_stride_b, L->swa_stride_b, s);
+    if (e != hipSuccess) return launched(e, "csa_decode_step/swa_append");
+    const int swa_head = (L->swa_head + 1) % L->w;
+    const int swa_len = L->swa_len + 1 < L->w ? L->swa_len + 1 : L->w;
+
+    // b. compress the completed block (main KV and indexer key)
+    if (completes) {
+        const int blk = io->pos / L->m;
+        const bool joint = L->overlap && blk > 0;
+        const long long skip_main = joint ? static_cast<long long>(L->m) * 2 * L->d : 0;
+        const long long skip_idx = joint ? static_cast<long long>(L->m) * 2 * L->d_i : 0;
+        char* ck = static_cast<char*>(L->comp_kv) + static_cast<long long>(L->n_comp) * L->d * es;
+        char* ik = static_cast<char*>(L->idx_keys) + static_cast<long long>(L->n_comp) * L->d_i * es;
+        e = csa::launch_compress(io->z_main + skip_main, io->c_main + skip_main, L->main_bias, L->main_norm,
+                                 ck, bf, L->batch, 1, L->m, L->d, L->overlap != 0, blk,
+                                 io->zc_main_stride_b, L->comp_kv_stride_b, s);
+        if (e != hipSuccess) return launched(e, "csa_decode_step/compress_main");
+        e = csa::launch_compress(io->z_idx + skip_idx, io->c_idx + skip_idx, L->idx_bias, L->idx_norm,
+                                 ik, bf, L->batch, 1, L->m, L->d_i, L->overlap != 0, blk,
+                                 io->zc_idx_stride_b, L->idx_keys_stride_b, s);
+        if (e != hipSuccess) return launched(e, "csa_decode_step/compress_idx");
+    }
+
+    // c. score (fused radix histogram) -> top-k -> gather -> attention
+    void* tws = ws;
+    void* aws = static_cast<char*>(ws) + step_topk_bytes(L);
+    e = csa::launch_topk_ws_clear(tws, L->batch, N, L->top_k, s);
+    if (e != hipSuccess) return launched(e, "csa_decode_step/topk_clear");
+    csa::ScoreArgs sa{io->q_idx, io->w_idx, L->idx_keys, io->scores, L->batch, 1, L->h_i, L->d_i, N,
+                      nullptr, L->m, io->q_idx_stride_b, io->w_stride_b, L->idx_keys_stride_b,
+                      io->scores_stride_b, N, csa::topk_ws_hist(tws)};
+    e = bf ? csa::launch_index_score_bf16(sa, s) : csa::launch_index_score_f32(sa, s);
+    if (e != hipSuccess) return launched(e, "csa_decode_step/index_score");
+    csa::TopkArgs ta{io->scores, L->batch, 1, N, N, io->scores_stride_b, L->top_k, io->topk_idx,
+                     io->topk_count, tws};
+    e = csa::launch_topk(ta, true, s);
+    if (e != hipSuccess) return launched(e, "csa_decode_step/topk");
+    e = csa::launch_gather(L->comp_kv, N, io->topk_idx, io->topk_count, L->top_k, L->swa, swa_head,
+                           swa_len, L->w, io->gather_buf, io->n_valid, es, L->batch, L->d,
+                           L->comp_kv_stride_b, L->swa_stride_b, io->gather_stride_b, s);
+    if (e != hipSuccess) return launched(e, "csa_decode_step/gather");
+    e = bf ? csa::launch_attn_bf16(io->q, io->gather_buf, io->n_valid, L->sink, L->scale, io->out,
+                                   L->out_dtype == CSA_BF16, io->lse, L->batch, L->h, L->d, n_max,
+                                   io->q_stride_b, io->gather_stride_b, io->out_stride_b, aws, s)
+           : csa::launch_attn_f32(io->q, io->gather_buf, io->n_valid, L->sink, L->scale, io->out,
+                                  L->out_dtype == CSA_BF16, io->lse, L->batch, L->h, L->d, n_max,
+                                  io->q_stride_b, io->gather_stride_b, io->out_stride_b, s);
+    return launched(e, "csa_decode_step/attention");
+}
+
+int csa_layer_advance(csa_layer_desc* L, int pos) {
+    CHECK(L && L->w >= 1 && L->m >= 1 && pos >= 0, "csa_layer_advance: bad arguments");
+    if (pos % L->m == L->m - 1) {
+        CHECK(L->n_comp < L->max_comp, "csa_layer_advance: compressed cache full");
+        L->n_comp += 1;
+    }
+    L->swa_head = (L->swa_head + 1) % L->w;
+    L->swa_len = L->swa_len + 1 < L->w ? L->swa_len + 1 : L->w;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,275 @@
+/*
+ * csa.h — C ABI of the compressed-sparse-attention (CSA) decode path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Five steps and their fused composition, as described on the source pages
+ * (git compare views of the nvfp4-megamoe-kernel repository, a DeepSeek-V4
+ * inference bring-up):
+ *
+ *   1. csa_compress     — compressor reduce: per channel, softmax over a block's
+ *                         token rows of Z + B, then the weighted sum of C.
+ *   2. csa_index_score  — lightning indexer: sum over heads of w * ReLU(q . K),
+ *                         one key per compressed block shared by every head.
+ *   3. csa_topk         — fixed-shape top-k, score descending, lower index first.
+ *   4. csa_gather       — selected compressed rows, then the sliding window,
+ *                         into one preallocated gather_buf.
+ *   5. csa_sparse_attn  — one softmax over gather_buf rows (K = V) plus a
+ *                         per-head sink logit that adds to the denominator only.
+ *   6. csa_decode_step  — 1..5 for one new token of one layer, stream-ordered.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every tensor argument is DEVICE memory owned by the caller; the
+ *           library allocates nothing, frees nothing and keeps no state
+ *           between calls other than the thread-local error message and a
+ *           cache of each device's compute-unit count.
+ *           Scratch memory is passed in as a workspace whose size is queried
+ *           first (the *_workspace_size functions).
+ * Layout.   Row-major.  "[B][N][D] with stride_b" means element (b, n, d)
+ *           lives at base + b * stride_b + n * D + d, counted in ELEMENTS of
+ *           the tensor's own type.  Batch strides may be 0 only where stated.
+ * Types.    csa_dtype selects float32 or bfloat16 storage for the tensors an
+ *           entry point documents as "dtype"; everything else is float32
+ *           (weights, biases, sinks, scores) or int32 (indices, counts).
+ *           Arithmetic is float32 throughout; bfloat16 outputs are rounded
+ *           once, to nearest even.
+ * Streams.  All work is enqueued on `stream` (a hipStream_t; NULL = the
+ *           default stream).  No call synchronises the host, reads device
+ *           memory on the host, or allocates; every call can be recorded
+ *           into a HIP graph.
+ * Errors.   Only host-known integers and pointers are validated.  A failed
+ *           check returns CSA_ERR_INVALID_ARG (or CSA_ERR_UNSUPPORTED /
+ *           CSA_ERR_WORKSPACE) before anything is enqueued; a launch failure
+ *           returns CSA_ERR_LAUNCH.  csa_last_error() describes the last
+ *           non-OK status of the calling thread.  Device-side index values
+ *           are clamped into range, never trusted for memory addressing.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CSA_OK = 0,
+    CSA_ERR_INVALID_ARG = -1,
+    CSA_ERR_UNSUPPORTED = -2,
+    CSA_ERR_LAUNCH = -3,
+    CSA_ERR_WORKSPACE = -4
+} csa_status;
+
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
+
+typedef void *csa_stream; /* hipStream_t */
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char *csa_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * 1. Compressor reduce.
+ *
+ * Source: page 1 (compare v0.1-e2e-working...v-c1-c2-c3-20260602), file
+ * dsv4/kernels/cuda/compressor_reduce.cu, header (paper eq. 9-12) and the
+ * kernels hca_compress_reduce_kernel / csa_compress_reduce_kernel, with the
+ * fix of page 2 and page 3 ("Fix two correctness bugs: compressor pos bias on
+ * KV"): B is added to the logits Z only, never to C.  Optional weighted
+ * RMSNorm of each output row (apply_kv_norm_kernel, eps 1e-6).
+ *
+ * overlap = 0: block i of batch b uses rows i*m .. i*m+m-1 of Z and C
+ *   ([B][rows][d], stride_b = zc_stride_b floats) with bias row t for its t-th
+ *   row; B is [m][d].
+ * overlap = 1: Z, C rows are 2*d wide (a half | b half) and B is [m][2*d].
+ *   Global block g = first_block + i uses, in one joint softmax, the m rows of
+ *   block g-1 from the a half followed by its own m rows from the b half; block
+ *   g = 0 uses its own b-half rows only.  z and c point at the first row of
+ *   block first_block; when first_block > 0 the m rows before z and c (block
+ *   first_block - 1) must be readable.
+ * out:    [B][n_blocks][d] of out_dtype, stride_b = out_stride_b elements.
+ * norm_w: [d] float32 or NULL (no norm).
+ * Limits: 1 <= m <= 1024, 1 <= d <= 4096, batch >= 1, n_blocks >= 0.
+ * ------------------------------------------------------------------------ */
+int csa_compress(const float *z, const float *c, const float *bias, const float *norm_w,
+                 void *out, csa_dtype out_dtype, int batch, int n_blocks, int m, int d,
+                 int overlap, int first_block, long long zc_stride_b, long long out_stride_b,
+                 csa_stream stream);
+
+/* ------------------------------------------------------------------------
+ * 2. Lightning-indexer score.
+ *
+ * Source: page 1, ARCHITECTURE_AND_MEMORY_AUDIT.md, finding F3 (paper
+ * section 2.3.1, eq. 16): I[t,s] = sum_h w[t,h] * ReLU(q[t,h] . K[s]); one
+ * d_i-wide key per compressed block, shared by all h_i heads.  No scale.
+ * Causal form: page 1, archived_plans/NEXT_STEPS.md, Issue 2 — block s is
+ * visible to a query at position p iff ratio*s + ratio - 1 <= p, otherwise
+ * its score is -inf.
+ *
+ * q:      [B][t][h_i][d_i] of dtype, stride_b = q_stride_b elements.
+ * w:      [B][t][h_i] float32, stride_b = w_stride_b.
+ * k:      [B][n][d_i] of dtype, stride_b = k_stride_b (0 = shared keys).
+ * scores: [B][t][ld_s] float32, stride_b = s_stride_b; columns 0..n-1 written.
+ * q_pos:  [B][t] int32 device positions for the causal mask, or NULL.
+ * Supported: bfloat16 with h_i = 64, d_i = 128 (matrix-core path) and
+ *   float32 with h_i <= 64, d_i <= 256, h_i * d_i <= 8192.  n >= 0; ld_s >= n.
+ * ------------------------------------------------------------------------ */
+int csa_index_score(const void *q, const float *w, const void *k, float *scores,
+                    csa_dtype dtype, int batch, int t, int h_i, int d_i, int n,
+                    const int *q_pos, int ratio, long long q_stride_b, long long w_stride_b,
+                    long long k_stride_b, long long s_stride_b, long long ld_s,
+                    csa_stream stream);
+
+/* ------------------------------------------------------------------------
+ * 3. Top-k.
+ *
+ * Source: page 1, ARCHITECTURE_AND_MEMORY_AUDIT.md, F3 code
+ * (tk = min(top_k, n_comp); total.topk(tk, -1)) and page 3,
+ * GETTING+CUDAGRAPH_READY.md, Section C item 3 (always k slots, invalid ones
+ * masked, no host read of the count).
+ *
+ * For each of the rows = batch * t score rows (row r of batch b at
+ * scores + b * s_stride_b + (r % t) * ld_s), select the k largest valid
+ * scores (valid = greater than -inf; NaN is out of contract), ordered by
+ * score descending, then index ascending (+0 and -0 are equal).
+ * idx:   [B][t][k] int32, unused slots -1.   count: [B][t] int32 = min(k, valid)
+ *        (count may be NULL).
+ * ws:    csa_topk_workspace_size(batch, t, n, k) bytes of device memory,
+ *        16-byte aligned; contents need no initialisation.
+ * Limits: 1 <= k <= 2048, 0 <= n < 2^31.
+ * ------------------------------------------------------------------------ */
+size_t csa_topk_workspace_size(int batch, int t, int n, int k);
+int csa_topk(const float *scores, int batch, int t, int n, long long ld_s, long long s_stride_b,
+             int k, int *idx, int *count, void *ws, size_t ws_bytes, csa_stream stream);
+
+/* ------------------------------------------------------------------------
+ * 4. Gather into gather_buf.
+ *
+ * Source: page 1 commit message C2 (one preallocated (top_k + window, hd)
+ * buffer, filled by slice assignment, no concatenation) and C3 (the SWA ring
+ * may wrap); page 1, PERFORMANCE_AUDIT.md, P2 (slot (swa_head + i) % W,
+ * swa_len = min(swa_len + T, W)); compressed rows first, then the window
+ * (ARCHITECTURE_AND_MEMORY_AUDIT.md, B2).
+ *
+ * For batch b: rows 0..count[b]-1 of gather_buf are comp_kv[idx[b][j]]
+ * (indices clamped to 0..n_comp-1), followed by the swa_len live window rows
+ * oldest first: swa[(swa_head - swa_len + j) mod w].  n_valid[b] =
+ * count[b] + swa_len.  Rows at and beyond n_valid are not written.
+ * comp_kv:    [B][n_comp][d] of dtype, stride kv_stride_b.
+ * idx, count: [B][k] and [B] int32 (from csa_topk; count NULL = k).
+ * swa:        [B][w][d] of dtype, stride swa_stride_b; swa_head is the next
+ *             write slot (0 <= swa_head < w), 0 <= swa_len <= w.
+ * gather_buf: [B][k + w][d] of dtype, stride buf_stride_b.
+ * n_valid:    [B] int32 (may be NULL).
+ * Limits: d * sizeof(dtype) must be a multiple of 16 bytes.
+ * ------------------------------------------------------------------------ */
+int csa_gather(const void *comp_kv, int n_comp, const int *idx, const int *count, int k,
+               const void *swa, int swa_head, int swa_len, int w, void *gather_buf, int *n_valid,
+               csa_dtype dtype, int batch, int d, long long kv_stride_b, long long swa_stride_b,
+               long long buf_stride_b, csa_stream stream);
+
+/* ------------------------------------------------------------------------
+ * 5. Shared-KV sparse attention with a per-head sink.
+ *
+ * Source: page 1, dsv4/kernels/attention/fmha_6warp_tma_multirow_multitile.cuh,
+ * hunk "Sink bias correction (D5c: single softmax over [S_comp, S_swa +
+ * sink])": after all rows, M = max(m, sink); the running sum and output are
+ * rescaled by exp(m - M) and the sum gains exp(sink - M); the sink has no
+ * value row and is already in the scaled domain.  K = V (page 1,
+ * PERFORMANCE_AUDIT.md P4; fmha_multitile_op.py, MQA head stride 0).
+ *
+ * For head h of batch b over rows j < n_valid[b] (clamped to n_max):
+ *   s_j = scale * q[h] . kv[j];  M = max(max_j s_j, sink[h]);
+ *   out[h] = sum_j exp(s_j - M) kv[j] / (sum_j exp(s_j - M) + exp(sink[h] - M));
+ *   lse[h] = M + ln(denominator).  No rows and no sink: out = 0, lse = -inf.
+ * q:   [B][h][d] of dtype, stride q_stride_b.     kv: [B][n_max][d] of dtype.
+ * sink:[h] float32 or NULL.   out: [B][h][d] of out_dtype.   lse: [B][h] or NULL.
+ * ws:  csa_sparse_attn_workspace_size(batch, h, d, n_max) bytes.
+ * Supported: bfloat16 with h % 16 == 0, d % 32 == 0, d <= 512;
+ *            float32 with d <= 1024, n_max <= 8192.
+ * ------------------------------------------------------------------------ */
+size_t csa_sparse_attn_workspace_size(int batch, int h, int d, int n_max);
+int csa_sparse_attn(const void *q, const void *kv, const int *n_valid, const float *sink,
+                    float scale, void *out, float *lse, csa_dtype dtype, csa_dtype out_dtype,
+                    int batch, int h, int d, int n_max, long long q_stride_b,
+                    long long kv_stride_b, long long out_stride_b, void *ws, size_t ws_bytes,
+                    csa_stream stream);
+
+/* ------------------------------------------------------------------------
+ * 6. One decode step of one CSA layer.
+ *
+ * Source: page 2 (compare master..pure-nvfp4), single_shot_inference.py,
+ * eager_attention: append the new token's KV to the SWA ring, run the main
+ * compressor and the indexer's key compressor, indexer top-k, gather, then
+ * attention.  The compressors emit an entry only when the token completes a
+ * block (page 1, PERFORMANCE_AUDIT.md P7): pos % m == m - 1.
+ *
+ * The layer state is host-known integers plus caller-owned device caches.
+ * The call enqueues, in stream order:
+ *   a. swa[swa_head] = kv_new (every batch element);
+ *   b. if pos % m == m - 1: comp_kv[n_comp] = compress(z_main, c_main) and
+ *      idx_keys[n_comp] = compress(z_idx, c_idx) (overlap convention as in
+ *      csa_compress, with first_block = pos / m);
+ *   c. scores over the N = n_comp (+1 if b ran) keys, top-k, gather, attention.
+ * It does NOT update the host integers: afterwards the caller sets
+ * swa_head = (swa_head + 1) % w, swa_len = min(swa_len + 1, w) and, if a block
+ * completed, n_comp += 1 (csa_layer_advance does exactly this).
+ * ------------------------------------------------------------------------ */
+typedef struct csa_layer_desc {
+    int batch;       /* sequences, each with its own caches             */
+    int h, d;        /* main attention heads and head dim (K = V)       */
+    int h_i, d_i;    /* indexer heads and key width                     */
+    int m;           /* compression ratio                               */
+    int w;           /* SWA window                                      */
+    int top_k;
+    int overlap;     /* 0: plain ratio-m blocks; 1: overlapped a|b form */
+    csa_dtype dtype; /* storage of q, q_idx, kv_new and all caches      */
+    csa_dtype out_dtype;
+    void *comp_kv;  long long comp_kv_stride_b;   /* [B][max_comp][d]   */
+    void *idx_keys; long long idx_keys_stride_b;  /* [B][max_comp][d_i] */
+    void *swa;      long long swa_stride_b;       /* [B][w][d]          */
+    int max_comp;
+    const float *main_bias; /* [m][d] (overlap: [m][2d])     */
+    const float *idx_bias;  /* [m][d_i] (overlap: [m][2d_i]) */
+    const float *main_norm; /* [d] or NULL   */
+    const float *idx_norm;  /* [d_i] or NULL */
+    const float *sink;      /* [h] or NULL   */
+    float scale;            /* attention logit scale (usually 1/sqrt(d)) */
+    int n_comp;             /* compressed entries before this step */
+    int swa_head;           /* next SWA write slot */
+    int swa_len;            /* live SWA rows */
+} csa_layer_desc;
+
+typedef struct csa_step_io {
+    int pos;                                          /* position of the new token   */
+    const void *q;      long long q_stride_b;         /* [B][h][d]                   */
+    const void *q_idx;  long long q_idx_stride_b;     /* [B][h_i][d_i]               */
+    const float *w_idx; long long w_stride_b;         /* [B][h_i]                    */
+    const void *kv_new; long long kv_new_stride_b;    /* [B][d]                      */
+    /* rows of the block this token completes (read only when it does):
+     * overlap 0: [B][m][d] / [B][m][d_i]; overlap 1: [B][2m][2d] / [B][2m][2d_i]
+     * holding block pos/m - 1 then block pos/m (block 0: its m rows only).   */
+    const float *z_main, *c_main; long long zc_main_stride_b;
+    const float *z_idx,  *c_idx;  long long zc_idx_stride_b;
+    /* outputs (device, caller-owned) */
+    float *scores;      long long scores_stride_b;    /* [B][>= N] float32           */
+    int *topk_idx;                                    /* [B][top_k]                  */
+    int *topk_count;                                  /* [B]                         */
+    void *gather_buf;   long long gather_stride_b;    /* [B][top_k + w][d] of dtype  */
+    int *n_valid;                                     /* [B]                         */
+    void *out;          long long out_stride_b;       /* [B][h][d] of out_dtype      */
+    float *lse;                                       /* [B][h] or NULL              */
+} csa_step_io;
+
+size_t csa_decode_step_workspace_size(const csa_layer_desc *layer);
+int csa_decode_step(const csa_layer_desc *layer, const csa_step_io *io, void *ws,
+                    size_t ws_bytes, csa_stream stream);
+
+/* Advance the host-known counters of `layer` past a step at position pos. */
+int csa_layer_advance(csa_layer_desc *layer, int pos);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

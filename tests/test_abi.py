@@ -1,0 +1,192 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every symbol that
+include/csa.h declares, lays out its structs as the C compiler does, and
+rejects bad host-known arguments before anything is enqueued (no GPU call is
+made by any test here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "csa.h")
+FAKE = 0x10000  # never dereferenced: validation fails before any device work
+
+
+@pytest.fixture(scope="module")
+def csa():
+    import compressed_sparse_attention_reduce_amd as pkg
+    from compressed_sparse_attention_reduce_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from compressed_sparse_attention_reduce_amd.build import build
+        build()
+    pkg.lib()
+    return pkg
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(csa):
+    names = _declared_functions()
+    assert {"csa_compress", "csa_index_score", "csa_topk", "csa_gather", "csa_sparse_attn",
+            "csa_decode_step"} <= set(names)
+    lib = csa.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", csa.binding.LIB_PATH], capture_output=True, text=True)
+    exported = set(re.findall(r" T (\w+)", out.stdout))
+    missing = [n for n in names if n not in exported]
+    assert not missing, f"not exported: {missing}"
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_struct_layout_matches_c(csa):
+    from compressed_sparse_attention_reduce_amd.binding import LayerDesc, StepIO
+    fields = {"csa_layer_desc": LayerDesc, "csa_step_io": StepIO}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){"]
+    for cname, cls in fields.items():
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0;}")
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.c")
+        exe = os.path.join(d, "t")
+        open(src, "w").write("\n".join(lines))
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", src, "-o", exe], check=True)
+        res = dict(l.split() for l in subprocess.run([exe], capture_output=True, text=True).stdout.splitlines())
+    for cname, cls in fields.items():
+        assert int(res[cname]) == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert int(res[f"{cname}.{f}"]) == getattr(cls, f).offset, f"{cname}.{f}"
+
+
+def test_compress_rejects_bad_args(csa):
+    lib = csa.lib()
+    ok_args = [FAKE, FAKE, FAKE, None, FAKE, 0, 1, 1, 4, 128, 0, 0, 0, 0, None]
+
+    def call(**kw):
+        a = list(ok_args)
+        names = ["z", "c", "bias", "norm", "out", "odt", "batch", "nb", "m", "d", "ov", "fb", "zs", "os", "s"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return lib.csa_compress(*a)
+
+    assert call(z=None) == csa.binding.CSA_ERR_INVALID_ARG
+    assert "null" in csa.csa_last_error()
+    assert call(m=0) == csa.binding.CSA_ERR_INVALID_ARG
+    assert call(d=5000) == csa.binding.CSA_ERR_INVALID_ARG
+    assert call(ov=2) == csa.binding.CSA_ERR_INVALID_ARG
+    assert call(odt=7) == csa.binding.CSA_ERR_INVALID_ARG
+    assert call(batch=2) == csa.binding.CSA_ERR_INVALID_ARG  # zero batch strides with batch 2
+
+
+def test_index_score_rejects_bad_args(csa):
+    lib = csa.lib()
+    B = csa.binding
+    base = [FAKE, FAKE, FAKE, FAKE, B.CSA_BF16, 1, 1, 64, 128, 1000, None, 4, 0, 0, 0, 0, 1000, None]
+    a = list(base); a[7] = 32
+    assert lib.csa_index_score(*a) == B.CSA_ERR_UNSUPPORTED
+    a = list(base); a[0] = None
+    assert lib.csa_index_score(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(base); a[16] = 10  # ld_s < n
+    assert lib.csa_index_score(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(base); a[0] = FAKE + 2  # misaligned bf16 q
+    assert lib.csa_index_score(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(base); a[4] = B.CSA_F32; a[8] = 512
+    assert lib.csa_index_score(*a) == B.CSA_ERR_UNSUPPORTED
+
+
+def test_topk_rejects_bad_args_and_sizes_workspace(csa):
+    lib = csa.lib()
+    B = csa.binding
+    need = csa.csa_topk_workspace_size(1, 1, 250000, 512)
+    assert need > 0 and need % 256 == 0
+    assert csa.csa_topk_workspace_size(8, 1, 250000, 512) > need
+    assert csa.csa_topk_workspace_size(1, 1, 0, 0) == 0
+    args = [FAKE, 1, 1, 250000, 250000, 0, 512, FAKE, FAKE, FAKE, need, None]
+    a = list(args); a[6] = 4096
+    assert lib.csa_topk(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(args); a[10] = need - 1
+    assert lib.csa_topk(*a) == B.CSA_ERR_WORKSPACE
+    a = list(args); a[4] = 100
+    assert lib.csa_topk(*a) == B.CSA_ERR_INVALID_ARG
+
+
+def test_gather_rejects_bad_args(csa):
+    lib = csa.lib()
+    B = csa.binding
+    args = [FAKE, 100, FAKE, FAKE, 512, FAKE, 0, 128, 128, FAKE, FAKE, B.CSA_BF16, 1, 512, 0, 0, 0, None]
+    a = list(args); a[6] = 128  # head == w
+    assert lib.csa_gather(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(args); a[7] = 129  # len > w
+    assert lib.csa_gather(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(args); a[13] = 4  # 8-byte rows
+    assert lib.csa_gather(*a) == B.CSA_ERR_INVALID_ARG
+
+
+def test_attn_rejects_bad_args(csa):
+    lib = csa.lib()
+    B = csa.binding
+    ws = csa.csa_sparse_attn_workspace_size(1, 64, 512, 640)
+    assert ws >= 64 * 20 * 514 * 4
+    args = [FAKE, FAKE, FAKE, None, 0.04, FAKE, None, B.CSA_BF16, B.CSA_BF16, 1, 64, 512, 640, 0, 0, 0, FAKE, ws, None]
+    a = list(args); a[10] = 60
+    assert lib.csa_sparse_attn(*a) == B.CSA_ERR_UNSUPPORTED
+    a = list(args); a[17] = ws - 1
+    assert lib.csa_sparse_attn(*a) == B.CSA_ERR_WORKSPACE
+    a = list(args); a[2] = None
+    assert lib.csa_sparse_attn(*a) == B.CSA_ERR_INVALID_ARG
+
+
+def _desc(csa, **kw):
+    L = csa.LayerDesc()
+    L.batch, L.h, L.d, L.h_i, L.d_i, L.m, L.w, L.top_k = 1, 64, 512, 64, 128, 4, 128, 512
+    L.dtype = L.out_dtype = csa.CSA_BF16
+    L.comp_kv = L.idx_keys = L.swa = L.main_bias = L.idx_bias = FAKE
+    L.max_comp, L.n_comp, L.swa_head, L.swa_len = 1000, 999, 5, 128
+    L.scale = 0.044
+    for k, v in kw.items():
+        setattr(L, k, v)
+    return L
+
+
+def _io(csa, pos):
+    io = csa.StepIO()
+    for f, _ in io._fields_:
+        if f.endswith("stride_b"):
+            continue
+        setattr(io, f, FAKE if f != "pos" else pos)
+    return io
+
+
+def test_decode_step_validation_and_advance(csa):
+    B = csa.binding
+    lib = csa.lib()
+    L = _desc(csa)
+    need = csa.csa_decode_step_workspace_size(L)
+    assert need > csa.csa_topk_workspace_size(1, 1, 1000, 512)
+    io = _io(csa, pos=3999)  # completes a block while the cache is full-but-one: fine
+    L.n_comp = 1000          # now full
+    assert lib.csa_decode_step(ctypes.byref(L), ctypes.byref(io), FAKE, need, None) == B.CSA_ERR_INVALID_ARG
+    assert "full" in csa.csa_last_error()
+    L.n_comp = 999
+    assert lib.csa_decode_step(ctypes.byref(L), ctypes.byref(io), FAKE, need - 1, None) == B.CSA_ERR_WORKSPACE
+    L2 = _desc(csa, top_k=4096)
+    assert lib.csa_decode_step(ctypes.byref(L2), ctypes.byref(io), FAKE, need, None) == B.CSA_ERR_INVALID_ARG
+    # host-side counter advance: block completion and ring wrap
+    L3 = _desc(csa, n_comp=10, swa_head=127, swa_len=127)
+    csa.csa_layer_advance(L3, 42)   # 42 % 4 != 3
+    assert (L3.n_comp, L3.swa_head, L3.swa_len) == (10, 0, 128)
+    csa.csa_layer_advance(L3, 43)
+    assert (L3.n_comp, L3.swa_head, L3.swa_len) == (11, 1, 128)
+    L4 = _desc(csa, n_comp=1000)
+    with pytest.raises(csa.CsaError):
+        csa.csa_layer_advance(L4, 3)

@@ -1,0 +1,540 @@
+"""GPU parity: every C-ABI entry point against the float64 CPU oracle on the
+same seeded inputs.
+
+Tolerances (from the accuracy targets of this path):
+* float32 outputs: max|gpu - oracle| / max|oracle| <= 1e-4;
+* bfloat16 outputs: relative error <= 2e-2, and bf16-stored compressor
+  entries within 1 ulp of round-to-nearest-even(oracle);
+* indices / copies (top-k on identical scores, gather): bit-exact;
+* top-k against the oracle's own float64 scores: exact sets when the
+  k/(k+1) gap exceeds 1e-3 relative, else only near-threshold swaps.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import numfmt
+from tests.gpu_util import (DEV, as_f64, assert_bf16_close, assert_topk_gap_rule, dev_bf16, dev_f32,
+                            dev_store, host_bits, host_f64, rel_err)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def csa():
+    import compressed_sparse_attention_reduce_amd as pkg
+    pkg.lib()
+    return pkg
+
+
+def _g(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# ---------------------------------------------------------------------------
+# 1. compressor reduce
+# ---------------------------------------------------------------------------
+
+COMPRESS_CASES = [
+    # name, batch, n_blocks, m, d, overlap, first_block, out_bf16, norm, extra_rows
+    ("tiny_f32", 1, 1, 4, 128, 0, 0, False, False, 0),
+    ("main_bf16_batch8", 8, 1, 4, 512, 0, 0, True, False, 0),
+    ("prefill_ragged_tail", 2, 13, 4, 512, 0, 0, False, False, 3),
+    ("overlap_from_block0", 2, 7, 4, 128, 1, 0, False, False, 2),
+    ("overlap_streaming", 1, 3, 4, 512, 1, 5, True, False, 0),
+    ("kv_norm_bf16", 2, 4, 4, 512, 0, 0, True, True, 0),
+    ("ratio128", 1, 2, 128, 512, 0, 0, False, False, 0),
+    ("ratio1", 1, 5, 1, 64, 0, 0, False, False, 0),
+    ("odd_width", 3, 2, 4, 100, 0, 0, False, True, 0),
+    ("no_blocks", 1, 0, 4, 128, 0, 0, False, False, 2),
+]
+
+
+@pytest.mark.parametrize("case", COMPRESS_CASES, ids=[c[0] for c in COMPRESS_CASES])
+def test_compress(csa, case):
+    name, B, nb, m, d, ov, fb, out_bf16, norm, extra = case
+    g = _g(sum(map(ord, name)))
+    width = 2 * d if ov else d
+    lead = fb * m  # rows of earlier blocks (overlap streaming reads block fb-1)
+    rows = lead + nb * m + extra
+    Z = g.standard_normal((B, rows, width), dtype=np.float32)
+    C = g.standard_normal((B, rows, width), dtype=np.float32)
+    Bias = (g.standard_normal((m, width), dtype=np.float32) * 0.1).astype(np.float32)
+    nw = g.standard_normal(d, dtype=np.float32) if norm else None
+    dt = torch.bfloat16 if out_bf16 else torch.float32
+    out = torch.full((B, max(nb, 1), d), 7.0, dtype=dt, device=DEV)
+    z_d, c_d = dev_f32(Z), dev_f32(C)
+    csa.csa_compress(z_d[:, lead:], c_d[:, lead:], dev_f32(Bias), out, m=m, overlap=ov, first_block=fb,
+                     norm_w=None if nw is None else dev_f32(nw), n_blocks=nb)
+    torch.cuda.synchronize()
+    if nb == 0:
+        assert (out.float() == 7.0).all()
+        return
+    for b in range(B):
+        ref = oracle.compress(Z[b], C[b], Bias, m, overlap=bool(ov))[fb:fb + nb]
+        if nw is not None:
+            ref = oracle.kv_norm(ref, nw)
+        if out_bf16:
+            assert_bf16_close(host_bits(out[b]), ref)
+            assert rel_err(host_f64(out[b]), ref) <= 2e-2
+        else:
+            assert rel_err(host_f64(out[b]), ref) <= 1e-4
+
+
+# ---------------------------------------------------------------------------
+# 2. lightning-indexer score
+# ---------------------------------------------------------------------------
+
+def _score_inputs(g, B, t, n, bf16, h_i=64, d_i=128):
+    q = (g.standard_normal((B, t, h_i, d_i), dtype=np.float32) / np.float32(np.sqrt(d_i))).astype(np.float32)
+    w = g.standard_normal((B, t, h_i), dtype=np.float32)
+    K = g.standard_normal((B, n, d_i), dtype=np.float32)
+    if bf16:
+        q, K = synth.to_bf16_bits(q), synth.to_bf16_bits(K)
+    return q, w, K
+
+
+SCORE_CASES = [
+    # name, B, t, n, bf16, causal
+    ("bf16_ragged_tail", 2, 1, 1000, True, False),
+    ("bf16_batch8", 8, 1, 4096, True, False),
+    ("bf16_one_key", 1, 1, 1, True, False),
+    ("bf16_31_keys", 1, 1, 31, True, False),
+    ("bf16_33_keys", 3, 1, 33, True, False),
+    ("bf16_causal_multiquery", 1, 5, 600, True, True),
+    ("f32_tiny", 1, 1, 256, False, False),
+    ("f32_causal", 2, 3, 77, False, True),
+]
+
+
+@pytest.mark.parametrize("case", SCORE_CASES, ids=[c[0] for c in SCORE_CASES])
+def test_index_score(csa, case):
+    name, B, t, n, bf16, causal = case
+    g = _g(len(name) * 31 + n)
+    q, w, K = _score_inputs(g, B, t, n, bf16)
+    ld = n + 5
+    scores = torch.full((B, t, ld), 123.0, device=DEV)
+    pos = None
+    pos_np = None
+    if causal:
+        pos_np = (4 * n - 4 * t - 10 + 3 * np.arange(B * t)).astype(np.int32).reshape(B, t)
+        pos = torch.from_numpy(pos_np).to(DEV)
+    csa.csa_index_score(dev_store(q), dev_f32(w), dev_store(K), scores, q_pos=pos, ratio=4)
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy().astype(np.float64)
+    assert (got[:, :, n:] == 123.0).all(), "wrote past n"
+    for b in range(B):
+        ref = oracle.index_score(as_f64(q[b]), w[b], as_f64(K[b]),
+                                 q_pos=None if pos_np is None else pos_np[b], ratio=4)
+        fin = np.isfinite(ref)
+        assert (np.isfinite(got[b, :, :n]) == fin).all(), "mask differs"
+        assert rel_err(got[b, :, :n][fin], ref[fin]) <= 1e-4
+
+
+def test_index_score_full_size_sampled(csa):
+    """n_comp = 250000 (1M context) in the bench's launch configuration; the
+    oracle recomputes a sample of 4096 keys (plus the first and last tiles)."""
+    shape = synth.SHAPES["ctx1m"]
+    x = synth.make_decode_inputs_torch(shape, seed=None, device=DEV, layers=1)[0]
+    n = shape.n_comp
+    scores = torch.empty(1, 1, n, device=DEV)
+    csa.csa_index_score(x["q_idx"][:, None], x["w_idx"][:, None], x["idx_keys"], scores)
+    torch.cuda.synchronize()
+    g = _g(44)
+    sample = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n), g.integers(0, n, 4096)]))
+    Ks = host_f64(x["idx_keys"][0, torch.from_numpy(sample).to(DEV)])
+    ref = oracle.index_score(host_f64(x["q_idx"][0])[None], host_f64(x["w_idx"][0])[None], Ks)[0]
+    got = scores[0, 0].cpu().numpy().astype(np.float64)[sample]
+    assert rel_err(got, ref) <= 1e-4
+
+
+# ---------------------------------------------------------------------------
+# 3. top-k
+# ---------------------------------------------------------------------------
+
+def _run_topk(csa, scores_np, k, n=None):
+    B, t, ld = scores_np.shape
+    n = ld if n is None else n
+    s = torch.from_numpy(np.ascontiguousarray(scores_np, dtype=np.float32)).to(DEV)
+    idx = torch.full((B, t, k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((B, t), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(csa.csa_topk_workspace_size(B, t, n, k), 16), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xAB)  # the workspace needs no initialisation
+    csa.csa_topk(s, k, idx, cnt, ws, n=n)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), cnt.cpu().numpy()
+
+
+def _check_topk(scores_np, k, idx, cnt, n=None):
+    B, t, ld = scores_np.shape
+    n = ld if n is None else n
+    for b in range(B):
+        ri, rc = oracle.topk(scores_np[b, :, :n].astype(np.float64), k)
+        np.testing.assert_array_equal(idx[b], ri)
+        np.testing.assert_array_equal(cnt[b], rc)
+
+
+TOPK_CASES = [
+    # name, B, t, n, k, kind
+    ("normal_1m_ctx", 1, 1, 250000, 512, "normal"),
+    ("normal_8k_batch8", 8, 1, 2048, 512, "normal"),
+    ("fewer_than_k", 2, 1, 300, 512, "normal"),
+    ("k1", 1, 1, 5000, 1, "normal"),
+    ("kmax_2048", 1, 1, 100000, 2048, "normal"),
+    ("integer_ties", 1, 1, 20000, 512, "ties"),
+    ("all_equal_overflow", 1, 1, 50000, 512, "equal"),
+    ("signed_zero_and_masked", 2, 1, 5000, 512, "zeros"),
+    ("causal_rows", 1, 3, 65536, 512, "causal"),
+    ("exactly_k", 1, 1, 512, 512, "normal"),
+    ("heavy_tail_cands", 1, 1, 200000, 512, "lowres"),
+]
+
+
+def _topk_scores(kind, B, t, n, g):
+    if kind == "normal":
+        return g.standard_normal((B, t, n), dtype=np.float32) * 5
+    if kind == "ties":
+        return g.integers(-3, 4, size=(B, t, n)).astype(np.float32)
+    if kind == "equal":
+        return np.full((B, t, n), 2.5, dtype=np.float32)
+    if kind == "zeros":
+        s = g.standard_normal((B, t, n), dtype=np.float32)
+        s[:, :, ::3] = 0.0
+        s[:, :, 1::7] = -0.0
+        s[s < -0.5] = -np.inf
+        s[:, :, :100] = np.where(g.random((B, t, 100)) < 0.5, 0.0, -0.0)
+        return s
+    if kind == "causal":
+        s = g.standard_normal((B, t, n), dtype=np.float32)
+        for tt in range(t):
+            s[:, tt, n - 700 + 200 * tt:] = -np.inf
+        return s
+    if kind == "lowres":  # few distinct values near the top: large threshold bin
+        return np.round(g.standard_normal((B, t, n)) * 2).astype(np.float32) + g.integers(0, 2, (B, t, n)).astype(np.float32) * np.float32(1e-3)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("case", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
+def test_topk(csa, case):
+    name, B, t, n, k, kind = case
+    s = _topk_scores(kind, B, t, n, _g(n + k))
+    idx, cnt = _run_topk(csa, s, k)
+    _check_topk(s, k, idx, cnt)
+
+
+def test_topk_strided_rows_and_empty(csa):
+    g = _g(5)
+    s = g.standard_normal((3, 2, 1500), dtype=np.float32)
+    idx, cnt = _run_topk(csa, s, 64, n=1200)  # ld 1500, only 1200 columns valid
+    _check_topk(s, 64, idx, cnt, n=1200)
+    idx, cnt = _run_topk(csa, np.zeros((1, 1, 4), np.float32), 8, n=0)
+    assert (idx == -1).all() and (cnt == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# 4. gather
+# ---------------------------------------------------------------------------
+
+GATHER_CASES = [
+    # name, B, n_comp, k, count, W, head, len, d, bf16
+    ("ctx1m_wrap", 1, 250000, 512, 512, 128, 64, 128, 512, True),
+    ("batch_partial_count", 4, 3000, 512, 200, 128, 0, 128, 512, True),
+    ("empty_cache", 2, 0, 512, 0, 128, 17, 40, 512, True),
+    ("short_window", 1, 100, 64, 64, 128, 30, 30, 128, False),
+    ("tiny_f32_wrap", 1, 256, 64, 64, 128, 0, 128, 128, False),
+]
+
+
+@pytest.mark.parametrize("case", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_gather(csa, case):
+    name, B, n_comp, k, count, W, head, ln, d, bf16 = case
+    g = _g(n_comp + k + d)
+    torch.manual_seed(n_comp + k + d)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    comp = torch.randn(B, max(n_comp, 1), d, device=DEV).to(dt)
+    swa = torch.randn(B, W, d, device=DEV).to(dt)
+    idx_np = np.full((B, k), -1, np.int32)
+    for b in range(B):
+        if count:
+            idx_np[b, :count] = g.choice(n_comp, size=count, replace=False)
+    cnt_np = np.full(B, count, np.int32)
+    buf = torch.zeros(B, k + W, d, dtype=dt, device=DEV)
+    nv = torch.full((B,), -1, dtype=torch.int32, device=DEV)
+    csa.csa_gather(comp, torch.from_numpy(idx_np).to(DEV), torch.from_numpy(cnt_np).to(DEV), swa, head, ln,
+                   buf, nv, n_comp=n_comp)
+    torch.cuda.synchronize()
+    rawc = comp.view(torch.int16 if bf16 else torch.int32).cpu().numpy()
+    raws = swa.view(torch.int16 if bf16 else torch.int32).cpu().numpy()
+    rawb = buf.view(torch.int16 if bf16 else torch.int32).cpu().numpy()
+    for b in range(B):
+        rows, n_valid = oracle.gather(rawc[b], idx_np[b], count, raws[b], head, ln)
+        assert int(nv[b]) == n_valid
+        np.testing.assert_array_equal(rawb[b, :n_valid], rows)
+        assert (rawb[b, n_valid:] == 0).all(), "rows past n_valid were written"
+
+
+# ---------------------------------------------------------------------------
+# 5. sparse attention
+# ---------------------------------------------------------------------------
+
+ATTN_CASES = [
+    # name, B, H, D, n_max, n_valid list, sink, bf16, out_bf16
+    ("gather_buf_640", 1, 64, 512, 640, [640], True, True, True),
+    ("ragged_37", 1, 64, 512, 640, [37], True, True, True),
+    ("batch_mixed", 4, 64, 512, 640, [640, 1, 333, 129], True, True, False),
+    ("no_sink", 1, 32, 256, 96, [96], False, True, True),
+    ("empty_with_sink", 1, 16, 128, 64, [0], True, True, False),
+    ("empty_no_sink", 1, 16, 128, 64, [0], False, True, False),
+    ("f32_tiny", 1, 16, 128, 192, [192], True, False, False),
+    ("f32_ragged", 2, 16, 128, 192, [5, 0], True, False, False),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_sparse_attn(csa, case):
+    name, B, H, D, n_max, nvs, use_sink, bf16, out_bf16 = case
+    g = _g(H * D + n_max)
+    q = g.standard_normal((B, H, D), dtype=np.float32)
+    kv = g.standard_normal((B, n_max, D), dtype=np.float32)
+    if bf16:
+        q, kv = synth.to_bf16_bits(q), synth.to_bf16_bits(kv)
+    sink = g.standard_normal(H, dtype=np.float32) if use_sink else None
+    out = torch.full((B, H, D), 9.0, dtype=torch.bfloat16 if out_bf16 else torch.float32, device=DEV)
+    lse = torch.empty(B, H, device=DEV)
+    nv = torch.tensor(nvs, dtype=torch.int32, device=DEV)
+    ws = torch.empty(csa.csa_sparse_attn_workspace_size(B, H, D, n_max), dtype=torch.uint8, device=DEV)
+    scale = 1.0 / np.sqrt(D)
+    csa.csa_sparse_attn(dev_store(q), dev_store(kv), nv, None if sink is None else dev_f32(sink), scale, out,
+                        lse, ws)
+    torch.cuda.synchronize()
+    tol = 2e-2 if (bf16 or out_bf16) else 1e-4
+    for b in range(B):
+        ro, rl = oracle.sparse_attn(as_f64(q[b]), as_f64(kv[b])[: nvs[b]], sink, scale)
+        go = host_f64(out[b])
+        if nvs[b] == 0:
+            assert (go == 0).all()
+        else:
+            assert rel_err(go, ro) <= tol, name
+        gl = lse[b].cpu().numpy().astype(np.float64)
+        if np.isinf(rl).all():
+            assert np.isinf(gl).all() and (gl < 0).all()
+        else:
+            assert np.abs(gl - rl).max() <= (1e-2 if bf16 else 1e-5)
+
+
+# ---------------------------------------------------------------------------
+# 6. fused decode step
+# ---------------------------------------------------------------------------
+
+def _run_step(csa, x, shape, with_lse=True):
+    """Upload one decode step's inputs, run csa_decode_step, return device state."""
+    B, D, K, W = shape.batch, shape.d, shape.top_k, shape.w
+    dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    st = {k: dev_store(x[k]) for k in ("comp_kv", "idx_keys", "swa", "q", "q_idx", "kv_new")}
+    for k in ("main_bias", "idx_bias", "sink", "w_idx", "z_main", "c_main", "z_idx", "c_idx"):
+        st[k] = dev_f32(x[k])
+    L = csa.make_layer_desc(comp_kv=st["comp_kv"], idx_keys=st["idx_keys"], swa=st["swa"],
+                            main_bias=st["main_bias"], idx_bias=st["idx_bias"], sink=st["sink"],
+                            n_comp=x["n_comp"], swa_head=x["swa_head"], swa_len=x["swa_len"], h=shape.h,
+                            h_i=shape.h_i, m=shape.m, top_k=K, overlap=int(shape.overlap))
+    outs = dict(scores=torch.full((B, x["comp_kv"].shape[1]), 55.0, device=DEV),
+                topk_idx=torch.empty(B, K, dtype=torch.int32, device=DEV),
+                topk_count=torch.empty(B, dtype=torch.int32, device=DEV),
+                gather_buf=torch.zeros(B, K + W, D, dtype=dt, device=DEV),
+                n_valid=torch.empty(B, dtype=torch.int32, device=DEV),
+                out=torch.empty(B, shape.h, D, dtype=dt, device=DEV),
+                lse=torch.empty(B, shape.h, device=DEV) if with_lse else None)
+    io = csa.make_step_io(pos=x["pos"], q=st["q"], q_idx=st["q_idx"], w_idx=st["w_idx"], kv_new=st["kv_new"],
+                          z_main=st["z_main"], c_main=st["c_main"], z_idx=st["z_idx"], c_idx=st["c_idx"],
+                          **outs)
+    ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+    csa.csa_decode_step(L, io, ws)
+    torch.cuda.synchronize()
+    return st, outs, L
+
+
+def _check_step(x, shape, st, outs, b):
+    """Compare one sequence of a decode step with the oracle, stage by stage."""
+    bf = shape.dtype == "bf16"
+    m, K = shape.m, shape.top_k
+    N0 = x["n_comp"]
+    completes = x["pos"] % m == m - 1
+    N = N0 + int(completes)
+    # a. SWA append
+    assert np.array_equal(host_f64(st["swa"][b, x["swa_head"]]), as_f64(x["kv_new"][b]))
+    # b. compressed entries
+    comp = host_f64(st["comp_kv"][b, :N])
+    keys = host_f64(st["idx_keys"][b, :N])
+    if completes:
+        ym = oracle.compress(x["z_main"][b], x["c_main"][b], x["main_bias"], m, overlap=shape.overlap)[-1]
+        yi = oracle.compress(x["z_idx"][b], x["c_idx"][b], x["idx_bias"], m, overlap=shape.overlap)[-1]
+        if bf:
+            assert_bf16_close(host_bits(st["comp_kv"][b, N0]), ym)
+            assert_bf16_close(host_bits(st["idx_keys"][b, N0]), yi)
+        else:
+            assert rel_err(comp[N0], ym) <= 1e-4 and rel_err(keys[N0], yi) <= 1e-4
+    np.testing.assert_array_equal(comp[:N0], as_f64(x["comp_kv"][b, :N0]))
+    # c. scores (oracle on the cache as the GPU holds it)
+    ref_s = oracle.index_score(as_f64(x["q_idx"][b])[None], x["w_idx"][b][None], keys)[0]
+    got_s = outs["scores"][b, :N].cpu().numpy().astype(np.float64)
+    assert rel_err(got_s, ref_s) <= 1e-4
+    # d. top-k: bit-exact on the GPU's own scores, gap rule against the oracle's
+    gi = outs["topk_idx"][b].cpu().numpy()
+    gc = int(outs["topk_count"][b])
+    oi, oc = oracle.topk(got_s[None], K)
+    np.testing.assert_array_equal(gi, oi[0])
+    assert gc == int(oc[0])
+    assert_topk_gap_rule(gi, gc, ref_s, K)
+    # e. gather (bit-exact, GPU selection)
+    swa_rows = host_f64(st["swa"][b])
+    head = (x["swa_head"] + 1) % shape.w
+    ln = min(x["swa_len"] + 1, shape.w)
+    rows, n_valid = oracle.gather(comp, gi, gc, swa_rows, head, ln)
+    assert int(outs["n_valid"][b]) == n_valid
+    np.testing.assert_array_equal(host_f64(outs["gather_buf"][b, :n_valid]), rows)
+    # f. attention over the gathered rows
+    ro, rl = oracle.sparse_attn(as_f64(x["q"][b]), rows, x["sink"], 1.0 / np.sqrt(shape.d))
+    assert rel_err(host_f64(outs["out"][b]), ro) <= (2e-2 if bf else 1e-4)
+    if outs["lse"] is not None:
+        assert np.abs(outs["lse"][b].cpu().numpy() - rl).max() <= (1e-2 if bf else 1e-5)
+
+
+STEP_CASES = [
+    # name, shape, seed, cache capacity (None = n_comp)
+    ("tiny_f32", synth.SHAPES["tiny"], 1001, None),
+    ("ctx8k_bf16", synth.SHAPES["ctx8k"], 2001, None),
+    ("no_block_completion", synth.with_(synth.SHAPES["ctx8k"], ctx=8190, n_comp=2047), 2002, None),
+    ("first_token", synth.with_(synth.SHAPES["ctx8k"], ctx=1, n_comp=0, top_k=64), 2003, 8),
+    ("first_block", synth.with_(synth.SHAPES["ctx8k"], ctx=4, n_comp=1, top_k=64), 2004, None),
+    ("overlap_bf16", synth.with_(synth.SHAPES["ctx8k"], ctx=4000, n_comp=1000, overlap=True), 2005, None),
+    ("k_covers_all", synth.with_(synth.SHAPES["ctx8k"], ctx=800, n_comp=200), 2006, 256),
+    ("tiny_f32_batch3", synth.with_(synth.SHAPES["tiny"], batch=3), 1002, None),
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=[c[0] for c in STEP_CASES])
+def test_decode_step(csa, case):
+    name, shape, seed, cap = case
+    x = synth.make_decode_inputs(shape, seed, max_comp=cap)
+    st, outs, _ = _run_step(csa, x, shape)
+    for b in range(shape.batch):
+        _check_step(x, shape, st, outs, b)
+
+
+def test_decode_step_batch128k_full_size(csa):
+    shape = synth.SHAPES["batch128k"]
+    x = synth.make_decode_inputs(shape, 3000)
+    st, outs, _ = _run_step(csa, x, shape, with_lse=False)
+    for b in range(shape.batch):
+        _check_step(x, shape, st, outs, b)
+
+
+def test_decode_step_ctx1m_full_size(csa):
+    """One layer of the 1M-context workload (n_comp 250,000, SWA wrap) through
+    csa_decode_step, as the benchmark runs it; the oracle scores every key."""
+    shape = synth.SHAPES["ctx1m"]
+    x = synth.make_decode_inputs_torch(shape, seed=None, device=DEV, layers=1)[0]
+    B, K, W, D = shape.batch, shape.top_k, shape.w, shape.d
+    pristine_keys = x["idx_keys"][0, : x["n_comp"]].clone()
+    L = csa.make_layer_desc(comp_kv=x["comp_kv"], idx_keys=x["idx_keys"], swa=x["swa"],
+                            main_bias=x["main_bias"], idx_bias=x["idx_bias"], sink=x["sink"],
+                            n_comp=x["n_comp"], swa_head=x["swa_head"], swa_len=x["swa_len"], h=shape.h,
+                            h_i=shape.h_i, top_k=K)
+    outs = dict(scores=torch.empty(B, shape.max_comp, device=DEV),
+                topk_idx=torch.empty(B, K, dtype=torch.int32, device=DEV),
+                topk_count=torch.empty(B, dtype=torch.int32, device=DEV),
+                gather_buf=torch.zeros(B, K + W, D, dtype=torch.bfloat16, device=DEV),
+                n_valid=torch.empty(B, dtype=torch.int32, device=DEV),
+                out=torch.empty(B, shape.h, D, dtype=torch.bfloat16, device=DEV),
+                lse=torch.empty(B, shape.h, device=DEV))
+    io = csa.make_step_io(pos=x["pos"], q=x["q"], q_idx=x["q_idx"], w_idx=x["w_idx"], kv_new=x["kv_new"],
+                          z_main=x["z_main"], c_main=x["c_main"], z_idx=x["z_idx"], c_idx=x["c_idx"], **outs)
+    ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+    csa.csa_decode_step(L, io, ws)
+    torch.cuda.synchronize()
+    N = shape.n_comp
+    assert torch.equal(x["idx_keys"][0, : N - 1], pristine_keys[: N - 1])
+    yi = oracle.compress(x["z_idx"][0].cpu().numpy(), x["c_idx"][0].cpu().numpy(),
+                         x["idx_bias"].cpu().numpy(), 4)[-1]
+    assert_bf16_close(host_bits(x["idx_keys"][0, N - 1]), yi)
+    keys = host_f64(x["idx_keys"][0, :N])
+    ref_s = oracle.index_score(host_f64(x["q_idx"][0])[None], host_f64(x["w_idx"][0])[None], keys)[0]
+    got_s = outs["scores"][0].cpu().numpy().astype(np.float64)
+    assert rel_err(got_s, ref_s) <= 1e-4
+    gi = outs["topk_idx"][0].cpu().numpy()
+    oi, oc = oracle.topk(got_s[None], K)
+    np.testing.assert_array_equal(gi, oi[0])
+    assert_topk_gap_rule(gi, int(outs["topk_count"][0]), ref_s, K)
+    sel = host_f64(x["comp_kv"][0, torch.from_numpy(gi).to(DEV).long()])
+    swa_rows = host_f64(x["swa"][0])
+    head = (x["swa_head"] + 1) % W
+    win = np.stack([swa_rows[(head - W + j) % W] for j in range(W)])
+    rows = np.concatenate([sel, win])
+    assert int(outs["n_valid"][0]) == K + W
+    np.testing.assert_array_equal(host_f64(outs["gather_buf"][0]), rows)
+    ro, rl = oracle.sparse_attn(host_f64(x["q"][0]), rows, host_f64(x["sink"]), 1.0 / np.sqrt(D))
+    assert rel_err(host_f64(outs["out"][0]), ro) <= 2e-2
+    assert np.abs(outs["lse"][0].cpu().numpy() - rl).max() <= 1e-2
+
+
+def test_decode_steps_in_sequence(csa):
+    """Nine consecutive steps (two block completions, ring wrap) with the host
+    counters advanced by csa_layer_advance; each step checked against the
+    oracle's evolving state."""
+    shape = synth.with_(synth.SHAPES["ctx8k"], ctx=600, n_comp=150, top_k=64, w=8)
+    x = synth.make_decode_inputs(shape, 4001, max_comp=200)
+    g = _g(4002)
+    dt = torch.bfloat16
+    comp = dev_bf16(x["comp_kv"]); keys = dev_bf16(x["idx_keys"]); swa = dev_bf16(x["swa"])
+    mb, ib, sink = dev_f32(x["main_bias"]), dev_f32(x["idx_bias"]), dev_f32(x["sink"])
+    L = csa.make_layer_desc(comp_kv=comp, idx_keys=keys, swa=swa, main_bias=mb, idx_bias=ib, sink=sink,
+                            n_comp=x["n_comp"], swa_head=x["swa_head"], swa_len=x["swa_len"], h=64, h_i=64,
+                            top_k=64)
+    f = numfmt.bf16_bits_to_f64
+    ost = oracle.LayerState(comp_kv=f(x["comp_kv"][0]), idx_keys=f(x["idx_keys"][0]), n_comp=x["n_comp"],
+                            swa=oracle.SwaRing(f(x["swa"][0]), x["swa_head"], x["swa_len"]),
+                            main_bias=x["main_bias"], idx_bias=x["idx_bias"], sink=x["sink"],
+                            round_cache=numfmt.bf16_round_f64)
+    ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+    for pos in range(x["pos"], x["pos"] + 9):
+        q = synth.to_bf16_bits(g.standard_normal((1, 64, 512), dtype=np.float32))
+        qi = synth.to_bf16_bits((g.standard_normal((1, 64, 128), dtype=np.float32) / np.float32(np.sqrt(128))))
+        wi = g.standard_normal((1, 64), dtype=np.float32)
+        kvn = synth.to_bf16_bits(g.standard_normal((1, 512), dtype=np.float32))
+        zm, cm = g.standard_normal((2, 1, 4, 512), dtype=np.float32)
+        zi, ci = g.standard_normal((2, 1, 4, 128), dtype=np.float32)
+        outs = dict(scores=torch.empty(1, 200, device=DEV), topk_idx=torch.empty(1, 64, dtype=torch.int32, device=DEV),
+                    topk_count=torch.empty(1, dtype=torch.int32, device=DEV),
+                    gather_buf=torch.zeros(1, 72, 512, dtype=dt, device=DEV),
+                    n_valid=torch.empty(1, dtype=torch.int32, device=DEV),
+                    out=torch.empty(1, 64, 512, dtype=dt, device=DEV))
+        io = csa.make_step_io(pos=pos, q=dev_bf16(q), q_idx=dev_bf16(qi), w_idx=dev_f32(wi), kv_new=dev_bf16(kvn),
+                              z_main=dev_f32(zm), c_main=dev_f32(cm), z_idx=dev_f32(zi), c_idx=dev_f32(ci), **outs)
+        csa.csa_decode_step(L, io, ws)
+        csa.csa_layer_advance(L, pos)
+        torch.cuda.synchronize()
+        completes = pos % 4 == 3
+        n0 = ost.n_comp
+        oracle.decode_step(ost, q=f(q[0]), q_idx=f(qi[0]), w_idx=wi[0], kv_new=f(kvn[0]), pos=pos, top_k=64,
+                           z_main=zm[0], c_main=cm[0], z_idx=zi[0], c_idx=ci[0], scale=1 / np.sqrt(512))
+        assert (L.n_comp, L.swa_head, L.swa_len) == (ost.n_comp, ost.swa.head, ost.swa.length)
+        N = ost.n_comp
+        if completes:  # new entries within one bf16 ulp of the oracle's, then adopt the GPU's bits
+            assert_bf16_close(host_bits(comp[0, n0]), oracle.compress(zm[0], cm[0], x["main_bias"], 4)[0])
+            assert_bf16_close(host_bits(keys[0, n0]), oracle.compress(zi[0], ci[0], x["idx_bias"], 4)[0])
+        ost.comp_kv[:N] = host_f64(comp[0, :N])
+        ost.idx_keys[:N] = host_f64(keys[0, :N])
+        ref_s = oracle.index_score(f(qi[0])[None], wi[0][None], ost.idx_keys[:N])[0]
+        got_s = outs["scores"][0, :N].cpu().numpy().astype(np.float64)
+        assert rel_err(got_s, ref_s) <= 1e-4
+        gi, gc = outs["topk_idx"][0].cpu().numpy(), int(outs["topk_count"][0])
+        np.testing.assert_array_equal(gi, oracle.topk(got_s[None], 64)[0][0])
+        assert_topk_gap_rule(gi, gc, ref_s, 64)
+        rows, n_valid = oracle.gather(ost.comp_kv[:N], gi, gc, ost.swa.rows, ost.swa.head, ost.swa.length)
+        assert int(outs["n_valid"][0]) == n_valid
+        np.testing.assert_array_equal(host_f64(outs["gather_buf"][0, :n_valid]), rows)
+        ro, _ = oracle.sparse_attn(f(q[0]), rows, x["sink"], 1 / np.sqrt(512))
+        assert rel_err(host_f64(outs["out"][0]), ro) <= 2e-2
