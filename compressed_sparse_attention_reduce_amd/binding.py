@@ -227,7 +227,8 @@ def make_layer_desc(*, comp_kv, idx_keys, swa, main_bias, idx_bias, sink, n_comp
                     overlap: int = 0, out_dtype=None, scale: Optional[float] = None,
                     main_norm=None, idx_norm=None) -> LayerDesc:
     """Fill a LayerDesc from cache tensors: comp_kv [B, max_comp, d], idx_keys
-    [B, max_comp, d_i], swa [B, W, d]."""
+    [B, max_comp, d_i], swa [B, W, d].  The returned struct keeps references to
+    every tensor it points at."""
     B, max_comp, d = comp_kv.shape
     L = LayerDesc()
     L.batch, L.h, L.d, L.h_i, L.d_i = B, h, d, h_i, idx_keys.shape[2]
@@ -243,6 +244,8 @@ def make_layer_desc(*, comp_kv, idx_keys, swa, main_bias, idx_bias, sink, n_comp
     L.sink = _ptr(sink)
     L.scale = (1.0 / d ** 0.5) if scale is None else scale
     L.n_comp, L.swa_head, L.swa_len = n_comp, swa_head, swa_len
+    # the struct holds raw device pointers: keep the tensors alive with it
+    L._keep = (comp_kv, idx_keys, swa, main_bias, idx_bias, sink, main_norm, idx_norm)
     return L
 
 
@@ -264,4 +267,7 @@ def make_step_io(*, pos: int, q, q_idx, w_idx, kv_new, z_main, c_main, z_idx, c_
     io.n_valid = n_valid.data_ptr()
     io.out, io.out_stride_b = out.data_ptr(), out.stride(0)
     io.lse = _ptr(lse)
+    # the struct holds raw device pointers: keep the tensors alive with it
+    io._keep = (q, q_idx, w_idx, kv_new, z_main, c_main, z_idx, c_idx, scores, topk_idx, topk_count,
+                gather_buf, n_valid, out, lse)
     return io

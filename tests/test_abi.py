@@ -190,3 +190,36 @@ def test_decode_step_validation_and_advance(csa):
     L4 = _desc(csa, n_comp=1000)
     with pytest.raises(csa.CsaError):
         csa.csa_layer_advance(L4, 3)
+
+
+def test_descriptors_keep_their_tensors_alive(csa):
+    """make_layer_desc / make_step_io store raw pointers; the returned structs
+    must keep the tensors alive, or temporaries passed in would be freed and
+    their memory reused before the step runs."""
+    import gc
+    import weakref
+
+    import torch
+
+    bias = torch.zeros(4, 128)
+    ref = weakref.ref(bias)
+    L = csa.make_layer_desc(comp_kv=torch.zeros(1, 8, 128), idx_keys=torch.zeros(1, 8, 128),
+                            swa=torch.zeros(1, 16, 128), main_bias=torch.zeros(4, 128), idx_bias=bias,
+                            sink=torch.zeros(16), n_comp=3, swa_head=0, swa_len=3, h=16, h_i=64, top_k=4)
+    del bias
+    gc.collect()
+    assert ref() is not None and L.idx_bias == ref().data_ptr()
+    q = torch.zeros(1, 16, 128)
+    rq = weakref.ref(q)
+    io = csa.make_step_io(pos=3, q=q, q_idx=torch.zeros(1, 64, 128), w_idx=torch.zeros(1, 64),
+                          kv_new=torch.zeros(1, 128), z_main=torch.zeros(1, 4, 128), c_main=torch.zeros(1, 4, 128),
+                          z_idx=torch.zeros(1, 4, 128), c_idx=torch.zeros(1, 4, 128), scores=torch.zeros(1, 8),
+                          topk_idx=torch.zeros(1, 4, dtype=torch.int32), topk_count=torch.zeros(1, dtype=torch.int32),
+                          gather_buf=torch.zeros(1, 20, 128), n_valid=torch.zeros(1, dtype=torch.int32),
+                          out=torch.zeros(1, 16, 128))
+    del q
+    gc.collect()
+    assert rq() is not None and io.q == rq().data_ptr()
+    del L, io
+    gc.collect()
+    assert ref() is None and rq() is None
