@@ -7,17 +7,20 @@
 // K = V (page 1, PERFORMANCE_AUDIT.md P4; MQA, one KV head for all heads).
 //
 // bf16 path, split-K ("flash decoding") in two launches:
-//   k_attn_partial_bf16 — grid (row split of 32, group of 16 heads, sequence).
-//     The 32 x d key/value tile is loaded once into LDS (coalesced 16 B
-//     lanes; rows past n_valid are zero-filled).  S = q K^T on
-//     v_mfma_f32_16x16x32_bf16 with the d contraction split over the 4 waves,
-//     a local softmax (max m, sum l of the bf16-rounded weights), then
-//     O = P V on the same MFMA with V read from LDS column-wise.  Partial
+//   k_attn_partial_bf16 — grid (row split, group of 16 heads, sequence).  The
+//     split's rows are loaded once into LDS with 16-byte lanes (zero-filled
+//     past n_valid).  In gather mode (the fused decode step) the rows come
+//     straight from the compressed cache through the top-k indices and from the
+//     SWA ring, and the head-group-0 workgroups also write them to gather_buf,
+//     so the gather costs no launch and no second pass.  Each wave computes
+//     S = q K^T for 16 rows on v_mfma_f32_16x16x32_bf16 with the query staged
+//     in LDS; the split's softmax statistics are combined across waves in LDS;
+//     O = P V runs on the same MFMA with V read column-wise from LDS.  Partial
 //     (m, l, O) go to the workspace in float32.
-//   k_attn_merge — per (head, sequence): M = max(max m_s, sink), rescale and
-//     add the partials, add exp(sink - M) to the denominator once, divide.
+//   k_attn_merge — one workgroup per (head, sequence): M = max(max_s m_s, sink),
+//     rescale and add the partials, add exp(sink - M) once, divide.
 // float32 path (small correctness workloads): one workgroup per (head,
-// sequence) computing the whole softmax in float32 on the vector ALUs.
+// sequence), the whole softmax in float32 on the vector ALUs.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,116 +29,200 @@ namespace csa {
 namespace {
 
 constexpr int kAttnThreads = 256;
-constexpr int kSplitRows = 32;
 constexpr int kHeadGroup = 16;
-constexpr int kMaxD = 512;
 
-inline int attn_splits(int n_max) { return n_max > 0 ? (n_max + kSplitRows - 1) / kSplitRows : 1; }
+inline int attn_rows_per_split(int n_max) { return n_max > 256 ? 64 : 32; }
+inline int attn_splits(int n_max) {
+    const int r = attn_rows_per_split(n_max);
+    return n_max > 0 ? (n_max + r - 1) / r : 1;
+}
 
-__global__ __launch_bounds__(kAttnThreads) void k_attn_partial_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int* __restrict__ n_valid,
-    float scale, int h, int d, int n_max, long long q_stride_b, long long kv_stride_b,
-    float* __restrict__ ws_o, float* __restrict__ ws_ml, int n_splits) {
-    __shared__ __attribute__((aligned(16))) uint16_t tile[kSplitRows * (kMaxD + 8)];
-    __shared__ __attribute__((aligned(16))) uint16_t pl[kHeadGroup * (kSplitRows + 8)];
-    __shared__ float spart[4][kHeadGroup][kSplitRows];
+template <int R>
+__global__ __launch_bounds__(kAttnThreads) void k_attn_partial_bf16(AttnArgs a, int n_splits) {
+    constexpr int kNt = R / 16;       // 16-row tiles, one per wave (R = 64) or two waves idle (R = 32)
+    constexpr int kPPitch = R + 8;
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    uint16_t* tile = smem;                                   // [R][d + 8]
+    uint16_t* qs = tile + R * (a.d + 8);                      // [16][d + 8]
+    uint16_t* pl = qs + kHeadGroup * (a.d + 8);               // [16][R + 8]
+    __shared__ float wmax[4][kHeadGroup];
+    __shared__ float wsum[4][kHeadGroup];
 
+    __shared__ const uint16_t* rowptr[R];
     const int split = blockIdx.x;
     const int hg = blockIdx.y;
     const int b = blockIdx.z;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
+    const int d = a.d;
     const int pitch = d + 8;
-    int nv = n_valid[b];
-    nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
-    const int r0 = split * kSplitRows;
-    const int rows = max(0, min(kSplitRows, nv - r0));
-    const long long ml_base = (static_cast<long long>(b) * h + hg * kHeadGroup) * n_splits + split;
+    const int r0 = split * R;
+    const int cpr = d / 8;  // 16-byte chunks per row
 
-    if (rows == 0) {  // nothing to attend in this split: mark it empty
+    // 0. the query group's loads go first (independent of everything below)
+    const uint16_t* qg = a.q + b * a.q_stride_b + static_cast<long long>(hg * kHeadGroup) * d;
+    constexpr int kQBatch = kHeadGroup * 64 / kAttnThreads;  // pieces per thread at d = 512
+    uint4 qv[kQBatch];
+#pragma unroll
+    for (int u = 0; u < kQBatch; ++u) {
+        const int c = threadIdx.x + u * kAttnThreads;
+        qv[u] = c < kHeadGroup * cpr ? *reinterpret_cast<const uint4*>(qg + (c / cpr) * d + (c % cpr) * 8)
+                                     : make_uint4(0, 0, 0, 0);
+    }
+
+    // valid rows: n_valid from the device (gather mode: top-k count + window).
+    // The row's top-k index is loaded alongside the count (not after it).
+    int my_idx = 0;
+    if (a.idx && threadIdx.x < R && r0 + static_cast<int>(threadIdx.x) < a.k)
+        my_idx = a.idx[static_cast<long long>(b) * a.k + r0 + threadIdx.x];
+    int cnt = 0, nv;
+    if (a.idx) {
+        cnt = a.count ? a.count[b] : a.k;
+        cnt = cnt < 0 ? 0 : (cnt > a.k ? a.k : cnt);
+        if (a.n_comp <= 0) cnt = 0;
+        nv = cnt + a.swa_len;
+        if (split == 0 && hg == 0 && threadIdx.x == 0 && a.n_valid_out) a.n_valid_out[b] = nv;
+    } else {
+        nv = a.n_valid[b];
+    }
+    nv = nv < 0 ? 0 : (nv > a.n_max ? a.n_max : nv);
+    const int rows = max(0, min(R, nv - r0));
+    const long long ml_base = (static_cast<long long>(b) * a.h + hg * kHeadGroup) * n_splits + split;
+    if (rows == 0) {
         if (threadIdx.x < kHeadGroup) {
-            ws_ml[2 * (ml_base + static_cast<long long>(threadIdx.x) * n_splits) + 0] = -INFINITY;
-            ws_ml[2 * (ml_base + static_cast<long long>(threadIdx.x) * n_splits) + 1] = 0.f;
+            a.ws_ml[2 * (ml_base + static_cast<long long>(threadIdx.x) * n_splits) + 0] = -INFINITY;
+            a.ws_ml[2 * (ml_base + static_cast<long long>(threadIdx.x) * n_splits) + 1] = 0.f;
         }
         return;
     }
 
-    // 1. key/value tile -> LDS (zero rows beyond n_valid so P*V stays finite)
-    const int cpr = d / 8;  // 16-byte chunks per row
-    const uint16_t* kvb = kv + b * kv_stride_b + static_cast<long long>(r0) * d;
-    for (int c = threadIdx.x; c < kSplitRows * cpr; c += kAttnThreads) {
-        const int r = c / cpr;
-        const int cc = c - r * cpr;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < rows) v = *reinterpret_cast<const uint4*>(kvb + static_cast<long long>(r) * d + cc * 8);
-        *reinterpret_cast<uint4*>(tile + r * pitch + cc * 8) = v;
+    // 1. one source pointer per row (top-k index or SWA slot), then all row
+    //    loads in unrolled batches: rows -> LDS (and gather_buf); query -> LDS
+    if (threadIdx.x < R) {
+        const int r = threadIdx.x;
+        const int j = r0 + r;
+        const uint16_t* src = nullptr;
+        if (r < rows) {
+            if (!a.idx) {
+                src = a.kv + b * a.kv_stride_b + static_cast<long long>(j) * d;
+            } else if (j < cnt) {
+                const int ri = my_idx < 0 ? 0 : (my_idx >= a.n_comp ? a.n_comp - 1 : my_idx);
+                src = a.comp_kv + b * a.comp_kv_stride_b + static_cast<long long>(ri) * d;
+            } else {
+                int slot = (a.swa_head - a.swa_len + (j - cnt)) % a.w;
+                if (slot < 0) slot += a.w;
+                src = a.swa + b * a.swa_stride_b + static_cast<long long>(slot) * d;
+            }
+        }
+        rowptr[r] = src;
+    }
+#pragma unroll
+    for (int u = 0; u < kQBatch; ++u) {
+        const int c = threadIdx.x + u * kAttnThreads;
+        if (c < kHeadGroup * cpr) *reinterpret_cast<uint4*>(qs + (c / cpr) * pitch + (c % cpr) * 8) = qv[u];
     }
     __syncthreads();
-
-    // 2. S = q K^T: M = 16 heads, N = 2 x 16 rows, K = d split across waves.
-    const int li = lane & 15;
-    const int lg = lane >> 4;
-    const uint16_t* qh = q + b * q_stride_b + static_cast<long long>(hg * kHeadGroup + li) * d + 8 * lg;
-    f32x4 s0 = {}, s1 = {};
-    for (int ks = wv; ks < d / 32; ks += 4) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qh + 32 * ks);
-        const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(tile + li * pitch + 32 * ks + 8 * lg);
-        const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(tile + (16 + li) * pitch + 32 * ks + 8 * lg);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, s1, 0, 0, 0);
-    }
-    // accumulator layout: register r <-> head 4*lg + r, row li (+16 for s1)
+    const bool write_buf = a.idx && a.gather_buf && hg == 0;
+    constexpr int kBatch = 8;
+    for (int base = 0; base < R * cpr; base += kAttnThreads * kBatch) {
+        uint4 v[kBatch];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        spart[wv][4 * lg + r][li] = s0[r];
-        spart[wv][4 * lg + r][16 + li] = s1[r];
-    }
-    __syncthreads();
-
-    // 3. local softmax: thread -> head hh = tid/16, rows 2*(tid%16) + {0,1}
-    {
-        const int hh = threadIdx.x >> 4;
-        const int j0 = 2 * (threadIdx.x & 15);
-        float x0 = (spart[0][hh][j0] + spart[1][hh][j0] + spart[2][hh][j0] + spart[3][hh][j0]) * scale;
-        float x1 = (spart[0][hh][j0 + 1] + spart[1][hh][j0 + 1] + spart[2][hh][j0 + 1] + spart[3][hh][j0 + 1]) * scale;
-        if (j0 >= rows) x0 = -INFINITY;
-        if (j0 + 1 >= rows) x1 = -INFINITY;
-        float mx = fmaxf(x0, x1);
+        for (int u = 0; u < kBatch; ++u) {
+            const int c = base + u * kAttnThreads + threadIdx.x;
+            const uint16_t* src = c < R * cpr ? rowptr[c / cpr] : nullptr;
+            v[u] = src ? *reinterpret_cast<const uint4*>(src + (c % cpr) * 8) : make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        // rows >= 1 here, so mx is finite
-        const uint16_t p0 = f32_to_bf16(expf(x0 - mx));
-        const uint16_t p1 = f32_to_bf16(expf(x1 - mx));
-        float l = bf16_to_f32(p0) + bf16_to_f32(p1);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o);
-        pl[hh * (kSplitRows + 8) + j0] = p0;
-        pl[hh * (kSplitRows + 8) + j0 + 1] = p1;
-        if ((threadIdx.x & 15) == 0) {
-            ws_ml[2 * (ml_base + static_cast<long long>(hh) * n_splits) + 0] = mx;
-            ws_ml[2 * (ml_base + static_cast<long long>(hh) * n_splits) + 1] = l;
+        for (int u = 0; u < kBatch; ++u) {
+            const int c = base + u * kAttnThreads + threadIdx.x;
+            if (c < R * cpr) {
+                const int r = c / cpr;
+                const int cc = c % cpr;
+                *reinterpret_cast<uint4*>(tile + r * pitch + cc * 8) = v[u];
+                if (write_buf && r < rows)
+                    *reinterpret_cast<uint4*>(a.gather_buf + b * a.buf_stride_b + static_cast<long long>(r0 + r) * d + cc * 8) = v[u];
+            }
         }
     }
     __syncthreads();
 
-    // 4. O = P V: M = 16 heads, K = 32 rows (one MFMA step), N = d in 16-wide tiles.
-    const bf16x8 pa = *reinterpret_cast<const bf16x8*>(pl + li * (kSplitRows + 8) + 8 * lg);
-    float* ob = ws_o + (static_cast<long long>(b) * h + hg * kHeadGroup) * n_splits * d +
+    // 2. S = q K^T: wave wv owns rows 16*wv .. 16*wv+15 (if R allows)
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    const bool has_tile = wv < kNt;
+    if (has_tile) {
+        for (int ks = 0; ks < d / 32; ++ks) {
+            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + li * pitch + 32 * ks + 8 * lg);
+            const bf16x8 kb = *reinterpret_cast<const bf16x8*>(tile + (16 * wv + li) * pitch + 32 * ks + 8 * lg);
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb, s, 0, 0, 0);
+        }
+    }
+    // accumulator register r <-> head 4*lg + r, row 16*wv + li
+    const int my_row = 16 * wv + li;
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = (has_tile && my_row < rows) ? s[r] * a.scale : -INFINITY;
+    // 3. split softmax: per-head max and sum over the R rows (lanes, then waves)
+    float mx[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float v = x[r];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+        mx[r] = v;
+    }
+    if (li == 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wmax[wv][4 * lg + r] = mx[r];
+    __syncthreads();
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int hh = 4 * lg + r;
+        const float M = fmaxf(fmaxf(wmax[0][hh], wmax[1][hh]), fmaxf(wmax[2][hh], wmax[3][hh]));
+        // rows >= 1, so M is finite; masked rows give exp(-inf) = 0
+        const uint16_t pb = f32_to_bf16(expf(x[r] - M));
+        p[r] = bf16_to_f32(pb);
+        if (has_tile) pl[hh * kPPitch + my_row] = pb;
+        else if (my_row < R) pl[hh * kPPitch + my_row] = 0;
+        float v = p[r];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+        if (li == 0) wsum[wv][hh] = has_tile ? v : 0.f;
+        mx[r] = M;
+    }
+    __syncthreads();
+    if (threadIdx.x < kHeadGroup) {
+        const int hh = threadIdx.x;
+        const float M = fmaxf(fmaxf(wmax[0][hh], wmax[1][hh]), fmaxf(wmax[2][hh], wmax[3][hh]));
+        const float l = wsum[0][hh] + wsum[1][hh] + wsum[2][hh] + wsum[3][hh];
+        a.ws_ml[2 * (ml_base + static_cast<long long>(hh) * n_splits) + 0] = M;
+        a.ws_ml[2 * (ml_base + static_cast<long long>(hh) * n_splits) + 1] = l;
+    }
+
+    // 4. O = P V: M = 16 heads, K = R rows (R/32 MFMA steps), N = d in 16-wide tiles
+    float* ob = a.ws_o + (static_cast<long long>(b) * a.h + hg * kHeadGroup) * n_splits * d +
                 static_cast<long long>(split) * d;
     for (int nt = wv; nt < d / 16; nt += 4) {
         const int col = 16 * nt + li;
-        bf16x8 vb;
-        uint16_t tmp[8];
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tmp[e] = tile[(8 * lg + e) * pitch + col];
-        __builtin_memcpy(&vb, tmp, sizeof(vb));
-        f32x4 o = {};
-        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o, 0, 0, 0);
+        for (int ks = 0; ks < R / 32; ++ks) {
+            const bf16x8 pa = *reinterpret_cast<const bf16x8*>(pl + li * kPPitch + 32 * ks + 8 * lg);
+            bf16x8 vb;
+            uint16_t tmp[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            ob[static_cast<long long>(4 * lg + r) * n_splits * d + col] = o[r];
+            for (int e = 0; e < 8; ++e) tmp[e] = tile[(32 * ks + 8 * lg + e) * pitch + col];
+            __builtin_memcpy(&vb, tmp, sizeof(vb));
+            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ob[static_cast<long long>(4 * lg + r) * n_splits * d + col] = o[r];
     }
 }
+
+constexpr int kMaxSplits = 256;
 
 __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __restrict__ ws_o,
                                                              const float* __restrict__ ws_ml,
@@ -143,32 +230,68 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
                                                              int d, int n_splits, void* __restrict__ out,
                                                              int out_bf16, float* __restrict__ lse,
                                                              long long out_stride_b) {
+    __shared__ float coef[kMaxSplits];
+    __shared__ float red[2];
     const int hh = blockIdx.x;
     const int b = blockIdx.y;
     const long long base = (static_cast<long long>(b) * h + hh) * n_splits;
     const float* ml = ws_ml + 2 * base;
-    float M = sink ? sink[hh] : -INFINITY;
-    for (int s = 0; s < n_splits; ++s)
-        if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
-    float den = 0.f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < n_splits; ++s)
-            if (ml[2 * s + 1] > 0.f) den += ml[2 * s + 1] * expf(ml[2 * s] - M);
-        if (sink) den += expf(sink[hh] - M);
-    }
-    const float inv = den > 0.f ? 1.0f / den : 0.f;
     const float* ob = ws_o + base * d;
-    for (int dd = threadIdx.x; dd < d; dd += blockDim.x) {
-        float acc = 0.f;
-        for (int s = 0; s < n_splits; ++s)
-            if (ml[2 * s + 1] > 0.f) acc += ob[static_cast<long long>(s) * d + dd] * expf(ml[2 * s] - M);
-        const float y = acc * inv;
-        const long long o = b * out_stride_b + static_cast<long long>(hh) * d + dd;
-        if (out_bf16) static_cast<uint16_t*>(out)[o] = f32_to_bf16(y);
-        else static_cast<float*>(out)[o] = y;
+    // Partials of empty splits are never written: their loads below read stale
+    // workspace bytes that are discarded by a select (never multiplied).
+    constexpr int kBatch = 8;
+    constexpr int kCols = 2;  // d <= 512 with 256 threads
+    float v[kCols][kBatch];
+#pragma unroll
+    for (int cix = 0; cix < kCols; ++cix)
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int dd = threadIdx.x + cix * blockDim.x;
+            v[cix][u] = (dd < d && u < n_splits) ? ob[static_cast<long long>(u) * d + dd] : 0.f;
+        }
+    if (threadIdx.x < kWave) {
+        // one wave derives M, the denominator and the per-split weights
+        float M = sink ? sink[hh] : -INFINITY;
+        for (int s = threadIdx.x; s < n_splits; s += kWave)
+            if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
+        M = wave_max(M);
+        float den = 0.f;
+        if (M != -INFINITY)
+            for (int s = threadIdx.x; s < n_splits; s += kWave)
+                if (ml[2 * s + 1] > 0.f) den += ml[2 * s + 1] * expf(ml[2 * s] - M);
+        den = wave_sum(den);
+        if (M != -INFINITY && sink) den += expf(sink[hh] - M);
+        const float inv = den > 0.f ? 1.0f / den : 0.f;
+        for (int s = threadIdx.x; s < n_splits; s += kWave)
+            coef[s] = (ml[2 * s + 1] > 0.f && M != -INFINITY) ? expf(ml[2 * s] - M) * inv : 0.f;
+        if (threadIdx.x == 0) { red[0] = M; red[1] = den; }
     }
-    if (lse && threadIdx.x == 0)
+    __syncthreads();
+#pragma unroll
+    for (int cix = 0; cix < kCols; ++cix) {
+        const int dd = threadIdx.x + cix * blockDim.x;
+        if (dd >= d) continue;
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (u < n_splits && coef[u] != 0.f) acc += v[cix][u] * coef[u];
+        for (int s0 = kBatch; s0 < n_splits; s0 += kBatch) {
+            float w[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                w[u] = (s0 + u < n_splits && coef[s0 + u] != 0.f) ? ob[static_cast<long long>(s0 + u) * d + dd] : 0.f;
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                if (s0 + u < n_splits && coef[s0 + u] != 0.f) acc += w[u] * coef[s0 + u];
+        }
+        const long long o = b * out_stride_b + static_cast<long long>(hh) * d + dd;
+        if (out_bf16) static_cast<uint16_t*>(out)[o] = f32_to_bf16(acc);
+        else static_cast<float*>(out)[o] = acc;
+    }
+    if (lse && threadIdx.x == 0) {
+        const float M = red[0], den = red[1];
         lse[static_cast<long long>(b) * h + hh] = den > 0.f ? M + logf(den) : -INFINITY;
+    }
 }
 
 // float32 path
@@ -253,18 +376,35 @@ size_t attn_workspace_bytes(bool bf16, int batch, int h, int d, int n_max) {
     return sizeof(float) * static_cast<size_t>(batch) * h * ns * (static_cast<size_t>(d) + 2);
 }
 
-hipError_t launch_attn_bf16(const void* q, const void* kv, const int* n_valid, const float* sink,
-                            float scale, void* out, bool out_bf16, float* lse, int batch, int h,
-                            int d, int n_max, long long q_stride_b, long long kv_stride_b,
-                            long long out_stride_b, void* ws, hipStream_t s) {
-    const int ns = attn_splits(n_max);
-    float* ws_o = static_cast<float*>(ws);
-    float* ws_ml = ws_o + static_cast<size_t>(batch) * h * ns * d;
-    hipLaunchKernelGGL(k_attn_partial_bf16, dim3(ns, h / kHeadGroup, batch), dim3(kAttnThreads), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), n_valid,
-                       scale, h, d, n_max, q_stride_b, kv_stride_b, ws_o, ws_ml, ns);
-    hipLaunchKernelGGL(k_attn_merge, dim3(h, batch), dim3(kAttnThreads), 0, s, ws_o, ws_ml, sink, h,
-                       d, ns, out, out_bf16 ? 1 : 0, lse, out_stride_b);
+int attn_max_splits() { return kMaxSplits; }
+
+int attn_max_rows() { return kMaxSplits * 32; }
+
+hipError_t launch_attn_bf16(AttnArgs a, hipStream_t s) {
+    const int ns = attn_splits(a.n_max);
+    const int R = attn_rows_per_split(a.n_max);
+    a.ws_o = static_cast<float*>(a.ws);
+    a.ws_ml = a.ws_o + static_cast<size_t>(a.batch) * a.h * ns * a.d;
+    const size_t lds = sizeof(uint16_t) * (static_cast<size_t>(R + kHeadGroup) * (a.d + 8) + kHeadGroup * (R + 8));
+    // above 64 KB of dynamic LDS the kernel must opt in (gfx950 has 160 KB per workgroup)
+    static bool opted_in = false;
+    if (!opted_in) {
+        hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_partial_bf16<64>),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
+        hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_partial_bf16<32>),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
+        if (e1 != hipSuccess) return e1;
+        if (e2 != hipSuccess) return e2;
+        opted_in = true;
+    }
+    if (R == 64)
+        hipLaunchKernelGGL(k_attn_partial_bf16<64>, dim3(ns, a.h / kHeadGroup, a.batch), dim3(kAttnThreads), lds, s,
+                           a, ns);
+    else
+        hipLaunchKernelGGL(k_attn_partial_bf16<32>, dim3(ns, a.h / kHeadGroup, a.batch), dim3(kAttnThreads), lds, s,
+                           a, ns);
+    hipLaunchKernelGGL(k_attn_merge, dim3(a.h, a.batch), dim3(kAttnThreads), 0, s, a.ws_o, a.ws_ml, a.sink, a.h,
+                       a.d, ns, a.out, a.out_bf16 ? 1 : 0, a.lse, a.out_stride_b);
     return hipGetLastError();
 }
 

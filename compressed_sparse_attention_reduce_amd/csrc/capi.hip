@@ -121,7 +121,7 @@ int csa_index_score(const void* q, const float* w, const void* k, float* scores,
                                     w_stride_b, k_stride_b, s_stride_b, ld_s, "csa_index_score");
     if (rc != CSA_OK) return rc;
     csa::ScoreArgs a{q, w, k, scores, batch, t, h_i, d_i, n, q_pos, ratio,
-                     q_stride_b, w_stride_b, k_stride_b, s_stride_b, ld_s, nullptr};
+                     q_stride_b, w_stride_b, k_stride_b, s_stride_b, ld_s, csa::CandArgs{nullptr, 0, 0}};
     const hipStream_t s = static_cast<hipStream_t>(stream);
     return launched(dtype == CSA_BF16 ? csa::launch_index_score_bf16(a, s)
                                       : csa::launch_index_score_f32(a, s),
@@ -145,7 +145,7 @@ int csa_topk(const float* scores, int batch, int t, int n, long long ld_s, long 
         return fail(CSA_ERR_WORKSPACE, "csa_topk: workspace %zu < %zu bytes", ws_bytes,
                     csa_topk_workspace_size(batch, t, n, k));
     csa::TopkArgs a{scores, batch, t, n, ld_s, s_stride_b, k, idx, count, ws};
-    return launched(csa::launch_topk(a, false, static_cast<hipStream_t>(stream)), "csa_topk");
+    return launched(csa::launch_topk(a, nullptr, static_cast<hipStream_t>(stream)), "csa_topk");
 }
 
 int csa_gather(const void* comp_kv, int n_comp, const int* idx, const int* count, int k,
@@ -186,8 +186,9 @@ static int check_attn(const void* q, const void* kv, const int* n_valid, void* o
     CHECK(batch >= 1 && h >= 1 && d >= 1 && n_max >= 0, "%s: bad sizes", who);
     CHECK(q_stride_b >= 0 && kv_stride_b >= 0 && out_stride_b >= 0, "%s: negative stride", who);
     if (dtype == CSA_BF16) {
-        if (h % 16 != 0 || d % 32 != 0 || d > 512)
-            return fail(CSA_ERR_UNSUPPORTED, "%s: bf16 path needs h%%16==0, d%%32==0, d<=512", who);
+        if (h % 16 != 0 || d % 32 != 0 || d > 512 || n_max > csa::attn_max_rows())
+            return fail(CSA_ERR_UNSUPPORTED, "%s: bf16 path needs h%%16==0, d%%32==0, d<=512, n_max<=%d", who,
+                        csa::attn_max_rows());
         CHECK(aligned16(q) && aligned16(kv), "%s: q, kv must be 16-byte aligned", who);
         CHECK(q_stride_b % 8 == 0 && kv_stride_b % 8 == 0, "%s: batch strides must keep 16-byte alignment", who);
         CHECK(batch <= 65535 && h / 16 <= 65535, "%s: grid too large", who);
@@ -211,10 +212,24 @@ int csa_sparse_attn(const void* q, const void* kv, const int* n_valid, const flo
         const size_t need = csa::attn_workspace_bytes(true, batch, h, d, n_max);
         if (ws_bytes < need)
             return fail(CSA_ERR_WORKSPACE, "csa_sparse_attn: workspace %zu < %zu bytes", ws_bytes, need);
-        return launched(csa::launch_attn_bf16(q, kv, n_valid, sink, scale, out, out_dtype == CSA_BF16,
-                                              lse, batch, h, d, n_max, q_stride_b, kv_stride_b,
-                                              out_stride_b, ws, s),
-                        "csa_sparse_attn");
+        csa::AttnArgs a{};
+        a.q = static_cast<const uint16_t*>(q);
+        a.q_stride_b = q_stride_b;
+        a.kv = static_cast<const uint16_t*>(kv);
+        a.kv_stride_b = kv_stride_b;
+        a.n_valid = n_valid;
+        a.sink = sink;
+        a.scale = scale;
+        a.out = out;
+        a.out_bf16 = out_dtype == CSA_BF16;
+        a.lse = lse;
+        a.out_stride_b = out_stride_b;
+        a.batch = batch;
+        a.h = h;
+        a.d = d;
+        a.n_max = n_max;
+        a.ws = ws;
+        return launched(csa::launch_attn_bf16(a, s), "csa_sparse_attn");
     }
     return launched(csa::launch_attn_f32(q, kv, n_valid, sink, scale, out, out_dtype == CSA_BF16, lse,
                                          batch, h, d, n_max, q_stride_b, kv_stride_b, out_stride_b, s),
@@ -223,8 +238,13 @@ int csa_sparse_attn(const void* q, const void* kv, const int* n_valid, const flo
 
 // ---- fused decode step ------------------------------------------------------------
 
+// Candidate slots reserved per sequence for the score kernel's top-k lists
+// (the kernel uses two workgroups per compute unit; beyond this many the step
+// falls back to the exact top-k path).
+constexpr int kStepMaxSlots = 1024;
+
 static size_t step_topk_bytes(const csa_layer_desc* L) {
-    return align256(csa::topk_workspace_bytes(L->batch, L->max_comp, L->top_k));
+    return align256(static_cast<size_t>(L->batch) * kStepMaxSlots * csa::kMaxCandM1 * sizeof(unsigned long long));
 }
 
 size_t csa_decode_step_workspace_size(const csa_layer_desc* L) {
@@ -273,59 +293,116 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
     const int es = elem_size(L->dtype);
     CHECK((static_cast<long long>(L->d) * es) % 16 == 0, "csa_decode_step: row bytes must be a multiple of 16");
 
+    CHECK(L->d <= csa::kPrepMaxD && L->d_i <= csa::kPrepMaxD, "csa_decode_step: head dims above %d", csa::kPrepMaxD);
+    CHECK((static_cast<long long>(L->d_i) * es) % 16 == 0 || !completes, "csa_decode_step: d_i row bytes must be a multiple of 16");
+
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf = L->dtype == CSA_BF16;
     hipError_t e;
-
-    // a. new token -> SWA ring
-    e = csa::launch_swa_append(io->kv_new, L->swa, L->swa_head, es, L->batch, L->d,
-                               io->kv_new_stride_b, L->swa_stride_b, s);
-    if (e != hipSuccess) return launched(e, "csa_decode_step/swa_append");
+    void* tws = ws;
+    void* aws = static_cast<char*>(ws) + step_topk_bytes(L);
     const int swa_head = (L->swa_head + 1) % L->w;
     const int swa_len = L->swa_len + 1 < L->w ? L->swa_len + 1 : L->w;
 
-    // b. compress the completed block (main KV and indexer key)
+    // a+b. SWA append and compression of the completed block
+    csa::PrepArgs pa{};
+    pa.batch = L->batch;
+    pa.es = es;
+    pa.d = L->d;
+    pa.d_i = L->d_i;
+    pa.m = L->m;
+    pa.overlap = L->overlap;
+    pa.completes = completes ? 1 : 0;
+    pa.n_comp = L->n_comp;
+    pa.block = io->pos / L->m;
+    pa.kv_new = io->kv_new;
+    pa.kv_new_stride_b = io->kv_new_stride_b;
+    pa.swa = L->swa;
+    pa.swa_stride_b = L->swa_stride_b;
+    pa.swa_slot = L->swa_head;
     if (completes) {
-        const int blk = io->pos / L->m;
-        const bool joint = L->overlap && blk > 0;
+        // the overlapped form passes the previous block's rows first
+        const bool joint = L->overlap && io->pos / L->m > 0;
         const long long skip_main = joint ? static_cast<long long>(L->m) * 2 * L->d : 0;
         const long long skip_idx = joint ? static_cast<long long>(L->m) * 2 * L->d_i : 0;
-        char* ck = static_cast<char*>(L->comp_kv) + static_cast<long long>(L->n_comp) * L->d * es;
-        char* ik = static_cast<char*>(L->idx_keys) + static_cast<long long>(L->n_comp) * L->d_i * es;
-        e = csa::launch_compress(io->z_main + skip_main, io->c_main + skip_main, L->main_bias, L->main_norm,
-                                 ck, bf, L->batch, 1, L->m, L->d, L->overlap != 0, blk,
-                                 io->zc_main_stride_b, L->comp_kv_stride_b, s);
-        if (e != hipSuccess) return launched(e, "csa_decode_step/compress_main");
-        e = csa::launch_compress(io->z_idx + skip_idx, io->c_idx + skip_idx, L->idx_bias, L->idx_norm,
-                                 ik, bf, L->batch, 1, L->m, L->d_i, L->overlap != 0, blk,
-                                 io->zc_idx_stride_b, L->idx_keys_stride_b, s);
-        if (e != hipSuccess) return launched(e, "csa_decode_step/compress_idx");
+        pa.z_main = io->z_main + skip_main;
+        pa.c_main = io->c_main + skip_main;
+        pa.z_idx = io->z_idx + skip_idx;
+        pa.c_idx = io->c_idx + skip_idx;
     }
+    pa.zc_main_stride_b = io->zc_main_stride_b;
+    pa.zc_idx_stride_b = io->zc_idx_stride_b;
+    pa.main_bias = L->main_bias;
+    pa.idx_bias = L->idx_bias;
+    pa.main_norm = L->main_norm;
+    pa.idx_norm = L->idx_norm;
+    pa.comp_kv = L->comp_kv;
+    pa.comp_kv_stride_b = L->comp_kv_stride_b;
+    pa.idx_keys = L->idx_keys;
+    pa.idx_keys_stride_b = L->idx_keys_stride_b;
+    e = csa::launch_step_prep(pa, s);
+    if (e != hipSuccess) return launched(e, "csa_decode_step/prep");
 
-    // c. score (fused radix histogram) -> top-k -> gather -> attention
-    void* tws = ws;
-    void* aws = static_cast<char*>(ws) + step_topk_bytes(L);
-    e = csa::launch_topk_ws_clear(tws, L->batch, N, L->top_k, s);
-    if (e != hipSuccess) return launched(e, "csa_decode_step/topk_clear");
+    // c. score, with every workgroup's top-k candidates when the rows are long,
+    //    then the exact top-k
+    csa::CandArgs ca{nullptr, 0, 0};
+    if (bf && N > 0) {
+        const int slots = csa::index_score_bf16_wgs(L->batch, N);
+        const int kpw = csa::index_score_bf16_keys_per_wg(L->batch, N);
+        const int m = kpw > 0 ? csa::topk_cand_m(N, L->top_k, kpw) : -1;
+        if (m > 0 && slots <= kStepMaxSlots && N > 4 * L->top_k)
+            ca = csa::CandArgs{static_cast<unsigned long long*>(tws), slots, m};
+    }
     csa::ScoreArgs sa{io->q_idx, io->w_idx, L->idx_keys, io->scores, L->batch, 1, L->h_i, L->d_i, N,
                       nullptr, L->m, io->q_idx_stride_b, io->w_stride_b, L->idx_keys_stride_b,
-                      io->scores_stride_b, N, csa::topk_ws_hist(tws)};
+                      io->scores_stride_b, N, ca};
     e = bf ? csa::launch_index_score_bf16(sa, s) : csa::launch_index_score_f32(sa, s);
     if (e != hipSuccess) return launched(e, "csa_decode_step/index_score");
     csa::TopkArgs ta{io->scores, L->batch, 1, N, N, io->scores_stride_b, L->top_k, io->topk_idx,
                      io->topk_count, tws};
-    e = csa::launch_topk(ta, true, s);
+    e = csa::launch_topk(ta, ca.lists ? &ca : nullptr, s);
     if (e != hipSuccess) return launched(e, "csa_decode_step/topk");
+
+    // d+e. gather (fused into the attention on the bf16 path) and attention
+    if (bf) {
+        csa::AttnArgs a{};
+        a.q = static_cast<const uint16_t*>(io->q);
+        a.q_stride_b = io->q_stride_b;
+        a.comp_kv = static_cast<const uint16_t*>(L->comp_kv);
+        a.comp_kv_stride_b = L->comp_kv_stride_b;
+        a.n_comp = N;
+        a.idx = io->topk_idx;
+        a.count = io->topk_count;
+        a.k = L->top_k;
+        a.swa = static_cast<const uint16_t*>(L->swa);
+        a.swa_stride_b = L->swa_stride_b;
+        a.swa_head = swa_head;
+        a.swa_len = swa_len;
+        a.w = L->w;
+        a.gather_buf = static_cast<uint16_t*>(io->gather_buf);
+        a.buf_stride_b = io->gather_stride_b;
+        a.n_valid_out = io->n_valid;
+        a.sink = L->sink;
+        a.scale = L->scale;
+        a.out = io->out;
+        a.out_bf16 = L->out_dtype == CSA_BF16;
+        a.lse = io->lse;
+        a.out_stride_b = io->out_stride_b;
+        a.batch = L->batch;
+        a.h = L->h;
+        a.d = L->d;
+        a.n_max = n_max;
+        a.ws = aws;
+        e = csa::launch_attn_bf16(a, s);
+        return launched(e, "csa_decode_step/attention");
+    }
     e = csa::launch_gather(L->comp_kv, N, io->topk_idx, io->topk_count, L->top_k, L->swa, swa_head,
                            swa_len, L->w, io->gather_buf, io->n_valid, es, L->batch, L->d,
                            L->comp_kv_stride_b, L->swa_stride_b, io->gather_stride_b, s);
     if (e != hipSuccess) return launched(e, "csa_decode_step/gather");
-    e = bf ? csa::launch_attn_bf16(io->q, io->gather_buf, io->n_valid, L->sink, L->scale, io->out,
-                                   L->out_dtype == CSA_BF16, io->lse, L->batch, L->h, L->d, n_max,
-                                   io->q_stride_b, io->gather_stride_b, io->out_stride_b, aws, s)
-           : csa::launch_attn_f32(io->q, io->gather_buf, io->n_valid, L->sink, L->scale, io->out,
-                                  L->out_dtype == CSA_BF16, io->lse, L->batch, L->h, L->d, n_max,
-                                  io->q_stride_b, io->gather_stride_b, io->out_stride_b, s);
+    e = csa::launch_attn_f32(io->q, io->gather_buf, io->n_valid, L->sink, L->scale, io->out,
+                             L->out_dtype == CSA_BF16, io->lse, L->batch, L->h, L->d, n_max,
+                             io->q_stride_b, io->gather_stride_b, io->out_stride_b, s);
     return launched(e, "csa_decode_step/attention");
 }
 

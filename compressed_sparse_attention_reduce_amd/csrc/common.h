@@ -36,6 +36,28 @@ __device__ __forceinline__ bool key_valid(uint32_t k, float x) {
     return k > kKeyNegInf && x == x;
 }
 
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int mask) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), mask);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), mask);
+    return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long w = shfl_xor_u64(v, o);
+        v = w > v ? w : v;
+    }
+    return v;
+}
+__device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long w = shfl_xor_u64(v, o);
+        v = w < v ? w : v;
+    }
+    return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

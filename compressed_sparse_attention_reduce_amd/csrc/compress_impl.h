@@ -1,0 +1,92 @@
+// Compressor reduce for one block of one sequence, run by one workgroup.
+//
+// Page 1, dsv4/kernels/cuda/compressor_reduce.cu (paper eq. 9-12), with the
+// fix of pages 2/3: per channel, softmax over the block's rows of Z + B (the
+// positional bias is added to the logits only), then the weighted sum of C.
+// Optional weighted RMSNorm of the output row (apply_kv_norm_kernel).
+//
+// Threads stride over channels so every row read is coalesced.  The softmax
+// runs in one pass with a running maximum (rescaling the partial sums when the
+// maximum grows), so each row is read once.
+#pragma once
+
+#include "common.h"
+
+namespace csa {
+
+// z, c: this sequence's rows, pointing at the first row of block i (local
+// index); global block g = first_block + i decides whether the overlapped
+// form joins the previous block's a half.  ybuf: d floats of LDS (norm only);
+// red: blockDim/64 floats of LDS.
+__device__ inline void compress_block(const float* __restrict__ z, const float* __restrict__ c,
+                                      const float* __restrict__ bias, const float* __restrict__ norm_w,
+                                      void* __restrict__ out_row, bool out_bf16, int m, int d,
+                                      bool overlap, long long g, float* ybuf, float* red) {
+    const int width = overlap ? 2 * d : d;
+    const bool joint = overlap && g > 0;  // previous block's a half joins the softmax
+    const int own_col = overlap ? d : 0;  // this block's rows: b half when overlapped
+    const int rows = joint ? 2 * m : m;   // logical rows of the joint softmax
+    float ss = 0.f;
+    for (int ch = threadIdx.x; ch < d; ch += blockDim.x) {
+        // one pass with a running max; the rows' loads are issued in batches
+        // so their latencies overlap
+        float mx = -INFINITY, den = 0.f, acc = 0.f;
+        constexpr int kBatch = 8;
+        for (int r0 = 0; r0 < rows; r0 += kBatch) {
+            float lz[kBatch], lc[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int r = r0 + u;
+                lz[u] = -INFINITY;
+                lc[u] = 0.f;
+                if (r < rows) {
+                    // logical row r: block g-1's a half first (rows before z), then own rows
+                    const bool prev = joint && r < m;
+                    const int t = prev ? r : (joint ? r - m : r);
+                    const int col = prev ? ch : own_col + ch;
+                    const long long o = (prev ? -static_cast<long long>(m) * width : 0) +
+                                        static_cast<long long>(t) * width + col;
+                    lz[u] = z[o] + bias[t * width + col];
+                    lc[u] = c[o];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (r0 + u < rows) {
+                    if (lz[u] > mx) {
+                        const float sc = expf(mx - lz[u]);  // 0 on the first row
+                        den *= sc;
+                        acc *= sc;
+                        mx = lz[u];
+                    }
+                    const float e = expf(lz[u] - mx);
+                    den += e;
+                    acc += e * lc[u];
+                }
+            }
+        }
+        const float y = acc / den;
+        if (norm_w) {
+            ybuf[ch] = y;
+            ss += y * y;
+        } else if (out_bf16) {
+            static_cast<uint16_t*>(out_row)[ch] = f32_to_bf16(y);
+        } else {
+            static_cast<float*>(out_row)[ch] = y;
+        }
+    }
+    if (!norm_w) return;
+    ss = wave_sum(ss);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int wv = 0; wv < static_cast<int>(blockDim.x / kWave); ++wv) tot += red[wv];
+    const float inv = 1.0f / sqrtf(tot / d + 1e-6f);
+    for (int ch = threadIdx.x; ch < d; ch += blockDim.x) {
+        const float y = ybuf[ch] * inv * norm_w[ch];
+        if (out_bf16) static_cast<uint16_t*>(out_row)[ch] = f32_to_bf16(y);
+        else static_cast<float*>(out_row)[ch] = y;
+    }
+}
+
+}  // namespace csa

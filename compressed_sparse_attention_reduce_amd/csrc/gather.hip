@@ -1,4 +1,4 @@
-// Gather into the preallocated gather_buf, and the SWA ring append.
+// Gather into the preallocated gather_buf (standalone entry point).
 //
 // Page 1 commit message C2 (one (top_k + window, hd) buffer filled by slice
 // assignment, no concatenation on the hot path) and C3 (the ring may wrap);
@@ -47,18 +47,6 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(
         *reinterpret_cast<uint4*>(dst + o) = *reinterpret_cast<const uint4*>(src + o);
 }
 
-__global__ __launch_bounds__(kGatherThreads) void k_swa_append(const char* __restrict__ kv_new,
-                                                               char* __restrict__ swa, int slot,
-                                                               int row_bytes,
-                                                               long long kv_new_stride_b,
-                                                               long long swa_stride_b) {
-    const int b = blockIdx.x;
-    const char* src = kv_new + b * kv_new_stride_b;
-    char* dst = swa + b * swa_stride_b + static_cast<long long>(slot) * row_bytes;
-    for (int o = threadIdx.x * 16; o < row_bytes; o += blockDim.x * 16)
-        *reinterpret_cast<uint4*>(dst + o) = *reinterpret_cast<const uint4*>(src + o);
-}
-
 }  // namespace
 
 hipError_t launch_gather(const void* comp_kv, int n_comp, const int* idx, const int* count, int k,
@@ -72,15 +60,6 @@ hipError_t launch_gather(const void* comp_kv, int n_comp, const int* idx, const 
                        static_cast<const char*>(swa), swa_head, swa_len, w, static_cast<char*>(buf),
                        n_valid, d * elem_bytes, kv_stride_b * elem_bytes, swa_stride_b * elem_bytes,
                        buf_stride_b * elem_bytes);
-    return hipGetLastError();
-}
-
-hipError_t launch_swa_append(const void* kv_new, void* swa, int slot, int elem_bytes, int batch,
-                             int d, long long kv_new_stride_b, long long swa_stride_b,
-                             hipStream_t s) {
-    hipLaunchKernelGGL(k_swa_append, dim3(batch), dim3(kGatherThreads), 0, s,
-                       static_cast<const char*>(kv_new), static_cast<char*>(swa), slot, d * elem_bytes,
-                       kv_new_stride_b * elem_bytes, swa_stride_b * elem_bytes);
     return hipGetLastError();
 }
 

@@ -4,21 +4,26 @@
 // eq. 16): one d_i = 128 key per compressed block, shared by all 64 indexer
 // heads (MQA).  Causal form: page 1, archived_plans/NEXT_STEPS.md, Issue 2.
 //
-// bf16 path (the decode hot spot, HBM-bound at 64 FLOP per key byte):
-//   * each wave keeps the query (64 heads x 128 = 16 KB) resident in VGPRs as
-//     the A operand of v_mfma_f32_32x32x16_bf16 (heads = M, two 32-row tiles);
-//   * key tiles of 32 blocks stream straight from HBM into B-operand VGPRs
-//     (each lane loads 16 contiguous bytes of one key row; lanes l and l+32
-//     cover 32 contiguous bytes of the same row per k-step), one tile ahead;
-//   * the epilogue applies ReLU and the head weights in registers — every lane
-//     holds 32 heads of one key — and finishes the head sum with one lane
-//     swap (l <-> l+32), so scores leave as one coalesced 128 B store per tile;
-//   * optionally it also builds the 12-bit radix histogram of the scores that
-//     the top-k filter uses (LDS atomics, flushed once per workgroup).
-// Workgroups own contiguous key ranges of one query row; the grid is sized to
-// fill every CU with two 4-wave workgroups.
+// bf16 path (the decode hot spot; 64 FLOP per key byte, so HBM-bound on the
+// matrix cores):
+//   * v_mfma_f32_16x16x32_bf16 with heads as M (4 tiles of 16) and keys as N
+//     (tiles of 16 blocks); the query (64 x 128) is staged once per workgroup
+//     through LDS into A-operand VGPRs and stays there;
+//   * every wave owns an interleaved set of key tiles and keeps a ring of
+//     kRing tiles in flight: each lane loads 16 contiguous bytes of one key
+//     row per k-step straight into B-operand VGPRs (one instruction covers 16
+//     rows x 64 B), and a tile's slot is refilled right after it is consumed,
+//     so HBM latency is covered by kRing tiles per wave;
+//   * the epilogue applies ReLU and the head weights in registers (each lane
+//     holds 16 heads of one key) and finishes the head sum with two lane
+//     swaps; 16 scores leave per tile as one 64 B store;
+//   * with candidate lists the kernel also keeps its scores as unique
+//     (score, index) composites in LDS and, at the end, writes the workgroup's
+//     top m + 1 to its private slot; the top-k kernel merges those slots (no
+//     cross-workgroup atomics or fences, which serialise on this chip).
 #include "common.h"
 #include "kernels.h"
+#include "topk_common.h"
 
 namespace csa {
 
@@ -26,108 +31,136 @@ namespace {
 
 constexpr int kScoreThreads = 256;
 constexpr int kWavesPerWg = kScoreThreads / kWave;
-constexpr int kTileKeys = 32;
+constexpr int kTileKeys = 16;
 constexpr int kHeads = 64;
 constexpr int kDi = 128;
-constexpr int kSteps = kDi / 16;  // k-steps of the 32x32x16 MFMA
+constexpr int kSteps = kDi / 32;   // k-steps of the 16x16x32 MFMA
+constexpr int kMTiles = kHeads / 16;
+constexpr int kRing = 4;           // key tiles in flight per wave
+constexpr int kQPitch = kDi + 8;   // LDS row pitch of the staged query (bank spread)
+constexpr int kMaxTilesPerWave = 32;                  // with candidates: LDS holds every score of the workgroup
+constexpr int kWgKeys = kMaxTilesPerWave * kWavesPerWg * kTileKeys;
 
-template <bool kHist>
-__global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs a,
-                                                                       int tiles_per_row,
-                                                                       int tiles_per_wg) {
-    __shared__ uint32_t lhist[kHist ? kHistBins : 1];
+template <bool kCands>
+__global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs a, int tiles_per_row) {
+    __shared__ __attribute__((aligned(16))) uint16_t qs[kHeads * kQPitch];
+    __shared__ __attribute__((aligned(16))) float ws[kHeads];
+    __shared__ u64 vals[kCands ? kWgKeys : 1];
+    __shared__ CandSmem cs;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const int row = blockIdx.y;
     const int b = row / a.t;
     const int tt = row - b * a.t;
-    const int tile0 = blockIdx.x * tiles_per_wg;
-    const int tile1 = min(tile0 + tiles_per_wg, tiles_per_row);
-    const int hi = lane & 31;   // M row (head) of the A operand / N column (key) of B
-    const int grp = lane >> 5;  // which 8-element half of each 16-wide k-step
-
-    if (kHist) {
-        for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) lhist[i] = 0;
-        __syncthreads();
-    }
-
-    // A operand: q[head][16*s + 8*grp + e] for heads hi and 32 + hi.
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + b * a.q_stride_b +
-                           static_cast<long long>(tt) * kHeads * kDi;
-    bf16x8 qa0[kSteps], qa1[kSteps];
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        qa0[s] = *reinterpret_cast<const bf16x8*>(qrow + hi * kDi + 16 * s + 8 * grp);
-        qa1[s] = *reinterpret_cast<const bf16x8*>(qrow + (32 + hi) * kDi + 16 * s + 8 * grp);
-    }
-    // Head weights for the 16 accumulator rows this lane holds in each M tile:
-    // register r <-> head 8*(r/4) + 4*grp + (r%4).
-    const float* wrow = a.w + b * a.w_stride_b + static_cast<long long>(tt) * kHeads;
-    float w0[16], w1[16];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 v0 = *reinterpret_cast<const float4*>(wrow + 8 * q4 + 4 * grp);
-        const float4 v1 = *reinterpret_cast<const float4*>(wrow + 32 + 8 * q4 + 4 * grp);
-        w0[4 * q4 + 0] = v0.x; w0[4 * q4 + 1] = v0.y; w0[4 * q4 + 2] = v0.z; w0[4 * q4 + 3] = v0.w;
-        w1[4 * q4 + 0] = v1.x; w1[4 * q4 + 1] = v1.y; w1[4 * q4 + 2] = v1.z; w1[4 * q4 + 3] = v1.w;
-    }
-
-    const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_stride_b;
-    float* srow = a.scores + b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s;
-    const long long pos = a.q_pos ? static_cast<long long>(a.q_pos[row]) : 0;
+    const int li = lane & 15;   // key column of B / head row of A within a 16-tile
+    const int lg = lane >> 4;   // 8-element group of each 32-wide k-step
     const int n = a.n;
+    const int waves_per_row = gridDim.x * kWavesPerWg;
+    const int gw = blockIdx.x * kWavesPerWg + wv;
+    const int n_mine = gw < tiles_per_row ? (tiles_per_row - gw + waves_per_row - 1) / waves_per_row : 0;
 
-    auto load_tile = [&](int tile, bf16x8* dst) {
-        const int key = min(tile * kTileKeys + hi, n - 1);  // tail lanes re-read a valid row
-        const uint16_t* p = kbase + static_cast<long long>(key) * kDi + 8 * grp;
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_stride_b + 8 * lg;
+    auto load_tile = [&](int j, bf16x8* dst) {
+        const int key = j < n_mine ? min((gw + j * waves_per_row) * kTileKeys + li, n - 1) : n - 1;
+        const uint16_t* p = kbase + static_cast<long long>(key) * kDi;
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) dst[s] = *reinterpret_cast<const bf16x8*>(p + 16 * s);
+        for (int s = 0; s < kSteps; ++s) dst[s] = *reinterpret_cast<const bf16x8*>(p + 32 * s);
     };
 
-    int tile = tile0 + wv;
-    bf16x8 kb[kSteps];
-    if (tile < tile1) load_tile(tile, kb);
-    for (; tile < tile1; tile += kWavesPerWg) {
-        bf16x8 kn[kSteps];
-        const int nxt = tile + kWavesPerWg;
-        if (nxt < tile1) load_tile(nxt, kn);
-
-        f32x16 acc0 = {}, acc1 = {};
+    // 1. query (16 KB: four 16-byte pieces per thread) and head weights first,
+    //    then the first kRing key tiles, so that waiting for the query below
+    //    leaves the key loads in flight
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + b * a.q_stride_b +
+                           static_cast<long long>(tt) * kHeads * kDi;
+    static_assert(kHeads * kDi / 8 == 4 * kScoreThreads, "four 16-byte query pieces per thread");
+    auto qpiece = [&](int u) -> uint4 {
+        const int c = threadIdx.x + u * kScoreThreads;
+        return *reinterpret_cast<const uint4*>(qrow + (c / (kDi / 8)) * kDi + (c % (kDi / 8)) * 8);
+    };
+    const uint4 qv0 = qpiece(0), qv1 = qpiece(1), qv2 = qpiece(2), qv3 = qpiece(3);
+    const float* wrow = a.w + b * a.w_stride_b + static_cast<long long>(tt) * kHeads;
+    const float4 wv4 = *reinterpret_cast<const float4*>(wrow + 4 * (threadIdx.x & 15));
+    // keep the key loads younger than the query loads (the wait below is in order)
+    __builtin_amdgcn_sched_barrier(0);
+    // Ring refills are unconditional so every iteration issues the same loads
+    // (the wait counts stay exact); slots past this wave's last tile re-read
+    // the row's last key, which stays in L2.
+    bf16x8 kb[kRing][kSteps];
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa0[s], kb[s], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa1[s], kb[s], acc1, 0, 0, 0);
-        }
-        float part = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            part += w0[r] * fmaxf(acc0[r], 0.f);
-            part += w1[r] * fmaxf(acc1[r], 0.f);
-        }
-        part += __shfl_xor(part, 32);
+    for (int i = 0; i < kRing; ++i) load_tile(i, kb[i]);
 
-        const int key = tile * kTileKeys + hi;
-        if (grp == 0 && key < n) {
-            float sc = part;
-            if (a.q_pos && static_cast<long long>(a.ratio) * key + a.ratio - 1 > pos) sc = -INFINITY;
-            srow[key] = sc;
-            if (kHist) {
-                const uint32_t kk = score_key(sc);
-                if (key_valid(kk, sc)) atomicAdd(&lhist[kk >> (32 - kHistBits)], 1u);
+    // 2. stage the query and weights through LDS into registers
+    auto qstage = [&](int u, const uint4& v) {
+        const int c = threadIdx.x + u * kScoreThreads;
+        *reinterpret_cast<uint4*>(qs + (c / (kDi / 8)) * kQPitch + (c % (kDi / 8)) * 8) = v;
+    };
+    qstage(0, qv0);
+    qstage(1, qv1);
+    qstage(2, qv2);
+    qstage(3, qv3);
+    if (threadIdx.x < 16) *reinterpret_cast<float4*>(ws + 4 * threadIdx.x) = wv4;
+    if (kCands)
+        for (int i = threadIdx.x; i < kWgKeys; i += kScoreThreads) vals[i] = 0ull;
+    __syncthreads();
+    bf16x8 qa[kMTiles][kSteps];
+#pragma unroll
+    for (int mt = 0; mt < kMTiles; ++mt)
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s)
+            qa[mt][s] = *reinterpret_cast<const bf16x8*>(qs + (16 * mt + li) * kQPitch + 32 * s + 8 * lg);
+    float wr[kMTiles][4];
+#pragma unroll
+    for (int mt = 0; mt < kMTiles; ++mt) {
+        const float4 v = *reinterpret_cast<const float4*>(ws + 16 * mt + 4 * lg);
+        wr[mt][0] = v.x; wr[mt][1] = v.y; wr[mt][2] = v.z; wr[mt][3] = v.w;
+    }
+
+    float* srow = a.scores + b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s;
+    const long long pos = a.q_pos ? static_cast<long long>(a.q_pos[row]) : 0;
+
+    // 3. stream: consume a tile, refill its ring slot kRing tiles ahead
+    for (int j0 = 0; j0 < n_mine; j0 += kRing) {
+#pragma unroll
+        for (int i = 0; i < kRing; ++i) {
+            const int j = j0 + i;
+            f32x4 acc[kMTiles];
+#pragma unroll
+            for (int mt = 0; mt < kMTiles; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+                for (int mt = 0; mt < kMTiles; ++mt)
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], kb[i][s], acc[mt], 0, 0, 0);
+            load_tile(j + kRing, kb[i]);
+            // accumulator register r of M tile mt <-> head 16*mt + 4*lg + r, key li
+            float part = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < kMTiles; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) part += wr[mt][r] * fmaxf(acc[mt][r], 0.f);
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            const int key = (gw + j * waves_per_row) * kTileKeys + li;
+            if (j < n_mine && lg == 0 && key < n) {
+                float sc = part;
+                if (a.q_pos && static_cast<long long>(a.ratio) * key + a.ratio - 1 > pos) sc = -INFINITY;
+                srow[key] = sc;
+                if (kCands) {
+                    const uint32_t kk = score_key(sc);
+                    if (key_valid(kk, sc))
+                        vals[(j * kWavesPerWg + wv) * kTileKeys + li] = composite(kk, static_cast<uint32_t>(key));
+                }
             }
         }
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) kb[s] = kn[s];
     }
 
-    if (kHist) {
-        __syncthreads();
-        uint32_t* gh = a.hist + static_cast<long long>(row) * kHistBins;
-        for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) {
-            const uint32_t v = lhist[i];
-            if (v) atomicAdd(gh + i, v);
-        }
-    }
+    if (!kCands) return;
+    // 4. this workgroup's best m + 1 to its candidate slot
+    __syncthreads();
+    const int m1 = a.cands.m + 1;
+    const int nv = ((tiles_per_row + waves_per_row - 1) / waves_per_row) * kWavesPerWg * kTileKeys;
+    block_top_m1(vals, nv < kWgKeys ? nv : kWgKeys, m1,
+                 a.cands.lists + (static_cast<long long>(row) * a.cands.slots + blockIdx.x) * m1, cs);
 }
 
 // float32 path (small correctness workloads): one thread per key, the query
@@ -146,43 +179,47 @@ __global__ __launch_bounds__(kScoreF32Threads) void k_index_score_f32(ScoreArgs 
     for (int i = threadIdx.x; i < a.h_i; i += blockDim.x) qs[hd + i] = wrow[i];
     __syncthreads();
     const int key = blockIdx.x * blockDim.x + threadIdx.x;
-    if (key >= a.n) return;
-    const float* kr = static_cast<const float*>(a.k) + b * a.k_stride_b + static_cast<long long>(key) * a.d_i;
-    float sc = 0.f;
-    for (int h = 0; h < a.h_i; ++h) {
-        float dot = 0.f;
-        for (int d = 0; d < a.d_i; ++d) dot += qs[h * a.d_i + d] * kr[d];
-        sc += qs[hd + h] * fmaxf(dot, 0.f);
-    }
-    if (a.q_pos && static_cast<long long>(a.ratio) * key + a.ratio - 1 > a.q_pos[row]) sc = -INFINITY;
-    a.scores[b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s + key] = sc;
-    if (a.hist) {
-        const uint32_t kk = score_key(sc);
-        if (key_valid(kk, sc))
-            atomicAdd(a.hist + static_cast<long long>(row) * kHistBins + (kk >> (32 - kHistBits)), 1u);
+    if (key < a.n) {
+        const float* kr = static_cast<const float*>(a.k) + b * a.k_stride_b + static_cast<long long>(key) * a.d_i;
+        float sc = 0.f;
+        for (int h = 0; h < a.h_i; ++h) {
+            float dot = 0.f;
+            for (int d = 0; d < a.d_i; ++d) dot += qs[h * a.d_i + d] * kr[d];
+            sc += qs[hd + h] * fmaxf(dot, 0.f);
+        }
+        if (a.q_pos && static_cast<long long>(a.ratio) * key + a.ratio - 1 > a.q_pos[row]) sc = -INFINITY;
+        a.scores[b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s + key] = sc;
     }
 }
 
 }  // namespace
 
+int index_score_bf16_wgs(int rows, int n) {
+    const int tiles = (n + kTileKeys - 1) / kTileKeys;
+    const int target = 2 * device_cu_count();
+    int wgs = (target + rows - 1) / rows;
+    // at least kRing tiles per wave where the row is long enough
+    const int max_wgs = (tiles + kWavesPerWg * kRing - 1) / (kWavesPerWg * kRing);
+    if (wgs > max_wgs) wgs = max_wgs;
+    return wgs < 1 ? 1 : wgs;
+}
+
+int index_score_bf16_keys_per_wg(int rows, int n) {
+    const int tiles = (n + kTileKeys - 1) / kTileKeys;
+    const int waves = index_score_bf16_wgs(rows, n) * kWavesPerWg;
+    const int per_wave = (tiles + waves - 1) / waves;
+    return per_wave <= kMaxTilesPerWave ? per_wave * kWavesPerWg * kTileKeys : -1;
+}
+
 hipError_t launch_index_score_bf16(const ScoreArgs& a, hipStream_t s) {
     if (a.n == 0) return hipSuccess;
     const int rows = a.batch * a.t;
     const int tiles = (a.n + kTileKeys - 1) / kTileKeys;
-    const int target = 2 * device_cu_count();
-    int wgs = (target + rows - 1) / rows;
-    const int max_wgs = (tiles + kWavesPerWg - 1) / kWavesPerWg;
-    if (wgs > max_wgs) wgs = max_wgs;
-    if (wgs < 1) wgs = 1;
-    int per = (tiles + wgs - 1) / wgs;
-    per = (per + kWavesPerWg - 1) / kWavesPerWg * kWavesPerWg;
-    wgs = (tiles + per - 1) / per;
-    if (a.hist)
-        hipLaunchKernelGGL(k_index_score_bf16<true>, dim3(wgs, rows), dim3(kScoreThreads), 0, s, a,
-                           tiles, per);
+    const int wgs = index_score_bf16_wgs(rows, a.n);
+    if (a.cands.lists && a.cands.slots == wgs && index_score_bf16_keys_per_wg(rows, a.n) > 0)
+        hipLaunchKernelGGL(k_index_score_bf16<true>, dim3(wgs, rows), dim3(kScoreThreads), 0, s, a, tiles);
     else
-        hipLaunchKernelGGL(k_index_score_bf16<false>, dim3(wgs, rows), dim3(kScoreThreads), 0, s, a,
-                           tiles, per);
+        hipLaunchKernelGGL(k_index_score_bf16<false>, dim3(wgs, rows), dim3(kScoreThreads), 0, s, a, tiles);
     return hipGetLastError();
 }
 

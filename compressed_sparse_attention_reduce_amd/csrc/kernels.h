@@ -11,11 +11,25 @@ namespace csa {
 
 int device_cu_count();
 
+constexpr int kTopkMaxK = 2048;
+
 // ---- compressor reduce -------------------------------------------------------
 hipError_t launch_compress(const float* z, const float* c, const float* bias, const float* norm_w,
                            void* out, bool out_bf16, int batch, int n_blocks, int m, int d,
                            bool overlap, int first_block, long long zc_stride_b,
                            long long out_stride_b, hipStream_t s);
+
+// ---- top-k candidates ------------------------------------------------------------
+constexpr int kMaxCandM1 = 64;  // longest per-slot candidate list
+// Per-slot candidate lists: [rows][slots][m + 1] composites, each slot's top
+// m + 1 (sorted, zero padded); the (m+1)-th is the largest one it dropped.
+struct CandArgs {
+    unsigned long long* lists;
+    int slots;
+    int m;
+};
+// m for slots of keys_per_slot keys, or -1 if lists would be too long.
+int topk_cand_m(int n, int k, int keys_per_slot);
 
 // ---- lightning-indexer score -------------------------------------------------
 struct ScoreArgs {
@@ -27,15 +41,17 @@ struct ScoreArgs {
     const int* q_pos;
     int ratio;
     long long q_stride_b, w_stride_b, k_stride_b, s_stride_b, ld_s;
-    uint32_t* hist;  // optional [batch*t][kHistBins] radix histogram of the scores
+    // optional top-k candidates: every workgroup writes the top m + 1 of its
+    // keys to its slot of cands.lists (cands.slots must equal its grid width)
+    CandArgs cands;
 };
+// workgroups per row and keys per workgroup of the bf16 score kernel
+int index_score_bf16_wgs(int rows, int n);
+int index_score_bf16_keys_per_wg(int rows, int n);
 hipError_t launch_index_score_bf16(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_index_score_f32(const ScoreArgs& a, hipStream_t s);
 
 // ---- top-k -------------------------------------------------------------------
-constexpr int kTopkMaxK = 2048;
-constexpr int kHistBits = 12;               // first radix digit (from the score kernel)
-constexpr int kHistBins = 1 << kHistBits;
 size_t topk_workspace_bytes(int rows, int n, int k);
 struct TopkArgs {
     const float* scores;
@@ -46,12 +62,9 @@ struct TopkArgs {
     int* count;
     void* ws;
 };
-// hist_ready: the workspace histogram was already filled by the score kernel
-// (and zeroed before it); otherwise the launcher builds it.
-hipError_t launch_topk(const TopkArgs& a, bool hist_ready, hipStream_t s);
-// Zeroes the workspace histogram/counters so a score kernel can fill it.
-hipError_t launch_topk_ws_clear(void* ws, int rows, int n, int k, hipStream_t s);
-uint32_t* topk_ws_hist(void* ws);
+// cands: per-slot candidate lists already produced (by the score kernel), or
+// nullptr (the launcher produces them itself when the rows are long).
+hipError_t launch_topk(const TopkArgs& a, const CandArgs* cands, hipStream_t s);
 
 // ---- gather ------------------------------------------------------------------
 hipError_t launch_gather(const void* comp_kv, int n_comp, const int* idx, const int* count, int k,
@@ -60,19 +73,66 @@ hipError_t launch_gather(const void* comp_kv, int n_comp, const int* idx, const 
                          long long swa_stride_b, long long buf_stride_b, hipStream_t s);
 
 // ---- sparse attention ----------------------------------------------------------
+struct AttnArgs {
+    const uint16_t* q;
+    long long q_stride_b;
+    // plain mode: rows kv[b][0 .. n_valid[b]) of [batch][n_max][d]
+    const uint16_t* kv;
+    long long kv_stride_b;
+    const int* n_valid;
+    // gather mode (idx != nullptr): rows = comp_kv[idx[b][0 .. count[b])] then
+    // the live SWA window; written to gather_buf and n_valid_out on the way
+    const uint16_t* comp_kv;
+    long long comp_kv_stride_b;
+    int n_comp;
+    const int* idx;
+    const int* count;
+    int k;
+    const uint16_t* swa;
+    long long swa_stride_b;
+    int swa_head, swa_len, w;
+    uint16_t* gather_buf;
+    long long buf_stride_b;
+    int* n_valid_out;
+    // common
+    const float* sink;
+    float scale;
+    void* out;
+    bool out_bf16;
+    float* lse;
+    long long out_stride_b;
+    int batch, h, d, n_max;
+    void* ws;
+    float* ws_o;   // set by the launcher
+    float* ws_ml;  // set by the launcher
+};
 size_t attn_workspace_bytes(bool bf16, int batch, int h, int d, int n_max);
-hipError_t launch_attn_bf16(const void* q, const void* kv, const int* n_valid, const float* sink,
-                            float scale, void* out, bool out_bf16, float* lse, int batch, int h,
-                            int d, int n_max, long long q_stride_b, long long kv_stride_b,
-                            long long out_stride_b, void* ws, hipStream_t s);
+int attn_max_splits();
+int attn_max_rows();
+hipError_t launch_attn_bf16(AttnArgs a, hipStream_t s);
 hipError_t launch_attn_f32(const void* q, const void* kv, const int* n_valid, const float* sink,
                            float scale, void* out, bool out_bf16, float* lse, int batch, int h,
                            int d, int n_max, long long q_stride_b, long long kv_stride_b,
                            long long out_stride_b, hipStream_t s);
 
-// ---- small helpers for the fused step ------------------------------------------
-hipError_t launch_swa_append(const void* kv_new, void* swa, int slot, int elem_bytes, int batch,
-                             int d, long long kv_new_stride_b, long long swa_stride_b,
-                             hipStream_t s);
+// ---- first kernel of the fused decode step ------------------------------------------
+constexpr int kPrepMaxD = 4096;
+struct PrepArgs {
+    int batch, es, d, d_i, m, overlap, completes, n_comp;
+    long long block;
+    const void* kv_new;
+    long long kv_new_stride_b;
+    void* swa;
+    long long swa_stride_b;
+    int swa_slot;
+    const float *z_main, *c_main, *z_idx, *c_idx;
+    long long zc_main_stride_b, zc_idx_stride_b;
+    const float *main_bias, *idx_bias, *main_norm, *idx_norm;
+    void* comp_kv;
+    long long comp_kv_stride_b;
+    void* idx_keys;
+    long long idx_keys_stride_b;
+};
+hipError_t launch_step_prep(const PrepArgs& a, hipStream_t s);
 
 }  // namespace csa

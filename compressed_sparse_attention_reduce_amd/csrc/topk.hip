@@ -6,144 +6,45 @@
 // (fixed k, invalid entries masked, no host read of the count).
 //
 // Every element gets a unique 64-bit composite  c = key(score) << 32 | ~index
-// (key is order preserving, -0 folded onto +0), so "largest k composites" is
-// exactly the wanted set and order, whatever the ties; the result does not
-// depend on the order in which parallel workers find candidates.
+// (key order-preserving, -0 folded onto +0), so "the k largest composites" is
+// exactly the wanted set and order whatever the ties.
 //
-// Pipeline for one row of n scores (radix select, most significant digit first):
-//   1. histogram of the top 12 key bits (built by the score kernel when fused,
-//      otherwise by k_topk_hist) -> threshold bin tb: fewer than k valid
-//      elements lie above tb, at least k at or above it;
-//   2. k_topk_filter, many workgroups: elements above tb go to the "sure" list
-//      (always < k of them), elements in tb to the candidate list;
-//   3. k_topk_final, one workgroup per row: keeps the sure list, picks the
-//      remaining best candidates (bitonic sort in LDS when they fit, else
-//      further 10-bit radix digits over the 64-bit composite), and sorts the
-//      k winners.
+// Cross-workgroup atomics and fences are slow on this chip (hundreds of
+// workgroups hitting one address serialise), so the selection uses none:
+//   * candidates: every producer workgroup (the score kernel's, or
+//     k_topk_cands for a standalone call) writes the top m+1 composites of its
+//     own slice to a private slot of the workspace;
+//   * k_topk_final, one workgroup per row, selects the top k of the union of
+//     the kept m per slot and checks that every slot's (m+1)-th composite
+//     (the largest it dropped) is below the k-th pick, which proves the union
+//     held the true top k.  If the check fails (adversarial ties, or no
+//     candidates were produced) it runs an exact radix select over the whole
+//     row instead: 12-bit key histogram, threshold bin, then further digits of
+//     the composite until the remaining candidates fit in LDS.
+// Either way the result is exact; only the time differs.
+#include <cmath>
+
 #include "common.h"
 #include "kernels.h"
+#include "topk_common.h"
 
 namespace csa {
 
 namespace {
 
-typedef unsigned long long u64;
-
-constexpr int kFilterThreads = 256;
-constexpr int kFilterChunk = 8192;   // scores per filter workgroup
 constexpr int kFinalThreads = 1024;
-constexpr int kCandLds = 4096;       // candidates sorted in LDS
-constexpr int kGlobalCandCap = 16384;
+constexpr int kUnionCap = 8192;       // candidates of the fast path held in LDS
+constexpr int kPool = 2048;           // exact-path candidates held in LDS
 constexpr int kRefineBits = 10;
+constexpr int kCandThreads = 256;
+constexpr int kCandChunk = 2048;      // scores per k_topk_cands workgroup
 
-struct RowWs {
-    uint32_t* hist;  // [kHistBins]
-    uint32_t* ctr;   // [0] sure count, [1] candidate count
-    u64* sure;       // [k]
-    u64* cand;       // [cap]
-};
-
-// Workspace: all rows' histograms first (contiguous, so the score kernel can
-// fill them with a plain row stride), then counters, sure lists, candidates.
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-__host__ __device__ inline int cand_cap(int n) { return n < kGlobalCandCap ? (n > 0 ? n : 1) : kGlobalCandCap; }
-struct WsLayout {
-    size_t ctr, sure, cand, total;
-};
-__host__ __device__ inline WsLayout ws_layout(int rows, int n, int k) {
-    WsLayout l;
-    const size_t r = static_cast<size_t>(rows);
-    l.ctr = align256(r * kHistBins * sizeof(uint32_t));
-    l.sure = l.ctr + align256(r * 4 * sizeof(uint32_t));
-    l.cand = l.sure + align256(r * static_cast<size_t>(k) * sizeof(u64));
-    l.total = l.cand + align256(r * static_cast<size_t>(cand_cap(n)) * sizeof(u64));
-    return l;
-}
-__device__ inline RowWs row_ws(void* ws, int row, int rows, int n, int k) {
-    const WsLayout l = ws_layout(rows, n, k);
-    char* p = static_cast<char*>(ws);
-    RowWs r;
-    r.hist = reinterpret_cast<uint32_t*>(p) + static_cast<size_t>(row) * kHistBins;
-    r.ctr = reinterpret_cast<uint32_t*>(p + l.ctr) + static_cast<size_t>(row) * 4;
-    r.sure = reinterpret_cast<u64*>(p + l.sure) + static_cast<size_t>(row) * k;
-    r.cand = reinterpret_cast<u64*>(p + l.cand) + static_cast<size_t>(row) * cand_cap(n);
-    return r;
-}
-
-__device__ inline u64 composite(uint32_t key, uint32_t idx) {
-    return (static_cast<u64>(key) << 32) | static_cast<u64>(0xffffffffu - idx);
-}
-__device__ inline int composite_index(u64 c) {
-    return static_cast<int>(0xffffffffu - static_cast<uint32_t>(c));
-}
 
 __device__ inline const float* score_row(const TopkArgs& a, int row) {
     const int b = row / a.t;
     const int tt = row - b * a.t;
     return a.scores + b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s;
-}
-
-// Block-wide search over a histogram held in LDS: the largest bin `tb` with
-// suffix(tb) >= need (suffix(x) = elements in bins >= x).  above =
-// suffix(tb + 1), at = hist[tb].  If the total is below `need`, tb = -1 and
-// above = total.  `scratch` holds one uint32 per thread.  All threads return
-// the same values.
-__device__ void find_threshold(const uint32_t* hist, int nbins, uint32_t need, uint32_t* scratch,
-                               int* out3, int& tb, uint32_t& above, uint32_t& at) {
-    const int nt = blockDim.x;
-    const int per = (nbins + nt - 1) / nt;
-    const int lo = threadIdx.x * per;
-    const int hi = min(lo + per, nbins);
-    uint32_t mine = 0;
-    for (int i = lo; i < hi; ++i) mine += hist[i];
-    scratch[threadIdx.x] = mine;
-    if (threadIdx.x == 0) { out3[0] = -1; out3[1] = 0; out3[2] = 0; }
-    __syncthreads();
-    // inclusive suffix scan (Hillis-Steele) over the per-thread sums
-    for (int off = 1; off < nt; off <<= 1) {
-        const uint32_t add = (threadIdx.x + off < nt) ? scratch[threadIdx.x + off] : 0u;
-        __syncthreads();
-        scratch[threadIdx.x] += add;
-        __syncthreads();
-    }
-    const uint32_t incl = scratch[threadIdx.x];
-    const uint32_t excl = incl - mine;
-    const uint32_t total = scratch[0];
-    if (total < need) {
-        if (threadIdx.x == 0) { out3[0] = -1; out3[1] = static_cast<int>(total); out3[2] = 0; }
-    } else if (excl < need && incl >= need) {
-        uint32_t acc = excl;
-        for (int i = hi - 1; i >= lo; --i) {
-            if (acc + hist[i] >= need) {
-                out3[0] = i;
-                out3[1] = static_cast<int>(acc);
-                out3[2] = static_cast<int>(hist[i]);
-                break;
-            }
-            acc += hist[i];
-        }
-    }
-    __syncthreads();
-    tb = out3[0];
-    above = static_cast<uint32_t>(out3[1]);
-    at = static_cast<uint32_t>(out3[2]);
-    __syncthreads();
-}
-
-// Append `val` to list[ctr++] for every lane with pred (one atomic per wave).
-__device__ inline void wave_append(bool pred, u64 val, uint32_t* ctr, u64* list, uint32_t cap) {
-    const u64 mask = __ballot(pred);
-    if (mask == 0) return;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int leader = __ffsll(static_cast<long long>(mask)) - 1;
-    uint32_t base = 0;
-    if (lane == leader) base = atomicAdd(ctr, static_cast<uint32_t>(__popcll(mask)));
-    base = __shfl(base, leader);
-    if (pred) {
-        const u64 below = lane ? (mask & (~0ull >> (64 - lane))) : 0ull;
-        const uint32_t pos = base + static_cast<uint32_t>(__popcll(below));
-        if (pos < cap) list[pos] = val;
-    }
 }
 
 // Descending bitonic sort of buf[0..n) in LDS (n a power of two).
@@ -168,209 +69,248 @@ __device__ inline int next_pow2(int x) {
     return p;
 }
 
-// ---- kernels -------------------------------------------------------------------
-
-__global__ __launch_bounds__(kFilterThreads) void k_topk_clear(void* ws, int rows, int n, int k) {
-    RowWs w = row_ws(ws, blockIdx.x, rows, n, k);
-    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) w.hist[i] = 0;
-    if (threadIdx.x < 4) w.ctr[threadIdx.x] = 0;
-}
-
-__global__ __launch_bounds__(kFilterThreads) void k_topk_hist(TopkArgs a) {
-    __shared__ uint32_t lh[kHistBins];
-    const int row = blockIdx.y;
-    const float* s = score_row(a, row);
-    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lh[i] = 0;
-    __syncthreads();
-    const long long beg = static_cast<long long>(blockIdx.x) * kFilterChunk;
-    const long long end = min(beg + kFilterChunk, static_cast<long long>(a.n));
-    for (long long i = beg + threadIdx.x; i < end; i += blockDim.x) {
-        const float x = s[i];
-        const uint32_t key = score_key(x);
-        if (key_valid(key, x)) atomicAdd(&lh[key >> (32 - kHistBits)], 1u);
-    }
-    __syncthreads();
-    RowWs w = row_ws(a.ws, row, a.batch * a.t, a.n, a.k);
-    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x)
-        if (lh[i]) atomicAdd(&w.hist[i], lh[i]);
-}
-
-__global__ __launch_bounds__(kFilterThreads) void k_topk_filter(TopkArgs a) {
-    __shared__ uint32_t lh[kHistBins];
-    __shared__ uint32_t scratch[kFilterThreads];
-    __shared__ int res[3];
-    const int row = blockIdx.y;
-    RowWs w = row_ws(a.ws, row, a.batch * a.t, a.n, a.k);
-    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lh[i] = w.hist[i];
-    __syncthreads();
-    int tb;
-    uint32_t above, at;
-    find_threshold(lh, kHistBins, static_cast<uint32_t>(a.k), scratch, res, tb, above, at);
-    const float* s = score_row(a, row);
-    const uint32_t cap = static_cast<uint32_t>(cand_cap(a.n));
-    const long long beg = static_cast<long long>(blockIdx.x) * kFilterChunk;
-    const long long end = min(beg + kFilterChunk, static_cast<long long>(a.n));
-    for (long long base = beg; base < end; base += blockDim.x) {
-        const long long i = base + threadIdx.x;
-        bool sure = false, cand = false;
-        u64 c = 0;
-        if (i < end) {
-            const float x = s[i];
-            const uint32_t key = score_key(x);
-            if (key_valid(key, x)) {
-                const int bin = static_cast<int>(key >> (32 - kHistBits));
-                sure = bin > tb;
-                cand = bin == tb;
-                c = composite(key, static_cast<uint32_t>(i));
-            }
-        }
-        wave_append(sure, c, &w.ctr[0], w.sure, static_cast<uint32_t>(a.k));
-        wave_append(cand, c, &w.ctr[1], w.cand, cap);
-    }
-}
-
-// Source of candidates for the refinement: a list of composites, or the
-// score row itself restricted to keys whose top 12 bits equal the first
-// threshold bin.
-struct Source {
-    const u64* list;
-    const float* row;
-    long long len;
-    uint32_t bin12;
-};
-
-__device__ inline bool source_get(const Source& src, long long i, u64& c) {
-    if (src.list) {
-        c = src.list[i];
-        return true;
-    }
-    const float x = src.row[i];
+// Source of elements for the exact path: the score row (valid entries whose
+// key's top 12 bits equal bin12, or all valid entries when bin12 < 0).
+__device__ inline bool row_get(const float* row, long long i, int bin12, u64& c) {
+    const float x = row[i];
     const uint32_t key = score_key(x);
-    if (!key_valid(key, x) || (key >> (32 - kHistBits)) != src.bin12) return false;
+    if (!key_valid(key, x)) return false;
+    if (bin12 >= 0 && static_cast<int>(key >> (32 - kHistBits)) != bin12) return false;
     c = composite(key, static_cast<uint32_t>(i));
     return true;
 }
 
-__global__ __launch_bounds__(kFinalThreads) void k_topk_final(TopkArgs a) {
-    __shared__ u64 sel[kTopkMaxK];
-    __shared__ u64 pool[kCandLds];  // candidates; doubles as histogram space
-    __shared__ uint32_t scratch[kFinalThreads];
-    __shared__ int res[3];
-    __shared__ uint32_t n_sel, n_pool;
-    uint32_t* hist = reinterpret_cast<uint32_t*>(pool);
+struct FinalSmem {
+    u64 sel[kTopkMaxK];        // winners (unordered until the final sort)
+    u64 pool[kUnionCap];       // candidates (fast path: the union; exact path: the threshold bin)
+    uint32_t hist[kHistBins];
+    uint32_t n_sel, n_pool, flag;
+    u64 maxdrop;
+};
 
-    const int row = blockIdx.x;
-    RowWs w = row_ws(a.ws, row, a.batch * a.t, a.n, a.k);
-    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) hist[i] = w.hist[i];
+__device__ inline void pool_select(FinalSmem& sm, uint32_t np, uint32_t need, int pb) {
+    lds_select(sm.pool, np, need, pb, 1024, pb == 0 ? kHistBits : 8, sm.sel, &sm.n_sel, &sm.n_pool, sm.hist);
+}
+
+// Exact top-k of one score row by one workgroup.  Returns k_eff.
+__device__ uint32_t exact_row_topk(FinalSmem& sm, const float* row, int n, int k) {
+    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) sm.hist[i] = 0;
+    if (threadIdx.x == 0) { sm.n_sel = 0; sm.n_pool = 0; }
+    __syncthreads();
+    for (long long i = threadIdx.x; i < n; i += blockDim.x) {
+        const float x = row[i];
+        const uint32_t key = score_key(x);
+        if (key_valid(key, x)) atomicAdd(&sm.hist[key >> (32 - kHistBits)], 1u);
+    }
     __syncthreads();
     int tb;
-    uint32_t above, at;
-    find_threshold(hist, kHistBins, static_cast<uint32_t>(a.k), scratch, res, tb, above, at);
-    const uint32_t k_eff = tb < 0 ? above : static_cast<uint32_t>(a.k);
-    const uint32_t n_sure = min(w.ctr[0], k_eff);
-    const uint32_t n_cand = w.ctr[1];
-    for (uint32_t i = threadIdx.x; i < n_sure; i += blockDim.x) sel[i] = w.sure[i];
-    if (threadIdx.x == 0) { n_sel = n_sure; n_pool = 0; }
-    __syncthreads();
-
-    uint32_t need = k_eff - n_sure;  // > 0 only if bin tb holds the rest
-    if (need > 0) {
-        const uint32_t cap = static_cast<uint32_t>(cand_cap(a.n));
-        Source src;
-        src.list = nullptr;
-        src.row = score_row(a, row);
-        src.len = a.n;
-        src.bin12 = static_cast<uint32_t>(tb);
-        if (n_cand <= cap) { src.list = w.cand; src.len = n_cand; }
-        bool done = false;
-        if (n_cand <= kCandLds) {
-            for (uint32_t i = threadIdx.x; i < n_cand; i += blockDim.x) pool[i] = w.cand[i];
-            if (threadIdx.x == 0) n_pool = n_cand;
-            __syncthreads();
-            done = true;
-        }
-        // Radix refinement over the 64-bit composite: after the 12-bit key
-        // digit, 10-bit digits until the remaining candidates fit in LDS.
-        u64 prefix = static_cast<u64>(tb);
-        int pb = kHistBits;
-        while (!done) {
-            const int db = min(kRefineBits, 64 - pb);
-            const int nb = 1 << db;
-            for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[i] = 0;
-            __syncthreads();
-            for (long long i = threadIdx.x; i < src.len; i += blockDim.x) {
-                u64 c;
-                if (source_get(src, i, c) && (c >> (64 - pb)) == prefix)
-                    atomicAdd(&hist[(c >> (64 - pb - db)) & (nb - 1)], 1u);
-            }
-            __syncthreads();
-            int td;
-            uint32_t ab, at2;
-            find_threshold(hist, nb, need, scratch, res, td, ab, at2);
-            const bool fits = at2 <= kCandLds;
-            __syncthreads();  // hist (aliasing pool) is dead from here on
-            for (long long i = threadIdx.x; i < src.len; i += blockDim.x) {
-                u64 c;
-                if (source_get(src, i, c) && (c >> (64 - pb)) == prefix) {
-                    const int dg = static_cast<int>((c >> (64 - pb - db)) & (nb - 1));
-                    if (dg > td) sel[atomicAdd(&n_sel, 1u)] = c;
-                    else if (dg == td && fits) pool[atomicAdd(&n_pool, 1u)] = c;
-                }
-            }
-            __syncthreads();
-            need -= ab;
-            prefix = (prefix << db) | static_cast<u64>(td);
-            pb += db;
-            done = fits;
-        }
-        // best `need` of the pooled candidates
-        const int np = static_cast<int>(n_pool);
-        const int p2 = next_pow2(np > 1 ? np : 1);
-        for (int i = np + threadIdx.x; i < p2; i += blockDim.x) pool[i] = 0;
-        __syncthreads();
-        bitonic_desc(pool, p2);
-        const uint32_t base = n_sel;
-        for (uint32_t i = threadIdx.x; i < need; i += blockDim.x) sel[base + i] = pool[i];
-        __syncthreads();
+    uint32_t above, at, total;
+    block_threshold(sm.hist, kHistBins, static_cast<uint32_t>(k), tb, above, at, total);
+    const uint32_t k_eff = tb < 0 ? total : static_cast<uint32_t>(k);
+    const bool pool_fits = at <= kPool;
+    for (long long base = 0; base < n; base += blockDim.x) {
+        const long long i = base + threadIdx.x;
+        u64 c = 0;
+        int bin = -2;
+        if (i < n && row_get(row, i, -1, c)) bin = static_cast<int>(c >> (64 - kHistBits));
+        const uint32_t ps = wave_append_pos(bin > tb, &sm.n_sel);
+        if (bin > tb) sm.sel[ps] = c;
+        const uint32_t pp = wave_append_pos(bin == tb && pool_fits, &sm.n_pool);
+        if (bin == tb && pool_fits) sm.pool[pp] = c;
     }
+    __syncthreads();
+    if (tb < 0) return k_eff;
+    uint32_t need = k_eff - above;
+    u64 prefix = static_cast<u64>(tb);
+    int pb = kHistBits;
+    // the threshold bin overflowed the pool: more digits over the row
+    while (!pool_fits || sm.n_pool > kPool) {
+        const int db = min(kRefineBits, 64 - pb);
+        const int nb = 1 << db;
+        for (int i = threadIdx.x; i < nb; i += blockDim.x) sm.hist[i] = 0;
+        __syncthreads();
+        for (long long i = threadIdx.x; i < n; i += blockDim.x) {
+            u64 c;
+            if (row_get(row, i, tb, c) && (c >> (64 - pb)) == prefix)
+                atomicAdd(&sm.hist[(c >> (64 - pb - db)) & (nb - 1)], 1u);
+        }
+        __syncthreads();
+        int td;
+        uint32_t ab, at2, tot;
+        block_threshold(sm.hist, nb, need, td, ab, at2, tot);
+        const bool fits = at2 <= kPool;
+        if (threadIdx.x == 0) sm.n_pool = 0;
+        __syncthreads();
+        for (long long base = 0; base < n; base += blockDim.x) {
+            const long long i = base + threadIdx.x;
+            u64 c = 0;
+            int dg = -2;
+            if (i < n && row_get(row, i, tb, c) && (c >> (64 - pb)) == prefix)
+                dg = static_cast<int>((c >> (64 - pb - db)) & (nb - 1));
+            const uint32_t ps = wave_append_pos(dg > td, &sm.n_sel);
+            if (dg > td) sm.sel[ps] = c;
+            const uint32_t pp = wave_append_pos(dg == td && fits, &sm.n_pool);
+            if (dg == td && fits) sm.pool[pp] = c;
+        }
+        __syncthreads();
+        need -= ab;
+        prefix = (prefix << db) | static_cast<u64>(static_cast<uint32_t>(td));
+        pb += db;
+        if (fits) break;
+    }
+    pool_select(sm, sm.n_pool, need, pb);
+    return k_eff;
+}
 
+// Fast path: top-k of the union of per-slot candidates, with the containment
+// check.  Returns false if the union cannot prove the answer.
+__device__ bool union_topk(FinalSmem& sm, const CandArgs& c, int row, int k) {
+    const int slots = c.slots;
+    const int m1 = c.m + 1;
+    const u64* lists = c.lists + static_cast<long long>(row) * slots * m1;
+    if (threadIdx.x == 0) { sm.n_pool = 0; sm.n_sel = 0; sm.maxdrop = 0; sm.flag = 0; }
+    __syncthreads();
+    // kept entries (first m of every slot) into the pool; the (m+1)-th of each
+    // slot is the largest composite that slot dropped.  Loads are batched so
+    // their latencies overlap.
+    u64 mine = 0;
+    const int total = slots * m1;
+    constexpr int kBatch = 8;
+    for (int base = 0; base < total; base += blockDim.x * kBatch) {
+        u64 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = base + u * blockDim.x + threadIdx.x;
+            v[u] = i < total ? lists[i] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = base + u * blockDim.x + threadIdx.x;
+            const bool drop = i < total && i % m1 == c.m;
+            if (drop) mine = v[u] > mine ? v[u] : mine;
+            const bool keep = !drop && v[u] != 0;
+            const uint32_t p = wave_append_pos(keep, &sm.n_pool);
+            if (keep && p < kUnionCap) sm.pool[p] = v[u];
+        }
+    }
+    // block max of the dropped composites
+    for (int o = 32; o > 0; o >>= 1) {
+        const u64 other = __shfl_xor(mine, o);
+        mine = other > mine ? other : mine;
+    }
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) atomicMax(&sm.maxdrop, mine);
+    __syncthreads();
+    const uint32_t np = sm.n_pool;
+    if (np > kUnionCap) return false;
+    const u64 maxdrop = sm.maxdrop;
+    if (np < static_cast<uint32_t>(k)) {
+        // fewer valid candidates than k: exact only if no slot dropped anything valid
+        if (maxdrop != 0) return false;
+        for (uint32_t i = threadIdx.x; i < np; i += blockDim.x) sm.sel[i] = sm.pool[i];
+        __syncthreads();
+        if (threadIdx.x == 0) sm.n_sel = np;
+        __syncthreads();
+        return true;
+    }
+    pool_select(sm, np, static_cast<uint32_t>(k), 0);
+    // containment: the k-th pick must beat everything any slot dropped
+    u64 kmin = ~0ull;
+    for (int i = threadIdx.x; i < k; i += blockDim.x) kmin = sm.sel[i] < kmin ? sm.sel[i] : kmin;
+    for (int o = 32; o > 0; o >>= 1) {
+        const u64 other = __shfl_xor(kmin, o);
+        kmin = other < kmin ? other : kmin;
+    }
+    if ((threadIdx.x & (kWave - 1)) == 0 && kmin <= maxdrop) atomicOr(&sm.flag, 1u);
+    __syncthreads();
+    return sm.flag == 0;
+}
+
+__global__ __launch_bounds__(kFinalThreads) void k_topk_final(TopkArgs a, CandArgs c) {
+    __shared__ FinalSmem sm;
+    const int row = blockIdx.x;
+    bool done = false;
+    uint32_t k_eff = 0;
+    if (c.lists) {
+        done = union_topk(sm, c, row, a.k);
+        if (done) k_eff = sm.n_sel;
+    }
+    if (!done) k_eff = exact_row_topk(sm, score_row(a, row), a.n, a.k);
     // final order of the k_eff winners
     const int ns = static_cast<int>(k_eff);
     const int p2 = next_pow2(ns > 1 ? ns : 1);
-    for (int i = ns + threadIdx.x; i < p2; i += blockDim.x) sel[i] = 0;
+    for (int i = ns + threadIdx.x; i < p2; i += blockDim.x) sm.sel[i] = 0;
     __syncthreads();
-    bitonic_desc(sel, p2);
+    bitonic_desc(sm.sel, p2);
     const int b = row / a.t;
     const int tt = row - b * a.t;
     int* out = a.idx + (static_cast<long long>(b) * a.t + tt) * a.k;
-    for (int j = threadIdx.x; j < a.k; j += blockDim.x)
-        out[j] = j < ns ? composite_index(sel[j]) : -1;
+    for (int j = threadIdx.x; j < a.k; j += blockDim.x) out[j] = j < ns ? composite_index(sm.sel[j]) : -1;
     if (a.count && threadIdx.x == 0) a.count[static_cast<long long>(b) * a.t + tt] = ns;
+}
+
+// Standalone candidate producer: each workgroup keeps the top m+1 of its
+// chunk of scores (the same per-slot lists the score kernel writes).
+__global__ __launch_bounds__(kCandThreads) void k_topk_cands(TopkArgs a, CandArgs c) {
+    __shared__ u64 vals[kCandChunk];
+    __shared__ CandSmem cs;
+    const int row = blockIdx.y;
+    const float* s = score_row(a, row);
+    const long long beg = static_cast<long long>(blockIdx.x) * kCandChunk;
+    constexpr int kPer = kCandChunk / kCandThreads;
+    float x[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const long long i = beg + u * kCandThreads + threadIdx.x;
+        x[u] = i < a.n ? s[i] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const long long i = beg + u * kCandThreads + threadIdx.x;
+        const uint32_t key = score_key(x[u]);
+        vals[u * kCandThreads + threadIdx.x] = key_valid(key, x[u]) ? composite(key, static_cast<uint32_t>(i)) : 0ull;
+    }
+    __syncthreads();
+    block_top_m1(vals, kCandChunk, c.m + 1, c.lists + (static_cast<long long>(row) * c.slots + blockIdx.x) * (c.m + 1), cs);
 }
 
 }  // namespace
 
-size_t topk_workspace_bytes(int rows, int n, int k) { return ws_layout(rows, n, k).total; }
-
-uint32_t* topk_ws_hist(void* ws) { return static_cast<uint32_t*>(ws); }
-
-hipError_t launch_topk_ws_clear(void* ws, int rows, int n, int k, hipStream_t s) {
-    if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_topk_clear, dim3(rows), dim3(kFilterThreads), 0, s, ws, rows, n, k);
-    return hipGetLastError();
+int topk_cand_m(int n, int k, int keys_per_slot) {
+    // slots hold m + 1 entries; m covers the expected share of the top k of a
+    // slot plus six standard deviations (the final kernel proves containment
+    // and falls back to the exact path if a slot held more)
+    if (n <= 0 || keys_per_slot <= 0) return -1;
+    const double e = static_cast<double>(k) * keys_per_slot / n;
+    const int m = static_cast<int>(e + 6.0 * sqrt(e) + 4.0 + 0.999);
+    return m + 1 <= kMaxCandM1 ? m : -1;
 }
 
-hipError_t launch_topk(const TopkArgs& a, bool hist_ready, hipStream_t s) {
+size_t topk_workspace_bytes(int rows, int n, int k) {
+    // per-slot candidate lists of the standalone producer
+    const int slots = n > 0 ? (n + kCandChunk - 1) / kCandChunk : 1;
+    const int m = topk_cand_m(n, k, kCandChunk);
+    return align256(static_cast<size_t>(rows) * slots * (m > 0 ? m + 1 : 1) * sizeof(u64));
+}
+
+hipError_t launch_topk(const TopkArgs& a, const CandArgs* cands, hipStream_t s) {
     const int rows = a.batch * a.t;
     if (rows == 0) return hipSuccess;
-    const int chunks = a.n > 0 ? (a.n + kFilterChunk - 1) / kFilterChunk : 0;
-    if (!hist_ready) {
-        hipLaunchKernelGGL(k_topk_clear, dim3(rows), dim3(kFilterThreads), 0, s, a.ws, rows, a.n, a.k);
-        if (chunks)
-            hipLaunchKernelGGL(k_topk_hist, dim3(chunks, rows), dim3(kFilterThreads), 0, s, a);
+    CandArgs c{};
+    if (cands) {
+        c = *cands;
+    } else if (a.n > 2 * kCandChunk) {
+        // standalone: produce per-chunk candidates when the row is long
+        const int slots = (a.n + kCandChunk - 1) / kCandChunk;
+        const int m = topk_cand_m(a.n, a.k, kCandChunk);
+        if (m > 0) {
+            c.lists = static_cast<u64*>(a.ws);
+            c.slots = slots;
+            c.m = m;
+            hipLaunchKernelGGL(k_topk_cands, dim3(slots, rows), dim3(kCandThreads), 0, s, a, c);
+        }
     }
-    if (chunks) hipLaunchKernelGGL(k_topk_filter, dim3(chunks, rows), dim3(kFilterThreads), 0, s, a);
-    hipLaunchKernelGGL(k_topk_final, dim3(rows), dim3(kFinalThreads), 0, s, a);
+    hipLaunchKernelGGL(k_topk_final, dim3(rows), dim3(kFinalThreads), 0, s, a, c);
     return hipGetLastError();
 }
 
