@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial_bf16(AttnArgs a, 
     for (int r = 0; r < 4; ++r) {
         float v = x[r];
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+        for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, row16_xor(v, o));
         mx[r] = v;
     }
     if (li == 0)
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial_bf16(AttnArgs a, 
         else if (my_row < R) pl[hh * kPPitch + my_row] = 0;
         float v = p[r];
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+        for (int o = 1; o < 16; o <<= 1) v += row16_xor(v, o);
         if (li == 0) wsum[wv][hh] = has_tile ? v : 0.f;
         mx[r] = M;
     }

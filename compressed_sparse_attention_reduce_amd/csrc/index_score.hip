@@ -17,10 +17,13 @@
 //   * the epilogue applies ReLU and the head weights in registers (each lane
 //     holds 16 heads of one key) and finishes the head sum with two lane
 //     swaps; 16 scores leave per tile as one 64 B store;
-//   * with candidate lists the kernel also keeps its scores as unique
-//     (score, index) composites in LDS and, at the end, writes the workgroup's
-//     top m + 1 to its private slot; the top-k kernel merges those slots (no
-//     cross-workgroup atomics or fences, which serialise on this chip).
+//   * with candidate lists every lane also keeps a short sorted list of its
+//     best (score, index) composites in registers (lane group g takes the
+//     keys of every fourth tile); at the end the waves extract their top m
+//     with wave-wide exchanges, merge by rank, and the workgroup writes its
+//     top m plus a bound of the rest to its private slot; the top-k kernel
+//     merges those slots (no cross-workgroup atomics or fences, which
+//     serialise on this chip).
 #include "common.h"
 #include "kernels.h"
 #include "topk_common.h"
@@ -38,14 +41,14 @@ constexpr int kSteps = kDi / 32;   // k-steps of the 16x16x32 MFMA
 constexpr int kMTiles = kHeads / 16;
 constexpr int kRing = 4;           // key tiles in flight per wave
 constexpr int kQPitch = kDi + 8;   // LDS row pitch of the staged query (bank spread)
-constexpr int kMaxTilesPerWave = 32;                  // with candidates: LDS holds every score of the workgroup
-constexpr int kWgKeys = kMaxTilesPerWave * kWavesPerWg * kTileKeys;
+constexpr int kMaxTilesPerWave = 32;  // with candidates: at most 8 keys per lane list
+constexpr int kLaneTop = 4;           // composites a lane keeps
+static_assert(kRing % 4 == 0, "ring slot i feeds the lists of lane group i % 4");
 
 template <bool kCands>
 __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs a, int tiles_per_row) {
     __shared__ __attribute__((aligned(16))) uint16_t qs[kHeads * kQPitch];
     __shared__ __attribute__((aligned(16))) float ws[kHeads];
-    __shared__ u64 vals[kCands ? kWgKeys : 1];
     __shared__ CandSmem cs;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
@@ -99,8 +102,6 @@ __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs
     qstage(2, qv2);
     qstage(3, qv3);
     if (threadIdx.x < 16) *reinterpret_cast<float4*>(ws + 4 * threadIdx.x) = wv4;
-    if (kCands)
-        for (int i = threadIdx.x; i < kWgKeys; i += kScoreThreads) vals[i] = 0ull;
     __syncthreads();
     bf16x8 qa[kMTiles][kSteps];
 #pragma unroll
@@ -117,6 +118,10 @@ __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs
 
     float* srow = a.scores + b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s;
     const long long pos = a.q_pos ? static_cast<long long>(a.q_pos[row]) : 0;
+    u64 top[kLaneTop];
+    u64 drop = 0;
+#pragma unroll
+    for (int i = 0; i < kLaneTop; ++i) top[i] = 0;
 
     // 3. stream: consume a tile, refill its ring slot kRing tiles ahead
     for (int j0 = 0; j0 < n_mine; j0 += kRing) {
@@ -138,29 +143,25 @@ __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs
             for (int mt = 0; mt < kMTiles; ++mt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) part += wr[mt][r] * fmaxf(acc[mt][r], 0.f);
-            part += __shfl_xor(part, 16);
-            part += __shfl_xor(part, 32);
+            part += xor_lanes_f32<16>(part);
+            part += xor_lanes_f32<32>(part);
             const int key = (gw + j * waves_per_row) * kTileKeys + li;
-            if (j < n_mine && lg == 0 && key < n) {
-                float sc = part;
-                if (a.q_pos && static_cast<long long>(a.ratio) * key + a.ratio - 1 > pos) sc = -INFINITY;
-                srow[key] = sc;
-                if (kCands) {
-                    const uint32_t kk = score_key(sc);
-                    if (key_valid(kk, sc))
-                        vals[(j * kWavesPerWg + wv) * kTileKeys + li] = composite(kk, static_cast<uint32_t>(key));
-                }
+            const bool live = j < n_mine && key < n;
+            float sc = part;
+            if (a.q_pos && static_cast<long long>(a.ratio) * key + a.ratio - 1 > pos) sc = -INFINITY;
+            if (live && lg == 0) srow[key] = sc;
+            if (kCands) {
+                const uint32_t kk = score_key(sc);
+                const bool mine = live && lg == (i & 3) && key_valid(kk, sc);
+                lane_insert(top, drop, mine ? composite(kk, static_cast<uint32_t>(key)) : 0ull);
             }
         }
     }
 
     if (!kCands) return;
-    // 4. this workgroup's best m + 1 to its candidate slot
-    __syncthreads();
-    const int m1 = a.cands.m + 1;
-    const int nv = ((tiles_per_row + waves_per_row - 1) / waves_per_row) * kWavesPerWg * kTileKeys;
-    block_top_m1(vals, nv < kWgKeys ? nv : kWgKeys, m1,
-                 a.cands.lists + (static_cast<long long>(row) * a.cands.slots + blockIdx.x) * m1, cs);
+    // 4. this workgroup's best m and their bound to its candidate slot
+    block_top_m(top, drop, a.cands.m,
+                a.cands.lists + (static_cast<long long>(row) * a.cands.slots + blockIdx.x) * (a.cands.m + 1), cs);
 }
 
 // float32 path (small correctness workloads): one thread per key, the query

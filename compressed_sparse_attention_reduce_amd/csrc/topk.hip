@@ -14,13 +14,16 @@
 //   * candidates: every producer workgroup (the score kernel's, or
 //     k_topk_cands for a standalone call) writes the top m+1 composites of its
 //     own slice to a private slot of the workspace;
-//   * k_topk_final, one workgroup per row, selects the top k of the union of
-//     the kept m per slot and checks that every slot's (m+1)-th composite
-//     (the largest it dropped) is below the k-th pick, which proves the union
-//     held the true top k.  If the check fails (adversarial ties, or no
-//     candidates were produced) it runs an exact radix select over the whole
-//     row instead: 12-bit key histogram, threshold bin, then further digits of
-//     the composite until the remaining candidates fit in LDS.
+//   * k_topk_final, one workgroup per row, loads the union of the kept m per
+//     slot into registers and keeps only entries above every slot's bound
+//     (entry m + 1 of a slot: at least the largest composite it did not
+//     keep).  If k entries remain they are provably the true top k; they are
+//     selected and sorted in one go (a radix digit placed where they differ,
+//     bin starts giving final positions, ranks inside each bin).  Otherwise
+//     (adversarial ties, or no candidates were produced) it runs an exact
+//     select over the whole row: 12-bit key histogram, threshold bin, further
+//     digits until the remaining candidates fit in LDS, then the same sorted
+//     select over them.
 // Either way the result is exact; only the time differs.
 #include <cmath>
 
@@ -33,11 +36,14 @@ namespace csa {
 namespace {
 
 constexpr int kFinalThreads = 1024;
-constexpr int kUnionCap = 8192;       // candidates of the fast path held in LDS
+constexpr int kUnionRegs = 8;         // union entries per thread of the fast path
 constexpr int kPool = 2048;           // exact-path candidates held in LDS
+constexpr int kPoolRegs = kPool / kFinalThreads;
+constexpr int kSortRegs = kTopkMaxK / kFinalThreads;
 constexpr int kRefineBits = 10;
 constexpr int kCandThreads = 256;
 constexpr int kCandChunk = 2048;      // scores per k_topk_cands workgroup
+constexpr int kCandPer = kCandChunk / kCandThreads;
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -45,28 +51,6 @@ __device__ inline const float* score_row(const TopkArgs& a, int row) {
     const int b = row / a.t;
     const int tt = row - b * a.t;
     return a.scores + b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s;
-}
-
-// Descending bitonic sort of buf[0..n) in LDS (n a power of two).
-__device__ void bitonic_desc(u64* buf, int n) {
-    for (int size = 2; size <= n; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < (n >> 1); i += blockDim.x) {
-                const int p = 2 * i - (i & (stride - 1));
-                const int q = p + stride;
-                const bool desc = (p & size) == 0;
-                const u64 x = buf[p], y = buf[q];
-                if ((x < y) == desc) { buf[p] = y; buf[q] = x; }
-            }
-            __syncthreads();
-        }
-    }
-}
-
-__device__ inline int next_pow2(int x) {
-    int p = 1;
-    while (p < x) p <<= 1;
-    return p;
 }
 
 // Source of elements for the exact path: the score row (valid entries whose
@@ -81,18 +65,38 @@ __device__ inline bool row_get(const float* row, long long i, int bin12, u64& c)
 }
 
 struct FinalSmem {
-    u64 sel[kTopkMaxK];        // winners (unordered until the final sort)
-    u64 pool[kUnionCap];       // candidates (fast path: the union; exact path: the threshold bin)
-    uint32_t hist[kHistBins];
-    uint32_t n_sel, n_pool, flag;
-    u64 maxdrop;
+    u64 sel[kTopkMaxK];                 // winners, sorted at the end
+    u64 pool[kTopkMaxK + kStageCap];    // exact path: the threshold bin; then the sort's staging
+    union {
+        uint32_t hist[kHistBins];       // row histograms of the exact path
+        SortSmem ss;                    // counters of the sorted select (used after them)
+    };
+    u64 wmax[16], wmin[16];
+    uint32_t n_sel, n_pool;
 };
 
-__device__ inline void pool_select(FinalSmem& sm, uint32_t np, uint32_t need, int pb) {
-    lds_select(sm.pool, np, need, pb, 1024, pb == 0 ? kHistBits : 8, sm.sel, &sm.n_sel, &sm.n_pool, sm.hist);
+// The largest and (through complements) the smallest of the threads' a and
+// b over the block, in every thread.
+__device__ inline void block_max2(FinalSmem& sm, u64& a, u64& b) {
+    const int wv = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    a = wave_max_u64(a);
+    b = wave_max_u64(b);
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        sm.wmax[wv] = a;
+        sm.wmin[wv] = b;
+    }
+    __syncthreads();
+    a = 0;
+    b = 0;
+    for (int w = 0; w < nw; ++w) {
+        a = umax64(a, sm.wmax[w]);
+        b = umax64(b, sm.wmin[w]);
+    }
 }
 
-// Exact top-k of one score row by one workgroup.  Returns k_eff.
+// Exact top-k of one score row by one workgroup, sorted into sm.sel.
+// Returns k_eff.
 __device__ uint32_t exact_row_topk(FinalSmem& sm, const float* row, int n, int k) {
     for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) sm.hist[i] = 0;
     if (threadIdx.x == 0) { sm.n_sel = 0; sm.n_pool = 0; }
@@ -106,7 +110,6 @@ __device__ uint32_t exact_row_topk(FinalSmem& sm, const float* row, int n, int k
     int tb;
     uint32_t above, at, total;
     block_threshold(sm.hist, kHistBins, static_cast<uint32_t>(k), tb, above, at, total);
-    const uint32_t k_eff = tb < 0 ? total : static_cast<uint32_t>(k);
     const bool pool_fits = at <= kPool;
     for (long long base = 0; base < n; base += blockDim.x) {
         const long long i = base + threadIdx.x;
@@ -119,129 +122,124 @@ __device__ uint32_t exact_row_topk(FinalSmem& sm, const float* row, int n, int k
         if (bin == tb && pool_fits) sm.pool[pp] = c;
     }
     __syncthreads();
-    if (tb < 0) return k_eff;
-    uint32_t need = k_eff - above;
-    u64 prefix = static_cast<u64>(tb);
-    int pb = kHistBits;
-    // the threshold bin overflowed the pool: more digits over the row
-    while (!pool_fits || sm.n_pool > kPool) {
-        const int db = min(kRefineBits, 64 - pb);
-        const int nb = 1 << db;
-        for (int i = threadIdx.x; i < nb; i += blockDim.x) sm.hist[i] = 0;
-        __syncthreads();
-        for (long long i = threadIdx.x; i < n; i += blockDim.x) {
-            u64 c;
-            if (row_get(row, i, tb, c) && (c >> (64 - pb)) == prefix)
-                atomicAdd(&sm.hist[(c >> (64 - pb - db)) & (nb - 1)], 1u);
+    if (tb >= 0) {
+        uint32_t need = static_cast<uint32_t>(k) - above;
+        u64 prefix = static_cast<u64>(tb);
+        int pb = kHistBits;
+        // the threshold bin overflowed the pool: more digits over the row
+        while (!pool_fits || sm.n_pool > kPool) {
+            const int db = min(kRefineBits, 64 - pb);
+            const int nb = 1 << db;
+            for (int i = threadIdx.x; i < nb; i += blockDim.x) sm.hist[i] = 0;
+            __syncthreads();
+            for (long long i = threadIdx.x; i < n; i += blockDim.x) {
+                u64 c;
+                if (row_get(row, i, tb, c) && (c >> (64 - pb)) == prefix)
+                    atomicAdd(&sm.hist[(c >> (64 - pb - db)) & (nb - 1)], 1u);
+            }
+            __syncthreads();
+            int td;
+            uint32_t ab, at2, tot;
+            block_threshold(sm.hist, nb, need, td, ab, at2, tot);
+            const bool fits = at2 <= kPool;
+            if (threadIdx.x == 0) sm.n_pool = 0;
+            __syncthreads();
+            for (long long base = 0; base < n; base += blockDim.x) {
+                const long long i = base + threadIdx.x;
+                u64 c = 0;
+                int dg = -2;
+                if (i < n && row_get(row, i, tb, c) && (c >> (64 - pb)) == prefix)
+                    dg = static_cast<int>((c >> (64 - pb - db)) & (nb - 1));
+                const uint32_t ps = wave_append_pos(dg > td, &sm.n_sel);
+                if (dg > td) sm.sel[ps] = c;
+                const uint32_t pp = wave_append_pos(dg == td && fits, &sm.n_pool);
+                if (dg == td && fits) sm.pool[pp] = c;
+            }
+            __syncthreads();
+            need -= ab;
+            prefix = (prefix << db) | static_cast<u64>(static_cast<uint32_t>(td));
+            pb += db;
+            if (fits) break;
         }
-        __syncthreads();
-        int td;
-        uint32_t ab, at2, tot;
-        block_threshold(sm.hist, nb, need, td, ab, at2, tot);
-        const bool fits = at2 <= kPool;
-        if (threadIdx.x == 0) sm.n_pool = 0;
-        __syncthreads();
-        for (long long base = 0; base < n; base += blockDim.x) {
-            const long long i = base + threadIdx.x;
-            u64 c = 0;
-            int dg = -2;
-            if (i < n && row_get(row, i, tb, c) && (c >> (64 - pb)) == prefix)
-                dg = static_cast<int>((c >> (64 - pb - db)) & (nb - 1));
-            const uint32_t ps = wave_append_pos(dg > td, &sm.n_sel);
-            if (dg > td) sm.sel[ps] = c;
-            const uint32_t pp = wave_append_pos(dg == td && fits, &sm.n_pool);
-            if (dg == td && fits) sm.pool[pp] = c;
-        }
-        __syncthreads();
-        need -= ab;
-        prefix = (prefix << db) | static_cast<u64>(static_cast<uint32_t>(td));
-        pb += db;
-        if (fits) break;
     }
-    pool_select(sm, sm.n_pool, need, pb);
-    return k_eff;
+    // every candidate (the picks above the threshold and the threshold bin's
+    // entries, at most kTopkMaxK + kPool) to registers, then the sorted select
+    const uint32_t ns = sm.n_sel;
+    const uint32_t np = tb >= 0 ? sm.n_pool : 0u;
+    u64 v[kPoolRegs + kSortRegs];
+#pragma unroll
+    for (int u = 0; u < kPoolRegs; ++u) {
+        const uint32_t i = threadIdx.x + u * kFinalThreads;
+        v[u] = i < np ? sm.pool[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kSortRegs; ++u) {
+        const uint32_t i = threadIdx.x + u * kFinalThreads;
+        v[kPoolRegs + u] = i < ns ? sm.sel[i] : 0ull;
+    }
+    // the candidates share the top bits where their largest and smallest agree
+    u64 hi = 0, lo_c = 0;
+#pragma unroll
+    for (int u = 0; u < kPoolRegs + kSortRegs; ++u) {
+        hi = umax64(hi, v[u]);
+        lo_c = umax64(lo_c, v[u] ? ~v[u] : 0ull);
+    }
+    block_max2(sm, hi, lo_c);  // its barrier also ends every read of sel and pool above
+    const int pb = hi == 0 ? 0 : __clzll(static_cast<long long>(hi ^ ~lo_c));
+    return select_sorted(v, static_cast<uint32_t>(k), pb < 64 ? pb : 63, sm.sel, sm.pool, sm.ss);
 }
 
-// Fast path: top-k of the union of per-slot candidates, with the containment
-// check.  Returns false if the union cannot prove the answer.
-__device__ bool union_topk(FinalSmem& sm, const CandArgs& c, int row, int k) {
-    const int slots = c.slots;
+// Fast path: top-k of the union of per-slot candidates, sorted into sm.sel.
+// Returns false if the union cannot prove the answer.
+__device__ bool union_topk(FinalSmem& sm, const CandArgs& c, int row, int k, uint32_t& k_eff) {
     const int m1 = c.m + 1;
-    const u64* lists = c.lists + static_cast<long long>(row) * slots * m1;
-    if (threadIdx.x == 0) { sm.n_pool = 0; sm.n_sel = 0; sm.maxdrop = 0; sm.flag = 0; }
-    __syncthreads();
-    // kept entries (first m of every slot) into the pool; the (m+1)-th of each
-    // slot is the largest composite that slot dropped.  Loads are batched so
-    // their latencies overlap.
-    u64 mine = 0;
-    const int total = slots * m1;
-    constexpr int kBatch = 8;
-    for (int base = 0; base < total; base += blockDim.x * kBatch) {
-        u64 v[kBatch];
+    const int total = c.slots * m1;
+    if (total > kUnionRegs * kFinalThreads) return false;
+    const u64* lists = c.lists + static_cast<long long>(row) * total;
+    // kept entries (first m of every slot) stay in registers; entry m of each
+    // slot bounds what that slot did not keep
+    u64 v[kUnionRegs];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int i = base + u * blockDim.x + threadIdx.x;
-            v[u] = i < total ? lists[i] : 0ull;
-        }
+    for (int u = 0; u < kUnionRegs; ++u) {
+        const int i = threadIdx.x + u * kFinalThreads;
+        v[u] = i < total ? lists[i] : 0ull;
+    }
+    u64 maxdrop = 0, mx = 0;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int i = base + u * blockDim.x + threadIdx.x;
-            const bool drop = i < total && i % m1 == c.m;
-            if (drop) mine = v[u] > mine ? v[u] : mine;
-            const bool keep = !drop && v[u] != 0;
-            const uint32_t p = wave_append_pos(keep, &sm.n_pool);
-            if (keep && p < kUnionCap) sm.pool[p] = v[u];
+    for (int u = 0; u < kUnionRegs; ++u) {
+        const int i = threadIdx.x + u * kFinalThreads;
+        if (i < total && i % m1 == c.m) {
+            maxdrop = umax64(maxdrop, v[u]);
+            v[u] = 0;
         }
+        mx = umax64(mx, v[u]);
     }
-    // block max of the dropped composites
-    for (int o = 32; o > 0; o >>= 1) {
-        const u64 other = __shfl_xor(mine, o);
-        mine = other > mine ? other : mine;
+    block_max2(sm, maxdrop, mx);
+    // the top k must all beat every slot's bound to be proven: only such
+    // entries take part (they share the top bits where maxdrop and mx agree)
+#pragma unroll
+    for (int u = 0; u < kUnionRegs; ++u) v[u] = v[u] > maxdrop ? v[u] : 0ull;
+    uint32_t ns = 0;
+    if (mx > maxdrop) {
+        const int pb = __clzll(static_cast<long long>(mx ^ maxdrop));
+        ns = select_sorted(v, static_cast<uint32_t>(k), pb, sm.sel, sm.pool, sm.ss);
     }
-    __syncthreads();
-    if ((threadIdx.x & (kWave - 1)) == 0) atomicMax(&sm.maxdrop, mine);
-    __syncthreads();
-    const uint32_t np = sm.n_pool;
-    if (np > kUnionCap) return false;
-    const u64 maxdrop = sm.maxdrop;
-    if (np < static_cast<uint32_t>(k)) {
-        // fewer valid candidates than k: exact only if no slot dropped anything valid
-        if (maxdrop != 0) return false;
-        for (uint32_t i = threadIdx.x; i < np; i += blockDim.x) sm.sel[i] = sm.pool[i];
-        __syncthreads();
-        if (threadIdx.x == 0) sm.n_sel = np;
-        __syncthreads();
-        return true;
-    }
-    pool_select(sm, np, static_cast<uint32_t>(k), 0);
-    // containment: the k-th pick must beat everything any slot dropped
-    u64 kmin = ~0ull;
-    for (int i = threadIdx.x; i < k; i += blockDim.x) kmin = sm.sel[i] < kmin ? sm.sel[i] : kmin;
-    for (int o = 32; o > 0; o >>= 1) {
-        const u64 other = __shfl_xor(kmin, o);
-        kmin = other < kmin ? other : kmin;
-    }
-    if ((threadIdx.x & (kWave - 1)) == 0 && kmin <= maxdrop) atomicOr(&sm.flag, 1u);
-    __syncthreads();
-    return sm.flag == 0;
+    // fewer than k proven entries: exact only if no slot left anything valid out
+    if (ns < static_cast<uint32_t>(k) && maxdrop != 0) return false;
+    k_eff = ns;
+    return true;
 }
 
 __global__ __launch_bounds__(kFinalThreads) void k_topk_final(TopkArgs a, CandArgs c) {
     __shared__ FinalSmem sm;
     const int row = blockIdx.x;
-    bool done = false;
     uint32_t k_eff = 0;
-    if (c.lists) {
-        done = union_topk(sm, c, row, a.k);
-        if (done) k_eff = sm.n_sel;
+    const bool done = c.lists && union_topk(sm, c, row, a.k, k_eff);
+    if (!done) {
+        __syncthreads();  // the fast path's reads of sm are over
+        k_eff = exact_row_topk(sm, score_row(a, row), a.n, a.k);
     }
-    if (!done) k_eff = exact_row_topk(sm, score_row(a, row), a.n, a.k);
-    // final order of the k_eff winners
     const int ns = static_cast<int>(k_eff);
-    const int p2 = next_pow2(ns > 1 ? ns : 1);
-    for (int i = ns + threadIdx.x; i < p2; i += blockDim.x) sm.sel[i] = 0;
-    __syncthreads();
-    bitonic_desc(sm.sel, p2);
     const int b = row / a.t;
     const int tt = row - b * a.t;
     int* out = a.idx + (static_cast<long long>(b) * a.t + tt) * a.k;
@@ -249,29 +247,31 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(TopkArgs a, CandAr
     if (a.count && threadIdx.x == 0) a.count[static_cast<long long>(b) * a.t + tt] = ns;
 }
 
-// Standalone candidate producer: each workgroup keeps the top m+1 of its
-// chunk of scores (the same per-slot lists the score kernel writes).
+// Standalone candidate producer: each workgroup lists the top m of its chunk
+// of scores plus a bound of the rest (the same per-slot lists the score
+// kernel writes).
 __global__ __launch_bounds__(kCandThreads) void k_topk_cands(TopkArgs a, CandArgs c) {
-    __shared__ u64 vals[kCandChunk];
     __shared__ CandSmem cs;
     const int row = blockIdx.y;
     const float* s = score_row(a, row);
     const long long beg = static_cast<long long>(blockIdx.x) * kCandChunk;
-    constexpr int kPer = kCandChunk / kCandThreads;
-    float x[kPer];
+    float x[kCandPer];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
+    for (int u = 0; u < kCandPer; ++u) {
         const long long i = beg + u * kCandThreads + threadIdx.x;
         x[u] = i < a.n ? s[i] : -INFINITY;
     }
+    u64 top[kCandPer];
+    u64 drop = 0;
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
+    for (int u = 0; u < kCandPer; ++u) top[u] = 0;
+#pragma unroll
+    for (int u = 0; u < kCandPer; ++u) {
         const long long i = beg + u * kCandThreads + threadIdx.x;
         const uint32_t key = score_key(x[u]);
-        vals[u * kCandThreads + threadIdx.x] = key_valid(key, x[u]) ? composite(key, static_cast<uint32_t>(i)) : 0ull;
+        lane_insert(top, drop, key_valid(key, x[u]) ? composite(key, static_cast<uint32_t>(i)) : 0ull);
     }
-    __syncthreads();
-    block_top_m1(vals, kCandChunk, c.m + 1, c.lists + (static_cast<long long>(row) * c.slots + blockIdx.x) * (c.m + 1), cs);
+    block_top_m(top, drop, c.m, c.lists + (static_cast<long long>(row) * c.slots + blockIdx.x) * (c.m + 1), cs);
 }
 
 }  // namespace

@@ -1,5 +1,11 @@
-// Device helpers of the radix top-k, shared by the score kernel (which keeps
-// every workgroup's best candidates) and the top-k kernels.
+// Device helpers of the top-k, shared by the score kernel (which keeps every
+// workgroup's best candidates) and the top-k kernels.
+//
+// Everything here works on unique 64-bit composites (order-preserving score
+// key << 32 | inverted index; zero means "no element"), so a set of the n
+// largest is unique and ties need no special handling.  The helpers are built
+// to keep barriers and LDS round trips few: per-lane sorted lists, wave-wide
+// exchanges through DPP and permlane swaps, register-resident candidate pools.
 #pragma once
 
 #include "common.h"
@@ -9,8 +15,9 @@ namespace csa {
 
 typedef unsigned long long u64;
 
-constexpr int kHistBits = 12;               // first radix digit: top 12 bits of the score key
+constexpr int kHistBits = 12;               // first radix digit over a raw score row
 constexpr int kHistBins = 1 << kHistBits;
+constexpr int kSelBits = 11;                // digits of the register-resident sorted select
 
 // Unique sort key of an element: order-preserving score key, then the
 // inverted index (so equal scores rank the lower index higher).
@@ -19,53 +26,8 @@ __device__ inline u64 composite(uint32_t key, uint32_t idx) {
 }
 __device__ inline int composite_index(u64 c) { return static_cast<int>(0xffffffffu - static_cast<uint32_t>(c)); }
 
-// Block-wide search over a histogram in LDS: the largest bin `tb` with
-// suffix(tb) >= need (suffix(x) = count in bins >= x); above = suffix(tb+1),
-// at = hist[tb], total = suffix(0).  If total < need: tb = -1, above = total.
-// Every thread returns the same values.  Uses its own LDS scratch.
-__device__ inline void block_threshold(const uint32_t* hist, int nbins, uint32_t need, int& tb,
-                                       uint32_t& above, uint32_t& at, uint32_t& total) {
-    __shared__ uint32_t scan[1024];
-    __shared__ uint32_t res[4];
-    const int nt = blockDim.x;
-    const int per = (nbins + nt - 1) / nt;
-    const int lo = threadIdx.x * per;
-    const int hi = min(lo + per, nbins);
-    uint32_t mine = 0;
-    for (int i = lo; i < hi; ++i) mine += hist[i];
-    scan[threadIdx.x] = mine;
-    if (threadIdx.x == 0) { res[0] = 0xffffffffu; res[1] = 0; res[2] = 0; }
-    __syncthreads();
-    for (int off = 1; off < nt; off <<= 1) {  // inclusive suffix scan of the per-thread sums
-        const uint32_t add = (threadIdx.x + off < nt) ? scan[threadIdx.x + off] : 0u;
-        __syncthreads();
-        scan[threadIdx.x] += add;
-        __syncthreads();
-    }
-    const uint32_t incl = scan[threadIdx.x];
-    const uint32_t excl = incl - mine;
-    const uint32_t tot = scan[0];
-    if (tot < need) {
-        if (threadIdx.x == 0) { res[0] = 0xffffffffu; res[1] = tot; res[2] = 0; }
-    } else if (excl < need && incl >= need) {
-        uint32_t acc = excl;
-        for (int i = hi - 1; i >= lo; --i) {
-            if (acc + hist[i] >= need) {
-                res[0] = static_cast<uint32_t>(i);
-                res[1] = acc;
-                res[2] = hist[i];
-                break;
-            }
-            acc += hist[i];
-        }
-    }
-    __syncthreads();
-    tb = static_cast<int>(res[0]);
-    above = res[1];
-    at = res[2];
-    total = tot;
-    __syncthreads();
-}
+__device__ inline u64 umax64(u64 a, u64 b) { return a > b ? a : b; }
+__device__ inline u64 umin64(u64 a, u64 b) { return a < b ? a : b; }
 
 // Position of this lane's entry when the lanes with `pred` append to a list
 // whose length is *ctr: one LDS atomic per wave instead of one per lane (lanes
@@ -78,94 +40,292 @@ __device__ inline uint32_t wave_append_pos(bool pred, uint32_t* ctr) {
     const int leader = __ffsll(static_cast<long long>(mask)) - 1;
     uint32_t base = 0;
     if (lane == leader) base = atomicAdd(ctr, static_cast<uint32_t>(__popcll(mask)));
-    base = __shfl(base, leader);
+    base = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(base), leader));
     const u64 below = lane ? (mask & (~0ull >> (64 - lane))) : 0ull;
     return base + static_cast<uint32_t>(__popcll(below));
 }
 
-// Select the `need` largest composites of pool[0..np) (LDS, unique; zero
-// entries count as the smallest) and append them, in no particular order, to
-// sel[*n_sel ..].  While the pool holds more than rank_max entries it is
-// narrowed by radix digits of the composite below bit 64 - pb (first digit
-// first_bits wide, then 8): entries above the threshold digit are selected,
-// entries on it stay in the pool (compacted in place); the rest are picked by
-// rank counting.  np >= need.  hist: 1 << max(first_bits, 8) uint32 of LDS.
-// Every thread of the block must call it.
-__device__ inline void lds_select(u64* pool, uint32_t np, uint32_t need, int pb, uint32_t rank_max, int first_bits,
-                                  u64* sel, uint32_t* n_sel, uint32_t* n_pool, uint32_t* hist) {
-    int dbits = first_bits;
-    while (np > rank_max && pb < 64) {
-        const int db = min(dbits, 64 - pb);
-        dbits = 8;
-        const int nb = 1 << db;
-        for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[i] = 0;
-        __syncthreads();
-        for (uint32_t i = threadIdx.x; i < np; i += blockDim.x)
-            atomicAdd(&hist[(pool[i] >> (64 - pb - db)) & (nb - 1)], 1u);
-        __syncthreads();
-        int td;
-        uint32_t ab, at, tot;
-        block_threshold(hist, nb, need, td, ab, at, tot);
-        if (threadIdx.x == 0) *n_pool = 0;
-        __syncthreads();
-        for (uint32_t base = 0; base < np; base += blockDim.x) {
-            const uint32_t i = base + threadIdx.x;
-            u64 c = 0;
-            int dg = -1;
-            if (i < np) {
-                c = pool[i];
-                dg = static_cast<int>((c >> (64 - pb - db)) & (nb - 1));
+// Block-wide search over a histogram in LDS: the largest bin tb with
+// suffix(tb) >= need, where suffix(x) counts the entries in bins >= x;
+// above = suffix(tb + 1), at = hist[tb], total = suffix(0).  If total < need:
+// tb = -1 and above = total.  Thread t owns a run of bins counted from the
+// top, so the suffix sums are prefix sums over threads: a butterfly inside
+// each wave, one LDS exchange of the wave totals.  Every thread returns the
+// same values.  At most 16 waves.
+__device__ inline void block_threshold(const uint32_t* hist, int nbins, uint32_t need, int& tb,
+                                       uint32_t& above, uint32_t& at, uint32_t& total) {
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t res[3];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    const int per = (nbins + blockDim.x - 1) / blockDim.x;
+    const int hi = max(nbins - per * static_cast<int>(threadIdx.x), 0);  // bins [lo, hi)
+    const int lo = max(hi - per, 0);
+    uint32_t mine = 0;
+    for (int b = lo; b < hi; ++b) mine += hist[b];
+    // inclusive prefix over the lanes: blocks of 2o lanes merge, the upper half adding the lower's total
+    uint32_t pre = mine, sum = mine;
+#define CSA_SCAN_STEP(o)                                         \
+    {                                                            \
+        const uint32_t other = xor_lanes<o>(sum);                \
+        if (lane & (o)) pre += other;                            \
+        sum += other;                                            \
+    }
+    CSA_SCAN_STEP(1) CSA_SCAN_STEP(2) CSA_SCAN_STEP(4) CSA_SCAN_STEP(8) CSA_SCAN_STEP(16) CSA_SCAN_STEP(32)
+#undef CSA_SCAN_STEP
+    if (lane == 0) wsum[wv] = sum;
+    if (threadIdx.x == 0) { res[0] = 0xffffffffu; res[1] = 0; res[2] = 0; }
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+        const uint32_t x = wsum[w];
+        tot += x;
+        before += w < wv ? x : 0u;
+    }
+    const uint32_t incl = before + pre;  // entries in bins >= lo
+    const uint32_t excl = incl - mine;   // entries in bins >= hi
+    if (tot < need) {
+        if (threadIdx.x == 0) res[1] = tot;
+    } else if (excl < need && incl >= need) {
+        uint32_t acc = excl;
+        for (int b = hi - 1; b >= lo; --b) {
+            if (acc + hist[b] >= need) {
+                res[0] = static_cast<uint32_t>(b);
+                res[1] = acc;
+                res[2] = hist[b];
+                break;
             }
-            __syncthreads();  // this block of the pool is read before compaction writes land in it
-            const uint32_t ps = wave_append_pos(dg > td, n_sel);
-            if (dg > td) sel[ps] = c;
-            const uint32_t pp = wave_append_pos(dg == td, n_pool);
-            if (dg == td) pool[pp] = c;
-            __syncthreads();
+            acc += hist[b];
         }
-        np = *n_pool;
-        need -= ab;
-        pb += db;
-        __syncthreads();
-    }
-    const uint32_t base = *n_sel;
-    // equal (zero) entries share a rank and leave later slots unwritten: those are zero
-    for (uint32_t i = threadIdx.x; i < need; i += blockDim.x) sel[base + i] = 0ull;
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < np; i += blockDim.x) {
-        const u64 c = pool[i];
-        uint32_t rank = 0;
-        for (uint32_t j = 0; j < np; ++j) rank += pool[j] > c ? 1u : 0u;
-        if (rank < need && c != 0) sel[base + rank] = c;
     }
     __syncthreads();
-    if (threadIdx.x == 0) *n_sel = base + need;
+    tb = static_cast<int>(res[0]);
+    above = res[1];
+    at = res[2];
+    total = tot;
     __syncthreads();
 }
 
-// LDS scratch of block_top_m1.
+// ---- per-lane lists and the workgroup candidate list --------------------------------
+
+// Insert c into a lane's descending list; whatever falls off the end raises
+// `drop` (the largest composite this lane discarded).
+template <int L>
+__device__ inline void lane_insert(u64 (&top)[L], u64& drop, u64 c) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const u64 hi = umax64(top[i], c);
+        c = umin64(top[i], c);
+        top[i] = hi;
+    }
+    drop = umax64(drop, c);
+}
+
+// The wave's `cnt` largest listed composites, descending, to out[0..cnt)
+// (LDS, written by lane 0; zero where the wave has fewer).  Returns, in every
+// lane, the largest composite of the wave not extracted (a list's next head
+// or anything a lane dropped), and in *n_out how many nonzero were extracted.
+template <int L>
+__device__ inline u64 wave_extract_top(u64 (&top)[L], u64 drop, int cnt, u64* out, int* n_out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int r = 0;
+    for (; r < cnt; ++r) {
+        const u64 wm = wave_max_u64(top[0]);
+        if (wm == 0) break;  // wave-uniform
+        if (lane == 0) out[r] = wm;
+        if (top[0] == wm) {  // composites are unique: exactly one lane pops its head
+#pragma unroll
+            for (int i = 0; i + 1 < L; ++i) top[i] = top[i + 1];
+            top[L - 1] = 0;
+        }
+    }
+    *n_out = r;
+    for (int j = r + lane; j < cnt; j += kWave) out[j] = 0;
+    return umax64(wave_max_u64(top[0]), wave_max_u64(drop));
+}
+
+// LDS scratch of block_top_m.
 struct CandSmem {
-    uint32_t hist[kHistBins];
-    uint32_t n_sel, n_pool;
-    u64 sel[kMaxCandM1];
+    u64 wtop[16][kMaxCandM1];
+    u64 wbound[16];
+    int wcount[16];
 };
 
-// The m1 largest composites of vals[0..nv) (LDS; zero entries are empty),
-// written sorted descending to out[0..m1), zero padded (nv >= m1; vals is
-// reordered).  Every thread of the block must call it.
-__device__ inline void block_top_m1(u64* vals, int nv, int m1, u64* out, CandSmem& cs) {
-    if (threadIdx.x == 0) { cs.n_sel = 0; cs.n_pool = 0; }
-    __syncthreads();
-    lds_select(vals, static_cast<uint32_t>(nv), static_cast<uint32_t>(m1), 0, 128, kHistBits, cs.sel, &cs.n_sel,
-               &cs.n_pool, cs.hist);
-    // sort the picks by rank (at most kMaxCandM1 of them; empty picks are 0)
-    for (int i = threadIdx.x; i < m1; i += blockDim.x) {
-        const u64 c = cs.sel[i];
-        uint32_t rank = 0;
-        for (int j = 0; j < m1; ++j) rank += (cs.sel[j] > c || (cs.sel[j] == c && j < i)) ? 1u : 0u;
-        out[rank] = c;
+// Workgroup candidate list from the lanes' lists: out[0..m) (global) = the m
+// largest listed composites of the workgroup, descending, zero padded;
+// out[m] = an upper bound of every composite of the workgroup not in
+// out[0..m) (the largest of them, when lanes dropped nothing that matters).
+// m < kMaxCandM1; at most 16 waves.  Every thread calls it.
+template <int L>
+__device__ inline void block_top_m(u64 (&top)[L], u64 drop, int m, u64* out, CandSmem& cs) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    int cnt;
+    const u64 bound = wave_extract_top(top, drop, m, cs.wtop[wv], &cnt);
+    if (lane == 0) {
+        cs.wbound[wv] = bound;
+        cs.wcount[wv] = cnt;
     }
     __syncthreads();
+    // merge: rank of each wave's entries among all waves' lists (unique values)
+    u64 maxb = 0;
+    int total = 0;
+    for (int w = 0; w < nw; ++w) {
+        maxb = umax64(maxb, cs.wbound[w]);
+        total += cs.wcount[w];
+    }
+    if (lane < cs.wcount[wv]) {
+        const u64 x = cs.wtop[wv][lane];
+        int rank = lane;
+        for (int w = 0; w < nw; ++w) {
+            if (w == wv) continue;
+            const int cw = cs.wcount[w];
+            for (int j = 0; j < cw; ++j) rank += cs.wtop[w][j] > x ? 1 : 0;
+        }
+        if (rank < m) out[rank] = x;
+        else if (rank == m) out[m] = umax64(x, maxb);
+    }
+    if (wv == 0) {
+        for (int j = total + lane; j < m; j += kWave) out[j] = 0;
+        if (lane == 0 && total <= m) out[m] = maxb;
+    }
+}
+
+// ---- register-resident sorted selection ----------------------------------------------
+
+constexpr int kStageCap = 256;  // threshold-bin entries that are ranked in place
+
+// Per-bin starts over a histogram in LDS, bins ordered from the top:
+// start[b] = entries in bins > b.  Also finds, like block_threshold, the
+// largest bin tb with suffix(tb) >= need (tb = -1 if total < need), with
+// above = start[tb], at = cnt[tb], total = all entries; and zeroes cnt so it
+// can serve as per-bin cursors.  Ends with a barrier.  At most 16 waves.
+__device__ inline void bin_starts(uint32_t* cnt, uint32_t* start, int nbins, uint32_t need, int& tb,
+                                  uint32_t& above, uint32_t& at, uint32_t& total) {
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t res[3];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    const int per = (nbins + blockDim.x - 1) / blockDim.x;
+    const int hi = max(nbins - per * static_cast<int>(threadIdx.x), 0);  // bins [lo, hi)
+    const int lo = max(hi - per, 0);
+    uint32_t mine = 0;
+    for (int b = lo; b < hi; ++b) mine += cnt[b];
+    uint32_t pre = mine, sum = mine;
+#define CSA_SCAN_STEP(o)                                         \
+    {                                                            \
+        const uint32_t other = xor_lanes<o>(sum);                \
+        if (lane & (o)) pre += other;                            \
+        sum += other;                                            \
+    }
+    CSA_SCAN_STEP(1) CSA_SCAN_STEP(2) CSA_SCAN_STEP(4) CSA_SCAN_STEP(8) CSA_SCAN_STEP(16) CSA_SCAN_STEP(32)
+#undef CSA_SCAN_STEP
+    if (lane == 0) wsum[wv] = sum;
+    if (threadIdx.x == 0) { res[0] = 0xffffffffu; res[1] = 0; res[2] = 0; }
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+        const uint32_t x = wsum[w];
+        tot += x;
+        before += w < wv ? x : 0u;
+    }
+    uint32_t acc = before + pre - mine;  // entries in bins >= hi
+    for (int b = hi - 1; b >= lo; --b) {
+        const uint32_t c = cnt[b];
+        start[b] = acc;
+        if (tot >= need && acc < need && acc + c >= need) {
+            res[0] = static_cast<uint32_t>(b);
+            res[1] = acc;
+            res[2] = c;
+        }
+        acc += c;
+        cnt[b] = 0;
+    }
+    if (tot < need && threadIdx.x == 0) res[1] = tot;
+    __syncthreads();
+    tb = static_cast<int>(res[0]);
+    above = res[1];
+    at = res[2];
+    total = tot;
+}
+
+// LDS scratch of select_sorted.
+struct SortSmem {
+    uint32_t cnt[1 << kSelBits];
+    uint32_t start[1 << kSelBits];
+};
+
+// The `need` largest nonzero composites held in the threads' v[] (each
+// thread's entries, zero = none), written sorted descending to out[0 ..);
+// all of them if there are fewer.  Returns how many were written.  Every
+// live entry must share its top pb bits with the others.
+//
+// Each pass histograms the kSelBits-wide digit after those pb bits.  The
+// bins' starts place every entry of the bins above the threshold bin (and of
+// the threshold bin itself when it holds at most kStageCap entries) at its
+// final position: entries are staged bin by bin and ranked inside their bin.
+// A larger threshold bin goes on to the next digit alone.  v is consumed;
+// stage holds kTopkMaxK + kStageCap composites.  Every thread calls it; out
+// is complete when it returns.
+template <int V>
+__device__ inline uint32_t select_sorted(u64 (&v)[V], uint32_t need, int pb, u64* out, u64* stage, SortSmem& ss) {
+    uint32_t off = 0, written = 0;
+    while (true) {
+        const int db = min(kSelBits, 64 - pb);
+        const int nb = 1 << db;
+        const int shift = 64 - pb - db;
+        const u64 dmask = static_cast<u64>(nb - 1);
+        for (int i = threadIdx.x; i < nb; i += blockDim.x) ss.cnt[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < V; ++u)
+            if (v[u]) atomicAdd(&ss.cnt[(v[u] >> shift) & dmask], 1u);
+        __syncthreads();
+        int td;
+        uint32_t above, at, total;
+        bin_starts(ss.cnt, ss.start, nb, need, td, above, at, total);
+        const bool all = td < 0;
+        const bool stage_td = !all && at <= static_cast<uint32_t>(kStageCap);
+        int dg[V];
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            dg[u] = v[u] ? static_cast<int>((v[u] >> shift) & dmask) : -1;
+            const bool staged = dg[u] >= 0 && (all || dg[u] > td || (dg[u] == td && stage_td));
+            if (staged) stage[ss.start[dg[u]] + atomicAdd(&ss.cnt[dg[u]], 1u)] = v[u];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            const bool staged = dg[u] >= 0 && (all || dg[u] > td || (dg[u] == td && stage_td));
+            if (staged) {
+                const uint32_t s = ss.start[dg[u]];
+                const uint32_t c = ss.cnt[dg[u]];
+                uint32_t r = 0;
+                for (uint32_t j = 0; j < c; ++j) r += stage[s + j] > v[u] ? 1u : 0u;
+                if (all || dg[u] > td || r < need - above) out[off + s + r] = v[u];
+            }
+        }
+        if (all) {
+            written = off + total;
+            break;
+        }
+        if (stage_td) {
+            written = off + need;
+            break;
+        }
+#pragma unroll
+        for (int u = 0; u < V; ++u)
+            if (dg[u] != td) v[u] = 0;
+        off += above;
+        need -= above;
+        pb += db;
+        __syncthreads();  // stage and counters are read before the next pass rewrites them
+    }
+    __syncthreads();
+    return written;
 }
 
 }  // namespace csa
