@@ -123,7 +123,7 @@ int csa_index_score(const void* q, const float* w, const void* k, float* scores,
     csa::ScoreArgs a{q, w, k, scores, batch, t, h_i, d_i, n, q_pos, ratio,
                      q_stride_b, w_stride_b, k_stride_b, s_stride_b, ld_s, csa::CandArgs{nullptr, 0, 0}};
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    return launched(dtype == CSA_BF16 ? csa::launch_index_score_bf16(a, s)
+    return launched(dtype == CSA_BF16 ? csa::launch_index_score_bf16(a, nullptr, s)
                                       : csa::launch_index_score_f32(a, s),
                     "csa_index_score");
 }
@@ -340,23 +340,29 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
     pa.comp_kv_stride_b = L->comp_kv_stride_b;
     pa.idx_keys = L->idx_keys;
     pa.idx_keys_stride_b = L->idx_keys_stride_b;
-    e = csa::launch_step_prep(pa, s);
-    if (e != hipSuccess) return launched(e, "csa_decode_step/prep");
+    // The bf16 score kernel runs these jobs in its first workgroups (and
+    // scores the new key itself); the float32 path launches them first.
+    const int n_scan = bf ? L->n_comp : N;
+    const int prep_wgs = bf ? (completes ? 3 : 1) : 0;
+    if (!bf) {
+        e = csa::launch_step_prep(pa, s);
+        if (e != hipSuccess) return launched(e, "csa_decode_step/prep");
+    }
 
     // c. score, with every workgroup's top-k candidates when the rows are long,
     //    then the exact top-k
     csa::CandArgs ca{nullptr, 0, 0};
     if (bf && N > 0) {
-        const int slots = csa::index_score_bf16_wgs(L->batch, N);
-        const int kpw = csa::index_score_bf16_keys_per_wg(L->batch, N);
+        const int slots = csa::index_score_bf16_wgs(L->batch, n_scan, prep_wgs) + (completes ? 1 : 0);
+        const int kpw = csa::index_score_bf16_keys_per_wg(L->batch, n_scan, prep_wgs);
         const int m = kpw > 0 ? csa::topk_cand_m(N, L->top_k, kpw) : -1;
         if (m > 0 && slots <= kStepMaxSlots && N > 4 * L->top_k)
             ca = csa::CandArgs{static_cast<unsigned long long*>(tws), slots, m};
     }
-    csa::ScoreArgs sa{io->q_idx, io->w_idx, L->idx_keys, io->scores, L->batch, 1, L->h_i, L->d_i, N,
+    csa::ScoreArgs sa{io->q_idx, io->w_idx, L->idx_keys, io->scores, L->batch, 1, L->h_i, L->d_i, n_scan,
                       nullptr, L->m, io->q_idx_stride_b, io->w_stride_b, L->idx_keys_stride_b,
                       io->scores_stride_b, N, ca};
-    e = bf ? csa::launch_index_score_bf16(sa, s) : csa::launch_index_score_f32(sa, s);
+    e = bf ? csa::launch_index_score_bf16(sa, &pa, s) : csa::launch_index_score_f32(sa, s);
     if (e != hipSuccess) return launched(e, "csa_decode_step/index_score");
     csa::TopkArgs ta{io->scores, L->batch, 1, N, N, io->scores_stride_b, L->top_k, io->topk_idx,
                      io->topk_count, tws};

@@ -17,11 +17,14 @@ namespace csa {
 // z, c: this sequence's rows, pointing at the first row of block i (local
 // index); global block g = first_block + i decides whether the overlapped
 // form joins the previous block's a half.  ybuf: d floats of LDS (norm only);
-// red: blockDim/64 floats of LDS.
+// red: blockDim/64 floats of LDS.  keep (LDS, may be ybuf): if set, also
+// receives the output as stored (after the bf16 rounding when out_bf16), and
+// the workgroup is synchronised before the call returns.
 __device__ inline void compress_block(const float* __restrict__ z, const float* __restrict__ c,
                                       const float* __restrict__ bias, const float* __restrict__ norm_w,
                                       void* __restrict__ out_row, bool out_bf16, int m, int d,
-                                      bool overlap, long long g, float* ybuf, float* red) {
+                                      bool overlap, long long g, float* ybuf, float* red,
+                                      float* keep = nullptr) {
     const int width = overlap ? 2 * d : d;
     const bool joint = overlap && g > 0;  // previous block's a half joins the softmax
     const int own_col = overlap ? d : 0;  // this block's rows: b half when overlapped
@@ -70,12 +73,18 @@ __device__ inline void compress_block(const float* __restrict__ z, const float* 
             ybuf[ch] = y;
             ss += y * y;
         } else if (out_bf16) {
-            static_cast<uint16_t*>(out_row)[ch] = f32_to_bf16(y);
+            const uint16_t yb = f32_to_bf16(y);
+            static_cast<uint16_t*>(out_row)[ch] = yb;
+            if (keep) keep[ch] = bf16_to_f32(yb);
         } else {
             static_cast<float*>(out_row)[ch] = y;
+            if (keep) keep[ch] = y;
         }
     }
-    if (!norm_w) return;
+    if (!norm_w) {
+        if (keep) __syncthreads();
+        return;
+    }
     ss = wave_sum(ss);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = ss;
     __syncthreads();
@@ -84,9 +93,16 @@ __device__ inline void compress_block(const float* __restrict__ z, const float* 
     const float inv = 1.0f / sqrtf(tot / d + 1e-6f);
     for (int ch = threadIdx.x; ch < d; ch += blockDim.x) {
         const float y = ybuf[ch] * inv * norm_w[ch];
-        if (out_bf16) static_cast<uint16_t*>(out_row)[ch] = f32_to_bf16(y);
-        else static_cast<float*>(out_row)[ch] = y;
+        if (out_bf16) {
+            const uint16_t yb = f32_to_bf16(y);
+            static_cast<uint16_t*>(out_row)[ch] = yb;
+            if (keep) keep[ch] = bf16_to_f32(yb);
+        } else {
+            static_cast<float*>(out_row)[ch] = y;
+            if (keep) keep[ch] = y;
+        }
     }
+    if (keep) __syncthreads();
 }
 
 }  // namespace csa

@@ -26,6 +26,7 @@
 //     serialise on this chip).
 #include "common.h"
 #include "kernels.h"
+#include "step_prep.h"
 #include "topk_common.h"
 
 namespace csa {
@@ -45,8 +46,40 @@ constexpr int kMaxTilesPerWave = 32;  // with candidates: at most 8 keys per lan
 constexpr int kLaneTop = 4;           // composites a lane keeps
 static_assert(kRing % 4 == 0, "ring slot i feeds the lists of lane group i % 4");
 
+static_assert(kHeads * kQPitch * sizeof(uint16_t) >= kPrepMaxD * sizeof(float), "prep roles reuse the query LDS");
+
+// Score of one key held in LDS (as floats) for query row (b, tt): each quad
+// of lanes takes one head (a quarter of the key each).  Returns the score in
+// every thread.  red: 4 floats of LDS.
+__device__ inline float score_one_key(const ScoreArgs& a, int b, int tt, const float* key, float* red) {
+    const int h = threadIdx.x >> 2;
+    const int part = threadIdx.x & 3;
+    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + b * a.q_stride_b +
+                         (static_cast<long long>(tt) * kHeads + h) * kDi + 32 * part;
+    float dot = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint4 v = *reinterpret_cast<const uint4*>(qh + 8 * u);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            dot += bf16_to_f32(static_cast<uint16_t>(w4[e] & 0xffffu)) * key[32 * part + 8 * u + 2 * e];
+            dot += bf16_to_f32(static_cast<uint16_t>(w4[e] >> 16)) * key[32 * part + 8 * u + 2 * e + 1];
+        }
+    }
+    dot += xor_lanes_f32<1>(dot);
+    dot += xor_lanes_f32<2>(dot);
+    const float wh = a.w[b * a.w_stride_b + static_cast<long long>(tt) * kHeads + h];
+    float sc = part == 0 ? wh * fmaxf(dot, 0.f) : 0.f;
+    sc = wave_sum(sc);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = sc;
+    __syncthreads();
+    return red[0] + red[1] + red[2] + red[3];
+}
+
 template <bool kCands>
-__global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs a, int tiles_per_row) {
+__global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs a, int tiles_per_row, PrepArgs p,
+                                                                       int prep_wgs) {
     __shared__ __attribute__((aligned(16))) uint16_t qs[kHeads * kQPitch];
     __shared__ __attribute__((aligned(16))) float ws[kHeads];
     __shared__ CandSmem cs;
@@ -55,11 +88,38 @@ __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs
     const int row = blockIdx.y;
     const int b = row / a.t;
     const int tt = row - b * a.t;
+
+    // 0. the decode step's small jobs (one query row per sequence), and the
+    //    new key of a completed block: compressed, scored, given its own slot
+    if (static_cast<int>(blockIdx.x) < prep_wgs) {
+        float* ybuf = reinterpret_cast<float*>(qs);
+        step_prep_role(p, blockIdx.x, b, ybuf, ws, ybuf);
+        if (blockIdx.x == 2 && p.completes) {
+            float sc = score_one_key(a, b, tt, ybuf, ws + 8);
+            const int key = a.n;
+            if (a.q_pos && static_cast<long long>(a.ratio) * key + a.ratio - 1 > a.q_pos[row]) sc = -INFINITY;
+            if (threadIdx.x == 0) a.scores[b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s + key] = sc;
+            if (kCands && threadIdx.x <= a.cands.m) {
+                const uint32_t kk = score_key(sc);
+                u64* slot = a.cands.lists + (static_cast<long long>(row) * a.cands.slots + a.cands.slots - 1) *
+                                                (a.cands.m + 1);
+                slot[threadIdx.x] = (threadIdx.x == 0 && key_valid(kk, sc)) ? composite(kk, static_cast<uint32_t>(key)) : 0ull;
+            }
+        }
+        return;
+    }
+    const int wg = blockIdx.x - prep_wgs;  // scan workgroup of this row
+    const int scan_wgs = gridDim.x - prep_wgs;
     const int li = lane & 15;   // key column of B / head row of A within a 16-tile
     const int lg = lane >> 4;   // 8-element group of each 32-wide k-step
     const int n = a.n;
-    const int waves_per_row = gridDim.x * kWavesPerWg;
-    const int gw = blockIdx.x * kWavesPerWg + wv;
+    if (n <= 0) {  // nothing to scan: an empty candidate list
+        if (kCands && threadIdx.x <= a.cands.m)
+            a.cands.lists[(static_cast<long long>(row) * a.cands.slots + wg) * (a.cands.m + 1) + threadIdx.x] = 0ull;
+        return;
+    }
+    const int waves_per_row = scan_wgs * kWavesPerWg;
+    const int gw = wg * kWavesPerWg + wv;
     const int n_mine = gw < tiles_per_row ? (tiles_per_row - gw + waves_per_row - 1) / waves_per_row : 0;
 
     const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_stride_b + 8 * lg;
@@ -161,7 +221,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs
     if (!kCands) return;
     // 4. this workgroup's best m and their bound to its candidate slot
     block_top_m(top, drop, a.cands.m,
-                a.cands.lists + (static_cast<long long>(row) * a.cands.slots + blockIdx.x) * (a.cands.m + 1), cs);
+                a.cands.lists + (static_cast<long long>(row) * a.cands.slots + wg) * (a.cands.m + 1), cs);
 }
 
 // float32 path (small correctness workloads): one thread per key, the query
@@ -195,32 +255,45 @@ __global__ __launch_bounds__(kScoreF32Threads) void k_index_score_f32(ScoreArgs 
 
 }  // namespace
 
-int index_score_bf16_wgs(int rows, int n) {
+int index_score_bf16_wgs(int rows, int n, int extra) {
     const int tiles = (n + kTileKeys - 1) / kTileKeys;
+    // two workgroups per CU in all, the extra ones included
     const int target = 2 * device_cu_count();
-    int wgs = (target + rows - 1) / rows;
+    int wgs = (target + rows - 1) / rows - extra;
     // at least kRing tiles per wave where the row is long enough
     const int max_wgs = (tiles + kWavesPerWg * kRing - 1) / (kWavesPerWg * kRing);
     if (wgs > max_wgs) wgs = max_wgs;
     return wgs < 1 ? 1 : wgs;
 }
 
-int index_score_bf16_keys_per_wg(int rows, int n) {
+int index_score_bf16_keys_per_wg(int rows, int n, int extra) {
     const int tiles = (n + kTileKeys - 1) / kTileKeys;
-    const int waves = index_score_bf16_wgs(rows, n) * kWavesPerWg;
+    const int waves = index_score_bf16_wgs(rows, n, extra) * kWavesPerWg;
     const int per_wave = (tiles + waves - 1) / waves;
     return per_wave <= kMaxTilesPerWave ? per_wave * kWavesPerWg * kTileKeys : -1;
 }
 
-hipError_t launch_index_score_bf16(const ScoreArgs& a, hipStream_t s) {
-    if (a.n == 0) return hipSuccess;
+hipError_t launch_index_score_bf16(const ScoreArgs& a, const PrepArgs* fold, hipStream_t s) {
     const int rows = a.batch * a.t;
+    if (rows == 0 || (a.n == 0 && !fold)) return hipSuccess;
     const int tiles = (a.n + kTileKeys - 1) / kTileKeys;
-    const int wgs = index_score_bf16_wgs(rows, a.n);
-    if (a.cands.lists && a.cands.slots == wgs && index_score_bf16_keys_per_wg(rows, a.n) > 0)
-        hipLaunchKernelGGL(k_index_score_bf16<true>, dim3(wgs, rows), dim3(kScoreThreads), 0, s, a, tiles);
+    PrepArgs p{};
+    int prep_wgs = 0;
+    if (fold) {
+        if (a.t != 1) return hipErrorInvalidValue;
+        p = *fold;
+        prep_wgs = p.completes ? 3 : 1;
+    }
+    const int wgs = index_score_bf16_wgs(rows, a.n, prep_wgs);
+    const int new_slot = fold && p.completes ? 1 : 0;
+    if (a.cands.lists && a.cands.slots == wgs + new_slot && (a.n == 0 || index_score_bf16_keys_per_wg(rows, a.n, prep_wgs) > 0))
+        hipLaunchKernelGGL(k_index_score_bf16<true>, dim3(prep_wgs + wgs, rows), dim3(kScoreThreads), 0, s, a, tiles,
+                           p, prep_wgs);
+    else if (!a.cands.lists)
+        hipLaunchKernelGGL(k_index_score_bf16<false>, dim3(prep_wgs + wgs, rows), dim3(kScoreThreads), 0, s, a, tiles,
+                           p, prep_wgs);
     else
-        hipLaunchKernelGGL(k_index_score_bf16<false>, dim3(wgs, rows), dim3(kScoreThreads), 0, s, a, tiles);
+        return hipErrorInvalidValue;  // candidate slots that do not match the grid
     return hipGetLastError();
 }
 

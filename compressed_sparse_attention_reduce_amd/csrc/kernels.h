@@ -45,10 +45,17 @@ struct ScoreArgs {
     // keys to its slot of cands.lists (cands.slots must equal its grid width)
     CandArgs cands;
 };
-// workgroups per row and keys per workgroup of the bf16 score kernel
-int index_score_bf16_wgs(int rows, int n);
-int index_score_bf16_keys_per_wg(int rows, int n);
-hipError_t launch_index_score_bf16(const ScoreArgs& a, hipStream_t s);
+// Scan workgroups per row and keys per scan workgroup of the bf16 score
+// kernel (extra = workgroups per row the kernel also runs for other jobs).
+int index_score_bf16_wgs(int rows, int n, int extra);
+int index_score_bf16_keys_per_wg(int rows, int n, int extra);
+struct PrepArgs;
+// fold (optional, one query row per sequence): the decode step's small jobs
+// (step_prep.h) run by the first workgroups of each row; with fold->completes
+// the kernel also scores the new key at index a.n (its indexer key is the
+// one role 2 compresses) and gives it the last candidate slot.  a.n counts
+// the keys already in the cache.
+hipError_t launch_index_score_bf16(const ScoreArgs& a, const PrepArgs* fold, hipStream_t s);
 hipError_t launch_index_score_f32(const ScoreArgs& a, hipStream_t s);
 
 // ---- top-k -------------------------------------------------------------------

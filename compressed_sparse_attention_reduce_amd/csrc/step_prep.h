@@ -1,0 +1,36 @@
+// The small per-sequence jobs of a decode step, one workgroup each:
+//   role 0  append the new token's KV row to the SWA ring (page 1, P2: the
+//           token lands in slot swa_head);
+//   role 1  compress the block the token completes into comp_kv[n_comp];
+//   role 2  compress that block's indexer key into idx_keys[n_comp].
+// Roles 1 and 2 run only when the token completes a block.
+#pragma once
+
+#include "compress_impl.h"
+#include "kernels.h"
+
+namespace csa {
+
+// ybuf: kPrepMaxD floats of LDS; red: blockDim/64 floats of LDS.  key (LDS,
+// may be ybuf): role 2 leaves the stored key there as floats (synchronised).
+__device__ inline void step_prep_role(const PrepArgs& a, int role, int b, float* ybuf, float* red,
+                                      float* key = nullptr) {
+    if (role == 0) {
+        const char* src = static_cast<const char*>(a.kv_new) + b * a.kv_new_stride_b * a.es;
+        char* dst = static_cast<char*>(a.swa) + (b * a.swa_stride_b + static_cast<long long>(a.swa_slot) * a.d) * a.es;
+        for (int o = threadIdx.x * 16; o < a.d * a.es; o += blockDim.x * 16)
+            *reinterpret_cast<uint4*>(dst + o) = *reinterpret_cast<const uint4*>(src + o);
+        return;
+    }
+    if (!a.completes) return;
+    const bool main = role == 1;
+    const int d = main ? a.d : a.d_i;
+    const float* z = (main ? a.z_main : a.z_idx) + b * (main ? a.zc_main_stride_b : a.zc_idx_stride_b);
+    const float* c = (main ? a.c_main : a.c_idx) + b * (main ? a.zc_main_stride_b : a.zc_idx_stride_b);
+    char* out = static_cast<char*>(main ? a.comp_kv : a.idx_keys) +
+                (b * (main ? a.comp_kv_stride_b : a.idx_keys_stride_b) + static_cast<long long>(a.n_comp) * d) * a.es;
+    compress_block(z, c, main ? a.main_bias : a.idx_bias, main ? a.main_norm : a.idx_norm, out, a.es == 2, a.m, d,
+                   a.overlap != 0, a.block, ybuf, red, main ? nullptr : key);
+}
+
+}  // namespace csa

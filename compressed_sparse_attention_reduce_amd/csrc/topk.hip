@@ -37,13 +37,13 @@ namespace {
 
 constexpr int kFinalThreads = 1024;
 constexpr int kUnionRegs = 8;         // union entries per thread of the fast path
-constexpr int kPool = 2048;           // exact-path candidates held in LDS
-constexpr int kPoolRegs = kPool / kFinalThreads;
-constexpr int kSortRegs = kTopkMaxK / kFinalThreads;
+constexpr int kUnionCap = kUnionRegs * kFinalThreads;
+constexpr int kPool = 2048;           // exact path: threshold-bin entries held in LDS
 constexpr int kRefineBits = 10;
 constexpr int kCandThreads = 256;
 constexpr int kCandChunk = 2048;      // scores per k_topk_cands workgroup
 constexpr int kCandPer = kCandChunk / kCandThreads;
+static_assert(kPool + kTopkMaxK <= kUnionCap, "exact-path candidates fit the pool");
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -64,19 +64,19 @@ __device__ inline bool row_get(const float* row, long long i, int bin12, u64& c)
     return true;
 }
 
+// Dynamic LDS of k_topk_final (about 100 KB).
 struct FinalSmem {
-    u64 sel[kTopkMaxK];                 // winners, sorted at the end
-    u64 pool[kTopkMaxK + kStageCap];    // exact path: the threshold bin; then the sort's staging
+    u64 pool[kUnionCap];                  // candidates of the sorted select
+    u64 stage[kTopkMaxK + kStageCap];     // its staging; the exact path's picks above the threshold before
     union {
-        uint32_t hist[kHistBins];       // row histograms of the exact path
-        SortSmem ss;                    // counters of the sorted select (used after them)
+        uint32_t hist[kHistBins];         // row histograms of the exact path
+        SortSmem ss;                      // counters of the sorted select (used after them)
     };
     u64 wmax[16], wmin[16];
     uint32_t n_sel, n_pool;
 };
 
-// The largest and (through complements) the smallest of the threads' a and
-// b over the block, in every thread.
+// Block maxima of the threads' a and b, in every thread.
 __device__ inline void block_max2(FinalSmem& sm, u64& a, u64& b) {
     const int wv = threadIdx.x / kWave;
     const int nw = blockDim.x / kWave;
@@ -95,9 +95,9 @@ __device__ inline void block_max2(FinalSmem& sm, u64& a, u64& b) {
     }
 }
 
-// Exact top-k of one score row by one workgroup, sorted into sm.sel.
+// Exact top-k of one score row by one workgroup, as sorted indices into out.
 // Returns k_eff.
-__device__ uint32_t exact_row_topk(FinalSmem& sm, const float* row, int n, int k) {
+__device__ uint32_t exact_row_topk(FinalSmem& sm, const float* row, int n, int k, int* out) {
     for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) sm.hist[i] = 0;
     if (threadIdx.x == 0) { sm.n_sel = 0; sm.n_pool = 0; }
     __syncthreads();
@@ -111,13 +111,14 @@ __device__ uint32_t exact_row_topk(FinalSmem& sm, const float* row, int n, int k
     uint32_t above, at, total;
     block_threshold(sm.hist, kHistBins, static_cast<uint32_t>(k), tb, above, at, total);
     const bool pool_fits = at <= kPool;
+    // picks above the threshold bin go to stage, the bin's entries to pool
     for (long long base = 0; base < n; base += blockDim.x) {
         const long long i = base + threadIdx.x;
         u64 c = 0;
         int bin = -2;
         if (i < n && row_get(row, i, -1, c)) bin = static_cast<int>(c >> (64 - kHistBits));
         const uint32_t ps = wave_append_pos(bin > tb, &sm.n_sel);
-        if (bin > tb) sm.sel[ps] = c;
+        if (bin > tb) sm.stage[ps] = c;
         const uint32_t pp = wave_append_pos(bin == tb && pool_fits, &sm.n_pool);
         if (bin == tb && pool_fits) sm.pool[pp] = c;
     }
@@ -151,7 +152,7 @@ __device__ uint32_t exact_row_topk(FinalSmem& sm, const float* row, int n, int k
                 if (i < n && row_get(row, i, tb, c) && (c >> (64 - pb)) == prefix)
                     dg = static_cast<int>((c >> (64 - pb - db)) & (nb - 1));
                 const uint32_t ps = wave_append_pos(dg > td, &sm.n_sel);
-                if (dg > td) sm.sel[ps] = c;
+                if (dg > td) sm.stage[ps] = c;
                 const uint32_t pp = wave_append_pos(dg == td && fits, &sm.n_pool);
                 if (dg == td && fits) sm.pool[pp] = c;
             }
@@ -162,41 +163,31 @@ __device__ uint32_t exact_row_topk(FinalSmem& sm, const float* row, int n, int k
             if (fits) break;
         }
     }
-    // every candidate (the picks above the threshold and the threshold bin's
-    // entries, at most kTopkMaxK + kPool) to registers, then the sorted select
+    // all candidates (the bin's entries, then the picks above it) into the pool
+    const uint32_t nb_pool = tb >= 0 ? sm.n_pool : 0u;
     const uint32_t ns = sm.n_sel;
-    const uint32_t np = tb >= 0 ? sm.n_pool : 0u;
-    u64 v[kPoolRegs + kSortRegs];
-#pragma unroll
-    for (int u = 0; u < kPoolRegs; ++u) {
-        const uint32_t i = threadIdx.x + u * kFinalThreads;
-        v[u] = i < np ? sm.pool[i] : 0ull;
-    }
-#pragma unroll
-    for (int u = 0; u < kSortRegs; ++u) {
-        const uint32_t i = threadIdx.x + u * kFinalThreads;
-        v[kPoolRegs + u] = i < ns ? sm.sel[i] : 0ull;
-    }
-    // the candidates share the top bits where their largest and smallest agree
+    for (uint32_t i = threadIdx.x; i < ns; i += blockDim.x) sm.pool[nb_pool + i] = sm.stage[i];
+    __syncthreads();
+    const uint32_t np = nb_pool + ns;
+    // they share the top bits where their largest and smallest agree
     u64 hi = 0, lo_c = 0;
-#pragma unroll
-    for (int u = 0; u < kPoolRegs + kSortRegs; ++u) {
-        hi = umax64(hi, v[u]);
-        lo_c = umax64(lo_c, v[u] ? ~v[u] : 0ull);
+    for (uint32_t i = threadIdx.x; i < np; i += blockDim.x) {
+        hi = umax64(hi, sm.pool[i]);
+        lo_c = umax64(lo_c, ~sm.pool[i]);
     }
-    block_max2(sm, hi, lo_c);  // its barrier also ends every read of sel and pool above
-    const int pb = hi == 0 ? 0 : __clzll(static_cast<long long>(hi ^ ~lo_c));
-    return select_sorted(v, static_cast<uint32_t>(k), pb < 64 ? pb : 63, sm.sel, sm.pool, sm.ss);
+    block_max2(sm, hi, lo_c);
+    const int pb = np <= 1 ? 0 : __clzll(static_cast<long long>(hi ^ ~lo_c));
+    return select_sorted<kUnionRegs>(sm.pool, np, static_cast<uint32_t>(k), pb, out, sm.stage, sm.ss, &sm.n_pool);
 }
 
-// Fast path: top-k of the union of per-slot candidates, sorted into sm.sel.
-// Returns false if the union cannot prove the answer.
-__device__ bool union_topk(FinalSmem& sm, const CandArgs& c, int row, int k, uint32_t& k_eff) {
+// Fast path: top-k of the union of per-slot candidates, as sorted indices
+// into out.  Returns false if the union cannot prove the answer.
+__device__ bool union_topk(FinalSmem& sm, const CandArgs& c, int row, int k, int* out, uint32_t& k_eff) {
     const int m1 = c.m + 1;
     const int total = c.slots * m1;
-    if (total > kUnionRegs * kFinalThreads) return false;
+    if (total > kUnionCap) return false;
     const u64* lists = c.lists + static_cast<long long>(row) * total;
-    // kept entries (first m of every slot) stay in registers; entry m of each
+    // kept entries (first m of every slot) into registers; entry m of each
     // slot bounds what that slot did not keep
     u64 v[kUnionRegs];
 #pragma unroll
@@ -214,36 +205,42 @@ __device__ bool union_topk(FinalSmem& sm, const CandArgs& c, int row, int k, uin
         }
         mx = umax64(mx, v[u]);
     }
+    if (threadIdx.x == 0) sm.n_pool = 0;
     block_max2(sm, maxdrop, mx);
-    // the top k must all beat every slot's bound to be proven: only such
-    // entries take part (they share the top bits where maxdrop and mx agree)
+    // only entries above every slot's bound can be proven; they go to the
+    // pool (and share the top bits where maxdrop and mx agree)
 #pragma unroll
-    for (int u = 0; u < kUnionRegs; ++u) v[u] = v[u] > maxdrop ? v[u] : 0ull;
-    uint32_t ns = 0;
-    if (mx > maxdrop) {
-        const int pb = __clzll(static_cast<long long>(mx ^ maxdrop));
-        ns = select_sorted(v, static_cast<uint32_t>(k), pb, sm.sel, sm.pool, sm.ss);
+    for (int u = 0; u < kUnionRegs; ++u) {
+        const bool live = v[u] > maxdrop;
+        const uint32_t p = wave_append_pos(live, &sm.n_pool);
+        if (live) sm.pool[p] = v[u];
     }
+    __syncthreads();
+    const uint32_t np = sm.n_pool;
     // fewer than k proven entries: exact only if no slot left anything valid out
-    if (ns < static_cast<uint32_t>(k) && maxdrop != 0) return false;
-    k_eff = ns;
+    if (np < static_cast<uint32_t>(k) && maxdrop != 0) return false;
+    k_eff = np == 0 ? 0u
+                    : select_sorted<kUnionRegs>(sm.pool, np, static_cast<uint32_t>(k),
+                                                __clzll(static_cast<long long>(mx ^ maxdrop)), out, sm.stage,
+                                                sm.ss, &sm.n_pool);
     return true;
 }
 
 __global__ __launch_bounds__(kFinalThreads) void k_topk_final(TopkArgs a, CandArgs c) {
-    __shared__ FinalSmem sm;
+    extern __shared__ __attribute__((aligned(16))) unsigned char final_smem[];
+    FinalSmem& sm = *reinterpret_cast<FinalSmem*>(final_smem);
     const int row = blockIdx.x;
-    uint32_t k_eff = 0;
-    const bool done = c.lists && union_topk(sm, c, row, a.k, k_eff);
-    if (!done) {
-        __syncthreads();  // the fast path's reads of sm are over
-        k_eff = exact_row_topk(sm, score_row(a, row), a.n, a.k);
-    }
-    const int ns = static_cast<int>(k_eff);
     const int b = row / a.t;
     const int tt = row - b * a.t;
     int* out = a.idx + (static_cast<long long>(b) * a.t + tt) * a.k;
-    for (int j = threadIdx.x; j < a.k; j += blockDim.x) out[j] = j < ns ? composite_index(sm.sel[j]) : -1;
+    uint32_t k_eff = 0;
+    const bool done = c.lists && union_topk(sm, c, row, a.k, out, k_eff);
+    if (!done) {
+        __syncthreads();  // the fast path's reads of sm are over
+        k_eff = exact_row_topk(sm, score_row(a, row), a.n, a.k, out);
+    }
+    const int ns = static_cast<int>(k_eff);
+    for (int j = ns + threadIdx.x; j < a.k; j += blockDim.x) out[j] = -1;
     if (a.count && threadIdx.x == 0) a.count[static_cast<long long>(b) * a.t + tt] = ns;
 }
 
@@ -275,6 +272,18 @@ __global__ __launch_bounds__(kCandThreads) void k_topk_cands(TopkArgs a, CandArg
 }
 
 }  // namespace
+
+// k_topk_final takes more than 64 KB of LDS: opt in once per device.
+static bool final_lds_opted_in() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    static bool done[64] = {};
+    if (!done[dev])
+        done[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_topk_final),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        static_cast<int>(sizeof(FinalSmem))) == hipSuccess;
+    return done[dev];
+}
 
 int topk_cand_m(int n, int k, int keys_per_slot) {
     // slots hold m + 1 entries; m covers the expected share of the top k of a
@@ -310,7 +319,8 @@ hipError_t launch_topk(const TopkArgs& a, const CandArgs* cands, hipStream_t s) 
             hipLaunchKernelGGL(k_topk_cands, dim3(slots, rows), dim3(kCandThreads), 0, s, a, c);
         }
     }
-    hipLaunchKernelGGL(k_topk_final, dim3(rows), dim3(kFinalThreads), 0, s, a, c);
+    if (!final_lds_opted_in()) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_topk_final, dim3(rows), dim3(kFinalThreads), sizeof(FinalSmem), s, a, c);
     return hipGetLastError();
 }
 

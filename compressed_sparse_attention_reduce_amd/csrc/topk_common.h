@@ -258,21 +258,23 @@ struct SortSmem {
     uint32_t start[1 << kSelBits];
 };
 
-// The `need` largest nonzero composites held in the threads' v[] (each
-// thread's entries, zero = none), written sorted descending to out[0 ..);
-// all of them if there are fewer.  Returns how many were written.  Every
-// live entry must share its top pb bits with the others.
+// The `need` largest of the unique nonzero composites pool[0..np) (LDS),
+// written sorted descending as indices to out[0 ..) (global); all of them if
+// there are fewer.  Returns how many were written.  Every entry must share
+// its top pb bits with the others.
 //
 // Each pass histograms the kSelBits-wide digit after those pb bits.  The
 // bins' starts place every entry of the bins above the threshold bin (and of
 // the threshold bin itself when it holds at most kStageCap entries) at its
-// final position: entries are staged bin by bin and ranked inside their bin.
-// A larger threshold bin goes on to the next digit alone.  v is consumed;
-// stage holds kTopkMaxK + kStageCap composites.  Every thread calls it; out
-// is complete when it returns.
-template <int V>
-__device__ inline uint32_t select_sorted(u64 (&v)[V], uint32_t need, int pb, u64* out, u64* stage, SortSmem& ss) {
-    uint32_t off = 0, written = 0;
+// final position: entries are staged bin by bin, then each is ranked inside
+// its bin.  A larger threshold bin is compacted to the front of the pool and
+// goes on to the next digit alone.  np <= kPoolRegs * blockDim.x; stage
+// holds kTopkMaxK + kStageCap composites; *n_pool is a spare LDS counter.
+// Every thread calls it; pool is consumed.
+template <int kPoolRegs>
+__device__ inline uint32_t select_sorted(u64* pool, uint32_t np, uint32_t need, int pb, int* out, u64* stage,
+                                         SortSmem& ss, uint32_t* n_pool) {
+    uint32_t off = 0;
     while (true) {
         const int db = min(kSelBits, 64 - pb);
         const int nb = 1 << db;
@@ -280,52 +282,53 @@ __device__ inline uint32_t select_sorted(u64 (&v)[V], uint32_t need, int pb, u64
         const u64 dmask = static_cast<u64>(nb - 1);
         for (int i = threadIdx.x; i < nb; i += blockDim.x) ss.cnt[i] = 0;
         __syncthreads();
-#pragma unroll
-        for (int u = 0; u < V; ++u)
-            if (v[u]) atomicAdd(&ss.cnt[(v[u] >> shift) & dmask], 1u);
+        for (uint32_t i = threadIdx.x; i < np; i += blockDim.x)
+            atomicAdd(&ss.cnt[(pool[i] >> shift) & dmask], 1u);
         __syncthreads();
         int td;
         uint32_t above, at, total;
         bin_starts(ss.cnt, ss.start, nb, need, td, above, at, total);
         const bool all = td < 0;
         const bool stage_td = !all && at <= static_cast<uint32_t>(kStageCap);
-        int dg[V];
-#pragma unroll
-        for (int u = 0; u < V; ++u) {
-            dg[u] = v[u] ? static_cast<int>((v[u] >> shift) & dmask) : -1;
-            const bool staged = dg[u] >= 0 && (all || dg[u] > td || (dg[u] == td && stage_td));
-            if (staged) stage[ss.start[dg[u]] + atomicAdd(&ss.cnt[dg[u]], 1u)] = v[u];
+        for (uint32_t i = threadIdx.x; i < np; i += blockDim.x) {
+            const u64 x = pool[i];
+            const int d = static_cast<int>((x >> shift) & dmask);
+            if (all || d > td || (d == td && stage_td)) stage[ss.start[d] + atomicAdd(&ss.cnt[d], 1u)] = x;
         }
         __syncthreads();
+        const uint32_t nst = all ? total : above + (stage_td ? at : 0u);
+        for (uint32_t i = threadIdx.x; i < nst; i += blockDim.x) {
+            const u64 x = stage[i];
+            const int d = static_cast<int>((x >> shift) & dmask);
+            const uint32_t s = ss.start[d];
+            const uint32_t c = ss.cnt[d];
+            uint32_t r = 0;
+            for (uint32_t j = 0; j < c; ++j) r += stage[s + j] > x ? 1u : 0u;
+            if (all || d > td || r < need - above) out[off + s + r] = composite_index(x);
+        }
+        if (all) return off + total;
+        if (stage_td) return off + need;
+        // the threshold bin alone goes on with the next digit
+        u64 keep[kPoolRegs];
 #pragma unroll
-        for (int u = 0; u < V; ++u) {
-            const bool staged = dg[u] >= 0 && (all || dg[u] > td || (dg[u] == td && stage_td));
-            if (staged) {
-                const uint32_t s = ss.start[dg[u]];
-                const uint32_t c = ss.cnt[dg[u]];
-                uint32_t r = 0;
-                for (uint32_t j = 0; j < c; ++j) r += stage[s + j] > v[u] ? 1u : 0u;
-                if (all || dg[u] > td || r < need - above) out[off + s + r] = v[u];
-            }
+        for (int u = 0; u < kPoolRegs; ++u) {
+            const uint32_t i = threadIdx.x + u * blockDim.x;
+            const u64 x = i < np ? pool[i] : 0ull;
+            keep[u] = (i < np && static_cast<int>((x >> shift) & dmask) == td) ? x : 0ull;
         }
-        if (all) {
-            written = off + total;
-            break;
-        }
-        if (stage_td) {
-            written = off + need;
-            break;
-        }
+        if (threadIdx.x == 0) *n_pool = 0;
+        __syncthreads();
 #pragma unroll
-        for (int u = 0; u < V; ++u)
-            if (dg[u] != td) v[u] = 0;
+        for (int u = 0; u < kPoolRegs; ++u) {
+            const uint32_t p = wave_append_pos(keep[u] != 0, n_pool);
+            if (keep[u]) pool[p] = keep[u];
+        }
+        __syncthreads();
+        np = at;
         off += above;
         need -= above;
         pb += db;
-        __syncthreads();  // stage and counters are read before the next pass rewrites them
     }
-    __syncthreads();
-    return written;
 }
 
 }  // namespace csa
