@@ -31,7 +31,9 @@ namespace {
 constexpr int kAttnThreads = 256;
 constexpr int kHeadGroup = 16;
 
-inline int attn_rows_per_split(int n_max) { return n_max > 256 ? 64 : 32; }
+// 32 rows per split: every thread issues all its row loads at once, and
+// short rows give more workgroups to spread the loads over.
+inline int attn_rows_per_split(int) { return 32; }
 inline int attn_splits(int n_max) {
     const int r = attn_rows_per_split(n_max);
     return n_max > 0 ? (n_max + r - 1) / r : 1;
@@ -48,7 +50,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial_bf16(AttnArgs a, 
     __shared__ float wmax[4][kHeadGroup];
     __shared__ float wsum[4][kHeadGroup];
 
-    __shared__ const uint16_t* rowptr[R];
     const int split = blockIdx.x;
     const int hg = blockIdx.y;
     const int b = blockIdx.z;
@@ -71,10 +72,18 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial_bf16(AttnArgs a, 
     }
 
     // valid rows: n_valid from the device (gather mode: top-k count + window).
-    // The row's top-k index is loaded alongside the count (not after it).
-    int my_idx = 0;
-    if (a.idx && threadIdx.x < R && r0 + static_cast<int>(threadIdx.x) < a.k)
-        my_idx = a.idx[static_cast<long long>(b) * a.k + r0 + threadIdx.x];
+    // Each thread loads the top-k index of every row its chunks fall in
+    // alongside the count, so the row loads below wait for one round trip
+    // only (lanes of a wave mostly share a row: one request).
+    constexpr int kChunks = R * 64 / kAttnThreads;  // 16-byte chunks per thread at d = 512
+    const int n_chunks = R * cpr;
+    int my_idx[kChunks];
+#pragma unroll
+    for (int u = 0; u < kChunks; ++u) {
+        const int c = u * kAttnThreads + threadIdx.x;
+        const int j = r0 + c / cpr;
+        my_idx[u] = (a.idx && c < n_chunks && j < a.k) ? a.idx[static_cast<long long>(b) * a.k + j] : 0;
+    }
     int cnt = 0, nv;
     if (a.idx) {
         cnt = a.count ? a.count[b] : a.k;
@@ -96,17 +105,21 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial_bf16(AttnArgs a, 
         return;
     }
 
-    // 1. one source pointer per row (top-k index or SWA slot), then all row
-    //    loads in unrolled batches: rows -> LDS (and gather_buf); query -> LDS
-    if (threadIdx.x < R) {
-        const int r = threadIdx.x;
+    // 1. every chunk's source (top-k row of the compressed cache, SWA slot, or
+    //    the plain kv rows), all loads in one unrolled batch: rows -> LDS (and
+    //    gather_buf); query -> LDS
+    uint4 v[kChunks];
+#pragma unroll
+    for (int u = 0; u < kChunks; ++u) {
+        const int c = u * kAttnThreads + threadIdx.x;
+        const int r = c / cpr;
         const int j = r0 + r;
         const uint16_t* src = nullptr;
-        if (r < rows) {
+        if (c < n_chunks && r < rows) {
             if (!a.idx) {
                 src = a.kv + b * a.kv_stride_b + static_cast<long long>(j) * d;
             } else if (j < cnt) {
-                const int ri = my_idx < 0 ? 0 : (my_idx >= a.n_comp ? a.n_comp - 1 : my_idx);
+                const int ri = my_idx[u] < 0 ? 0 : (my_idx[u] >= a.n_comp ? a.n_comp - 1 : my_idx[u]);
                 src = a.comp_kv + b * a.comp_kv_stride_b + static_cast<long long>(ri) * d;
             } else {
                 int slot = (a.swa_head - a.swa_len + (j - cnt)) % a.w;
@@ -114,34 +127,23 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial_bf16(AttnArgs a, 
                 src = a.swa + b * a.swa_stride_b + static_cast<long long>(slot) * d;
             }
         }
-        rowptr[r] = src;
+        v[u] = src ? *reinterpret_cast<const uint4*>(src + (c % cpr) * 8) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kQBatch; ++u) {
         const int c = threadIdx.x + u * kAttnThreads;
         if (c < kHeadGroup * cpr) *reinterpret_cast<uint4*>(qs + (c / cpr) * pitch + (c % cpr) * 8) = qv[u];
     }
-    __syncthreads();
     const bool write_buf = a.idx && a.gather_buf && hg == 0;
-    constexpr int kBatch = 8;
-    for (int base = 0; base < R * cpr; base += kAttnThreads * kBatch) {
-        uint4 v[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int c = base + u * kAttnThreads + threadIdx.x;
-            const uint16_t* src = c < R * cpr ? rowptr[c / cpr] : nullptr;
-            v[u] = src ? *reinterpret_cast<const uint4*>(src + (c % cpr) * 8) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int c = base + u * kAttnThreads + threadIdx.x;
-            if (c < R * cpr) {
-                const int r = c / cpr;
-                const int cc = c % cpr;
-                *reinterpret_cast<uint4*>(tile + r * pitch + cc * 8) = v[u];
-                if (write_buf && r < rows)
-                    *reinterpret_cast<uint4*>(a.gather_buf + b * a.buf_stride_b + static_cast<long long>(r0 + r) * d + cc * 8) = v[u];
-            }
+    for (int u = 0; u < kChunks; ++u) {
+        const int c = u * kAttnThreads + threadIdx.x;
+        if (c < n_chunks) {
+            const int r = c / cpr;
+            const int cc = c % cpr;
+            *reinterpret_cast<uint4*>(tile + r * pitch + cc * 8) = v[u];
+            if (write_buf && r < rows)
+                *reinterpret_cast<uint4*>(a.gather_buf + b * a.buf_stride_b + static_cast<long long>(r0 + r) * d + cc * 8) = v[u];
         }
     }
     __syncthreads();
@@ -230,68 +232,94 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
                                                              int d, int n_splits, void* __restrict__ out,
                                                              int out_bf16, float* __restrict__ lse,
                                                              long long out_stride_b) {
-    __shared__ float coef[kMaxSplits];
-    __shared__ float red[2];
     const int hh = blockIdx.x;
     const int b = blockIdx.y;
+    const int lane = threadIdx.x & (kWave - 1);
     const long long base = (static_cast<long long>(b) * h + hh) * n_splits;
     const float* ml = ws_ml + 2 * base;
     const float* ob = ws_o + base * d;
-    // Partials of empty splits are never written: their loads below read stale
-    // workspace bytes that are discarded by a select (never multiplied).
-    constexpr int kBatch = 8;
-    constexpr int kCols = 2;  // d <= 512 with 256 threads
-    float v[kCols][kBatch];
+    // Partials of empty splits (l = 0) are never written: their loads read
+    // stale workspace bytes that are skipped below (never multiplied).
+    // Thread t owns columns 2t and 2t + 1; the first splits' loads go first.
+    const int col = 2 * threadIdx.x;
+    const bool has_col = col < d;
+    constexpr int kBatch = 16;
+    float2 v[kBatch];
 #pragma unroll
-    for (int cix = 0; cix < kCols; ++cix)
+    for (int u = 0; u < kBatch; ++u)
+        v[u] = (has_col && u < n_splits) ? *reinterpret_cast<const float2*>(ob + static_cast<long long>(u) * d + col)
+                                         : make_float2(0.f, 0.f);
+    // split weights, derived by every wave on its own (no barrier): lane s
+    // holds split s of each group of 64
+    constexpr int kGroups = kMaxSplits / kWave;
+    float ms[kGroups], ls[kGroups];
+    float M = sink ? sink[hh] : -INFINITY;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int dd = threadIdx.x + cix * blockDim.x;
-            v[cix][u] = (dd < d && u < n_splits) ? ob[static_cast<long long>(u) * d + dd] : 0.f;
-        }
-    if (threadIdx.x < kWave) {
-        // one wave derives M, the denominator and the per-split weights
-        float M = sink ? sink[hh] : -INFINITY;
-        for (int s = threadIdx.x; s < n_splits; s += kWave)
-            if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
-        M = wave_max(M);
-        float den = 0.f;
-        if (M != -INFINITY)
-            for (int s = threadIdx.x; s < n_splits; s += kWave)
-                if (ml[2 * s + 1] > 0.f) den += ml[2 * s + 1] * expf(ml[2 * s] - M);
-        den = wave_sum(den);
-        if (M != -INFINITY && sink) den += expf(sink[hh] - M);
-        const float inv = den > 0.f ? 1.0f / den : 0.f;
-        for (int s = threadIdx.x; s < n_splits; s += kWave)
-            coef[s] = (ml[2 * s + 1] > 0.f && M != -INFINITY) ? expf(ml[2 * s] - M) * inv : 0.f;
-        if (threadIdx.x == 0) { red[0] = M; red[1] = den; }
+    for (int g = 0; g < kGroups; ++g) {
+        const int sp = g * kWave + lane;
+        ms[g] = sp < n_splits ? ml[2 * sp] : -INFINITY;
+        ls[g] = sp < n_splits ? ml[2 * sp + 1] : 0.f;
+        if (ls[g] > 0.f) M = fmaxf(M, ms[g]);
     }
-    __syncthreads();
+    M = wave_max(M);
+    float den = 0.f;
+    if (M != -INFINITY)
 #pragma unroll
-    for (int cix = 0; cix < kCols; ++cix) {
-        const int dd = threadIdx.x + cix * blockDim.x;
-        if (dd >= d) continue;
-        float acc = 0.f;
+        for (int g = 0; g < kGroups; ++g)
+            if (ls[g] > 0.f) den += ls[g] * expf(ms[g] - M);
+    den = wave_sum(den);
+    if (M != -INFINITY && sink) den += expf(sink[hh] - M);
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    float cf[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) cf[g] = (ls[g] > 0.f && M != -INFINITY) ? expf(ms[g] - M) * inv : 0.f;
+    auto coef = [&](int sp) -> float {  // sp is uniform: one scalar read of lane sp % 64
+        float c = 0.f;
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+            if (sp / kWave == g) c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cf[g]), sp % kWave));
+        return c;
+    };
+    float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        if (u < n_splits) {
+            const float c = coef(u);
+            if (c != 0.f) {
+                acc.x += v[u].x * c;
+                acc.y += v[u].y * c;
+            }
+        }
+    }
+    for (int s0 = kBatch; s0 < n_splits; s0 += kBatch) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
-            if (u < n_splits && coef[u] != 0.f) acc += v[cix][u] * coef[u];
-        for (int s0 = kBatch; s0 < n_splits; s0 += kBatch) {
-            float w[kBatch];
+            v[u] = (has_col && s0 + u < n_splits)
+                       ? *reinterpret_cast<const float2*>(ob + static_cast<long long>(s0 + u) * d + col)
+                       : make_float2(0.f, 0.f);
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u)
-                w[u] = (s0 + u < n_splits && coef[s0 + u] != 0.f) ? ob[static_cast<long long>(s0 + u) * d + dd] : 0.f;
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u)
-                if (s0 + u < n_splits && coef[s0 + u] != 0.f) acc += w[u] * coef[s0 + u];
+        for (int u = 0; u < kBatch; ++u) {
+            if (s0 + u < n_splits) {
+                const float c = coef(s0 + u);
+                if (c != 0.f) {
+                    acc.x += v[u].x * c;
+                    acc.y += v[u].y * c;
+                }
+            }
         }
-        const long long o = b * out_stride_b + static_cast<long long>(hh) * d + dd;
-        if (out_bf16) static_cast<uint16_t*>(out)[o] = f32_to_bf16(acc);
-        else static_cast<float*>(out)[o] = acc;
     }
-    if (lse && threadIdx.x == 0) {
-        const float M = red[0], den = red[1];
+    if (has_col) {
+        const long long o = b * out_stride_b + static_cast<long long>(hh) * d + col;
+        if (out_bf16) {
+            static_cast<uint16_t*>(out)[o] = f32_to_bf16(acc.x);
+            static_cast<uint16_t*>(out)[o + 1] = f32_to_bf16(acc.y);
+        } else {
+            static_cast<float*>(out)[o] = acc.x;
+            static_cast<float*>(out)[o + 1] = acc.y;
+        }
+    }
+    if (lse && threadIdx.x == 0)
         lse[static_cast<long long>(b) * h + hh] = den > 0.f ? M + logf(den) : -INFINITY;
-    }
 }
 
 // float32 path
@@ -386,23 +414,21 @@ hipError_t launch_attn_bf16(AttnArgs a, hipStream_t s) {
     a.ws_o = static_cast<float*>(a.ws);
     a.ws_ml = a.ws_o + static_cast<size_t>(a.batch) * a.h * ns * a.d;
     const size_t lds = sizeof(uint16_t) * (static_cast<size_t>(R + kHeadGroup) * (a.d + 8) + kHeadGroup * (R + 8));
-    // above 64 KB of dynamic LDS the kernel must opt in (gfx950 has 160 KB per workgroup)
-    static bool opted_in = false;
-    if (!opted_in) {
-        hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_partial_bf16<64>),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
-        hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_partial_bf16<32>),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
-        if (e1 != hipSuccess) return e1;
-        if (e2 != hipSuccess) return e2;
-        opted_in = true;
+    // above 64 KB of dynamic LDS the kernel must opt in (gfx950 has 160 KB per workgroup), once per device
+    {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+        static bool opted_in[64] = {};
+        if (!opted_in[dev]) {
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_partial_bf16<32>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
+            if (e != hipSuccess) return e;
+            opted_in[dev] = true;
+        }
     }
-    if (R == 64)
-        hipLaunchKernelGGL(k_attn_partial_bf16<64>, dim3(ns, a.h / kHeadGroup, a.batch), dim3(kAttnThreads), lds, s,
-                           a, ns);
-    else
-        hipLaunchKernelGGL(k_attn_partial_bf16<32>, dim3(ns, a.h / kHeadGroup, a.batch), dim3(kAttnThreads), lds, s,
-                           a, ns);
+    if (R != 32) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_attn_partial_bf16<32>, dim3(ns, a.h / kHeadGroup, a.batch), dim3(kAttnThreads), lds, s, a,
+                       ns);
     hipLaunchKernelGGL(k_attn_merge, dim3(a.h, a.batch), dim3(kAttnThreads), 0, s, a.ws_o, a.ws_ml, a.sink, a.h,
                        a.d, ns, a.out, a.out_bf16 ? 1 : 0, a.lse, a.out_stride_b);
     return hipGetLastError();
