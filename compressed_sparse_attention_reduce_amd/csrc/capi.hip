@@ -351,13 +351,14 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
 
     // c. score, with every workgroup's top-k candidates when the rows are long,
     //    then the exact top-k
-    csa::CandArgs ca{nullptr, 0, 0};
+    csa::CandArgs ca{nullptr, 0, 0, 0};
     if (bf && N > 0) {
         const int slots = csa::index_score_bf16_wgs(L->batch, n_scan, prep_wgs) + (completes ? 1 : 0);
         const int kpw = csa::index_score_bf16_keys_per_wg(L->batch, n_scan, prep_wgs);
         const int m = kpw > 0 ? csa::topk_cand_m(N, L->top_k, kpw) : -1;
+        const int mw = kpw > 0 ? csa::topk_cand_m(N, L->top_k, kpw / csa::kScoreWavesPerWg) : -1;
         if (m > 0 && slots <= kStepMaxSlots && N > 4 * L->top_k)
-            ca = csa::CandArgs{static_cast<unsigned long long*>(tws), slots, m};
+            ca = csa::CandArgs{static_cast<unsigned long long*>(tws), slots, m, mw < m ? mw : m};
     }
     csa::ScoreArgs sa{io->q_idx, io->w_idx, L->idx_keys, io->scores, L->batch, 1, L->h_i, L->d_i, n_scan,
                       nullptr, L->m, io->q_idx_stride_b, io->w_stride_b, L->idx_keys_stride_b,

@@ -35,6 +35,7 @@ namespace {
 
 constexpr int kScoreThreads = 256;
 constexpr int kWavesPerWg = kScoreThreads / kWave;
+static_assert(kWavesPerWg == kScoreWavesPerWg, "waves per workgroup as the host assumes");
 constexpr int kTileKeys = 16;
 constexpr int kHeads = 64;
 constexpr int kDi = 128;
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs
 
     if (!kCands) return;
     // 4. this workgroup's best m and their bound to its candidate slot
-    block_top_m(top, drop, a.cands.m,
+    block_top_m(top, drop, a.cands.m, a.cands.mw,
                 a.cands.lists + (static_cast<long long>(row) * a.cands.slots + wg) * (a.cands.m + 1), cs);
 }
 

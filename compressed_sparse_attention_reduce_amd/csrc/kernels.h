@@ -21,14 +21,18 @@ hipError_t launch_compress(const float* z, const float* c, const float* bias, co
 
 // ---- top-k candidates ------------------------------------------------------------
 constexpr int kMaxCandM1 = 64;  // longest per-slot candidate list
-// Per-slot candidate lists: [rows][slots][m + 1] composites, each slot's top
-// m + 1 (sorted, zero padded); the (m+1)-th is the largest one it dropped.
+// Per-slot candidate lists: [rows][slots][m + 1] composites: up to m of the
+// slot's largest (zero padded), then a bound at least as large as every
+// composite of the slot not listed.  Each wave of a producing workgroup
+// extracts its mw largest (mw <= m) before the workgroup merges them.
 struct CandArgs {
     unsigned long long* lists;
     int slots;
     int m;
+    int mw;
 };
-// m for slots of keys_per_slot keys, or -1 if lists would be too long.
+// m for slots of keys_per_slot keys (also mw, for a wave's share of them),
+// or -1 if lists would be too long.
 int topk_cand_m(int n, int k, int keys_per_slot);
 
 // ---- lightning-indexer score -------------------------------------------------
@@ -45,6 +49,7 @@ struct ScoreArgs {
     // keys to its slot of cands.lists (cands.slots must equal its grid width)
     CandArgs cands;
 };
+constexpr int kScoreWavesPerWg = 4;  // waves per workgroup of the bf16 score kernel
 // Scan workgroups per row and keys per scan workgroup of the bf16 score
 // kernel (extra = workgroups per row the kernel also runs for other jobs).
 int index_score_bf16_wgs(int rows, int n, int extra);

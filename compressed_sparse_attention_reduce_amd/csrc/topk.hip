@@ -73,6 +73,7 @@ struct FinalSmem {
         SortSmem ss;                      // counters of the sorted select (used after them)
     };
     u64 wmax[16], wmin[16];
+    uint32_t wcnt[16];
     uint32_t n_sel, n_pool;
 };
 
@@ -205,18 +206,19 @@ __device__ bool union_topk(FinalSmem& sm, const CandArgs& c, int row, int k, int
         }
         mx = umax64(mx, v[u]);
     }
-    if (threadIdx.x == 0) sm.n_pool = 0;
     block_max2(sm, maxdrop, mx);
     // only entries above every slot's bound can be proven; they go to the
-    // pool (and share the top bits where maxdrop and mx agree)
+    // pool, placed by a prefix sum (they share the top bits where maxdrop and
+    // mx agree)
+    uint32_t mine = 0;
 #pragma unroll
-    for (int u = 0; u < kUnionRegs; ++u) {
-        const bool live = v[u] > maxdrop;
-        const uint32_t p = wave_append_pos(live, &sm.n_pool);
-        if (live) sm.pool[p] = v[u];
-    }
+    for (int u = 0; u < kUnionRegs; ++u) mine += v[u] > maxdrop ? 1u : 0u;
+    uint32_t pos, np;
+    block_exclusive_scan(mine, sm.wcnt, pos, np);
+#pragma unroll
+    for (int u = 0; u < kUnionRegs; ++u)
+        if (v[u] > maxdrop) sm.pool[pos++] = v[u];
     __syncthreads();
-    const uint32_t np = sm.n_pool;
     // fewer than k proven entries: exact only if no slot left anything valid out
     if (np < static_cast<uint32_t>(k) && maxdrop != 0) return false;
     k_eff = np == 0 ? 0u
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(kCandThreads) void k_topk_cands(TopkArgs a, CandArg
         const uint32_t key = score_key(x[u]);
         lane_insert(top, drop, key_valid(key, x[u]) ? composite(key, static_cast<uint32_t>(i)) : 0ull);
     }
-    block_top_m(top, drop, c.m, c.lists + (static_cast<long long>(row) * c.slots + blockIdx.x) * (c.m + 1), cs);
+    block_top_m(top, drop, c.m, c.mw, c.lists + (static_cast<long long>(row) * c.slots + blockIdx.x) * (c.m + 1), cs);
 }
 
 }  // namespace
@@ -312,10 +314,12 @@ hipError_t launch_topk(const TopkArgs& a, const CandArgs* cands, hipStream_t s) 
         // standalone: produce per-chunk candidates when the row is long
         const int slots = (a.n + kCandChunk - 1) / kCandChunk;
         const int m = topk_cand_m(a.n, a.k, kCandChunk);
+        const int mw = topk_cand_m(a.n, a.k, kCandChunk / (kCandThreads / kWave));
         if (m > 0) {
             c.lists = static_cast<u64*>(a.ws);
             c.slots = slots;
             c.m = m;
+            c.mw = mw < m ? mw : m;
             hipLaunchKernelGGL(k_topk_cands, dim3(slots, rows), dim3(kCandThreads), 0, s, a, c);
         }
     }

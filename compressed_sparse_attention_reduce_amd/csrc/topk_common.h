@@ -107,6 +107,35 @@ __device__ inline void block_threshold(const uint32_t* hist, int nbins, uint32_t
     __syncthreads();
 }
 
+// Exclusive prefix of the threads' counts over the block (thread order) and
+// the block total, in every thread.  A butterfly inside each wave, one LDS
+// exchange of the wave totals (wtot: 16 uint32 of LDS).  At most 16 waves;
+// every thread calls it.
+__device__ inline void block_exclusive_scan(uint32_t mine, uint32_t* wtot, uint32_t& excl, uint32_t& total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    uint32_t pre = mine, sum = mine;
+#define CSA_SCAN_STEP(o)                                         \
+    {                                                            \
+        const uint32_t other = xor_lanes<o>(sum);                \
+        if (lane & (o)) pre += other;                            \
+        sum += other;                                            \
+    }
+    CSA_SCAN_STEP(1) CSA_SCAN_STEP(2) CSA_SCAN_STEP(4) CSA_SCAN_STEP(8) CSA_SCAN_STEP(16) CSA_SCAN_STEP(32)
+#undef CSA_SCAN_STEP
+    if (lane == 0) wtot[wv] = sum;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+        const uint32_t x = wtot[w];
+        tot += x;
+        before += w < wv ? x : 0u;
+    }
+    excl = before + pre - mine;
+    total = tot;
+}
+
 // ---- per-lane lists and the workgroup candidate list --------------------------------
 
 // Insert c into a lane's descending list; whatever falls off the end raises
@@ -123,9 +152,10 @@ __device__ inline void lane_insert(u64 (&top)[L], u64& drop, u64 c) {
 }
 
 // The wave's `cnt` largest listed composites, descending, to out[0..cnt)
-// (LDS, written by lane 0; zero where the wave has fewer).  Returns, in every
-// lane, the largest composite of the wave not extracted (a list's next head
-// or anything a lane dropped), and in *n_out how many nonzero were extracted.
+// (LDS, written by lane 0), zero padded up to a multiple of 8.  Returns, in
+// every lane, the largest composite of the wave not extracted (a list's next
+// head or anything a lane dropped), and in *n_out how many nonzero were
+// extracted.
 template <int L>
 __device__ inline u64 wave_extract_top(u64 (&top)[L], u64 drop, int cnt, u64* out, int* n_out) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -141,7 +171,7 @@ __device__ inline u64 wave_extract_top(u64 (&top)[L], u64 drop, int cnt, u64* ou
         }
     }
     *n_out = r;
-    for (int j = r + lane; j < cnt; j += kWave) out[j] = 0;
+    for (int j = r + lane; j < ((cnt + 7) & ~7); j += kWave) out[j] = 0;
     return umax64(wave_max_u64(top[0]), wave_max_u64(drop));
 }
 
@@ -153,37 +183,41 @@ struct CandSmem {
 };
 
 // Workgroup candidate list from the lanes' lists: out[0..m) (global) = the m
-// largest listed composites of the workgroup, descending, zero padded;
-// out[m] = an upper bound of every composite of the workgroup not in
-// out[0..m) (the largest of them, when lanes dropped nothing that matters).
-// m < kMaxCandM1; at most 16 waves.  Every thread calls it.
+// largest of the composites the waves extracted (each wave its mw largest),
+// descending, zero padded; out[m] = a bound at least as large as every
+// composite of the workgroup not in out[0..m).  mw <= m < kMaxCandM1; at
+// most 16 waves.  Every thread calls it, once per kernel.
 template <int L>
-__device__ inline void block_top_m(u64 (&top)[L], u64 drop, int m, u64* out, CandSmem& cs) {
+__device__ inline void block_top_m(u64 (&top)[L], u64 drop, int m, int mw, u64* out, CandSmem& cs) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const int nw = blockDim.x / kWave;
     int cnt;
-    const u64 bound = wave_extract_top(top, drop, m, cs.wtop[wv], &cnt);
+    const u64 bound = wave_extract_top(top, drop, mw, cs.wtop[wv], &cnt);
     if (lane == 0) {
         cs.wbound[wv] = bound;
         cs.wcount[wv] = cnt;
     }
     __syncthreads();
-    // merge: rank of each wave's entries among all waves' lists (unique values)
+    // merge: an entry's rank is the number of larger entries over all lists
+    // (unique values; the zero padding never counts); reads in unrolled runs
+    // of 8 so they are in flight together
     u64 maxb = 0;
     int total = 0;
     for (int w = 0; w < nw; ++w) {
         maxb = umax64(maxb, cs.wbound[w]);
         total += cs.wcount[w];
     }
+    const int mw8 = (mw + 7) & ~7;
     if (lane < cs.wcount[wv]) {
         const u64 x = cs.wtop[wv][lane];
-        int rank = lane;
-        for (int w = 0; w < nw; ++w) {
-            if (w == wv) continue;
-            const int cw = cs.wcount[w];
-            for (int j = 0; j < cw; ++j) rank += cs.wtop[w][j] > x ? 1 : 0;
-        }
+        int rank = 0;
+        for (int w = 0; w < nw; ++w)
+            for (int j0 = 0; j0 < mw8; j0 += 8) {
+                const u64* row = cs.wtop[w] + j0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) rank += row[j] > x ? 1 : 0;
+            }
         if (rank < m) out[rank] = x;
         else if (rank == m) out[m] = umax64(x, maxb);
     }
