@@ -184,40 +184,51 @@ __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs
 #pragma unroll
     for (int i = 0; i < kLaneTop; ++i) top[i] = 0;
 
-    // 3. stream: consume a tile, refill its ring slot kRing tiles ahead
-    for (int j0 = 0; j0 < n_mine; j0 += kRing) {
+    // 3. stream: consume a tile, refill its ring slot kRing tiles ahead.
+    //    The steady loop only refills tiles that exist; one more group may
+    //    refill past the end (clamped, as in the preload); the last group
+    //    refills nothing.  Every path leaves the same loads in flight, so the
+    //    waits stay exact, and no useless load is left outstanding at the end.
+    auto step = [&](int i, int j, bool refill) {
+        f32x4 acc[kMTiles];
 #pragma unroll
-        for (int i = 0; i < kRing; ++i) {
-            const int j = j0 + i;
-            f32x4 acc[kMTiles];
+        for (int mt = 0; mt < kMTiles; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int mt = 0; mt < kMTiles; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < kSteps; ++s)
-#pragma unroll
-                for (int mt = 0; mt < kMTiles; ++mt)
-                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], kb[i][s], acc[mt], 0, 0, 0);
-            load_tile(j + kRing, kb[i]);
-            // accumulator register r of M tile mt <-> head 16*mt + 4*lg + r, key li
-            float part = 0.f;
+        for (int s = 0; s < kSteps; ++s)
 #pragma unroll
             for (int mt = 0; mt < kMTiles; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], kb[i][s], acc[mt], 0, 0, 0);
+        if (refill) load_tile(j + kRing, kb[i]);
+        // accumulator register r of M tile mt <-> head 16*mt + 4*lg + r, key li
+        float part = 0.f;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) part += wr[mt][r] * fmaxf(acc[mt][r], 0.f);
-            part += xor_lanes_f32<16>(part);
-            part += xor_lanes_f32<32>(part);
-            const int key = (gw + j * waves_per_row) * kTileKeys + li;
-            const bool live = j < n_mine && key < n;
-            float sc = part;
-            if (a.q_pos && static_cast<long long>(a.ratio) * key + a.ratio - 1 > pos) sc = -INFINITY;
-            if (live && lg == 0) srow[key] = sc;
-            if (kCands) {
-                const uint32_t kk = score_key(sc);
-                const bool mine = live && lg == (i & 3) && key_valid(kk, sc);
-                lane_insert(top, drop, mine ? composite(kk, static_cast<uint32_t>(key)) : 0ull);
-            }
+        for (int mt = 0; mt < kMTiles; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part += wr[mt][r] * fmaxf(acc[mt][r], 0.f);
+        part += xor_lanes_f32<16>(part);
+        part += xor_lanes_f32<32>(part);
+        const int key = (gw + j * waves_per_row) * kTileKeys + li;
+        const bool live = j < n_mine && key < n;
+        float sc = part;
+        if (a.q_pos && static_cast<long long>(a.ratio) * key + a.ratio - 1 > pos) sc = -INFINITY;
+        if (live && lg == 0) srow[key] = sc;
+        if (kCands) {
+            const uint32_t kk = score_key(sc);
+            const bool mine = live && lg == (i & 3) && key_valid(kk, sc);
+            lane_insert(top, drop, mine ? composite(kk, static_cast<uint32_t>(key)) : 0ull);
         }
+    };
+    int j0 = 0;
+    for (; j0 + 2 * kRing <= n_mine; j0 += kRing)
+#pragma unroll
+        for (int i = 0; i < kRing; ++i) step(i, j0 + i, true);
+    if (j0 + kRing < n_mine) {  // wave-uniform
+#pragma unroll
+        for (int i = 0; i < kRing; ++i) step(i, j0 + i, true);
+        j0 += kRing;
     }
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) step(i, j0 + i, false);
 
     if (!kCands) return;
     // 4. this workgroup's best m and their bound to its candidate slot
