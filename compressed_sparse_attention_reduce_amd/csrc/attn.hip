@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
     // Thread t owns columns 2t and 2t + 1; the first splits' loads go first.
     const int col = 2 * threadIdx.x;
     const bool has_col = col < d;
-    constexpr int kBatch = 16;
+    constexpr int kBatch = 32;  // all splits of a 1024-row window in one round trip
     float2 v[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)

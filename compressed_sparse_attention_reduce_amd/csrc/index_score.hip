@@ -33,7 +33,7 @@ namespace csa {
 
 namespace {
 
-constexpr int kScoreThreads = 256;
+constexpr int kScoreThreads = 256;  // two workgroups per CU: one's tail overlaps the other's stream
 constexpr int kWavesPerWg = kScoreThreads / kWave;
 static_assert(kWavesPerWg == kScoreWavesPerWg, "waves per workgroup as the host assumes");
 constexpr int kTileKeys = 16;
@@ -49,33 +49,39 @@ static_assert(kRing % 4 == 0, "ring slot i feeds the lists of lane group i % 4")
 
 static_assert(kHeads * kQPitch * sizeof(uint16_t) >= kPrepMaxD * sizeof(float), "prep roles reuse the query LDS");
 
-// Score of one key held in LDS (as floats) for query row (b, tt): each quad
-// of lanes takes one head (a quarter of the key each).  Returns the score in
-// every thread.  red: 4 floats of LDS.
+// Score of one key held in LDS (as floats) for query row (b, tt): each run
+// of kDi / kPer lanes takes one head (kPer elements of the key each).
+// Returns the score in every thread.  red: kWavesPerWg floats of LDS.
 __device__ inline float score_one_key(const ScoreArgs& a, int b, int tt, const float* key, float* red) {
-    const int h = threadIdx.x >> 2;
-    const int part = threadIdx.x & 3;
+    constexpr int kPer = kDi * kHeads / kScoreThreads;  // key elements per thread
+    static_assert(kPer % 8 == 0 && kDi / kPer <= 8, "whole 16-byte query pieces, at most 8 lanes per head");
+    const int h = threadIdx.x / (kDi / kPer);
+    const int part = threadIdx.x % (kDi / kPer);
     const uint16_t* qh = static_cast<const uint16_t*>(a.q) + b * a.q_stride_b +
-                         (static_cast<long long>(tt) * kHeads + h) * kDi + 32 * part;
+                         (static_cast<long long>(tt) * kHeads + h) * kDi + kPer * part;
     float dot = 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kPer / 8; ++u) {
         const uint4 v = *reinterpret_cast<const uint4*>(qh + 8 * u);
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            dot += bf16_to_f32(static_cast<uint16_t>(w4[e] & 0xffffu)) * key[32 * part + 8 * u + 2 * e];
-            dot += bf16_to_f32(static_cast<uint16_t>(w4[e] >> 16)) * key[32 * part + 8 * u + 2 * e + 1];
+            dot += bf16_to_f32(static_cast<uint16_t>(w4[e] & 0xffffu)) * key[kPer * part + 8 * u + 2 * e];
+            dot += bf16_to_f32(static_cast<uint16_t>(w4[e] >> 16)) * key[kPer * part + 8 * u + 2 * e + 1];
         }
     }
-    dot += xor_lanes_f32<1>(dot);
-    dot += xor_lanes_f32<2>(dot);
+    if (kDi / kPer > 1) dot += xor_lanes_f32<1>(dot);
+    if (kDi / kPer > 2) dot += xor_lanes_f32<2>(dot);
+    if (kDi / kPer > 4) dot += xor_lanes_f32<4>(dot);
     const float wh = a.w[b * a.w_stride_b + static_cast<long long>(tt) * kHeads + h];
     float sc = part == 0 ? wh * fmaxf(dot, 0.f) : 0.f;
     sc = wave_sum(sc);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = sc;
     __syncthreads();
-    return red[0] + red[1] + red[2] + red[3];
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWavesPerWg; ++w) tot += red[w];
+    return tot;
 }
 
 template <bool kCands>
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs
     qstage(1, qv1);
     qstage(2, qv2);
     qstage(3, qv3);
-    if (threadIdx.x < 16) *reinterpret_cast<float4*>(ws + 4 * threadIdx.x) = wv4;
+    if (threadIdx.x < 16) *reinterpret_cast<float4*>(ws + 4 * threadIdx.x) = wv4;  // ws: 64 floats
     __syncthreads();
     bf16x8 qa[kMTiles][kSteps];
 #pragma unroll
