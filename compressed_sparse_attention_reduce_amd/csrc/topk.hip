@@ -206,25 +206,26 @@ __device__ bool union_topk(FinalSmem& sm, const CandArgs& c, int row, int k, int
         }
         mx = umax64(mx, v[u]);
     }
+    // (the sorted select's bin counters are cleared under the same barrier)
+    for (int i = threadIdx.x; i < (1 << kSelBits); i += kFinalThreads) sm.ss.cnt[i] = 0;
     block_max2(sm, maxdrop, mx);
-    // only entries above every slot's bound can be proven; they go to the
-    // pool, placed by a prefix sum (they share the top bits where maxdrop and
-    // mx agree)
-    uint32_t mine = 0;
+    // only entries above every slot's bound can be proven (they share the
+    // top bits where maxdrop and mx agree); the sorted select takes its first
+    // pass over them straight from the registers
 #pragma unroll
-    for (int u = 0; u < kUnionRegs; ++u) mine += v[u] > maxdrop ? 1u : 0u;
-    uint32_t pos, np;
-    block_exclusive_scan(mine, sm.wcnt, pos, np);
-#pragma unroll
-    for (int u = 0; u < kUnionRegs; ++u)
-        if (v[u] > maxdrop) sm.pool[pos++] = v[u];
-    __syncthreads();
+    for (int u = 0; u < kUnionRegs; ++u) v[u] = v[u] > maxdrop ? v[u] : 0ull;
+    if (mx <= maxdrop) {  // nothing provable
+        if (maxdrop != 0) return false;
+        k_eff = 0;
+        return true;
+    }
+    const FirstPass fp = select_first_pass(v, static_cast<uint32_t>(k), __clzll(static_cast<long long>(mx ^ maxdrop)),
+                                           out, sm.stage, sm.ss, sm.pool, &sm.n_pool);
     // fewer than k proven entries: exact only if no slot left anything valid out
-    if (np < static_cast<uint32_t>(k) && maxdrop != 0) return false;
-    k_eff = np == 0 ? 0u
-                    : select_sorted<kUnionRegs>(sm.pool, np, static_cast<uint32_t>(k),
-                                                __clzll(static_cast<long long>(mx ^ maxdrop)), out, sm.stage,
-                                                sm.ss, &sm.n_pool);
+    if (fp.total < static_cast<uint32_t>(k) && maxdrop != 0) return false;
+    k_eff = fp.done ? fp.written
+                    : fp.off + select_sorted<kUnionRegs>(sm.pool, fp.np, fp.need, fp.pb, out + fp.off, sm.stage,
+                                                         sm.ss, &sm.n_pool);
     return true;
 }
 

@@ -292,6 +292,83 @@ struct SortSmem {
     uint32_t start[1 << kSelBits];
 };
 
+// Outcome of select_first_pass.
+struct FirstPass {
+    uint32_t total;    // live entries
+    uint32_t written;  // indices written (when done)
+    bool done;
+    // otherwise the threshold bin's entries wait in pool[0..np): the rest of
+    // the selection is the `need` largest of them, written from out[off] on,
+    // with digits from bit pb
+    uint32_t np, off, need;
+    int pb;
+};
+
+// The first pass of select_sorted taken straight from registers: the
+// threads' v[] hold the live entries (zero = none), all sharing their top pb
+// bits; ss.cnt must be zero over its 1 << kSelBits bins, visible to every
+// thread.  Writes the indices of every entry that the pass places (the bins
+// above the threshold bin, and that bin too when it holds at most kStageCap
+// entries) to their final positions in out.  If the threshold bin is larger,
+// its entries are compacted into pool for select_sorted to finish.  Every
+// thread calls it; the result is the same in every thread.
+template <int V>
+__device__ inline FirstPass select_first_pass(u64 (&v)[V], uint32_t need, int pb, int* out, u64* stage, SortSmem& ss,
+                                              u64* pool, uint32_t* n_pool) {
+    const int db = min(kSelBits, 64 - pb);
+    const int nb = 1 << db;
+    const int shift = 64 - pb - db;
+    const u64 dmask = static_cast<u64>(nb - 1);
+#pragma unroll
+    for (int u = 0; u < V; ++u)
+        if (v[u]) atomicAdd(&ss.cnt[(v[u] >> shift) & dmask], 1u);
+    __syncthreads();
+    int td;
+    uint32_t above, at, total;
+    bin_starts(ss.cnt, ss.start, nb, need, td, above, at, total);
+    const bool all = td < 0;
+    const bool stage_td = !all && at <= static_cast<uint32_t>(kStageCap);
+    int dg[V];
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        dg[u] = v[u] ? static_cast<int>((v[u] >> shift) & dmask) : -1;
+        if (dg[u] >= 0 && (all || dg[u] > td || (dg[u] == td && stage_td)))
+            stage[ss.start[dg[u]] + atomicAdd(&ss.cnt[dg[u]], 1u)] = v[u];
+    }
+    if (threadIdx.x == 0) *n_pool = 0;
+    __syncthreads();
+    const uint32_t nst = all ? total : above + (stage_td ? at : 0u);
+    for (uint32_t i = threadIdx.x; i < nst; i += blockDim.x) {
+        const u64 x = stage[i];
+        const int d = static_cast<int>((x >> shift) & dmask);
+        const uint32_t s0 = ss.start[d];
+        const uint32_t c = ss.cnt[d];
+        uint32_t r = 0;
+        for (uint32_t j = 0; j < c; ++j) r += stage[s0 + j] > x ? 1u : 0u;
+        if (all || d > td || r < need - above) out[s0 + r] = composite_index(x);
+    }
+    FirstPass fp{};
+    fp.total = total;
+    if (all || stage_td) {
+        fp.done = true;
+        fp.written = all ? total : need;
+        return fp;
+    }
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const bool keep = dg[u] == td;
+        const uint32_t p = wave_append_pos(keep, n_pool);
+        if (keep) pool[p] = v[u];
+    }
+    __syncthreads();
+    fp.done = false;
+    fp.np = at;
+    fp.off = above;
+    fp.need = need - above;
+    fp.pb = pb + db;
+    return fp;
+}
+
 // The `need` largest of the unique nonzero composites pool[0..np) (LDS),
 // written sorted descending as indices to out[0 ..) (global); all of them if
 // there are fewer.  Returns how many were written.  Every entry must share
