@@ -242,6 +242,8 @@ int csa_sparse_attn(const void* q, const void* kv, const int* n_valid, const flo
 // (the kernel uses two workgroups per compute unit; beyond this many the step
 // falls back to the exact top-k path).
 constexpr int kStepMaxSlots = 1024;
+// rows short enough for every attention workgroup to take the exact top-k path itself
+constexpr int kFuseExactMaxN = 8192;
 
 static size_t step_topk_bytes(const csa_layer_desc* L) {
     return align256(static_cast<size_t>(L->batch) * kStepMaxSlots * csa::kMaxCandM1 * sizeof(unsigned long long));
@@ -367,8 +369,13 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
     if (e != hipSuccess) return launched(e, "csa_decode_step/index_score");
     csa::TopkArgs ta{io->scores, L->batch, 1, N, N, io->scores_stride_b, L->top_k, io->topk_idx,
                      io->topk_count, tws};
-    e = csa::launch_topk(ta, ca.lists ? &ca : nullptr, s);
-    if (e != hipSuccess) return launched(e, "csa_decode_step/topk");
+    // bf16 with candidate lists (or a short row): every attention workgroup
+    // selects the top k itself, no separate top-k launch
+    const bool fuse = bf && (ca.lists || N <= kFuseExactMaxN);
+    if (!fuse) {
+        e = csa::launch_topk(ta, ca.lists ? &ca : nullptr, s);
+        if (e != hipSuccess) return launched(e, "csa_decode_step/topk");
+    }
 
     // d+e. gather (fused into the attention on the bf16 path) and attention
     if (bf) {
@@ -400,7 +407,7 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
         a.d = L->d;
         a.n_max = n_max;
         a.ws = aws;
-        e = csa::launch_attn_bf16(a, s);
+        e = fuse ? csa::launch_topk_attn(ta, ca.lists ? &ca : nullptr, a, s) : csa::launch_attn_bf16(a, s);
         return launched(e, "csa_decode_step/attention");
     }
     e = csa::launch_gather(L->comp_kv, N, io->topk_idx, io->topk_count, L->top_k, L->swa, swa_head,

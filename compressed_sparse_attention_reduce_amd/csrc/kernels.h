@@ -122,6 +122,12 @@ size_t attn_workspace_bytes(bool bf16, int batch, int h, int d, int n_max);
 int attn_max_splits();
 int attn_max_rows();
 hipError_t launch_attn_bf16(AttnArgs a, hipStream_t s);
+// merge of the split partials already in a.ws (ws_o / ws_ml set), ns splits
+hipError_t launch_attn_merge(const AttnArgs& a, int ns, hipStream_t s);
+// decode step, bf16 gather mode, one query row per sequence: every attention
+// workgroup selects the top k itself (from cands when given, else the
+// exact path over the scores), then attends; topk idx / count written too.
+hipError_t launch_topk_attn(const TopkArgs& t, const CandArgs* cands, AttnArgs a, hipStream_t s);
 hipError_t launch_attn_f32(const void* q, const void* kv, const int* n_valid, const float* sink,
                            float scale, void* out, bool out_bf16, float* lse, int batch, int h,
                            int d, int n_max, long long q_stride_b, long long kv_stride_b,

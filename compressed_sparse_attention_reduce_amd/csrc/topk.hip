@@ -30,204 +30,17 @@
 #include "common.h"
 #include "kernels.h"
 #include "topk_common.h"
+#include "topk_final.h"
 
 namespace csa {
 
 namespace {
 
-constexpr int kFinalThreads = 1024;
-constexpr int kUnionRegs = 8;         // union entries per thread of the fast path
-constexpr int kUnionCap = kUnionRegs * kFinalThreads;
-constexpr int kPool = 2048;           // exact path: threshold-bin entries held in LDS
-constexpr int kRefineBits = 10;
 constexpr int kCandThreads = 256;
 constexpr int kCandChunk = 2048;      // scores per k_topk_cands workgroup
 constexpr int kCandPer = kCandChunk / kCandThreads;
-static_assert(kPool + kTopkMaxK <= kUnionCap, "exact-path candidates fit the pool");
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
-__device__ inline const float* score_row(const TopkArgs& a, int row) {
-    const int b = row / a.t;
-    const int tt = row - b * a.t;
-    return a.scores + b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s;
-}
-
-// Source of elements for the exact path: the score row (valid entries whose
-// key's top 12 bits equal bin12, or all valid entries when bin12 < 0).
-__device__ inline bool row_get(const float* row, long long i, int bin12, u64& c) {
-    const float x = row[i];
-    const uint32_t key = score_key(x);
-    if (!key_valid(key, x)) return false;
-    if (bin12 >= 0 && static_cast<int>(key >> (32 - kHistBits)) != bin12) return false;
-    c = composite(key, static_cast<uint32_t>(i));
-    return true;
-}
-
-// Dynamic LDS of k_topk_final (about 100 KB).
-struct FinalSmem {
-    u64 pool[kUnionCap];                  // candidates of the sorted select
-    u64 stage[kTopkMaxK + kStageCap];     // its staging; the exact path's picks above the threshold before
-    union {
-        uint32_t hist[kHistBins];         // row histograms of the exact path
-        SortSmem ss;                      // counters of the sorted select (used after them)
-    };
-    u64 wmax[16], wmin[16];
-    uint32_t wcnt[16];
-    uint32_t n_sel, n_pool;
-};
-
-// Block maxima of the threads' a and b, in every thread.
-__device__ inline void block_max2(FinalSmem& sm, u64& a, u64& b) {
-    const int wv = threadIdx.x / kWave;
-    const int nw = blockDim.x / kWave;
-    a = wave_max_u64(a);
-    b = wave_max_u64(b);
-    if ((threadIdx.x & (kWave - 1)) == 0) {
-        sm.wmax[wv] = a;
-        sm.wmin[wv] = b;
-    }
-    __syncthreads();
-    a = 0;
-    b = 0;
-    for (int w = 0; w < nw; ++w) {
-        a = umax64(a, sm.wmax[w]);
-        b = umax64(b, sm.wmin[w]);
-    }
-}
-
-// Exact top-k of one score row by one workgroup, as sorted indices into out.
-// Returns k_eff.
-__device__ uint32_t exact_row_topk(FinalSmem& sm, const float* row, int n, int k, int* out) {
-    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) sm.hist[i] = 0;
-    if (threadIdx.x == 0) { sm.n_sel = 0; sm.n_pool = 0; }
-    __syncthreads();
-    for (long long i = threadIdx.x; i < n; i += blockDim.x) {
-        const float x = row[i];
-        const uint32_t key = score_key(x);
-        if (key_valid(key, x)) atomicAdd(&sm.hist[key >> (32 - kHistBits)], 1u);
-    }
-    __syncthreads();
-    int tb;
-    uint32_t above, at, total;
-    block_threshold(sm.hist, kHistBins, static_cast<uint32_t>(k), tb, above, at, total);
-    const bool pool_fits = at <= kPool;
-    // picks above the threshold bin go to stage, the bin's entries to pool
-    for (long long base = 0; base < n; base += blockDim.x) {
-        const long long i = base + threadIdx.x;
-        u64 c = 0;
-        int bin = -2;
-        if (i < n && row_get(row, i, -1, c)) bin = static_cast<int>(c >> (64 - kHistBits));
-        const uint32_t ps = wave_append_pos(bin > tb, &sm.n_sel);
-        if (bin > tb) sm.stage[ps] = c;
-        const uint32_t pp = wave_append_pos(bin == tb && pool_fits, &sm.n_pool);
-        if (bin == tb && pool_fits) sm.pool[pp] = c;
-    }
-    __syncthreads();
-    if (tb >= 0) {
-        uint32_t need = static_cast<uint32_t>(k) - above;
-        u64 prefix = static_cast<u64>(tb);
-        int pb = kHistBits;
-        // the threshold bin overflowed the pool: more digits over the row
-        while (!pool_fits || sm.n_pool > kPool) {
-            const int db = min(kRefineBits, 64 - pb);
-            const int nb = 1 << db;
-            for (int i = threadIdx.x; i < nb; i += blockDim.x) sm.hist[i] = 0;
-            __syncthreads();
-            for (long long i = threadIdx.x; i < n; i += blockDim.x) {
-                u64 c;
-                if (row_get(row, i, tb, c) && (c >> (64 - pb)) == prefix)
-                    atomicAdd(&sm.hist[(c >> (64 - pb - db)) & (nb - 1)], 1u);
-            }
-            __syncthreads();
-            int td;
-            uint32_t ab, at2, tot;
-            block_threshold(sm.hist, nb, need, td, ab, at2, tot);
-            const bool fits = at2 <= kPool;
-            if (threadIdx.x == 0) sm.n_pool = 0;
-            __syncthreads();
-            for (long long base = 0; base < n; base += blockDim.x) {
-                const long long i = base + threadIdx.x;
-                u64 c = 0;
-                int dg = -2;
-                if (i < n && row_get(row, i, tb, c) && (c >> (64 - pb)) == prefix)
-                    dg = static_cast<int>((c >> (64 - pb - db)) & (nb - 1));
-                const uint32_t ps = wave_append_pos(dg > td, &sm.n_sel);
-                if (dg > td) sm.stage[ps] = c;
-                const uint32_t pp = wave_append_pos(dg == td && fits, &sm.n_pool);
-                if (dg == td && fits) sm.pool[pp] = c;
-            }
-            __syncthreads();
-            need -= ab;
-            prefix = (prefix << db) | static_cast<u64>(static_cast<uint32_t>(td));
-            pb += db;
-            if (fits) break;
-        }
-    }
-    // all candidates (the bin's entries, then the picks above it) into the pool
-    const uint32_t nb_pool = tb >= 0 ? sm.n_pool : 0u;
-    const uint32_t ns = sm.n_sel;
-    for (uint32_t i = threadIdx.x; i < ns; i += blockDim.x) sm.pool[nb_pool + i] = sm.stage[i];
-    __syncthreads();
-    const uint32_t np = nb_pool + ns;
-    // they share the top bits where their largest and smallest agree
-    u64 hi = 0, lo_c = 0;
-    for (uint32_t i = threadIdx.x; i < np; i += blockDim.x) {
-        hi = umax64(hi, sm.pool[i]);
-        lo_c = umax64(lo_c, ~sm.pool[i]);
-    }
-    block_max2(sm, hi, lo_c);
-    const int pb = np <= 1 ? 0 : __clzll(static_cast<long long>(hi ^ ~lo_c));
-    return select_sorted<kUnionRegs>(sm.pool, np, static_cast<uint32_t>(k), pb, out, sm.stage, sm.ss, &sm.n_pool);
-}
-
-// Fast path: top-k of the union of per-slot candidates, as sorted indices
-// into out.  Returns false if the union cannot prove the answer.
-__device__ bool union_topk(FinalSmem& sm, const CandArgs& c, int row, int k, int* out, uint32_t& k_eff) {
-    const int m1 = c.m + 1;
-    const int total = c.slots * m1;
-    if (total > kUnionCap) return false;
-    const u64* lists = c.lists + static_cast<long long>(row) * total;
-    // kept entries (first m of every slot) into registers; entry m of each
-    // slot bounds what that slot did not keep
-    u64 v[kUnionRegs];
-#pragma unroll
-    for (int u = 0; u < kUnionRegs; ++u) {
-        const int i = threadIdx.x + u * kFinalThreads;
-        v[u] = i < total ? lists[i] : 0ull;
-    }
-    u64 maxdrop = 0, mx = 0;
-#pragma unroll
-    for (int u = 0; u < kUnionRegs; ++u) {
-        const int i = threadIdx.x + u * kFinalThreads;
-        if (i < total && i % m1 == c.m) {
-            maxdrop = umax64(maxdrop, v[u]);
-            v[u] = 0;
-        }
-        mx = umax64(mx, v[u]);
-    }
-    // (the sorted select's bin counters are cleared under the same barrier)
-    for (int i = threadIdx.x; i < (1 << kSelBits); i += kFinalThreads) sm.ss.cnt[i] = 0;
-    block_max2(sm, maxdrop, mx);
-    // only entries above every slot's bound can be proven (they share the
-    // top bits where maxdrop and mx agree); the sorted select takes its first
-    // pass over them straight from the registers
-#pragma unroll
-    for (int u = 0; u < kUnionRegs; ++u) v[u] = v[u] > maxdrop ? v[u] : 0ull;
-    if (mx <= maxdrop) {  // nothing provable
-        if (maxdrop != 0) return false;
-        k_eff = 0;
-        return true;
-    }
-    const FirstPass fp = select_first_pass(v, static_cast<uint32_t>(k), __clzll(static_cast<long long>(mx ^ maxdrop)),
-                                           out, sm.stage, sm.ss, sm.pool, &sm.n_pool);
-    // fewer than k proven entries: exact only if no slot left anything valid out
-    if (fp.total < static_cast<uint32_t>(k) && maxdrop != 0) return false;
-    k_eff = fp.done ? fp.written
-                    : fp.off + select_sorted<kUnionRegs>(sm.pool, fp.np, fp.need, fp.pb, out + fp.off, sm.stage,
-                                                         sm.ss, &sm.n_pool);
-    return true;
-}
 
 __global__ __launch_bounds__(kFinalThreads) void k_topk_final(TopkArgs a, CandArgs c) {
     extern __shared__ __attribute__((aligned(16))) unsigned char final_smem[];
