@@ -157,11 +157,24 @@ __device__ inline void attn_split(const AttnArgs& a, int n_splits, int split, in
     float x[4];
     if (has_tile) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
-        for (int ks = 0; ks < d / 32; ++ks) {
-            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + li * pitch + 32 * ks + 8 * lg);
-            const bf16x8 kb = *reinterpret_cast<const bf16x8*>(tile + my_row * pitch + 32 * ks + 8 * lg);
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb, s, 0, 0, 0);
+        const uint16_t* qrow = qs + li * pitch + 8 * lg;
+        const uint16_t* krow = tile + my_row * pitch + 8 * lg;
+        const int nks = d / 32;
+        int ks = 0;
+        for (; ks + 4 <= nks; ks += 4) {  // four k-steps' operands in flight at once
+            bf16x8 qa[4], kb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                qa[u] = *reinterpret_cast<const bf16x8*>(qrow + 32 * (ks + u));
+                kb[u] = *reinterpret_cast<const bf16x8*>(krow + 32 * (ks + u));
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[u], kb[u], s, 0, 0, 0);
         }
+        for (; ks < nks; ++ks)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(qrow + 32 * ks),
+                                                        *reinterpret_cast<const bf16x8*>(krow + 32 * ks), s, 0,
+                                                        0, 0);
         // accumulator register r <-> head 4*lg + r, row my_row
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] = my_row < rows ? s[r] * a.scale : -INFINITY;

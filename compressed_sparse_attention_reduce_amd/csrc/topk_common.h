@@ -77,12 +77,9 @@ __device__ inline void block_threshold(const uint32_t* hist, int nbins, uint32_t
     if (lane == 0) wsum[wv] = sum;
     if (threadIdx.x == 0) { res[0] = 0xffffffffu; res[1] = 0; res[2] = 0; }
     __syncthreads();
-    uint32_t before = 0, tot = 0;
-    for (int w = 0; w < nw; ++w) {
-        const uint32_t x = wsum[w];
-        tot += x;
-        before += w < wv ? x : 0u;
-    }
+    const uint32_t wt = lane < nw ? wsum[lane] : 0u;
+    const uint32_t tot = wave_sum_u32(wt);
+    const uint32_t before = wave_sum_u32(lane < wv ? wt : 0u);
     const uint32_t incl = before + pre;  // entries in bins >= lo
     const uint32_t excl = incl - mine;   // entries in bins >= hi
     if (tot < need) {
@@ -105,35 +102,6 @@ __device__ inline void block_threshold(const uint32_t* hist, int nbins, uint32_t
     at = res[2];
     total = tot;
     __syncthreads();
-}
-
-// Exclusive prefix of the threads' counts over the block (thread order) and
-// the block total, in every thread.  A butterfly inside each wave, one LDS
-// exchange of the wave totals (wtot: 16 uint32 of LDS).  At most 16 waves;
-// every thread calls it.
-__device__ inline void block_exclusive_scan(uint32_t mine, uint32_t* wtot, uint32_t& excl, uint32_t& total) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
-    const int nw = blockDim.x / kWave;
-    uint32_t pre = mine, sum = mine;
-#define CSA_SCAN_STEP(o)                                         \
-    {                                                            \
-        const uint32_t other = xor_lanes<o>(sum);                \
-        if (lane & (o)) pre += other;                            \
-        sum += other;                                            \
-    }
-    CSA_SCAN_STEP(1) CSA_SCAN_STEP(2) CSA_SCAN_STEP(4) CSA_SCAN_STEP(8) CSA_SCAN_STEP(16) CSA_SCAN_STEP(32)
-#undef CSA_SCAN_STEP
-    if (lane == 0) wtot[wv] = sum;
-    __syncthreads();
-    uint32_t before = 0, tot = 0;
-    for (int w = 0; w < nw; ++w) {
-        const uint32_t x = wtot[w];
-        tot += x;
-        before += w < wv ? x : 0u;
-    }
-    excl = before + pre - mine;
-    total = tot;
 }
 
 // ---- per-lane lists and the workgroup candidate list --------------------------------
@@ -235,55 +203,115 @@ constexpr int kStageCap = 256;  // threshold-bin entries that are ranked in plac
 // start[b] = entries in bins > b.  Also finds, like block_threshold, the
 // largest bin tb with suffix(tb) >= need (tb = -1 if total < need), with
 // above = start[tb], at = cnt[tb], total = all entries; and zeroes cnt so it
-// can serve as per-bin cursors.  Ends with a barrier.  At most 16 waves.
+// can serve as per-bin cursors.  The first kScanWaves waves do the scan, each
+// lane a run of bins counted from the top (moved through registers with
+// 16-byte LDS accesses), then lane prefixes and one exchange of the wave
+// totals; the other waves only wait.  nbins <= 1 << kSelBits, a power of
+// two; cnt and start 16-byte aligned; blockDim >= kScanWaves * 64.  Ends
+// with a barrier.
+constexpr int kScanWaves = 4;
 __device__ inline void bin_starts(uint32_t* cnt, uint32_t* start, int nbins, uint32_t need, int& tb,
                                   uint32_t& above, uint32_t& at, uint32_t& total) {
-    __shared__ uint32_t wsum[16];
-    __shared__ uint32_t res[3];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
-    const int nw = blockDim.x / kWave;
-    const int per = (nbins + blockDim.x - 1) / blockDim.x;
-    const int hi = max(nbins - per * static_cast<int>(threadIdx.x), 0);  // bins [lo, hi)
+    __shared__ uint32_t wsum[kScanWaves];
+    __shared__ uint32_t res[4];
+    constexpr int kLanes = kScanWaves * kWave;
+    constexpr int kPer = (1 << kSelBits) / kLanes;  // bins per lane at full width
+    static_assert(kPer % 4 == 0, "whole 16-byte groups of bins");
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wv = t / kWave;
+    const bool scanner = t < kLanes;
+    const bool full = nbins == (1 << kSelBits);
+    // this lane's run of bins [lo, hi), runs ordered from the top bin down
+    const int per = full ? kPer : (nbins + kLanes - 1) / kLanes;
+    const int hi = scanner ? max(nbins - per * t, 0) : 0;
     const int lo = max(hi - per, 0);
+    uint4 q[kPer / 4];
     uint32_t mine = 0;
-    for (int b = lo; b < hi; ++b) mine += cnt[b];
-    uint32_t pre = mine, sum = mine;
-#define CSA_SCAN_STEP(o)                                         \
-    {                                                            \
-        const uint32_t other = xor_lanes<o>(sum);                \
-        if (lane & (o)) pre += other;                            \
-        sum += other;                                            \
-    }
-    CSA_SCAN_STEP(1) CSA_SCAN_STEP(2) CSA_SCAN_STEP(4) CSA_SCAN_STEP(8) CSA_SCAN_STEP(16) CSA_SCAN_STEP(32)
-#undef CSA_SCAN_STEP
-    if (lane == 0) wsum[wv] = sum;
-    if (threadIdx.x == 0) { res[0] = 0xffffffffu; res[1] = 0; res[2] = 0; }
-    __syncthreads();
-    uint32_t before = 0, tot = 0;
-    for (int w = 0; w < nw; ++w) {
-        const uint32_t x = wsum[w];
-        tot += x;
-        before += w < wv ? x : 0u;
-    }
-    uint32_t acc = before + pre - mine;  // entries in bins >= hi
-    for (int b = hi - 1; b >= lo; --b) {
-        const uint32_t c = cnt[b];
-        start[b] = acc;
-        if (tot >= need && acc < need && acc + c >= need) {
-            res[0] = static_cast<uint32_t>(b);
-            res[1] = acc;
-            res[2] = c;
+    if (scanner) {
+        if (full) {
+#pragma unroll
+            for (int j = 0; j < kPer / 4; ++j) {
+                q[j] = *reinterpret_cast<const uint4*>(cnt + lo + 4 * j);
+                mine += q[j].x + q[j].y + q[j].z + q[j].w;
+            }
+        } else {
+            for (int b = lo; b < hi; ++b) mine += cnt[b];
         }
-        acc += c;
-        cnt[b] = 0;
     }
-    if (tot < need && threadIdx.x == 0) res[1] = tot;
+    uint32_t pre = mine, sum = mine;
+    if (wv < kScanWaves) {
+#define CSA_SCAN_STEP(o)                                         \
+        {                                                        \
+            const uint32_t other = xor_lanes<o>(sum);            \
+            if (lane & (o)) pre += other;                        \
+            sum += other;                                        \
+        }
+        CSA_SCAN_STEP(1) CSA_SCAN_STEP(2) CSA_SCAN_STEP(4) CSA_SCAN_STEP(8) CSA_SCAN_STEP(16) CSA_SCAN_STEP(32)
+#undef CSA_SCAN_STEP
+        if (lane == 0) wsum[wv] = sum;
+    }
+    __syncthreads();
+    if (wv < kScanWaves) {
+        uint32_t tot = 0, before = 0;
+#pragma unroll
+        for (int w = 0; w < kScanWaves; ++w) {
+            const uint32_t x = wsum[w];
+            tot += x;
+            before += w < wv ? x : 0u;
+        }
+        uint32_t acc = before + pre - mine;  // entries in bins >= hi
+        int found = -1;
+        uint32_t f_above = 0, f_at = 0;
+        auto visit = [&](uint32_t c, int b) -> uint32_t {
+            const uint32_t s0 = acc;
+            if (tot >= need && acc < need && acc + c >= need) {
+                found = b;
+                f_above = acc;
+                f_at = c;
+            }
+            acc += c;
+            return s0;
+        };
+        if (full) {
+            uint4 st[kPer / 4];
+#pragma unroll
+            for (int j = kPer / 4 - 1; j >= 0; --j) {  // from the run's top bin down
+                st[j].w = visit(q[j].w, lo + 4 * j + 3);
+                st[j].z = visit(q[j].z, lo + 4 * j + 2);
+                st[j].y = visit(q[j].y, lo + 4 * j + 1);
+                st[j].x = visit(q[j].x, lo + 4 * j);
+            }
+#pragma unroll
+            for (int j = 0; j < kPer / 4; ++j) {
+                *reinterpret_cast<uint4*>(start + lo + 4 * j) = st[j];
+                *reinterpret_cast<uint4*>(cnt + lo + 4 * j) = make_uint4(0, 0, 0, 0);
+            }
+        } else {
+            for (int b = hi - 1; b >= lo; --b) {
+                start[b] = visit(cnt[b], b);
+                cnt[b] = 0;
+            }
+        }
+        if (found >= 0) {
+            res[0] = static_cast<uint32_t>(found);
+            res[1] = f_above;
+            res[2] = f_at;
+        }
+        if (t == 0) {
+            res[3] = tot;
+            if (tot < need) {
+                res[0] = 0xffffffffu;
+                res[1] = tot;
+                res[2] = 0;
+            }
+        }
+    }
     __syncthreads();
     tb = static_cast<int>(res[0]);
     above = res[1];
     at = res[2];
-    total = tot;
+    total = res[3];
 }
 
 // LDS scratch of select_sorted.

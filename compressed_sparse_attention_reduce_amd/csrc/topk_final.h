@@ -46,27 +46,41 @@ struct FinalSmem {
         SortSmem ss;                      // counters of the sorted select (used after them)
     };
     u64 wmax[16], wmin[16];
-    uint32_t wcnt[16];
+    uint32_t wcnt[16], wcnt2[16];
     uint32_t n_sel, n_pool;
 };
 
-// Block maxima of the threads' a and b, in every thread.
+// Block maxima of the threads' a and b, in every thread: lane reductions,
+// one LDS exchange of the wave results (one read per lane), lane reductions.
 __device__ inline void block_max2(FinalSmem& sm, u64& a, u64& b) {
+    const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const int nw = blockDim.x / kWave;
     a = wave_max_u64(a);
     b = wave_max_u64(b);
-    if ((threadIdx.x & (kWave - 1)) == 0) {
+    if (lane == 0) {
         sm.wmax[wv] = a;
         sm.wmin[wv] = b;
     }
     __syncthreads();
-    a = 0;
-    b = 0;
-    for (int w = 0; w < nw; ++w) {
-        a = umax64(a, sm.wmax[w]);
-        b = umax64(b, sm.wmin[w]);
+    a = wave_max_u64(lane < nw ? sm.wmax[lane] : 0ull);
+    b = wave_max_u64(lane < nw ? sm.wmin[lane] : 0ull);
+}
+
+// The same for 32-bit values.
+__device__ inline void block_max2_u32(FinalSmem& sm, uint32_t& a, uint32_t& b) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    a = wave_max_u32(a);
+    b = wave_max_u32(b);
+    if (lane == 0) {
+        sm.wcnt[wv] = a;
+        sm.wcnt2[wv] = b;
     }
+    __syncthreads();
+    a = wave_max_u32(lane < nw ? sm.wcnt[lane] : 0u);
+    b = wave_max_u32(lane < nw ? sm.wcnt2[lane] : 0u);
 }
 
 // Exact top-k of one score row by one workgroup, as sorted indices into out.
@@ -169,31 +183,44 @@ __device__ bool union_topk(FinalSmem& sm, const CandArgs& c, int row, int k, int
         const int i = threadIdx.x + u * kFinalThreads;
         v[u] = i < total ? lists[i] : 0ull;
     }
-    u64 maxdrop = 0, mx = 0;
+    // The bound test only needs the score-key words (the high 32 bits): the
+    // largest bound rounded up to the end of its key is still an upper bound
+    // of everything the slots left out, and entries above it are provable.
+    uint32_t drop_hi = 0, mx_hi = 0;
+    // entry i is a slot's bound when i % m1 == m; i = t + u * kFinalThreads,
+    // so the remainder advances by a fixed step (no division per entry)
+    const int rstep = kFinalThreads % m1;
+    int rem = static_cast<int>(threadIdx.x) % m1;
 #pragma unroll
     for (int u = 0; u < kUnionRegs; ++u) {
-        const int i = threadIdx.x + u * kFinalThreads;
-        if (i < total && i % m1 == c.m) {
-            maxdrop = umax64(maxdrop, v[u]);
+        const uint32_t hi = static_cast<uint32_t>(v[u] >> 32);
+        if (rem == c.m) {
+            drop_hi = hi > drop_hi ? hi : drop_hi;
             v[u] = 0;
+        } else {
+            mx_hi = hi > mx_hi ? hi : mx_hi;
         }
-        mx = umax64(mx, v[u]);
+        rem += rstep;
+        rem -= rem >= m1 ? m1 : 0;
     }
     // (the sorted select's bin counters are cleared under the same barrier)
     for (int i = threadIdx.x; i < (1 << kSelBits); i += kFinalThreads) sm.ss.cnt[i] = 0;
-    block_max2(sm, maxdrop, mx);
+    block_max2_u32(sm, drop_hi, mx_hi);
+    const u64 maxdrop = drop_hi ? ((static_cast<u64>(drop_hi) << 32) | 0xffffffffull) : 0ull;
     // only entries above every slot's bound can be proven (they share the
-    // top bits where maxdrop and mx agree); the sorted select takes its first
-    // pass over them straight from the registers
+    // top bits where the key words of maxdrop and the largest entry agree);
+    // the sorted select takes its first pass over them straight from the
+    // registers
 #pragma unroll
     for (int u = 0; u < kUnionRegs; ++u) v[u] = v[u] > maxdrop ? v[u] : 0ull;
-    if (mx <= maxdrop) {  // nothing provable
+    if (mx_hi <= drop_hi) {  // nothing provable
         if (maxdrop != 0) return false;
         k_eff = 0;
         return true;
     }
-    const FirstPass fp = select_first_pass(v, static_cast<uint32_t>(k), __clzll(static_cast<long long>(mx ^ maxdrop)),
-                                           out, sm.stage, sm.ss, sm.pool, &sm.n_pool);
+    const int pb = __clz(static_cast<int>(mx_hi ^ drop_hi));
+    const FirstPass fp = select_first_pass(v, static_cast<uint32_t>(k), pb, out, sm.stage, sm.ss, sm.pool,
+                                           &sm.n_pool);
     // fewer than k proven entries: exact only if no slot left anything valid out
     if (fp.total < static_cast<uint32_t>(k) && maxdrop != 0) return false;
     k_eff = fp.done ? fp.written
