@@ -424,6 +424,33 @@ def test_decode_step(csa, case):
         _check_step(x, shape, st, outs, b)
 
 
+def test_decode_step_clustered_scores_take_exact_path(csa):
+    """600 consecutive indexer keys set to copies of the best key: every tile
+    they fall in holds 16 of the top k, more than any candidate list keeps, so
+    the union cannot prove the answer and the top-k takes the exact select over
+    the score row.  The result must still be the oracle's, ties between the
+    copies broken by the lower index."""
+    shape = synth.with_(synth.SHAPES["ctx8k"], ctx=131072, n_comp=32768)
+    x = synth.make_decode_inputs(shape, 4001)
+    n0 = x["n_comp"]
+    s = oracle.index_score(as_f64(x["q_idx"][0])[None], x["w_idx"][0][None], as_f64(x["idx_keys"][0, :n0]))[0]
+    x["idx_keys"][0, 10000:10600] = x["idx_keys"][0, int(np.argmax(s))]
+    st, outs, _ = _run_step(csa, x, shape)
+    _check_step(x, shape, st, outs, 0)
+    # the scenario happened: the selection is (all but possibly one of) the copies
+    gi = outs["topk_idx"][0].cpu().numpy()
+    assert np.isin(gi, np.arange(10000, 10600)).sum() >= shape.top_k - 1
+
+
+def test_decode_step_long_top_k_without_candidate_lists(csa):
+    """top_k 2048 over 10,000 blocks: candidate lists would be too long, so
+    the step runs the separate top-k and attention kernels."""
+    shape = synth.with_(synth.SHAPES["ctx8k"], ctx=40000, n_comp=10000, top_k=2048)
+    x = synth.make_decode_inputs(shape, 4002)
+    st, outs, _ = _run_step(csa, x, shape)
+    _check_step(x, shape, st, outs, 0)
+
+
 def test_decode_step_batch128k_full_size(csa):
     shape = synth.SHAPES["batch128k"]
     x = synth.make_decode_inputs(shape, 3000)
