@@ -17,6 +17,7 @@ from .csa import (
     decode_step,
     gather,
     index_score,
+    index_score_fp8,
     kv_norm,
     sparse_attn,
     topk,
@@ -27,6 +28,7 @@ __all__ = [
     "compress",
     "kv_norm",
     "index_score",
+    "index_score_fp8",
     "topk",
     "gather",
     "sparse_attn",

@@ -169,6 +169,39 @@ def index_score(q, w, K, q_pos=None, ratio: int = 4) -> np.ndarray:
     return out
 
 
+def index_score_fp8(q_codes, w, k_codes, k_scale, q_pos=None, ratio: int = 4) -> np.ndarray:
+    """The index score with FP8 E4M3 query and keys (the pages' FP8 scoring
+    path: keys stored as FP8_E4M3, page 1, ``single_shot_inference.py``, "B2").
+
+    Key s decodes to ``e4m3(k_codes[s]) * k_scale[s]``; the query decodes to
+    ``e4m3(q_codes)`` with any per-head scale already folded into ``w`` (for a
+    positive scale c, ``ReLU(c * x) = c * ReLU(x)``).  So
+    ``I[t,s] = sum_h w[t,h] * ReLU(k_scale[s] * (e4m3(q[t,h]) . e4m3(K[s])))``,
+    computed exactly in float64 from the decoded values.  ``q_codes``
+    ``[T, H, d]`` uint8, ``w`` ``[T, H]``, ``k_codes`` ``[N, d]`` uint8,
+    ``k_scale`` ``[N]``.  Returns float64 ``[T, N]`` (causal mask as in
+    :func:`index_score`).
+    """
+    from .numfmt import e4m3_decode
+
+    qd = e4m3_decode(np.asarray(q_codes, dtype=np.uint8))
+    kd = e4m3_decode(np.asarray(k_codes, dtype=np.uint8))
+    ks = np.asarray(k_scale, dtype=np.float64)
+    if kd.ndim != 2 or ks.shape != (kd.shape[0],):
+        raise ValueError(f"bad key shapes {kd.shape} {ks.shape}")
+    w = np.asarray(w, dtype=np.float64)
+    T, H, _ = qd.shape
+    out = np.empty((T, kd.shape[0]), dtype=np.float64)
+    for t in range(T):
+        dots = (qd[t] @ kd.T) * ks[None, :]    # [H, N]: k_scale[s] * (q[t,h] . K[s])
+        out[t] = (w[t][:, None] * np.maximum(dots, 0.0)).sum(axis=0)
+    if q_pos is not None:
+        pos = np.asarray(q_pos, dtype=np.int64).reshape(T)
+        block_end = ratio * np.arange(kd.shape[0], dtype=np.int64) + (ratio - 1)
+        out[block_end[None, :] > pos[:, None]] = -np.inf
+    return out
+
+
 # ---------------------------------------------------------------------------
 # (3) top-k
 # ---------------------------------------------------------------------------

@@ -10,6 +10,13 @@ decoded here from their published definitions, never through a GPU library:
   sizes"; page 1, dsv4/kernels/compressor/production_compress.py, the
   ``compressed.bfloat16()`` return).
 * float32: numpy's own binary32 (RNE on conversion).
+* FP8 E4M3 (the OCP 8-bit floating point "E4M3FN" encoding): sign bit, 4
+  exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+  subnormals m/8 * 2^-6; the all-ones pattern S.1111.111 is NaN; there is no
+  infinity; the largest finite magnitude is 1.75 * 2^8 = 448.  The pages store
+  indexer keys as FP8_E4M3 in the KV cache for the tensor-core scoring path
+  (page 1, ``single_shot_inference.py``, comment "B2: FP8 tensor-core scoring
+  path"); the codec below is written from the format's definition.
 
 Nothing in this module is shared with the HIP library.
 """
@@ -23,6 +30,10 @@ __all__ = [
     "f32_to_bf16_bits",
     "f64_to_bf16_bits",
     "bf16_round_f64",
+    "E4M3_MAX",
+    "e4m3_decode",
+    "e4m3_encode",
+    "quantize_e4m3_rows",
 ]
 
 
@@ -78,3 +89,77 @@ def f64_to_bf16_bits(x) -> np.ndarray:
     """Bit patterns of :func:`bf16_round_f64` (the rounded value is exact in fp32)."""
     r = bf16_round_f64(x).astype(np.float32)
     return (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def _e4m3_value(code: int) -> float:
+    s = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return s * (m / 8.0) * 2.0 ** -6
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+_E4M3_TABLE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Decode FP8 E4M3 codes (uint8 array) to float64 exactly."""
+    c = np.asarray(codes)
+    if c.dtype != np.uint8:
+        raise TypeError(f"e4m3 codes must be uint8, got {c.dtype}")
+    return _E4M3_TABLE[c]
+
+
+# the non-negative finite codes in increasing order of value (0x00 .. 0x7E)
+_POS_CODES = np.arange(0x7F, dtype=np.uint8)
+_POS_VALUES = _E4M3_TABLE[:0x7F]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round values to FP8 E4M3 codes: nearest representable magnitude, ties
+    to the even code (the one whose lowest mantissa bit is 0), magnitudes
+    above 448 saturated to 448, the sign kept (so -0.0 gives 0x80).  NaN is
+    out of contract.  Works on the exact value of its float64 input."""
+    v = np.asarray(x, dtype=np.float64)
+    if np.isnan(v).any():
+        raise ValueError("NaN is out of contract for the e4m3 encoder")
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    hi = np.searchsorted(_POS_VALUES, a, side="left")      # first value >= a
+    hi = np.clip(hi, 0, len(_POS_VALUES) - 1)
+    lo = np.clip(hi - 1, 0, len(_POS_VALUES) - 1)
+    d_hi = _POS_VALUES[hi] - a
+    d_lo = a - _POS_VALUES[lo]
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((_POS_CODES[hi] & 1) == 0))
+    code = np.where(take_hi, _POS_CODES[hi], _POS_CODES[lo]).astype(np.uint8)
+    code = np.where(a == _POS_VALUES[hi], _POS_CODES[hi], code).astype(np.uint8)
+    neg = np.signbit(v)
+    return np.where(neg, code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def quantize_e4m3_rows(x):
+    """Per-row FP8 E4M3 quantisation of a [rows, d] array of float32 values.
+
+    scale = max|row| / 448 (binary32 division; 1 for an all-zero row), then
+    every element is divided by its row's scale in binary32 and encoded with
+    :func:`e4m3_encode` (so the row's largest magnitude maps to 448 exactly).
+    Returns (codes uint8 [rows, d], scales float32 [rows]); the decoded value
+    of element j is ``e4m3_decode(codes[j]) * scales``.
+    """
+    f = np.asarray(x, dtype=np.float32)
+    if f.ndim != 2:
+        raise ValueError("rows x d expected")
+    amax = np.abs(f).max(axis=1)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    scale = np.where(amax == 0, np.float32(1.0), scale).astype(np.float32)
+    y = (f / scale[:, None]).astype(np.float32)
+    return e4m3_encode(y.astype(np.float64)), scale

@@ -615,3 +615,95 @@ def test_synth_inputs_deterministic_and_shaped():
     sh2 = synth.SHAPES["ctx8k"]
     c = synth.make_decode_inputs(synth.with_(sh2, n_comp=64, ctx=256), 5)
     assert c["comp_kv"].dtype == np.uint16 and c["q"].shape == (1, 64, 512)
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 codec, row quantiser and the FP8 index score
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decode_closed_forms():
+    """Spot values fixed by the format's definition (bias 7, 3 mantissa bits,
+    exponent field 0 = subnormals m/8 * 2^-6, S.1111.111 = NaN, no inf)."""
+    d = lambda c: float(numfmt.e4m3_decode(np.array([c], dtype=np.uint8))[0])  # noqa: E731
+    assert d(0x00) == 0.0 and math.copysign(1.0, d(0x80)) == -1.0
+    assert d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9
+    assert d(0x08) == 2.0 ** -6                      # smallest normal
+    assert d(0x38) == 1.0 and d(0x39) == 1.125 and d(0x3F) == 1.875 and d(0x40) == 2.0
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0    # largest finite
+    assert d(0xB8) == -1.0
+    assert math.isnan(d(0x7F)) and math.isnan(d(0xFF))
+    vals = numfmt.e4m3_decode(np.arange(256, dtype=np.uint8))
+    assert np.isnan(vals).sum() == 2 and np.isinf(vals).sum() == 0
+    # the non-negative codes are monotone in value
+    assert np.all(np.diff(vals[:0x7F]) > 0)
+
+
+def test_e4m3_encode_round_trip_every_finite_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = numfmt.e4m3_decode(codes)
+    np.testing.assert_array_equal(numfmt.e4m3_encode(vals), codes)
+
+
+def test_e4m3_encode_ties_to_even_and_saturation():
+    enc = lambda x: int(numfmt.e4m3_encode(np.array([x]))[0])  # noqa: E731
+    assert enc(1.0625) == 0x38       # midway 1 and 1.125: even mantissa
+    assert enc(1.1875) == 0x3A       # midway 1.125 and 1.25: even mantissa
+    assert enc(1.9375) == 0x40       # midway 1.875 and 2: carries into the exponent
+    assert enc(2.0 ** -10) == 0x00   # midway 0 and the smallest subnormal
+    assert enc(3 * 2.0 ** -10) == 0x02
+    assert enc(1.07) == 0x39 and enc(1.05) == 0x38
+    assert enc(449.0) == 0x7E and enc(1e9) == 0x7E and enc(-1e9) == 0xFE
+    assert enc(-0.0) == 0x80 and enc(0.0) == 0x00
+
+
+def test_e4m3_encode_is_nearest_by_brute_force():
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(2000) * 50, rng.standard_normal(500) * 2.0 ** -7,
+                        rng.uniform(-448, 448, 500)])
+    got = numfmt.e4m3_decode(numfmt.e4m3_encode(x))
+    grid = numfmt.e4m3_decode(np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8))
+    best = np.abs(x[:, None] - grid[None, :]).min(axis=1)
+    np.testing.assert_array_equal(np.abs(x - got), best)
+    assert np.all(np.sign(got[got != 0]) == np.sign(x[got != 0]))
+
+
+def test_quantize_e4m3_rows():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((40, 128)).astype(np.float32)
+    x[3] = 0.0
+    x[5, 17] = -9.5            # a negative row maximum
+    codes, scale = numfmt.quantize_e4m3_rows(x)
+    assert codes.dtype == np.uint8 and scale.dtype == np.float32
+    assert scale[3] == 1.0 and not codes[3].any()
+    for r in (0, 5, 39):
+        j = int(np.argmax(np.abs(x[r])))
+        assert codes[r, j] in (0x7E, 0xFE)                          # the row maximum maps to +-448
+        assert scale[r] == np.float32(np.abs(x[r]).max()) / np.float32(448.0)
+    deq = numfmt.e4m3_decode(codes) * scale[:, None].astype(np.float64)
+    # relative error of a normal e4m3 value is at most 2^-4 (half of 2^-3)
+    big = np.abs(x) > 2.0 ** -6 * scale[:, None]
+    assert np.all(np.abs(deq - x)[big] <= np.abs(x)[big] * 2.0 ** -4 + 1e-12)
+
+
+def test_index_score_fp8_integer_brute_force():
+    """Codes of small integers and k_scale values that are powers of two give
+    exactly known scores, summed by hand in integers."""
+    enc = {0: 0x00, 1: 0x38, 2: 0x40, -1: 0xB8, -2: 0xC0, 3: 0x44}
+    rng = np.random.default_rng(13)
+    H, D, N = 4, 8, 6
+    qi = rng.choice([0, 1, 2, -1, -2, 3], size=(1, H, D))
+    ki = rng.choice([0, 1, 2, -1, -2, 3], size=(N, D))
+    q = np.vectorize(enc.get)(qi).astype(np.uint8)
+    k = np.vectorize(enc.get)(ki).astype(np.uint8)
+    ks = np.array([1.0, 2.0, 0.5, 4.0, 0.25, 1.0])
+    w = np.array([[1.0, -2.0, 0.5, 3.0]])
+    got = oracle.index_score_fp8(q, w, k, ks)
+    for s in range(N):
+        ref = 0.0
+        for h in range(H):
+            dot = sum(int(qi[0, h, d]) * int(ki[s, d]) for d in range(D))
+            ref += w[0, h] * max(0.0, ks[s] * dot)
+        assert got[0, s] == ref
+    # the causal form hides blocks past the position
+    masked = oracle.index_score_fp8(q, w, k, ks, q_pos=[9], ratio=4)
+    assert np.isneginf(masked[0, 3:]).all() and np.array_equal(masked[0, :2], got[0, :2])
