@@ -8,6 +8,7 @@ binding.  Build the library with ``compressed_sparse_attention_reduce_amd.build.
 from .binding import (  # noqa: F401
     CSA_BF16,
     CSA_F32,
+    CSA_FP8_E4M3,
     CsaError,
     LayerDesc,
     StepIO,
@@ -16,8 +17,10 @@ from .binding import (  # noqa: F401
     csa_decode_step_workspace_size,
     csa_gather,
     csa_index_score,
+    csa_index_score_fp8,
     csa_last_error,
     csa_layer_advance,
+    csa_quantize_fp8,
     csa_sparse_attn,
     csa_sparse_attn_workspace_size,
     csa_topk,

@@ -24,6 +24,7 @@ CSA_ERR_LAUNCH = -3
 CSA_ERR_WORKSPACE = -4
 CSA_F32 = 0
 CSA_BF16 = 1
+CSA_FP8_E4M3 = 2
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -75,6 +76,9 @@ _SIGS = {
     "csa_compress": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _ll, _ll, _vp]),
     "csa_index_score": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _ll, _ll, _ll,
                              _ll, _ll, _vp]),
+    "csa_quantize_fp8": (_i, [_vp, _i, _vp, _vp, _ll, _i, _vp]),
+    "csa_index_score_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _ll, _ll, _ll,
+                                 _ll, _ll, _ll, _vp]),
     "csa_topk_workspace_size": (_sz, [_i, _i, _i, _i]),
     "csa_topk": (_i, [_vp, _i, _i, _i, _ll, _ll, _i, _vp, _vp, _vp, _sz, _vp]),
     "csa_gather": (_i, [_vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _i, _i, _i, _ll, _ll,
@@ -164,6 +168,37 @@ def csa_index_score(q, w, k, scores, q_pos=None, ratio: int = 4, n: Optional[int
                                  _ptr(q_pos), ratio, q.stride(0), w.stride(0),
                                  k.stride(0) if k.shape[0] > 1 else 0, scores.stride(0),
                                  scores.shape[2], _stream(stream)))
+
+
+def csa_quantize_fp8(x, codes, scales, stream=None) -> None:
+    """x [..., d] float32 / bfloat16 (contiguous) -> codes [..., d] uint8, scales [...] float32."""
+    for t_, nm in ((x, "x"), (codes, "codes"), (scales, "scales")):
+        if not t_.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if codes.dtype != torch.uint8 or scales.dtype != torch.float32:
+        raise TypeError("codes must be uint8 and scales float32")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if codes.shape != x.shape or scales.numel() != rows:
+        raise ValueError("codes must match x and scales hold one value per row")
+    _check(lib().csa_quantize_fp8(_ptr(x), _dt(x), _ptr(codes), _ptr(scales), rows, d, _stream(stream)))
+
+
+def csa_index_score_fp8(q, w, k, k_scale, scores, q_pos=None, ratio: int = 4, n: Optional[int] = None,
+                        stream=None) -> None:
+    """q [B, t, 64, 128] uint8 E4M3; w [B, t, 64] float32 (query scales folded in);
+    k [B, N, 128] uint8 E4M3; k_scale [B, N] float32; scores [B, t, ld] float32."""
+    for t_, nm in ((q, "q"), (w, "w"), (k, "k"), (k_scale, "k_scale"), (scores, "scores")):
+        _inner_contig(t_, nm)
+    if q.dtype != torch.uint8 or k.dtype != torch.uint8:
+        raise TypeError("q and k must hold uint8 E4M3 codes")
+    B, t, h_i, d_i = q.shape
+    n = k.shape[1] if n is None else n
+    _check(lib().csa_index_score_fp8(_ptr(q), _ptr(w), _ptr(k), _ptr(k_scale), _ptr(scores), B, t, h_i, d_i,
+                                     n, _ptr(q_pos), ratio, q.stride(0), w.stride(0),
+                                     k.stride(0) if k.shape[0] > 1 else 0,
+                                     k_scale.stride(0) if k_scale.shape[0] > 1 else 0, scores.stride(0),
+                                     scores.shape[2], _stream(stream)))
 
 
 def csa_topk_workspace_size(batch: int, t: int, n: int, k: int) -> int:

@@ -128,6 +128,38 @@ int csa_index_score(const void* q, const float* w, const void* k, float* scores,
                     "csa_index_score");
 }
 
+int csa_quantize_fp8(const void* x, csa_dtype x_dtype, unsigned char* codes, float* scales, long long rows,
+                     int d, csa_stream stream) {
+    CHECK((x && codes && scales) || rows == 0, "csa_quantize_fp8: null pointer argument");
+    CHECK(x_dtype == CSA_F32 || x_dtype == CSA_BF16, "csa_quantize_fp8: x must be float32 or bfloat16");
+    CHECK(rows >= 0 && rows <= (1LL << 31) * 64, "csa_quantize_fp8: rows %lld", rows);
+    CHECK(d >= 1 && d <= 65536, "csa_quantize_fp8: d=%d out of 1..65536", d);
+    return launched(csa::launch_quantize_fp8(x, x_dtype == CSA_BF16, codes, scales, rows, d,
+                                             static_cast<hipStream_t>(stream)),
+                    "csa_quantize_fp8");
+}
+
+int csa_index_score_fp8(const unsigned char* q, const float* w, const unsigned char* k, const float* k_scale,
+                        float* scores, int batch, int t, int h_i, int d_i, int n, const int* q_pos, int ratio,
+                        long long q_stride_b, long long w_stride_b, long long k_stride_b, long long ks_stride_b,
+                        long long s_stride_b, long long ld_s, csa_stream stream) {
+    CHECK(q && w && k && k_scale && scores, "csa_index_score_fp8: null pointer argument");
+    CHECK(batch >= 1 && t >= 1 && n >= 0, "csa_index_score_fp8: batch %d t %d n %d", batch, t, n);
+    CHECK(batch * static_cast<long long>(t) <= 65535, "csa_index_score_fp8: batch*t above 65535");
+    CHECK(ratio >= 1, "csa_index_score_fp8: ratio %d", ratio);
+    CHECK(ld_s >= n && q_stride_b >= 0 && w_stride_b >= 0 && k_stride_b >= 0 && ks_stride_b >= 0 &&
+              s_stride_b >= 0,
+          "csa_index_score_fp8: bad strides");
+    if (h_i != 64 || d_i != 128)
+        return fail(CSA_ERR_UNSUPPORTED, "csa_index_score_fp8: needs h_i=64, d_i=128 (got %d, %d)", h_i, d_i);
+    CHECK(aligned16(q) && aligned16(k) && aligned16(w), "csa_index_score_fp8: q, k, w must be 16-byte aligned");
+    CHECK(q_stride_b % 16 == 0 && k_stride_b % 16 == 0 && w_stride_b % 4 == 0,
+          "csa_index_score_fp8: batch strides must keep 16-byte alignment");
+    csa::Fp8ScoreArgs a{q, w, k, k_scale, scores, batch, t, n, q_pos, ratio,
+                        q_stride_b, w_stride_b, k_stride_b, ks_stride_b, s_stride_b, ld_s};
+    return launched(csa::launch_index_score_fp8(a, static_cast<hipStream_t>(stream)), "csa_index_score_fp8");
+}
+
 size_t csa_topk_workspace_size(int batch, int t, int n, int k) {
     if (batch < 1 || t < 1 || n < 0 || k < 1) return 0;
     return csa::topk_workspace_bytes(batch * t, n, k);

@@ -63,6 +63,22 @@ struct PrepArgs;
 hipError_t launch_index_score_bf16(const ScoreArgs& a, const PrepArgs* fold, hipStream_t s);
 hipError_t launch_index_score_f32(const ScoreArgs& a, hipStream_t s);
 
+// ---- FP8 E4M3 indexer keys ------------------------------------------------------
+hipError_t launch_quantize_fp8(const void* x, bool x_bf16, uint8_t* codes, float* scales, long long rows, int d,
+                               hipStream_t s);
+struct Fp8ScoreArgs {
+    const uint8_t* q;      // [B][t][64][128] E4M3
+    const float* w;        // [B][t][64], query scales folded in
+    const uint8_t* k;      // [B][n][128] E4M3
+    const float* k_scale;  // [B][n]
+    float* scores;
+    int batch, t, n;
+    const int* q_pos;
+    int ratio;
+    long long q_stride_b, w_stride_b, k_stride_b, ks_stride_b, s_stride_b, ld_s;
+};
+hipError_t launch_index_score_fp8(const Fp8ScoreArgs& a, hipStream_t s);
+
 // ---- top-k -------------------------------------------------------------------
 size_t topk_workspace_bytes(int rows, int n, int k);
 struct TopkArgs {

@@ -61,7 +61,9 @@ typedef enum {
     CSA_ERR_WORKSPACE = -4
 } csa_status;
 
-typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
+/* CSA_FP8_E4M3 (OCP E4M3 codes, one byte per element) is accepted only where
+ * an entry point says so. */
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 } csa_dtype;
 
 typedef void *csa_stream; /* hipStream_t */
 
@@ -119,6 +121,43 @@ int csa_index_score(const void *q, const float *w, const void *k, float *scores,
                     const int *q_pos, int ratio, long long q_stride_b, long long w_stride_b,
                     long long k_stride_b, long long s_stride_b, long long ld_s,
                     csa_stream stream);
+
+/* ------------------------------------------------------------------------
+ * 2b. FP8 E4M3 indexer keys: quantisation and the FP8 index score.
+ *
+ * Source: page 1, single_shot_inference.py, comment "B2: FP8 tensor-core
+ * scoring path" (indexer keys stored as FP8_E4M3 in the KV cache).  The pages
+ * do not spell out the scaling; here every row (a key, or one head of a
+ * query) carries one float32 scale and its value is e4m3(code) * scale.
+ * E4M3 is the OCP encoding: sign, 4 exponent bits (bias 7), 3 mantissa bits,
+ * subnormals, NaN = S.1111.111, no infinity, largest finite 448.
+ *
+ * csa_quantize_fp8: x [rows][d] float32 or bfloat16 (x_dtype), contiguous ->
+ *   codes [rows][d] uint8 and scales [rows] float32: scale = max|row| / 448
+ *   (1 for an all-zero row), code = E4M3 of x / scale (binary32 division),
+ *   rounded to nearest, ties to the even code, saturating at +-448; -0 keeps
+ *   its sign.  NaN inputs are out of contract.  Limits: 1 <= d <= 65536.
+ *
+ * csa_index_score_fp8:
+ *   I[t,s] = sum_h w[t,h] * ReLU(k_scale[s] * (e4m3(q[t,h]) . e4m3(k[s])))
+ *   q:       [B][t][h_i][d_i] uint8 codes, stride_b = q_stride_b bytes.
+ *   w:       [B][t][h_i] float32, stride_b = w_stride_b; a per-head query
+ *            scale is folded in by the caller (ReLU(c x) = c ReLU(x), c > 0).
+ *   k:       [B][n][d_i] uint8 codes, stride_b = k_stride_b bytes (0 = shared).
+ *   k_scale: [B][n] float32, stride_b = ks_stride_b (0 = shared).
+ *   scores:  [B][t][ld_s] float32, stride_b = s_stride_b; columns 0..n-1.
+ *   q_pos, ratio: the causal form, as for csa_index_score.
+ * Supported: h_i = 64, d_i = 128; q, k, w 16-byte aligned and strides that
+ * keep them so.  Products of E4M3 values are exact in float32; sums are
+ * float32.
+ * ------------------------------------------------------------------------ */
+int csa_quantize_fp8(const void *x, csa_dtype x_dtype, unsigned char *codes, float *scales,
+                     long long rows, int d, csa_stream stream);
+int csa_index_score_fp8(const unsigned char *q, const float *w, const unsigned char *k,
+                        const float *k_scale, float *scores, int batch, int t, int h_i, int d_i,
+                        int n, const int *q_pos, int ratio, long long q_stride_b,
+                        long long w_stride_b, long long k_stride_b, long long ks_stride_b,
+                        long long s_stride_b, long long ld_s, csa_stream stream);
 
 /* ------------------------------------------------------------------------
  * 3. Top-k.

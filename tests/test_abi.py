@@ -104,6 +104,31 @@ def test_index_score_rejects_bad_args(csa):
     assert lib.csa_index_score(*a) == B.CSA_ERR_UNSUPPORTED
 
 
+def test_fp8_entry_points_reject_bad_args(csa):
+    lib = csa.lib()
+    B = csa.binding
+    q = [FAKE, B.CSA_F32, FAKE, FAKE, 10, 128, None]
+    a = list(q); a[1] = B.CSA_FP8_E4M3          # input must be float32 or bf16
+    assert lib.csa_quantize_fp8(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(q); a[5] = 0
+    assert lib.csa_quantize_fp8(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(q); a[2] = None
+    assert lib.csa_quantize_fp8(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(q); a[0] = None; a[2] = None; a[3] = None; a[4] = 0   # nothing to do
+    assert lib.csa_quantize_fp8(*a) == B.CSA_OK
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 128, 1000, None, 4, 0, 0, 0, 0, 0, 1000, None]
+    a = list(base); a[8] = 64
+    assert lib.csa_index_score_fp8(*a) == B.CSA_ERR_UNSUPPORTED
+    a = list(base); a[3] = None                 # no key scales
+    assert lib.csa_index_score_fp8(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(base); a[17] = 999                 # ld_s < n
+    assert lib.csa_index_score_fp8(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(base); a[2] = FAKE + 8             # misaligned keys
+    assert lib.csa_index_score_fp8(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(base); a[5] = 2; a[14] = 8         # batch stride that breaks alignment
+    assert lib.csa_index_score_fp8(*a) == B.CSA_ERR_INVALID_ARG
+
+
 def test_topk_rejects_bad_args_and_sizes_workspace(csa):
     lib = csa.lib()
     B = csa.binding

@@ -152,6 +152,123 @@ def test_index_score_full_size_sampled(csa):
 
 
 # ---------------------------------------------------------------------------
+# 2b. FP8 E4M3 indexer keys: quantisation (bit-exact) and the FP8 score
+# ---------------------------------------------------------------------------
+
+def _quant_rows(g, rows, d):
+    x = (g.standard_normal((rows, d)) * np.exp(g.uniform(-6, 6, (rows, 1)))).astype(np.float32)
+    x[0] = 0.0                                        # all-zero row: scale 1
+    if rows > 2:
+        x[1] = 0.0
+        x[1, 0] = 448.0                               # scale exactly 1: the rest is encoded as given
+        x[1, 1:12] = [1.0625, 1.1875, 1.9375, 2.0 ** -10, 3 * 2.0 ** -10, -0.0, 1e-30, 449.0,
+                      -447.9, 2.0 ** -7 + 2.0 ** -12, -1.0625]
+    if rows > 3:
+        x[2] = -x[2]                                  # negative row maxima
+    return x
+
+
+QUANT_CASES = [("f32_128", 37, 128, False), ("bf16_512", 9, 512, True), ("f32_odd_width", 5, 100, False),
+               ("f32_one_row_d1", 1, 1, False)]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=[c[0] for c in QUANT_CASES])
+def test_quantize_fp8_bit_exact(csa, case):
+    name, rows, d, bf16 = case
+    x = _quant_rows(_g(rows * 7 + d), rows, d)
+    if bf16:
+        xb = numfmt.f32_to_bf16_bits(x)
+        xd = dev_bf16(xb)
+        x = numfmt.bf16_bits_to_f64(xb).astype(np.float32)
+    else:
+        xd = torch.from_numpy(x).to(DEV)
+    codes = torch.full((rows, d), 0x55, dtype=torch.uint8, device=DEV)
+    scales = torch.zeros(rows, dtype=torch.float32, device=DEV)
+    csa.csa_quantize_fp8(xd, codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = numfmt.quantize_e4m3_rows(x)
+    np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
+def _fp8_inputs(g, B, t, n):
+    """Query and keys drawn like the bf16 workloads, quantised by the oracle;
+    the query's per-head scales are folded into w."""
+    q = (g.standard_normal((B, t, 64, 128)) / np.sqrt(128)).astype(np.float32)
+    w = g.standard_normal((B, t, 64)).astype(np.float32)
+    K = g.standard_normal((B, n, 128)).astype(np.float32)
+    qc, qs = numfmt.quantize_e4m3_rows(q.reshape(-1, 128))
+    kc, ks = numfmt.quantize_e4m3_rows(K.reshape(-1, 128))
+    w2 = (w * qs.reshape(B, t, 64)).astype(np.float32)
+    return (qc.reshape(B, t, 64, 128), w2, kc.reshape(B, n, 128), ks.reshape(B, n), K)
+
+
+FP8_SCORE_CASES = [
+    # name, B, t, n, causal
+    ("decode_ctx8k", 1, 1, 2048, False),
+    ("ragged_tail", 1, 1, 1000, False),
+    ("batch3", 3, 1, 4100, False),
+    ("short", 1, 1, 17, False),
+    ("causal_rows", 2, 3, 700, True),
+    ("long_row", 1, 1, 65536, False),
+]
+
+
+@pytest.mark.parametrize("case", FP8_SCORE_CASES, ids=[c[0] for c in FP8_SCORE_CASES])
+def test_index_score_fp8(csa, case):
+    name, B, t, n, causal = case
+    qc, w, kc, ks, _ = _fp8_inputs(_g(len(name) * 17 + n), B, t, n)
+    ld = n + 3
+    scores = torch.full((B, t, ld), 123.0, device=DEV)
+    pos_np = (4 * n - 4 * t - 10 + 3 * np.arange(B * t)).astype(np.int32).reshape(B, t) if causal else None
+    csa.csa_index_score_fp8(torch.from_numpy(qc).to(DEV), dev_f32(w), torch.from_numpy(kc).to(DEV),
+                            dev_f32(ks), scores, q_pos=None if pos_np is None else torch.from_numpy(pos_np).to(DEV))
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy().astype(np.float64)
+    assert (got[:, :, n:] == 123.0).all(), "wrote past n"
+    for b in range(B):
+        ref = oracle.index_score_fp8(qc[b], w[b], kc[b], ks[b], q_pos=None if pos_np is None else pos_np[b])
+        fin = np.isfinite(ref)
+        assert (np.isfinite(got[b, :, :n]) == fin).all(), "mask differs"
+        assert rel_err(got[b, :, :n][fin], ref[fin]) <= 1e-4
+
+
+def test_index_score_fp8_full_size_sampled_and_recall(csa):
+    """n = 250,000 FP8 keys quantised on the GPU from the 1M-context bf16
+    cache: scores on a sample against the oracle; the FP8 top-512 against the
+    bf16 scores' top-512 (recall is reported, not a parity bar: E4M3's
+    3-bit significand moves scores near the threshold)."""
+    shape = synth.SHAPES["ctx1m"]
+    x = synth.make_decode_inputs_torch(shape, seed=None, device=DEV, layers=1)[0]
+    n = shape.n_comp
+    keys = x["idx_keys"][:, :n].contiguous()
+    kc = torch.empty(1, n, 128, dtype=torch.uint8, device=DEV)
+    ks = torch.empty(1, n, dtype=torch.float32, device=DEV)
+    csa.csa_quantize_fp8(keys, kc, ks)
+    q = x["q_idx"][:, None].contiguous()               # [1, 1, 64, 128] bf16
+    qc = torch.empty(1, 1, 64, 128, dtype=torch.uint8, device=DEV)
+    qs = torch.empty(1, 1, 64, dtype=torch.float32, device=DEV)
+    csa.csa_quantize_fp8(q, qc, qs)
+    w8 = (x["w_idx"][:, None] * qs).contiguous()
+    s8 = torch.empty(1, 1, n, device=DEV)
+    csa.csa_index_score_fp8(qc, w8, kc, ks, s8)
+    s16 = torch.empty(1, 1, n, device=DEV)
+    csa.csa_index_score(q, x["w_idx"][:, None].contiguous(), keys, s16)
+    torch.cuda.synchronize()
+    g = _g(45)
+    sample = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n), g.integers(0, n, 4096)]))
+    idx = torch.from_numpy(sample).to(DEV)
+    ref = oracle.index_score_fp8(qc[0].cpu().numpy(), w8[0].cpu().numpy(), kc[0, idx].cpu().numpy(),
+                                 ks[0, idx].cpu().numpy())[0]
+    assert rel_err(s8[0, 0].cpu().numpy().astype(np.float64)[sample], ref) <= 1e-4
+    top8 = set(torch.topk(s8[0, 0], 512).indices.cpu().tolist())
+    top16 = set(torch.topk(s16[0, 0], 512).indices.cpu().tolist())
+    recall = len(top8 & top16) / 512
+    print(f"fp8 top-512 recall vs bf16 keys at n=250000: {recall:.4f}")
+    assert recall >= 0.9
+
+
+# ---------------------------------------------------------------------------
 # 3. top-k
 # ---------------------------------------------------------------------------
 
