@@ -88,6 +88,7 @@ constexpr int kRing = 8;            // key tiles in flight per wave
 constexpr int kQPitch = kDi + 16;   // LDS row pitch of the staged query (bytes)
 
 typedef long fp8x8;  // eight E4M3 codes, one MFMA operand
+constexpr int kFp8WgsPerCu = 2;  // one per CU measured slower (11.3 vs 10.9 us at n = 250,000)
 
 __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a, int tiles_per_row) {
     __shared__ __attribute__((aligned(16))) uint8_t qs[kHeads * kQPitch];
@@ -209,7 +210,7 @@ hipError_t launch_index_score_fp8(const Fp8ScoreArgs& a, hipStream_t s) {
     const int rows = a.batch * a.t;
     if (rows == 0 || a.n == 0) return hipSuccess;
     const int tiles = (a.n + kTileKeys - 1) / kTileKeys;
-    int wgs = (2 * device_cu_count() + rows - 1) / rows;
+    int wgs = (kFp8WgsPerCu * device_cu_count() + rows - 1) / rows;
     const int max_wgs = (tiles + kWaves * 4 - 1) / (kWaves * 4);  // at least 4 tiles per wave
     wgs = wgs > max_wgs ? max_wgs : wgs;
     wgs = wgs < 1 ? 1 : wgs;
