@@ -19,6 +19,7 @@ from .csa import (
     index_score,
     index_score_fp8,
     kv_norm,
+    prefill_chunk,
     sparse_attn,
     topk,
 )
@@ -35,4 +36,5 @@ __all__ = [
     "SwaRing",
     "LayerState",
     "decode_step",
+    "prefill_chunk",
 ]

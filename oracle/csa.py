@@ -37,6 +37,7 @@ __all__ = [
     "SwaRing",
     "LayerState",
     "decode_step",
+    "prefill_chunk",
 ]
 
 
@@ -416,3 +417,48 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
         "out": out,
         "lse": lse,
     }
+
+
+# ---------------------------------------------------------------------------
+# (7) a prefill-shaped chunk of query tokens against the compressed history
+# ---------------------------------------------------------------------------
+
+def prefill_chunk(*, q, q_idx, w_idx, idx_keys, comp_kv, win_kv, pos0: int, top_k: int, window: int,
+                  sink=None, scale: Optional[float] = None, ratio: int = 4):
+    """Score, select and attend for ``T`` consecutive query tokens at once.
+
+    The query at position ``p = pos0 + t`` does what one decode step at ``p``
+    does after its own token and every block complete at ``p`` are in the
+    caches (page 2, ``single_shot_inference.py``, ``eager_attention``): the
+    index score over the compressed history with the causal block mask (page
+    1, ``archived_plans/NEXT_STEPS.md``, Issue 2: block ``s`` visible iff
+    ``ratio*s + ratio - 1 <= p``), the fixed-shape top-k, then one softmax
+    over the selected compressed rows followed by the sliding window — the raw
+    KV rows of positions ``max(0, p - window + 1) .. p``, oldest first — plus
+    the sink.
+
+    ``q``: ``[T, H, D]``, ``q_idx``: ``[T, H_I, d_I]``, ``w_idx``: ``[T, H_I]``,
+    ``idx_keys``: ``[N, d_I]``, ``comp_kv``: ``[N, D]`` (the chunk's own
+    blocks included: the mask hides those not yet complete), ``win_kv``:
+    ``[T + window - 1, D]``, row ``r`` holding position ``pos0 - window + 1 + r``
+    (rows of negative positions are never read).  Returns a dict with
+    ``scores [T, N]``, ``idx [T, top_k]``, ``count [T]``, ``out [T, H, D]`` and
+    ``lse [T, H]``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    win_kv = np.asarray(win_kv, dtype=np.float64)
+    comp_kv = np.asarray(comp_kv, dtype=np.float64)
+    T = q.shape[0]
+    pos = pos0 + np.arange(T, dtype=np.int64)
+    scores = index_score(q_idx, w_idx, idx_keys, q_pos=pos, ratio=ratio)
+    idx, count = topk(scores, top_k)
+    out = np.zeros(q.shape, dtype=np.float64)
+    lse = np.zeros(q.shape[:2], dtype=np.float64)
+    for t in range(T):
+        p = int(pos[t])
+        first = max(0, p - window + 1)
+        win = [win_kv[x - (pos0 - window + 1)] for x in range(first, p + 1)]
+        sel = [comp_kv[int(idx[t, j])] for j in range(int(count[t]))]
+        rows = np.stack(sel + win, axis=0)
+        out[t], lse[t] = sparse_attn(q[t], rows, sink, scale)
+    return {"scores": scores, "idx": idx, "count": count, "out": out, "lse": lse}

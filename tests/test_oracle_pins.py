@@ -585,6 +585,58 @@ def test_decode_step_cache_rounding_applies():
 
 
 # ---------------------------------------------------------------------------
+# (7) prefill chunk: the same as one decode step per token
+# ---------------------------------------------------------------------------
+
+def _prefill_vs_decode_steps(pos0, T, top_k, W=8, seed=23, prefill=oracle.prefill_chunk):
+    """Run decode steps for positions 0 .. pos0+T-1 and the prefill chunk for
+    the last T of them on the final caches; both must agree token by token."""
+    g = _g(seed)
+    L = _empty_state(g, W=W)
+    per_token = []
+    kv_rows = []
+    for pos in range(pos0 + T):
+        inp = _step_inputs(g)
+        kv_rows.append(inp["kv_new"])
+        r = oracle.decode_step(L, pos=pos, top_k=top_k, **inp)
+        if pos >= pos0:
+            per_token.append((inp, r))
+    first = pos0 - W + 1
+    win = np.stack([kv_rows[x] if x >= 0 else np.full(16, np.nan) for x in range(first, pos0 + T)])
+    N = L.n_comp
+    got = prefill(q=np.stack([i["q"] for i, _ in per_token]), q_idx=np.stack([i["q_idx"] for i, _ in per_token]),
+                  w_idx=np.stack([i["w_idx"] for i, _ in per_token]), idx_keys=L.idx_keys[:N],
+                  comp_kv=L.comp_kv[:N], win_kv=win, pos0=pos0, top_k=top_k, window=W, sink=L.sink)
+    for t, (_, r) in enumerate(per_token):
+        assert got["count"][t] == r["count"]
+        assert got["idx"][t].tolist() == r["idx"].tolist()
+        np.testing.assert_allclose(got["out"][t], r["out"], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(got["lse"][t], r["lse"], rtol=1e-13)
+
+
+@pytest.mark.parametrize("pos0,T,top_k", [(21, 9, 3), (2, 10, 2), (13, 6, 64), (0, 5, 1)])
+def test_prefill_chunk_equals_decode_steps(pos0, T, top_k):
+    """Each query of the chunk gets exactly what a decode step at its position
+    gets: causal mask = blocks complete by then, window = the last W tokens
+    (clipped at position 0), top_k >= n_comp = dense attention."""
+    _prefill_vs_decode_steps(pos0, T, top_k)
+
+
+def test_mutation_prefill_pins_catch_planted_mistakes():
+    def window_one_late(**kw):  # window rows shifted by one position
+        kw = dict(kw)
+        kw["win_kv"] = np.concatenate([kw["win_kv"][1:], kw["win_kv"][-1:]])
+        return oracle.prefill_chunk(**kw)
+
+    def positions_one_early(**kw):  # every query one position early (mask and window)
+        return oracle.prefill_chunk(**dict(kw, pos0=kw["pos0"] - 1))
+
+    for bad in (window_one_late, positions_one_early):
+        with pytest.raises(AssertionError):
+            _prefill_vs_decode_steps(21, 9, 3, prefill=bad)
+
+
+# ---------------------------------------------------------------------------
 # workload shapes against the pages' printed sizes
 # ---------------------------------------------------------------------------
 
