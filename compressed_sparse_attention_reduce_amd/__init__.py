@@ -18,8 +18,11 @@ from .binding import (  # noqa: F401
     csa_gather,
     csa_index_score,
     csa_index_score_fp8,
+    csa_index_topk,
+    csa_index_topk_workspace_size,
     csa_last_error,
     csa_layer_advance,
+    csa_prefill_attn,
     csa_quantize_fp8,
     csa_sparse_attn,
     csa_sparse_attn_workspace_size,

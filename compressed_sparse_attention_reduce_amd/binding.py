@@ -89,6 +89,10 @@ _SIGS = {
     "csa_decode_step_workspace_size": (_sz, [ctypes.POINTER(LayerDesc)]),
     "csa_decode_step": (_i, [ctypes.POINTER(LayerDesc), ctypes.POINTER(StepIO), _vp, _sz, _vp]),
     "csa_layer_advance": (_i, [ctypes.POINTER(LayerDesc), _i]),
+    "csa_index_topk_workspace_size": (_sz, [_i, _i, _i]),
+    "csa_index_topk": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _ll, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "csa_prefill_attn": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _ll, _vp, _f, _vp, _i, _vp, _i, _i, _i,
+                              _vp]),
 }
 
 _lib = None
@@ -306,3 +310,37 @@ def make_step_io(*, pos: int, q, q_idx, w_idx, kv_new, z_main, c_main, z_idx, c_
     io._keep = (q, q_idx, w_idx, kv_new, z_main, c_main, z_idx, c_idx, scores, topk_idx, topk_count,
                 gather_buf, n_valid, out, lse)
     return io
+
+
+def csa_index_topk_workspace_size(t: int, n: int, top_k: int) -> int:
+    return lib().csa_index_topk_workspace_size(t, n, top_k)
+
+
+def csa_index_topk(q, w, k, idx, count, ws, pos0: int = -1, ratio: int = 4, n: Optional[int] = None,
+                   stream=None) -> None:
+    """q [t, 64, 128] bf16; w [t, 64] float32; k [N, 128] bf16 (first n rows);
+    idx [t, top_k] int32; count [t] int32 or None; query row r sits at
+    position pos0 + r (pos0 < 0: no causal mask)."""
+    for t_, nm in ((q, "q"), (w, "w"), (k, "k"), (idx, "idx")):
+        if not t_.is_contiguous():
+            raise ValueError(f"{nm}: must be contiguous")
+    t, h_i, d_i = q.shape
+    n = k.shape[0] if n is None else n
+    _check(lib().csa_index_topk(_ptr(q), _ptr(w), _ptr(k), t, h_i, d_i, n, pos0, ratio, idx.shape[1], _ptr(idx),
+                                _ptr(count), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def csa_prefill_attn(q, comp_kv, idx, count, win_kv, window: int, pos0: int, sink, scale: float, out,
+                     lse=None, n_comp: Optional[int] = None, stream=None) -> None:
+    """q [t, h, d] bf16; comp_kv [N, d] bf16; idx [t, k] int32; count [t] int32
+    or None; win_kv [t + window - 1, d] bf16 (row i = position
+    pos0 - window + 1 + i); sink [h] float32 or None; out [t, h, d] float32
+    or bf16; lse [t, h] float32 or None."""
+    for t_, nm in ((q, "q"), (comp_kv, "comp_kv"), (idx, "idx"), (win_kv, "win_kv"), (out, "out")):
+        if not t_.is_contiguous():
+            raise ValueError(f"{nm}: must be contiguous")
+    t, h, d = q.shape
+    n_comp = comp_kv.shape[0] if n_comp is None else n_comp
+    _check(lib().csa_prefill_attn(_ptr(q), _ptr(comp_kv), n_comp, _ptr(idx), _ptr(count), idx.shape[1],
+                                  _ptr(win_kv), window, pos0, _ptr(sink), scale, _ptr(out), _dt(out), _ptr(lse),
+                                  t, h, d, _stream(stream)))

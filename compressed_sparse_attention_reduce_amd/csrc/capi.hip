@@ -11,6 +11,7 @@
 
 #include "../../include/csa.h"
 #include "kernels.h"
+#include "prefill.h"
 
 namespace csa {
 
@@ -123,6 +124,8 @@ int csa_index_score(const void* q, const float* w, const void* k, float* scores,
     csa::ScoreArgs a{q, w, k, scores, batch, t, h_i, d_i, n, q_pos, ratio,
                      q_stride_b, w_stride_b, k_stride_b, s_stride_b, ld_s, csa::CandArgs{nullptr, 0, 0}};
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == CSA_BF16 && t >= csa::kMqMinRows)
+        return launched(csa::launch_index_score_mq(a, -1, s), "csa_index_score");
     return launched(dtype == CSA_BF16 ? csa::launch_index_score_bf16(a, nullptr, s)
                                       : csa::launch_index_score_f32(a, s),
                     "csa_index_score");
@@ -461,6 +464,49 @@ int csa_layer_advance(csa_layer_desc* L, int pos) {
     L->swa_head = (L->swa_head + 1) % L->w;
     L->swa_len = L->swa_len + 1 < L->w ? L->swa_len + 1 : L->w;
     return ok();
+}
+
+size_t csa_index_topk_workspace_size(int t, int n, int top_k) {
+    if (t < 1 || n < 0 || top_k < 1) return 0;
+    return csa::index_topk_workspace_bytes(t, n, top_k);
+}
+
+int csa_index_topk(const void* q, const float* w, const void* k, int t, int h_i, int d_i, int n,
+                   long long pos0, int ratio, int top_k, int* idx, int* count, void* ws, size_t ws_bytes,
+                   csa_stream stream) {
+    CHECK(q && w && idx && ws && (k || n == 0), "csa_index_topk: null pointer argument");
+    CHECK(t >= 1 && n >= 0, "csa_index_topk: t %d n %d", t, n);
+    CHECK(ratio >= 1, "csa_index_topk: ratio %d", ratio);
+    CHECK(top_k >= 1 && top_k <= csa::kTopkMaxK, "csa_index_topk: top_k=%d out of 1..%d", top_k, csa::kTopkMaxK);
+    if (h_i != 64 || d_i != 128)
+        return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk: needs h_i=64, d_i=128 (got %d, %d)", h_i, d_i);
+    CHECK(aligned16(q) && aligned16(w) && aligned16(ws) && (n == 0 || aligned16(k)),
+          "csa_index_topk: q, w, k and ws must be 16-byte aligned");
+    if (ws_bytes < csa_index_topk_workspace_size(t, n, top_k))
+        return fail(CSA_ERR_WORKSPACE, "csa_index_topk: workspace %zu < %zu bytes", ws_bytes,
+                    csa_index_topk_workspace_size(t, n, top_k));
+    csa::IndexTopkArgs a{static_cast<const uint16_t*>(q), w, static_cast<const uint16_t*>(k), t, n, pos0, ratio,
+                         top_k, idx, count, ws};
+    return launched(csa::launch_index_topk(a, static_cast<hipStream_t>(stream)), "csa_index_topk");
+}
+
+int csa_prefill_attn(const void* q, const void* comp_kv, int n_comp, const int* idx, const int* count, int k,
+                     const void* win_kv, int window, long long pos0, const float* sink, float scale, void* out,
+                     csa_dtype out_dtype, float* lse, int t, int h, int d, csa_stream stream) {
+    CHECK(q && idx && win_kv && out && (comp_kv || n_comp == 0), "csa_prefill_attn: null pointer argument");
+    CHECK(t >= 1 && n_comp >= 0, "csa_prefill_attn: t %d n_comp %d", t, n_comp);
+    CHECK(k >= 1 && k <= csa::kTopkMaxK, "csa_prefill_attn: k=%d out of 1..%d", k, csa::kTopkMaxK);
+    CHECK(window >= 1 && pos0 >= 0, "csa_prefill_attn: window %d / pos0 %lld", window, pos0);
+    CHECK(out_dtype == CSA_F32 || out_dtype == CSA_BF16, "csa_prefill_attn: bad out_dtype %d", (int)out_dtype);
+    if (!csa::prefill_attn_supported(h, d))
+        return fail(CSA_ERR_UNSUPPORTED, "csa_prefill_attn: needs h a multiple of 16 up to 64 and d in {128, 256, 512} "
+                    "(got %d, %d)", h, d);
+    CHECK(aligned16(q) && aligned16(win_kv) && aligned16(out) && (n_comp == 0 || aligned16(comp_kv)),
+          "csa_prefill_attn: q, comp_kv, win_kv and out must be 16-byte aligned");
+    csa::PrefillAttnArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(comp_kv), n_comp, idx,
+                           count, k, static_cast<const uint16_t*>(win_kv), window, pos0, sink, scale, out,
+                           out_dtype == CSA_BF16, lse, t, h, d};
+    return launched(csa::launch_prefill_attn(a, static_cast<hipStream_t>(stream)), "csa_prefill_attn");
 }
 
 }  // extern "C"

@@ -26,6 +26,7 @@
 //     serialise on this chip).
 #include "common.h"
 #include "kernels.h"
+#include "score_tile.h"
 #include "step_prep.h"
 #include "topk_common.h"
 
@@ -205,14 +206,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs
             for (int mt = 0; mt < kMTiles; ++mt)
                 acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], kb[i][s], acc[mt], 0, 0, 0);
         if (refill) load_tile(j + kRing, kb[i]);
-        // accumulator register r of M tile mt <-> head 16*mt + 4*lg + r, key li
-        float part = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < kMTiles; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) part += wr[mt][r] * fmaxf(acc[mt][r], 0.f);
-        part += xor_lanes_f32<16>(part);
-        part += xor_lanes_f32<32>(part);
+        const float part = tile_head_sum(acc, wr);
         const int key = (gw + j * waves_per_row) * kTileKeys + li;
         const bool live = j < n_mine && key < n;
         float sc = part;

@@ -1,0 +1,461 @@
+// Prefill-shaped CSA chunk: T query tokens at consecutive positions against
+// one compressed history (its own blocks included, hidden by the causal
+// mask until complete), then per-token sparse attention.
+//
+// Page 1, ARCHITECTURE_AND_MEMORY_AUDIT.md, finding F3 (paper section 2.3.1,
+// eq. 16) for the score; page 1, archived_plans/NEXT_STEPS.md, Issue 2 for the
+// causal block mask; page 2, single_shot_inference.py, eager_attention for
+// the per-query composition (score -> top-k -> one softmax over the selected
+// compressed rows and the sliding window, with the sink of the D5c hunk).
+//
+// Score (k_index_score_mq).  With many queries the score is a dense
+// [T x 64] x [128 x N] contraction, so it is bound by the matrix cores, not
+// by HBM: 2 x 64 x 128 FLOP per (query, key) pair.  Each wave keeps the
+// 64 x 128 query of two tokens resident as A operands (4 head tiles x 4
+// k-steps of v_mfma_f32_16x16x32_bf16 each) and streams 16-key tiles as B
+// operands straight from memory; the eight waves of a workgroup walk the
+// same key range, so the tiles come from L1/L2 after the first wave.  The
+// workgroup -> XCD assignment (consecutive workgroup ids go to consecutive
+// XCDs) puts every query group of one key range on the same XCD, so each key
+// range is fetched from HBM once per XCD and stays in that XCD's L2.  The
+// per-tile epilogue is the decode scan's (score_tile.h), so both produce the
+// same bits.  Scores of up to kPrefillChunkRows queries are held in the
+// workspace at a time (67 MB at N = 65536: resident in the 256 MB
+// last-level cache) and selected by the top-k kernels before the next chunk.
+//
+// Attention (k_prefill_attn).  One workgroup per query token computes all 64
+// heads, so each selected row is read once per token.  Rows arrive in
+// chunks of 32 (compressed rows by index, then the window rows, oldest
+// first), staged in LDS both row-major (for S^T = K Q^T) and transposed (for
+// O^T = V^T P^T), so every MFMA operand is a contiguous LDS read and the
+// probabilities never leave registers: the S^T accumulator layout of a lane
+// (rows 4*lg + r and 16 + 4*lg + r, head li) is exactly its B operand of the
+// PV product.  Online softmax across chunks; the next chunk's rows are
+// loaded into registers while the current one is computed.
+#include "common.h"
+#include "kernels.h"
+#include "prefill.h"
+#include "score_tile.h"
+
+namespace csa {
+
+namespace {
+
+__host__ __device__ inline size_t pf_align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// ---------------------------------------------------------------------------
+// multi-query index score
+// ---------------------------------------------------------------------------
+
+// Shape of the multi-query scan: query rows per wave, waves per workgroup,
+// key tiles in flight per wave.  16 query rows per workgroup either way.
+#ifndef CSA_MQ_SHAPE
+#define CSA_MQ_SHAPE 4, 4, 2
+#endif
+template <int kTok, int kWaves, int kRing>
+struct MqShape {
+    static constexpr int kThreads = kWaves * kWave;
+    static constexpr int kRows = kWaves * kTok;
+};
+using Mq = MqShape<CSA_MQ_SHAPE>;
+constexpr int kMqRowsPerWg = Mq::kRows;
+constexpr int kIdxHeads = 64;
+constexpr int kIdxDi = 128;
+constexpr int kIdxSteps = kIdxDi / 32;
+
+struct MqArgs {
+    const uint16_t* q;   // [B][t][64][128]
+    const float* w;      // [B][t][64]
+    const uint16_t* k;   // [B][n][128]
+    float* scores;       // [B][t][ld]
+    int t, n;
+    long long ld;
+    const int* q_pos;    // [B][t] positions, or nullptr: pos0 + row (pos0 < 0: no mask)
+    long long pos0;
+    int ratio;
+    int keys_per_wg;
+    long long q_stride_b, w_stride_b, k_stride_b, s_stride_b;
+};
+
+template <int kMqTok, int kMqWaves, int kMqRing>
+__global__ __launch_bounds__(kMqWaves * kWave, 1) void k_index_score_mq(MqArgs a) {
+    constexpr int kMqRowsPerWg = kMqWaves * kMqTok;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+    const int b = blockIdx.z;
+    const int row0 = blockIdx.y * kMqRowsPerWg + kMqTok * wv;
+    if (row0 >= a.t) return;  // no barriers in this kernel
+    const int k0 = blockIdx.x * a.keys_per_wg;
+    const int k1 = min(a.n, k0 + a.keys_per_wg);
+    if (k0 >= k1) return;
+    const int n_tiles = (k1 - k0 + 15) / 16;
+    int rows[kMqTok];  // a missing second row repeats the first; nothing of it is stored
+    long long pos[kMqTok];
+#pragma unroll
+    for (int u = 0; u < kMqTok; ++u) {
+        rows[u] = min(row0 + u, a.t - 1);
+        pos[u] = a.q_pos ? static_cast<long long>(a.q_pos[static_cast<long long>(b) * a.t + rows[u]])
+                         : (a.pos0 >= 0 ? a.pos0 + rows[u] : -1);
+    }
+    const bool masked = a.q_pos || a.pos0 >= 0;
+    const uint16_t* qb = a.q + b * a.q_stride_b;
+    const float* wb = a.w + b * a.w_stride_b;
+    float* sb = a.scores + b * a.s_stride_b;
+
+    const uint16_t* kbase = a.k + b * a.k_stride_b + 8 * lg;
+    auto load_tile = [&](int j, bf16x8* dst) {
+        const int key = min(k0 + 16 * min(j, n_tiles - 1) + li, k1 - 1);
+        const uint16_t* p = kbase + static_cast<long long>(key) * kIdxDi;
+#pragma unroll
+        for (int s = 0; s < kIdxSteps; ++s) dst[s] = *reinterpret_cast<const bf16x8*>(p + 32 * s);
+    };
+
+    bf16x8 qa[kMqTok][4][kIdxSteps];
+    float wr[kMqTok][4][4];
+#pragma unroll
+    for (int u = 0; u < kMqTok; ++u) {
+        const uint16_t* qr = qb + static_cast<long long>(rows[u]) * kIdxHeads * kIdxDi;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int s = 0; s < kIdxSteps; ++s)
+                qa[u][mt][s] = *reinterpret_cast<const bf16x8*>(qr + (16 * mt + li) * kIdxDi + 32 * s + 8 * lg);
+        const float* wrow = wb + static_cast<long long>(rows[u]) * kIdxHeads;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const float4 v = *reinterpret_cast<const float4*>(wrow + 16 * mt + 4 * lg);
+            wr[u][mt][0] = v.x; wr[u][mt][1] = v.y; wr[u][mt][2] = v.z; wr[u][mt][3] = v.w;
+        }
+    }
+    bf16x8 kb[kMqRing][kIdxSteps];
+#pragma unroll
+    for (int i = 0; i < kMqRing; ++i) load_tile(i, kb[i]);
+
+    // Same ring discipline as the decode scan: refills only for tiles that
+    // exist in the steady loop, one clamped extra group, a last group with no
+    // refills, so every path leaves the same loads in flight.
+    auto step = [&](int i, int j, bool refill) {
+        const int key = k0 + 16 * j + li;
+        const bool live = j < n_tiles && key < k1;
+#pragma unroll
+        for (int u = 0; u < kMqTok; ++u) {
+            f32x4 acc[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < kIdxSteps; ++s)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[u][mt][s], kb[i][s], acc[mt], 0, 0, 0);
+            if (refill && u == kMqTok - 1) load_tile(j + kMqRing, kb[i]);
+            float sc = tile_head_sum(acc, wr[u]);
+            if (masked && static_cast<long long>(a.ratio) * key + a.ratio - 1 > pos[u]) sc = -INFINITY;
+            if (live && lg == u && row0 + u < a.t) sb[static_cast<long long>(row0 + u) * a.ld + key] = sc;
+        }
+    };
+    int j0 = 0;
+    for (; j0 + 2 * kMqRing <= n_tiles; j0 += kMqRing)
+#pragma unroll
+        for (int i = 0; i < kMqRing; ++i) step(i, j0 + i, true);
+    if (j0 + kMqRing < n_tiles) {  // wave-uniform
+#pragma unroll
+        for (int i = 0; i < kMqRing; ++i) step(i, j0 + i, true);
+        j0 += kMqRing;
+    }
+#pragma unroll
+    for (int i = 0; i < kMqRing; ++i) step(i, j0 + i, false);
+}
+
+// ---------------------------------------------------------------------------
+// per-query attention over indexed rows + the sliding window
+// ---------------------------------------------------------------------------
+
+constexpr int kPaThreads = 256;          // four waves: one 16-head tile each (h <= 64)
+constexpr int kPaWaves = kPaThreads / kWave;
+constexpr int kPaRows = 32;              // rows per chunk
+constexpr int kVtPitch = kPaRows + 4;    // transposed rows: 72 B per column (bank spread)
+
+template <int D>
+struct PaCfg {
+    static constexpr int kKrPitch = D + 8;                 // row-major rows (bank spread)
+    static constexpr int kKs = D / 32;                     // k-steps of S^T
+    static constexpr int kMd = D / 16;                     // 16-column tiles of O^T
+    static constexpr int kItems = (kPaRows / 4) * (D / 8); // (4-row group, 16-byte column) items per chunk
+    static constexpr int kIpt = (kItems + kPaThreads - 1) / kPaThreads;
+    static constexpr size_t kLdsRows = sizeof(uint16_t) * (static_cast<size_t>(kPaRows) * kKrPitch +
+                                                          static_cast<size_t>(D) * kVtPitch);
+};
+
+template <int D>
+__global__ __launch_bounds__(kPaThreads, D >= 512 ? 1 : 2) void k_prefill_attn(PrefillAttnArgs a) {
+    using C = PaCfg<D>;
+    extern __shared__ __attribute__((aligned(16))) uint16_t pa_lds[];
+    uint16_t* kr = pa_lds;                                      // [32][D + 8]
+    uint16_t* vt = kr + kPaRows * C::kKrPitch;                  // [D][36]
+    int* sidx = reinterpret_cast<int*>(vt + D * kVtPitch);      // [k]
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+    const int tq = blockIdx.x;
+    const long long p = a.pos0 + tq;
+    const int wl = static_cast<int>(min(static_cast<long long>(a.window), p + 1));
+    int cnt = a.count ? a.count[tq] : a.k;
+    cnt = cnt < 0 ? 0 : (cnt > a.k ? a.k : cnt);
+    if (a.n_comp <= 0) cnt = 0;
+    const int nv = cnt + wl;
+    const bool active = 16 * wv < a.h;
+    const uint16_t* win = a.win_kv + (static_cast<long long>(tq) + a.window - wl) * D;
+
+    // this token's selected indices to LDS; the query tile's B operands
+    const int* idx = a.idx + static_cast<long long>(tq) * a.k;
+    for (int j = threadIdx.x; j < cnt; j += kPaThreads) {
+        const int r = idx[j];
+        sidx[j] = r < 0 ? 0 : (r >= a.n_comp ? a.n_comp - 1 : r);
+    }
+    bf16x8 qb[C::kKs];
+    if (active) {
+        const uint16_t* qh = a.q + (static_cast<long long>(tq) * a.h + 16 * wv + li) * D + 8 * lg;
+#pragma unroll
+        for (int ks = 0; ks < C::kKs; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qh + 32 * ks);
+    }
+    __syncthreads();
+
+    uint4 v[C::kIpt][4];
+    auto load_chunk = [&](int j0) {
+#pragma unroll
+        for (int u = 0; u < C::kIpt; ++u) {
+            const int it = threadIdx.x + u * kPaThreads;
+            const int rg = it % (kPaRows / 4);
+            const int cc = it / (kPaRows / 4);
+#pragma unroll
+            for (int u2 = 0; u2 < 4; ++u2) {
+                const int j = j0 + 4 * rg + u2;
+                const uint16_t* src = nullptr;
+                if (it < C::kItems && j < nv)
+                    src = j < cnt ? a.comp_kv + static_cast<long long>(sidx[j]) * D
+                                  : win + static_cast<long long>(j - cnt) * D;
+                v[u][u2] = src ? *reinterpret_cast<const uint4*>(src + 8 * cc) : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto store_chunk = [&]() {
+#pragma unroll
+        for (int u = 0; u < C::kIpt; ++u) {
+            const int it = threadIdx.x + u * kPaThreads;
+            if (it >= C::kItems) continue;
+            const int rg = it % (kPaRows / 4);
+            const int cc = it / (kPaRows / 4);
+#pragma unroll
+            for (int u2 = 0; u2 < 4; ++u2)
+                *reinterpret_cast<uint4*>(kr + (4 * rg + u2) * C::kKrPitch + 8 * cc) = v[u][u2];
+            // transpose: column 8*cc + e gets rows 4*rg .. 4*rg + 3 (one 8-byte write)
+            const uint32_t w0[4] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w};
+            const uint32_t w1[4] = {v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+            const uint32_t w2[4] = {v[u][2].x, v[u][2].y, v[u][2].z, v[u][2].w};
+            const uint32_t w3[4] = {v[u][3].x, v[u][3].y, v[u][3].z, v[u][3].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int sh = 16 * (e & 1);
+                const uint32_t r0 = (w0[e >> 1] >> sh) & 0xffffu, r1 = (w1[e >> 1] >> sh) & 0xffffu;
+                const uint32_t r2 = (w2[e >> 1] >> sh) & 0xffffu, r3 = (w3[e >> 1] >> sh) & 0xffffu;
+                *reinterpret_cast<uint2*>(vt + (8 * cc + e) * kVtPitch + 4 * rg) =
+                    make_uint2(r0 | (r1 << 16), r2 | (r3 << 16));
+            }
+        }
+    };
+
+    f32x4 o[C::kMd];
+#pragma unroll
+    for (int md = 0; md < C::kMd; ++md) o[md] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const int n_chunks = (nv + kPaRows - 1) / kPaRows;
+    load_chunk(0);
+    for (int c = 0; c < n_chunks; ++c) {
+        store_chunk();
+        __syncthreads();
+        if (c + 1 < n_chunks) load_chunk(kPaRows * (c + 1));
+        if (active) {
+            // S^T = K Q^T: lane holds rows 16*mt + 4*lg + r, head li
+            f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ks = 0; ks < C::kKs; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kr + (16 * mt + li) * C::kKrPitch + 32 * ks + 8 * lg);
+                    st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[ks], st[mt], 0, 0, 0);
+                }
+            const int j0 = kPaRows * c;
+            float sv[8];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = j0 + 16 * mt + 4 * lg + r;
+                    sv[4 * mt + r] = j < nv ? st[mt][r] * a.scale : -INFINITY;
+                }
+            float cm = sv[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) cm = fmaxf(cm, sv[e]);
+            cm = fmaxf(cm, xor_lanes_f32<16>(cm));
+            cm = fmaxf(cm, xor_lanes_f32<32>(cm));
+            const float m_new = fmaxf(m_run, cm);  // every chunk holds a valid row: finite
+            const float alpha = expf(m_run - m_new);
+            uint16_t pb[8];
+            float ls = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pb[e] = f32_to_bf16(expf(sv[e] - m_new));
+                ls += bf16_to_f32(pb[e]);
+            }
+            ls += xor_lanes_f32<16>(ls);
+            ls += xor_lanes_f32<32>(ls);
+            l_run = l_run * alpha + ls;
+            m_run = m_new;
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+                for (int md = 0; md < C::kMd; ++md) o[md] *= alpha;
+            }
+            bf16x8 pv;
+            __builtin_memcpy(&pv, pb, sizeof(pv));
+            // O^T += V^T P^T: k-slots 0..3 <-> rows 4*lg + e, 4..7 <-> rows 16 + 4*lg + e - 4
+#pragma unroll
+            for (int md = 0; md < C::kMd; ++md) {
+                const uint16_t* vr = vt + (16 * md + li) * kVtPitch + 4 * lg;
+                const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+                const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+                const uint32_t wv4[4] = {lo.x, lo.y, hi.x, hi.y};
+                bf16x8 va;
+                __builtin_memcpy(&va, wv4, sizeof(va));
+                o[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pv, o[md], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+    if (!active) return;
+    // the sink joins the denominator once, at the end
+    const int hh = 16 * wv + li;
+    const float sk = a.sink ? a.sink[hh] : -INFINITY;
+    const float M = fmaxf(m_run, sk);
+    const float em = expf(m_run - M);
+    const float es = sk == -INFINITY ? 0.f : expf(sk - M);
+    const float den = l_run * em + es;
+    const float f = em / den;
+    const long long ob = (static_cast<long long>(tq) * a.h + hh) * D + 4 * lg;
+#pragma unroll
+    for (int md = 0; md < C::kMd; ++md) {
+        if (a.out_bf16) {
+            const uint32_t x0 = f32_to_bf16(o[md][0] * f) | (static_cast<uint32_t>(f32_to_bf16(o[md][1] * f)) << 16);
+            const uint32_t x1 = f32_to_bf16(o[md][2] * f) | (static_cast<uint32_t>(f32_to_bf16(o[md][3] * f)) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + ob + 16 * md) = make_uint2(x0, x1);
+        } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + ob + 16 * md) =
+                make_float4(o[md][0] * f, o[md][1] * f, o[md][2] * f, o[md][3] * f);
+        }
+    }
+    if (a.lse && lg == 0) a.lse[static_cast<long long>(tq) * a.h + hh] = M + logf(den);
+}
+
+template <int D>
+size_t prefill_attn_lds(int k) {
+    return PaCfg<D>::kLdsRows + sizeof(int) * static_cast<size_t>(k);
+}
+
+template <int D>
+hipError_t launch_prefill_attn_d(const PrefillAttnArgs& a, hipStream_t s) {
+    const size_t lds = prefill_attn_lds<D>(a.k);
+    if (lds > 64 * 1024) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+        static size_t opted[64] = {};
+        if (opted[dev] < lds) {
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<D>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     static_cast<int>(prefill_attn_lds<D>(kTopkMaxK)));
+            if (e != hipSuccess) return e;
+            opted[dev] = prefill_attn_lds<D>(kTopkMaxK);
+        }
+    }
+    hipLaunchKernelGGL(k_prefill_attn<D>, dim3(a.t), dim3(kPaThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_index_score_mq(const ScoreArgs& sa, long long pos0, hipStream_t s) {
+    if (sa.t <= 0 || sa.n <= 0 || sa.batch <= 0) return hipSuccess;
+    const int groups = (sa.t + kMqRowsPerWg - 1) / kMqRowsPerWg;
+    // one workgroup per CU in all; each key range is a whole number of 16-key tiles
+    const long long per_split = static_cast<long long>(groups) * sa.batch;
+    int splits = static_cast<int>((device_cu_count() + per_split - 1) / per_split);
+    if (splits < 1) splits = 1;
+    int kpw = (sa.n + splits - 1) / splits;
+    kpw = (kpw + 15) / 16 * 16;
+    splits = (sa.n + kpw - 1) / kpw;
+    MqArgs a{static_cast<const uint16_t*>(sa.q), sa.w, static_cast<const uint16_t*>(sa.k), sa.scores, sa.t, sa.n,
+             sa.ld_s, sa.q_pos, pos0, sa.ratio, kpw, sa.q_stride_b, sa.w_stride_b, sa.k_stride_b, sa.s_stride_b};
+    hipLaunchKernelGGL((k_index_score_mq<CSA_MQ_SHAPE>), dim3(splits, groups, sa.batch), dim3(Mq::kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+size_t index_topk_workspace_bytes(int t, int n, int top_k) {
+    const int rows = t < kPrefillChunkRows ? t : kPrefillChunkRows;
+    return pf_align256(sizeof(float) * static_cast<size_t>(rows) * (n > 0 ? n : 0)) +
+           pf_align256(topk_workspace_bytes(rows, n, top_k));
+}
+
+hipError_t launch_index_topk(const IndexTopkArgs& a, hipStream_t s) {
+    if (a.t <= 0) return hipSuccess;
+    const int rows_max = a.t < kPrefillChunkRows ? a.t : kPrefillChunkRows;
+    float* sc = static_cast<float*>(a.ws);
+    void* tws = static_cast<char*>(a.ws) + pf_align256(sizeof(float) * static_cast<size_t>(rows_max) * a.n);
+    for (int r0 = 0; r0 < a.t; r0 += kPrefillChunkRows) {
+        const int rows = a.t - r0 < kPrefillChunkRows ? a.t - r0 : kPrefillChunkRows;
+        ScoreArgs sa{};
+        sa.q = a.q + static_cast<long long>(r0) * kIdxHeads * kIdxDi;
+        sa.w = a.w + static_cast<long long>(r0) * kIdxHeads;
+        sa.k = a.k;
+        sa.scores = sc;
+        sa.batch = 1;
+        sa.t = rows;
+        sa.h_i = kIdxHeads;
+        sa.d_i = kIdxDi;
+        sa.n = a.n;
+        sa.ratio = a.ratio;
+        sa.ld_s = a.n;
+        hipError_t e = launch_index_score_mq(sa, a.pos0 < 0 ? -1 : a.pos0 + r0, s);
+        if (e != hipSuccess) return e;
+        TopkArgs ta{};
+        ta.scores = sc;
+        ta.batch = 1;
+        ta.t = rows;
+        ta.n = a.n;
+        ta.ld_s = a.n;
+        ta.s_stride_b = 0;
+        ta.k = a.top_k;
+        ta.idx = a.idx + static_cast<long long>(r0) * a.top_k;
+        ta.count = a.count ? a.count + r0 : nullptr;
+        ta.ws = tws;
+        e = launch_topk(ta, nullptr, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+bool prefill_attn_supported(int h, int d) {
+    return h > 0 && h % 16 == 0 && h <= 16 * kPaWaves && (d == 128 || d == 256 || d == 512);
+}
+
+hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
+    if (a.t <= 0) return hipSuccess;
+    switch (a.d) {
+        case 128: return launch_prefill_attn_d<128>(a, s);
+        case 256: return launch_prefill_attn_d<256>(a, s);
+        case 512: return launch_prefill_attn_d<512>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace csa

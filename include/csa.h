@@ -115,6 +115,8 @@ int csa_compress(const float *z, const float *c, const float *bias, const float 
  * q_pos:  [B][t] int32 device positions for the causal mask, or NULL.
  * Supported: bfloat16 with h_i = 64, d_i = 128 (matrix-core path) and
  *   float32 with h_i <= 64, d_i <= 256, h_i * d_i <= 8192.  n >= 0; ld_s >= n.
+ * With bfloat16 and t >= 16 query rows the multi-query scan of section 7
+ * runs; every bfloat16 path gives the same bits for the same (query, key).
  * ------------------------------------------------------------------------ */
 int csa_index_score(const void *q, const float *w, const void *k, float *scores,
                     csa_dtype dtype, int batch, int t, int h_i, int d_i, int n,
@@ -306,6 +308,55 @@ int csa_decode_step(const csa_layer_desc *layer, const csa_step_io *io, void *ws
 
 /* Advance the host-known counters of `layer` past a step at position pos. */
 int csa_layer_advance(csa_layer_desc *layer, int pos);
+
+/* ------------------------------------------------------------------------
+ * 7. Prefill-shaped chunk: t query tokens at positions pos0, pos0+1, ...
+ *    against one compressed history.
+ *
+ * Sources: the index score and its causal mask as in section 2; the
+ * fixed-shape top-k of section 3; the per-query composition of page 2,
+ * single_shot_inference.py, eager_attention (score -> top-k -> one softmax
+ * over the selected compressed rows, then the sliding window, plus the sink
+ * of the D5c hunk on page 1).  The history holds the chunk's own blocks too:
+ * the causal mask hides each block until the query that completes it.  The
+ * window of the query at position p is the raw KV of positions
+ * max(0, p - window + 1) .. p, oldest first (the decode step's SWA window,
+ * applied per query).
+ *
+ * csa_index_topk: score + causal mask + top-k for every query, bfloat16 keys
+ *   and queries (h_i = 64, d_i = 128), without holding all t x n scores:
+ *   at most 256 query rows of scores live in the workspace at a time.
+ *   q: [t][64][128] bf16, w: [t][64] float32, k: [n][128] bf16 (16-byte
+ *   aligned); pos0 >= 0 gives query row r the position pos0 + r (pos0 < 0:
+ *   no mask).  idx: [t][top_k] int32 out (rank order: score descending,
+ *   lower index first on ties; -1 past the count), count: [t] int32 out
+ *   (nullable) = min(top_k, visible blocks).  1 <= top_k <= 2048.
+ *   ws: csa_index_topk_workspace_size(t, n, top_k) bytes, 16-byte aligned.
+ *
+ * csa_prefill_attn: per query row r, one softmax (scale, then the sink in the
+ *   denominator only) over comp_kv[idx[r][0 .. count[r])] followed by its
+ *   window rows.  q: [t][h][d] bf16; comp_kv: [n_comp][d] bf16; idx/count as
+ *   csa_index_topk writes them (count nullable: k rows; indices outside
+ *   0..n_comp-1 are clamped); win_kv: [t + window - 1][d] bf16, row i
+ *   holding position pos0 - window + 1 + i (rows of negative positions are
+ *   never read); sink: [h] float32 or NULL; out: [t][h][d] of out_dtype
+ *   (float32 or bfloat16); lse: [t][h] float32 (sink included) or NULL.
+ *   Supported: h a multiple of 16 up to 64, d in {128, 256, 512},
+ *   pos0 >= 0, window >= 1, 1 <= k <= 2048.  No workspace.
+ *
+ * Both only enqueue work on `stream`; all pointers are device memory owned
+ * by the caller.  Errors: CSA_ERR_INVALID_ARG for null/misaligned pointers
+ * or out-of-range sizes, CSA_ERR_UNSUPPORTED for other head/width shapes,
+ * CSA_ERR_WORKSPACE for a short workspace, CSA_ERR_LAUNCH on launch failure.
+ * ------------------------------------------------------------------------ */
+size_t csa_index_topk_workspace_size(int t, int n, int top_k);
+int csa_index_topk(const void *q, const float *w, const void *k, int t, int h_i, int d_i, int n,
+                   long long pos0, int ratio, int top_k, int *idx, int *count, void *ws,
+                   size_t ws_bytes, csa_stream stream);
+int csa_prefill_attn(const void *q, const void *comp_kv, int n_comp, const int *idx,
+                     const int *count, int k, const void *win_kv, int window, long long pos0,
+                     const float *sink, float scale, void *out, csa_dtype out_dtype, float *lse,
+                     int t, int h, int d, csa_stream stream);
 
 #ifdef __cplusplus
 }

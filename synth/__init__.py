@@ -42,7 +42,8 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = ["Shape", "SHAPES", "CONFIG_NUMBER", "seed_for", "make_decode_inputs",
-           "make_decode_inputs_torch", "to_bf16_bits", "rng"]
+           "make_decode_inputs_torch", "make_prefill_inputs", "make_prefill_inputs_torch",
+           "to_bf16_bits", "rng"]
 
 
 @dataclass(frozen=True)
@@ -214,6 +215,68 @@ def make_decode_inputs_torch(shape: Shape, seed: int, device, layers: Optional[i
                  swa_len=min(pos, W), pos=pos)
         res.append(d)
     return res
+
+
+def make_prefill_inputs(shape: Shape, seed: int) -> dict:
+    """Host (numpy) inputs of a prefill-shaped chunk: ``shape.t`` query tokens
+    at positions ``pos0 .. pos0 + t - 1`` (``pos0 = ctx - t``) against
+    ``n_comp`` compressed blocks (the chunk's own blocks included).
+
+    Returns ``q_idx [t, H_I, d_I]``, ``w_idx [t, H_I]``, ``idx_keys [N, d_I]``,
+    ``comp_kv [N, D]``, ``q [t, H, D]``, ``win_kv [t + W - 1, D]`` (row ``i``
+    = the raw KV of position ``pos0 - W + 1 + i``), ``sink [H]`` and ``pos0``.
+    """
+    g = rng(seed)
+    T, N, D, di, W = shape.t, shape.n_comp, shape.d, shape.d_i, shape.w
+    f32 = np.float32
+
+    def normal(*sz, std=1.0):
+        return (g.standard_normal(sz, dtype=f32) * f32(std)).astype(f32)
+
+    def rows(*sz):
+        x = normal(*sz)
+        return _rms_rows(x) if shape.rms_norm else x
+
+    return {
+        "q_idx": _store(normal(T, shape.h_i, di, std=1.0 / np.sqrt(di)), shape.dtype),
+        "w_idx": normal(T, shape.h_i),
+        "idx_keys": _store(normal(N, di), shape.dtype),
+        "comp_kv": _store(rows(N, D), shape.dtype),
+        "q": _store(rows(T, shape.h, D), shape.dtype),
+        "win_kv": _store(rows(T + W - 1, D), shape.dtype),
+        "sink": normal(shape.h),
+        "pos0": shape.ctx - T,
+    }
+
+
+def make_prefill_inputs_torch(shape: Shape, seed: Optional[int], device) -> dict:
+    """Device-resident prefill inputs (same layout and distributions as
+    :func:`make_prefill_inputs`), drawn with torch's seeded generator."""
+    import torch
+    dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    T, N, D, di, W = shape.t, shape.n_comp, shape.d, shape.d_i, shape.w
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed_for(shape) if seed is None else seed)
+
+    def normal(*sz, std=1.0):
+        return torch.randn(*sz, generator=gen, device=device, dtype=torch.float32) * std
+
+    def rows(*sz):
+        x = normal(*sz)
+        if shape.rms_norm:
+            x = x * torch.rsqrt(x.square().mean(-1, keepdim=True) + 1e-6)
+        return x
+
+    return {
+        "q_idx": (normal(T, shape.h_i, di) / float(np.sqrt(di))).to(dt),
+        "w_idx": normal(T, shape.h_i),
+        "idx_keys": normal(N, di).to(dt),
+        "comp_kv": rows(N, D).to(dt),
+        "q": rows(T, shape.h, D).to(dt),
+        "win_kv": rows(T + W - 1, D).to(dt),
+        "sink": normal(shape.h),
+        "pos0": shape.ctx - T,
+    }
 
 
 def with_(shape: Shape, **kw) -> Shape:

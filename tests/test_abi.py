@@ -129,6 +129,49 @@ def test_fp8_entry_points_reject_bad_args(csa):
     assert lib.csa_index_score_fp8(*a) == B.CSA_ERR_INVALID_ARG
 
 
+def test_prefill_entry_points_reject_bad_args(csa):
+    lib = csa.lib()
+    B = csa.binding
+    ws = lib.csa_index_topk_workspace_size(2048, 65536, 512)
+    # 256 query rows of scores at a time, plus the top-k lists of those rows
+    assert ws >= 256 * 65536 * 4
+    assert lib.csa_index_topk_workspace_size(16, 65536, 512) < ws
+    assert lib.csa_index_topk_workspace_size(0, 65536, 512) == 0
+    base = [FAKE, FAKE, FAKE, 2048, 64, 128, 65536, 260096, 4, 512, FAKE, FAKE, FAKE, ws, None]
+    a = list(base); a[5] = 64
+    assert lib.csa_index_topk(*a) == B.CSA_ERR_UNSUPPORTED
+    a = list(base); a[9] = 0
+    assert lib.csa_index_topk(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(base); a[9] = 2049
+    assert lib.csa_index_topk(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(base); a[13] = ws - 1
+    assert lib.csa_index_topk(*a) == B.CSA_ERR_WORKSPACE
+    a = list(base); a[2] = FAKE + 8
+    assert lib.csa_index_topk(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(base); a[10] = None
+    assert lib.csa_index_topk(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(base); a[8] = 0
+    assert lib.csa_index_topk(*a) == B.CSA_ERR_INVALID_ARG
+    attn = [FAKE, FAKE, 65536, FAKE, FAKE, 512, FAKE, 128, 260096, FAKE, 0.04, FAKE, B.CSA_BF16, None,
+            2048, 64, 512, None]
+    a = list(attn); a[15] = 8                   # heads not a multiple of 16
+    assert lib.csa_prefill_attn(*a) == B.CSA_ERR_UNSUPPORTED
+    a = list(attn); a[16] = 384                 # unsupported width
+    assert lib.csa_prefill_attn(*a) == B.CSA_ERR_UNSUPPORTED
+    a = list(attn); a[7] = 0                    # empty window
+    assert lib.csa_prefill_attn(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(attn); a[8] = -1                   # negative position
+    assert lib.csa_prefill_attn(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(attn); a[5] = 4096                 # k above the top-k limit
+    assert lib.csa_prefill_attn(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(attn); a[12] = B.CSA_FP8_E4M3
+    assert lib.csa_prefill_attn(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(attn); a[6] = FAKE + 2             # misaligned window rows
+    assert lib.csa_prefill_attn(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(attn); a[3] = None
+    assert lib.csa_prefill_attn(*a) == B.CSA_ERR_INVALID_ARG
+
+
 def test_topk_rejects_bad_args_and_sizes_workspace(csa):
     lib = csa.lib()
     B = csa.binding

@@ -1,0 +1,292 @@
+"""GPU parity of the prefill-shaped chunk (many query tokens at consecutive
+positions against one compressed history) against the float64 CPU oracle.
+
+* multi-query index score (csa_index_score with >= 16 query rows): 1e-4
+  relative, and bit-identical to the one-query scan on the same inputs;
+* csa_index_topk: bit-exact against the oracle's top-k of the GPU's own
+  scores, and the gap rule against the oracle's float64 scores;
+* csa_prefill_attn: bfloat16 outputs within 2e-2 relative of the oracle's
+  attention over the same selected rows and window.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import DEV, as_f64, assert_topk_gap_rule, dev_bf16, dev_f32, host_f64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def csa():
+    import compressed_sparse_attention_reduce_amd as pkg
+    pkg.lib()
+    return pkg
+
+
+def _g(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _bf16(g, shape, std=1.0):
+    return synth.to_bf16_bits((g.standard_normal(shape, dtype=np.float32) * np.float32(std)))
+
+
+def _visible(pos, n, ratio=4):
+    return np.clip((np.asarray(pos, dtype=np.int64) - (ratio - 1)) // ratio + 1, 0, n)
+
+
+# ---------------------------------------------------------------------------
+# multi-query index score
+# ---------------------------------------------------------------------------
+
+MQ_CASES = [
+    # name, B, t, n, causal
+    ("mq_causal_ragged_batch2", 2, 37, 1000, True),
+    ("mq_16_rows_31_keys", 1, 16, 31, False),
+    ("mq_70_rows_4111_keys", 1, 70, 4111, True),
+    ("mq_one_key", 3, 17, 1, False),
+]
+
+
+@pytest.mark.parametrize("case", MQ_CASES, ids=[c[0] for c in MQ_CASES])
+def test_multi_query_score(csa, case):
+    name, B, t, n, causal = case
+    g = _g(t * 1000 + n)
+    q = _bf16(g, (B, t, 64, 128), 1 / np.sqrt(128))
+    w = g.standard_normal((B, t, 64), dtype=np.float32)
+    K = _bf16(g, (B, n, 128))
+    ld = n + 3
+    scores = torch.full((B, t, ld), 123.0, device=DEV)
+    pos_np = None
+    pos = None
+    if causal:
+        pos_np = (4 * n - 2 * t - 9 + 2 * np.arange(B * t)).astype(np.int32).reshape(B, t)
+        pos = torch.from_numpy(pos_np).to(DEV)
+    csa.csa_index_score(dev_bf16(q), dev_f32(w), dev_bf16(K), scores, q_pos=pos, ratio=4)
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy().astype(np.float64)
+    assert (got[:, :, n:] == 123.0).all(), "wrote past n"
+    for b in range(B):
+        ref = oracle.index_score(as_f64(q[b]), w[b], as_f64(K[b]), q_pos=None if pos_np is None else pos_np[b])
+        fin = np.isfinite(ref)
+        assert (np.isfinite(got[b, :, :n]) == fin).all(), "mask differs"
+        assert rel_err(got[b, :, :n][fin], ref[fin]) <= 1e-4
+
+
+def test_multi_query_score_bit_identical_to_one_query_scan(csa):
+    """24 query rows in one call (multi-query scan) and one row per call (the
+    decode scan): the same bits for every (query, key)."""
+    g = _g(77)
+    t, n = 24, 2500
+    q = dev_bf16(_bf16(g, (1, t, 64, 128), 1 / np.sqrt(128)))
+    w = dev_f32(g.standard_normal((1, t, 64), dtype=np.float32))
+    K = dev_bf16(_bf16(g, (1, n, 128)))
+    many = torch.empty(1, t, n, device=DEV)
+    csa.csa_index_score(q, w, K, many)
+    one = torch.empty(1, t, n, device=DEV)
+    for r in range(t):
+        csa.csa_index_score(q[:, r:r + 1], w[:, r:r + 1], K, one[:, r:r + 1])
+    torch.cuda.synchronize()
+    assert torch.equal(many, one)
+
+
+# ---------------------------------------------------------------------------
+# fused score + top-k over the chunk
+# ---------------------------------------------------------------------------
+
+TOPK_CASES = [
+    # name, t, n, k, pos0
+    ("two_chunks_causal", 300, 2000, 64, 7800),
+    ("fewer_visible_than_k", 20, 400, 512, 1000),
+    ("no_mask", 17, 5000, 512, -1),
+    ("k1_one_chunk", 40, 3000, 1, 11997),
+    ("ragged_last_chunk", 261, 700, 128, 2600),
+]
+
+
+def _run_index_topk(csa, q, w, K, k, pos0, n=None):
+    t = q.shape[0]
+    n = K.shape[0] if n is None else n
+    idx = torch.full((t, k), -5, dtype=torch.int32, device=DEV)
+    cnt = torch.full((t,), -5, dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(csa.csa_index_topk_workspace_size(t, n, k), 16), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xCD)  # needs no initialisation
+    csa.csa_index_topk(q, w, K, idx, cnt, ws, pos0=pos0, n=n)
+    return idx, cnt
+
+
+@pytest.mark.parametrize("case", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
+def test_index_topk(csa, case):
+    name, t, n, k, pos0 = case
+    g = _g(t + 7 * n + k)
+    qn = _bf16(g, (t, 64, 128), 1 / np.sqrt(128))
+    wn = g.standard_normal((t, 64), dtype=np.float32)
+    Kn = _bf16(g, (n, 128))
+    q, w, K = dev_bf16(qn), dev_f32(wn), dev_bf16(Kn)
+    idx, cnt = _run_index_topk(csa, q, w, K, k, pos0)
+    # the GPU's own scores (same bits as the chunk scan), with the same mask
+    scores = torch.empty(1, t, n, device=DEV)
+    pos = None
+    if pos0 >= 0:
+        pos = torch.arange(pos0, pos0 + t, dtype=torch.int32, device=DEV)[None]
+    csa.csa_index_score(q[None], w[None], K[None], scores, q_pos=pos)
+    torch.cuda.synchronize()
+    gs = scores[0].cpu().numpy().astype(np.float64)
+    ri, rc = oracle.topk(gs, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+    if pos0 >= 0:
+        np.testing.assert_array_equal(rc, np.minimum(k, _visible(pos0 + np.arange(t), n)))
+    # against the oracle's float64 scores on a few rows
+    rows = sorted({0, t // 2, t - 1})
+    ref = oracle.index_score(as_f64(qn[rows]), wn[rows], as_f64(Kn),
+                             q_pos=None if pos0 < 0 else pos0 + np.array(rows))
+    for i, r in enumerate(rows):
+        assert_topk_gap_rule(idx[r].cpu().numpy(), int(cnt[r]), ref[i], k)
+
+
+def test_index_topk_empty_history(csa):
+    g = _g(5)
+    q = dev_bf16(_bf16(g, (16, 64, 128)))
+    w = dev_f32(g.standard_normal((16, 64), dtype=np.float32))
+    K = torch.empty(0, 128, dtype=torch.bfloat16, device=DEV)
+    idx, cnt = _run_index_topk(csa, q, w, K, 8, 0)
+    torch.cuda.synchronize()
+    assert (idx == -1).all() and (cnt == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# per-query attention over the selected rows and the window
+# ---------------------------------------------------------------------------
+
+ATTN_CASES = [
+    # name, t, h, d, n_comp, k, window, pos0, sink, out_bf16, full_count
+    ("h64_d512_clipped_windows", 40, 64, 512, 3000, 64, 128, 50, True, True, True),
+    ("h16_d128_short_counts", 33, 16, 128, 500, 100, 16, 1000, True, True, False),
+    ("h32_d256_f32_no_sink", 18, 32, 256, 700, 40, 8, 7, False, False, False),
+    ("h64_d512_from_position0", 20, 64, 512, 0, 16, 128, 0, True, True, False),
+]
+
+
+def _attn_ref(q, comp, idx, cnt, win, window, pos0, sink, scale):
+    t = q.shape[0]
+    outs, lses = [], []
+    for r in range(t):
+        p = pos0 + r
+        first = max(0, p - window + 1)
+        wrows = [win[x - (pos0 - window + 1)] for x in range(first, p + 1)]
+        sel = [comp[int(idx[r, j])] for j in range(int(cnt[r]))]
+        o, l = oracle.sparse_attn(q[r], np.stack(sel + wrows), sink, scale)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_prefill_attn(csa, case):
+    name, t, h, d, n_comp, k, window, pos0, use_sink, out_bf16, full = case
+    g = _g(t * h + d + n_comp)
+    qn = _bf16(g, (t, h, d))
+    comp = _bf16(g, (max(n_comp, 1), d))
+    win = _bf16(g, (t + window - 1, d))
+    sink = g.standard_normal(h, dtype=np.float32) if use_sink else None
+    idx = g.integers(0, max(n_comp, 1), size=(t, k)).astype(np.int32)
+    cnt = np.full(t, k if n_comp else 0, dtype=np.int32) if full else \
+        g.integers(0, k + 1, size=t).astype(np.int32) * (n_comp > 0)
+    for r in range(t):
+        idx[r, cnt[r]:] = -1
+    out = torch.full((t, h, d), 7.0, dtype=torch.bfloat16 if out_bf16 else torch.float32, device=DEV)
+    lse = torch.empty(t, h, device=DEV)
+    scale = 1.0 / np.sqrt(d)
+    comp_d = dev_bf16(comp)[:n_comp] if n_comp else dev_bf16(comp)
+    csa.csa_prefill_attn(dev_bf16(qn), comp_d, torch.from_numpy(idx).to(DEV), torch.from_numpy(cnt).to(DEV),
+                         dev_bf16(win), window, pos0, None if sink is None else dev_f32(sink), scale, out, lse=lse,
+                         n_comp=n_comp)
+    torch.cuda.synchronize()
+    ro, rl = _attn_ref(as_f64(qn), as_f64(comp), idx, cnt, as_f64(win), window, pos0,
+                       None if sink is None else sink.astype(np.float64), scale)
+    assert rel_err(host_f64(out), ro) <= 2e-2
+    assert np.abs(lse.cpu().numpy() - rl).max() <= 1e-2
+
+
+# ---------------------------------------------------------------------------
+# the whole chunk against the oracle's composition
+# ---------------------------------------------------------------------------
+
+def test_prefill_chunk_matches_oracle_composition(csa):
+    shape = synth.with_(synth.SHAPES["prefill"], t=48, n_comp=900, ctx=3600, top_k=96)
+    x = synth.make_prefill_inputs(shape, 5005)
+    T, k, W = shape.t, shape.top_k, shape.w
+    q_idx, w_idx, keys = dev_bf16(x["q_idx"]), dev_f32(x["w_idx"]), dev_bf16(x["idx_keys"])
+    idx, cnt = _run_index_topk(csa, q_idx, w_idx, keys, k, x["pos0"])
+    out = torch.empty(T, shape.h, shape.d, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(T, shape.h, device=DEV)
+    csa.csa_prefill_attn(dev_bf16(x["q"]), dev_bf16(x["comp_kv"]), idx, cnt, dev_bf16(x["win_kv"]), W, x["pos0"],
+                         dev_f32(x["sink"]), 1.0 / np.sqrt(shape.d), out, lse=lse)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_chunk(q=as_f64(x["q"]), q_idx=as_f64(x["q_idx"]), w_idx=x["w_idx"],
+                               idx_keys=as_f64(x["idx_keys"]), comp_kv=as_f64(x["comp_kv"]),
+                               win_kv=as_f64(x["win_kv"]), pos0=x["pos0"], top_k=k, window=W, sink=x["sink"])
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    for r in range(T):
+        assert_topk_gap_rule(gi[r], int(gc[r]), ref["scores"][r], k)
+    # attention over the GPU's selection (near-tie swaps allowed above)
+    ro, rl = _attn_ref(as_f64(x["q"]), as_f64(x["comp_kv"]), gi, gc, as_f64(x["win_kv"]), W, x["pos0"],
+                       x["sink"].astype(np.float64), 1.0 / np.sqrt(shape.d))
+    assert rel_err(host_f64(out), ro) <= 2e-2
+    assert np.abs(lse.cpu().numpy() - rl).max() <= 1e-2
+    same = [r for r in range(T) if (gi[r] == ref["idx"][r]).all()]
+    assert len(same) >= T // 2
+    assert rel_err(host_f64(out)[same], ref["out"][same]) <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# the full prefill workload (2048 queries, 65536 blocks), sampled
+# ---------------------------------------------------------------------------
+
+def test_prefill_full_size_sampled(csa):
+    shape = synth.SHAPES["prefill"]
+    x = synth.make_prefill_inputs_torch(shape, None, DEV)
+    T, N, k, W = shape.t, shape.n_comp, shape.top_k, shape.w
+    idx, cnt = _run_index_topk(csa, x["q_idx"], x["w_idx"], x["idx_keys"], k, x["pos0"])
+    out = torch.empty(T, shape.h, shape.d, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(T, shape.h, device=DEV)
+    csa.csa_prefill_attn(x["q"], x["comp_kv"], idx, cnt, x["win_kv"], W, x["pos0"], x["sink"],
+                         1.0 / np.sqrt(shape.d), out, lse=lse)
+    torch.cuda.synchronize()
+    pos = x["pos0"] + np.arange(T)
+    assert (cnt.cpu().numpy() == np.minimum(k, _visible(pos, N))).all()
+    rows = [0, 1, 255, 256, 1027, 2046, 2047]
+    sel = torch.tensor(rows, device=DEV)
+    scores = torch.empty(1, len(rows), N, device=DEV)
+    csa.csa_index_score(x["q_idx"][sel][None], x["w_idx"][sel][None], x["idx_keys"][None], scores,
+                        q_pos=torch.from_numpy(pos[rows].astype(np.int32)).to(DEV)[None])
+    torch.cuda.synchronize()
+    gs = scores[0].cpu().numpy().astype(np.float64)
+    ri, rc = oracle.topk(gs, k)
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    np.testing.assert_array_equal(gi[rows], ri)
+    np.testing.assert_array_equal(gc[rows], rc)
+    keys = host_f64(x["idx_keys"])
+    for i in (0, len(rows) - 1):
+        r = rows[i]
+        ref = oracle.index_score(host_f64(x["q_idx"][r])[None], host_f64(x["w_idx"][r])[None], keys,
+                                 q_pos=np.array([pos[r]]))[0]
+        assert rel_err(gs[i][np.isfinite(ref)], ref[np.isfinite(ref)]) <= 1e-4
+        assert_topk_gap_rule(gi[r], int(gc[r]), ref, k)
+    comp = host_f64(x["comp_kv"])
+    win = host_f64(x["win_kv"])
+    qh = host_f64(x["q"][sel])
+    sink = host_f64(x["sink"])
+    outs = host_f64(out[sel])
+    for i, r in enumerate(rows):
+        p = int(pos[r])
+        wrows = [win[xx - (x["pos0"] - W + 1)] for xx in range(p - W + 1, p + 1)]
+        kv = np.concatenate([comp[gi[r, :gc[r]]], np.stack(wrows)])
+        o, l = oracle.sparse_attn(qh[i], kv, sink, 1.0 / np.sqrt(shape.d))
+        assert rel_err(outs[i], o) <= 2e-2
+        assert np.abs(lse[r].cpu().numpy() - l).max() <= 1e-2
