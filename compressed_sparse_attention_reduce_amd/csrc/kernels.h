@@ -93,6 +93,9 @@ struct TopkArgs {
 // cands: per-slot candidate lists already produced (by the score kernel), or
 // nullptr (the launcher produces them itself when the rows are long).
 hipError_t launch_topk(const TopkArgs& a, const CandArgs* cands, hipStream_t s);
+// Many rows of at most 65536 scores: one workgroup per row, the row held in
+// registers (no workspace); longer rows go to launch_topk.
+hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t s);
 
 // ---- gather ------------------------------------------------------------------
 hipError_t launch_gather(const void* comp_kv, int n_comp, const int* idx, const int* count, int k,

@@ -47,21 +47,27 @@ __host__ __device__ inline size_t pf_align256(size_t x) { return (x + 255) & ~st
 // multi-query index score
 // ---------------------------------------------------------------------------
 
-// Shape of the multi-query scan: query rows per wave, waves per workgroup,
-// key tiles in flight per wave.  16 query rows per workgroup either way.
-#ifndef CSA_MQ_SHAPE
-#define CSA_MQ_SHAPE 4, 4, 2
-#endif
-template <int kTok, int kWaves, int kRing>
-struct MqShape {
-    static constexpr int kThreads = kWaves * kWave;
-    static constexpr int kRows = kWaves * kTok;
-};
-using Mq = MqShape<CSA_MQ_SHAPE>;
-constexpr int kMqRowsPerWg = Mq::kRows;
 constexpr int kIdxHeads = 64;
 constexpr int kIdxDi = 128;
 constexpr int kIdxSteps = kIdxDi / 32;
+
+// Shape of the multi-query scan: query rows per wave, waves per workgroup,
+// key tiles per LDS group.  16 query rows per workgroup either way.
+#ifndef CSA_MQ_SHAPE
+#define CSA_MQ_SHAPE 2, 8, 8
+#endif
+template <int kTok, int kWaves, int kGroup>
+struct MqShape {
+    static constexpr int kThreads = kWaves * kWave;
+    static constexpr int kRows = kWaves * kTok;
+    static constexpr int kGroupTiles = kGroup;
+};
+using Mq = MqShape<CSA_MQ_SHAPE>;
+constexpr int kMqRowsPerWg = Mq::kRows;
+// s_waitcnt immediate: vmcnt(0), the other counters left free
+constexpr int kVmcntZero = 0x0f70;
+constexpr int kMqPitch = kIdxDi + 8;  // LDS key row: 272 B, so the 16 rows of a B operand spread over the banks
+constexpr size_t kMqLds = sizeof(uint16_t) * 2 * Mq::kGroupTiles * 16 * kMqPitch;
 
 struct MqArgs {
     const uint16_t* q;   // [B][t][64][128]
@@ -77,41 +83,79 @@ struct MqArgs {
     long long q_stride_b, w_stride_b, k_stride_b, s_stride_b;
 };
 
-template <int kMqTok, int kMqWaves, int kMqRing>
+// Every workgroup walks its key range in groups of kGroup 16-key tiles (4 KB
+// each, contiguous in memory).  Each thread owns one piece of every tile; it
+// holds the next group's pieces in registers while the current group is
+// computed from LDS, parks them in the other LDS slot at the start of the
+// next group and meets the others at one barrier per group, so the waves of
+// a SIMD drift apart within a group and one's MFMAs overlap the other's
+// epilogue.  The slot written at group g was last read at group g - 1,
+// before the previous barrier.
+template <int kMqTok, int kMqWaves, int kGroup>
 __global__ __launch_bounds__(kMqWaves * kWave, 1) void k_index_score_mq(MqArgs a) {
-    constexpr int kMqRowsPerWg = kMqWaves * kMqTok;
+    constexpr int kThreads = kMqWaves * kWave;
+    constexpr int kRowsWg = kMqWaves * kMqTok;
+    constexpr int kPer = 16 * kIdxDi / kThreads;  // bf16 elements of a tile per thread
+    constexpr int kSlot = kGroup * 16 * kMqPitch; // elements of one LDS group slot
+    static_assert(kPer == 8 || kPer == 4 || kPer == 2, "one 16-, 8- or 4-byte piece per thread");
+    static_assert(kMqTok % 2 == 0, "query rows go through the epilogue in pairs");
+    using Piece = typename std::conditional<kPer == 8, uint4,
+                                            typename std::conditional<kPer == 4, uint2, uint32_t>::type>::type;
+    extern __shared__ __attribute__((aligned(16))) uint16_t mq_lds[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const int li = lane & 15;
     const int lg = lane >> 4;
     const int b = blockIdx.z;
-    const int row0 = blockIdx.y * kMqRowsPerWg + kMqTok * wv;
-    if (row0 >= a.t) return;  // no barriers in this kernel
+    const int row0 = blockIdx.y * kRowsWg + kMqTok * wv;  // may be >= t: such waves only load and wait
     const int k0 = blockIdx.x * a.keys_per_wg;
     const int k1 = min(a.n, k0 + a.keys_per_wg);
-    if (k0 >= k1) return;
+    if (k0 >= k1) return;  // whole workgroup
     const int n_tiles = (k1 - k0 + 15) / 16;
-    int rows[kMqTok];  // a missing second row repeats the first; nothing of it is stored
-    long long pos[kMqTok];
+    const int n_groups = (n_tiles + kGroup - 1) / kGroup;
+    int rows[kMqTok];  // rows past the end repeat the last one; nothing of them is stored
+    int vis[kMqTok];   // keys visible to the row: key < vis (causal mask)
+    const bool masked = a.q_pos || a.pos0 >= 0;
 #pragma unroll
     for (int u = 0; u < kMqTok; ++u) {
         rows[u] = min(row0 + u, a.t - 1);
-        pos[u] = a.q_pos ? static_cast<long long>(a.q_pos[static_cast<long long>(b) * a.t + rows[u]])
-                         : (a.pos0 >= 0 ? a.pos0 + rows[u] : -1);
+        const long long p = a.q_pos ? static_cast<long long>(a.q_pos[static_cast<long long>(b) * a.t + rows[u]])
+                                    : a.pos0 + rows[u];
+        // block s is visible iff ratio*s + ratio - 1 <= p
+        const long long v = p >= a.ratio - 1 ? (p - (a.ratio - 1)) / a.ratio + 1 : 0;
+        vis[u] = !masked ? a.n : static_cast<int>(v < a.n ? v : a.n);
     }
-    const bool masked = a.q_pos || a.pos0 >= 0;
     const uint16_t* qb = a.q + b * a.q_stride_b;
     const float* wb = a.w + b * a.w_stride_b;
-    float* sb = a.scores + b * a.s_stride_b;
-
-    const uint16_t* kbase = a.k + b * a.k_stride_b + 8 * lg;
-    auto load_tile = [&](int j, bf16x8* dst) {
-        const int key = min(k0 + 16 * min(j, n_tiles - 1) + li, k1 - 1);
-        const uint16_t* p = kbase + static_cast<long long>(key) * kIdxDi;
+    // row pair v: lanes of rows 1 and 3 (lane & 16) store row 2v + 1, the others row 2v
+    const int odd = (lane >> 4) & 1;
+    float* my_row[kMqTok / 2];
+    int my_vis[kMqTok / 2];
 #pragma unroll
-        for (int s = 0; s < kIdxSteps; ++s) dst[s] = *reinterpret_cast<const bf16x8*>(p + 32 * s);
+    for (int v = 0; v < kMqTok / 2; ++v) {
+        my_row[v] = a.scores + b * a.s_stride_b + static_cast<long long>(rows[2 * v + odd]) * a.ld;
+        my_vis[v] = odd ? vis[2 * v + 1] : vis[2 * v];
+    }
+
+    // loader: thread -> (key of the tile, element offset in the row)
+    const int lk = threadIdx.x / (kIdxDi / kPer);
+    const int lo = (threadIdx.x % (kIdxDi / kPer)) * kPer;
+    const uint16_t* kbase = a.k + b * a.k_stride_b + lo;
+    auto gload = [&](int j) -> Piece {
+        const int key = min(k0 + 16 * min(j, n_tiles - 1) + lk, k1 - 1);
+        return *reinterpret_cast<const Piece*>(kbase + static_cast<long long>(key) * kIdxDi);
+    };
+    auto lstore = [&](int slot, int i, const Piece& v) {
+        *reinterpret_cast<Piece*>(mq_lds + slot * kSlot + i * 16 * kMqPitch + lk * kMqPitch + lo) = v;
     };
 
+    Piece pre[kGroup];
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) pre[i] = gload(i);
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) lstore(0, i, pre[i]);
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) pre[i] = gload(kGroup + i);
     bf16x8 qa[kMqTok][4][kIdxSteps];
     float wr[kMqTok][4][4];
 #pragma unroll
@@ -129,43 +173,56 @@ __global__ __launch_bounds__(kMqWaves * kWave, 1) void k_index_score_mq(MqArgs a
             wr[u][mt][0] = v.x; wr[u][mt][1] = v.y; wr[u][mt][2] = v.z; wr[u][mt][3] = v.w;
         }
     }
-    bf16x8 kb[kMqRing][kIdxSteps];
-#pragma unroll
-    for (int i = 0; i < kMqRing; ++i) load_tile(i, kb[i]);
+    // Every load so far (query, weights, the next group's pieces) lands before
+    // the loop: otherwise the wait inserted for the query registers inside the
+    // loop also waits, at run time, for the prefetch issued in the loop.
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    __syncthreads();
 
-    // Same ring discipline as the decode scan: refills only for tiles that
-    // exist in the steady loop, one clamped extra group, a last group with no
-    // refills, so every path leaves the same loads in flight.
-    auto step = [&](int i, int j, bool refill) {
-        const int key = k0 + 16 * j + li;
-        const bool live = j < n_tiles && key < k1;
+    for (int g = 0; g < n_groups; ++g) {
+        const int slot = g & 1;
+        if (g + 1 < n_groups) {  // uniform: park group g + 1, fetch group g + 2
 #pragma unroll
-        for (int u = 0; u < kMqTok; ++u) {
-            f32x4 acc[4];
+            for (int i = 0; i < kGroup; ++i) lstore(slot ^ 1, i, pre[i]);
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < kGroup; ++i) pre[i] = gload((g + 2) * kGroup + i);
+        }
+        const uint16_t* ks = mq_lds + slot * kSlot + li * kMqPitch + 8 * lg;
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) {
+            // tiles past the last one repeat it (clamped loads): no branch, so
+            // every group issues the same memory operations
+            const int j = min(g * kGroup + i, n_tiles - 1);
+            bf16x8 kb[kIdxSteps];
 #pragma unroll
             for (int s = 0; s < kIdxSteps; ++s)
+                kb[s] = *reinterpret_cast<const bf16x8*>(ks + i * 16 * kMqPitch + 32 * s);
+            // past-the-end keys repeat the last one (same data, same value)
+            const int keyc = min(k0 + 16 * j + li, k1 - 1);
+            // rows in pairs: the products of both, then one epilogue that
+            // leaves row 2v's score in lanes of rows 0/2, row 2v+1's in 1/3
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[u][mt][s], kb[i][s], acc[mt], 0, 0, 0);
-            if (refill && u == kMqTok - 1) load_tile(j + kMqRing, kb[i]);
-            float sc = tile_head_sum(acc, wr[u]);
-            if (masked && static_cast<long long>(a.ratio) * key + a.ratio - 1 > pos[u]) sc = -INFINITY;
-            if (live && lg == u && row0 + u < a.t) sb[static_cast<long long>(row0 + u) * a.ld + key] = sc;
+            for (int v = 0; v < kMqTok / 2; ++v) {
+                f32x4 acc[2][4];
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) acc[e][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < kIdxSteps; ++s)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+#pragma unroll
+                        for (int mt = 0; mt < 4; ++mt)
+                            acc[e][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[2 * v + e][mt][s], kb[s],
+                                                                                 acc[e][mt], 0, 0, 0);
+                const float sc = tile_head_sum2(acc[0], wr[2 * v], acc[1], wr[2 * v + 1]);
+                // every lane stores (lane groups repeat the value): no branch
+                my_row[v][keyc] = keyc < my_vis[v] ? sc : -INFINITY;
+            }
         }
-    };
-    int j0 = 0;
-    for (; j0 + 2 * kMqRing <= n_tiles; j0 += kMqRing)
-#pragma unroll
-        for (int i = 0; i < kMqRing; ++i) step(i, j0 + i, true);
-    if (j0 + kMqRing < n_tiles) {  // wave-uniform
-#pragma unroll
-        for (int i = 0; i < kMqRing; ++i) step(i, j0 + i, true);
-        j0 += kMqRing;
+        __syncthreads();
     }
-#pragma unroll
-    for (int i = 0; i < kMqRing; ++i) step(i, j0 + i, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -396,14 +453,27 @@ hipError_t launch_index_score_mq(const ScoreArgs& sa, long long pos0, hipStream_
     splits = (sa.n + kpw - 1) / kpw;
     MqArgs a{static_cast<const uint16_t*>(sa.q), sa.w, static_cast<const uint16_t*>(sa.k), sa.scores, sa.t, sa.n,
              sa.ld_s, sa.q_pos, pos0, sa.ratio, kpw, sa.q_stride_b, sa.w_stride_b, sa.k_stride_b, sa.s_stride_b};
-    hipLaunchKernelGGL((k_index_score_mq<CSA_MQ_SHAPE>), dim3(splits, groups, sa.batch), dim3(Mq::kThreads), 0, s, a);
+    if (kMqLds > 64 * 1024) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+        static bool opted[64] = {};
+        if (!opted[dev]) {
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_index_score_mq<CSA_MQ_SHAPE>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     static_cast<int>(kMqLds));
+            if (e != hipSuccess) return e;
+            opted[dev] = true;
+        }
+    }
+    hipLaunchKernelGGL((k_index_score_mq<CSA_MQ_SHAPE>), dim3(splits, groups, sa.batch), dim3(Mq::kThreads), kMqLds,
+                       s, a);
     return hipGetLastError();
 }
 
 size_t index_topk_workspace_bytes(int t, int n, int top_k) {
     const int rows = t < kPrefillChunkRows ? t : kPrefillChunkRows;
     return pf_align256(sizeof(float) * static_cast<size_t>(rows) * (n > 0 ? n : 0)) +
-           pf_align256(topk_workspace_bytes(rows, n, top_k));
+           pf_align256(topk_workspace_bytes(rows, n, top_k));  // used only by rows over 65536 scores
 }
 
 hipError_t launch_index_topk(const IndexTopkArgs& a, hipStream_t s) {
@@ -438,7 +508,7 @@ hipError_t launch_index_topk(const IndexTopkArgs& a, hipStream_t s) {
         ta.idx = a.idx + static_cast<long long>(r0) * a.top_k;
         ta.count = a.count ? a.count + r0 : nullptr;
         ta.ws = tws;
-        e = launch_topk(ta, nullptr, s);
+        e = launch_topk_rows(ta, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

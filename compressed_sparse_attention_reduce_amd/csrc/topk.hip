@@ -60,6 +60,25 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(TopkArgs a, CandAr
     if (a.count && threadIdx.x == 0) a.count[static_cast<long long>(b) * a.t + tt] = ns;
 }
 
+// Many long rows (the prefill chunk): one workgroup per row selects from the
+// row held in registers (long_row_topk), the exact path if that overflows.
+__global__ __launch_bounds__(kFinalThreads) void k_topk_long(TopkArgs a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char final_smem[];
+    FinalSmem& sm = *reinterpret_cast<FinalSmem*>(final_smem);
+    const int row = blockIdx.x;
+    const int b = row / a.t;
+    const int tt = row - b * a.t;
+    int* out = a.idx + (static_cast<long long>(b) * a.t + tt) * a.k;
+    uint32_t k_eff = 0;
+    if (!long_row_topk(sm, score_row(a, row), a.n, a.k, out, k_eff)) {
+        __syncthreads();
+        k_eff = exact_row_topk(sm, score_row(a, row), a.n, a.k, out);
+    }
+    const int ns = static_cast<int>(k_eff);
+    for (int j = ns + threadIdx.x; j < a.k; j += blockDim.x) out[j] = -1;
+    if (a.count && threadIdx.x == 0) a.count[static_cast<long long>(b) * a.t + tt] = ns;
+}
+
 // Standalone candidate producer: each workgroup lists the top m of its chunk
 // of scores plus a bound of the rest (the same per-slot lists the score
 // kernel writes).
@@ -99,6 +118,26 @@ static bool final_lds_opted_in() {
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                         static_cast<int>(sizeof(FinalSmem))) == hipSuccess;
     return done[dev];
+}
+
+static bool long_lds_opted_in() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    static bool done[64] = {};
+    if (!done[dev])
+        done[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_topk_long),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        static_cast<int>(sizeof(FinalSmem))) == hipSuccess;
+    return done[dev];
+}
+
+hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t s) {
+    const int rows = a.batch * a.t;
+    if (rows == 0) return hipSuccess;
+    if (a.n > kLongPer * kFinalThreads) return launch_topk(a, nullptr, s);
+    if (!long_lds_opted_in()) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_topk_long, dim3(rows), dim3(kFinalThreads), sizeof(FinalSmem), s, a);
+    return hipGetLastError();
 }
 
 int topk_cand_m(int n, int k, int keys_per_slot) {

@@ -168,6 +168,90 @@ __device__ uint32_t exact_row_topk(FinalSmem& sm, const float* row, int n, int k
     return select_sorted<kUnionRegs>(sm.pool, np, static_cast<uint32_t>(k), pb, out, sm.stage, sm.ss, &sm.n_pool);
 }
 
+// Long rows (n <= kLongPer * blockDim.x): the k-th largest of the threads'
+// maxima bounds the k-th largest score from below (at least k entries, the
+// maxima themselves, are not smaller), so every entry in or above the
+// histogram bin of that maximum is a candidate and the top k are among them.
+// For independent scores that is about 1.5 k - 4 k entries out of n; a second
+// read of the row (from L2) compacts them into the pool for the sorted
+// select.  Returns false (nothing written) when the candidates overflow the
+// pool — heavily tied scores — and the caller takes the exact path.
+constexpr int kLongPer = 64;
+__device__ inline uint32_t long_key(const float* row, int i, int n) {
+    const float x = i < n ? row[i] : -INFINITY;
+    const uint32_t kk = score_key(x);
+    return key_valid(kk, x) ? kk : 0u;
+}
+__device__ bool long_row_topk(FinalSmem& sm, const float* row, int n, int k, int* out, uint32_t& k_eff) {
+    if (n > kLongPer * static_cast<int>(blockDim.x)) return false;
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t tmax = 0;
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {  // a batch of kLongPer / 2 loads in flight
+        uint32_t key[kLongPer / 2];
+#pragma unroll
+        for (int u = 0; u < kLongPer / 2; ++u) key[u] = long_key(row, (h * kLongPer / 2 + u) * blockDim.x + threadIdx.x, n);
+#pragma unroll
+        for (int u = 0; u < kLongPer / 2; ++u) tmax = key[u] > tmax ? key[u] : tmax;
+    }
+    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) sm.hist[i] = 0;
+    if (threadIdx.x == 0) { sm.n_sel = 0; sm.n_pool = 0; }
+    __syncthreads();
+    if (tmax) atomicAdd(&sm.hist[tmax >> (32 - kHistBits)], 1u);
+    __syncthreads();
+    int tb;
+    uint32_t above, at, total;
+    block_threshold(sm.hist, kHistBins, static_cast<uint32_t>(k), tb, above, at, total);
+    // fewer than k thread maxima: every valid entry is a candidate (invalid
+    // entries hold key 0, below every valid key)
+    const uint32_t edge = tb >= 0 ? static_cast<uint32_t>(tb) << (32 - kHistBits) : 0u;
+    const uint32_t lo = edge > kKeyNegInf ? edge : kKeyNegInf + 1;
+    // second read: each half's candidates go straight to the pool; every wave
+    // reserves its slots with one counter bump (a scan over its lanes)
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+        uint32_t key[kLongPer / 2];
+#pragma unroll
+        for (int u = 0; u < kLongPer / 2; ++u) key[u] = long_key(row, (h * kLongPer / 2 + u) * blockDim.x + threadIdx.x, n);
+        uint32_t c = 0;
+#pragma unroll
+        for (int u = 0; u < kLongPer / 2; ++u) c += key[u] >= lo ? 1u : 0u;
+        uint32_t pre = c, sum = c;
+#define CSA_SCAN_STEP(o)                              \
+        {                                             \
+            const uint32_t other = xor_lanes<o>(sum); \
+            if (lane & (o)) pre += other;             \
+            sum += other;                             \
+        }
+        CSA_SCAN_STEP(1) CSA_SCAN_STEP(2) CSA_SCAN_STEP(4) CSA_SCAN_STEP(8) CSA_SCAN_STEP(16) CSA_SCAN_STEP(32)
+#undef CSA_SCAN_STEP
+        uint32_t base = 0;
+        if (lane == 0 && sum) base = atomicAdd(&sm.n_sel, sum);
+        base = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(base)));
+        uint32_t off = base + pre - c;
+        if (base + sum <= static_cast<uint32_t>(kUnionCap)) {  // else overflow: the total shows it
+#pragma unroll
+            for (int u = 0; u < kLongPer / 2; ++u)
+                if (key[u] >= lo)
+                    sm.pool[off++] = composite(key[u], static_cast<uint32_t>((h * kLongPer / 2 + u) * blockDim.x +
+                                                                             threadIdx.x));
+        }
+    }
+    __syncthreads();
+    const uint32_t np = sm.n_sel;
+    if (np > static_cast<uint32_t>(kUnionCap)) return false;
+    // they share the top bits where their largest and smallest agree
+    u64 hi = 0, lo_c = 0;
+    for (uint32_t i = threadIdx.x; i < np; i += blockDim.x) {
+        hi = umax64(hi, sm.pool[i]);
+        lo_c = umax64(lo_c, ~sm.pool[i]);
+    }
+    block_max2(sm, hi, lo_c);
+    const int pb = np <= 1 ? 0 : __clzll(static_cast<long long>(hi ^ ~lo_c));
+    k_eff = select_sorted<kUnionRegs>(sm.pool, np, static_cast<uint32_t>(k), pb, out, sm.stage, sm.ss, &sm.n_pool);
+    return true;
+}
+
 // Fast path: top-k of the union of per-slot candidates, as sorted indices
 // into out.  Returns false if the union cannot prove the answer.
 __device__ bool union_topk(FinalSmem& sm, const CandArgs& c, int row, int k, int* out, uint32_t& k_eff) {

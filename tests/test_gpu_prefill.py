@@ -149,6 +149,21 @@ def test_index_topk(csa, case):
         assert_topk_gap_rule(idx[r].cpu().numpy(), int(cnt[r]), ref[i], k)
 
 
+def test_index_topk_tied_scores_take_exact_path(csa):
+    """Zero queries: every visible block scores 0, so the candidates of the
+    row selector overflow and it falls back to the exact path; the answer is
+    the lowest visible indices."""
+    t, n, k = 20, 30000, 512
+    q = torch.zeros(t, 64, 128, dtype=torch.bfloat16, device=DEV)
+    w = dev_f32(_g(6).standard_normal((t, 64), dtype=np.float32))
+    K = dev_bf16(_bf16(_g(7), (n, 128)))
+    pos0 = 4 * 20000
+    idx, cnt = _run_index_topk(csa, q, w, K, k, pos0)
+    torch.cuda.synchronize()
+    assert (cnt.cpu().numpy() == k).all()
+    np.testing.assert_array_equal(idx.cpu().numpy(), np.tile(np.arange(k, dtype=np.int32), (t, 1)))
+
+
 def test_index_topk_empty_history(csa):
     g = _g(5)
     q = dev_bf16(_bf16(g, (16, 64, 128)))
