@@ -231,27 +231,49 @@ __global__ __launch_bounds__(kMqWaves * kWave, 1) void k_index_score_mq(MqArgs a
 
 constexpr int kPaThreads = 256;          // four waves: one 16-head tile each (h <= 64)
 constexpr int kPaWaves = kPaThreads / kWave;
-constexpr int kPaRows = 32;              // rows per chunk
-constexpr int kVtPitch = kPaRows + 4;    // transposed rows: 72 B per column (bank spread)
+// The softmax reference max moves only when a chunk's max exceeds it by more
+// than this (natural-log units): exp(s - ref) then stays below e^8, far from
+// float or bfloat16 overflow, and the output is rescaled rarely (never, for
+// logits of unit scale) instead of at every chunk.
+constexpr float kLazyRescale = 8.f;
+
+// Slot swizzle of the transposed rows: columns 16 B apart (cc, cc + 1) share
+// a bank offset once the column pitch is taken mod 256 B, so their row
+// groups are xor-ed with cc / 2 (the 16 columns of one PV read share it).
+// Two floats to packed bfloat16 (round to nearest even, the low half from a):
+// one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    const __bf16 ha = static_cast<__bf16>(a);
+    const __bf16 hb = static_cast<__bf16>(b);
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, ha)) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hb)) << 16);
+}
+
+template <int kSlots>
+__device__ __forceinline__ int pa_swz(int cc) { return (cc >> 1) & (kSlots - 1); }
 
 template <int D>
 struct PaCfg {
-    static constexpr int kKrPitch = D + 8;                 // row-major rows (bank spread)
-    static constexpr int kKs = D / 32;                     // k-steps of S^T
-    static constexpr int kMd = D / 16;                     // 16-column tiles of O^T
-    static constexpr int kItems = (kPaRows / 4) * (D / 8); // (4-row group, 16-byte column) items per chunk
+    static constexpr int kRows = D >= 512 ? 64 : 32;       // rows per chunk
+    static constexpr int kMt = kRows / 16;                  // 16-row tiles of S^T
+    static constexpr int kKrPitch = D + 8;                  // row-major rows: 16-lane reads hit distinct banks
+    static constexpr int kVtPitch = kRows + 8;              // transposed rows: 144 B (R = 64) per column
+    static constexpr int kKs = D / 32;                      // k-steps of S^T
+    static constexpr int kMd = D / 16;                      // 16-column tiles of O^T
+    static constexpr int kItems = (kRows / 4) * (D / 8);    // (4-row group, 16-byte column) items per chunk
     static constexpr int kIpt = (kItems + kPaThreads - 1) / kPaThreads;
-    static constexpr size_t kLdsRows = sizeof(uint16_t) * (static_cast<size_t>(kPaRows) * kKrPitch +
+    static constexpr size_t kLdsRows = sizeof(uint16_t) * (static_cast<size_t>(kRows) * kKrPitch +
                                                           static_cast<size_t>(D) * kVtPitch);
 };
 
 template <int D>
 __global__ __launch_bounds__(kPaThreads, D >= 512 ? 1 : 2) void k_prefill_attn(PrefillAttnArgs a) {
     using C = PaCfg<D>;
+    constexpr int R = C::kRows;
     extern __shared__ __attribute__((aligned(16))) uint16_t pa_lds[];
-    uint16_t* kr = pa_lds;                                      // [32][D + 8]
-    uint16_t* vt = kr + kPaRows * C::kKrPitch;                  // [D][36]
-    int* sidx = reinterpret_cast<int*>(vt + D * kVtPitch);      // [k]
+    uint16_t* kr = pa_lds;                                      // [R][D + 8]
+    uint16_t* vt = kr + R * C::kKrPitch;                        // [D][R + 8]
+    int* sidx = reinterpret_cast<int*>(vt + D * C::kVtPitch);   // [k]
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const int li = lane & 15;
@@ -280,21 +302,28 @@ __global__ __launch_bounds__(kPaThreads, D >= 512 ? 1 : 2) void k_prefill_attn(P
     }
     __syncthreads();
 
+    // Items (4-row group rg, 16-byte column cc), column fastest: a wave loads
+    // whole 1 KB rows (coalesced) and writes them row-major without bank
+    // conflicts.  The transposed copy puts rows 4*rg .. 4*rg + 3 of column d
+    // at slot rg ^ swz(d): the columns a wave writes at once land in distinct
+    // banks, and the PV reads (16 columns, one slot) stay conflict-free too.
+    // Rows past the valid ones repeat the token's last row: their
+    // probabilities are exactly 0 and their values finite, so they add
+    // nothing, and every load is unconditional.
+    const uint16_t* last_row = win + static_cast<long long>(wl - 1) * D;
     uint4 v[C::kIpt][4];
     auto load_chunk = [&](int j0) {
 #pragma unroll
         for (int u = 0; u < C::kIpt; ++u) {
             const int it = threadIdx.x + u * kPaThreads;
-            const int rg = it % (kPaRows / 4);
-            const int cc = it / (kPaRows / 4);
+            const int cc = it % (D / 8);
+            const int rg = min(it / (D / 8), R / 4 - 1);  // items past the end repeat the last (not stored)
 #pragma unroll
             for (int u2 = 0; u2 < 4; ++u2) {
                 const int j = j0 + 4 * rg + u2;
-                const uint16_t* src = nullptr;
-                if (it < C::kItems && j < nv)
-                    src = j < cnt ? a.comp_kv + static_cast<long long>(sidx[j]) * D
-                                  : win + static_cast<long long>(j - cnt) * D;
-                v[u][u2] = src ? *reinterpret_cast<const uint4*>(src + 8 * cc) : make_uint4(0, 0, 0, 0);
+                const uint16_t* src = j < cnt ? a.comp_kv + static_cast<long long>(sidx[j]) * D
+                                              : (j < nv ? win + static_cast<long long>(j - cnt) * D : last_row);
+                v[u][u2] = *reinterpret_cast<const uint4*>(src + 8 * cc);
             }
         }
     };
@@ -302,24 +331,28 @@ __global__ __launch_bounds__(kPaThreads, D >= 512 ? 1 : 2) void k_prefill_attn(P
 #pragma unroll
         for (int u = 0; u < C::kIpt; ++u) {
             const int it = threadIdx.x + u * kPaThreads;
-            if (it >= C::kItems) continue;
-            const int rg = it % (kPaRows / 4);
-            const int cc = it / (kPaRows / 4);
+            if (C::kItems % kPaThreads != 0 && it >= C::kItems) continue;
+            const int cc = it % (D / 8);
+            const int rg = it / (D / 8);
 #pragma unroll
             for (int u2 = 0; u2 < 4; ++u2)
                 *reinterpret_cast<uint4*>(kr + (4 * rg + u2) * C::kKrPitch + 8 * cc) = v[u][u2];
-            // transpose: column 8*cc + e gets rows 4*rg .. 4*rg + 3 (one 8-byte write)
+            // column 8*cc + e gets rows 4*rg .. 4*rg + 3 (one 8-byte write),
+            // element pairs gathered by byte permutes
             const uint32_t w0[4] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w};
             const uint32_t w1[4] = {v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
             const uint32_t w2[4] = {v[u][2].x, v[u][2].y, v[u][2].z, v[u][2].w};
             const uint32_t w3[4] = {v[u][3].x, v[u][3].y, v[u][3].z, v[u][3].w};
+            const int slot = rg ^ pa_swz<R / 4>(cc);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int sh = 16 * (e & 1);
-                const uint32_t r0 = (w0[e >> 1] >> sh) & 0xffffu, r1 = (w1[e >> 1] >> sh) & 0xffffu;
-                const uint32_t r2 = (w2[e >> 1] >> sh) & 0xffffu, r3 = (w3[e >> 1] >> sh) & 0xffffu;
-                *reinterpret_cast<uint2*>(vt + (8 * cc + e) * kVtPitch + 4 * rg) =
-                    make_uint2(r0 | (r1 << 16), r2 | (r3 << 16));
+            for (int q = 0; q < 4; ++q) {
+                // low halves (column 8cc + 2q), then high halves (8cc + 2q + 1)
+                const uint32_t lo01 = __builtin_amdgcn_perm(w1[q], w0[q], 0x05040100u);
+                const uint32_t lo23 = __builtin_amdgcn_perm(w3[q], w2[q], 0x05040100u);
+                const uint32_t hi01 = __builtin_amdgcn_perm(w1[q], w0[q], 0x07060302u);
+                const uint32_t hi23 = __builtin_amdgcn_perm(w3[q], w2[q], 0x07060302u);
+                *reinterpret_cast<uint2*>(vt + (8 * cc + 2 * q) * C::kVtPitch + 4 * slot) = make_uint2(lo01, lo23);
+                *reinterpret_cast<uint2*>(vt + (8 * cc + 2 * q + 1) * C::kVtPitch + 4 * slot) = make_uint2(hi01, hi23);
             }
         }
     };
@@ -327,27 +360,29 @@ __global__ __launch_bounds__(kPaThreads, D >= 512 ? 1 : 2) void k_prefill_attn(P
     f32x4 o[C::kMd];
 #pragma unroll
     for (int md = 0; md < C::kMd; ++md) o[md] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
-    const int n_chunks = (nv + kPaRows - 1) / kPaRows;
+    float m_ref = -INFINITY, l_run = 0.f;
+    const int n_chunks = (nv + R - 1) / R;
     load_chunk(0);
     for (int c = 0; c < n_chunks; ++c) {
         store_chunk();
         __syncthreads();
-        if (c + 1 < n_chunks) load_chunk(kPaRows * (c + 1));
+        if (c + 1 < n_chunks) load_chunk(R * (c + 1));
         if (active) {
             // S^T = K Q^T: lane holds rows 16*mt + 4*lg + r, head li
-            f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            f32x4 st[C::kMt];
+#pragma unroll
+            for (int mt = 0; mt < C::kMt; ++mt) st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < C::kKs; ++ks)
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
+                for (int mt = 0; mt < C::kMt; ++mt) {
                     const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kr + (16 * mt + li) * C::kKrPitch + 32 * ks + 8 * lg);
                     st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[ks], st[mt], 0, 0, 0);
                 }
-            const int j0 = kPaRows * c;
-            float sv[8];
+            const int j0 = R * c;
+            float sv[4 * C::kMt];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < C::kMt; ++mt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int j = j0 + 16 * mt + 4 * lg + r;
@@ -355,38 +390,47 @@ __global__ __launch_bounds__(kPaThreads, D >= 512 ? 1 : 2) void k_prefill_attn(P
                 }
             float cm = sv[0];
 #pragma unroll
-            for (int e = 1; e < 8; ++e) cm = fmaxf(cm, sv[e]);
+            for (int e = 1; e < 4 * C::kMt; ++e) cm = fmaxf(cm, sv[e]);
             cm = fmaxf(cm, xor_lanes_f32<16>(cm));
             cm = fmaxf(cm, xor_lanes_f32<32>(cm));
-            const float m_new = fmaxf(m_run, cm);  // every chunk holds a valid row: finite
-            const float alpha = expf(m_run - m_new);
-            uint16_t pb[8];
+            // every chunk holds a valid row: cm is finite
+            if (__builtin_amdgcn_ballot_w64(cm > m_ref + kLazyRescale)) {  // rare: move the reference
+                const float m_new = fmaxf(m_ref, cm);
+                const float alpha = expf(m_ref - m_new);  // 0 on the first chunk
+                l_run *= alpha;
+#pragma unroll
+                for (int md = 0; md < C::kMd; ++md) o[md] *= alpha;
+                m_ref = m_new;
+            }
+            uint32_t pb[2 * C::kMt];  // probabilities, bf16 pairs
             float ls = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pb[e] = f32_to_bf16(expf(sv[e] - m_new));
-                ls += bf16_to_f32(pb[e]);
+            for (int e = 0; e < 2 * C::kMt; ++e) {
+                pb[e] = bf16x2_rne(expf(sv[2 * e] - m_ref), expf(sv[2 * e + 1] - m_ref));
+                ls += __uint_as_float(pb[e] << 16) + __uint_as_float(pb[e] & 0xffff0000u);
             }
             ls += xor_lanes_f32<16>(ls);
             ls += xor_lanes_f32<32>(ls);
-            l_run = l_run * alpha + ls;
-            m_run = m_new;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+            l_run += ls;
+            // O^T += V^T P^T, one MFMA per 32 rows: k-slots 0..3 <-> rows
+            // 32*ks + 4*lg + e, 4..7 <-> rows 32*ks + 16 + 4*lg + e - 4 (the
+            // lane's own S^T values of tiles 2*ks and 2*ks + 1)
 #pragma unroll
-                for (int md = 0; md < C::kMd; ++md) o[md] *= alpha;
-            }
-            bf16x8 pv;
-            __builtin_memcpy(&pv, pb, sizeof(pv));
-            // O^T += V^T P^T: k-slots 0..3 <-> rows 4*lg + e, 4..7 <-> rows 16 + 4*lg + e - 4
+            for (int ks = 0; ks < R / 32; ++ks) {
+                bf16x8 pv;
+                __builtin_memcpy(&pv, pb + 4 * ks, sizeof(pv));
 #pragma unroll
-            for (int md = 0; md < C::kMd; ++md) {
-                const uint16_t* vr = vt + (16 * md + li) * kVtPitch + 4 * lg;
-                const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-                const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-                const uint32_t wv4[4] = {lo.x, lo.y, hi.x, hi.y};
-                bf16x8 va;
-                __builtin_memcpy(&va, wv4, sizeof(va));
-                o[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pv, o[md], 0, 0, 0);
+                for (int md = 0; md < C::kMd; ++md) {
+                    // column d = 16*md + li; row groups 8*ks + lg and 8*ks + 4 + lg
+                    const int sw = pa_swz<R / 4>(2 * md);
+                    const uint16_t* vr = vt + (16 * md + li) * C::kVtPitch;
+                    const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * ((8 * ks + lg) ^ sw));
+                    const uint2 hi = *reinterpret_cast<const uint2*>(vr + 4 * ((8 * ks + 4 + lg) ^ sw));
+                    const uint32_t wv4[4] = {lo.x, lo.y, hi.x, hi.y};
+                    bf16x8 va;
+                    __builtin_memcpy(&va, wv4, sizeof(va));
+                    o[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pv, o[md], 0, 0, 0);
+                }
             }
         }
         __syncthreads();
@@ -395,22 +439,24 @@ __global__ __launch_bounds__(kPaThreads, D >= 512 ? 1 : 2) void k_prefill_attn(P
     // the sink joins the denominator once, at the end
     const int hh = 16 * wv + li;
     const float sk = a.sink ? a.sink[hh] : -INFINITY;
-    const float M = fmaxf(m_run, sk);
-    const float em = expf(m_run - M);
+    const float M = fmaxf(m_ref, sk);
+    const float em = expf(m_ref - M);
     const float es = sk == -INFINITY ? 0.f : expf(sk - M);
     const float den = l_run * em + es;
     const float f = em / den;
     const long long ob = (static_cast<long long>(tq) * a.h + hh) * D + 4 * lg;
+    if (a.out_bf16) {
 #pragma unroll
-    for (int md = 0; md < C::kMd; ++md) {
-        if (a.out_bf16) {
-            const uint32_t x0 = f32_to_bf16(o[md][0] * f) | (static_cast<uint32_t>(f32_to_bf16(o[md][1] * f)) << 16);
-            const uint32_t x1 = f32_to_bf16(o[md][2] * f) | (static_cast<uint32_t>(f32_to_bf16(o[md][3] * f)) << 16);
+        for (int md = 0; md < C::kMd; ++md) {
+            const uint32_t x0 = bf16x2_rne(o[md][0] * f, o[md][1] * f);
+            const uint32_t x1 = bf16x2_rne(o[md][2] * f, o[md][3] * f);
             *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + ob + 16 * md) = make_uint2(x0, x1);
-        } else {
+        }
+    } else {
+#pragma unroll
+        for (int md = 0; md < C::kMd; ++md)
             *reinterpret_cast<float4*>(static_cast<float*>(a.out) + ob + 16 * md) =
                 make_float4(o[md][0] * f, o[md][1] * f, o[md][2] * f, o[md][3] * f);
-        }
     }
     if (a.lse && lg == 0) a.lse[static_cast<long long>(tq) * a.h + hh] = M + logf(den);
 }
