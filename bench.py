@@ -27,6 +27,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 
 
 def algorithmic_bytes(shape) -> dict:
@@ -175,6 +176,96 @@ def time_fp8_scan(csa, layers, shape, reps: int):
     return e0.elapsed_time(e1) / (reps * len(layers)), alg
 
 
+def time_prefill(csa, reps: int):
+    """The prefill-shaped chunk (2048 queries at positions 260096..262143
+    against 65536 compressed blocks, causal): csa_index_topk (multi-query
+    MFMA score in chunks of 256 queries + per-query top-512) and
+    csa_prefill_attn (64 heads x 512, 512 selected rows + the 128-token
+    window per query), each timed with HIP events over `reps` calls; plus the
+    score kernel alone on the chunk shape (8 launches of 256 queries captured
+    in a graph) for its matrix-core rate."""
+    import numpy as np
+    import torch
+    import synth
+
+    shape = synth.SHAPES["prefill"]
+    x = synth.make_prefill_inputs_torch(shape, None, "cuda")
+    T, N, k, W = shape.t, shape.n_comp, shape.top_k, shape.w
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(T, dtype=torch.int32, device="cuda")
+    ws = torch.empty(csa.csa_index_topk_workspace_size(T, N, k), dtype=torch.uint8, device="cuda")
+    out = torch.empty(T, shape.h, shape.d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(T, shape.h, device="cuda")
+    scale = 1.0 / np.sqrt(shape.d)
+
+    def topk():
+        csa.csa_index_topk(x["q_idx"], x["w_idx"], x["idx_keys"], idx, cnt, ws, pos0=x["pos0"])
+
+    def attn():
+        csa.csa_prefill_attn(x["q"], x["comp_kv"], idx, cnt, x["win_kv"], W, x["pos0"], x["sink"], scale, out,
+                             lse=lse)
+
+    def timed(f, n):
+        f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    topk_ms = timed(topk, reps)
+    attn_ms = timed(attn, reps)
+    # the score kernel alone: the chunks' launches back to back in a graph
+    rows = 256
+    sc = torch.empty(1, rows, N, device="cuda")
+    pos = torch.arange(x["pos0"], x["pos0"] + T, dtype=torch.int32, device="cuda")[None]
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for r0 in range(0, T, rows):
+                csa.csa_index_score(x["q_idx"][None, r0:r0 + rows], x["w_idx"][None, r0:r0 + rows],
+                                    x["idx_keys"][None], sc, q_pos=pos[:, r0:r0 + rows], stream=stream)
+        g.replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    stream.synchronize()
+    launches = reps * (T // rows)
+    score_us = e0.elapsed_time(e1) * 1e3 / launches
+    flop = 2.0 * rows * 64 * 128 * N
+    tflops = flop / (score_us * 1e-6) / 1e12
+    attn_flop = 4.0 * T * shape.h * (k + W) * shape.d
+    return {
+        "workload": "prefill chunk: 2048 queries at positions 260096..262143 against 65536 compressed "
+                    "blocks (causal), indexer 64x128 bf16, top_k 512, main attention 64 heads x 512 bf16 "
+                    "over 512 selected rows + the 128-token window per query",
+        "index_topk_ms": round(topk_ms, 4),
+        "attn_ms": round(attn_ms, 4),
+        "chunk_ms": round(topk_ms + attn_ms, 4),
+        "queries_per_s": round(T / ((topk_ms + attn_ms) * 1e-3), 1),
+        "score_kernel": {
+            "kernel": "k_index_score_mq",
+            "bound": "mfma",
+            "rows_per_launch": rows,
+            "avg_launch_us": round(score_us, 2),
+            "achieved": round(tflops, 1),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+        },
+        "attn_tflops": round(attn_flop / (attn_ms * 1e-3) / 1e12, 1),
+    }
+
+
 def cpu_baseline(layers, shape, budget_s: float):
     """The float64 oracle on the host, layer by layer, until the budget is spent."""
     import numpy as np
@@ -304,6 +395,9 @@ def main() -> int:
     cpu = None
     if args.cpu_budget > 0:
         cpu = cpu_baseline(layers, shape, args.cpu_budget)
+    del layers  # the 1M-context caches make room for the prefill workload
+    torch.cuda.empty_cache()
+    prefill = time_prefill(csa, max(2, args.scan_reps // 2))
 
     res = {
         "metric": "CSA decode steps/s and indexer-scan HBM GB/s at 1M ctx (250K comp entries)",
@@ -349,6 +443,7 @@ def main() -> int:
             "achieved_gbps": round(fp8_gbs, 1),
             "frac": round(fp8_gbs / HBM_PEAK_GBS, 4),
         },
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
