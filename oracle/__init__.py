@@ -16,6 +16,7 @@ from .csa import (
     compress,
     decode_step,
     gather,
+    hca_decode_step,
     index_score,
     index_score_fp8,
     kv_norm,
@@ -36,5 +37,6 @@ __all__ = [
     "SwaRing",
     "LayerState",
     "decode_step",
+    "hca_decode_step",
     "prefill_chunk",
 ]

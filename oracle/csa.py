@@ -37,6 +37,7 @@ __all__ = [
     "SwaRing",
     "LayerState",
     "decode_step",
+    "hca_decode_step",
     "prefill_chunk",
 ]
 
@@ -417,6 +418,45 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
         "out": out,
         "lse": lse,
     }
+
+
+# ---------------------------------------------------------------------------
+# (6b) one decode step of a heavily compressed (HCA) layer
+# ---------------------------------------------------------------------------
+
+def hca_decode_step(L: LayerState, *, q, kv_new, pos: int, z_main=None, c_main=None,
+                    scale: Optional[float] = None):
+    """One token through one HCA layer: the CSA step without the indexer.
+
+    Page 1, ``PERFORMANCE_AUDIT.md`` (the ``forward_attention`` branches):
+    layers with a compression ratio above 4 attend to ALL compressed entries
+    followed by the SWA window (``torch.cat([kv_cache.comp_kv, swa_kv])``);
+    page 2, ``single_shot_inference.py``, ``eager_attention`` (the same branch
+    in the mixed-precision gather, ``gather_mixed_all``).  The compressor is the
+    plain, non-overlapped ratio-``m`` reduce (page 1,
+    ``hca_compress_reduce_kernel``), run when the token completes a block.
+    ``L.idx_keys`` is not used.  Mutates ``L``; returns the new entry, the
+    attended rows and ``out``/``lse``.
+    """
+    m = L.m
+    L.swa.append(np.asarray(kv_new, dtype=np.float64))
+    rnd = L.round_cache if L.round_cache is not None else (lambda a: a)
+    new_entry = None
+    if pos % m == m - 1:
+        ym = compress(z_main, c_main, L.main_bias, m, overlap=False)[-1]
+        if L.main_norm is not None:
+            ym = kv_norm(ym, L.main_norm)
+        L.comp_kv[L.n_comp] = rnd(ym)
+        new_entry = ym
+        L.n_comp += 1
+    N = L.n_comp
+    W = L.swa.rows.shape[0]
+    win = [L.swa.rows[(L.swa.head - L.swa.length + j) % W] for j in range(L.swa.length)]
+    D = L.comp_kv.shape[1]
+    rows = np.concatenate([np.asarray(L.comp_kv[:N], dtype=np.float64),
+                           np.stack(win) if win else np.zeros((0, D))], axis=0)
+    out, lse = sparse_attn(q, rows, L.sink, scale)
+    return {"new_entry": new_entry, "rows": rows, "n_valid": rows.shape[0], "out": out, "lse": lse}
 
 
 # ---------------------------------------------------------------------------

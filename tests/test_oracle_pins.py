@@ -585,6 +585,45 @@ def test_decode_step_cache_rounding_applies():
 
 
 # ---------------------------------------------------------------------------
+# (6b) HCA step: the dense special case of the CSA step
+# ---------------------------------------------------------------------------
+
+def test_hca_step_equals_csa_step_with_top_k_covering_all():
+    """An HCA step attends to every compressed entry and the window; a CSA
+    step whose top-k covers every entry selects the same rows in another
+    order, and attention does not depend on the order — so both give the same
+    output for any indexer keys (ratio 8, four block completions, ring wrap)."""
+    g = _g(24)
+    m, W, D, H = 8, 6, 16, 4
+    Lh = _empty_state(g, D=D, W=W, H=H, m=m)
+    Lc = _empty_state(g, D=D, W=W, H=H, m=m)
+    Lc.main_bias, Lc.sink = Lh.main_bias, Lh.sink
+    for pos in range(37):
+        inp = _step_inputs(g, D=D, H=H, m=m)
+        rh = oracle.hca_decode_step(Lh, q=inp["q"], kv_new=inp["kv_new"], pos=pos,
+                                    z_main=inp["z_main"], c_main=inp["c_main"])
+        rc = oracle.decode_step(Lc, pos=pos, top_k=64, **inp)
+        assert Lh.n_comp == Lc.n_comp == (pos + 1) // m
+        assert rh["n_valid"] == rc["n_valid"] == Lh.n_comp + min(pos + 1, W)
+        np.testing.assert_allclose(rh["out"], rc["out"], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(rh["lse"], rc["lse"], rtol=1e-13)
+
+
+def test_hca_step_rows_are_cache_then_window():
+    g = _g(25)
+    L = _empty_state(g, W=4, m=2)
+    L.sink = None
+    for pos in range(7):
+        inp = _step_inputs(g, m=2)
+        r = oracle.hca_decode_step(L, q=inp["q"], kv_new=inp["kv_new"], pos=pos, z_main=inp["z_main"],
+                                   c_main=inp["c_main"])
+    # three entries (positions 1, 3, 5 complete blocks 0..2; position 6 does not), then window 3..6
+    assert L.n_comp == 3 and r["n_valid"] == 3 + 4
+    np.testing.assert_array_equal(r["rows"][:3], L.comp_kv[:3])
+    np.testing.assert_array_equal(r["rows"][3], L.swa.rows[(L.swa.head - 4) % 4])
+
+
+# ---------------------------------------------------------------------------
 # (7) prefill chunk: the same as one decode step per token
 # ---------------------------------------------------------------------------
 
