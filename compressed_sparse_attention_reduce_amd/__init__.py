@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     csa_decode_step,
     csa_decode_step_workspace_size,
     csa_gather,
+    csa_hca_decode_step,
+    csa_hca_decode_step_workspace_size,
     csa_index_score,
     csa_index_score_fp8,
     csa_index_topk,

@@ -89,6 +89,8 @@ _SIGS = {
     "csa_decode_step_workspace_size": (_sz, [ctypes.POINTER(LayerDesc)]),
     "csa_decode_step": (_i, [ctypes.POINTER(LayerDesc), ctypes.POINTER(StepIO), _vp, _sz, _vp]),
     "csa_layer_advance": (_i, [ctypes.POINTER(LayerDesc), _i]),
+    "csa_hca_decode_step_workspace_size": (_sz, [ctypes.POINTER(LayerDesc)]),
+    "csa_hca_decode_step": (_i, [ctypes.POINTER(LayerDesc), ctypes.POINTER(StepIO), _vp, _sz, _vp]),
     "csa_index_topk_workspace_size": (_sz, [_i, _i, _i]),
     "csa_index_topk": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _ll, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "csa_prefill_attn": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _ll, _vp, _f, _vp, _i, _vp, _i, _i, _i,
@@ -257,6 +259,15 @@ def csa_decode_step(layer: LayerDesc, io: StepIO, ws, stream=None) -> None:
                                  ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def csa_hca_decode_step_workspace_size(layer: LayerDesc) -> int:
+    return lib().csa_hca_decode_step_workspace_size(ctypes.byref(layer))
+
+
+def csa_hca_decode_step(layer: LayerDesc, io: StepIO, ws, stream=None) -> None:
+    _check(lib().csa_hca_decode_step(ctypes.byref(layer), ctypes.byref(io), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def csa_layer_advance(layer: LayerDesc, pos: int) -> None:
     _check(lib().csa_layer_advance(ctypes.byref(layer), pos))
 
@@ -266,19 +277,20 @@ def make_layer_desc(*, comp_kv, idx_keys, swa, main_bias, idx_bias, sink, n_comp
                     overlap: int = 0, out_dtype=None, scale: Optional[float] = None,
                     main_norm=None, idx_norm=None) -> LayerDesc:
     """Fill a LayerDesc from cache tensors: comp_kv [B, max_comp, d], idx_keys
-    [B, max_comp, d_i], swa [B, W, d].  The returned struct keeps references to
-    every tensor it points at."""
+    [B, max_comp, d_i] (None for an HCA layer, with idx_bias None, h_i and
+    top_k 0), swa [B, W, d].  The returned struct keeps references to every
+    tensor it points at."""
     B, max_comp, d = comp_kv.shape
     L = LayerDesc()
-    L.batch, L.h, L.d, L.h_i, L.d_i = B, h, d, h_i, idx_keys.shape[2]
+    L.batch, L.h, L.d, L.h_i, L.d_i = B, h, d, h_i, (idx_keys.shape[2] if idx_keys is not None else 0)
     L.m, L.w, L.top_k, L.overlap = m, swa.shape[1], top_k, overlap
     L.dtype = _dt(comp_kv)
     L.out_dtype = _dt(comp_kv) if out_dtype is None else (CSA_BF16 if out_dtype == torch.bfloat16 else CSA_F32)
     L.comp_kv, L.comp_kv_stride_b = comp_kv.data_ptr(), comp_kv.stride(0)
-    L.idx_keys, L.idx_keys_stride_b = idx_keys.data_ptr(), idx_keys.stride(0)
+    L.idx_keys, L.idx_keys_stride_b = _ptr(idx_keys), (idx_keys.stride(0) if idx_keys is not None else 0)
     L.swa, L.swa_stride_b = swa.data_ptr(), swa.stride(0)
     L.max_comp = max_comp
-    L.main_bias, L.idx_bias = main_bias.data_ptr(), idx_bias.data_ptr()
+    L.main_bias, L.idx_bias = main_bias.data_ptr(), _ptr(idx_bias)
     L.main_norm, L.idx_norm = _ptr(main_norm), _ptr(idx_norm)
     L.sink = _ptr(sink)
     L.scale = (1.0 / d ** 0.5) if scale is None else scale
@@ -288,22 +300,27 @@ def make_layer_desc(*, comp_kv, idx_keys, swa, main_bias, idx_bias, sink, n_comp
     return L
 
 
-def make_step_io(*, pos: int, q, q_idx, w_idx, kv_new, z_main, c_main, z_idx, c_idx, scores,
-                 topk_idx, topk_count, gather_buf, n_valid, out, lse=None) -> StepIO:
+def make_step_io(*, pos: int, q, q_idx=None, w_idx=None, kv_new, z_main, c_main, z_idx=None, c_idx=None,
+                 scores=None, topk_idx=None, topk_count=None, gather_buf=None, n_valid=None, out,
+                 lse=None) -> StepIO:
     """q [B, h, d]; q_idx [B, h_i, d_i]; w_idx [B, h_i]; kv_new [B, d]; z/c [B, rows, width];
-    scores [B, >=N]; topk_idx [B, k]; topk_count [B]; gather_buf [B, k+W, d]; out [B, h, d]."""
+    scores [B, >=N]; topk_idx [B, k]; topk_count [B]; gather_buf [B, k+W, d]; out [B, h, d].
+    The indexer fields may be None for an HCA step."""
+    def st(t):
+        return t.stride(0) if t is not None else 0
+
     io = StepIO()
     io.pos = pos
     io.q, io.q_stride_b = q.data_ptr(), q.stride(0)
-    io.q_idx, io.q_idx_stride_b = q_idx.data_ptr(), q_idx.stride(0)
-    io.w_idx, io.w_stride_b = w_idx.data_ptr(), w_idx.stride(0)
+    io.q_idx, io.q_idx_stride_b = _ptr(q_idx), st(q_idx)
+    io.w_idx, io.w_stride_b = _ptr(w_idx), st(w_idx)
     io.kv_new, io.kv_new_stride_b = kv_new.data_ptr(), kv_new.stride(0)
     io.z_main, io.c_main, io.zc_main_stride_b = z_main.data_ptr(), c_main.data_ptr(), z_main.stride(0)
-    io.z_idx, io.c_idx, io.zc_idx_stride_b = z_idx.data_ptr(), c_idx.data_ptr(), z_idx.stride(0)
-    io.scores, io.scores_stride_b = scores.data_ptr(), scores.stride(0)
-    io.topk_idx, io.topk_count = topk_idx.data_ptr(), topk_count.data_ptr()
-    io.gather_buf, io.gather_stride_b = gather_buf.data_ptr(), gather_buf.stride(0)
-    io.n_valid = n_valid.data_ptr()
+    io.z_idx, io.c_idx, io.zc_idx_stride_b = _ptr(z_idx), _ptr(c_idx), st(z_idx)
+    io.scores, io.scores_stride_b = _ptr(scores), st(scores)
+    io.topk_idx, io.topk_count = _ptr(topk_idx), _ptr(topk_count)
+    io.gather_buf, io.gather_stride_b = _ptr(gather_buf), st(gather_buf)
+    io.n_valid = _ptr(n_valid)
     io.out, io.out_stride_b = out.data_ptr(), out.stride(0)
     io.lse = _ptr(lse)
     # the struct holds raw device pointers: keep the tensors alive with it

@@ -54,7 +54,8 @@ __device__ inline void attn_load_q(const AttnArgs& a, int hg, int b, uint4 (&qv)
 
 // One split of the partial attention: rows [kR * split, kR * split + kR) of
 // the gathered set (gather mode: top-k rows of the compressed cache, then the
-// SWA window) or of kv (plain mode), for the 16 heads of group hg.  Partial
+// SWA window; dense mode: every compressed row in order, then the window) or
+// of kv (plain mode), for the 16 heads of group hg.  Partial
 // (m, l, O) go to the workspace.  rows_idx: this sequence's top-k indices
 // (global or LDS); cnt_in: their count if known, else < 0 (read from
 // a.count).  smem: attn_split_lds_bytes(d) of LDS.  Every thread calls it.
@@ -83,13 +84,17 @@ __device__ inline void attn_split(const AttnArgs& a, int n_splits, int split, in
     for (int u = 0; u < G::kChunks; ++u) {
         const int c = u * NT + threadIdx.x;
         const int j = r0 + c / cpr;
-        my_idx[u] = (a.idx && c < n_chunks && j < a.k) ? rows_idx[j] : 0;
+        my_idx[u] = a.dense ? j : ((a.idx && c < n_chunks && j < a.k) ? rows_idx[j] : 0);
     }
     int cnt = 0, nv;
-    if (a.idx) {
-        cnt = cnt_in >= 0 ? cnt_in : (a.count ? a.count[b] : a.k);
-        cnt = cnt < 0 ? 0 : (cnt > a.k ? a.k : cnt);
-        if (a.n_comp <= 0) cnt = 0;
+    if (a.idx || a.dense) {
+        if (a.dense) {
+            cnt = a.n_comp > 0 ? a.n_comp : 0;
+        } else {
+            cnt = cnt_in >= 0 ? cnt_in : (a.count ? a.count[b] : a.k);
+            cnt = cnt < 0 ? 0 : (cnt > a.k ? a.k : cnt);
+            if (a.n_comp <= 0) cnt = 0;
+        }
         nv = cnt + a.swa_len;
         if (split == 0 && hg == 0 && threadIdx.x == 0 && a.n_valid_out) a.n_valid_out[b] = nv;
     } else {
@@ -117,7 +122,7 @@ __device__ inline void attn_split(const AttnArgs& a, int n_splits, int split, in
         const int j = r0 + r;
         const uint16_t* src = nullptr;
         if (c < n_chunks && r < rows) {
-            if (!a.idx) {
+            if (!a.idx && !a.dense) {
                 src = a.kv + b * a.kv_stride_b + static_cast<long long>(j) * d;
             } else if (j < cnt) {
                 const int ri = my_idx[u] < 0 ? 0 : (my_idx[u] >= a.n_comp ? a.n_comp - 1 : my_idx[u]);
@@ -135,7 +140,7 @@ __device__ inline void attn_split(const AttnArgs& a, int n_splits, int split, in
         const int c = threadIdx.x + u * NT;
         if (c < kHeadGroup * cpr) *reinterpret_cast<uint4*>(qs + (c / cpr) * pitch + (c % cpr) * 8) = qv[u];
     }
-    const bool write_buf = a.idx && a.gather_buf && hg == 0;
+    const bool write_buf = (a.idx || a.dense) && a.gather_buf && hg == 0;
 #pragma unroll
     for (int u = 0; u < G::kChunks; ++u) {
         const int c = u * NT + threadIdx.x;

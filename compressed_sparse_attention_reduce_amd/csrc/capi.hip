@@ -455,6 +455,104 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
     return launched(e, "csa_decode_step/attention");
 }
 
+size_t csa_hca_decode_step_workspace_size(const csa_layer_desc* L) {
+    if (!L || L->batch < 1 || L->max_comp < 0 || L->w < 1) return 0;
+    return align256(csa::attn_workspace_bytes(true, L->batch, L->h, L->d, L->max_comp + L->w)) + 256;
+}
+
+int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes,
+                        csa_stream stream) {
+    CHECK(L && io, "csa_hca_decode_step: null layer or io");
+    if (L->dtype != CSA_BF16)
+        return fail(CSA_ERR_UNSUPPORTED, "csa_hca_decode_step: bfloat16 caches only");
+    CHECK(dtype_ok(L->out_dtype), "csa_hca_decode_step: bad out_dtype");
+    CHECK(L->batch >= 1 && L->m >= 1 && L->w >= 1, "csa_hca_decode_step: bad batch/m/w");
+    CHECK(L->overlap == 0, "csa_hca_decode_step: the HCA compressor is not overlapped (overlap must be 0)");
+    CHECK(L->comp_kv && L->swa && L->main_bias, "csa_hca_decode_step: null cache or bias pointer");
+    CHECK(io->q && io->kv_new && io->out, "csa_hca_decode_step: null io pointer");
+    CHECK(io->pos >= 0, "csa_hca_decode_step: pos < 0");
+    CHECK(L->n_comp >= 0 && L->n_comp <= L->max_comp, "csa_hca_decode_step: n_comp %d outside 0..max_comp %d",
+          L->n_comp, L->max_comp);
+    CHECK(L->swa_head >= 0 && L->swa_head < L->w && L->swa_len >= 0 && L->swa_len <= L->w,
+          "csa_hca_decode_step: bad SWA state");
+    const bool completes = io->pos % L->m == L->m - 1;
+    if (completes) {
+        CHECK(io->z_main && io->c_main, "csa_hca_decode_step: block rows missing");
+        CHECK(L->n_comp < L->max_comp, "csa_hca_decode_step: compressed cache full (max_comp %d)", L->max_comp);
+    }
+    const int n_max = L->max_comp + L->w;
+    if (n_max > csa::attn_max_rows())
+        return fail(CSA_ERR_UNSUPPORTED, "csa_hca_decode_step: max_comp + w = %d above %d rows", n_max,
+                    csa::attn_max_rows());
+    CHECK(L->h >= 16 && L->h % 16 == 0 && L->d >= 32 && L->d % 32 == 0 && L->d <= 512,
+          "csa_hca_decode_step: needs h a multiple of 16 and d a multiple of 32 up to 512");
+    CHECK(L->d <= csa::kPrepMaxD, "csa_hca_decode_step: head dim above %d", csa::kPrepMaxD);
+    CHECK(aligned16(io->q) && aligned16(L->comp_kv) && aligned16(L->swa) && aligned16(io->kv_new) &&
+              aligned16(io->out),
+          "csa_hca_decode_step: q, caches, kv_new and out must be 16-byte aligned");
+    CHECK(io->q_stride_b % 8 == 0 && L->comp_kv_stride_b % 8 == 0 && L->swa_stride_b % 8 == 0 &&
+              io->kv_new_stride_b % 8 == 0,
+          "csa_hca_decode_step: batch strides must keep 16-byte alignment");
+    if (!aligned16(ws)) return fail(CSA_ERR_INVALID_ARG, "csa_hca_decode_step: workspace must be 16-byte aligned");
+    if (ws_bytes < csa_hca_decode_step_workspace_size(L))
+        return fail(CSA_ERR_WORKSPACE, "csa_hca_decode_step: workspace %zu < %zu bytes", ws_bytes,
+                    csa_hca_decode_step_workspace_size(L));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int N = L->n_comp + (completes ? 1 : 0);
+
+    // a+b. SWA append and (on completion) the main compressor; no indexer key
+    csa::PrepArgs pa{};
+    pa.batch = L->batch;
+    pa.es = 2;
+    pa.d = L->d;
+    pa.m = L->m;
+    pa.completes = completes ? 1 : 0;
+    pa.n_comp = L->n_comp;
+    pa.block = io->pos / L->m;
+    pa.kv_new = io->kv_new;
+    pa.kv_new_stride_b = io->kv_new_stride_b;
+    pa.swa = L->swa;
+    pa.swa_stride_b = L->swa_stride_b;
+    pa.swa_slot = L->swa_head;
+    pa.z_main = io->z_main;
+    pa.c_main = io->c_main;
+    pa.zc_main_stride_b = io->zc_main_stride_b;
+    pa.main_bias = L->main_bias;
+    pa.main_norm = L->main_norm;
+    pa.comp_kv = L->comp_kv;
+    pa.comp_kv_stride_b = L->comp_kv_stride_b;
+    pa.idx_keys = nullptr;
+    hipError_t e = csa::launch_step_prep(pa, s);
+    if (e != hipSuccess) return launched(e, "csa_hca_decode_step/prep");
+
+    // c. attention over every compressed entry, then the window
+    csa::AttnArgs a{};
+    a.q = static_cast<const uint16_t*>(io->q);
+    a.q_stride_b = io->q_stride_b;
+    a.comp_kv = static_cast<const uint16_t*>(L->comp_kv);
+    a.comp_kv_stride_b = L->comp_kv_stride_b;
+    a.n_comp = N;
+    a.dense = true;
+    a.swa = static_cast<const uint16_t*>(L->swa);
+    a.swa_stride_b = L->swa_stride_b;
+    a.swa_head = (L->swa_head + 1) % L->w;
+    a.swa_len = L->swa_len + 1 < L->w ? L->swa_len + 1 : L->w;
+    a.w = L->w;
+    a.n_valid_out = io->n_valid;
+    a.sink = L->sink;
+    a.scale = L->scale;
+    a.out = io->out;
+    a.out_bf16 = L->out_dtype == CSA_BF16;
+    a.lse = io->lse;
+    a.out_stride_b = io->out_stride_b;
+    a.batch = L->batch;
+    a.h = L->h;
+    a.d = L->d;
+    a.n_max = n_max;
+    a.ws = ws;
+    return launched(csa::launch_attn_bf16(a, s), "csa_hca_decode_step/attention");
+}
+
 int csa_layer_advance(csa_layer_desc* L, int pos) {
     CHECK(L && L->w >= 1 && L->m >= 1 && pos >= 0, "csa_layer_advance: bad arguments");
     if (pos % L->m == L->m - 1) {

@@ -112,7 +112,10 @@ struct AttnArgs {
     long long kv_stride_b;
     const int* n_valid;
     // gather mode (idx != nullptr): rows = comp_kv[idx[b][0 .. count[b])] then
-    // the live SWA window; written to gather_buf and n_valid_out on the way
+    // the live SWA window; written to gather_buf and n_valid_out on the way.
+    // dense mode (dense, idx == nullptr): rows = comp_kv[0 .. n_comp) then the
+    // live SWA window (the HCA layers' attention)
+    bool dense;
     const uint16_t* comp_kv;
     long long comp_kv_stride_b;
     int n_comp;

@@ -2,7 +2,8 @@
 //   role 0  append the new token's KV row to the SWA ring (page 1, P2: the
 //           token lands in slot swa_head);
 //   role 1  compress the block the token completes into comp_kv[n_comp];
-//   role 2  compress that block's indexer key into idx_keys[n_comp].
+//   role 2  compress that block's indexer key into idx_keys[n_comp] (none
+//           for a layer without an indexer: idx_keys == nullptr).
 // Roles 1 and 2 run only when the token completes a block.
 #pragma once
 
@@ -24,6 +25,7 @@ __device__ inline void step_prep_role(const PrepArgs& a, int role, int b, float*
     }
     if (!a.completes) return;
     const bool main = role == 1;
+    if (!main && !a.idx_keys) return;  // a layer without an indexer (HCA)
     const int d = main ? a.d : a.d_i;
     const float* z = (main ? a.z_main : a.z_idx) + b * (main ? a.zc_main_stride_b : a.zc_idx_stride_b);
     const float* c = (main ? a.c_main : a.c_idx) + b * (main ? a.zc_main_stride_b : a.zc_idx_stride_b);

@@ -310,6 +310,33 @@ int csa_decode_step(const csa_layer_desc *layer, const csa_step_io *io, void *ws
 int csa_layer_advance(csa_layer_desc *layer, int pos);
 
 /* ------------------------------------------------------------------------
+ * 6b. One decode step of an HCA layer (heavily compressed attention).
+ *
+ * Source: page 1, PERFORMANCE_AUDIT.md, the forward_attention branches —
+ * layers with a compression ratio above 4 attend to ALL compressed entries
+ * followed by the SWA window (torch.cat([kv_cache.comp_kv, swa_kv])); page 2,
+ * single_shot_inference.py, eager_attention (gather_mixed_all for ratio > 4);
+ * the non-overlapped compressor of page 1, hca_compress_reduce_kernel.
+ *
+ * The same descriptor and io as csa_decode_step, with the indexer fields
+ * ignored (idx_keys, idx_bias, idx_norm, h_i, d_i, top_k; q_idx, w_idx,
+ * z_idx, c_idx, scores, topk_idx, topk_count, gather_buf).  Enqueues:
+ *   a. swa[swa_head] = kv_new;
+ *   b. if pos % m == m - 1: comp_kv[n_comp] = compress(z_main, c_main)
+ *      (overlap must be 0);
+ *   c. one softmax (scale, sink in the denominator) over comp_kv[0 .. N)
+ *      then the live window, N = n_comp (+1 if b ran); out [B][h][d],
+ *      lse [B][h] (nullable), n_valid [B] = N + window rows (nullable).
+ * bfloat16 caches only (CSA_ERR_UNSUPPORTED otherwise); h a multiple of 16,
+ * d a multiple of 32 up to 512, max_comp + w <= 8192.  The host integers are
+ * advanced by the caller (csa_layer_advance) as for csa_decode_step.
+ * Workspace: csa_hca_decode_step_workspace_size(layer) bytes, 16-byte aligned.
+ * ------------------------------------------------------------------------ */
+size_t csa_hca_decode_step_workspace_size(const csa_layer_desc *layer);
+int csa_hca_decode_step(const csa_layer_desc *layer, const csa_step_io *io, void *ws,
+                        size_t ws_bytes, csa_stream stream);
+
+/* ------------------------------------------------------------------------
  * 7. Prefill-shaped chunk: t query tokens at positions pos0, pos0+1, ...
  *    against one compressed history.
  *

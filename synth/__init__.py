@@ -20,6 +20,8 @@ this library is measured on:
 * ``ctx1m``    — context 1,000,000 (n_comp 250,000), batch 1, bf16, 30 layers.
 * ``prefill``  — 2048 query tokens at positions 260096..262143 against 65536
   compressed blocks with the causal block mask.
+* ``hca1m``    — an HCA layer (ratio 128, no indexer) at context 1,000,064
+  (n_comp 7813 after the step), 30 layers; main attention as ``ctx1m``.
 
 Context ``ctx`` counts the new token: it sits at position ``ctx - 1``.  With
 ratio 4 and ``ctx % 4 == 0`` the new token completes block ``n_comp - 1``, so
@@ -84,9 +86,12 @@ SHAPES: Dict[str, Shape] = {
     "batch128k": Shape("batch128k", batch=8, n_comp=32768, ctx=131072),
     "ctx1m": Shape("ctx1m", batch=1, n_comp=250000, ctx=1000000, layers=30),
     "prefill": Shape("prefill", batch=1, n_comp=65536, ctx=262144, t=2048),
+    # an HCA layer (ratio 128, no indexer) at 1M context; ctx = 7813 * 128 so
+    # the step completes a block, as the CSA workloads do
+    "hca1m": Shape("hca1m", batch=1, n_comp=7813, ctx=1_000_064, m=128, layers=30),
 }
 
-CONFIG_NUMBER = {"tiny": 1, "ctx8k": 2, "batch128k": 3, "ctx1m": 4, "prefill": 5}
+CONFIG_NUMBER = {"tiny": 1, "ctx8k": 2, "batch128k": 3, "ctx1m": 4, "prefill": 5, "hca1m": 6}
 
 
 def seed_for(shape: Shape, layer: int = 0) -> int:

@@ -260,6 +260,37 @@ def test_decode_step_validation_and_advance(csa):
         csa.csa_layer_advance(L4, 3)
 
 
+def test_hca_step_validation(csa):
+    B = csa.binding
+    L = B.LayerDesc()
+    L.batch, L.h, L.d, L.m, L.w, L.overlap = 1, 64, 512, 128, 128, 0
+    L.dtype = L.out_dtype = B.CSA_BF16
+    L.comp_kv, L.swa, L.main_bias = FAKE, FAKE, FAKE
+    L.max_comp, L.n_comp, L.swa_head, L.swa_len, L.scale = 7813, 7812, 64, 128, 0.04
+    io = B.StepIO()
+    io.pos, io.q, io.kv_new, io.out, io.z_main, io.c_main = 1000063, FAKE, FAKE, FAKE, FAKE, FAKE
+    lib = csa.lib()
+    need = lib.csa_hca_decode_step_workspace_size(ctypes.byref(L))
+    assert need >= 64 * 249 * 514 * 4  # partials of every 32-row split of 7941 rows
+    def call(ws_bytes=need):
+        return lib.csa_hca_decode_step(ctypes.byref(L), ctypes.byref(io), FAKE, ws_bytes, None)
+    assert call(need - 1) == B.CSA_ERR_WORKSPACE
+    L.dtype = B.CSA_F32
+    assert call() == B.CSA_ERR_UNSUPPORTED
+    L.dtype = B.CSA_BF16
+    L.overlap = 1
+    assert call() == B.CSA_ERR_INVALID_ARG
+    L.overlap = 0
+    L.n_comp = 7813  # cache full and the step completes a block
+    assert call() == B.CSA_ERR_INVALID_ARG
+    L.n_comp = 7812
+    io.z_main = None
+    assert call() == B.CSA_ERR_INVALID_ARG
+    io.z_main = FAKE
+    L.max_comp = 9000  # max_comp + w above the attention's row limit
+    assert lib.csa_hca_decode_step(ctypes.byref(L), ctypes.byref(io), FAKE, 1 << 40, None) == B.CSA_ERR_UNSUPPORTED
+
+
 def test_descriptors_keep_their_tensors_alive(csa):
     """make_layer_desc / make_step_io store raw pointers; the returned structs
     must keep the tensors alive, or temporaries passed in would be freed and

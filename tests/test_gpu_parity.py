@@ -682,3 +682,83 @@ def test_decode_steps_in_sequence(csa):
         np.testing.assert_array_equal(host_f64(outs["gather_buf"][0, :n_valid]), rows)
         ro, _ = oracle.sparse_attn(f(q[0]), rows, x["sink"], 1 / np.sqrt(512))
         assert rel_err(host_f64(outs["out"][0]), ro) <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# 6b. HCA layer step (ratio-m compressor, attention over every entry + window)
+# ---------------------------------------------------------------------------
+
+def test_hca_steps_in_sequence(csa):
+    """Twenty HCA steps at ratio 8 (three block completions, ring wrap) with
+    the host counters advanced by csa_layer_advance; each step against the
+    oracle's evolving state."""
+    m, W, D, H = 8, 8, 512, 64
+    g = _g(6001)
+    n0, pos0, max_comp = 37, 37 * 8 + 5, 48
+    comp = dev_bf16(synth.to_bf16_bits(g.standard_normal((1, max_comp, D), dtype=np.float32)))
+    swa = dev_bf16(synth.to_bf16_bits(g.standard_normal((1, W, D), dtype=np.float32)))
+    mb = dev_f32(g.standard_normal((m, D), dtype=np.float32) * np.float32(0.1))
+    sink = dev_f32(g.standard_normal(H, dtype=np.float32))
+    L = csa.make_layer_desc(comp_kv=comp, idx_keys=None, swa=swa, main_bias=mb, idx_bias=None, sink=sink,
+                            n_comp=n0, swa_head=pos0 % W, swa_len=W, h=H, h_i=0, m=m, top_k=0)
+    f = numfmt.bf16_bits_to_f64
+    ost = oracle.LayerState(comp_kv=host_f64(comp[0]), idx_keys=np.zeros((max_comp, 1)), n_comp=n0,
+                            swa=oracle.SwaRing(host_f64(swa[0]), pos0 % W, W), main_bias=host_f64(mb),
+                            idx_bias=np.zeros((m, 1)), sink=host_f64(sink), m=m, round_cache=numfmt.bf16_round_f64)
+    ws = torch.empty(csa.csa_hca_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+    for pos in range(pos0, pos0 + 20):
+        q = synth.to_bf16_bits(g.standard_normal((1, H, D), dtype=np.float32))
+        kvn = synth.to_bf16_bits(g.standard_normal((1, D), dtype=np.float32))
+        zm, cm = g.standard_normal((2, 1, m, D), dtype=np.float32)
+        out = torch.empty(1, H, D, dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty(1, H, device=DEV)
+        n_valid = torch.empty(1, dtype=torch.int32, device=DEV)
+        io = csa.make_step_io(pos=pos, q=dev_bf16(q), kv_new=dev_bf16(kvn), z_main=dev_f32(zm), c_main=dev_f32(cm),
+                              out=out, lse=lse, n_valid=n_valid)
+        csa.csa_hca_decode_step(L, io, ws)
+        csa.csa_layer_advance(L, pos)
+        torch.cuda.synchronize()
+        nprev = ost.n_comp
+        r = oracle.hca_decode_step(ost, q=f(q[0]), kv_new=f(kvn[0]), pos=pos, z_main=zm[0], c_main=cm[0],
+                                   scale=1 / np.sqrt(D))
+        assert (L.n_comp, L.swa_head, L.swa_len) == (ost.n_comp, ost.swa.head, ost.swa.length)
+        if pos % m == m - 1:  # the new entry within one bf16 ulp, then adopt the GPU's bits
+            assert_bf16_close(host_bits(comp[0, nprev]), oracle.compress(zm[0], cm[0], host_f64(mb), m)[0])
+            ost.comp_kv[nprev] = host_f64(comp[0, nprev])
+            r = oracle.sparse_attn(f(q[0]), np.concatenate([ost.comp_kv[:ost.n_comp], r["rows"][ost.n_comp:]]),
+                                   host_f64(sink), 1 / np.sqrt(D))
+            r = {"out": r[0], "lse": r[1], "n_valid": ost.n_comp + ost.swa.length}
+        assert int(n_valid[0]) == r["n_valid"]
+        assert rel_err(host_f64(out[0]), r["out"]) <= 2e-2
+        assert np.abs(lse[0].cpu().numpy() - r["lse"]).max() <= 1e-2
+
+
+def test_hca_step_full_size(csa):
+    """HCA at 1M context (ratio 128: 7812 entries + the one this step
+    completes, window 128 with wrap), one layer, against the oracle over all
+    7941 rows."""
+    shape = synth.SHAPES["hca1m"]
+    x = synth.make_decode_inputs_torch(shape, seed=None, device=DEV, layers=1)[0]
+    H, D, W = shape.h, shape.d, shape.w
+    L = csa.make_layer_desc(comp_kv=x["comp_kv"], idx_keys=None, swa=x["swa"], main_bias=x["main_bias"],
+                            idx_bias=None, sink=x["sink"], n_comp=x["n_comp"], swa_head=x["swa_head"],
+                            swa_len=x["swa_len"], h=H, h_i=0, m=shape.m, top_k=0)
+    out = torch.empty(1, H, D, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(1, H, device=DEV)
+    io = csa.make_step_io(pos=x["pos"], q=x["q"], kv_new=x["kv_new"], z_main=x["z_main"], c_main=x["c_main"],
+                          out=out, lse=lse)
+    ws = torch.empty(csa.csa_hca_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+    csa.csa_hca_decode_step(L, io, ws)
+    torch.cuda.synchronize()
+    N = x["n_comp"] + 1
+    assert N == shape.n_comp
+    assert_bf16_close(host_bits(x["comp_kv"][0, N - 1]),
+                      oracle.compress(host_f64(x["z_main"][0]), host_f64(x["c_main"][0]), host_f64(x["main_bias"]),
+                                      shape.m)[0])
+    head = (x["swa_head"] + 1) % W
+    swa = host_f64(x["swa"][0])
+    win = np.stack([swa[(head - W + j) % W] for j in range(W)])
+    rows = np.concatenate([host_f64(x["comp_kv"][0, :N]), win])
+    ro, rl = oracle.sparse_attn(host_f64(x["q"][0]), rows, host_f64(x["sink"]), 1 / np.sqrt(D))
+    assert rel_err(host_f64(out[0]), ro) <= 2e-2
+    assert np.abs(lse[0].cpu().numpy() - rl).max() <= 1e-2
