@@ -266,6 +266,59 @@ def time_prefill(csa, reps: int):
     }
 
 
+def time_hca(csa, reps: int):
+    """HCA layers at 1M context (ratio 128, 7813 compressed entries after the
+    step, window 128, 64 heads x 512): 30 independent layer caches, one
+    csa_hca_decode_step each, captured in one graph and replayed `reps`
+    times.  Returns the mean per-layer time and its algorithmic bytes."""
+    import torch
+    import synth
+
+    shape = synth.SHAPES["hca1m"]
+    xs = synth.make_decode_inputs_torch(shape, seed=None, device="cuda")
+    steps = []
+    for x in xs:
+        L = csa.make_layer_desc(comp_kv=x["comp_kv"], idx_keys=None, swa=x["swa"], main_bias=x["main_bias"],
+                                idx_bias=None, sink=x["sink"], n_comp=x["n_comp"], swa_head=x["swa_head"],
+                                swa_len=x["swa_len"], h=shape.h, h_i=0, m=shape.m, top_k=0)
+        out = torch.empty(1, shape.h, shape.d, dtype=torch.bfloat16, device="cuda")
+        io = csa.make_step_io(pos=x["pos"], q=x["q"], kv_new=x["kv_new"], z_main=x["z_main"], c_main=x["c_main"],
+                              out=out)
+        ws = torch.empty(csa.csa_hca_decode_step_workspace_size(L), dtype=torch.uint8, device="cuda")
+        steps.append((L, io, ws))
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for L, io, ws in steps:
+                csa.csa_hca_decode_step(L, io, ws, stream=stream)
+        g.replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    stream.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(steps))
+    n, d, w, h, m = shape.n_comp, shape.d, shape.w, shape.h, shape.m
+    # cache rows + window + q read, out written; the block's Z/C read and the entry written; the new row appended
+    alg = (n + w) * d * 2 + h * d * 2 + h * d * 2 + 2 * m * d * 4 + d * 2 + 2 * d * 2
+    del steps, xs
+    torch.cuda.empty_cache()
+    return {
+        "workload": "hca1m: one decode token through 30 HCA layers (ratio 128, no indexer), context 1,000,064 "
+                    "(7813 compressed entries incl. the one this step completes, SWA 128 with wrap), batch 1, "
+                    "main attention 64 heads x 512 bf16 with sink over every entry + the window",
+        "us_per_layer": round(us, 3),
+        "steps_per_s_30_layers": round(1e6 / (us * 30), 1),
+        "alg_bytes_per_layer": alg,
+        "achieved_gbps": round(alg / (us * 1e-6) / 1e9, 1),
+        "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
 def cpu_baseline(layers, shape, budget_s: float):
     """The float64 oracle on the host, layer by layer, until the budget is spent."""
     import numpy as np
@@ -398,6 +451,7 @@ def main() -> int:
     del layers  # the 1M-context caches make room for the prefill workload
     torch.cuda.empty_cache()
     prefill = time_prefill(csa, max(2, args.scan_reps // 2))
+    hca = time_hca(csa, args.scan_reps)
 
     res = {
         "metric": "CSA decode steps/s and indexer-scan HBM GB/s at 1M ctx (250K comp entries)",
@@ -444,6 +498,7 @@ def main() -> int:
             "frac": round(fp8_gbs / HBM_PEAK_GBS, 4),
         },
         "prefill": prefill,
+        "hca": hca,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

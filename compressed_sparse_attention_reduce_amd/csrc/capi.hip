@@ -456,8 +456,9 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
 }
 
 size_t csa_hca_decode_step_workspace_size(const csa_layer_desc* L) {
-    if (!L || L->batch < 1 || L->max_comp < 0 || L->w < 1) return 0;
-    return align256(csa::attn_workspace_bytes(true, L->batch, L->h, L->d, L->max_comp + L->w)) + 256;
+    if (!L || L->batch < 1 || L->max_comp < 0 || L->w < 1 || L->h < 1 || L->d < 1) return 0;
+    const size_t ns = static_cast<size_t>(csa::attn_dense_splits(L->max_comp + L->w));
+    return align256(sizeof(float) * static_cast<size_t>(L->batch) * L->h * ns * (static_cast<size_t>(L->d) + 2)) + 256;
 }
 
 int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes,
@@ -522,6 +523,8 @@ int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws
     pa.comp_kv = L->comp_kv;
     pa.comp_kv_stride_b = L->comp_kv_stride_b;
     pa.idx_keys = nullptr;
+    // long blocks without a norm: channel slices over several workgroups
+    pa.main_wgs = (L->m >= 32 && !L->main_norm) ? (L->d + 31) / 32 : 1;
     hipError_t e = csa::launch_step_prep(pa, s);
     if (e != hipSuccess) return launched(e, "csa_hca_decode_step/prep");
 
@@ -550,7 +553,7 @@ int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws
     a.d = L->d;
     a.n_max = n_max;
     a.ws = ws;
-    return launched(csa::launch_attn_bf16(a, s), "csa_hca_decode_step/attention");
+    return launched(csa::launch_attn_dense_bf16(a, s), "csa_hca_decode_step/attention");
 }
 
 int csa_layer_advance(csa_layer_desc* L, int pos) {

@@ -105,4 +105,76 @@ __device__ inline void compress_block(const float* __restrict__ z, const float* 
     if (keep) __syncthreads();
 }
 
+// Long blocks (large m, no norm) split over workgroups and row slices: this
+// workgroup computes channels [ch0, ch0 + nch) of the output row; its
+// blockDim.x / nch thread slices each take a contiguous range of the m rows
+// (all of a slice's loads in flight at once), and the slices' running
+// (max, denominator, weighted sum) are combined in LDS:
+// M = max_s mx_s, den = sum_s den_s e^(mx_s - M), acc likewise, y = acc / den.
+// part: 3 * blockDim.x floats of LDS.  Plain (non-overlapped) blocks only.
+__device__ inline void compress_block_slice(const float* __restrict__ z, const float* __restrict__ c,
+                                            const float* __restrict__ bias, void* __restrict__ out_row,
+                                            bool out_bf16, int m, int d, int ch0, int nch, float* part) {
+    const int slices = blockDim.x / nch;
+    const int t = threadIdx.x % nch;
+    const int sl = threadIdx.x / nch;
+    const int ch = ch0 + t;
+    const int per = (m + slices - 1) / slices;
+    const int r_lo = sl * per;
+    const int r_hi = min(m, r_lo + per);
+    float mx = -INFINITY, den = 0.f, acc = 0.f;
+    if (sl < slices && ch < d) {
+        constexpr int kBatch = 16;
+        for (int r0 = r_lo; r0 < r_hi; r0 += kBatch) {
+            float lz[kBatch], lc[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int r = r0 + u;
+                lz[u] = -INFINITY;
+                lc[u] = 0.f;
+                if (r < r_hi) {
+                    const long long o = static_cast<long long>(r) * d + ch;
+                    lz[u] = z[o] + bias[o];
+                    lc[u] = c[o];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (r0 + u < r_hi) {
+                    if (lz[u] > mx) {
+                        const float sc = expf(mx - lz[u]);  // 0 on the slice's first row
+                        den *= sc;
+                        acc *= sc;
+                        mx = lz[u];
+                    }
+                    const float e = expf(lz[u] - mx);
+                    den += e;
+                    acc += e * lc[u];
+                }
+            }
+        }
+    }
+    part[threadIdx.x] = mx;
+    part[blockDim.x + threadIdx.x] = den;
+    part[2 * blockDim.x + threadIdx.x] = acc;
+    __syncthreads();
+    if (sl == 0 && ch < d) {
+        float M = -INFINITY;
+        for (int s2 = 0; s2 < slices; ++s2) M = fmaxf(M, part[s2 * nch + t]);
+        float dsum = 0.f, asum = 0.f;
+        for (int s2 = 0; s2 < slices; ++s2) {
+            const float mxs = part[s2 * nch + t];
+            if (mxs == -INFINITY) continue;  // an empty slice
+            const float f = expf(mxs - M);
+            dsum += part[blockDim.x + s2 * nch + t] * f;
+            asum += part[2 * blockDim.x + s2 * nch + t] * f;
+        }
+        const float y = asum / dsum;
+        if (out_bf16)
+            static_cast<uint16_t*>(out_row)[ch] = f32_to_bf16(y);
+        else
+            static_cast<float*>(out_row)[ch] = y;
+    }
+}
+
 }  // namespace csa

@@ -146,6 +146,10 @@ int attn_max_rows();
 hipError_t launch_attn_bf16(AttnArgs a, hipStream_t s);
 // merge of the split partials already in a.ws (ws_o / ws_ml set), ns splits
 hipError_t launch_attn_merge(const AttnArgs& a, int ns, hipStream_t s);
+// dense mode (a.dense) with splits of several 32-row chunks (the HCA layers);
+// workspace: sizeof(float) * batch * h * attn_dense_splits(n_max) * (d + 2)
+int attn_dense_splits(int n_max);
+hipError_t launch_attn_dense_bf16(AttnArgs a, hipStream_t s);
 // decode step, bf16 gather mode, one query row per sequence: every attention
 // workgroup selects the top k itself (from cands when given, else the
 // exact path over the scores), then attends; topk idx / count written too.
@@ -159,6 +163,7 @@ hipError_t launch_attn_f32(const void* q, const void* kv, const int* n_valid, co
 constexpr int kPrepMaxD = 4096;
 struct PrepArgs {
     int batch, es, d, d_i, m, overlap, completes, n_comp;
+    int main_wgs;  // > 1: the main block is compressed in that many channel slices (roles 1 .. main_wgs)
     long long block;
     const void* kv_new;
     long long kv_new_stride_b;

@@ -18,7 +18,8 @@ __global__ __launch_bounds__(kPrepThreads) void k_step_prep(PrepArgs a) {
 }  // namespace
 
 hipError_t launch_step_prep(const PrepArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(k_step_prep, dim3(a.completes ? 3 : 1, a.batch), dim3(kPrepThreads), 0, s, a);
+    const int roles = !a.completes ? 1 : (a.main_wgs > 1 ? 1 + a.main_wgs : 3);
+    hipLaunchKernelGGL(k_step_prep, dim3(roles, a.batch), dim3(kPrepThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -4,7 +4,9 @@
 //   role 1  compress the block the token completes into comp_kv[n_comp];
 //   role 2  compress that block's indexer key into idx_keys[n_comp] (none
 //           for a layer without an indexer: idx_keys == nullptr).
-// Roles 1 and 2 run only when the token completes a block.
+// Roles 1 and 2 run only when the token completes a block.  A long main
+// block (main_wgs > 1: HCA ratios, no norm) is split over roles
+// 1 .. main_wgs by channel ranges instead, with no indexer role.
 #pragma once
 
 #include "compress_impl.h"
@@ -24,6 +26,16 @@ __device__ inline void step_prep_role(const PrepArgs& a, int role, int b, float*
         return;
     }
     if (!a.completes) return;
+    if (a.main_wgs > 1) {  // roles 1 .. main_wgs: channel slices of a long main block
+        if (role > a.main_wgs) return;
+        const int nch = (a.d + a.main_wgs - 1) / a.main_wgs;
+        const float* z = a.z_main + b * a.zc_main_stride_b;
+        const float* c = a.c_main + b * a.zc_main_stride_b;
+        char* out = static_cast<char*>(a.comp_kv) +
+                    (b * a.comp_kv_stride_b + static_cast<long long>(a.n_comp) * a.d) * a.es;
+        compress_block_slice(z, c, a.main_bias, out, a.es == 2, a.m, a.d, (role - 1) * nch, nch, ybuf);
+        return;
+    }
     const bool main = role == 1;
     if (!main && !a.idx_keys) return;  // a layer without an indexer (HCA)
     const int d = main ? a.d : a.d_i;

@@ -271,7 +271,7 @@ def test_hca_step_validation(csa):
     io.pos, io.q, io.kv_new, io.out, io.z_main, io.c_main = 1000063, FAKE, FAKE, FAKE, FAKE, FAKE
     lib = csa.lib()
     need = lib.csa_hca_decode_step_workspace_size(ctypes.byref(L))
-    assert need >= 64 * 249 * 514 * 4  # partials of every 32-row split of 7941 rows
+    assert need >= 64 * 63 * 514 * 4  # partials of every 128-row split of 7941 rows
     def call(ws_bytes=need):
         return lib.csa_hca_decode_step(ctypes.byref(L), ctypes.byref(io), FAKE, ws_bytes, None)
     assert call(need - 1) == B.CSA_ERR_WORKSPACE
