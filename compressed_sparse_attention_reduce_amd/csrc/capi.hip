@@ -499,7 +499,6 @@ int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws
         return fail(CSA_ERR_WORKSPACE, "csa_hca_decode_step: workspace %zu < %zu bytes", ws_bytes,
                     csa_hca_decode_step_workspace_size(L));
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const int N = L->n_comp + (completes ? 1 : 0);
 
     // a+b. SWA append and (on completion) the main compressor; no indexer key
     csa::PrepArgs pa{};
@@ -525,21 +524,21 @@ int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws
     pa.idx_keys = nullptr;
     // long blocks without a norm: channel slices over several workgroups
     pa.main_wgs = (L->m >= 32 && !L->main_norm) ? (L->d + 31) / 32 : 1;
-    hipError_t e = csa::launch_step_prep(pa, s);
-    if (e != hipSuccess) return launched(e, "csa_hca_decode_step/prep");
 
-    // c. attention over every compressed entry, then the window
+    // c. attention over the rows before the step — the entries before it and
+    //    the window rows that stay (the new token's slot is being written) —
+    //    in the same launch as a+b; the merge adds the new entry and token
     csa::AttnArgs a{};
     a.q = static_cast<const uint16_t*>(io->q);
     a.q_stride_b = io->q_stride_b;
     a.comp_kv = static_cast<const uint16_t*>(L->comp_kv);
     a.comp_kv_stride_b = L->comp_kv_stride_b;
-    a.n_comp = N;
+    a.n_comp = L->n_comp;
     a.dense = true;
     a.swa = static_cast<const uint16_t*>(L->swa);
     a.swa_stride_b = L->swa_stride_b;
-    a.swa_head = (L->swa_head + 1) % L->w;
-    a.swa_len = L->swa_len + 1 < L->w ? L->swa_len + 1 : L->w;
+    a.swa_head = L->swa_head;
+    a.swa_len = (L->swa_len + 1 < L->w ? L->swa_len + 1 : L->w) - 1;
     a.w = L->w;
     a.n_valid_out = io->n_valid;
     a.sink = L->sink;
@@ -553,7 +552,10 @@ int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws
     a.d = L->d;
     a.n_max = n_max;
     a.ws = ws;
-    return launched(csa::launch_attn_dense_bf16(a, s), "csa_hca_decode_step/attention");
+    const void* x0 = completes ? static_cast<const char*>(L->comp_kv) + 2 * static_cast<long long>(L->n_comp) * L->d
+                               : nullptr;
+    return launched(csa::launch_attn_dense_bf16(a, pa, x0, L->comp_kv_stride_b, io->kv_new, io->kv_new_stride_b, s),
+                    "csa_hca_decode_step");
 }
 
 int csa_layer_advance(csa_layer_desc* L, int pos) {

@@ -17,6 +17,7 @@
 #include "attn_split.h"
 #include "common.h"
 #include "kernels.h"
+#include "step_prep.h"
 
 namespace csa {
 
@@ -35,14 +36,24 @@ __host__ __device__ inline size_t dense_lds_bytes(int d) {
                                static_cast<size_t>(kHeadGroup) * kDensePPitch);
 }
 
-__global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, int n_splits) {
+__global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, int n_splits, int prep_wgs, PrepArgs p,
+                                                                    int extra_rows) {
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     __shared__ float wmax[kDenseWaves][kHeadGroup];
     __shared__ float wsum[kDenseWaves][kHeadGroup];
+    // the step's small jobs (SWA append, compression of a completed block) in
+    // their own workgroups; the rows they write are not
+    // read here (the attention covers the rows before the step, the merge
+    // adds the two new ones)
+    // (first in the grid, so they start before the attention fills the CUs)
+    if (static_cast<int>(blockIdx.x) < prep_wgs) {
+        step_prep_role(p, blockIdx.x, blockIdx.y, reinterpret_cast<float*>(smem), &wmax[0][0]);
+        return;
+    }
     const int groups = a.h / kHeadGroup;
     // workgroup id -> (split, head group): id % 8 = split % 8, so a split's
     // head groups share an XCD
-    const int id = blockIdx.x;
+    const int id = blockIdx.x - prep_wgs;
     const int rest = id / 8;
     const int hg = rest % groups;
     const int split = id % 8 + 8 * (rest / groups);
@@ -64,7 +75,7 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
     const int r0 = split * kDenseRows;
     const int rows = max(0, min(kDenseRows, nv - r0));
     const long long ml_base = (static_cast<long long>(b) * a.h + hg * kHeadGroup) * n_splits + split;
-    if (split == 0 && hg == 0 && threadIdx.x == 0 && a.n_valid_out) a.n_valid_out[b] = nv;
+    if (split == 0 && hg == 0 && threadIdx.x == 0 && a.n_valid_out) a.n_valid_out[b] = nv + extra_rows;
     if (rows == 0) {
         if (threadIdx.x < kHeadGroup) {
             a.ws_ml[2 * (ml_base + static_cast<long long>(threadIdx.x) * n_splits) + 0] = -INFINITY;
@@ -193,13 +204,112 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
     }
 }
 
+// Merge of the splits plus the step's new rows (the compressed entry of a
+// completed block, x0, if any; the new token's KV row, x1), one workgroup per
+// (head, sequence): M = max of the splits' maxima, the new rows' logits and
+// the sink; out = (sum_s e^(m_s - M) O_s + sum_i e^(s_i - M) x_i) / den with
+// den = sum_s e^(m_s - M) l_s + sum_i e^(s_i - M) + e^(sink - M).  At most
+// 64 splits (lane s of every wave holds split s's (m, l)).
+constexpr int kMergeThreads = 256;
+__global__ __launch_bounds__(kMergeThreads) void k_attn_merge_rows(AttnArgs a, int n_splits, const uint16_t* x0,
+                                                                   long long x0_stride_b, const uint16_t* x1,
+                                                                   long long x1_stride_b) {
+    __shared__ float red[2][kMergeThreads / kWave];
+    const int hh = blockIdx.x;
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int d = a.d;
+    const long long base = (static_cast<long long>(b) * a.h + hh) * n_splits;
+    const float* ob = a.ws_o + base * d;
+    const int col = 2 * threadIdx.x;
+    const bool has_col = col < d;
+    // the new rows' logits: q . x_i over the block, two sums at once
+    const uint16_t* qh = a.q + b * a.q_stride_b + static_cast<long long>(hh) * d;
+    float q0 = 0.f, q1 = 0.f, a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+    if (has_col) {
+        const uint32_t qq = *reinterpret_cast<const uint32_t*>(qh + col);
+        q0 = __uint_as_float(qq << 16);
+        q1 = __uint_as_float(qq & 0xffff0000u);
+        if (x0) {
+            const uint32_t xx = *reinterpret_cast<const uint32_t*>(x0 + b * x0_stride_b + col);
+            a0 = __uint_as_float(xx << 16);
+            a1 = __uint_as_float(xx & 0xffff0000u);
+        }
+        const uint32_t yy = *reinterpret_cast<const uint32_t*>(x1 + b * x1_stride_b + col);
+        b0 = __uint_as_float(yy << 16);
+        b1 = __uint_as_float(yy & 0xffff0000u);
+    }
+    float d0 = wave_sum(q0 * a0 + q1 * a1);
+    float d1 = wave_sum(q0 * b0 + q1 * b1);
+    if (lane == 0) {
+        red[0][wv] = d0;
+        red[1][wv] = d1;
+    }
+    __syncthreads();
+    d0 = 0.f;
+    d1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMergeThreads / kWave; ++w) {
+        d0 += red[0][w];
+        d1 += red[1][w];
+    }
+    const float s0 = x0 ? d0 * a.scale : -INFINITY;
+    const float s1 = d1 * a.scale;
+    // split weights
+    const float ms = lane < n_splits ? a.ws_ml[2 * (base + lane)] : -INFINITY;
+    const float ls = lane < n_splits ? a.ws_ml[2 * (base + lane) + 1] : 0.f;
+    float M = wave_max(ls > 0.f ? ms : -INFINITY);
+    M = fmaxf(M, fmaxf(s0, s1));
+    const float sk = a.sink ? a.sink[hh] : -INFINITY;
+    M = fmaxf(M, sk);  // finite: s1 is
+    const float wsp = ls > 0.f ? expf(ms - M) : 0.f;
+    const float e0 = x0 ? expf(s0 - M) : 0.f;
+    const float e1 = expf(s1 - M);
+    const float es = a.sink ? expf(sk - M) : 0.f;
+    const float den = wave_sum(wsp * ls) + e0 + e1 + es;
+    const float inv = 1.0f / den;
+    float acc0 = e0 * a0 + e1 * b0, acc1 = e0 * a1 + e1 * b1;
+    // the splits' outputs in batches of loads; empty splits' slots hold stale
+    // bytes, selected away (never multiplied)
+    constexpr int kBatch = 16;
+    for (int s0b = 0; s0b < n_splits; s0b += kBatch) {
+        float2 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            v[u] = (has_col && s0b + u < n_splits)
+                       ? *reinterpret_cast<const float2*>(ob + static_cast<long long>(s0b + u) * d + col)
+                       : make_float2(0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int sp = s0b + u < n_splits ? s0b + u : 0;
+            const float c = s0b + u < n_splits ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsp), sp)) : 0.f;
+            acc0 += c != 0.f ? c * v[u].x : 0.f;
+            acc1 += c != 0.f ? c * v[u].y : 0.f;
+        }
+    }
+    if (has_col) {
+        const long long o = b * a.out_stride_b + static_cast<long long>(hh) * d + col;
+        if (a.out_bf16) {
+            static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(acc0 * inv);
+            static_cast<uint16_t*>(a.out)[o + 1] = f32_to_bf16(acc1 * inv);
+        } else {
+            static_cast<float*>(a.out)[o] = acc0 * inv;
+            static_cast<float*>(a.out)[o + 1] = acc1 * inv;
+        }
+    }
+    if (a.lse && threadIdx.x == 0) a.lse[static_cast<long long>(b) * a.h + hh] = M + logf(den);
+}
+
 }  // namespace
 
 int attn_dense_splits(int n_max) { return n_max > 0 ? (n_max + kDenseRows - 1) / kDenseRows : 1; }
 
-hipError_t launch_attn_dense_bf16(AttnArgs a, hipStream_t s) {
-    if (a.d > kDenseMaxD || a.d % 32 != 0 || a.h % kHeadGroup != 0) return hipErrorInvalidValue;
+hipError_t launch_attn_dense_bf16(AttnArgs a, const PrepArgs& prep, const void* x0, long long x0_stride_b,
+                                  const void* x1, long long x1_stride_b, hipStream_t s) {
+    if (a.d > kDenseMaxD || a.d % 32 != 0 || a.h % kHeadGroup != 0 || !x1) return hipErrorInvalidValue;
     const int ns = attn_dense_splits(a.n_max);
+    if (ns > kWave) return hipErrorInvalidValue;
     a.ws_o = static_cast<float*>(a.ws);
     a.ws_ml = a.ws_o + static_cast<size_t>(a.batch) * a.h * ns * a.d;
     const size_t lds = dense_lds_bytes(a.d);
@@ -214,9 +324,14 @@ hipError_t launch_attn_dense_bf16(AttnArgs a, hipStream_t s) {
         opted[dev] = true;
     }
     const int groups = a.h / kHeadGroup;
-    const int wgs = 8 * groups * ((ns + 7) / 8);
-    hipLaunchKernelGGL(k_attn_dense_bf16, dim3(wgs, a.batch), dim3(kDenseThreads), lds, s, a, ns);
-    return launch_attn_merge(a, ns, s);
+    const int att_wgs = 8 * groups * ((ns + 7) / 8);
+    const int prep_wgs = !prep.completes ? 1 : (prep.main_wgs > 1 ? 1 + prep.main_wgs : 2);
+    const int extra = 1 + (x0 ? 1 : 0);
+    hipLaunchKernelGGL(k_attn_dense_bf16, dim3(att_wgs + prep_wgs, a.batch), dim3(kDenseThreads), lds, s, a, ns,
+                       prep_wgs, prep, extra);
+    hipLaunchKernelGGL(k_attn_merge_rows, dim3(a.h, a.batch), dim3(kMergeThreads), 0, s, a, ns,
+                       static_cast<const uint16_t*>(x0), x0_stride_b, static_cast<const uint16_t*>(x1), x1_stride_b);
+    return hipGetLastError();
 }
 
 }  // namespace csa

@@ -146,10 +146,16 @@ int attn_max_rows();
 hipError_t launch_attn_bf16(AttnArgs a, hipStream_t s);
 // merge of the split partials already in a.ws (ws_o / ws_ml set), ns splits
 hipError_t launch_attn_merge(const AttnArgs& a, int ns, hipStream_t s);
-// dense mode (a.dense) with splits of several 32-row chunks (the HCA layers);
-// workspace: sizeof(float) * batch * h * attn_dense_splits(n_max) * (d + 2)
+// The HCA step's attention (dense mode, a.dense): the rows before the step
+// (a.n_comp entries, a.swa_len window rows ending at slot a.swa_head - 1) in
+// 128-row splits, the step's jobs (prep) in the same launch, then a merge
+// that adds the new rows x0 (the entry of a completed block, or nullptr)
+// and x1 (the new token's row).  At most 64 splits.  Workspace:
+// sizeof(float) * batch * h * attn_dense_splits(n_max) * (d + 2).
+struct PrepArgs;
 int attn_dense_splits(int n_max);
-hipError_t launch_attn_dense_bf16(AttnArgs a, hipStream_t s);
+hipError_t launch_attn_dense_bf16(AttnArgs a, const PrepArgs& prep, const void* x0, long long x0_stride_b,
+                                  const void* x1, long long x1_stride_b, hipStream_t s);
 // decode step, bf16 gather mode, one query row per sequence: every attention
 // workgroup selects the top k itself (from cands when given, else the
 // exact path over the scores), then attends; topk idx / count written too.
