@@ -367,6 +367,11 @@ class LayerState:
     m: int = 4
     overlap: bool = False
     round_cache: Optional[callable] = field(default=None, repr=False)
+    # E4M3 indexer keys (page 1, single_shot_inference.py, "B2": keys kept as
+    # FP8_E4M3 in the cache): codes [max_comp, d_I] uint8 and float32 row
+    # scales [max_comp]; when set they replace idx_keys
+    idx_codes: Optional[np.ndarray] = None
+    idx_scales: Optional[np.ndarray] = None
 
 
 def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
@@ -384,8 +389,17 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
     rounding) is applied to entries written into the caches, which is what a
     later step reads back.  Mutates ``L`` and returns a dict of every
     intermediate.
+
+    With E4M3 indexer keys (``L.idx_codes`` set) the compressed key is taken
+    to float32 and quantised per row (:func:`numfmt.quantize_e4m3_rows`) into
+    ``L.idx_codes`` / ``L.idx_scales``, and the scores are
+    :func:`index_score_fp8` with ``q_idx`` the query's E4M3 codes and
+    ``w_idx`` the head weights with the query's scales folded in.
     """
+    from .numfmt import quantize_e4m3_rows
+
     m = L.m
+    fp8 = L.idx_codes is not None
     L.swa.append(np.asarray(kv_new, dtype=np.float64))
     rnd = L.round_cache if L.round_cache is not None else (lambda a: a)
     new_entry = None
@@ -400,11 +414,20 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
         if L.idx_norm is not None:
             yi = kv_norm(yi, L.idx_norm)
         L.comp_kv[L.n_comp] = rnd(ym)
-        L.idx_keys[L.n_comp] = rnd(yi)
+        if fp8:
+            codes, kscale = quantize_e4m3_rows(np.asarray(yi, dtype=np.float32)[None])
+            L.idx_codes[L.n_comp] = codes[0]
+            L.idx_scales[L.n_comp] = kscale[0]
+        else:
+            L.idx_keys[L.n_comp] = rnd(yi)
         new_entry = (ym, yi)
         L.n_comp += 1
     N = L.n_comp
-    scores = index_score(np.asarray(q_idx)[None], np.asarray(w_idx)[None], L.idx_keys[:N])[0]
+    if fp8:
+        scores = index_score_fp8(np.asarray(q_idx, dtype=np.uint8)[None], np.asarray(w_idx)[None],
+                                 L.idx_codes[:N], L.idx_scales[:N])[0]
+    else:
+        scores = index_score(np.asarray(q_idx)[None], np.asarray(w_idx)[None], L.idx_keys[:N])[0]
     idx, count = topk(scores[None], top_k)
     rows, n_valid = gather(L.comp_kv[:N], idx[0], int(count[0]), L.swa.rows, L.swa.head, L.swa.length)
     out, lse = sparse_attn(q, rows, L.sink, scale)

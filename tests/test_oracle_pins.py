@@ -584,6 +584,69 @@ def test_decode_step_cache_rounding_applies():
     np.testing.assert_array_equal(L.comp_kv[0], numfmt.bf16_round_f64(exact))
 
 
+def _e4m3_codes(g, shape):
+    """Random finite E4M3 codes of either sign (0x7F / 0xFF are NaN)."""
+    mag = g.integers(0, 0x7F, size=shape).astype(np.uint8)
+    return mag | (g.integers(0, 2, size=shape).astype(np.uint8) << 7)
+
+
+def test_decode_step_fp8_keys_equal_exact_keys_when_representable():
+    """E4M3 indexer keys lose nothing when every key is an E4M3 value times a
+    power of two and carries +-448 times that power (so max|row| / 448 is the
+    power itself): with ratio 1 the compressed key is the content row, its
+    quantisation is exact, and a step over E4M3 keys must match the step over
+    the same keys in float64 — scores, selection and output — as must the
+    stored codes and scales."""
+    g = _g(26)
+    D, di, H, W = 16, 8, 4, 6
+    Lp = _empty_state(g, D=D, di=di, H=H, W=W, m=1)
+    Lf = _empty_state(g, D=D, di=di, H=H, W=W, m=1)
+    Lf.main_bias, Lf.idx_bias, Lf.sink = Lp.main_bias, Lp.idx_bias, Lp.sink
+    Lf.idx_codes = np.zeros((64, di), dtype=np.uint8)
+    Lf.idx_scales = np.zeros(64, dtype=np.float32)
+    for pos in range(20):
+        inp = _step_inputs(g, D=D, di=di, H=H, m=1)
+        kc = _e4m3_codes(g, (1, di))
+        kc[0, pos % di] = 0x7E | (0x80 if pos % 3 == 0 else 0)   # +-448
+        inp["c_idx"] = numfmt.e4m3_decode(kc) * 0.125
+        qc = _e4m3_codes(g, (4, di))
+        rp = oracle.decode_step(Lp, pos=pos, top_k=5, **{**inp, "q_idx": numfmt.e4m3_decode(qc)})
+        rf = oracle.decode_step(Lf, pos=pos, top_k=5, **{**inp, "q_idx": qc})
+        np.testing.assert_array_equal(Lf.idx_codes[pos], kc[0])
+        assert Lf.idx_scales[pos] == np.float32(0.125)
+        np.testing.assert_allclose(rf["scores"], rp["scores"], rtol=1e-13, atol=1e-300)
+        np.testing.assert_array_equal(rf["idx"], rp["idx"])
+        np.testing.assert_allclose(rf["out"], rp["out"], rtol=1e-12, atol=1e-13)
+    assert Lf.n_comp == Lp.n_comp == 20
+
+
+def test_decode_step_fp8_key_within_e4m3_rounding():
+    """General compressor inputs: each stored E4M3 key decodes to within half
+    a unit of E4M3's last place of the float32 compressed key (3 significand
+    bits: relative 2^-4 in the normal range, absolute 2^-10 times the scale
+    below 2^-6), and the key's largest magnitude is stored as +-448."""
+    g = _g(27)
+    di = 32
+    L = _empty_state(g, di=di)
+    L.idx_codes = np.zeros((64, di), dtype=np.uint8)
+    L.idx_scales = np.zeros(64, dtype=np.float32)
+    for pos in range(16):
+        inp = _step_inputs(g, di=di)
+        inp["q_idx"] = _e4m3_codes(g, (4, di))
+        r = oracle.decode_step(L, pos=pos, **inp, top_k=3)
+        if r["new_entry"] is None:
+            continue
+        y = np.asarray(r["new_entry"][1], dtype=np.float32).astype(np.float64)
+        j = L.n_comp - 1
+        sc = float(L.idx_scales[j])
+        dec = numfmt.e4m3_decode(L.idx_codes[j]) * sc
+        assert sc == pytest.approx(np.abs(y).max() / 448, rel=1e-6)
+        bound = np.maximum(np.abs(y) * 2.0 ** -4, sc * 2.0 ** -10) * (1 + 1e-6)
+        assert (np.abs(dec - y) <= bound).all()
+        assert (L.idx_codes[j][np.argmax(np.abs(y))] & 0x7F) == 0x7E
+    assert L.n_comp == 4
+
+
 # ---------------------------------------------------------------------------
 # (6b) HCA step: the dense special case of the CSA step
 # ---------------------------------------------------------------------------
