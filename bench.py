@@ -135,45 +135,67 @@ def scan_traffic():
         return None
 
 
-def time_fp8_scan(csa, layers, shape, reps: int):
-    """The FP8 E4M3 variant of the scan (csa_index_score_fp8): every layer's
-    bf16 key cache quantised once (per-row scales) and the query per head;
-    timed like the bf16 scan (30 launches captured back to back in a graph).
-    Returns (average launch ms, algorithmic bytes per launch)."""
+def time_fp8(csa, layers, shape, reps: int, steps: int):
+    """The E4M3 indexer-key variant: every layer's bf16 key cache quantised
+    once (per-row scales) and the query per head.  Times (a) the FP8 scan
+    alone (csa_index_score_fp8, 30 launches captured back to back in a graph,
+    like the bf16 scan) and (b) the whole 30-layer decode step with E4M3 keys
+    (csa_decode_step, graph-replayed `steps` times).  Returns (average scan
+    launch ms, algorithmic bytes per scan launch, ms per step)."""
     import torch
 
     n = shape.n_comp
-    caches = []
+    fl = []
     for ly in layers:
         x = ly["x"]
-        kc = torch.empty(1, n, 128, dtype=torch.uint8, device="cuda")
-        ks = torch.empty(1, n, dtype=torch.float32, device="cuda")
-        csa.csa_quantize_fp8(x["idx_keys"][:, :n].contiguous(), kc, ks)
-        q = x["q_idx"][:, None].contiguous()
-        qc = torch.empty(1, 1, 64, 128, dtype=torch.uint8, device="cuda")
-        qs = torch.empty(1, 1, 64, dtype=torch.float32, device="cuda")
-        csa.csa_quantize_fp8(q, qc, qs)
-        w8 = (x["w_idx"][:, None] * qs).contiguous()
-        caches.append((qc, w8, kc, ks))
+        kc = torch.zeros(1, shape.max_comp, 128, dtype=torch.uint8, device="cuda")
+        ks = torch.zeros(1, shape.max_comp, dtype=torch.float32, device="cuda")
+        csa.csa_quantize_fp8(x["idx_keys"][:, :n].contiguous(), kc[:, :n], ks[:, :n])
+        qc = torch.empty(1, 64, 128, dtype=torch.uint8, device="cuda")
+        qs = torch.empty(1, 64, dtype=torch.float32, device="cuda")
+        csa.csa_quantize_fp8(x["q_idx"].contiguous(), qc, qs)
+        w8 = (x["w_idx"] * qs).contiguous()
+        L = csa.make_layer_desc(comp_kv=x["comp_kv"], idx_keys=kc, idx_scales=ks, swa=x["swa"],
+                                main_bias=x["main_bias"], idx_bias=x["idx_bias"], sink=x["sink"],
+                                n_comp=x["n_comp"], swa_head=x["swa_head"], swa_len=x["swa_len"],
+                                h=shape.h, h_i=shape.h_i, m=shape.m, top_k=shape.top_k)
+        io = csa.make_step_io(pos=x["pos"], q=x["q"], q_idx=qc, w_idx=w8, kv_new=x["kv_new"],
+                              z_main=x["z_main"], c_main=x["c_main"], z_idx=x["z_idx"], c_idx=x["c_idx"],
+                              **ly["outs"])
+        fl.append({"L": L, "io": io, "ws": ly["ws"], "qc": qc, "w8": w8, "kc": kc, "ks": ks, "outs": ly["outs"]})
     torch.cuda.synchronize()
-    stream = torch.cuda.Stream()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(g, stream=stream):
-            for (qc, w8, kc, ks), ly in zip(caches, layers):
-                csa.csa_index_score_fp8(qc, w8, kc, ks, ly["outs"]["scores"][:, None], stream=stream)
-        g.replay()
-        stream.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
+
+    def timed(body, count):
+        stream = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                body(stream)
             g.replay()
-        e1.record(stream)
-    stream.synchronize()
+            stream.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(count):
+                g.replay()
+            e1.record(stream)
+        stream.synchronize()
+        return e0.elapsed_time(e1) / count
+
+    def scans(stream):
+        for f in fl:
+            csa.csa_index_score_fp8(f["qc"][:, None], f["w8"][:, None], f["kc"], f["ks"],
+                                    f["outs"]["scores"][:, None], n=n, stream=stream)
+
+    def step(stream):
+        for f in fl:
+            csa.csa_decode_step(f["L"], f["io"], f["ws"], stream=stream)
+
+    scan_ms = timed(scans, reps) / len(fl)
+    step_ms = timed(step, steps)
     alg = n * 128 + n * 4 + 64 * 128 + 64 * 4 + n * 4  # keys + key scales + q + w read, scores written
-    del caches
-    return e0.elapsed_time(e1) / (reps * len(layers)), alg
+    del fl
+    return scan_ms, alg, step_ms
 
 
 def time_prefill(csa, reps: int):
@@ -442,7 +464,7 @@ def main() -> int:
     step_bytes = ab["per_layer"] * shape.layers
     step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    fp8_ms, fp8_bytes = time_fp8_scan(csa, layers, shape, args.scan_reps)
+    fp8_ms, fp8_bytes, fp8_step_ms = time_fp8(csa, layers, shape, args.scan_reps, max(20, args.steps // 2))
     fp8_gbs = fp8_bytes / (fp8_ms * 1e-3) / 1e9
 
     cpu = None
@@ -496,6 +518,8 @@ def main() -> int:
             "alg_bytes_per_launch": fp8_bytes,
             "achieved_gbps": round(fp8_gbs, 1),
             "frac": round(fp8_gbs / HBM_PEAK_GBS, 4),
+            "decode_steps_per_s": round(1e3 / fp8_step_ms, 2),
+            "decode_ms_per_step": round(fp8_step_ms, 5),
         },
         "prefill": prefill,
         "hca": hca,

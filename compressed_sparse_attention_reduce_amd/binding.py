@@ -50,6 +50,7 @@ class LayerDesc(ctypes.Structure):
         ("main_bias", _vp), ("idx_bias", _vp), ("main_norm", _vp), ("idx_norm", _vp), ("sink", _vp),
         ("scale", _f),
         ("n_comp", _i), ("swa_head", _i), ("swa_len", _i),
+        ("idx_dtype", _i), ("idx_scales", _vp), ("idx_scales_stride_b", _ll),
     ]
 
 
@@ -275,11 +276,12 @@ def csa_layer_advance(layer: LayerDesc, pos: int) -> None:
 def make_layer_desc(*, comp_kv, idx_keys, swa, main_bias, idx_bias, sink, n_comp: int,
                     swa_head: int, swa_len: int, h: int, h_i: int, m: int = 4, top_k: int,
                     overlap: int = 0, out_dtype=None, scale: Optional[float] = None,
-                    main_norm=None, idx_norm=None) -> LayerDesc:
+                    main_norm=None, idx_norm=None, idx_scales=None) -> LayerDesc:
     """Fill a LayerDesc from cache tensors: comp_kv [B, max_comp, d], idx_keys
     [B, max_comp, d_i] (None for an HCA layer, with idx_bias None, h_i and
-    top_k 0), swa [B, W, d].  The returned struct keeps references to every
-    tensor it points at."""
+    top_k 0), swa [B, W, d].  idx_keys of torch.uint8 are E4M3 codes, with
+    their row scales in idx_scales [B, max_comp] float32.  The returned struct
+    keeps references to every tensor it points at."""
     B, max_comp, d = comp_kv.shape
     L = LayerDesc()
     L.batch, L.h, L.d, L.h_i, L.d_i = B, h, d, h_i, (idx_keys.shape[2] if idx_keys is not None else 0)
@@ -295,8 +297,15 @@ def make_layer_desc(*, comp_kv, idx_keys, swa, main_bias, idx_bias, sink, n_comp
     L.sink = _ptr(sink)
     L.scale = (1.0 / d ** 0.5) if scale is None else scale
     L.n_comp, L.swa_head, L.swa_len = n_comp, swa_head, swa_len
+    if idx_keys is not None and idx_keys.dtype == torch.uint8:
+        if idx_scales is None or idx_scales.dtype != torch.float32:
+            raise ValueError("E4M3 idx_keys need float32 idx_scales [B, max_comp]")
+        L.idx_dtype = CSA_FP8_E4M3
+        L.idx_scales, L.idx_scales_stride_b = idx_scales.data_ptr(), idx_scales.stride(0)
+    else:
+        L.idx_dtype = L.dtype
     # the struct holds raw device pointers: keep the tensors alive with it
-    L._keep = (comp_kv, idx_keys, swa, main_bias, idx_bias, sink, main_norm, idx_norm)
+    L._keep = (comp_kv, idx_keys, swa, main_bias, idx_bias, sink, main_norm, idx_norm, idx_scales)
     return L
 
 

@@ -142,25 +142,36 @@ int csa_quantize_fp8(const void* x, csa_dtype x_dtype, unsigned char* codes, flo
                     "csa_quantize_fp8");
 }
 
+static int check_fp8_score_args(const void* q, const float* w, const void* k, const float* k_scale, float* scores,
+                                int batch, int t, int h_i, int d_i, int n, int ratio, long long q_stride_b,
+                                long long w_stride_b, long long k_stride_b, long long ks_stride_b,
+                                long long s_stride_b, long long ld_s, const char* who) {
+    CHECK(q && w && k && k_scale && scores, "%s: null pointer argument", who);
+    CHECK(batch >= 1 && t >= 1 && n >= 0, "%s: batch %d t %d n %d", who, batch, t, n);
+    CHECK(batch * static_cast<long long>(t) <= 65535, "%s: batch*t above 65535", who);
+    CHECK(ratio >= 1, "%s: ratio %d", who, ratio);
+    CHECK(ld_s >= n && q_stride_b >= 0 && w_stride_b >= 0 && k_stride_b >= 0 && ks_stride_b >= 0 &&
+              s_stride_b >= 0,
+          "%s: bad strides", who);
+    if (h_i != 64 || d_i != 128)
+        return fail(CSA_ERR_UNSUPPORTED, "%s: E4M3 keys need h_i=64, d_i=128 (got %d, %d)", who, h_i, d_i);
+    CHECK(aligned16(q) && aligned16(k) && aligned16(w), "%s: q, k, w must be 16-byte aligned", who);
+    CHECK(q_stride_b % 16 == 0 && k_stride_b % 16 == 0 && w_stride_b % 4 == 0,
+          "%s: batch strides must keep 16-byte alignment", who);
+    return CSA_OK;
+}
+
 int csa_index_score_fp8(const unsigned char* q, const float* w, const unsigned char* k, const float* k_scale,
                         float* scores, int batch, int t, int h_i, int d_i, int n, const int* q_pos, int ratio,
                         long long q_stride_b, long long w_stride_b, long long k_stride_b, long long ks_stride_b,
                         long long s_stride_b, long long ld_s, csa_stream stream) {
-    CHECK(q && w && k && k_scale && scores, "csa_index_score_fp8: null pointer argument");
-    CHECK(batch >= 1 && t >= 1 && n >= 0, "csa_index_score_fp8: batch %d t %d n %d", batch, t, n);
-    CHECK(batch * static_cast<long long>(t) <= 65535, "csa_index_score_fp8: batch*t above 65535");
-    CHECK(ratio >= 1, "csa_index_score_fp8: ratio %d", ratio);
-    CHECK(ld_s >= n && q_stride_b >= 0 && w_stride_b >= 0 && k_stride_b >= 0 && ks_stride_b >= 0 &&
-              s_stride_b >= 0,
-          "csa_index_score_fp8: bad strides");
-    if (h_i != 64 || d_i != 128)
-        return fail(CSA_ERR_UNSUPPORTED, "csa_index_score_fp8: needs h_i=64, d_i=128 (got %d, %d)", h_i, d_i);
-    CHECK(aligned16(q) && aligned16(k) && aligned16(w), "csa_index_score_fp8: q, k, w must be 16-byte aligned");
-    CHECK(q_stride_b % 16 == 0 && k_stride_b % 16 == 0 && w_stride_b % 4 == 0,
-          "csa_index_score_fp8: batch strides must keep 16-byte alignment");
+    const int rc = check_fp8_score_args(q, w, k, k_scale, scores, batch, t, h_i, d_i, n, ratio, q_stride_b,
+                                        w_stride_b, k_stride_b, ks_stride_b, s_stride_b, ld_s,
+                                        "csa_index_score_fp8");
+    if (rc != CSA_OK) return rc;
     csa::Fp8ScoreArgs a{q, w, k, k_scale, scores, batch, t, n, q_pos, ratio,
-                        q_stride_b, w_stride_b, k_stride_b, ks_stride_b, s_stride_b, ld_s};
-    return launched(csa::launch_index_score_fp8(a, static_cast<hipStream_t>(stream)), "csa_index_score_fp8");
+                        q_stride_b, w_stride_b, k_stride_b, ks_stride_b, s_stride_b, ld_s, csa::CandArgs{nullptr, 0, 0, 0}};
+    return launched(csa::launch_index_score_fp8(a, nullptr, static_cast<hipStream_t>(stream)), "csa_index_score_fp8");
 }
 
 size_t csa_topk_workspace_size(int batch, int t, int n, int k) {
@@ -318,9 +329,17 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
         return fail(CSA_ERR_WORKSPACE, "csa_decode_step: workspace %zu < %zu bytes", ws_bytes,
                     csa_decode_step_workspace_size(L));
     const int N = L->n_comp + (completes ? 1 : 0);
-    const int rc_s = check_score_args(io->q_idx, io->w_idx, L->idx_keys, io->scores, L->dtype, L->batch,
-                                      1, L->h_i, L->d_i, N, L->m, io->q_idx_stride_b, io->w_stride_b,
-                                      L->idx_keys_stride_b, io->scores_stride_b, N, "csa_decode_step");
+    // E4M3 indexer keys: bfloat16 everything else, the FP8 score kernel
+    const bool fp8 = L->idx_dtype == CSA_FP8_E4M3;
+    if (fp8 && L->dtype != CSA_BF16)
+        return fail(CSA_ERR_UNSUPPORTED, "csa_decode_step: E4M3 indexer keys need bfloat16 caches");
+    const int rc_s = fp8 ? check_fp8_score_args(io->q_idx, io->w_idx, L->idx_keys, L->idx_scales, io->scores,
+                                                L->batch, 1, L->h_i, L->d_i, N, L->m, io->q_idx_stride_b,
+                                                io->w_stride_b, L->idx_keys_stride_b, L->idx_scales_stride_b,
+                                                io->scores_stride_b, N, "csa_decode_step")
+                         : check_score_args(io->q_idx, io->w_idx, L->idx_keys, io->scores, L->dtype, L->batch,
+                                            1, L->h_i, L->d_i, N, L->m, io->q_idx_stride_b, io->w_stride_b,
+                                            L->idx_keys_stride_b, io->scores_stride_b, N, "csa_decode_step");
     if (rc_s != CSA_OK) return rc_s;
     const int n_max = L->top_k + L->w;
     const int rc_a = check_attn(io->q, io->gather_buf, io->n_valid, io->out, L->dtype, L->out_dtype,
@@ -377,7 +396,10 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
     pa.comp_kv_stride_b = L->comp_kv_stride_b;
     pa.idx_keys = L->idx_keys;
     pa.idx_keys_stride_b = L->idx_keys_stride_b;
-    // The bf16 score kernel runs these jobs in its first workgroups (and
+    pa.idx_fp8 = fp8 ? 1 : 0;
+    pa.idx_scales = fp8 ? L->idx_scales : nullptr;
+    pa.idx_scales_stride_b = fp8 ? L->idx_scales_stride_b : 0;
+    // The bf16 and E4M3 score kernels runs these jobs in its first workgroups (and
     // scores the new key itself); the float32 path launches them first.
     const int n_scan = bf ? L->n_comp : N;
     const int prep_wgs = bf ? (completes ? 3 : 1) : 0;
@@ -390,8 +412,11 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
     //    then the exact top-k
     csa::CandArgs ca{nullptr, 0, 0, 0};
     if (bf && N > 0) {
-        const int slots = csa::index_score_bf16_wgs(L->batch, n_scan, prep_wgs) + (completes ? 1 : 0);
-        const int kpw = csa::index_score_bf16_keys_per_wg(L->batch, n_scan, prep_wgs);
+        const int slots = (fp8 ? csa::index_score_fp8_wgs(L->batch, n_scan, prep_wgs)
+                               : csa::index_score_bf16_wgs(L->batch, n_scan, prep_wgs)) +
+                          (completes ? 1 : 0);
+        const int kpw = fp8 ? csa::index_score_fp8_keys_per_wg(L->batch, n_scan, prep_wgs)
+                            : csa::index_score_bf16_keys_per_wg(L->batch, n_scan, prep_wgs);
         const int m = kpw > 0 ? csa::topk_cand_m(N, L->top_k, kpw) : -1;
         const int mw = kpw > 0 ? csa::topk_cand_m(N, L->top_k, kpw / csa::kScoreWavesPerWg) : -1;
         if (m > 0 && slots <= kStepMaxSlots && N > 4 * L->top_k)
@@ -400,7 +425,15 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
     csa::ScoreArgs sa{io->q_idx, io->w_idx, L->idx_keys, io->scores, L->batch, 1, L->h_i, L->d_i, n_scan,
                       nullptr, L->m, io->q_idx_stride_b, io->w_stride_b, L->idx_keys_stride_b,
                       io->scores_stride_b, N, ca};
-    e = bf ? csa::launch_index_score_bf16(sa, &pa, s) : csa::launch_index_score_f32(sa, s);
+    if (fp8) {
+        const csa::Fp8ScoreArgs fa{static_cast<const uint8_t*>(io->q_idx), io->w_idx,
+                                   static_cast<const uint8_t*>(L->idx_keys), L->idx_scales, io->scores,
+                                   L->batch, 1, n_scan, nullptr, L->m, io->q_idx_stride_b, io->w_stride_b,
+                                   L->idx_keys_stride_b, L->idx_scales_stride_b, io->scores_stride_b, N, ca};
+        e = csa::launch_index_score_fp8(fa, &pa, s);
+    } else {
+        e = bf ? csa::launch_index_score_bf16(sa, &pa, s) : csa::launch_index_score_f32(sa, s);
+    }
     if (e != hipSuccess) return launched(e, "csa_decode_step/index_score");
     csa::TopkArgs ta{io->scores, L->batch, 1, N, N, io->scores_stride_b, L->top_k, io->topk_idx,
                      io->topk_count, tws};

@@ -19,40 +19,14 @@
 //   is byte 32g + 8s + e), plus the key's scale; a ring of 8 tiles per wave
 //   keeps as many bytes in flight as the bf16 kernel's 4.
 #include "common.h"
+#include "fp8_codec.h"
 #include "kernels.h"
+#include "step_prep.h"
+#include "topk_common.h"
 
 namespace csa {
 
 namespace {
-
-__device__ inline uint8_t e4m3_encode_rne(float y) {
-    const uint32_t u = __float_as_uint(y);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7fffffffu;
-    if (a >= 0x43e00000u) return static_cast<uint8_t>(sign | 0x7eu);  // |y| >= 448: saturate
-    const int e = static_cast<int>(a >> 23) - 127;
-    if (e >= -6) {  // normal E4M3
-        const uint32_t mant = a & 0x7fffffu;
-        uint32_t m3 = mant >> 20;
-        const uint32_t rem = mant & 0xfffffu;
-        if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
-        uint32_t ee = static_cast<uint32_t>(e + 7);
-        if (m3 == 8u) {
-            m3 = 0;
-            ++ee;
-        }
-        return static_cast<uint8_t>(sign | (ee << 3) | m3);
-    }
-    // subnormal E4M3: m * 2^-9, m = round(|y| * 2^9) in 0..8
-    const int sh = 14 - e;  // |y| * 2^9 = (1.mant * 2^23) >> sh
-    if (sh >= 25) return static_cast<uint8_t>(sign);  // below half the smallest subnormal
-    const uint32_t M = (a & 0x7fffffu) | 0x800000u;
-    uint32_t m = M >> sh;
-    const uint32_t rem = M & ((1u << sh) - 1u);
-    const uint32_t half = 1u << (sh - 1);
-    if (rem > half || (rem == half && (m & 1u))) ++m;
-    return static_cast<uint8_t>(sign | m);
-}
 
 constexpr int kQuantThreads = 256;
 constexpr int kQuantRowsPerWg = kQuantThreads / kWave;
@@ -87,31 +61,103 @@ constexpr int kMTiles = kHeads / 16;
 constexpr int kRing = 8;            // key tiles in flight per wave
 constexpr int kQPitch = kDi + 16;   // LDS row pitch of the staged query (bytes)
 
+constexpr int kLaneTop = 4;         // composites a lane keeps (candidate lists)
+constexpr int kMaxTilesPerWave = 32;  // with candidates: at most 8 keys per lane list
+static_assert(kRing % 4 == 0, "ring slot i feeds the lists of lane group i % 4");
+
+static_assert(kWaves == kScoreWavesPerWg, "waves per workgroup as the host assumes");
+
 typedef long fp8x8;  // eight E4M3 codes, one MFMA operand
 constexpr int kFp8WgsPerCu = 2;  // one per CU measured slower (11.3 vs 10.9 us at n = 250,000)
 
-__global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a, int tiles_per_row) {
-    __shared__ __attribute__((aligned(16))) uint8_t qs[kHeads * kQPitch];
+// Score of the new key (decoded E4M3 values key[0..128), scale key[128], in
+// LDS) for query row (b, tt): four lanes per head, 32 code bytes each.
+// Returns the score in every thread; red: kWaves floats of LDS.
+__device__ inline float score_one_key_fp8(const Fp8ScoreArgs& a, int b, int tt, const float* key, float* red) {
+    constexpr int kPer = kDi * kHeads / kThreads;  // key elements per thread
+    const int h = threadIdx.x / (kDi / kPer);
+    const int part = threadIdx.x % (kDi / kPer);
+    const uint8_t* qh = a.q + b * a.q_stride_b + (static_cast<long long>(tt) * kHeads + h) * kDi + kPer * part;
+    float dot = 0.f;
+#pragma unroll
+    for (int u = 0; u < kPer / 16; ++u) {
+        const uint4 v = *reinterpret_cast<const uint4*>(qh + 16 * u);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            dot += e4m3_decode((w4[e >> 2] >> (8 * (e & 3))) & 0xffu) * key[kPer * part + 16 * u + e];
+    }
+    dot += xor_lanes_f32<1>(dot);
+    dot += xor_lanes_f32<2>(dot);
+    const float wh = a.w[b * a.w_stride_b + static_cast<long long>(tt) * kHeads + h];
+    float sc = part == 0 ? wh * fmaxf(dot * key[kDi], 0.f) : 0.f;
+    sc = wave_sum(sc);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = sc;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tot += red[w];
+    return tot;
+}
+
+template <bool kCands>
+__global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a, int tiles_per_row, PrepArgs p,
+                                                                 int prep_wgs) {
+    // the query staging area doubles as the LDS of the decode step's small jobs
+    constexpr int kLdsFloats = kPrepMaxD + kDi + 8;
+    static_assert(kHeads * kQPitch <= kLdsFloats * sizeof(float), "query fits the shared area");
+    __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
     __shared__ __attribute__((aligned(16))) float ws[kHeads];
+    __shared__ CandSmem cs;
+    uint8_t* qs = reinterpret_cast<uint8_t*>(lds);
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const int row = blockIdx.y;
     const int b = row / a.t;
     const int tt = row - b * a.t;
+
+    // 0. the decode step's small jobs; the workgroup that quantises the new
+    //    indexer key also scores it and fills its candidate slot
+    if (static_cast<int>(blockIdx.x) < prep_wgs) {
+        float* ybuf = lds;
+        float* key = lds + kPrepMaxD;
+        step_prep_role(p, blockIdx.x, b, ybuf, ws, key);
+        if (blockIdx.x == 2 && p.completes) {
+            float sc = score_one_key_fp8(a, b, tt, key, ws + 8);
+            const int kidx = a.n;
+            if (a.q_pos && static_cast<long long>(a.ratio) * kidx + a.ratio - 1 > a.q_pos[row]) sc = -INFINITY;
+            if (threadIdx.x == 0) a.scores[b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s + kidx] = sc;
+            if (kCands && threadIdx.x <= a.cands.m) {
+                const uint32_t kk = score_key(sc);
+                unsigned long long* slot = a.cands.lists + (static_cast<long long>(row) * a.cands.slots +
+                                                            a.cands.slots - 1) * (a.cands.m + 1);
+                slot[threadIdx.x] =
+                    (threadIdx.x == 0 && key_valid(kk, sc)) ? composite(kk, static_cast<uint32_t>(kidx)) : 0ull;
+            }
+        }
+        return;
+    }
+    const int wg = blockIdx.x - prep_wgs;
+    const int scan_wgs = gridDim.x - prep_wgs;
     const int li = lane & 15;
     const int lg = lane >> 4;
     const int n = a.n;
-    const int waves_per_row = gridDim.x * kWaves;
-    const int gw = blockIdx.x * kWaves + wv;
+    if (n <= 0) {  // nothing to scan: an empty candidate list
+        if (kCands && threadIdx.x <= a.cands.m)
+            a.cands.lists[(static_cast<long long>(row) * a.cands.slots + wg) * (a.cands.m + 1) + threadIdx.x] = 0ull;
+        return;
+    }
+    const int waves_per_row = scan_wgs * kWaves;
+    const int gw = wg * kWaves + wv;
     const int n_mine = gw < tiles_per_row ? (tiles_per_row - gw + waves_per_row - 1) / waves_per_row : 0;
 
     const uint8_t* kbase = a.k + b * a.k_stride_b + 32 * lg;
     const float* sbase = a.k_scale + b * a.ks_stride_b;
     auto load_tile = [&](int j, uint4* dst, float& ks) {
         const int key = j < n_mine ? min((gw + j * waves_per_row) * kTileKeys + li, n - 1) : n - 1;
-        const uint8_t* p = kbase + static_cast<long long>(key) * kDi;
-        dst[0] = *reinterpret_cast<const uint4*>(p);
-        dst[1] = *reinterpret_cast<const uint4*>(p + 16);
+        const uint8_t* src = kbase + static_cast<long long>(key) * kDi;
+        dst[0] = *reinterpret_cast<const uint4*>(src);
+        dst[1] = *reinterpret_cast<const uint4*>(src + 16);
         ks = sbase[key];
     };
 
@@ -125,10 +171,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
     __builtin_amdgcn_sched_barrier(0);
     uint4 kb[kRing][2];
     float ksc[kRing];
-    if (n > 0) {
 #pragma unroll
-        for (int i = 0; i < kRing; ++i) load_tile(i, kb[i], ksc[i]);
-    }
+    for (int i = 0; i < kRing; ++i) load_tile(i, kb[i], ksc[i]);
 
     // 2. stage the query and weights through LDS into registers
     auto qstage = [&](int c, const uint4& v) {
@@ -138,7 +182,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
     qstage(threadIdx.x + kThreads, qv1);
     if (threadIdx.x < 16) *reinterpret_cast<float4*>(ws + 4 * threadIdx.x) = wv4;
     __syncthreads();
-    if (n <= 0) return;
     fp8x8 qa[kMTiles][kSteps];
 #pragma unroll
     for (int mt = 0; mt < kMTiles; ++mt)
@@ -154,6 +197,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
 
     float* srow = a.scores + b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s;
     const long long pos = a.q_pos ? static_cast<long long>(a.q_pos[row]) : 0;
+    u64 top[kLaneTop];
+    u64 drop = 0;
+#pragma unroll
+    for (int i = 0; i < kLaneTop; ++i) top[i] = 0;
 
     // 3. stream (the same ring discipline as the bf16 scan)
     auto step = [&](int i, int j, bool refill) {
@@ -163,10 +210,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
         fp8x8 kv[kSteps];
         __builtin_memcpy(kv, kb[i], sizeof(kv));
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s)
+        for (int s2 = 0; s2 < kSteps; ++s2)
 #pragma unroll
             for (int mt = 0; mt < kMTiles; ++mt)
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa[mt][s], kv[s], acc[mt], 0, 0, 0);
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa[mt][s2], kv[s2], acc[mt], 0, 0, 0);
         const float ks = ksc[i];
         if (refill) load_tile(j + kRing, kb[i], ksc[i]);
         // accumulator register r of M tile mt <-> head 16*mt + 4*lg + r, key li
@@ -178,9 +225,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
         part += xor_lanes_f32<16>(part);
         part += xor_lanes_f32<32>(part);
         const int key = (gw + j * waves_per_row) * kTileKeys + li;
+        const bool live = j < n_mine && key < n;
         float sc = part;
         if (a.q_pos && static_cast<long long>(a.ratio) * key + a.ratio - 1 > pos) sc = -INFINITY;
-        if (j < n_mine && key < n && lg == 0) srow[key] = sc;
+        if (live && lg == 0) srow[key] = sc;
+        if (kCands) {
+            const uint32_t kk = score_key(sc);
+            const bool mine = live && lg == (i & 3) && key_valid(kk, sc);
+            lane_insert(top, drop, mine ? composite(kk, static_cast<uint32_t>(key)) : 0ull);
+        }
     };
     int j0 = 0;
     for (; j0 + 2 * kRing <= n_mine; j0 += kRing)
@@ -193,6 +246,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
     }
 #pragma unroll
     for (int i = 0; i < kRing; ++i) step(i, j0 + i, false);
+
+    if (!kCands) return;
+    // 4. this workgroup's best m and their bound to its candidate slot
+    block_top_m(top, drop, a.cands.m, a.cands.mw,
+                a.cands.lists + (static_cast<long long>(row) * a.cands.slots + wg) * (a.cands.m + 1), cs);
 }
 
 }  // namespace
@@ -206,15 +264,42 @@ hipError_t launch_quantize_fp8(const void* x, bool x_bf16, uint8_t* codes, float
     return hipGetLastError();
 }
 
-hipError_t launch_index_score_fp8(const Fp8ScoreArgs& a, hipStream_t s) {
-    const int rows = a.batch * a.t;
-    if (rows == 0 || a.n == 0) return hipSuccess;
-    const int tiles = (a.n + kTileKeys - 1) / kTileKeys;
-    int wgs = (kFp8WgsPerCu * device_cu_count() + rows - 1) / rows;
+int index_score_fp8_wgs(int rows, int n, int extra) {
+    const int tiles = (n + kTileKeys - 1) / kTileKeys;
+    int wgs = (kFp8WgsPerCu * device_cu_count() + rows - 1) / rows - extra;
     const int max_wgs = (tiles + kWaves * 4 - 1) / (kWaves * 4);  // at least 4 tiles per wave
     wgs = wgs > max_wgs ? max_wgs : wgs;
-    wgs = wgs < 1 ? 1 : wgs;
-    hipLaunchKernelGGL(k_index_score_fp8, dim3(wgs, rows), dim3(kThreads), 0, s, a, tiles);
+    return wgs < 1 ? 1 : wgs;
+}
+
+int index_score_fp8_keys_per_wg(int rows, int n, int extra) {
+    const int tiles = (n + kTileKeys - 1) / kTileKeys;
+    const int waves = index_score_fp8_wgs(rows, n, extra) * kWaves;
+    const int per_wave = (tiles + waves - 1) / waves;
+    return per_wave <= kMaxTilesPerWave ? per_wave * kWaves * kTileKeys : -1;
+}
+
+hipError_t launch_index_score_fp8(const Fp8ScoreArgs& a, const PrepArgs* fold, hipStream_t s) {
+    const int rows = a.batch * a.t;
+    if (rows == 0 || (a.n == 0 && !fold)) return hipSuccess;
+    const int tiles = (a.n + kTileKeys - 1) / kTileKeys;
+    PrepArgs p{};
+    int prep_wgs = 0;
+    if (fold) {
+        if (a.t != 1) return hipErrorInvalidValue;
+        p = *fold;
+        prep_wgs = p.completes ? 3 : 1;
+    }
+    const int wgs = index_score_fp8_wgs(rows, a.n, prep_wgs);
+    const int new_slot = fold && p.completes ? 1 : 0;
+    if (a.cands.lists && a.cands.slots == wgs + new_slot && (a.n == 0 || index_score_fp8_keys_per_wg(rows, a.n, prep_wgs) > 0))
+        hipLaunchKernelGGL(k_index_score_fp8<true>, dim3(prep_wgs + wgs, rows), dim3(kThreads), 0, s, a, tiles, p,
+                           prep_wgs);
+    else if (!a.cands.lists)
+        hipLaunchKernelGGL(k_index_score_fp8<false>, dim3(prep_wgs + wgs, rows), dim3(kThreads), 0, s, a, tiles, p,
+                           prep_wgs);
+    else
+        return hipErrorInvalidValue;  // candidate slots that do not match the grid
     return hipGetLastError();
 }
 

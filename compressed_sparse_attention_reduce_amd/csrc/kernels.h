@@ -76,8 +76,15 @@ struct Fp8ScoreArgs {
     const int* q_pos;
     int ratio;
     long long q_stride_b, w_stride_b, k_stride_b, ks_stride_b, s_stride_b, ld_s;
+    // optional top-k candidates, as in ScoreArgs
+    CandArgs cands;
 };
-hipError_t launch_index_score_fp8(const Fp8ScoreArgs& a, hipStream_t s);
+// Scan workgroups per row and keys per scan workgroup of the FP8 scan.
+int index_score_fp8_wgs(int rows, int n, int extra);
+int index_score_fp8_keys_per_wg(int rows, int n, int extra);
+// fold: as for launch_index_score_bf16 (one query row per sequence); role 2
+// quantises the new key (fold->idx_fp8) and scores it.
+hipError_t launch_index_score_fp8(const Fp8ScoreArgs& a, const PrepArgs* fold, hipStream_t s);
 
 // ---- top-k -------------------------------------------------------------------
 size_t topk_workspace_bytes(int rows, int n, int k);
@@ -170,6 +177,9 @@ constexpr int kPrepMaxD = 4096;
 struct PrepArgs {
     int batch, es, d, d_i, m, overlap, completes, n_comp;
     int main_wgs;  // > 1: the main block is compressed in that many channel slices (roles 1 .. main_wgs)
+    int idx_fp8;   // the indexer keys are E4M3 codes with per-row scales (role 2 quantises the new key)
+    float* idx_scales;
+    long long idx_scales_stride_b;
     long long block;
     const void* kv_new;
     long long kv_new_stride_b;

@@ -10,12 +10,15 @@
 #pragma once
 
 #include "compress_impl.h"
+#include "fp8_codec.h"
 #include "kernels.h"
 
 namespace csa {
 
 // ybuf: kPrepMaxD floats of LDS; red: blockDim/64 floats of LDS.  key (LDS,
-// may be ybuf): role 2 leaves the stored key there as floats (synchronised).
+// may be ybuf): role 2 leaves the stored key there as floats (synchronised);
+// with E4M3 keys (idx_fp8) key must be d_i + 1 floats apart from ybuf, and
+// holds the decoded codes then the row scale.
 __device__ inline void step_prep_role(const PrepArgs& a, int role, int b, float* ybuf, float* red,
                                       float* key = nullptr) {
     if (role == 0) {
@@ -38,6 +41,38 @@ __device__ inline void step_prep_role(const PrepArgs& a, int role, int b, float*
     }
     const bool main = role == 1;
     if (!main && !a.idx_keys) return;  // a layer without an indexer (HCA)
+    if (!main && a.idx_fp8) {
+        // E4M3 indexer keys: the key in float32 (in `key`), quantised like
+        // csa_quantize_fp8 (scale = max|y| / 448, 1 for a zero row, codes by
+        // round to nearest even of y / scale); `key` is left holding the
+        // decoded codes and key[a.d_i] the scale (synchronised)
+        const float* z = a.z_idx + b * a.zc_idx_stride_b;
+        const float* c = a.c_idx + b * a.zc_idx_stride_b;
+        compress_block(z, c, a.idx_bias, a.idx_norm, key, false, a.m, a.d_i, a.overlap != 0, a.block, ybuf, red);
+        __syncthreads();
+        float amax = 0.f;
+        for (int j = threadIdx.x; j < a.d_i; j += blockDim.x) amax = fmaxf(amax, fabsf(key[j]));
+        amax = wave_max(amax);
+        if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = amax;
+        __syncthreads();
+        amax = 0.f;
+        for (int w = 0; w < static_cast<int>(blockDim.x / kWave); ++w) amax = fmaxf(amax, red[w]);
+        const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+        uint8_t* codes = static_cast<uint8_t*>(a.idx_keys) + b * a.idx_keys_stride_b +
+                         static_cast<long long>(a.n_comp) * a.d_i;
+        __syncthreads();  // every thread has read red
+        for (int j = threadIdx.x; j < a.d_i; j += blockDim.x) {
+            const uint8_t q = e4m3_encode_rne(key[j] / scale);
+            codes[j] = q;
+            key[j] = e4m3_decode(q);
+        }
+        if (threadIdx.x == 0) {
+            a.idx_scales[b * a.idx_scales_stride_b + a.n_comp] = scale;
+            key[a.d_i] = scale;
+        }
+        __syncthreads();
+        return;
+    }
     const int d = main ? a.d : a.d_i;
     const float* z = (main ? a.z_main : a.z_idx) + b * (main ? a.zc_main_stride_b : a.zc_idx_stride_b);
     const float* c = (main ? a.c_main : a.c_idx) + b * (main ? a.zc_main_stride_b : a.zc_idx_stride_b);

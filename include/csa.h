@@ -252,6 +252,10 @@ int csa_sparse_attn(const void *q, const void *kv, const int *n_valid, const flo
  *      idx_keys[n_comp] = compress(z_idx, c_idx) (overlap convention as in
  *      csa_compress, with first_block = pos / m);
  *   c. scores over the N = n_comp (+1 if b ran) keys, top-k, gather, attention.
+ * With E4M3 indexer keys (idx_dtype = CSA_FP8_E4M3; bfloat16 caches, h_i = 64,
+ * d_i = 128) step b stores the compressed key as csa_quantize_fp8 would
+ * (codes into idx_keys[n_comp], its scale into idx_scales[n_comp]) and step c
+ * scores as csa_index_score_fp8 does.
  * It does NOT update the host integers: afterwards the caller sets
  * swa_head = (swa_head + 1) % w, swa_len = min(swa_len + 1, w) and, if a block
  * completed, n_comp += 1 (csa_layer_advance does exactly this).
@@ -279,6 +283,14 @@ typedef struct csa_layer_desc {
     int n_comp;             /* compressed entries before this step */
     int swa_head;           /* next SWA write slot */
     int swa_len;            /* live SWA rows */
+    /* E4M3 indexer keys (section 2b; appended, so a zero-filled descriptor
+     * keeps keys of `dtype`): idx_dtype = CSA_FP8_E4M3 makes idx_keys
+     * [B][max_comp][d_i] uint8 codes (idx_keys_stride_b in bytes) with row
+     * scales idx_scales [B][max_comp] float32 (stride idx_scales_stride_b),
+     * and q_idx [B][h_i][d_i] E4M3 codes whose per-head scales the caller has
+     * folded into w_idx.  Any other value: keys stored as `dtype`. */
+    csa_dtype idx_dtype;
+    float *idx_scales; long long idx_scales_stride_b;
 } csa_layer_desc;
 
 typedef struct csa_step_io {

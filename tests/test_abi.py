@@ -260,6 +260,33 @@ def test_decode_step_validation_and_advance(csa):
         csa.csa_layer_advance(L4, 3)
 
 
+def test_decode_step_fp8_keys_validation(csa):
+    """E4M3 indexer keys: bfloat16 caches, 64 x 128 indexer, row scales given."""
+    B = csa.binding
+    lib = csa.lib()
+    L = _desc(csa, idx_dtype=csa.CSA_FP8_E4M3)
+    need = csa.csa_decode_step_workspace_size(L)
+    io = _io(csa, pos=3999)
+
+    def call(layer):
+        return lib.csa_decode_step(ctypes.byref(layer), ctypes.byref(io), FAKE, need, None)
+
+    assert call(L) == B.CSA_ERR_INVALID_ARG      # idx_scales missing
+    assert "null" in csa.csa_last_error()
+    L.idx_scales = FAKE
+    L.h_i = 32
+    assert call(L) == B.CSA_ERR_UNSUPPORTED
+    L.h_i = 64
+    L.dtype = csa.CSA_F32
+    assert call(L) == B.CSA_ERR_UNSUPPORTED
+    assert "bfloat16" in csa.csa_last_error()
+    L.dtype = csa.CSA_BF16
+    L.idx_scales_stride_b = -1
+    assert call(L) == B.CSA_ERR_INVALID_ARG
+    # a zero-filled descriptor keeps keys of the cache dtype
+    assert _desc(csa).idx_dtype == csa.CSA_F32 and _desc(csa).idx_scales is None
+
+
 def test_hca_step_validation(csa):
     B = csa.binding
     L = B.LayerDesc()

@@ -684,6 +684,155 @@ def test_decode_steps_in_sequence(csa):
         assert rel_err(host_f64(outs["out"][0]), ro) <= 2e-2
 
 
+def _assert_e4m3_key_close(codes, scale, y):
+    """A GPU-quantised key row (codes, scale) against the oracle's float64
+    compressed key y: the scale within 1e-5 of max|y| / 448 and every element
+    within half an E4M3 unit in the last place plus the float32 slack of the
+    compressor (the two sides may round a boundary case differently)."""
+    y = np.asarray(y, dtype=np.float64)
+    assert scale == pytest.approx(np.abs(y).max() / 448, rel=1e-5)
+    dec = numfmt.e4m3_decode(codes) * scale
+    bound = np.maximum(np.abs(y) * 2.0 ** -4, scale * 2.0 ** -10) + 1e-5 * np.abs(y).max()
+    assert (np.abs(dec - y) <= bound).all()
+
+
+def _fp8_query(qi, wi):
+    """E4M3 query codes and head weights with the query's per-head scales folded in."""
+    qc, qs = numfmt.quantize_e4m3_rows(qi.reshape(-1, qi.shape[-1]))
+    return qc.reshape(qi.shape), (wi * qs.reshape(wi.shape)).astype(np.float32)
+
+
+def test_decode_steps_in_sequence_fp8_keys(csa):
+    """Nine consecutive steps over E4M3 indexer keys (two block completions,
+    ring wrap): each new key quantised on the GPU within E4M3 rounding of the
+    oracle's, then adopted; scores against the oracle's FP8 score on the
+    cache as the GPU holds it, top-k, gather and attention as for bf16 keys."""
+    shape = synth.with_(synth.SHAPES["ctx8k"], ctx=600, n_comp=150, top_k=64, w=8)
+    x = synth.make_decode_inputs(shape, 4101, max_comp=200)
+    g = _g(4102)
+    dt = torch.bfloat16
+    f = numfmt.bf16_bits_to_f64
+    kc0, ks0 = numfmt.quantize_e4m3_rows(f(x["idx_keys"][0]).astype(np.float32))
+    comp = dev_bf16(x["comp_kv"]); swa = dev_bf16(x["swa"])
+    kc = torch.from_numpy(kc0[None].copy()).to(DEV)
+    ks = dev_f32(ks0[None])
+    mb, ib, sink = dev_f32(x["main_bias"]), dev_f32(x["idx_bias"]), dev_f32(x["sink"])
+    L = csa.make_layer_desc(comp_kv=comp, idx_keys=kc, idx_scales=ks, swa=swa, main_bias=mb, idx_bias=ib,
+                            sink=sink, n_comp=x["n_comp"], swa_head=x["swa_head"], swa_len=x["swa_len"], h=64,
+                            h_i=64, top_k=64)
+    assert L.idx_dtype == csa.CSA_FP8_E4M3
+    ost = oracle.LayerState(comp_kv=f(x["comp_kv"][0]), idx_keys=np.zeros((200, 128)), n_comp=x["n_comp"],
+                            swa=oracle.SwaRing(f(x["swa"][0]), x["swa_head"], x["swa_len"]),
+                            main_bias=x["main_bias"], idx_bias=x["idx_bias"], sink=x["sink"],
+                            round_cache=numfmt.bf16_round_f64, idx_codes=kc0.copy(), idx_scales=ks0.copy())
+    ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+    for pos in range(x["pos"], x["pos"] + 9):
+        q = synth.to_bf16_bits(g.standard_normal((1, 64, 512), dtype=np.float32))
+        qc, w8 = _fp8_query(g.standard_normal((1, 64, 128), dtype=np.float32) / np.float32(np.sqrt(128)),
+                            g.standard_normal((1, 64), dtype=np.float32))
+        kvn = synth.to_bf16_bits(g.standard_normal((1, 512), dtype=np.float32))
+        zm, cm = g.standard_normal((2, 1, 4, 512), dtype=np.float32)
+        zi, ci = g.standard_normal((2, 1, 4, 128), dtype=np.float32)
+        outs = dict(scores=torch.empty(1, 200, device=DEV), topk_idx=torch.empty(1, 64, dtype=torch.int32, device=DEV),
+                    topk_count=torch.empty(1, dtype=torch.int32, device=DEV),
+                    gather_buf=torch.zeros(1, 72, 512, dtype=dt, device=DEV),
+                    n_valid=torch.empty(1, dtype=torch.int32, device=DEV),
+                    out=torch.empty(1, 64, 512, dtype=dt, device=DEV))
+        io = csa.make_step_io(pos=pos, q=dev_bf16(q), q_idx=torch.from_numpy(qc).to(DEV), w_idx=dev_f32(w8),
+                              kv_new=dev_bf16(kvn), z_main=dev_f32(zm), c_main=dev_f32(cm), z_idx=dev_f32(zi),
+                              c_idx=dev_f32(ci), **outs)
+        print(f"fp8-key step pos={pos}", flush=True)
+        csa.csa_decode_step(L, io, ws)
+        csa.csa_layer_advance(L, pos)
+        torch.cuda.synchronize()
+        completes = pos % 4 == 3
+        n0 = ost.n_comp
+        oracle.decode_step(ost, q=f(q[0]), q_idx=qc[0], w_idx=w8[0], kv_new=f(kvn[0]), pos=pos, top_k=64,
+                           z_main=zm[0], c_main=cm[0], z_idx=zi[0], c_idx=ci[0], scale=1 / np.sqrt(512))
+        assert (L.n_comp, L.swa_head, L.swa_len) == (ost.n_comp, ost.swa.head, ost.swa.length)
+        N = ost.n_comp
+        gkc, gks = kc[0].cpu().numpy(), ks[0].cpu().numpy()
+        np.testing.assert_array_equal(gkc[:n0], ost.idx_codes[:n0])   # older keys untouched
+        if completes:  # the new entry and key close to the oracle's, then adopt the GPU's
+            assert_bf16_close(host_bits(comp[0, n0]), oracle.compress(zm[0], cm[0], x["main_bias"], 4)[0])
+            _assert_e4m3_key_close(gkc[n0], float(gks[n0]), oracle.compress(zi[0], ci[0], x["idx_bias"], 4)[0])
+        ost.comp_kv[:N] = host_f64(comp[0, :N])
+        ost.idx_codes[:N], ost.idx_scales[:N] = gkc[:N], gks[:N]
+        ref_s = oracle.index_score_fp8(qc, w8, ost.idx_codes[:N], ost.idx_scales[:N])[0]
+        got_s = outs["scores"][0, :N].cpu().numpy().astype(np.float64)
+        assert rel_err(got_s, ref_s) <= 1e-4
+        gi, gc = outs["topk_idx"][0].cpu().numpy(), int(outs["topk_count"][0])
+        np.testing.assert_array_equal(gi, oracle.topk(got_s[None], 64)[0][0])
+        assert_topk_gap_rule(gi, gc, ref_s, 64)
+        rows, n_valid = oracle.gather(ost.comp_kv[:N], gi, gc, ost.swa.rows, ost.swa.head, ost.swa.length)
+        assert int(outs["n_valid"][0]) == n_valid
+        np.testing.assert_array_equal(host_f64(outs["gather_buf"][0, :n_valid]), rows)
+        ro, _ = oracle.sparse_attn(f(q[0]), rows, x["sink"], 1 / np.sqrt(512))
+        assert rel_err(host_f64(outs["out"][0]), ro) <= 2e-2
+
+
+def test_decode_step_ctx1m_fp8_keys_full_size(csa):
+    """One layer of the 1M-context workload with E4M3 indexer keys (the cache
+    quantised on the GPU from the bf16 keys): the new key within E4M3 rounding
+    of the oracle's, every score against the oracle's FP8 score, the top-k
+    exact on the GPU's scores and by the gap rule on the oracle's, gather and
+    attention as for bf16 keys."""
+    shape = synth.SHAPES["ctx1m"]
+    x = synth.make_decode_inputs_torch(shape, seed=None, device=DEV, layers=1)[0]
+    B, K, W, D = shape.batch, shape.top_k, shape.w, shape.d
+    n0 = x["n_comp"]
+    kc = torch.zeros(B, shape.max_comp, 128, dtype=torch.uint8, device=DEV)
+    ks = torch.zeros(B, shape.max_comp, dtype=torch.float32, device=DEV)
+    csa.csa_quantize_fp8(x["idx_keys"][:, :n0].contiguous(), kc[:, :n0], ks[:, :n0])
+    q = x["q_idx"].contiguous()                        # [1, 64, 128] bf16
+    qc = torch.empty(1, 64, 128, dtype=torch.uint8, device=DEV)
+    qs = torch.empty(1, 64, dtype=torch.float32, device=DEV)
+    csa.csa_quantize_fp8(q, qc, qs)
+    w8 = (x["w_idx"] * qs).contiguous()
+    torch.cuda.synchronize()
+    pristine = kc[0, :n0].clone()
+    L = csa.make_layer_desc(comp_kv=x["comp_kv"], idx_keys=kc, idx_scales=ks, swa=x["swa"],
+                            main_bias=x["main_bias"], idx_bias=x["idx_bias"], sink=x["sink"],
+                            n_comp=n0, swa_head=x["swa_head"], swa_len=x["swa_len"], h=shape.h,
+                            h_i=shape.h_i, top_k=K)
+    outs = dict(scores=torch.empty(B, shape.max_comp, device=DEV),
+                topk_idx=torch.empty(B, K, dtype=torch.int32, device=DEV),
+                topk_count=torch.empty(B, dtype=torch.int32, device=DEV),
+                gather_buf=torch.zeros(B, K + W, D, dtype=torch.bfloat16, device=DEV),
+                n_valid=torch.empty(B, dtype=torch.int32, device=DEV),
+                out=torch.empty(B, shape.h, D, dtype=torch.bfloat16, device=DEV),
+                lse=torch.empty(B, shape.h, device=DEV))
+    io = csa.make_step_io(pos=x["pos"], q=x["q"], q_idx=qc, w_idx=w8, kv_new=x["kv_new"],
+                          z_main=x["z_main"], c_main=x["c_main"], z_idx=x["z_idx"], c_idx=x["c_idx"], **outs)
+    ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+    csa.csa_decode_step(L, io, ws)
+    torch.cuda.synchronize()
+    N = shape.n_comp
+    assert N == n0 + 1
+    assert torch.equal(kc[0, :n0], pristine)
+    yi = oracle.compress(x["z_idx"][0].cpu().numpy(), x["c_idx"][0].cpu().numpy(),
+                         x["idx_bias"].cpu().numpy(), 4)[-1]
+    codes, scales = kc[0, :N].cpu().numpy(), ks[0, :N].cpu().numpy()
+    _assert_e4m3_key_close(codes[n0], float(scales[n0]), yi)
+    ref_s = oracle.index_score_fp8(qc.cpu().numpy(), w8.cpu().numpy(), codes, scales)[0]
+    got_s = outs["scores"][0, :N].cpu().numpy().astype(np.float64)
+    assert rel_err(got_s, ref_s) <= 1e-4
+    gi = outs["topk_idx"][0].cpu().numpy()
+    oi, _ = oracle.topk(got_s[None], K)
+    np.testing.assert_array_equal(gi, oi[0])
+    assert_topk_gap_rule(gi, int(outs["topk_count"][0]), ref_s, K)
+    sel = host_f64(x["comp_kv"][0, torch.from_numpy(gi).to(DEV).long()])
+    swa_rows = host_f64(x["swa"][0])
+    head = (x["swa_head"] + 1) % W
+    win = np.stack([swa_rows[(head - W + j) % W] for j in range(W)])
+    rows = np.concatenate([sel, win])
+    assert int(outs["n_valid"][0]) == K + W
+    np.testing.assert_array_equal(host_f64(outs["gather_buf"][0]), rows)
+    ro, rl = oracle.sparse_attn(host_f64(x["q"][0]), rows, host_f64(x["sink"]), 1.0 / np.sqrt(D))
+    assert rel_err(host_f64(outs["out"][0]), ro) <= 2e-2
+    assert np.abs(outs["lse"][0].cpu().numpy() - rl).max() <= 1e-2
+
+
 # ---------------------------------------------------------------------------
 # 6b. HCA layer step (ratio-m compressor, attention over every entry + window)
 # ---------------------------------------------------------------------------
