@@ -109,7 +109,8 @@ def time_scan_kernel(csa, layers, shape, reps: int):
     return e0.elapsed_time(e1) / n, n
 
 
-SCAN_SOURCES = ["index_score.hip", "common.h", "kernels.h", "topk_common.h", "step_prep.h", "compress_impl.h"]
+SCAN_SOURCES = ["index_score.hip", "common.h", "kernels.h", "topk_common.h", "step_prep.h", "compress_impl.h",
+                "score_tile.h", "fp8_codec.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_index_score_bf16_ctx1m_hbm_traffic.md")
 
 
