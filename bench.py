@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 matrix peak, TFLOP/s
 
 
 def algorithmic_bytes(shape) -> dict:
@@ -267,6 +268,37 @@ def time_prefill(csa, reps: int):
     flop = 2.0 * rows * 64 * 128 * N
     tflops = flop / (score_us * 1e-6) / 1e12
     attn_flop = 4.0 * T * shape.h * (k + W) * shape.d
+
+    # the E4M3-key variant: keys and queries quantised once (per key row, per
+    # query head row; the query scales folded into w), outside the timed region
+    kc = torch.empty(N, 128, dtype=torch.uint8, device="cuda")
+    ks = torch.empty(N, dtype=torch.float32, device="cuda")
+    csa.csa_quantize_fp8(x["idx_keys"], kc, ks)
+    qc = torch.empty(T, 64, 128, dtype=torch.uint8, device="cuda")
+    qs = torch.empty(T, 64, dtype=torch.float32, device="cuda")
+    csa.csa_quantize_fp8(x["q_idx"], qc, qs)
+    w8 = (x["w_idx"] * qs).contiguous()
+    torch.cuda.synchronize()
+
+    def topk8():
+        csa.csa_index_topk_fp8(qc, w8, kc, ks, idx, cnt, ws, pos0=x["pos0"])
+
+    topk8_ms = timed(topk8, reps)
+    g8 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g8, stream=stream):
+            for r0 in range(0, T, rows):
+                csa.csa_index_score_fp8(qc[None, r0:r0 + rows], w8[None, r0:r0 + rows], kc[None], ks[None], sc,
+                                        q_pos=pos[:, r0:r0 + rows], stream=stream)
+        g8.replay()
+        stream.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            g8.replay()
+        e1.record(stream)
+    stream.synchronize()
+    score8_us = e0.elapsed_time(e1) * 1e3 / launches
+    tflops8 = flop / (score8_us * 1e-6) / 1e12
     return {
         "workload": "prefill chunk: 2048 queries at positions 260096..262143 against 65536 compressed "
                     "blocks (causal), indexer 64x128 bf16, top_k 512, main attention 64 heads x 512 bf16 "
@@ -286,6 +318,21 @@ def time_prefill(csa, reps: int):
             "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
         },
         "attn_tflops": round(attn_flop / (attn_ms * 1e-3) / 1e12, 1),
+        "fp8_keys": {
+            "index_topk_ms": round(topk8_ms, 4),
+            "chunk_ms": round(topk8_ms + attn_ms, 4),
+            "queries_per_s": round(T / ((topk8_ms + attn_ms) * 1e-3), 1),
+            "score_kernel": {
+                "kernel": "k_index_score_mq_fp8",
+                "bound": "mfma",
+                "rows_per_launch": rows,
+                "avg_launch_us": round(score8_us, 2),
+                "achieved": round(tflops8, 1),
+                "peak": FP8_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(tflops8 / FP8_MFMA_PEAK_TFLOPS, 4),
+            },
+        },
     }
 
 

@@ -94,6 +94,7 @@ _SIGS = {
     "csa_hca_decode_step": (_i, [ctypes.POINTER(LayerDesc), ctypes.POINTER(StepIO), _vp, _sz, _vp]),
     "csa_index_topk_workspace_size": (_sz, [_i, _i, _i]),
     "csa_index_topk": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _ll, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "csa_index_topk_fp8": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _ll, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "csa_prefill_attn": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _ll, _vp, _f, _vp, _i, _vp, _i, _i, _i,
                               _vp]),
 }
@@ -354,6 +355,23 @@ def csa_index_topk(q, w, k, idx, count, ws, pos0: int = -1, ratio: int = 4, n: O
     n = k.shape[0] if n is None else n
     _check(lib().csa_index_topk(_ptr(q), _ptr(w), _ptr(k), t, h_i, d_i, n, pos0, ratio, idx.shape[1], _ptr(idx),
                                 _ptr(count), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def csa_index_topk_fp8(q, w, k, k_scale, idx, count, ws, pos0: int = -1, ratio: int = 4,
+                       n: Optional[int] = None, stream=None) -> None:
+    """q [t, 64, 128] uint8 E4M3; w [t, 64] float32 (query scales folded in);
+    k [N, 128] uint8 E4M3 and k_scale [N] float32 (first n rows); idx, count,
+    pos0 as for csa_index_topk."""
+    for t_, nm in ((q, "q"), (w, "w"), (k, "k"), (k_scale, "k_scale"), (idx, "idx")):
+        if not t_.is_contiguous():
+            raise ValueError(f"{nm}: must be contiguous")
+    if q.dtype != torch.uint8 or k.dtype != torch.uint8 or k_scale.dtype != torch.float32:
+        raise TypeError("q and k must hold uint8 E4M3 codes, k_scale float32")
+    t, h_i, d_i = q.shape
+    n = k.shape[0] if n is None else n
+    _check(lib().csa_index_topk_fp8(_ptr(q), _ptr(w), _ptr(k), _ptr(k_scale), t, h_i, d_i, n, pos0, ratio,
+                                    idx.shape[1], _ptr(idx), _ptr(count), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)))
 
 
 def csa_prefill_attn(q, comp_kv, idx, count, win_kv, window: int, pos0: int, sink, scale: float, out,

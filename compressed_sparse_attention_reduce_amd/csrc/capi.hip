@@ -171,7 +171,10 @@ int csa_index_score_fp8(const unsigned char* q, const float* w, const unsigned c
     if (rc != CSA_OK) return rc;
     csa::Fp8ScoreArgs a{q, w, k, k_scale, scores, batch, t, n, q_pos, ratio,
                         q_stride_b, w_stride_b, k_stride_b, ks_stride_b, s_stride_b, ld_s, csa::CandArgs{nullptr, 0, 0, 0}};
-    return launched(csa::launch_index_score_fp8(a, nullptr, static_cast<hipStream_t>(stream)), "csa_index_score_fp8");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (t >= csa::kMqMinRows)
+        return launched(csa::launch_index_score_mq_fp8(a, -1, s), "csa_index_score_fp8");
+    return launched(csa::launch_index_score_fp8(a, nullptr, s), "csa_index_score_fp8");
 }
 
 size_t csa_topk_workspace_size(int batch, int t, int n, int k) {
@@ -624,6 +627,39 @@ int csa_index_topk(const void* q, const float* w, const void* k, int t, int h_i,
     csa::IndexTopkArgs a{static_cast<const uint16_t*>(q), w, static_cast<const uint16_t*>(k), t, n, pos0, ratio,
                          top_k, idx, count, ws};
     return launched(csa::launch_index_topk(a, static_cast<hipStream_t>(stream)), "csa_index_topk");
+}
+
+int csa_index_topk_fp8(const unsigned char* q, const float* w, const unsigned char* k, const float* k_scale, int t,
+                       int h_i, int d_i, int n, long long pos0, int ratio, int top_k, int* idx, int* count,
+                       void* ws, size_t ws_bytes, csa_stream stream) {
+    CHECK(q && w && idx && ws && ((k && k_scale) || n == 0), "csa_index_topk_fp8: null pointer argument");
+    CHECK(t >= 1 && n >= 0, "csa_index_topk_fp8: t %d n %d", t, n);
+    CHECK(ratio >= 1, "csa_index_topk_fp8: ratio %d", ratio);
+    CHECK(top_k >= 1 && top_k <= csa::kTopkMaxK, "csa_index_topk_fp8: top_k=%d out of 1..%d", top_k,
+          csa::kTopkMaxK);
+    if (h_i != 64 || d_i != 128)
+        return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk_fp8: needs h_i=64, d_i=128 (got %d, %d)", h_i, d_i);
+    CHECK(aligned16(q) && aligned16(w) && aligned16(ws) && (n == 0 || aligned16(k)),
+          "csa_index_topk_fp8: q, w, k and ws must be 16-byte aligned");
+    if (ws_bytes < csa_index_topk_workspace_size(t, n, top_k))
+        return fail(CSA_ERR_WORKSPACE, "csa_index_topk_fp8: workspace %zu < %zu bytes", ws_bytes,
+                    csa_index_topk_workspace_size(t, n, top_k));
+    csa::IndexTopkArgs a{};
+    a.w = w;
+    a.t = t;
+    a.n = n;
+    a.pos0 = pos0;
+    a.ratio = ratio;
+    a.top_k = top_k;
+    a.idx = idx;
+    a.count = count;
+    a.ws = ws;
+    a.q8 = q;
+    a.k8 = k;
+    // a non-null scale pointer selects the E4M3 scan (no key is read when n = 0)
+    static const float kNoKeys = 1.f;
+    a.k_scale = n > 0 ? k_scale : &kNoKeys;
+    return launched(csa::launch_index_topk(a, static_cast<hipStream_t>(stream)), "csa_index_topk_fp8");
 }
 
 int csa_prefill_attn(const void* q, const void* comp_kv, int n_comp, const int* idx, const int* count, int k,

@@ -158,6 +158,34 @@ __device__ inline void compress_block_slice(const float* __restrict__ z, const f
     part[blockDim.x + threadIdx.x] = den;
     part[2 * blockDim.x + threadIdx.x] = acc;
     __syncthreads();
+    if ((slices & (slices - 1)) == 0 && slices <= kWave && slices * nch == static_cast<int>(blockDim.x)) {
+        // one thread per (channel, slice), a channel's slices in consecutive
+        // lanes: the slices' (max, sum, weighted sum) merged by lane swaps
+        const int tc = threadIdx.x / slices;
+        const int s2 = threadIdx.x % slices;
+        float m2 = part[s2 * nch + tc];
+        float d2 = part[blockDim.x + s2 * nch + tc];
+        float a2 = part[2 * blockDim.x + s2 * nch + tc];
+        for (int off = 1; off < slices; off <<= 1) {
+            const float mo = __shfl_xor(m2, off);
+            const float dn = __shfl_xor(d2, off);
+            const float ao = __shfl_xor(a2, off);
+            const float M = fmaxf(m2, mo);
+            const float f1 = m2 == -INFINITY ? 0.f : expf(m2 - M);  // an empty slice adds nothing
+            const float f2 = mo == -INFINITY ? 0.f : expf(mo - M);
+            d2 = d2 * f1 + dn * f2;
+            a2 = a2 * f1 + ao * f2;
+            m2 = M;
+        }
+        if (s2 == 0 && ch0 + tc < d) {
+            const float y = a2 / d2;
+            if (out_bf16)
+                static_cast<uint16_t*>(out_row)[ch0 + tc] = f32_to_bf16(y);
+            else
+                static_cast<float*>(out_row)[ch0 + tc] = y;
+        }
+        return;
+    }
     if (sl == 0 && ch < d) {
         float M = -INFINITY;
         for (int s2 = 0; s2 < slices; ++s2) M = fmaxf(M, part[s2 * nch + t]);

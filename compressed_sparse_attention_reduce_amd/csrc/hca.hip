@@ -10,10 +10,13 @@
 // at once (one round of loads, eight waves: one 16-row tile of S = q K^T
 // each, then four 16-column tiles of O = P V each, both on
 // v_mfma_f32_16x16x32_bf16), so the partials are a quarter of the row bytes
-// and the merge (k_attn_merge, shared with the sparse path) reads a quarter
-// of the splits.  The four head groups of a split run on one XCD
-// (consecutive workgroup ids go to consecutive XCDs), so the rows come from
-// HBM once and from that XCD's L2 for the other three groups.
+// of 32-row splits, and k_attn_merge_rows merges them.  The four head groups
+// of a split run on one XCD (consecutive workgroup ids go to consecutive
+// XCDs), so the rows come from HBM once and from that XCD's L2 for the other
+// three groups.  One workgroup per split and head group and nothing else
+// (the step's SWA append aside), so that every workgroup is resident at
+// once: a ratio-m block the step completes is compressed by the attention
+// workgroups themselves, a slice of channels each.
 #include "attn_split.h"
 #include "common.h"
 #include "kernels.h"
@@ -30,6 +33,9 @@ constexpr int kDensePPitch = kDenseRows + 8;          // LDS pitch of the probab
 constexpr int kDenseMaxD = 512;
 constexpr int kDenseQPer = kHeadGroup * kDenseMaxD / 8 / kDenseThreads;  // query pieces per thread
 constexpr int kDenseRowPer = kDenseRows * kDenseMaxD / 8 / kDenseThreads; // row pieces per thread
+// channels of a folded block compression per workgroup, at least: 32 row
+// slices of 4 rows each for a 128-row block, merged by 16 threads
+constexpr int kFoldMinCh = 16;
 
 __host__ __device__ inline size_t dense_lds_bytes(int d) {
     return sizeof(uint16_t) * (static_cast<size_t>(kDenseRows + kHeadGroup) * (d + 8) +
@@ -37,7 +43,7 @@ __host__ __device__ inline size_t dense_lds_bytes(int d) {
 }
 
 __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, int n_splits, int prep_wgs, PrepArgs p,
-                                                                    int extra_rows) {
+                                                                    int extra_rows, int fold_ch) {
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     __shared__ float wmax[kDenseWaves][kHeadGroup];
     __shared__ float wsum[kDenseWaves][kHeadGroup];
@@ -51,14 +57,33 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
         return;
     }
     const int groups = a.h / kHeadGroup;
-    // workgroup id -> (split, head group): id % 8 = split % 8, so a split's
-    // head groups share an XCD
+    // workgroup id -> (split, head group): over the first 8 * (n_splits / 8)
+    // splits id % 8 = split % 8, so a split's head groups share an XCD; the
+    // remaining splits follow one after another
     const int id = blockIdx.x - prep_wgs;
-    const int rest = id / 8;
-    const int hg = rest % groups;
-    const int split = id % 8 + 8 * (rest / groups);
+    const int n_full = n_splits / 8 * 8;
+    int split, hg;
+    if (id < n_full * groups) {
+        const int rest = id / 8;
+        hg = rest % groups;
+        split = id % 8 + 8 * (rest / groups);
+    } else {
+        split = n_full + (id - n_full * groups) / groups;
+        hg = (id - n_full * groups) % groups;
+    }
     const int b = blockIdx.y;
-    if (split >= n_splits) return;  // padding of the grid: never merged
+    // A block this step completes is compressed here, fold_ch channels per
+    // workgroup by the first ones (ratio-m blocks are long: one workgroup
+    // alone would take longer than the attention).  Its rows are independent
+    // of the attention's, which covers the entries before the step only.
+    const bool fold = fold_ch > 0 && id * fold_ch < p.d;  // uniform
+    auto fold_block = [&](float* scratch) {
+        const float* z = p.z_main + b * p.zc_main_stride_b;
+        const float* c = p.c_main + b * p.zc_main_stride_b;
+        char* out = static_cast<char*>(p.comp_kv) + (b * p.comp_kv_stride_b + static_cast<long long>(p.n_comp) * p.d) * p.es;
+        const int ch0 = id * fold_ch;
+        compress_block_slice(z, c, p.main_bias, out, p.es == 2, p.m, p.d, ch0, min(fold_ch, p.d - ch0), scratch);
+    };
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const int li = lane & 15;
@@ -81,6 +106,7 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
             a.ws_ml[2 * (ml_base + static_cast<long long>(threadIdx.x) * n_splits) + 0] = -INFINITY;
             a.ws_ml[2 * (ml_base + static_cast<long long>(threadIdx.x) * n_splits) + 1] = 0.f;
         }
+        if (fold) fold_block(reinterpret_cast<float*>(smem));
         return;
     }
     // 1. query group and the split's rows to LDS, all loads in one batch
@@ -110,6 +136,11 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
             }
         }
         v[u] = src ? *reinterpret_cast<const uint4*>(src + (c % cpr) * 8) : make_uint4(0, 0, 0, 0);
+    }
+    // the block's channels while the rows are in flight (LDS as scratch first)
+    if (fold) {
+        fold_block(reinterpret_cast<float*>(smem));
+        __syncthreads();
     }
 #pragma unroll
     for (int u = 0; u < kDenseQPer; ++u) {
@@ -206,99 +237,125 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
 
 // Merge of the splits plus the step's new rows (the compressed entry of a
 // completed block, x0, if any; the new token's KV row, x1), one workgroup per
-// (head, sequence): M = max of the splits' maxima, the new rows' logits and
-// the sink; out = (sum_s e^(m_s - M) O_s + sum_i e^(s_i - M) x_i) / den with
-// den = sum_s e^(m_s - M) l_s + sum_i e^(s_i - M) + e^(sink - M).  At most
-// 64 splits (lane s of every wave holds split s's (m, l)).
+// (head, 128 columns, sequence): M = max of the splits' maxima, the new rows'
+// logits and the sink; out = (sum_s e^(m_s - M) O_s + sum_i e^(s_i - M) x_i)
+// / den with den = sum_s e^(m_s - M) l_s + sum_i e^(s_i - M) + e^(sink - M).
+// At most 64 splits (lane s of every wave holds split s's (m, l)).  Wave w
+// sums splits w, w + 4, ... for its 64 column pairs; the four partial sums
+// meet in LDS.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeWaves = kMergeThreads / kWave;
+constexpr int kMergeCols = 2 * kWave;  // columns per workgroup: a column pair per lane
 __global__ __launch_bounds__(kMergeThreads) void k_attn_merge_rows(AttnArgs a, int n_splits, const uint16_t* x0,
                                                                    long long x0_stride_b, const uint16_t* x1,
                                                                    long long x1_stride_b) {
-    __shared__ float red[2][kMergeThreads / kWave];
-    const int hh = blockIdx.x;
+    __shared__ float red[2][kMergeWaves];
+    __shared__ float2 part[kMergeWaves][kWave];
+    const int d = a.d;
+    const int col_blocks = (d + kMergeCols - 1) / kMergeCols;
+    const int hh = blockIdx.x / col_blocks;
+    const int cb = blockIdx.x % col_blocks;
     const int b = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
-    const int d = a.d;
     const long long base = (static_cast<long long>(b) * a.h + hh) * n_splits;
     const float* ob = a.ws_o + base * d;
-    const int col = 2 * threadIdx.x;
-    const bool has_col = col < d;
-    // the new rows' logits: q . x_i over the block, two sums at once
+    // the new rows' logits: q . x_i over the whole head, two sums at once
+    // (d <= 2 * kMergeThreads)
     const uint16_t* qh = a.q + b * a.q_stride_b + static_cast<long long>(hh) * d;
-    float q0 = 0.f, q1 = 0.f, a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
-    if (has_col) {
-        const uint32_t qq = *reinterpret_cast<const uint32_t*>(qh + col);
-        q0 = __uint_as_float(qq << 16);
-        q1 = __uint_as_float(qq & 0xffff0000u);
-        if (x0) {
-            const uint32_t xx = *reinterpret_cast<const uint32_t*>(x0 + b * x0_stride_b + col);
-            a0 = __uint_as_float(xx << 16);
-            a1 = __uint_as_float(xx & 0xffff0000u);
+    const uint16_t* x0b = x0 ? x0 + b * x0_stride_b : nullptr;
+    const uint16_t* x1b = x1 + b * x1_stride_b;
+    auto pair = [](const uint16_t* p, int c, float& lo, float& hi) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(p + c);
+        lo = __uint_as_float(v << 16);
+        hi = __uint_as_float(v & 0xffff0000u);
+    };
+    float d0 = 0.f, d1 = 0.f;
+    {
+        const int col = 2 * threadIdx.x;
+        if (col < d) {
+            float q0, q1, u0 = 0.f, u1 = 0.f, v0, v1;
+            pair(qh, col, q0, q1);
+            if (x0b) pair(x0b, col, u0, u1);
+            pair(x1b, col, v0, v1);
+            d0 = q0 * u0 + q1 * u1;
+            d1 = q0 * v0 + q1 * v1;
         }
-        const uint32_t yy = *reinterpret_cast<const uint32_t*>(x1 + b * x1_stride_b + col);
-        b0 = __uint_as_float(yy << 16);
-        b1 = __uint_as_float(yy & 0xffff0000u);
     }
-    float d0 = wave_sum(q0 * a0 + q1 * a1);
-    float d1 = wave_sum(q0 * b0 + q1 * b1);
+    d0 = wave_sum(d0);
+    d1 = wave_sum(d1);
     if (lane == 0) {
         red[0][wv] = d0;
         red[1][wv] = d1;
+    }
+    // split weights (every wave derives them)
+    const float ms = lane < n_splits ? a.ws_ml[2 * (base + lane)] : -INFINITY;
+    const float ls = lane < n_splits ? a.ws_ml[2 * (base + lane) + 1] : 0.f;
+    float M = wave_max(ls > 0.f ? ms : -INFINITY);
+    // this wave's splits for the workgroup's columns, in batches of loads;
+    // empty splits' slots hold stale bytes, selected away (never multiplied)
+    const int col2 = cb * kMergeCols + 2 * lane;
+    const bool has_col = col2 < d;
+    constexpr int kBatch = 16;
+    float2 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int sp = wv + kMergeWaves * u;
+        v[u] = (has_col && sp < n_splits) ? *reinterpret_cast<const float2*>(ob + static_cast<long long>(sp) * d + col2)
+                                          : make_float2(0.f, 0.f);
     }
     __syncthreads();
     d0 = 0.f;
     d1 = 0.f;
 #pragma unroll
-    for (int w = 0; w < kMergeThreads / kWave; ++w) {
+    for (int w = 0; w < kMergeWaves; ++w) {
         d0 += red[0][w];
         d1 += red[1][w];
     }
     const float s0 = x0 ? d0 * a.scale : -INFINITY;
     const float s1 = d1 * a.scale;
-    // split weights
-    const float ms = lane < n_splits ? a.ws_ml[2 * (base + lane)] : -INFINITY;
-    const float ls = lane < n_splits ? a.ws_ml[2 * (base + lane) + 1] : 0.f;
-    float M = wave_max(ls > 0.f ? ms : -INFINITY);
     M = fmaxf(M, fmaxf(s0, s1));
     const float sk = a.sink ? a.sink[hh] : -INFINITY;
     M = fmaxf(M, sk);  // finite: s1 is
     const float wsp = ls > 0.f ? expf(ms - M) : 0.f;
+    float acc0 = 0.f, acc1 = 0.f;
+    static_assert(kMergeWaves * kBatch >= kWave, "one batch covers every split");
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int sp = wv + kMergeWaves * u;
+        const float c = sp < n_splits ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsp), sp < kWave ? sp : 0))
+                                      : 0.f;
+        acc0 += c != 0.f ? c * v[u].x : 0.f;
+        acc1 += c != 0.f ? c * v[u].y : 0.f;
+    }
+    part[wv][lane] = make_float2(acc0, acc1);
+    __syncthreads();
+    if (wv != 0) return;
     const float e0 = x0 ? expf(s0 - M) : 0.f;
     const float e1 = expf(s1 - M);
     const float es = a.sink ? expf(sk - M) : 0.f;
     const float den = wave_sum(wsp * ls) + e0 + e1 + es;
     const float inv = 1.0f / den;
-    float acc0 = e0 * a0 + e1 * b0, acc1 = e0 * a1 + e1 * b1;
-    // the splits' outputs in batches of loads; empty splits' slots hold stale
-    // bytes, selected away (never multiplied)
-    constexpr int kBatch = 16;
-    for (int s0b = 0; s0b < n_splits; s0b += kBatch) {
-        float2 v[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u)
-            v[u] = (has_col && s0b + u < n_splits)
-                       ? *reinterpret_cast<const float2*>(ob + static_cast<long long>(s0b + u) * d + col)
-                       : make_float2(0.f, 0.f);
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int sp = s0b + u < n_splits ? s0b + u : 0;
-            const float c = s0b + u < n_splits ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsp), sp)) : 0.f;
-            acc0 += c != 0.f ? c * v[u].x : 0.f;
-            acc1 += c != 0.f ? c * v[u].y : 0.f;
-        }
-    }
     if (has_col) {
-        const long long o = b * a.out_stride_b + static_cast<long long>(hh) * d + col;
+        float u0 = 0.f, u1 = 0.f, w0, w1;
+        if (x0b) pair(x0b, col2, u0, u1);
+        pair(x1b, col2, w0, w1);
+        float o0 = e0 * u0 + e1 * w0, o1 = e0 * u1 + e1 * w1;
+#pragma unroll
+        for (int w = 0; w < kMergeWaves; ++w) {
+            o0 += part[w][lane].x;
+            o1 += part[w][lane].y;
+        }
+        const long long o = b * a.out_stride_b + static_cast<long long>(hh) * d + col2;
         if (a.out_bf16) {
-            static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(acc0 * inv);
-            static_cast<uint16_t*>(a.out)[o + 1] = f32_to_bf16(acc1 * inv);
+            static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(o0 * inv);
+            static_cast<uint16_t*>(a.out)[o + 1] = f32_to_bf16(o1 * inv);
         } else {
-            static_cast<float*>(a.out)[o] = acc0 * inv;
-            static_cast<float*>(a.out)[o + 1] = acc1 * inv;
+            static_cast<float*>(a.out)[o] = o0 * inv;
+            static_cast<float*>(a.out)[o + 1] = o1 * inv;
         }
     }
-    if (a.lse && threadIdx.x == 0) a.lse[static_cast<long long>(b) * a.h + hh] = M + logf(den);
+    if (a.lse && cb == 0 && lane == 0) a.lse[static_cast<long long>(b) * a.h + hh] = M + logf(den);
 }
 
 }  // namespace
@@ -324,12 +381,21 @@ hipError_t launch_attn_dense_bf16(AttnArgs a, const PrepArgs& prep, const void* 
         opted[dev] = true;
     }
     const int groups = a.h / kHeadGroup;
-    const int att_wgs = 8 * groups * ((ns + 7) / 8);
-    const int prep_wgs = !prep.completes ? 1 : (prep.main_wgs > 1 ? 1 + prep.main_wgs : 2);
+    const int att_wgs = groups * ns;
+    // a long main block (main_wgs > 1) is folded into the attention
+    // workgroups; otherwise one job workgroup compresses it
+    const bool fold = prep.completes && prep.main_wgs > 1;
+    const int prep_wgs = prep.completes && !fold ? 2 : 1;
+    int fold_ch = 0;
+    if (fold) {  // a power of two, so the slices of a channel merge by lane swaps
+        fold_ch = kFoldMinCh;
+        while (fold_ch * att_wgs < a.d) fold_ch *= 2;
+    }
     const int extra = 1 + (x0 ? 1 : 0);
     hipLaunchKernelGGL(k_attn_dense_bf16, dim3(att_wgs + prep_wgs, a.batch), dim3(kDenseThreads), lds, s, a, ns,
-                       prep_wgs, prep, extra);
-    hipLaunchKernelGGL(k_attn_merge_rows, dim3(a.h, a.batch), dim3(kMergeThreads), 0, s, a, ns,
+                       prep_wgs, prep, extra, fold_ch);
+    const int col_blocks = (a.d + kMergeCols - 1) / kMergeCols;
+    hipLaunchKernelGGL(k_attn_merge_rows, dim3(a.h * col_blocks, a.batch), dim3(kMergeThreads), 0, s, a, ns,
                        static_cast<const uint16_t*>(x0), x0_stride_b, static_cast<const uint16_t*>(x1), x1_stride_b);
     return hipGetLastError();
 }

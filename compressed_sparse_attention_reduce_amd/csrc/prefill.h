@@ -15,7 +15,7 @@ namespace csa {
 constexpr int kPrefillChunkRows = 256;  // query rows whose scores are held at once
 struct IndexTopkArgs {
     const uint16_t* q;  // [t][64][128] bf16
-    const float* w;     // [t][64]
+    const float* w;     // [t][64] (E4M3: query scales folded in)
     const uint16_t* k;  // [n][128] bf16
     int t, n;
     long long pos0;     // position of query 0; < 0: no causal mask
@@ -24,6 +24,11 @@ struct IndexTopkArgs {
     int* idx;           // [t][top_k]
     int* count;         // [t] or nullptr
     void* ws;
+    // E4M3 queries and keys instead (k_scale != nullptr): q8 [t][64][128],
+    // k8 [n][128] codes, k_scale [n] row scales; q and k unused then
+    const uint8_t* q8;
+    const uint8_t* k8;
+    const float* k_scale;
 };
 size_t index_topk_workspace_bytes(int t, int n, int top_k);
 hipError_t launch_index_topk(const IndexTopkArgs& a, hipStream_t s);
@@ -34,6 +39,8 @@ hipError_t launch_index_topk(const IndexTopkArgs& a, hipStream_t s);
 // Same bits as launch_index_score_bf16 for the same (query, key).
 constexpr int kMqMinRows = 16;  // query rows per sequence from which it is used
 hipError_t launch_index_score_mq(const ScoreArgs& a, long long pos0, hipStream_t s);
+// The same over E4M3 queries and keys (h_i = 64, d_i = 128; a.cands unused).
+hipError_t launch_index_score_mq_fp8(const Fp8ScoreArgs& a, long long pos0, hipStream_t s);
 
 // ---- per-query sparse attention over indexed rows + the sliding window --------
 struct PrefillAttnArgs {

@@ -529,19 +529,36 @@ hipError_t launch_index_topk(const IndexTopkArgs& a, hipStream_t s) {
     void* tws = static_cast<char*>(a.ws) + pf_align256(sizeof(float) * static_cast<size_t>(rows_max) * a.n);
     for (int r0 = 0; r0 < a.t; r0 += kPrefillChunkRows) {
         const int rows = a.t - r0 < kPrefillChunkRows ? a.t - r0 : kPrefillChunkRows;
-        ScoreArgs sa{};
-        sa.q = a.q + static_cast<long long>(r0) * kIdxHeads * kIdxDi;
-        sa.w = a.w + static_cast<long long>(r0) * kIdxHeads;
-        sa.k = a.k;
-        sa.scores = sc;
-        sa.batch = 1;
-        sa.t = rows;
-        sa.h_i = kIdxHeads;
-        sa.d_i = kIdxDi;
-        sa.n = a.n;
-        sa.ratio = a.ratio;
-        sa.ld_s = a.n;
-        hipError_t e = launch_index_score_mq(sa, a.pos0 < 0 ? -1 : a.pos0 + r0, s);
+        const long long p0 = a.pos0 < 0 ? -1 : a.pos0 + r0;
+        hipError_t e;
+        if (a.k_scale) {
+            Fp8ScoreArgs fa{};
+            fa.q = a.q8 + static_cast<long long>(r0) * kIdxHeads * kIdxDi;
+            fa.w = a.w + static_cast<long long>(r0) * kIdxHeads;
+            fa.k = a.k8;
+            fa.k_scale = a.k_scale;
+            fa.scores = sc;
+            fa.batch = 1;
+            fa.t = rows;
+            fa.n = a.n;
+            fa.ratio = a.ratio;
+            fa.ld_s = a.n;
+            e = launch_index_score_mq_fp8(fa, p0, s);
+        } else {
+            ScoreArgs sa{};
+            sa.q = a.q + static_cast<long long>(r0) * kIdxHeads * kIdxDi;
+            sa.w = a.w + static_cast<long long>(r0) * kIdxHeads;
+            sa.k = a.k;
+            sa.scores = sc;
+            sa.batch = 1;
+            sa.t = rows;
+            sa.h_i = kIdxHeads;
+            sa.d_i = kIdxDi;
+            sa.n = a.n;
+            sa.ratio = a.ratio;
+            sa.ld_s = a.n;
+            e = launch_index_score_mq(sa, p0, s);
+        }
         if (e != hipSuccess) return e;
         TopkArgs ta{};
         ta.scores = sc;

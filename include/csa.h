@@ -151,7 +151,10 @@ int csa_index_score(const void *q, const float *w, const void *k, float *scores,
  *   q_pos, ratio: the causal form, as for csa_index_score.
  * Supported: h_i = 64, d_i = 128; q, k, w 16-byte aligned and strides that
  * keep them so.  Products of E4M3 values are exact in float32; sums are
- * float32.
+ * float32.  From t = 16 query rows per sequence the multi-query form of
+ * section 7 runs (same values up to float32 summation order; the key scale
+ * is then applied after the head sum, which is exact in real arithmetic
+ * since k_scale > 0).
  * ------------------------------------------------------------------------ */
 int csa_quantize_fp8(const void *x, csa_dtype x_dtype, unsigned char *codes, float *scales,
                      long long rows, int d, csa_stream stream);
@@ -372,6 +375,12 @@ int csa_hca_decode_step(const csa_layer_desc *layer, const csa_step_io *io, void
  *   (nullable) = min(top_k, visible blocks).  1 <= top_k <= 2048.
  *   ws: csa_index_topk_workspace_size(t, n, top_k) bytes, 16-byte aligned.
  *
+ * csa_index_topk_fp8: the same over E4M3 queries and keys (section 2b):
+ *   q: [t][64][128] uint8 codes, w: [t][64] float32 with the query's per-head
+ *   scales folded in, k: [n][128] uint8 codes, k_scale: [n] float32 row
+ *   scales; scores as csa_index_score_fp8 computes them.  The same workspace
+ *   size, outputs and limits as csa_index_topk.
+ *
  * csa_prefill_attn: per query row r, one softmax (scale, then the sink in the
  *   denominator only) over comp_kv[idx[r][0 .. count[r])] followed by its
  *   window rows.  q: [t][h][d] bf16; comp_kv: [n_comp][d] bf16; idx/count as
@@ -392,6 +401,10 @@ size_t csa_index_topk_workspace_size(int t, int n, int top_k);
 int csa_index_topk(const void *q, const float *w, const void *k, int t, int h_i, int d_i, int n,
                    long long pos0, int ratio, int top_k, int *idx, int *count, void *ws,
                    size_t ws_bytes, csa_stream stream);
+int csa_index_topk_fp8(const unsigned char *q, const float *w, const unsigned char *k,
+                       const float *k_scale, int t, int h_i, int d_i, int n, long long pos0,
+                       int ratio, int top_k, int *idx, int *count, void *ws, size_t ws_bytes,
+                       csa_stream stream);
 int csa_prefill_attn(const void *q, const void *comp_kv, int n_comp, const int *idx,
                      const int *count, int k, const void *win_kv, int window, long long pos0,
                      const float *sink, float scale, void *out, csa_dtype out_dtype, float *lse,

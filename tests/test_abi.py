@@ -152,6 +152,16 @@ def test_prefill_entry_points_reject_bad_args(csa):
     assert lib.csa_index_topk(*a) == B.CSA_ERR_INVALID_ARG
     a = list(base); a[8] = 0
     assert lib.csa_index_topk(*a) == B.CSA_ERR_INVALID_ARG
+    # the E4M3 form: one more pointer (the key scales) after k
+    b8 = base[:3] + [FAKE] + base[3:]
+    a = list(b8); a[6] = 64
+    assert lib.csa_index_topk_fp8(*a) == B.CSA_ERR_UNSUPPORTED
+    a = list(b8); a[3] = None
+    assert lib.csa_index_topk_fp8(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(b8); a[14] = ws - 1
+    assert lib.csa_index_topk_fp8(*a) == B.CSA_ERR_WORKSPACE
+    a = list(b8); a[10] = 2049
+    assert lib.csa_index_topk_fp8(*a) == B.CSA_ERR_INVALID_ARG
     attn = [FAKE, FAKE, 65536, FAKE, FAKE, 512, FAKE, 128, 260096, FAKE, 0.04, FAKE, B.CSA_BF16, None,
             2048, 64, 512, None]
     a = list(attn); a[15] = 8                   # heads not a multiple of 16

@@ -837,13 +837,23 @@ def test_decode_step_ctx1m_fp8_keys_full_size(csa):
 # 6b. HCA layer step (ratio-m compressor, attention over every entry + window)
 # ---------------------------------------------------------------------------
 
-def test_hca_steps_in_sequence(csa):
-    """Twenty HCA steps at ratio 8 (three block completions, ring wrap) with
-    the host counters advanced by csa_layer_advance; each step against the
-    oracle's evolving state."""
-    m, W, D, H = 8, 8, 512, 64
-    g = _g(6001)
-    n0, pos0, max_comp = 37, 37 * 8 + 5, 48
+HCA_SEQ_CASES = [
+    # name, ratio m, heads, entries before, cache capacity, window
+    ("ratio8_h64", 8, 64, 37, 48, 8),           # one job workgroup compresses a block
+    ("ratio64_h16_fold", 64, 16, 5, 40, 8),     # the block folded into the one attention workgroup
+    ("ratio32_h32_fold", 32, 32, 20, 300, 16),  # folded over workgroups of empty splits too
+]
+
+
+@pytest.mark.parametrize("case", HCA_SEQ_CASES, ids=[c[0] for c in HCA_SEQ_CASES])
+def test_hca_steps_in_sequence(csa, case):
+    """Twenty HCA steps (block completions, ring wrap) with the host counters
+    advanced by csa_layer_advance; each step against the oracle's evolving
+    state."""
+    name, m, H, n0, max_comp, W = case
+    D = 512
+    g = _g(6001 + m)
+    pos0 = n0 * m + (5 if m == 8 else m - 10)
     comp = dev_bf16(synth.to_bf16_bits(g.standard_normal((1, max_comp, D), dtype=np.float32)))
     swa = dev_bf16(synth.to_bf16_bits(g.standard_normal((1, W, D), dtype=np.float32)))
     mb = dev_f32(g.standard_normal((m, D), dtype=np.float32) * np.float32(0.1))

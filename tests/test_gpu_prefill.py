@@ -15,6 +15,7 @@ import torch
 
 import oracle
 import synth
+from oracle import numfmt
 from tests.gpu_util import DEV, as_f64, assert_topk_gap_rule, dev_bf16, dev_f32, host_f64, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -172,6 +173,150 @@ def test_index_topk_empty_history(csa):
     idx, cnt = _run_index_topk(csa, q, w, K, 8, 0)
     torch.cuda.synchronize()
     assert (idx == -1).all() and (cnt == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# E4M3 keys: multi-query FP8 score and score + top-k
+# ---------------------------------------------------------------------------
+
+def _fp8(g, shape_q, n):
+    """E4M3 query (per head row) and keys (per key row), quantised by the
+    oracle's quantiser; the query's scales folded into w."""
+    q = (g.standard_normal(shape_q) / np.sqrt(128)).astype(np.float32)
+    w = g.standard_normal(shape_q[:-1]).astype(np.float32)
+    K = g.standard_normal((n, 128)).astype(np.float32)
+    qc, qs = numfmt.quantize_e4m3_rows(q.reshape(-1, 128))
+    kc, ks = numfmt.quantize_e4m3_rows(K) if n else (np.zeros((0, 128), np.uint8), np.zeros(0, np.float32))
+    return qc.reshape(shape_q), (w * qs.reshape(w.shape)).astype(np.float32), kc, ks
+
+
+MQ8_CASES = [
+    # name, B, t, n, causal
+    ("mq8_causal_ragged_batch2", 2, 37, 1000, True),
+    ("mq8_16_rows_31_keys", 1, 16, 31, False),
+    ("mq8_70_rows_4111_keys", 1, 70, 4111, True),
+    ("mq8_one_key", 3, 17, 1, False),
+    ("mq8_300_rows_2049_keys", 1, 300, 2049, True),
+]
+
+
+@pytest.mark.parametrize("case", MQ8_CASES, ids=[c[0] for c in MQ8_CASES])
+def test_multi_query_score_fp8(csa, case):
+    name, B, t, n, causal = case
+    g = _g(t * 1000 + n + 5)
+    qc, w, kc, ks = _fp8(g, (B, t, 64, 128), B * n)
+    kc, ks = kc.reshape(B, n, 128), ks.reshape(B, n)
+    ld = n + 3
+    scores = torch.full((B, t, ld), 123.0, device=DEV)
+    pos_np = None
+    if causal:
+        pos_np = (4 * n - 2 * t - 9 + 2 * np.arange(B * t)).astype(np.int32).reshape(B, t)
+    csa.csa_index_score_fp8(torch.from_numpy(qc).to(DEV), dev_f32(w), torch.from_numpy(kc).to(DEV), dev_f32(ks),
+                            scores, q_pos=None if pos_np is None else torch.from_numpy(pos_np).to(DEV))
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy().astype(np.float64)
+    assert (got[:, :, n:] == 123.0).all(), "wrote past n"
+    for b in range(B):
+        ref = oracle.index_score_fp8(qc[b], w[b], kc[b], ks[b], q_pos=None if pos_np is None else pos_np[b])
+        fin = np.isfinite(ref)
+        assert (np.isfinite(got[b, :, :n]) == fin).all(), "mask differs"
+        assert rel_err(got[b, :, :n][fin], ref[fin]) <= 1e-4
+
+
+def _run_index_topk_fp8(csa, qc, w8, kc, ks, k, pos0, n=None):
+    t = qc.shape[0]
+    n = kc.shape[0] if n is None else n
+    idx = torch.full((t, k), -5, dtype=torch.int32, device=DEV)
+    cnt = torch.full((t,), -5, dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(csa.csa_index_topk_workspace_size(t, n, k), 16), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xCD)
+    csa.csa_index_topk_fp8(qc, w8, kc, ks, idx, cnt, ws, pos0=pos0, n=n)
+    return idx, cnt
+
+
+@pytest.mark.parametrize("case", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
+def test_index_topk_fp8(csa, case):
+    """Top-k over the FP8 chunk scan: bit-exact against the oracle's top-k of
+    the same scan's scores (csa_index_score_fp8 runs the same multi-query
+    kernel from 16 rows on), the gap rule against the oracle's FP8 scores."""
+    name, t, n, k, pos0 = case
+    g = _g(t + 7 * n + k + 1)
+    qn, wn, kn, ksn = _fp8(g, (t, 64, 128), n)
+    qc, w8, kc, ks = torch.from_numpy(qn).to(DEV), dev_f32(wn), torch.from_numpy(kn).to(DEV), dev_f32(ksn)
+    idx, cnt = _run_index_topk_fp8(csa, qc, w8, kc, ks, k, pos0)
+    scores = torch.empty(1, t, n, device=DEV)
+    pos = None
+    if pos0 >= 0:
+        pos = torch.arange(pos0, pos0 + t, dtype=torch.int32, device=DEV)[None]
+    assert t >= 16  # the standalone call takes the multi-query kernel too
+    csa.csa_index_score_fp8(qc[None], w8[None], kc[None], ks[None], scores, q_pos=pos)
+    torch.cuda.synchronize()
+    gs = scores[0].cpu().numpy().astype(np.float64)
+    ri, rc = oracle.topk(gs, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+    if pos0 >= 0:
+        np.testing.assert_array_equal(rc, np.minimum(k, _visible(pos0 + np.arange(t), n)))
+    rows = sorted({0, t // 2, t - 1})
+    ref = oracle.index_score_fp8(qn[rows], wn[rows], kn, ksn, q_pos=None if pos0 < 0 else pos0 + np.array(rows))
+    for i, r in enumerate(rows):
+        assert_topk_gap_rule(idx[r].cpu().numpy(), int(cnt[r]), ref[i], k)
+
+
+def test_index_topk_fp8_empty_history(csa):
+    g = _g(15)
+    qn, wn, _, _ = _fp8(g, (16, 64, 128), 0)
+    kc = torch.empty(0, 128, dtype=torch.uint8, device=DEV)
+    ks = torch.empty(0, dtype=torch.float32, device=DEV)
+    idx, cnt = _run_index_topk_fp8(csa, torch.from_numpy(qn).to(DEV), dev_f32(wn), kc, ks, 8, 0)
+    torch.cuda.synchronize()
+    assert (idx == -1).all() and (cnt == 0).all()
+
+
+def test_prefill_fp8_keys_full_size_sampled(csa):
+    """The 2048 x 65536 chunk with E4M3 keys and queries quantised on the GPU:
+    counts, the top-512 of 16 sampled rows bit-exact against the oracle's
+    top-k of the same kernel's scores, the gap rule and the scores against
+    the oracle's FP8 score on two rows; the overlap with the bf16 top-512 is
+    printed (E4M3 moves scores near the threshold: no parity bar)."""
+    shape = synth.SHAPES["prefill"]
+    x = synth.make_prefill_inputs_torch(shape, None, DEV)
+    T, N, k = shape.t, shape.n_comp, shape.top_k
+    kc = torch.empty(N, 128, dtype=torch.uint8, device=DEV)
+    ks = torch.empty(N, dtype=torch.float32, device=DEV)
+    csa.csa_quantize_fp8(x["idx_keys"], kc, ks)
+    qc = torch.empty(T, 64, 128, dtype=torch.uint8, device=DEV)
+    qs = torch.empty(T, 64, dtype=torch.float32, device=DEV)
+    csa.csa_quantize_fp8(x["q_idx"], qc, qs)
+    w8 = (x["w_idx"] * qs).contiguous()
+    idx, cnt = _run_index_topk_fp8(csa, qc, w8, kc, ks, k, x["pos0"])
+    idx16, _ = _run_index_topk(csa, x["q_idx"], x["w_idx"], x["idx_keys"], k, x["pos0"])
+    torch.cuda.synchronize()
+    pos = x["pos0"] + np.arange(T)
+    assert (cnt.cpu().numpy() == np.minimum(k, _visible(pos, N))).all()
+    rows = [0, 1, 2, 3, 255, 256, 257, 511, 1024, 1027, 1500, 1800, 2000, 2045, 2046, 2047]
+    sel = torch.tensor(rows, device=DEV)
+    scores = torch.empty(1, len(rows), N, device=DEV)
+    csa.csa_index_score_fp8(qc[sel][None].contiguous(), w8[sel][None].contiguous(), kc[None], ks[None], scores,
+                            q_pos=torch.from_numpy(pos[rows].astype(np.int32)).to(DEV)[None])
+    torch.cuda.synchronize()
+    gs = scores[0].cpu().numpy().astype(np.float64)
+    ri, rc = oracle.topk(gs, k)
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    np.testing.assert_array_equal(gi[rows], ri)
+    np.testing.assert_array_equal(gc[rows], rc)
+    kcn, ksn = kc.cpu().numpy(), ks.cpu().numpy()
+    for i in (0, len(rows) - 1):
+        r = rows[i]
+        ref = oracle.index_score_fp8(qc[r].cpu().numpy()[None], w8[r].cpu().numpy()[None], kcn, ksn,
+                                     q_pos=np.array([pos[r]]))[0]
+        fin = np.isfinite(ref)
+        assert rel_err(gs[i][fin], ref[fin]) <= 1e-4
+        assert_topk_gap_rule(gi[r], int(gc[r]), ref, k)
+    i16 = idx16.cpu().numpy()
+    overlap = np.mean([len(set(gi[r]) & set(i16[r])) / k for r in range(0, T, 64)])
+    print(f"fp8 vs bf16 top-512 overlap over 32 sampled queries: {overlap:.4f}")
+    assert overlap >= 0.85
 
 
 # ---------------------------------------------------------------------------
