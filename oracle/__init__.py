@@ -20,7 +20,9 @@ from .csa import (
     index_score,
     index_score_fp8,
     kv_norm,
+    mixed_kv_row,
     prefill_chunk,
+    rope_rotate,
     sparse_attn,
     topk,
 )
@@ -29,6 +31,8 @@ __all__ = [
     "numfmt",
     "compress",
     "kv_norm",
+    "rope_rotate",
+    "mixed_kv_row",
     "index_score",
     "index_score_fp8",
     "topk",

@@ -329,6 +329,58 @@ def sparse_attn(q, kv, sink=None, scale: Optional[float] = None, return_weights:
 
 
 # ---------------------------------------------------------------------------
+# (5b) RoPE and the mixed E4M3 / bf16 main KV rows
+# ---------------------------------------------------------------------------
+
+def rope_rotate(x, cos, sin, inverse: bool = False) -> np.ndarray:
+    """Rotate the last ``2 * len(cos)`` entries of ``x`` (the RoPE dims) in
+    (even, odd) pairs; every other entry is returned unchanged.
+
+    Page 1, ``PERFORMANCE_AUDIT.md`` P5 (``_apply_rope`` /
+    ``_apply_rope_inplace``): the RoPE part is the trailing ``rope_dim``
+    entries, paired as ``0::2`` / ``1::2``; the inverse printed there is
+    ``(e c + o s, -e s + o c)``, so the forward rotation is its inverse,
+    ``(e c - o s, e s + o c)``.  ``cos``/``sin`` hold the table row of one
+    position (``rope_dim / 2`` values).  float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    c = np.asarray(cos, dtype=np.float64)
+    s = np.asarray(sin, dtype=np.float64)
+    rd = 2 * c.shape[-1]
+    out = x.copy()
+    ev = x[..., x.shape[-1] - rd::2]
+    od = x[..., x.shape[-1] - rd + 1::2]
+    if inverse:
+        out[..., x.shape[-1] - rd::2] = ev * c + od * s
+        out[..., x.shape[-1] - rd + 1::2] = -ev * s + od * c
+    else:
+        out[..., x.shape[-1] - rd::2] = ev * c - od * s
+        out[..., x.shape[-1] - rd + 1::2] = ev * s + od * c
+    return out
+
+
+def mixed_kv_row(y, rope_dim: int, cos=None, sin=None):
+    """One main-KV row in the mixed storage of page 2, ``eager_attention``
+    (the "B1 storage-native mixed path"): the NoPE part (all but the last
+    ``rope_dim`` entries) quantised from float32 to E4M3 with one row scale
+    (:func:`numfmt.quantize_e4m3_rows`), the RoPE part kept in bfloat16 —
+    rotated first when a table row is given (a compressed entry: its RoPE
+    part is rounded to bfloat16, rotated, and rounded again, as ``_apply_rope``
+    does on bfloat16 input).  Returns ``(codes, scale, rope, row)`` with
+    ``row`` the float64 values an attention reads back."""
+    from .numfmt import bf16_round_f64, e4m3_decode, quantize_e4m3_rows
+
+    y32 = np.asarray(y, dtype=np.float32)
+    nope = y32.shape[-1] - rope_dim
+    codes, scale = quantize_e4m3_rows(y32[None, :nope])
+    rope = bf16_round_f64(y32[nope:].astype(np.float64))
+    if cos is not None:
+        rope = bf16_round_f64(rope_rotate(rope, cos, sin))
+    row = np.concatenate([e4m3_decode(codes[0]) * np.float64(scale[0]), rope])
+    return codes[0], scale[0], rope, row
+
+
+# ---------------------------------------------------------------------------
 # (6) one decode step for one layer
 # ---------------------------------------------------------------------------
 
@@ -372,6 +424,17 @@ class LayerState:
     # scales [max_comp]; when set they replace idx_keys
     idx_codes: Optional[np.ndarray] = None
     idx_scales: Optional[np.ndarray] = None
+    # Mixed main KV (page 2, eager_attention, "B1"): comp_kv and the SWA ring
+    # hold the values of mixed rows (:func:`mixed_kv_row`); compressed entries
+    # get RoPE from the comp tables at their block index, the output inverse
+    # RoPE from the token tables at the token's position.  Tables:
+    # [rows, rope_dim / 2].
+    kv_mixed: bool = False
+    rope_dim: int = 64
+    rope_cos: Optional[np.ndarray] = None
+    rope_sin: Optional[np.ndarray] = None
+    comp_rope_cos: Optional[np.ndarray] = None
+    comp_rope_sin: Optional[np.ndarray] = None
 
 
 def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
@@ -395,12 +458,21 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
     ``L.idx_codes`` / ``L.idx_scales``, and the scores are
     :func:`index_score_fp8` with ``q_idx`` the query's E4M3 codes and
     ``w_idx`` the head weights with the query's scales folded in.
+
+    With mixed main KV (``L.kv_mixed``) the new token's row (already rotated
+    by the caller, as the pages' ``kv_roped``) and each compressed entry
+    (rotated here at its block index ``pos // m`` with the comp tables) are
+    stored as :func:`mixed_kv_row` values, and the attention output gets the
+    inverse rotation at ``pos`` (the pages' "Inverse RoPE" after the FMHA).
     """
     from .numfmt import quantize_e4m3_rows
 
     m = L.m
     fp8 = L.idx_codes is not None
-    L.swa.append(np.asarray(kv_new, dtype=np.float64))
+    if L.kv_mixed:  # the new token's row arrives with its RoPE applied
+        L.swa.append(mixed_kv_row(kv_new, L.rope_dim)[3])
+    else:
+        L.swa.append(np.asarray(kv_new, dtype=np.float64))
     rnd = L.round_cache if L.round_cache is not None else (lambda a: a)
     new_entry = None
     if pos % m == m - 1:
@@ -413,7 +485,11 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
             ym = kv_norm(ym, L.main_norm)
         if L.idx_norm is not None:
             yi = kv_norm(yi, L.idx_norm)
-        L.comp_kv[L.n_comp] = rnd(ym)
+        if L.kv_mixed:
+            blk = pos // m
+            L.comp_kv[L.n_comp] = mixed_kv_row(ym, L.rope_dim, L.comp_rope_cos[blk], L.comp_rope_sin[blk])[3]
+        else:
+            L.comp_kv[L.n_comp] = rnd(ym)
         if fp8:
             codes, kscale = quantize_e4m3_rows(np.asarray(yi, dtype=np.float32)[None])
             L.idx_codes[L.n_comp] = codes[0]
@@ -431,6 +507,8 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
     idx, count = topk(scores[None], top_k)
     rows, n_valid = gather(L.comp_kv[:N], idx[0], int(count[0]), L.swa.rows, L.swa.head, L.swa.length)
     out, lse = sparse_attn(q, rows, L.sink, scale)
+    if L.kv_mixed:  # inverse RoPE of the output at the token's position
+        out = rope_rotate(out, L.rope_cos[pos], L.rope_sin[pos], inverse=True)
     return {
         "new_entry": new_entry,
         "scores": scores,

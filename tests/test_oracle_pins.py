@@ -647,6 +647,118 @@ def test_decode_step_fp8_key_within_e4m3_rounding():
     assert L.n_comp == 4
 
 
+def _rope_tables(n_pos, rd, base=10000.0, offset=0.0):
+    """cos / sin rows of angle (p + offset) * base^(-2j/rd) (a test table)."""
+    ang = (np.arange(n_pos)[:, None] + offset) * base ** (-2.0 * np.arange(rd // 2)[None, :] / rd)
+    return np.cos(ang), np.sin(ang)
+
+
+def test_rope_rotation_closed_forms():
+    """The printed inverse, and the forward as its inverse: a quarter turn
+    maps the pair (e, o) to (-o, e); inverse(forward(x)) = x; the NoPE part is
+    untouched; pair norms are kept; and the score of two rotated vectors
+    depends only on the difference of their positions."""
+    g = _g(28)
+    x = g.standard_normal((3, 24))
+    c, s = np.zeros(4), np.ones(4)
+    f = oracle.rope_rotate(x, c, s)
+    np.testing.assert_array_equal(f[:, :16], x[:, :16])
+    np.testing.assert_allclose(f[:, 16::2], -x[:, 17::2], atol=0)
+    np.testing.assert_allclose(f[:, 17::2], x[:, 16::2], atol=0)
+    inv = oracle.rope_rotate(x, c, s, inverse=True)
+    np.testing.assert_allclose(inv[:, 16::2], x[:, 17::2], atol=0)
+    np.testing.assert_allclose(inv[:, 17::2], -x[:, 16::2], atol=0)
+    cos, sin = _rope_tables(50, 8)
+    for p in (0, 7, 49):
+        y = oracle.rope_rotate(x, cos[p], sin[p])
+        np.testing.assert_allclose(oracle.rope_rotate(y, cos[p], sin[p], inverse=True), x, rtol=1e-14, atol=1e-14)
+        pn = lambda a: a[:, 16::2] ** 2 + a[:, 17::2] ** 2
+        np.testing.assert_allclose(pn(y), pn(x), rtol=1e-13)
+    q, k = g.standard_normal(24), g.standard_normal(24)
+    dots = [oracle.rope_rotate(q, cos[p + 5], sin[p + 5]) @ oracle.rope_rotate(k, cos[p], sin[p]) for p in (0, 9, 30)]
+    np.testing.assert_allclose(dots, dots[0], rtol=1e-12)
+    np.testing.assert_allclose(dots[0], oracle.rope_rotate(q, cos[5], sin[5]) @ k, rtol=1e-12)
+
+
+def test_mixed_kv_row_exact_and_bounded():
+    """A row whose NoPE part is E4M3 values times a power of two (carrying
+    +-448 times it) and whose RoPE part is bfloat16 comes back exactly with a
+    zero rotation; a general row within E4M3 / bfloat16 rounding."""
+    g = _g(29)
+    codes = _e4m3_codes(g, (1, 28))
+    codes[0, 3] = 0x7E
+    rope = numfmt.bf16_round_f64(g.standard_normal(4))
+    y = np.concatenate([numfmt.e4m3_decode(codes[0]) * 0.25, rope])
+    c, sc, rp, row = oracle.mixed_kv_row(y, 4, np.ones(2), np.zeros(2))
+    np.testing.assert_array_equal(c, codes[0])
+    assert sc == np.float32(0.25)
+    np.testing.assert_array_equal(row, y)
+    y = g.standard_normal(32)
+    _, sc, _, row = oracle.mixed_kv_row(y, 8)
+    yf = y.astype(np.float32).astype(np.float64)
+    bound = np.maximum(np.abs(yf[:24]) * 2.0 ** -4, sc * 2.0 ** -10) * (1 + 1e-6)
+    assert (np.abs(row[:24] - yf[:24]) <= bound).all()
+    assert (np.abs(row[24:] - yf[24:]) <= np.abs(yf[24:]) * 2.0 ** -8).all()
+
+
+def test_decode_step_mixed_kv_equals_plain_step_when_exact():
+    """Mixed storage loses nothing when every stored value is representable
+    (E4M3 NoPE times a power of two, bfloat16 RoPE) and every rotation is the
+    identity: the mixed step then matches the float64 step — scores,
+    selection and output (ratio 1: each compressed entry is its content row)."""
+    g = _g(30)
+    D, di, H, W, rd = 16, 8, 4, 6, 4
+    Lp = _empty_state(g, D=D, di=di, H=H, W=W, m=1)
+    Lm = _empty_state(g, D=D, di=di, H=H, W=W, m=1)
+    Lm.main_bias, Lm.idx_bias, Lm.sink = Lp.main_bias, Lp.idx_bias, Lp.sink
+    Lm.kv_mixed, Lm.rope_dim = True, rd
+    one, zero = np.ones((64, rd // 2)), np.zeros((64, rd // 2))
+    Lm.rope_cos, Lm.rope_sin, Lm.comp_rope_cos, Lm.comp_rope_sin = one, zero, one, zero
+
+    def exact_row():
+        c = _e4m3_codes(g, (1, D - rd))
+        c[0, 0] = 0x7E
+        return np.concatenate([numfmt.e4m3_decode(c[0]) * 0.5, numfmt.bf16_round_f64(g.standard_normal(rd))])
+
+    for pos in range(12):
+        inp = _step_inputs(g, D=D, di=di, H=H, m=1)
+        inp["kv_new"] = exact_row()
+        inp["c_main"] = exact_row()[None]
+        rp = oracle.decode_step(Lp, pos=pos, top_k=4, **inp)
+        rm = oracle.decode_step(Lm, pos=pos, top_k=4, **inp)
+        np.testing.assert_array_equal(Lm.comp_kv[:Lm.n_comp], Lp.comp_kv[:Lp.n_comp])
+        np.testing.assert_array_equal(Lm.swa.rows, Lp.swa.rows)
+        np.testing.assert_array_equal(rm["idx"], rp["idx"])
+        np.testing.assert_allclose(rm["out"], rp["out"], rtol=1e-13, atol=1e-14)
+
+
+def test_decode_step_mixed_kv_rotations():
+    """Each compressed entry's RoPE part is rotated at its block index with
+    the comp tables, and the output gets the inverse rotation at the token's
+    position: with a sink-free first block attended alone, the output is the
+    entry itself rotated back."""
+    g = _g(31)
+    D, H, W, rd = 16, 4, 1, 4
+    L = _empty_state(g, D=D, H=H, W=W, m=2)
+    L.sink = None
+    L.kv_mixed, L.rope_dim = True, rd
+    L.rope_cos, L.rope_sin = _rope_tables(16, rd)
+    L.comp_rope_cos, L.comp_rope_sin = _rope_tables(8, rd, base=7.0, offset=0.5)
+    for pos in range(4):
+        inp = _step_inputs(g, D=D, H=H, m=2)
+        r = oracle.decode_step(L, pos=pos, top_k=4, **inp)
+    # position 3 completed block 1 (positions 2, 3)
+    ym = oracle.compress(inp["z_main"], inp["c_main"], L.main_bias, 2)[0]
+    _, _, _, want = oracle.mixed_kv_row(ym, rd, L.comp_rope_cos[1], L.comp_rope_sin[1])
+    np.testing.assert_array_equal(L.comp_kv[1], want)
+    rows = r["rows"]
+    o, _ = oracle.sparse_attn(inp["q"], rows, None)
+    np.testing.assert_allclose(r["out"], oracle.rope_rotate(o, L.rope_cos[3], L.rope_sin[3], inverse=True),
+                               rtol=1e-13, atol=1e-14)
+    # the RoPE part of the stored entry is not the unrotated one
+    assert not np.allclose(L.comp_kv[1][-rd:], numfmt.bf16_round_f64(ym[-rd:].astype(np.float32)))
+
+
 # ---------------------------------------------------------------------------
 # (6b) HCA step: the dense special case of the CSA step
 # ---------------------------------------------------------------------------
