@@ -200,6 +200,59 @@ def time_fp8(csa, layers, shape, reps: int, steps: int):
     return scan_ms, alg, step_ms
 
 
+def time_mixed_kv(csa, layers, shape, steps: int):
+    """The 30-layer decode step over mixed main KV (E4M3 NoPE codes + bf16
+    RoPE part per 592-byte record, RoPE on the new compressed entry, inverse
+    RoPE on the output): every layer's bf16 caches packed once with
+    csa_pack_kv_mixed, the step graph-captured and replayed `steps` times.
+    Returns ms per step."""
+    import numpy as np
+    import torch
+
+    def tables(rows, offset, base):
+        ang = (np.arange(rows)[:, None] + offset) * base ** (-2.0 * np.arange(32)[None, :] / 64)
+        return (torch.from_numpy(np.cos(ang).astype(np.float32)).cuda(),
+                torch.from_numpy(np.sin(ang).astype(np.float32)).cuda())
+
+    rope = tables(shape.ctx + 8, 0.5, 10000.0)
+    comp_rope = tables(shape.max_comp + 1, 0.25, 500.0)
+    B, K, W = shape.batch, shape.top_k, shape.w
+    ml = []
+    for ly in layers:
+        x = ly["x"]
+        comp = torch.empty(B, shape.max_comp, csa.MIX_REC_BYTES, dtype=torch.uint8, device="cuda")
+        swa = torch.empty(B, W, csa.MIX_REC_BYTES, dtype=torch.uint8, device="cuda")
+        csa.csa_pack_kv_mixed(x["comp_kv"], comp)
+        csa.csa_pack_kv_mixed(x["swa"], swa)
+        L = csa.make_layer_desc(comp_kv=comp, idx_keys=x["idx_keys"], swa=swa, main_bias=x["main_bias"],
+                                idx_bias=x["idx_bias"], sink=x["sink"], n_comp=x["n_comp"],
+                                swa_head=x["swa_head"], swa_len=x["swa_len"], h=shape.h, h_i=shape.h_i,
+                                m=shape.m, top_k=K, rope=rope, comp_rope=comp_rope)
+        outs = dict(ly["outs"])
+        outs["gather_buf"] = torch.zeros(B, K + W, csa.MIX_REC_BYTES, dtype=torch.uint8, device="cuda")
+        io = csa.make_step_io(pos=x["pos"], q=x["q"], q_idx=x["q_idx"], w_idx=x["w_idx"], kv_new=x["kv_new"],
+                              z_main=x["z_main"], c_main=x["c_main"], z_idx=x["z_idx"], c_idx=x["c_idx"], **outs)
+        ml.append((L, io, ly["ws"]))
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for L, io, ws in ml:
+                csa.csa_decode_step(L, io, ws, stream=stream)
+        g.replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        e1.record(stream)
+    stream.synchronize()
+    del ml, g
+    return e0.elapsed_time(e1) / steps
+
+
 def time_prefill(csa, reps: int):
     """The prefill-shaped chunk (2048 queries at positions 260096..262143
     against 65536 compressed blocks, causal): csa_index_topk (multi-query
@@ -514,6 +567,7 @@ def main() -> int:
 
     fp8_ms, fp8_bytes, fp8_step_ms = time_fp8(csa, layers, shape, args.scan_reps, max(20, args.steps // 2))
     fp8_gbs = fp8_bytes / (fp8_ms * 1e-3) / 1e9
+    mixed_ms = time_mixed_kv(csa, layers, shape, max(20, args.steps // 2))
 
     cpu = None
     if args.cpu_budget > 0:
@@ -568,6 +622,13 @@ def main() -> int:
             "frac": round(fp8_gbs / HBM_PEAK_GBS, 4),
             "decode_steps_per_s": round(1e3 / fp8_step_ms, 2),
             "decode_ms_per_step": round(fp8_step_ms, 5),
+        },
+        "mixed_kv": {
+            "workload": "ctx1m decode step as above with mixed main KV: every compressed entry and window row "
+                        "a 592-byte record (448 E4M3 NoPE codes + scale, 64 bf16 RoPE values), RoPE on the new "
+                        "entry, inverse RoPE on the output",
+            "decode_steps_per_s": round(1e3 / mixed_ms, 2),
+            "decode_ms_per_step": round(mixed_ms, 5),
         },
         "prefill": prefill,
         "hca": hca,

@@ -22,6 +22,8 @@ from .binding import (  # noqa: F401
     csa_index_score_fp8,
     csa_index_topk,
     csa_index_topk_fp8,
+    csa_pack_kv_mixed,
+    MIX_REC_BYTES,
     csa_index_topk_workspace_size,
     csa_last_error,
     csa_layer_advance,

@@ -51,6 +51,9 @@ class LayerDesc(ctypes.Structure):
         ("scale", _f),
         ("n_comp", _i), ("swa_head", _i), ("swa_len", _i),
         ("idx_dtype", _i), ("idx_scales", _vp), ("idx_scales_stride_b", _ll),
+        ("kv_dtype", _i), ("rope_dim", _i),
+        ("rope_cos", _vp), ("rope_sin", _vp), ("rope_rows", _i),
+        ("comp_rope_cos", _vp), ("comp_rope_sin", _vp), ("comp_rope_rows", _i),
     ]
 
 
@@ -78,6 +81,7 @@ _SIGS = {
     "csa_index_score": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _ll, _ll, _ll,
                              _ll, _ll, _vp]),
     "csa_quantize_fp8": (_i, [_vp, _i, _vp, _vp, _ll, _i, _vp]),
+    "csa_pack_kv_mixed": (_i, [_vp, _i, _vp, _ll, _i, _i, _vp]),
     "csa_index_score_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _ll, _ll, _ll,
                                  _ll, _ll, _ll, _vp]),
     "csa_topk_workspace_size": (_sz, [_i, _i, _i, _i]),
@@ -192,6 +196,20 @@ def csa_quantize_fp8(x, codes, scales, stream=None) -> None:
     _check(lib().csa_quantize_fp8(_ptr(x), _dt(x), _ptr(codes), _ptr(scales), rows, d, _stream(stream)))
 
 
+MIX_REC_BYTES = 592  # one mixed main-KV row: 448 E4M3 codes, 64 bf16 RoPE values, scale, pad
+
+
+def csa_pack_kv_mixed(x, rec, stream=None) -> None:
+    """x [..., 512] float32 / bfloat16 (contiguous) -> rec [..., 592] uint8 mixed records."""
+    for t_, nm in ((x, "x"), (rec, "rec")):
+        if not t_.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if rec.dtype != torch.uint8 or rec.shape[:-1] != x.shape[:-1] or rec.shape[-1] != MIX_REC_BYTES:
+        raise ValueError("rec must be uint8 [..., 592] matching x's rows")
+    rows = x.numel() // x.shape[-1]
+    _check(lib().csa_pack_kv_mixed(_ptr(x), _dt(x), _ptr(rec), rows, x.shape[-1], 64, _stream(stream)))
+
+
 def csa_index_score_fp8(q, w, k, k_scale, scores, q_pos=None, ratio: int = 4, n: Optional[int] = None,
                         stream=None) -> None:
     """q [B, t, 64, 128] uint8 E4M3; w [B, t, 64] float32 (query scales folded in);
@@ -277,18 +295,34 @@ def csa_layer_advance(layer: LayerDesc, pos: int) -> None:
 def make_layer_desc(*, comp_kv, idx_keys, swa, main_bias, idx_bias, sink, n_comp: int,
                     swa_head: int, swa_len: int, h: int, h_i: int, m: int = 4, top_k: int,
                     overlap: int = 0, out_dtype=None, scale: Optional[float] = None,
-                    main_norm=None, idx_norm=None, idx_scales=None) -> LayerDesc:
+                    main_norm=None, idx_norm=None, idx_scales=None, rope=None, comp_rope=None) -> LayerDesc:
     """Fill a LayerDesc from cache tensors: comp_kv [B, max_comp, d], idx_keys
     [B, max_comp, d_i] (None for an HCA layer, with idx_bias None, h_i and
     top_k 0), swa [B, W, d].  idx_keys of torch.uint8 are E4M3 codes, with
-    their row scales in idx_scales [B, max_comp] float32.  The returned struct
+    their row scales in idx_scales [B, max_comp] float32.  comp_kv and swa of
+    torch.uint8 [B, rows, 592] are mixed main-KV records (d = 512), with
+    rope = (cos, sin) and comp_rope = (cos, sin) float32 tables
+    [rows, 32] of token positions and of block indices.  The returned struct
     keeps references to every tensor it points at."""
     B, max_comp, d = comp_kv.shape
+    mixed = comp_kv.dtype == torch.uint8
+    if mixed:
+        if d != MIX_REC_BYTES or swa.dtype != torch.uint8 or rope is None or comp_rope is None:
+            raise ValueError("mixed KV: comp_kv / swa uint8 [B, rows, 592] and both RoPE tables")
+        d = 512
     L = LayerDesc()
     L.batch, L.h, L.d, L.h_i, L.d_i = B, h, d, h_i, (idx_keys.shape[2] if idx_keys is not None else 0)
     L.m, L.w, L.top_k, L.overlap = m, swa.shape[1], top_k, overlap
-    L.dtype = _dt(comp_kv)
-    L.out_dtype = _dt(comp_kv) if out_dtype is None else (CSA_BF16 if out_dtype == torch.bfloat16 else CSA_F32)
+    L.dtype = CSA_BF16 if mixed else _dt(comp_kv)
+    L.out_dtype = L.dtype if out_dtype is None else (CSA_BF16 if out_dtype == torch.bfloat16 else CSA_F32)
+    if mixed:
+        L.kv_dtype, L.rope_dim = CSA_FP8_E4M3, 64
+        for t_ in (*rope, *comp_rope):
+            if t_.dtype != torch.float32 or not t_.is_contiguous() or t_.shape[-1] != 32:
+                raise ValueError("RoPE tables must be contiguous float32 [rows, 32]")
+        L.rope_cos, L.rope_sin, L.rope_rows = rope[0].data_ptr(), rope[1].data_ptr(), rope[0].shape[0]
+        L.comp_rope_cos, L.comp_rope_sin = comp_rope[0].data_ptr(), comp_rope[1].data_ptr()
+        L.comp_rope_rows = comp_rope[0].shape[0]
     L.comp_kv, L.comp_kv_stride_b = comp_kv.data_ptr(), comp_kv.stride(0)
     L.idx_keys, L.idx_keys_stride_b = _ptr(idx_keys), (idx_keys.stride(0) if idx_keys is not None else 0)
     L.swa, L.swa_stride_b = swa.data_ptr(), swa.stride(0)
@@ -306,7 +340,7 @@ def make_layer_desc(*, comp_kv, idx_keys, swa, main_bias, idx_bias, sink, n_comp
     else:
         L.idx_dtype = L.dtype
     # the struct holds raw device pointers: keep the tensors alive with it
-    L._keep = (comp_kv, idx_keys, swa, main_bias, idx_bias, sink, main_norm, idx_norm, idx_scales)
+    L._keep = (comp_kv, idx_keys, swa, main_bias, idx_bias, sink, main_norm, idx_norm, idx_scales, rope, comp_rope)
     return L
 
 

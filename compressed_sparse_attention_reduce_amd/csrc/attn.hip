@@ -44,7 +44,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
                                                              const float* __restrict__ sink, int h,
                                                              int d, int n_splits, void* __restrict__ out,
                                                              int out_bf16, float* __restrict__ lse,
-                                                             long long out_stride_b) {
+                                                             long long out_stride_b, const float* inv_cos,
+                                                             const float* inv_sin, int rope_start) {
     const int hh = blockIdx.x;
     const int b = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
@@ -122,6 +123,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
         }
     }
     if (has_col) {
+        // the RoPE dims rotated back at the token's position (a thread holds
+        // one (even, odd) pair)
+        if (inv_cos && col >= rope_start) {
+            const int pr = (col - rope_start) / 2;
+            rope_pair(acc.x, acc.y, inv_cos[pr], inv_sin[pr], true);
+        }
         const long long o = b * out_stride_b + static_cast<long long>(hh) * d + col;
         if (out_bf16) {
             static_cast<uint16_t*>(out)[o] = f32_to_bf16(acc.x);
@@ -232,7 +239,8 @@ hipError_t launch_attn_bf16(AttnArgs a, hipStream_t s) {
 
 hipError_t launch_attn_merge(const AttnArgs& a, int ns, hipStream_t s) {
     hipLaunchKernelGGL(k_attn_merge, dim3(a.h, a.batch), dim3(kAttnThreads), 0, s, a.ws_o, a.ws_ml, a.sink, a.h,
-                       a.d, ns, a.out, a.out_bf16 ? 1 : 0, a.lse, a.out_stride_b);
+                       a.d, ns, a.out, a.out_bf16 ? 1 : 0, a.lse, a.out_stride_b, a.inv_cos, a.inv_sin,
+                       a.d - kMixRope);
     return hipGetLastError();
 }
 

@@ -161,6 +161,19 @@ static int check_fp8_score_args(const void* q, const float* w, const void* k, co
     return CSA_OK;
 }
 
+int csa_pack_kv_mixed(const void* x, csa_dtype x_dtype, unsigned char* rec, long long rows, int d, int rope_dim,
+                      csa_stream stream) {
+    CHECK((x && rec) || rows == 0, "csa_pack_kv_mixed: null pointer argument");
+    CHECK(x_dtype == CSA_F32 || x_dtype == CSA_BF16, "csa_pack_kv_mixed: x must be float32 or bfloat16");
+    CHECK(rows >= 0 && rows <= (1LL << 31) * 4, "csa_pack_kv_mixed: rows %lld", rows);
+    if (d != csa::kMixD || rope_dim != csa::kMixRope)
+        return fail(CSA_ERR_UNSUPPORTED, "csa_pack_kv_mixed: needs d = %d, rope_dim = %d", csa::kMixD,
+                    csa::kMixRope);
+    CHECK(aligned16(rec) || rows == 0, "csa_pack_kv_mixed: rec must be 16-byte aligned");
+    return launched(csa::launch_pack_kv_mixed(x, x_dtype == CSA_BF16, rec, rows, static_cast<hipStream_t>(stream)),
+                    "csa_pack_kv_mixed");
+}
+
 int csa_index_score_fp8(const unsigned char* q, const float* w, const unsigned char* k, const float* k_scale,
                         float* scores, int batch, int t, int h_i, int d_i, int n, const int* q_pos, int ratio,
                         long long q_stride_b, long long w_stride_b, long long k_stride_b, long long ks_stride_b,
@@ -351,6 +364,23 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
     if (rc_a != CSA_OK) return rc_a;
     const int es = elem_size(L->dtype);
     CHECK((static_cast<long long>(L->d) * es) % 16 == 0, "csa_decode_step: row bytes must be a multiple of 16");
+    // mixed main KV: 592-byte records (mixed_kv.h), RoPE tables
+    const bool mixed = L->kv_dtype == CSA_FP8_E4M3;
+    if (mixed) {
+        if (L->dtype != CSA_BF16 || L->d != csa::kMixD || L->rope_dim != csa::kMixRope)
+            return fail(CSA_ERR_UNSUPPORTED, "csa_decode_step: mixed KV needs bfloat16, d = %d, rope_dim = %d",
+                        csa::kMixD, csa::kMixRope);
+        CHECK(L->rope_cos && L->rope_sin && L->comp_rope_cos && L->comp_rope_sin,
+              "csa_decode_step: mixed KV needs both RoPE tables");
+        CHECK(io->pos < L->rope_rows, "csa_decode_step: pos %d outside the RoPE table (%d rows)", io->pos,
+              L->rope_rows);
+        CHECK(!completes || io->pos / L->m < L->comp_rope_rows,
+              "csa_decode_step: block %d outside the compressed-entry RoPE table (%d rows)", io->pos / L->m,
+              L->comp_rope_rows);
+        CHECK(aligned16(L->comp_kv) && aligned16(L->swa) && aligned16(io->gather_buf) &&
+                  L->comp_kv_stride_b % 16 == 0 && L->swa_stride_b % 16 == 0 && io->gather_stride_b % 16 == 0,
+              "csa_decode_step: mixed records and their batch strides must be 16-byte aligned");
+    }
 
     CHECK(L->d <= csa::kPrepMaxD && L->d_i <= csa::kPrepMaxD, "csa_decode_step: head dims above %d", csa::kPrepMaxD);
     CHECK((static_cast<long long>(L->d_i) * es) % 16 == 0 || !completes, "csa_decode_step: d_i row bytes must be a multiple of 16");
@@ -402,6 +432,12 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
     pa.idx_fp8 = fp8 ? 1 : 0;
     pa.idx_scales = fp8 ? L->idx_scales : nullptr;
     pa.idx_scales_stride_b = fp8 ? L->idx_scales_stride_b : 0;
+    pa.kv_mixed = mixed ? 1 : 0;
+    if (mixed && completes) {
+        const long long row = static_cast<long long>(io->pos / L->m) * (csa::kMixRope / 2);
+        pa.entry_cos = L->comp_rope_cos + row;
+        pa.entry_sin = L->comp_rope_sin + row;
+    }
     // The bf16 and E4M3 score kernels runs these jobs in its first workgroups (and
     // scores the new key itself); the float32 path launches them first.
     const int n_scan = bf ? L->n_comp : N;
@@ -478,6 +514,12 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
         a.d = L->d;
         a.n_max = n_max;
         a.ws = aws;
+        if (mixed) {
+            const long long row = static_cast<long long>(io->pos) * (csa::kMixRope / 2);
+            a.kv_mixed = true;
+            a.inv_cos = L->rope_cos + row;
+            a.inv_sin = L->rope_sin + row;
+        }
         e = fuse ? csa::launch_topk_attn(ta, ca.lists ? &ca : nullptr, a, s) : csa::launch_attn_bf16(a, s);
         return launched(e, "csa_decode_step/attention");
     }
@@ -500,8 +542,8 @@ size_t csa_hca_decode_step_workspace_size(const csa_layer_desc* L) {
 int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes,
                         csa_stream stream) {
     CHECK(L && io, "csa_hca_decode_step: null layer or io");
-    if (L->dtype != CSA_BF16)
-        return fail(CSA_ERR_UNSUPPORTED, "csa_hca_decode_step: bfloat16 caches only");
+    if (L->dtype != CSA_BF16 || L->kv_dtype == CSA_FP8_E4M3)
+        return fail(CSA_ERR_UNSUPPORTED, "csa_hca_decode_step: bfloat16 caches only (no mixed KV)");
     CHECK(dtype_ok(L->out_dtype), "csa_hca_decode_step: bad out_dtype");
     CHECK(L->batch >= 1 && L->m >= 1 && L->w >= 1, "csa_hca_decode_step: bad batch/m/w");
     CHECK(L->overlap == 0, "csa_hca_decode_step: the HCA compressor is not overlapped (overlap must be 0)");

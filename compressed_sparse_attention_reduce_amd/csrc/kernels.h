@@ -110,6 +110,14 @@ hipError_t launch_gather(const void* comp_kv, int n_comp, const int* idx, const 
                          int* n_valid, int elem_bytes, int batch, int d, long long kv_stride_b,
                          long long swa_stride_b, long long buf_stride_b, hipStream_t s);
 
+// ---- mixed main-KV records (layout in mixed_kv.h) ---------------------------------
+constexpr int kMixD = 512;        // row width
+constexpr int kMixRope = 64;      // trailing RoPE dims, kept in bfloat16
+constexpr int kMixNope = kMixD - kMixRope;
+constexpr int kMixRec = 592;      // bytes per record: codes, RoPE, scale, pad
+constexpr int kMixScaleOff = 576;
+hipError_t launch_pack_kv_mixed(const void* x, bool x_bf16, uint8_t* rec, long long rows, hipStream_t s);
+
 // ---- sparse attention ----------------------------------------------------------
 struct AttnArgs {
     const uint16_t* q;
@@ -146,6 +154,13 @@ struct AttnArgs {
     void* ws;
     float* ws_o;   // set by the launcher
     float* ws_ml;  // set by the launcher
+    // mixed main KV (mixed_kv.h): comp_kv, swa and gather_buf hold 592-byte
+    // records (their strides in bytes; d = 512), decoded to bfloat16 on load;
+    // inv_cos / inv_sin (nullable): the table row of the token's position,
+    // the output's RoPE dims rotated back with it
+    bool kv_mixed;
+    const float* inv_cos;
+    const float* inv_sin;
 };
 size_t attn_workspace_bytes(bool bf16, int batch, int h, int d, int n_max);
 int attn_max_splits();
@@ -193,6 +208,12 @@ struct PrepArgs {
     long long comp_kv_stride_b;
     void* idx_keys;
     long long idx_keys_stride_b;
+    // mixed main KV (mixed_kv.h; swa and comp_kv records, strides in bytes):
+    // role 0 packs kv_new, role 1 packs the compressed entry with its RoPE
+    // dims rotated by the table row entry_cos / entry_sin
+    int kv_mixed;
+    const float* entry_cos;
+    const float* entry_sin;
 };
 hipError_t launch_step_prep(const PrepArgs& a, hipStream_t s);
 

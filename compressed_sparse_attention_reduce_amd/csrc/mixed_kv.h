@@ -1,0 +1,89 @@
+// Mixed main-KV rows: the NoPE part in E4M3 with one row scale, the RoPE
+// part in bfloat16 — page 2, single_shot_inference.py, eager_attention (the
+// "B1 storage-native mixed path": kv_quantize's E4M3 NoPE codes and scale,
+// the RoPE part kept in bfloat16 and rotated at the entry's position;
+// "Inverse RoPE" on the attention output).  The pairing of the RoPE dims is
+// that of page 1, PERFORMANCE_AUDIT.md P5 (_apply_rope: even / odd entries
+// of the trailing rope_dim).
+//
+// One row is one 592-byte record (d = 512, 64 RoPE dims), 16-byte aligned:
+//   bytes   0 .. 447  E4M3 codes of the NoPE part (OCP E4M3, as csa_quantize_fp8)
+//   bytes 448 .. 575  the 64 RoPE values, bfloat16
+//   bytes 576 .. 579  float32 scale of the codes (max |NoPE| / 448, 1 for zero)
+//   bytes 580 .. 591  zero
+#pragma once
+
+#include "common.h"
+#include "fp8_codec.h"
+#include "kernels.h"
+
+namespace csa {
+
+namespace {
+
+// Rotate the RoPE pair (e, o) by the table entry (c, s): forward
+// (e c - o s, e s + o c), inverse (e c + o s, -e s + o c).
+__device__ __forceinline__ void rope_pair(float& e, float& o, float c, float s, bool inverse) {
+    const float e0 = e, o0 = o;
+    if (inverse) {
+        e = e0 * c + o0 * s;
+        o = -e0 * s + o0 * c;
+    } else {
+        e = e0 * c - o0 * s;
+        o = e0 * s + o0 * c;
+    }
+}
+
+__device__ __forceinline__ float bf16_round(float x) { return bf16_to_f32(f32_to_bf16(x)); }
+
+// One wave writes the record of a row whose value j is get(j) (float32):
+// the NoPE part quantised as csa_quantize_fp8 does (binary32 division by the
+// scale, nearest-even codes), the RoPE part rounded to bfloat16 and, with a
+// table row (cos, sin: kMixRope / 2 values), rotated and rounded again.
+template <class Get>
+__device__ inline void wave_pack_mixed(Get get, uint8_t* rec, const float* cos, const float* sin) {
+    const int lane = threadIdx.x & (kWave - 1);
+    constexpr int kPer = kMixNope / kWave;  // 7 NoPE values per lane, consecutive
+    static_assert(kPer * kWave == kMixNope, "whole NoPE values per lane");
+    float v[kPer];
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        v[e] = get(kPer * lane + e);
+        amax = fmaxf(amax, fabsf(v[e]));
+    }
+    amax = wave_max(amax);
+    const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) rec[kPer * lane + e] = e4m3_encode_rne(v[e] / scale);
+    if (lane < kMixRope / 2) {
+        float ev = bf16_round(get(kMixNope + 2 * lane));
+        float od = bf16_round(get(kMixNope + 2 * lane + 1));
+        if (cos) rope_pair(ev, od, cos[lane], sin[lane], false);
+        const uint32_t packed = static_cast<uint32_t>(f32_to_bf16(ev)) | (static_cast<uint32_t>(f32_to_bf16(od)) << 16);
+        *reinterpret_cast<uint32_t*>(rec + kMixNope + 4 * lane) = packed;
+    } else if (lane == kMixRope / 2) {
+        *reinterpret_cast<float*>(rec + kMixScaleOff) = scale;
+    } else if (lane < kMixRope / 2 + 4) {
+        *reinterpret_cast<uint32_t*>(rec + kMixScaleOff + 4 * (lane - kMixRope / 2)) = 0u;
+    }
+}
+
+// Eight E4M3 codes (two words) times the row scale, as eight bfloat16
+// (nearest even) in a 16-byte piece.
+__device__ __forceinline__ uint4 decode8_bf16(uint32_t lo, uint32_t hi, float scale) {
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t src = p < 2 ? lo : hi;
+        const int sh = 16 * (p & 1);
+        const float a = e4m3_decode((src >> sh) & 0xffu) * scale;
+        const float b = e4m3_decode((src >> (sh + 8)) & 0xffu) * scale;
+        w[p] = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+}  // namespace
+
+}  // namespace csa

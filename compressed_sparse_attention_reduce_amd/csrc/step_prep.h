@@ -12,6 +12,7 @@
 #include "compress_impl.h"
 #include "fp8_codec.h"
 #include "kernels.h"
+#include "mixed_kv.h"
 
 namespace csa {
 
@@ -21,6 +22,14 @@ namespace csa {
 // holds the decoded codes then the row scale.
 __device__ inline void step_prep_role(const PrepArgs& a, int role, int b, float* ybuf, float* red,
                                       float* key = nullptr) {
+    if (role == 0 && a.kv_mixed) {  // the new (rotated) row packed into its ring slot by one wave
+        if (threadIdx.x < kWave) {
+            const uint16_t* src = static_cast<const uint16_t*>(a.kv_new) + b * a.kv_new_stride_b;
+            uint8_t* rec = static_cast<uint8_t*>(a.swa) + b * a.swa_stride_b + static_cast<long long>(a.swa_slot) * kMixRec;
+            wave_pack_mixed([&](int j) { return bf16_to_f32(src[j]); }, rec, nullptr, nullptr);
+        }
+        return;
+    }
     if (role == 0) {
         const char* src = static_cast<const char*>(a.kv_new) + b * a.kv_new_stride_b * a.es;
         char* dst = static_cast<char*>(a.swa) + (b * a.swa_stride_b + static_cast<long long>(a.swa_slot) * a.d) * a.es;
@@ -40,6 +49,21 @@ __device__ inline void step_prep_role(const PrepArgs& a, int role, int b, float*
         return;
     }
     const bool main = role == 1;
+    if (main && a.kv_mixed) {
+        // the entry in float32 (LDS past the compressor's own buffer), then
+        // one wave packs it with its RoPE dims rotated at the block index
+        float* y = ybuf + kPrepMaxD / 2;
+        const float* z = a.z_main + b * a.zc_main_stride_b;
+        const float* c = a.c_main + b * a.zc_main_stride_b;
+        compress_block(z, c, a.main_bias, a.main_norm, y, false, a.m, a.d, a.overlap != 0, a.block, ybuf, red);
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            uint8_t* rec = static_cast<uint8_t*>(a.comp_kv) + b * a.comp_kv_stride_b +
+                           static_cast<long long>(a.n_comp) * kMixRec;
+            wave_pack_mixed([&](int j) { return y[j]; }, rec, a.entry_cos, a.entry_sin);
+        }
+        return;
+    }
     if (!main && !a.idx_keys) return;  // a layer without an indexer (HCA)
     if (!main && a.idx_fp8) {
         // E4M3 indexer keys: the key in float32 (in `key`), quantised like

@@ -255,6 +255,12 @@ int csa_sparse_attn(const void *q, const void *kv, const int *n_valid, const flo
  *      idx_keys[n_comp] = compress(z_idx, c_idx) (overlap convention as in
  *      csa_compress, with first_block = pos / m);
  *   c. scores over the N = n_comp (+1 if b ran) keys, top-k, gather, attention.
+ * With mixed main KV (kv_dtype = CSA_FP8_E4M3, section 6c) step a packs
+ * kv_new (already rotated) into its ring record, step b packs the
+ * compressed entry with its RoPE dims rotated by comp_rope row pos / m, the
+ * attention decodes the records (E4M3 times scale, rounded to bfloat16) and
+ * the output's RoPE dims are rotated back by rope row pos; gather_buf holds
+ * records (gather_stride_b in bytes).
  * With E4M3 indexer keys (idx_dtype = CSA_FP8_E4M3; bfloat16 caches, h_i = 64,
  * d_i = 128) step b stores the compressed key as csa_quantize_fp8 would
  * (codes into idx_keys[n_comp], its scale into idx_scales[n_comp]) and step c
@@ -294,6 +300,17 @@ typedef struct csa_layer_desc {
      * folded into w_idx.  Any other value: keys stored as `dtype`. */
     csa_dtype idx_dtype;
     float *idx_scales; long long idx_scales_stride_b;
+    /* Mixed main KV (section 6c; appended: zero keeps comp_kv / swa rows of
+     * `dtype`): kv_dtype = CSA_FP8_E4M3 makes every comp_kv and swa row a
+     * 592-byte record (csa_pack_kv_mixed), comp_kv_stride_b and swa_stride_b
+     * in bytes.  rope_cos / rope_sin: [rope_rows][rope_dim / 2] float32, the
+     * table rows of token positions; comp_rope_cos / comp_rope_sin:
+     * [comp_rope_rows][rope_dim / 2], the rows of compressed entries by block
+     * index (pos / m). */
+    csa_dtype kv_dtype;
+    int rope_dim;
+    const float *rope_cos, *rope_sin; int rope_rows;
+    const float *comp_rope_cos, *comp_rope_sin; int comp_rope_rows;
 } csa_layer_desc;
 
 typedef struct csa_step_io {
@@ -323,6 +340,29 @@ int csa_decode_step(const csa_layer_desc *layer, const csa_step_io *io, void *ws
 
 /* Advance the host-known counters of `layer` past a step at position pos. */
 int csa_layer_advance(csa_layer_desc *layer, int pos);
+
+/* ------------------------------------------------------------------------
+ * 6c. Mixed main KV: E4M3 NoPE codes + bfloat16 RoPE part per row.
+ *
+ * Source: page 2, single_shot_inference.py, eager_attention (the "B1
+ * storage-native mixed path": kv_quantize's quantize_fp8_e4m3_from_fp32 of
+ * the NoPE part, the RoPE part kept in bfloat16 and rotated at the
+ * compressed entry's position, the FMHA over the mixed rows, then "Inverse
+ * RoPE" of the output); the RoPE pairing of page 1, PERFORMANCE_AUDIT.md P5
+ * (even / odd entries of the trailing rope_dim; inverse (e c + o s,
+ * -e s + o c), forward its inverse).
+ *
+ * Record of one row (d = 512, rope_dim = 64), 592 bytes, 16-byte aligned:
+ *   bytes 0..447 E4M3 codes of entries 0..447 (as csa_quantize_fp8: scale =
+ *   max|x| / 448 over those entries, 1 if all zero, nearest-even codes),
+ *   bytes 448..575 entries 448..511 as bfloat16 (nearest even),
+ *   bytes 576..579 the float32 scale, bytes 580..591 zero.
+ *
+ * csa_pack_kv_mixed: x [rows][512] float32 or bfloat16, contiguous ->
+ *   rec [rows][592] bytes (no rotation: rows are taken as already rotated).
+ * ------------------------------------------------------------------------ */
+int csa_pack_kv_mixed(const void *x, csa_dtype x_dtype, unsigned char *rec, long long rows, int d,
+                      int rope_dim, csa_stream stream);
 
 /* ------------------------------------------------------------------------
  * 6b. One decode step of an HCA layer (heavily compressed attention).

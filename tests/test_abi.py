@@ -297,6 +297,43 @@ def test_decode_step_fp8_keys_validation(csa):
     assert _desc(csa).idx_dtype == csa.CSA_F32 and _desc(csa).idx_scales is None
 
 
+def test_mixed_kv_validation(csa):
+    """Mixed main KV: bfloat16, d = 512, rope_dim = 64, both tables, table
+    rows for the position and the block, 16-byte records; no HCA form."""
+    B = csa.binding
+    lib = csa.lib()
+    L = _desc(csa, kv_dtype=csa.CSA_FP8_E4M3, rope_dim=64, rope_rows=5000, comp_rope_rows=1000)
+    need = csa.csa_decode_step_workspace_size(L)
+    io = _io(csa, pos=3999)
+
+    def call(layer):
+        return lib.csa_decode_step(ctypes.byref(layer), ctypes.byref(io), FAKE, need, None)
+
+    assert call(L) == B.CSA_ERR_INVALID_ARG      # tables missing
+    assert "RoPE" in csa.csa_last_error()
+    L.rope_cos = L.rope_sin = L.comp_rope_cos = L.comp_rope_sin = FAKE
+    L.rope_rows = 3999                           # the position's row missing
+    assert call(L) == B.CSA_ERR_INVALID_ARG
+    L.rope_rows = 5000
+    L.comp_rope_rows = 999                       # block 999's row missing
+    assert call(L) == B.CSA_ERR_INVALID_ARG
+    L.comp_rope_rows = 1000
+    L.rope_dim = 32
+    assert call(L) == B.CSA_ERR_UNSUPPORTED
+    L.rope_dim = 64
+    L.swa_stride_b = 592 * 128 + 8               # records must stay 16-byte aligned
+    assert call(L) == B.CSA_ERR_INVALID_ARG
+    L.swa_stride_b = 0
+    L.dtype = csa.CSA_F32
+    assert call(L) == B.CSA_ERR_UNSUPPORTED
+    L.dtype = csa.CSA_BF16
+    L.m = 128
+    assert lib.csa_hca_decode_step(ctypes.byref(L), ctypes.byref(io), FAKE, 1 << 40, None) == B.CSA_ERR_UNSUPPORTED
+    assert lib.csa_pack_kv_mixed(FAKE, csa.CSA_BF16, FAKE, 10, 256, 64, None) == B.CSA_ERR_UNSUPPORTED
+    assert lib.csa_pack_kv_mixed(FAKE, csa.CSA_FP8_E4M3, FAKE, 10, 512, 64, None) == B.CSA_ERR_INVALID_ARG
+    assert lib.csa_pack_kv_mixed(FAKE + 8, csa.CSA_BF16, FAKE + 8, 10, 512, 64, None) == B.CSA_ERR_INVALID_ARG
+
+
 def test_hca_step_validation(csa):
     B = csa.binding
     L = B.LayerDesc()
