@@ -70,18 +70,20 @@ __device__ inline void wave_pack_mixed(Get get, uint8_t* rec, const float* cos, 
 }
 
 // Eight E4M3 codes (two words) times the row scale, as eight bfloat16
-// (nearest even) in a 16-byte piece.
+// (nearest even) in a 16-byte piece: v_cvt_pk_f32_fp8 decodes two codes
+// exactly (gfx950 reads OCP E4M3), one float32 multiply each, and
+// v_cvt_pk_bf16_f32 rounds a pair.
 __device__ __forceinline__ uint4 decode8_bf16(uint32_t lo, uint32_t hi, float scale) {
-    uint32_t w[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t src = p < 2 ? lo : hi;
-        const int sh = 16 * (p & 1);
-        const float a = e4m3_decode((src >> sh) & 0xffu) * scale;
-        const float b = e4m3_decode((src >> (sh + 8)) & 0xffu) * scale;
-        w[p] = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    auto pack = [scale](decltype(__builtin_amdgcn_cvt_pk_f32_fp8(0, false)) f) -> uint32_t {
+        const __bf16 a = static_cast<__bf16>(f[0] * scale);
+        const __bf16 b = static_cast<__bf16>(f[1] * scale);
+        return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+    };
+    return make_uint4(pack(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), false)),
+                      pack(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), true)),
+                      pack(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), false)),
+                      pack(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), true)));
 }
 
 }  // namespace

@@ -197,6 +197,48 @@ def test_decode_steps_in_sequence_mixed_kv(csa):
         assert np.abs(outs["lse"][0].cpu().numpy() - rl).max() <= 1e-2
 
 
+def test_mixed_step_decodes_every_code(csa):
+    """The first token of a layer with nothing before it: the attention sees
+    one row (the token's own record), so with no sink and identity tables
+    every head's output is that row exactly.  Its NoPE part holds every
+    finite E4M3 code times 1/8 (with +-448/8 setting the scale to 1/8), so
+    the attention's decoding of every code is checked bit for bit."""
+    g = _g(7301)
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    codes = np.resize(finite, NOPE)
+    codes[0] = 0x7E
+    vals = np.concatenate([numfmt.e4m3_decode(codes) * 0.125,
+                           numfmt.bf16_round_f64(g.standard_normal(ROPE))])
+    kvn = numfmt.f64_to_bf16_bits(vals)[None]
+    assert np.array_equal(numfmt.bf16_bits_to_f64(kvn[0]), vals)
+    H, K, W, max_comp = 16, 8, 4, 8
+    comp = torch.zeros(1, max_comp, REC, dtype=torch.uint8, device=DEV)
+    swa = torch.zeros(1, W, REC, dtype=torch.uint8, device=DEV)
+    keys = torch.zeros(1, max_comp, 128, dtype=torch.bfloat16, device=DEV)
+    ones, zeros = torch.ones(4, 32, device=DEV), torch.zeros(4, 32, device=DEV)
+    L = csa.make_layer_desc(comp_kv=comp, idx_keys=keys, swa=swa, main_bias=torch.zeros(4, 512, device=DEV),
+                            idx_bias=torch.zeros(4, 128, device=DEV), sink=None, n_comp=0, swa_head=0, swa_len=0,
+                            h=H, h_i=64, top_k=K, rope=(ones, zeros), comp_rope=(ones, zeros))
+    q = dev_bf16(synth.to_bf16_bits(g.standard_normal((1, H, 512), dtype=np.float32)))
+    qi = dev_bf16(synth.to_bf16_bits(g.standard_normal((1, 64, 128), dtype=np.float32)))
+    out = torch.empty(1, H, 512, dtype=torch.bfloat16, device=DEV)
+    io = csa.make_step_io(pos=0, q=q, q_idx=qi, w_idx=torch.ones(1, 64, device=DEV), kv_new=dev_bf16(kvn),
+                          z_main=torch.zeros(1, 4, 512, device=DEV), c_main=torch.zeros(1, 4, 512, device=DEV),
+                          z_idx=torch.zeros(1, 4, 128, device=DEV), c_idx=torch.zeros(1, 4, 128, device=DEV),
+                          scores=torch.empty(1, max_comp, device=DEV),
+                          topk_idx=torch.empty(1, K, dtype=torch.int32, device=DEV),
+                          topk_count=torch.empty(1, dtype=torch.int32, device=DEV),
+                          gather_buf=torch.zeros(1, K + W, REC, dtype=torch.uint8, device=DEV),
+                          n_valid=torch.empty(1, dtype=torch.int32, device=DEV), out=out)
+    ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+    csa.csa_decode_step(L, io, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(swa[0, 0, :NOPE].cpu().numpy(), codes)
+    got = host_f64(out[0])
+    for h in range(H):
+        np.testing.assert_array_equal(got[h], vals)
+
+
 def test_decode_step_ctx1m_mixed_kv_full_size(csa):
     """One layer of the 1M-context workload over mixed caches packed on the
     GPU (csa_pack_kv_mixed, bit-exact above) from the bf16 caches: gather_buf
