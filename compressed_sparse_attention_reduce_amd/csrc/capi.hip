@@ -318,8 +318,17 @@ size_t csa_decode_step_workspace_size(const csa_layer_desc* L) {
            256;
 }
 
-int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes,
-                    csa_stream stream) {
+size_t csa_decode_step_dev_ring_size(const csa_layer_desc* L) {
+    if (!L || L->batch < 1 || L->m < 1 || L->d < 1 || L->d_i < 0) return 0;
+    const size_t wm = static_cast<size_t>(L->overlap ? 2 * L->d : L->d);
+    const size_t wi = static_cast<size_t>(L->overlap ? 2 * L->d_i : L->d_i);
+    return sizeof(float) * static_cast<size_t>(L->batch) * 4 * L->m * (wm + wi);
+}
+
+// The decode step; dev != nullptr: the counters are read from and advanced
+// on the device (csa_decode_step_dev), the block rows kept in `ring`.
+static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes,
+                       csa_stream stream, csa::DevState* dev, float* ring, size_t ring_bytes) {
     CHECK(L && io, "csa_decode_step: null layer or io");
     CHECK(dtype_ok(L->dtype) && dtype_ok(L->out_dtype), "csa_decode_step: bad dtype");
     CHECK(L->batch >= 1 && L->m >= 1 && L->w >= 1 && L->top_k >= 1 && L->top_k <= csa::kTopkMaxK,
@@ -330,13 +339,27 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
     CHECK(io->q && io->q_idx && io->w_idx && io->kv_new && io->scores && io->topk_idx &&
               io->topk_count && io->gather_buf && io->n_valid && io->out,
           "csa_decode_step: null io pointer");
-    CHECK(io->pos >= 0, "csa_decode_step: pos < 0");
-    CHECK(L->n_comp >= 0 && L->n_comp <= L->max_comp, "csa_decode_step: n_comp %d outside 0..max_comp %d",
-          L->n_comp, L->max_comp);
-    CHECK(L->swa_head >= 0 && L->swa_head < L->w && L->swa_len >= 0 && L->swa_len <= L->w,
-          "csa_decode_step: bad SWA state");
-    const bool completes = io->pos % L->m == L->m - 1;
-    if (completes) {
+    if (dev) {
+        // the counters live on the device; every step brings its token's Z/C rows
+        CHECK(aligned16(dev), "csa_decode_step_dev: state must be 16-byte aligned");
+        CHECK(io->z_main && io->c_main && io->z_idx && io->c_idx, "csa_decode_step_dev: Z/C rows missing");
+        CHECK(ring && aligned16(ring), "csa_decode_step_dev: ring must be non-null and 16-byte aligned");
+        CHECK(ring_bytes >= csa_decode_step_dev_ring_size(L), "csa_decode_step_dev: ring %zu < %zu bytes",
+              ring_bytes, csa_decode_step_dev_ring_size(L));
+        CHECK(L->max_comp >= 1, "csa_decode_step_dev: max_comp must be positive");
+        if (L->dtype != CSA_BF16 || L->idx_dtype == CSA_FP8_E4M3)
+            return fail(CSA_ERR_UNSUPPORTED, "csa_decode_step_dev: bfloat16 caches and indexer keys only");
+    } else {
+        CHECK(io->pos >= 0, "csa_decode_step: pos < 0");
+        CHECK(L->n_comp >= 0 && L->n_comp <= L->max_comp, "csa_decode_step: n_comp %d outside 0..max_comp %d",
+              L->n_comp, L->max_comp);
+        CHECK(L->swa_head >= 0 && L->swa_head < L->w && L->swa_len >= 0 && L->swa_len <= L->w,
+              "csa_decode_step: bad SWA state");
+    }
+    // with device counters: the roles that may compress are launched, the
+    // kernels decide; N is bounded by the cache capacity
+    const bool completes = dev ? true : io->pos % L->m == L->m - 1;
+    if (completes && !dev) {
         CHECK(io->z_main && io->c_main && io->z_idx && io->c_idx, "csa_decode_step: block rows missing");
         CHECK(L->n_comp < L->max_comp, "csa_decode_step: compressed cache full (max_comp %d)", L->max_comp);
     }
@@ -344,7 +367,7 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
     if (ws_bytes < csa_decode_step_workspace_size(L))
         return fail(CSA_ERR_WORKSPACE, "csa_decode_step: workspace %zu < %zu bytes", ws_bytes,
                     csa_decode_step_workspace_size(L));
-    const int N = L->n_comp + (completes ? 1 : 0);
+    const int N = dev ? L->max_comp : L->n_comp + (completes ? 1 : 0);
     // E4M3 indexer keys: bfloat16 everything else, the FP8 score kernel
     const bool fp8 = L->idx_dtype == CSA_FP8_E4M3;
     if (fp8 && L->dtype != CSA_BF16)
@@ -372,9 +395,10 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
                         csa::kMixD, csa::kMixRope);
         CHECK(L->rope_cos && L->rope_sin && L->comp_rope_cos && L->comp_rope_sin,
               "csa_decode_step: mixed KV needs both RoPE tables");
-        CHECK(io->pos < L->rope_rows, "csa_decode_step: pos %d outside the RoPE table (%d rows)", io->pos,
+        CHECK(L->rope_rows >= 1 && L->comp_rope_rows >= 1, "csa_decode_step: empty RoPE table");
+        CHECK(dev || io->pos < L->rope_rows, "csa_decode_step: pos %d outside the RoPE table (%d rows)", io->pos,
               L->rope_rows);
-        CHECK(!completes || io->pos / L->m < L->comp_rope_rows,
+        CHECK(dev || !completes || io->pos / L->m < L->comp_rope_rows,
               "csa_decode_step: block %d outside the compressed-entry RoPE table (%d rows)", io->pos / L->m,
               L->comp_rope_rows);
         CHECK(aligned16(L->comp_kv) && aligned16(L->swa) && aligned16(io->gather_buf) &&
@@ -402,14 +426,14 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
     pa.m = L->m;
     pa.overlap = L->overlap;
     pa.completes = completes ? 1 : 0;
-    pa.n_comp = L->n_comp;
-    pa.block = io->pos / L->m;
+    pa.n_comp = dev ? 0 : L->n_comp;
+    pa.block = dev ? 0 : io->pos / L->m;
     pa.kv_new = io->kv_new;
     pa.kv_new_stride_b = io->kv_new_stride_b;
     pa.swa = L->swa;
     pa.swa_stride_b = L->swa_stride_b;
     pa.swa_slot = L->swa_head;
-    if (completes) {
+    if (completes && !dev) {
         // the overlapped form passes the previous block's rows first
         const bool joint = L->overlap && io->pos / L->m > 0;
         const long long skip_main = joint ? static_cast<long long>(L->m) * 2 * L->d : 0;
@@ -432,15 +456,29 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
     pa.idx_fp8 = fp8 ? 1 : 0;
     pa.idx_scales = fp8 ? L->idx_scales : nullptr;
     pa.idx_scales_stride_b = fp8 ? L->idx_scales_stride_b : 0;
+    if (dev) {  // the token's own rows; the kernels keep the block in the ring
+        pa.z_main = io->z_main;
+        pa.c_main = io->c_main;
+        pa.z_idx = io->z_idx;
+        pa.c_idx = io->c_idx;
+        pa.dev = dev;
+        pa.max_comp = L->max_comp;
+        pa.swa_w = L->w;
+        pa.dev_ring = ring;
+        pa.ring_stride_b = static_cast<long long>(csa_decode_step_dev_ring_size(L) / sizeof(float) / L->batch);
+        pa.comp_rope_cos = L->comp_rope_cos;
+        pa.comp_rope_sin = L->comp_rope_sin;
+        pa.comp_rope_rows = L->comp_rope_rows;
+    }
     pa.kv_mixed = mixed ? 1 : 0;
-    if (mixed && completes) {
+    if (mixed && completes && !dev) {
         const long long row = static_cast<long long>(io->pos / L->m) * (csa::kMixRope / 2);
         pa.entry_cos = L->comp_rope_cos + row;
         pa.entry_sin = L->comp_rope_sin + row;
     }
     // The bf16 and E4M3 score kernels runs these jobs in its first workgroups (and
     // scores the new key itself); the float32 path launches them first.
-    const int n_scan = bf ? L->n_comp : N;
+    const int n_scan = dev ? L->max_comp : (bf ? L->n_comp : N);
     const int prep_wgs = bf ? (completes ? 3 : 1) : 0;
     if (!bf) {
         e = csa::launch_step_prep(pa, s);
@@ -458,12 +496,12 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
                             : csa::index_score_bf16_keys_per_wg(L->batch, n_scan, prep_wgs);
         const int m = kpw > 0 ? csa::topk_cand_m(N, L->top_k, kpw) : -1;
         const int mw = kpw > 0 ? csa::topk_cand_m(N, L->top_k, kpw / csa::kScoreWavesPerWg) : -1;
-        if (m > 0 && slots <= kStepMaxSlots && N > 4 * L->top_k)
+        if (m > 0 && slots <= kStepMaxSlots && (dev || N > 4 * L->top_k))
             ca = csa::CandArgs{static_cast<unsigned long long*>(tws), slots, m, mw < m ? mw : m};
     }
     csa::ScoreArgs sa{io->q_idx, io->w_idx, L->idx_keys, io->scores, L->batch, 1, L->h_i, L->d_i, n_scan,
                       nullptr, L->m, io->q_idx_stride_b, io->w_stride_b, L->idx_keys_stride_b,
-                      io->scores_stride_b, N, ca};
+                      io->scores_stride_b, N, ca, dev};
     if (fp8) {
         const csa::Fp8ScoreArgs fa{static_cast<const uint8_t*>(io->q_idx), io->w_idx,
                                    static_cast<const uint8_t*>(L->idx_keys), L->idx_scales, io->scores,
@@ -478,7 +516,7 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
                      io->topk_count, tws};
     // bf16 with candidate lists (or a short row): every attention workgroup
     // selects the top k itself, no separate top-k launch
-    const bool fuse = bf && (ca.lists || N <= kFuseExactMaxN);
+    const bool fuse = bf && (ca.lists || N <= kFuseExactMaxN || dev);
     if (!fuse) {
         e = csa::launch_topk(ta, ca.lists ? &ca : nullptr, s);
         if (e != hipSuccess) return launched(e, "csa_decode_step/topk");
@@ -515,13 +553,24 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
         a.n_max = n_max;
         a.ws = aws;
         if (mixed) {
-            const long long row = static_cast<long long>(io->pos) * (csa::kMixRope / 2);
             a.kv_mixed = true;
-            a.inv_cos = L->rope_cos + row;
-            a.inv_sin = L->rope_sin + row;
+            if (!dev) {
+                const long long row = static_cast<long long>(io->pos) * (csa::kMixRope / 2);
+                a.inv_cos = L->rope_cos + row;
+                a.inv_sin = L->rope_sin + row;
+            }
+        }
+        if (dev) {
+            a.dev = dev;
+            a.m = L->m;
+            a.max_comp = L->max_comp;
+            a.rope_cos = L->rope_cos;
+            a.rope_sin = L->rope_sin;
+            a.rope_rows = L->rope_rows;
         }
         e = fuse ? csa::launch_topk_attn(ta, ca.lists ? &ca : nullptr, a, s) : csa::launch_attn_bf16(a, s);
-        return launched(e, "csa_decode_step/attention");
+        if (e != hipSuccess || !dev) return launched(e, "csa_decode_step/attention");
+        return launched(csa::launch_step_advance(dev, L->m, L->w, L->max_comp, s), "csa_decode_step_dev/advance");
     }
     e = csa::launch_gather(L->comp_kv, N, io->topk_idx, io->topk_count, L->top_k, L->swa, swa_head,
                            swa_len, L->w, io->gather_buf, io->n_valid, es, L->batch, L->d,
@@ -531,6 +580,18 @@ int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, si
                              L->out_dtype == CSA_BF16, io->lse, L->batch, L->h, L->d, n_max,
                              io->q_stride_b, io->gather_stride_b, io->out_stride_b, s);
     return launched(e, "csa_decode_step/attention");
+}
+
+int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes,
+                    csa_stream stream) {
+    return decode_step(L, io, ws, ws_bytes, stream, nullptr, nullptr, 0);
+}
+
+int csa_decode_step_dev(const csa_layer_desc* L, const csa_step_io* io, csa_dev_state* state, float* ring,
+                        size_t ring_bytes, void* ws, size_t ws_bytes, csa_stream stream) {
+    static_assert(sizeof(csa_dev_state) == sizeof(csa::DevState), "device counters as the kernels read them");
+    CHECK(state, "csa_decode_step_dev: null state");
+    return decode_step(L, io, ws, ws_bytes, stream, reinterpret_cast<csa::DevState*>(state), ring, ring_bytes);
 }
 
 size_t csa_hca_decode_step_workspace_size(const csa_layer_desc* L) {

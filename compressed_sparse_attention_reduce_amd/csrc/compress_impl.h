@@ -24,7 +24,7 @@ __device__ inline void compress_block(const float* __restrict__ z, const float* 
                                       const float* __restrict__ bias, const float* __restrict__ norm_w,
                                       void* __restrict__ out_row, bool out_bf16, int m, int d,
                                       bool overlap, long long g, float* ybuf, float* red,
-                                      float* keep = nullptr) {
+                                      float* keep = nullptr, long long prev_off = 0) {
     const int width = overlap ? 2 * d : d;
     const bool joint = overlap && g > 0;  // previous block's a half joins the softmax
     const int own_col = overlap ? d : 0;  // this block's rows: b half when overlapped
@@ -47,7 +47,8 @@ __device__ inline void compress_block(const float* __restrict__ z, const float* 
                     const bool prev = joint && r < m;
                     const int t = prev ? r : (joint ? r - m : r);
                     const int col = prev ? ch : own_col + ch;
-                    const long long o = (prev ? -static_cast<long long>(m) * width : 0) +
+                    // the previous block's rows: just before z, or prev_off elements from it
+                    const long long o = (prev ? (prev_off ? prev_off : -static_cast<long long>(m) * width) : 0) +
                                         static_cast<long long>(t) * width + col;
                     lz[u] = z[o] + bias[t * width + col];
                     lc[u] = c[o];

@@ -96,15 +96,22 @@ __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs
     const int row = blockIdx.y;
     const int b = row / a.t;
     const int tt = row - b * a.t;
+    // keys already in the cache (with device counters: as the step starts)
+    const int n_keys = a.dev ? dev_load(a.dev, p.swa_w > 0 ? p.swa_w : 1, a.n).n_comp : a.n;
 
     // 0. the decode step's small jobs (one query row per sequence), and the
     //    new key of a completed block: compressed, scored, given its own slot
     if (static_cast<int>(blockIdx.x) < prep_wgs) {
         float* ybuf = reinterpret_cast<float*>(qs);
         step_prep_role(p, blockIdx.x, b, ybuf, ws, ybuf);
-        if (blockIdx.x == 2 && p.completes) {
+        const bool completes = p.dev ? dev_completes(dev_load(p.dev, p.swa_w, p.max_comp), p.m, p.max_comp)
+                                     : p.completes != 0;
+        if (blockIdx.x == 2 && !completes && kCands && p.dev && threadIdx.x <= a.cands.m)  // an empty last slot
+            a.cands.lists[(static_cast<long long>(row) * a.cands.slots + a.cands.slots - 1) * (a.cands.m + 1) +
+                          threadIdx.x] = 0ull;
+        if (blockIdx.x == 2 && completes) {
             float sc = score_one_key(a, b, tt, ybuf, ws + 8);
-            const int key = a.n;
+            const int key = n_keys;
             if (a.q_pos && static_cast<long long>(a.ratio) * key + a.ratio - 1 > a.q_pos[row]) sc = -INFINITY;
             if (threadIdx.x == 0) a.scores[b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s + key] = sc;
             if (kCands && threadIdx.x <= a.cands.m) {
@@ -120,7 +127,8 @@ __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs
     const int scan_wgs = gridDim.x - prep_wgs;
     const int li = lane & 15;   // key column of B / head row of A within a 16-tile
     const int lg = lane >> 4;   // 8-element group of each 32-wide k-step
-    const int n = a.n;
+    const int n = n_keys;
+    if (a.dev) tiles_per_row = (n + kTileKeys - 1) / kTileKeys;
     if (n <= 0) {  // nothing to scan: an empty candidate list
         if (kCands && threadIdx.x <= a.cands.m)
             a.cands.lists[(static_cast<long long>(row) * a.cands.slots + wg) * (a.cands.m + 1) + threadIdx.x] = 0ull;

@@ -35,6 +35,30 @@ struct CandArgs {
 // or -1 if lists would be too long.
 int topk_cand_m(int n, int k, int keys_per_slot);
 
+// ---- counters of a decode step held on the device (graph replay) --------------
+// Same layout as csa_dev_state.  A step reads them when its kernels run and
+// k_step_advance moves them past the step afterwards.
+struct DevState {
+    int pos, n_comp, swa_head, swa_len, flags;
+};
+constexpr int kDevFlagCacheFull = 1;  // a completed block found the compressed cache full
+// The counters as the kernels use them: every index kept inside the caches
+// whatever the caller stored (pos >= 0, 0 <= n_comp <= max_comp, the ring
+// head and length inside the window w).
+__host__ __device__ inline DevState dev_load(const DevState* p, int w, int max_comp) {
+    DevState s = *p;
+    s.pos = s.pos < 0 ? 0 : s.pos;
+    s.n_comp = s.n_comp < 0 ? 0 : (s.n_comp > max_comp ? max_comp : s.n_comp);
+    s.swa_head = ((s.swa_head % w) + w) % w;
+    s.swa_len = s.swa_len < 0 ? 0 : (s.swa_len > w ? w : s.swa_len);
+    return s;
+}
+// The step completes a block (and has room for its entry).
+__host__ __device__ inline bool dev_completes(const DevState& s, int m, int max_comp) {
+    return s.pos % m == m - 1 && s.n_comp < max_comp;
+}
+hipError_t launch_step_advance(DevState* st, int m, int w, int max_comp, hipStream_t s);
+
 // ---- lightning-indexer score -------------------------------------------------
 struct ScoreArgs {
     const void* q;
@@ -48,6 +72,9 @@ struct ScoreArgs {
     // optional top-k candidates: every workgroup writes the top m + 1 of its
     // keys to its slot of cands.lists (cands.slots must equal its grid width)
     CandArgs cands;
+    // decode step with device counters: n = dev->n_comp when the kernel runs
+    // (the grid is sized for the n given here, the cache capacity)
+    const DevState* dev;
 };
 constexpr int kScoreWavesPerWg = 4;  // waves per workgroup of the bf16 score kernel
 // Scan workgroups per row and keys per scan workgroup of the bf16 score
@@ -161,6 +188,16 @@ struct AttnArgs {
     bool kv_mixed;
     const float* inv_cos;
     const float* inv_sin;
+    // decode step with device counters (gather mode): n_comp, swa_head,
+    // swa_len and the top-k row length are taken from dev when the kernel
+    // runs, as the step after the prep jobs sees them (m, max_comp decide a
+    // completed block); with mixed KV the inverse-RoPE row is rope_cos /
+    // rope_sin + pos * kMixRope / 2
+    const DevState* dev;
+    int m, max_comp;
+    const float* rope_cos;
+    const float* rope_sin;
+    int rope_rows;  // positions past the table use its last row
 };
 size_t attn_workspace_bytes(bool bf16, int batch, int h, int d, int n_max);
 int attn_max_splits();
@@ -214,6 +251,19 @@ struct PrepArgs {
     int kv_mixed;
     const float* entry_cos;
     const float* entry_sin;
+    // device counters (nullptr: the host values above): completes, n_comp,
+    // block and swa_slot come from dev; the block's Z/C rows are kept in a
+    // ring of two blocks per array (dev_ring: [B][4][2m][width] floats, the
+    // arrays z_main, c_main, z_idx, c_idx; z_* / c_* above are then the new
+    // token's rows); comp_rope_cos / _sin: table bases (mixed KV)
+    const DevState* dev;
+    int max_comp;
+    int swa_w;  // window rows (the ring head is kept below it)
+    float* dev_ring;
+    long long ring_stride_b;
+    const float* comp_rope_cos;
+    const float* comp_rope_sin;
+    int comp_rope_rows;  // blocks past the table use its last row
 };
 hipError_t launch_step_prep(const PrepArgs& a, hipStream_t s);
 

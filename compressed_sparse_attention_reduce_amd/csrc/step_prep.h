@@ -19,9 +19,11 @@ namespace csa {
 // ybuf: kPrepMaxD floats of LDS; red: blockDim/64 floats of LDS.  key (LDS,
 // may be ybuf): role 2 leaves the stored key there as floats (synchronised);
 // with E4M3 keys (idx_fp8) key must be d_i + 1 floats apart from ybuf, and
-// holds the decoded codes then the row scale.
-__device__ inline void step_prep_role(const PrepArgs& a, int role, int b, float* ybuf, float* red,
-                                      float* key = nullptr) {
+// holds the decoded codes then the row scale.  prev_main / prev_idx: where
+// the previous block's rows sit relative to the block's first row (0: just
+// before it).
+__device__ inline void step_prep_role_at(const PrepArgs& a, int role, int b, float* ybuf, float* red, float* key,
+                                         long long prev_main, long long prev_idx) {
     if (role == 0 && a.kv_mixed) {  // the new (rotated) row packed into its ring slot by one wave
         if (threadIdx.x < kWave) {
             const uint16_t* src = static_cast<const uint16_t*>(a.kv_new) + b * a.kv_new_stride_b;
@@ -55,7 +57,8 @@ __device__ inline void step_prep_role(const PrepArgs& a, int role, int b, float*
         float* y = ybuf + kPrepMaxD / 2;
         const float* z = a.z_main + b * a.zc_main_stride_b;
         const float* c = a.c_main + b * a.zc_main_stride_b;
-        compress_block(z, c, a.main_bias, a.main_norm, y, false, a.m, a.d, a.overlap != 0, a.block, ybuf, red);
+        compress_block(z, c, a.main_bias, a.main_norm, y, false, a.m, a.d, a.overlap != 0, a.block, ybuf, red,
+                       nullptr, prev_main);
         __syncthreads();
         if (threadIdx.x < kWave) {
             uint8_t* rec = static_cast<uint8_t*>(a.comp_kv) + b * a.comp_kv_stride_b +
@@ -72,7 +75,8 @@ __device__ inline void step_prep_role(const PrepArgs& a, int role, int b, float*
         // decoded codes and key[a.d_i] the scale (synchronised)
         const float* z = a.z_idx + b * a.zc_idx_stride_b;
         const float* c = a.c_idx + b * a.zc_idx_stride_b;
-        compress_block(z, c, a.idx_bias, a.idx_norm, key, false, a.m, a.d_i, a.overlap != 0, a.block, ybuf, red);
+        compress_block(z, c, a.idx_bias, a.idx_norm, key, false, a.m, a.d_i, a.overlap != 0, a.block, ybuf, red,
+                       nullptr, prev_idx);
         __syncthreads();
         float amax = 0.f;
         for (int j = threadIdx.x; j < a.d_i; j += blockDim.x) amax = fmaxf(amax, fabsf(key[j]));
@@ -103,7 +107,74 @@ __device__ inline void step_prep_role(const PrepArgs& a, int role, int b, float*
     char* out = static_cast<char*>(main ? a.comp_kv : a.idx_keys) +
                 (b * (main ? a.comp_kv_stride_b : a.idx_keys_stride_b) + static_cast<long long>(a.n_comp) * d) * a.es;
     compress_block(z, c, main ? a.main_bias : a.idx_bias, main ? a.main_norm : a.idx_norm, out, a.es == 2, a.m, d,
-                   a.overlap != 0, a.block, ybuf, red, main ? nullptr : key);
+                   a.overlap != 0, a.block, ybuf, red, main ? nullptr : key, main ? prev_main : prev_idx);
+}
+
+// The jobs with the counters on the device (a.dev): this step's completion,
+// entry index, block and ring slot come from *a.dev; the block's Z/C rows
+// from a ring of two blocks per array that every step adds its token's rows
+// to (role 0 when no block completes; roles 1 and 2 their own arrays, just
+// before compressing from the ring, when one does).
+__device__ inline void step_prep_role(const PrepArgs& a, int role, int b, float* ybuf, float* red,
+                                      float* key = nullptr) {
+    if (!a.dev) {
+        step_prep_role_at(a, role, b, ybuf, red, key, 0, 0);
+        return;
+    }
+    const DevState st = dev_load(a.dev, a.swa_w, a.max_comp);
+    PrepArgs p = a;
+    p.completes = dev_completes(st, a.m, a.max_comp) ? 1 : 0;
+    p.n_comp = st.n_comp;
+    p.block = st.pos / a.m;
+    p.swa_slot = st.swa_head;
+    if (p.kv_mixed && p.completes) {
+        const long long row = p.block < a.comp_rope_rows ? p.block : a.comp_rope_rows - 1;
+        p.entry_cos = a.comp_rope_cos + row * (kMixRope / 2);
+        p.entry_sin = a.comp_rope_sin + row * (kMixRope / 2);
+    }
+    const int wm = a.overlap ? 2 * a.d : a.d;
+    const int wi = a.overlap ? 2 * a.d_i : a.d_i;
+    float* ring = a.dev_ring + b * a.ring_stride_b;
+    float* rz_main = ring;
+    float* rc_main = ring + 2LL * a.m * wm;
+    float* rz_idx = ring + 4LL * a.m * wm;
+    float* rc_idx = rz_idx + 2LL * a.m * wi;
+    const int slot = st.pos % (2 * a.m);
+    auto put = [&](float* dst, const float* src, int width) {
+        for (int j = threadIdx.x; j < width; j += blockDim.x) dst[static_cast<long long>(slot) * width + j] = src[j];
+    };
+    const float* nz_main = a.z_main + b * a.zc_main_stride_b;
+    const float* nc_main = a.c_main + b * a.zc_main_stride_b;
+    const float* nz_idx = a.z_idx + b * a.zc_idx_stride_b;
+    const float* nc_idx = a.c_idx + b * a.zc_idx_stride_b;
+    const bool idx = a.idx_keys != nullptr;
+    if (role == 0 && !p.completes) {
+        put(rz_main, nz_main, wm);
+        put(rc_main, nc_main, wm);
+        if (idx) {
+            put(rz_idx, nz_idx, wi);
+            put(rc_idx, nc_idx, wi);
+        }
+    } else if (p.completes && (role == 1 || (role == 2 && idx))) {
+        if (role == 1) {
+            put(rz_main, nz_main, wm);
+            put(rc_main, nc_main, wm);
+        } else {
+            put(rz_idx, nz_idx, wi);
+            put(rc_idx, nc_idx, wi);
+        }
+        __syncthreads();  // the ring rows of this workgroup's array are complete
+    }
+    // the block's first row in the ring, and where the previous block's are
+    const long long cur = (p.block & 1) * static_cast<long long>(a.m);
+    const long long prev_rows = (1 - 2 * (p.block & 1)) * static_cast<long long>(a.m);
+    p.z_main = rz_main + cur * wm;
+    p.c_main = rc_main + cur * wm;
+    p.z_idx = rz_idx + cur * wi;
+    p.c_idx = rc_idx + cur * wi;
+    p.zc_main_stride_b = 0;  // already this sequence's ring
+    p.zc_idx_stride_b = 0;
+    step_prep_role_at(p, role, b, ybuf, red, key, prev_rows * wm, prev_rows * wi);
 }
 
 }  // namespace csa

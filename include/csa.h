@@ -338,6 +338,43 @@ size_t csa_decode_step_workspace_size(const csa_layer_desc *layer);
 int csa_decode_step(const csa_layer_desc *layer, const csa_step_io *io, void *ws,
                     size_t ws_bytes, csa_stream stream);
 
+/* ------------------------------------------------------------------------
+ * 6d. The decode step with its counters on the device (graph replay).
+ *
+ * Source: page 3, GETTING+CUDAGRAPH_READY.md, Section C: the compressor runs
+ * every step into a persistent partial state and emits its entry on the
+ * block boundary device-side (item 1), fixed shapes with masking (items 2,
+ * 3), positions advanced on the device (item 5).
+ *
+ * csa_decode_step_dev runs the same step as csa_decode_step, but reads pos,
+ * n_comp, swa_head and swa_len from `state` (device memory) when its kernels
+ * run, decides there whether the token completes a block, and advances the
+ * state afterwards (pos + 1; n_comp + 1 after a completed block; the SWA
+ * ring as csa_layer_advance does).  One captured graph of it therefore
+ * replays step after step with nothing decided on the host.  The layer's
+ * host counters and io->pos are ignored.  Differences from csa_decode_step:
+ *   - io->z_main, c_main, z_idx, c_idx are this token's rows only: [B][d]
+ *     and [B][d_i] (overlap 1: [B][2d], [B][2d_i]), every step; the step keeps
+ *     the rows of the current and the previous block in `ring`
+ *     (csa_decode_step_dev_ring_size bytes of caller-owned device memory, no
+ *     initialisation needed beyond what the steps themselves write: the
+ *     first block of a layer must be stepped from its first token);
+ *   - scores must hold max_comp columns per sequence;
+ *   - a completed block that finds the cache full (n_comp == max_comp)
+ *     writes nothing and sets bit 0 of state->flags;
+ *   - with mixed KV, positions and blocks past the RoPE tables use the
+ *     tables' last rows;
+ *   - bfloat16 caches and bfloat16 indexer keys only (CSA_ERR_UNSUPPORTED
+ *     otherwise).
+ * The workspace is csa_decode_step_workspace_size(layer) bytes.
+ * ------------------------------------------------------------------------ */
+typedef struct csa_dev_state {
+    int pos, n_comp, swa_head, swa_len, flags;
+} csa_dev_state;
+size_t csa_decode_step_dev_ring_size(const csa_layer_desc *layer);
+int csa_decode_step_dev(const csa_layer_desc *layer, const csa_step_io *io, csa_dev_state *state,
+                        float *ring, size_t ring_bytes, void *ws, size_t ws_bytes, csa_stream stream);
+
 /* Advance the host-known counters of `layer` past a step at position pos. */
 int csa_layer_advance(csa_layer_desc *layer, int pos);
 

@@ -334,6 +334,37 @@ def test_mixed_kv_validation(csa):
     assert lib.csa_pack_kv_mixed(FAKE + 8, csa.CSA_BF16, FAKE + 8, 10, 512, 64, None) == B.CSA_ERR_INVALID_ARG
 
 
+def test_dev_step_validation(csa):
+    """The device-counter step: state, ring of the stated size, Z/C rows,
+    bfloat16 caches and keys; the ring size follows the block rows."""
+    B = csa.binding
+    lib = csa.lib()
+    L = _desc(csa)
+    ring = lib.csa_decode_step_dev_ring_size(ctypes.byref(L))
+    assert ring == 4 * 1 * 4 * 4 * (512 + 128)  # floats x batch x arrays x 2 blocks x rows x widths
+    L.overlap = 1
+    assert lib.csa_decode_step_dev_ring_size(ctypes.byref(L)) == 2 * ring
+    L.overlap = 0
+    need = csa.csa_decode_step_workspace_size(L)
+    io = _io(csa, pos=-5)  # ignored: the position is on the device
+
+    def call(layer, state=FAKE, ring_ptr=FAKE, ring_bytes=ring):
+        return lib.csa_decode_step_dev(ctypes.byref(layer), ctypes.byref(io), state, ring_ptr, ring_bytes, FAKE,
+                                       need, None)
+
+    assert call(L, state=None) == B.CSA_ERR_INVALID_ARG
+    assert call(L, ring_bytes=ring - 4) == B.CSA_ERR_INVALID_ARG
+    assert call(L, ring_ptr=None) == B.CSA_ERR_INVALID_ARG
+    assert call(L, state=FAKE + 4) == B.CSA_ERR_INVALID_ARG
+    L2 = _desc(csa, dtype=csa.CSA_F32)
+    assert call(L2, ring_bytes=1 << 30) == B.CSA_ERR_UNSUPPORTED
+    L3 = _desc(csa, idx_dtype=csa.CSA_FP8_E4M3, idx_scales=FAKE)
+    assert call(L3) == B.CSA_ERR_UNSUPPORTED
+    io.z_idx = None
+    assert call(L) == B.CSA_ERR_INVALID_ARG
+    assert "Z/C" in csa.csa_last_error()
+
+
 def test_hca_step_validation(csa):
     B = csa.binding
     L = B.LayerDesc()

@@ -1,0 +1,202 @@
+"""GPU: the decode step with its counters on the device (csa_decode_step_dev)
+captured once in a HIP graph and replayed step after step, against the
+host-counter step (csa_decode_step, itself checked against the oracle in
+test_gpu_parity.py / test_gpu_mixed_kv.py) on the same inputs.  Every output
+must match bit for bit: the two run the same kernels, only where the
+counters come from differs.  Each replay is checked, with eager work and
+synchronisations between replays."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.gpu_util import DEV, dev_bf16, dev_f32
+
+pytestmark = pytest.mark.gpu
+
+REC = 592
+
+
+@pytest.fixture(scope="module")
+def csa():
+    import compressed_sparse_attention_reduce_amd as pkg
+    pkg.lib()
+    return pkg
+
+
+def _g(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _tables(rows, offset, base):
+    ang = (np.arange(rows)[:, None] + offset) * base ** (-2.0 * np.arange(32)[None, :] / 64)
+    return dev_f32(np.cos(ang).astype(np.float32)), dev_f32(np.sin(ang).astype(np.float32))
+
+
+def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64):
+    g = _g(seed)
+    D, Di, H = 512, 128, 64
+    m = 4
+    wm, wi = (2 * D, 2 * Di) if overlap else (D, Di)
+    comp_bits = synth.to_bf16_bits(g.standard_normal((B, max_comp, D), dtype=np.float32))
+    keys_bits = synth.to_bf16_bits(g.standard_normal((B, max_comp, Di), dtype=np.float32))
+    swa_bits = synth.to_bf16_bits(g.standard_normal((B, W, D), dtype=np.float32))
+    mb = dev_f32(g.standard_normal((m, wm), dtype=np.float32) * np.float32(0.1))
+    ib = dev_f32(g.standard_normal((m, wi), dtype=np.float32) * np.float32(0.1))
+    sink = dev_f32(g.standard_normal(H, dtype=np.float32))
+    rope = _tables(pos0 + steps + 4, 0.5, 10000.0) if mixed else None
+    comp_rope = _tables(max_comp + 2, 0.25, 500.0) if mixed else None
+
+    def caches():
+        keys = dev_bf16(keys_bits)
+        if mixed:
+            comp = torch.empty(B, max_comp, REC, dtype=torch.uint8, device=DEV)
+            swa = torch.empty(B, W, REC, dtype=torch.uint8, device=DEV)
+            csa.csa_pack_kv_mixed(dev_bf16(comp_bits), comp)
+            csa.csa_pack_kv_mixed(dev_bf16(swa_bits), swa)
+        else:
+            comp, swa = dev_bf16(comp_bits), dev_bf16(swa_bits)
+        return comp, keys, swa
+
+    def layer(comp, keys, swa):
+        return csa.make_layer_desc(comp_kv=comp, idx_keys=keys, swa=swa, main_bias=mb, idx_bias=ib, sink=sink,
+                                   n_comp=n0, swa_head=pos0 % W, swa_len=min(pos0, W), h=H, h_i=64, top_k=K,
+                                   overlap=overlap, rope=rope, comp_rope=comp_rope)
+
+    def outs():
+        return dict(scores=torch.zeros(B, max_comp, device=DEV),
+                    topk_idx=torch.zeros(B, K, dtype=torch.int32, device=DEV),
+                    topk_count=torch.zeros(B, dtype=torch.int32, device=DEV),
+                    gather_buf=torch.zeros(B, K + W, REC if mixed else D,
+                                           dtype=torch.uint8 if mixed else torch.bfloat16, device=DEV),
+                    n_valid=torch.zeros(B, dtype=torch.int32, device=DEV),
+                    out=torch.zeros(B, H, D, dtype=torch.bfloat16, device=DEV),
+                    lse=torch.zeros(B, H, device=DEV))
+
+    ch, kh, sh = caches()
+    Lh = layer(ch, kh, sh)
+    cd, kd, sd = caches()
+    Ld = layer(cd, kd, sd)
+    # static inputs of the captured step
+    st_in = dict(q=torch.zeros(B, H, D, dtype=torch.bfloat16, device=DEV),
+                 q_idx=torch.zeros(B, 64, Di, dtype=torch.bfloat16, device=DEV),
+                 w_idx=torch.zeros(B, 64, device=DEV),
+                 kv_new=torch.zeros(B, D, dtype=torch.bfloat16, device=DEV),
+                 z_main=torch.zeros(B, wm, device=DEV), c_main=torch.zeros(B, wm, device=DEV),
+                 z_idx=torch.zeros(B, wi, device=DEV), c_idx=torch.zeros(B, wi, device=DEV))
+    od = outs()
+    iod = csa.make_step_io(pos=0, **st_in, **od)
+    state = torch.tensor([pos0, n0, pos0 % W, min(pos0, W), 0], dtype=torch.int32, device=DEV)
+    ring = torch.zeros(csa.csa_decode_step_dev_ring_size(Ld) // 4, device=DEV)
+    wsd = torch.empty(csa.csa_decode_step_workspace_size(Ld), dtype=torch.uint8, device=DEV)
+    wsh = torch.empty(csa.csa_decode_step_workspace_size(Lh), dtype=torch.uint8, device=DEV)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            csa.csa_decode_step_dev(Ld, iod, state, ring, wsd, stream=stream)
+    torch.cuda.synchronize()
+
+    hist_z = {k: [] for k in ("z_main", "c_main", "z_idx", "c_idx")}
+    for pos in range(pos0, pos0 + steps):
+        x = dict(q=synth.to_bf16_bits(g.standard_normal((B, H, D), dtype=np.float32)),
+                 q_idx=synth.to_bf16_bits(g.standard_normal((B, 64, Di), dtype=np.float32) / np.float32(np.sqrt(Di))),
+                 w_idx=g.standard_normal((B, 64), dtype=np.float32),
+                 kv_new=synth.to_bf16_bits(g.standard_normal((B, D), dtype=np.float32)),
+                 z_main=g.standard_normal((B, wm), dtype=np.float32), c_main=g.standard_normal((B, wm), dtype=np.float32),
+                 z_idx=g.standard_normal((B, wi), dtype=np.float32), c_idx=g.standard_normal((B, wi), dtype=np.float32))
+        for k in hist_z:
+            hist_z[k].append(x[k])
+        # the captured step: new inputs into its static buffers, one replay
+        for k, v in x.items():
+            st_in[k].copy_(dev_bf16(v) if v.dtype == np.uint16 else dev_f32(v))
+        print(f"dev step pos={pos}", flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        # the host-counter step on the same inputs (block rows from the history)
+        completes = pos % m == m - 1
+        blk = {}
+        for k in hist_z:
+            rows = np.stack(hist_z[k][-m:], axis=1)                   # [B, m, w]
+            if overlap and pos // m > 0:
+                rows = np.stack(hist_z[k][-2 * m:], axis=1)           # previous block then this one
+            blk[k] = dev_f32(np.ascontiguousarray(rows)) if completes else dev_f32(np.zeros((B, m, rows.shape[2]), np.float32))
+        oh = outs()
+        ioh = csa.make_step_io(pos=pos, q=dev_bf16(x["q"]), q_idx=dev_bf16(x["q_idx"]), w_idx=dev_f32(x["w_idx"]),
+                               kv_new=dev_bf16(x["kv_new"]), **blk, **oh)
+        csa.csa_decode_step(Lh, ioh, wsh)
+        csa.csa_layer_advance(Lh, pos)
+        torch.cuda.synchronize()
+        N = Lh.n_comp
+        sv = state.cpu().numpy()
+        assert (sv[0], sv[1], sv[2], sv[3], sv[4]) == (pos + 1, N, Lh.swa_head, Lh.swa_len, 0)
+        assert torch.equal(od["scores"][:, :N], oh["scores"][:, :N])
+        for k in ("topk_idx", "topk_count", "n_valid", "out", "lse"):
+            assert torch.equal(od[k], oh[k]), (pos, k)
+        nv = int(oh["n_valid"].min())
+        assert torch.equal(od["gather_buf"][:, :nv], oh["gather_buf"][:, :nv])
+        assert torch.equal(cd[:, :N], ch[:, :N]) and torch.equal(kd[:, :N], kh[:, :N]) and torch.equal(sd, sh)
+    return state, cd, ch
+
+
+def test_dev_step_graph_replays_match_host_steps(csa):
+    """Ten replays from a block start (two completions, ring wrap), batch 2."""
+    _run(csa, mixed=False, overlap=0, B=2, n0=150, pos0=600, max_comp=200, steps=10, seed=8101)
+
+
+def test_dev_step_overlap_and_mixed_kv(csa):
+    """The overlapped compressor (the ring keeps the previous block) and mixed
+    main KV (RoPE rows from the device position), from the first token."""
+    _run(csa, mixed=True, overlap=1, B=1, n0=0, pos0=0, max_comp=16, steps=13, seed=8102)
+
+
+def test_dev_step_full_cache_sets_flag(csa):
+    """A block completing into a full cache writes nothing, keeps n_comp and
+    sets bit 0 of the flags; the step's attention is the one of a step that
+    completes nothing (the host step one position earlier, same state)."""
+    g = _g(8103)
+    B, D, Di, H, W, K, m = 1, 512, 128, 64, 8, 64, 4
+    max_comp = n0 = 20
+    pos = 79  # completes block 19, but the cache is full
+    comp = dev_bf16(synth.to_bf16_bits(g.standard_normal((B, max_comp, D), dtype=np.float32)))
+    keys = dev_bf16(synth.to_bf16_bits(g.standard_normal((B, max_comp, Di), dtype=np.float32)))
+    swa_bits = synth.to_bf16_bits(g.standard_normal((B, W, D), dtype=np.float32))
+    mb = dev_f32(g.standard_normal((m, D), dtype=np.float32))
+    ib = dev_f32(g.standard_normal((m, Di), dtype=np.float32))
+    sink = dev_f32(g.standard_normal(H, dtype=np.float32))
+    x = dict(q=dev_bf16(synth.to_bf16_bits(g.standard_normal((B, H, D), dtype=np.float32))),
+             q_idx=dev_bf16(synth.to_bf16_bits(g.standard_normal((B, 64, Di), dtype=np.float32))),
+             w_idx=dev_f32(g.standard_normal((B, 64), dtype=np.float32)),
+             kv_new=dev_bf16(synth.to_bf16_bits(g.standard_normal((B, D), dtype=np.float32))))
+    res = []
+    for dev in (True, False):
+        swa = dev_bf16(swa_bits)
+        L = csa.make_layer_desc(comp_kv=comp, idx_keys=keys, swa=swa, main_bias=mb, idx_bias=ib, sink=sink,
+                                n_comp=n0, swa_head=3, swa_len=W, h=H, h_i=64, top_k=K)
+        o = dict(scores=torch.zeros(B, max_comp, device=DEV), topk_idx=torch.zeros(B, K, dtype=torch.int32, device=DEV),
+                 topk_count=torch.zeros(B, dtype=torch.int32, device=DEV),
+                 gather_buf=torch.zeros(B, K + W, D, dtype=torch.bfloat16, device=DEV),
+                 n_valid=torch.zeros(B, dtype=torch.int32, device=DEV),
+                 out=torch.zeros(B, H, D, dtype=torch.bfloat16, device=DEV), lse=torch.zeros(B, H, device=DEV))
+        zc = dict(z_main=torch.ones(B, m, D, device=DEV), c_main=torch.ones(B, m, D, device=DEV),
+                  z_idx=torch.ones(B, m, Di, device=DEV), c_idx=torch.ones(B, m, Di, device=DEV))
+        ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+        before = comp.clone()
+        if dev:
+            io = csa.make_step_io(pos=0, **x, **{k: v[:, 0].contiguous() for k, v in zc.items()}, **o)
+            state = torch.tensor([pos, n0, 3, W, 0], dtype=torch.int32, device=DEV)
+            ring = torch.zeros(csa.csa_decode_step_dev_ring_size(L) // 4, device=DEV)
+            csa.csa_decode_step_dev(L, io, state, ring, ws)
+            torch.cuda.synchronize()
+            assert state.cpu().tolist() == [pos + 1, n0, 4, W, 1]
+        else:
+            io = csa.make_step_io(pos=pos - 1, **x, **zc, **o)
+            csa.csa_decode_step(L, io, ws)
+            torch.cuda.synchronize()
+        assert torch.equal(comp, before)
+        res.append((o, swa))
+    (od, sd), (oh, sh) = res
+    for k in ("scores", "topk_idx", "topk_count", "n_valid", "gather_buf", "out", "lse"):
+        assert torch.equal(od[k], oh[k]), k
+    assert torch.equal(sd, sh)
