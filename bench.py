@@ -253,6 +253,55 @@ def time_mixed_kv(csa, layers, shape, steps: int):
     return e0.elapsed_time(e1) / steps
 
 
+def time_dev_step(csa, layers, shape, steps: int, warmup: int):
+    """The 30-layer decode step with device-side counters
+    (csa_decode_step_dev): one graph captured once and replayed, each replay
+    a real next step (positions advance on the device, every fourth one
+    completes a block into the cache).  The counters start `replays / 4 + 1`
+    entries below the cache's capacity so that no completion finds it full.
+    Returns ms per step."""
+    import torch
+
+    total = warmup + steps
+    B = shape.batch
+    dl = []
+    for ly in layers:
+        x = ly["x"]
+        L = csa.make_layer_desc(comp_kv=x["comp_kv"], idx_keys=x["idx_keys"], swa=x["swa"],
+                                main_bias=x["main_bias"], idx_bias=x["idx_bias"], sink=x["sink"],
+                                n_comp=x["n_comp"], swa_head=x["swa_head"], swa_len=x["swa_len"],
+                                h=shape.h, h_i=shape.h_i, m=shape.m, top_k=shape.top_k)
+        rows = {k: x[k][:, 0].contiguous() for k in ("z_main", "c_main", "z_idx", "c_idx")}
+        io = csa.make_step_io(pos=0, q=x["q"], q_idx=x["q_idx"], w_idx=x["w_idx"], kv_new=x["kv_new"], **rows,
+                              **ly["outs"])
+        start = x["pos"] - shape.m + 1  # a block's first token
+        state = torch.tensor([start, shape.n_comp - total // shape.m - 2, x["swa_head"], x["swa_len"], 0],
+                             dtype=torch.int32, device="cuda")
+        ring = torch.zeros(csa.csa_decode_step_dev_ring_size(L) // 4, device="cuda")
+        dl.append((L, io, state, ring, ly["ws"]))
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for L, io, state, ring, ws in dl:
+                csa.csa_decode_step_dev(L, io, state, ring, ws, stream=stream)
+        for _ in range(warmup):
+            g.replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        e1.record(stream)
+    stream.synchronize()
+    flags = sum(int(st[4]) for _, _, st, _, _ in dl)
+    assert flags == 0, "a completed block found its cache full"
+    del dl, g
+    return e0.elapsed_time(e1) / steps
+
+
 def time_prefill(csa, reps: int):
     """The prefill-shaped chunk (2048 queries at positions 260096..262143
     against 65536 compressed blocks, causal): csa_index_topk (multi-query
@@ -568,6 +617,7 @@ def main() -> int:
     fp8_ms, fp8_bytes, fp8_step_ms = time_fp8(csa, layers, shape, args.scan_reps, max(20, args.steps // 2))
     fp8_gbs = fp8_bytes / (fp8_ms * 1e-3) / 1e9
     mixed_ms = time_mixed_kv(csa, layers, shape, max(20, args.steps // 2))
+    dev_ms = time_dev_step(csa, layers, shape, max(20, args.steps // 2), 4)
 
     cpu = None
     if args.cpu_budget > 0:
@@ -622,6 +672,12 @@ def main() -> int:
             "frac": round(fp8_gbs / HBM_PEAK_GBS, 4),
             "decode_steps_per_s": round(1e3 / fp8_step_ms, 2),
             "decode_ms_per_step": round(fp8_step_ms, 5),
+        },
+        "device_counters": {
+            "workload": "ctx1m decode step as above through csa_decode_step_dev: one graph replayed, each replay "
+                        "the next token (positions, block completions and the SWA ring advanced on the device)",
+            "decode_steps_per_s": round(1e3 / dev_ms, 2),
+            "decode_ms_per_step": round(dev_ms, 5),
         },
         "mixed_kv": {
             "workload": "ctx1m decode step as above with mixed main KV: every compressed entry and window row "
