@@ -110,6 +110,33 @@ def time_scan_kernel(csa, layers, shape, reps: int):
     return e0.elapsed_time(e1) / n, n
 
 
+def time_read_ceiling(csa, layers, reps: int):
+    """The practical read ceiling of one launch: csa_read_probe (plain
+    streaming loads, nothing else) over the same 30 key caches the scan
+    reads, back to back in a graph like the scan's launches.  Returns
+    (average launch us, bytes per launch)."""
+    import torch
+
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bufs = [ly["x"]["idx_keys"] for ly in layers]
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for b in bufs:
+                csa.csa_read_probe(b, sink, stream=stream)
+        g.replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    stream.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * len(bufs)), bufs[0].numel() * bufs[0].element_size()
+
+
 SCAN_SOURCES = ["index_score.hip", "common.h", "kernels.h", "topk_common.h", "step_prep.h", "compress_impl.h",
                 "score_tile.h", "fp8_codec.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_index_score_bf16_ctx1m_hbm_traffic.md")
@@ -609,6 +636,8 @@ def main() -> int:
     assert torch.equal(layers[0]["outs"]["out"], ref_out), "timed replays differ from eager"
 
     scan_ms, scan_launches = time_scan_kernel(csa, layers, shape, args.scan_reps)
+    ceil_us, ceil_bytes = time_read_ceiling(csa, layers, args.scan_reps)
+    ceil_gbs = ceil_bytes / (ceil_us * 1e-6) / 1e9
     ab = algorithmic_bytes(shape)
     scan_gbs = ab["scan_launch"] / (scan_ms * 1e-3) / 1e9
     step_bytes = ab["per_layer"] * shape.layers
@@ -663,6 +692,10 @@ def main() -> int:
             "alg_bytes_per_launch": ab["scan_launch"],
             "avg_launch_us": round(scan_ms * 1e3, 3),
             "launches_timed": scan_launches,
+            # context: a plain streaming read of the same caches, one launch each
+            "read_ceiling_gbps": round(ceil_gbs, 1),
+            "read_ceiling_us": round(ceil_us, 3),
+            "frac_of_read_ceiling": round(scan_gbs / ceil_gbs, 4),
         },
         "fp8_scan": {
             "kernel": "k_index_score_fp8",

@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     csa_index_topk,
     csa_index_topk_fp8,
     csa_pack_kv_mixed,
+    csa_read_probe,
     csa_decode_step_dev,
     csa_decode_step_dev_ring_size,
     MIX_REC_BYTES,

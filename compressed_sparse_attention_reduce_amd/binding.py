@@ -82,6 +82,7 @@ _SIGS = {
                              _ll, _ll, _vp]),
     "csa_quantize_fp8": (_i, [_vp, _i, _vp, _vp, _ll, _i, _vp]),
     "csa_pack_kv_mixed": (_i, [_vp, _i, _vp, _ll, _i, _i, _vp]),
+    "csa_read_probe": (_i, [_vp, _ll, _vp, _vp]),
     "csa_index_score_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _ll, _ll, _ll,
                                  _ll, _ll, _ll, _vp]),
     "csa_topk_workspace_size": (_sz, [_i, _i, _i, _i]),
@@ -196,6 +197,13 @@ def csa_quantize_fp8(x, codes, scales, stream=None) -> None:
     if codes.shape != x.shape or scales.numel() != rows:
         raise ValueError("codes must match x and scales hold one value per row")
     _check(lib().csa_quantize_fp8(_ptr(x), _dt(x), _ptr(codes), _ptr(scales), rows, d, _stream(stream)))
+
+
+def csa_read_probe(buf, sink, stream=None) -> None:
+    """Read every byte of the contiguous device tensor buf once (calibration)."""
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    _check(lib().csa_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 
 MIX_REC_BYTES = 592  # one mixed main-KV row: 448 E4M3 codes, 64 bf16 RoPE values, scale, pad

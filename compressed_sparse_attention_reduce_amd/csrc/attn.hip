@@ -17,7 +17,7 @@
 //     in LDS; the split's softmax statistics are combined across waves in LDS;
 //     O = P V runs on the same MFMA with V read column-wise from LDS.  Partial
 //     (m, l, O) go to the workspace in float32.
-//   k_attn_merge — one workgroup per (head, sequence): M = max(max_s m_s, sink),
+//   k_attn_merge — one workgroup per (head, 128 columns, sequence): M = max(max_s m_s, sink),
 //     rescale and add the partials, add exp(sink - M) once, divide.
 // float32 path (small correctness workloads): one workgroup per (head,
 // sequence), the whole softmax in float32 on the vector ALUs.
@@ -38,7 +38,15 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial_bf16(AttnArgs a, 
 }
 
 constexpr int kMaxSplits = 256;
+constexpr int kMergeWaves = kAttnThreads / kWave;
+constexpr int kMergeCols = 2 * kWave;  // columns per workgroup: one pair per lane
 
+// One workgroup per (head, 128 columns, sequence).  Every wave derives the
+// split weights itself (lane s holds split s of each group of 64, no
+// barrier); wave w sums splits w, w + 4, ... for the workgroup's columns and
+// the four partial sums meet in LDS.  Partials of empty splits (l = 0) are
+// never written: their loads read stale workspace bytes that are skipped
+// (never multiplied).
 __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __restrict__ ws_o,
                                                              const float* __restrict__ ws_ml,
                                                              const float* __restrict__ sink, int h,
@@ -48,31 +56,33 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
                                                              const float* inv_sin, int rope_start,
                                                              const DevState* dev, const float* rope_cos,
                                                              const float* rope_sin, int rope_rows) {
+    __shared__ float2 part[kMergeWaves][kWave];
     if (dev && rope_cos) {  // the inverse-RoPE row of the position on the device
         const int p = dev->pos < 0 ? 0 : (dev->pos < rope_rows ? dev->pos : rope_rows - 1);
         const long long row = static_cast<long long>(p) * (kMixRope / 2);
         inv_cos = rope_cos + row;
         inv_sin = rope_sin + row;
     }
-    const int hh = blockIdx.x;
+    const int col_blocks = (d + kMergeCols - 1) / kMergeCols;
+    const int hh = blockIdx.x / col_blocks;
+    const int cb = blockIdx.x % col_blocks;
     const int b = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
     const long long base = (static_cast<long long>(b) * h + hh) * n_splits;
     const float* ml = ws_ml + 2 * base;
     const float* ob = ws_o + base * d;
-    // Partials of empty splits (l = 0) are never written: their loads read
-    // stale workspace bytes that are skipped below (never multiplied).
-    // Thread t owns columns 2t and 2t + 1; the first splits' loads go first.
-    const int col = 2 * threadIdx.x;
+    const int col = cb * kMergeCols + 2 * lane;
     const bool has_col = col < d;
-    constexpr int kBatch = 32;  // all splits of a 1024-row window in one round trip
+    // this wave's first splits' loads go first
+    constexpr int kBatch = 16;
     float2 v[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-        v[u] = (has_col && u < n_splits) ? *reinterpret_cast<const float2*>(ob + static_cast<long long>(u) * d + col)
-                                         : make_float2(0.f, 0.f);
-    // split weights, derived by every wave on its own (no barrier): lane s
-    // holds split s of each group of 64
+    for (int u = 0; u < kBatch; ++u) {
+        const int sp = wv + kMergeWaves * u;
+        v[u] = (has_col && sp < n_splits) ? *reinterpret_cast<const float2*>(ob + static_cast<long long>(sp) * d + col)
+                                          : make_float2(0.f, 0.f);
+    }
     constexpr int kGroups = kMaxSplits / kWave;
     float ms[kGroups], ls[kGroups];
     float M = sink ? sink[hh] : -INFINITY;
@@ -103,26 +113,21 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
         return c;
     };
     float2 acc = make_float2(0.f, 0.f);
+    for (int s0 = 0; s0 < n_splits; s0 += kMergeWaves * kBatch) {
+        if (s0 > 0) {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        if (u < n_splits) {
-            const float c = coef(u);
-            if (c != 0.f) {
-                acc.x += v[u].x * c;
-                acc.y += v[u].y * c;
+            for (int u = 0; u < kBatch; ++u) {
+                const int sp = s0 + wv + kMergeWaves * u;
+                v[u] = (has_col && sp < n_splits)
+                           ? *reinterpret_cast<const float2*>(ob + static_cast<long long>(sp) * d + col)
+                           : make_float2(0.f, 0.f);
             }
         }
-    }
-    for (int s0 = kBatch; s0 < n_splits; s0 += kBatch) {
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u)
-            v[u] = (has_col && s0 + u < n_splits)
-                       ? *reinterpret_cast<const float2*>(ob + static_cast<long long>(s0 + u) * d + col)
-                       : make_float2(0.f, 0.f);
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            if (s0 + u < n_splits) {
-                const float c = coef(s0 + u);
+            const int sp = s0 + wv + kMergeWaves * u;
+            if (sp < n_splits) {
+                const float c = coef(sp);
                 if (c != 0.f) {
                     acc.x += v[u].x * c;
                     acc.y += v[u].y * c;
@@ -130,8 +135,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
             }
         }
     }
+    part[wv][lane] = acc;
+    __syncthreads();
+    if (wv != 0) return;
+#pragma unroll
+    for (int w = 1; w < kMergeWaves; ++w) {
+        acc.x += part[w][lane].x;
+        acc.y += part[w][lane].y;
+    }
     if (has_col) {
-        // the RoPE dims rotated back at the token's position (a thread holds
+        // the RoPE dims rotated back at the token's position (a lane holds
         // one (even, odd) pair)
         if (inv_cos && col >= rope_start) {
             const int pr = (col - rope_start) / 2;
@@ -146,7 +159,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
             static_cast<float*>(out)[o + 1] = acc.y;
         }
     }
-    if (lse && threadIdx.x == 0)
+    if (lse && cb == 0 && lane == 0)
         lse[static_cast<long long>(b) * h + hh] = den > 0.f ? M + logf(den) : -INFINITY;
 }
 
@@ -270,7 +283,9 @@ hipError_t launch_attn_bf16(AttnArgs a, hipStream_t s) {
 }
 
 hipError_t launch_attn_merge(const AttnArgs& a, int ns, hipStream_t s) {
-    hipLaunchKernelGGL(k_attn_merge, dim3(a.h, a.batch), dim3(kAttnThreads), 0, s, a.ws_o, a.ws_ml, a.sink, a.h,
+    const int col_blocks = (a.d + kMergeCols - 1) / kMergeCols;
+    hipLaunchKernelGGL(k_attn_merge, dim3(a.h * col_blocks, a.batch), dim3(kAttnThreads), 0, s, a.ws_o, a.ws_ml,
+                       a.sink, a.h,
                        a.d, ns, a.out, a.out_bf16 ? 1 : 0, a.lse, a.out_stride_b, a.inv_cos, a.inv_sin,
                        a.d - kMixRope, a.dev, a.kv_mixed ? a.rope_cos : nullptr, a.rope_sin, a.rope_rows);
     return hipGetLastError();

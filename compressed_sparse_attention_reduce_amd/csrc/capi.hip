@@ -161,6 +161,12 @@ static int check_fp8_score_args(const void* q, const float* w, const void* k, co
     return CSA_OK;
 }
 
+int csa_read_probe(const void* buf, long long bytes, unsigned* sink, csa_stream stream) {
+    CHECK((buf && sink) || bytes < 16, "csa_read_probe: null pointer argument");
+    CHECK(bytes >= 0 && aligned16(buf), "csa_read_probe: bytes %lld / unaligned buffer", bytes);
+    return launched(csa::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)), "csa_read_probe");
+}
+
 int csa_pack_kv_mixed(const void* x, csa_dtype x_dtype, unsigned char* rec, long long rows, int d, int rope_dim,
                       csa_stream stream) {
     CHECK((x && rec) || rows == 0, "csa_pack_kv_mixed: null pointer argument");

@@ -11,6 +11,9 @@ namespace csa {
 
 int device_cu_count();
 
+// calibration read (calib.hip): every 16-byte piece of buf read once
+hipError_t launch_read_probe(const void* buf, long long bytes, unsigned* sink, hipStream_t s);
+
 constexpr int kTopkMaxK = 2048;
 
 // ---- compressor reduce -------------------------------------------------------

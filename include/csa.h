@@ -487,6 +487,17 @@ int csa_prefill_attn(const void *q, const void *comp_kv, int n_comp, const int *
                      const float *sink, float scale, void *out, csa_dtype out_dtype, float *lse,
                      int t, int h, int d, csa_stream stream);
 
+/* ------------------------------------------------------------------------
+ * 8. Calibration (not a step of the method).
+ *
+ * csa_read_probe: read every byte of buf (device, 16-byte aligned, the first
+ *   bytes / 16 * 16 of them) once with plain streaming loads, as one launch:
+ *   timed over large buffers it gives the practical HBM read ceiling of one
+ *   launch that memory-bound kernels can be compared with.  sink: one
+ *   unsigned of device memory (rarely written).
+ * ------------------------------------------------------------------------ */
+int csa_read_probe(const void *buf, long long bytes, unsigned *sink, csa_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

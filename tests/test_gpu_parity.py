@@ -921,3 +921,13 @@ def test_hca_step_full_size(csa):
     ro, rl = oracle.sparse_attn(host_f64(x["q"][0]), rows, host_f64(x["sink"]), 1 / np.sqrt(D))
     assert rel_err(host_f64(out[0]), ro) <= 2e-2
     assert np.abs(lse[0].cpu().numpy() - rl).max() <= 1e-2
+
+
+def test_read_probe_runs(csa):
+    """The calibration read (csa_read_probe) runs over a buffer with a ragged
+    tail and leaves the sink alone for data whose xor is not its marker."""
+    buf = torch.zeros(1_000_003 * 4, dtype=torch.uint8, device=DEV)
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    csa.csa_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink[0]) == 0
