@@ -138,7 +138,7 @@ def time_read_ceiling(csa, layers, reps: int):
 
 
 SCAN_SOURCES = ["index_score.hip", "common.h", "kernels.h", "topk_common.h", "step_prep.h", "compress_impl.h",
-                "score_tile.h", "fp8_codec.h"]
+                "score_tile.h", "fp8_codec.h", "mixed_kv.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_index_score_bf16_ctx1m_hbm_traffic.md")
 
 

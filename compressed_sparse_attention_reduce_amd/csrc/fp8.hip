@@ -13,14 +13,18 @@
 //   nearest, ties to the even code, saturating at 448 (integer arithmetic on
 //   the binary32 bits, no conversion instruction).
 // k_index_score_fp8: the bf16 scan's design with half the bytes per key:
-//   v_mfma_f32_16x16x32_fp8_fp8, heads as M, 16-key tiles as N; each lane
-//   loads 32 contiguous bytes of its key row (the MFMA's k slots are
-//   permuted identically for the query and the keys: slot 8g + e of k-step s
-//   is byte 32g + 8s + e), plus the key's scale; a ring of 8 tiles per wave
-//   keeps as many bytes in flight as the bf16 kernel's 4.
+//   v_mfma_scale_f32_16x16x128_f8f6f4 (both formats E4M3, unit block scales:
+//   one instruction per 16-head tile covers the whole 128-byte key, at twice
+//   the rate of the 32-wide FP8 form), heads as M, 16-key tiles as N; each
+//   lane loads 32 contiguous bytes of its key row and supplies the same 32
+//   bytes of its query row, so the instruction pairs the same byte of query
+//   and key whatever order it takes k slots in; the key's scale multiplies
+//   the head sum (s > 0: sum_h w ReLU(s x) = s sum_h w ReLU(x)); a ring of 8
+//   tiles per wave keeps as many bytes in flight as the bf16 kernel's 4.
 #include "common.h"
 #include "fp8_codec.h"
 #include "kernels.h"
+#include "score_tile.h"
 #include "step_prep.h"
 #include "topk_common.h"
 
@@ -56,7 +60,6 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kTileKeys = 16;
 constexpr int kHeads = 64;
 constexpr int kDi = 128;            // key bytes (one per element)
-constexpr int kSteps = kDi / 32;    // k-steps of the 16x16x32 MFMA
 constexpr int kMTiles = kHeads / 16;
 constexpr int kRing = 8;            // key tiles in flight per wave
 constexpr int kQPitch = kDi + 16;   // LDS row pitch of the staged query (bytes)
@@ -67,7 +70,8 @@ static_assert(kRing % 4 == 0, "ring slot i feeds the lists of lane group i % 4")
 
 static_assert(kWaves == kScoreWavesPerWg, "waves per workgroup as the host assumes");
 
-typedef long fp8x8;  // eight E4M3 codes, one MFMA operand
+typedef int i32x8 __attribute__((ext_vector_type(8)));  // 32 E4M3 codes, one MFMA operand
+constexpr int kUnitScale = 127;  // E8M0 block scale 2^(127 - 127) = 1
 constexpr int kFp8WgsPerCu = 2;  // one per CU measured slower (11.3 vs 10.9 us at n = 250,000)
 
 // Score of the new key (decoded E4M3 values key[0..128), scale key[128], in
@@ -182,12 +186,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
     qstage(threadIdx.x + kThreads, qv1);
     if (threadIdx.x < 16) *reinterpret_cast<float4*>(ws + 4 * threadIdx.x) = wv4;
     __syncthreads();
-    fp8x8 qa[kMTiles][kSteps];
+    i32x8 qa[kMTiles];
 #pragma unroll
-    for (int mt = 0; mt < kMTiles; ++mt)
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s)
-            qa[mt][s] = *reinterpret_cast<const fp8x8*>(qs + (16 * mt + li) * kQPitch + 32 * lg + 8 * s);
+    for (int mt = 0; mt < kMTiles; ++mt) {
+        const uint8_t* qp = qs + (16 * mt + li) * kQPitch + 32 * lg;
+        const uint4 lo = *reinterpret_cast<const uint4*>(qp);
+        const uint4 hi = *reinterpret_cast<const uint4*>(qp + 16);
+        qa[mt] = i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                       static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+    }
     float wr[kMTiles][4];
 #pragma unroll
     for (int mt = 0; mt < kMTiles; ++mt) {
@@ -207,23 +214,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
         f32x4 acc[kMTiles];
 #pragma unroll
         for (int mt = 0; mt < kMTiles; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        fp8x8 kv[kSteps];
-        __builtin_memcpy(kv, kb[i], sizeof(kv));
-#pragma unroll
-        for (int s2 = 0; s2 < kSteps; ++s2)
-#pragma unroll
-            for (int mt = 0; mt < kMTiles; ++mt)
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa[mt][s2], kv[s2], acc[mt], 0, 0, 0);
-        const float ks = ksc[i];
-        if (refill) load_tile(j + kRing, kb[i], ksc[i]);
-        // accumulator register r of M tile mt <-> head 16*mt + 4*lg + r, key li
-        float part = 0.f;
+        const i32x8 kv = {static_cast<int>(kb[i][0].x), static_cast<int>(kb[i][0].y), static_cast<int>(kb[i][0].z),
+                          static_cast<int>(kb[i][0].w), static_cast<int>(kb[i][1].x), static_cast<int>(kb[i][1].y),
+                          static_cast<int>(kb[i][1].z), static_cast<int>(kb[i][1].w)};
 #pragma unroll
         for (int mt = 0; mt < kMTiles; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) part += wr[mt][r] * fmaxf(acc[mt][r] * ks, 0.f);
-        part += xor_lanes_f32<16>(part);
-        part += xor_lanes_f32<32>(part);
+            acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kv, acc[mt], 0, 0, 0, kUnitScale, 0,
+                                                                       kUnitScale);
+        const float ks = ksc[i];
+        if (refill) load_tile(j + kRing, kb[i], ksc[i]);
+        // accumulator register r of M tile mt <-> head 16*mt + 4*lg + r, key li;
+        // the key's scale applied once after the head sum (ks > 0)
+        const float part = tile_head_sum(acc, wr) * ks;
         const int key = (gw + j * waves_per_row) * kTileKeys + li;
         const bool live = j < n_mine && key < n;
         float sc = part;
