@@ -931,3 +931,35 @@ def test_read_probe_runs(csa):
     csa.csa_read_probe(buf, sink)
     torch.cuda.synchronize()
     assert int(sink[0]) == 0
+
+
+def test_fp8_scans_decode_every_code_pair(csa):
+    """Both FP8 scans (one query row per sequence; many rows per call) read
+    their operands as OCP E4M3, subnormals included: query row i holds only
+    finite code i in one byte of head 0 and its negation in head 1, key j only
+    finite code j in the same byte, so with weights (1, 2) and unit key
+    scales the score is the exact product p = e4m3(i) e4m3(j) when p > 0 and
+    2|p| otherwise — compared bit for bit for all 254 x 254 pairs."""
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    n = len(codes)
+    slot = 77  # any byte of the 128
+    q = np.zeros((n, 64, 128), dtype=np.uint8)
+    q[:, 0, slot] = codes
+    q[:, 1, slot] = codes ^ 0x80
+    k = np.zeros((n, 128), dtype=np.uint8)
+    k[:, slot] = codes
+    w = np.zeros((n, 64), dtype=np.float32)
+    w[:, 0], w[:, 1] = 1.0, 2.0
+    p = numfmt.e4m3_decode(codes)[:, None] * numfmt.e4m3_decode(codes)[None, :]
+    want = np.where(p > 0, p, -2.0 * p)
+    kd, ks = torch.from_numpy(k).to(DEV), torch.ones(n, device=DEV)
+    # many query rows in one call (the multi-query scan)
+    s1 = torch.empty(1, n, n, device=DEV)
+    csa.csa_index_score_fp8(torch.from_numpy(q[None]).to(DEV), dev_f32(w[None]), kd[None], ks[None], s1)
+    # one query row per sequence (the decode scan), keys shared
+    s2 = torch.empty(n, 1, n, device=DEV)
+    csa.csa_index_score_fp8(torch.from_numpy(q[:, None]).to(DEV), dev_f32(w[:, None]), kd[None].expand(n, n, 128),
+                            ks[None].expand(n, n), s2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(s1[0].cpu().numpy().astype(np.float64), want)
+    np.testing.assert_array_equal(s2[:, 0].cpu().numpy().astype(np.float64), want)
