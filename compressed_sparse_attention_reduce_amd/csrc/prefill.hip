@@ -254,10 +254,10 @@ __device__ __forceinline__ int pa_swz(int cc) { return (cc >> 1) & (kSlots - 1);
 
 template <int D>
 struct PaCfg {
-    static constexpr int kRows = D >= 512 ? 64 : 32;       // rows per chunk
+    static constexpr int kRows = 32;  // rows per chunk: 74 KB of LDS at D = 512, two workgroups per CU
     static constexpr int kMt = kRows / 16;                  // 16-row tiles of S^T
     static constexpr int kKrPitch = D + 8;                  // row-major rows: 16-lane reads hit distinct banks
-    static constexpr int kVtPitch = kRows + 8;              // transposed rows: 144 B (R = 64) per column
+    static constexpr int kVtPitch = kRows + 8;              // transposed rows: 80 B per column
     static constexpr int kKs = D / 32;                      // k-steps of S^T
     static constexpr int kMd = D / 16;                      // 16-column tiles of O^T
     static constexpr int kItems = (kRows / 4) * (D / 8);    // (4-row group, 16-byte column) items per chunk
@@ -267,7 +267,10 @@ struct PaCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(kPaThreads, D >= 512 ? 1 : 2) void k_prefill_attn(PrefillAttnArgs a) {
+// Two workgroups per CU: one's loads and barriers overlap the other's
+// matrix work (at D = 512 a few registers spill to scratch: measured 10%
+// faster than one workgroup per CU with 64-row chunks all the same).
+__global__ __launch_bounds__(kPaThreads, 2) void k_prefill_attn(PrefillAttnArgs a) {
     using C = PaCfg<D>;
     constexpr int R = C::kRows;
     extern __shared__ __attribute__((aligned(16))) uint16_t pa_lds[];
