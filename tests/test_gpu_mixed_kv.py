@@ -289,3 +289,85 @@ def test_decode_step_ctx1m_mixed_kv_full_size(csa):
     ro = oracle.rope_rotate(ro, rc[pos].astype(np.float64), rs[pos].astype(np.float64), inverse=True)
     assert rel_err(host_f64(outs["out"][0]), ro) <= 2e-2
     assert np.abs(outs["lse"][0].cpu().numpy() - rl).max() <= 1e-2
+
+
+def test_decode_step_mixed_kv_fp8_keys_batched(csa):
+    """Three sequences, E4M3 indexer keys and mixed main KV together, a step
+    that completes a block: each sequence's new records, scores, selection,
+    gather_buf and output against the oracle."""
+    B = 3
+    shape = synth.with_(synth.SHAPES["ctx8k"], batch=B, ctx=4000, n_comp=999)
+    x = synth.make_decode_inputs(shape, 7401, max_comp=1000)
+    g = _g(7402)
+    f = numfmt.bf16_bits_to_f64
+    pos = x["pos"]
+    assert pos % 4 == 3
+    comp_recs, comp_vals, swa_recs, swa_vals = [], [], [], []
+    for b in range(B):
+        r, v = oracle_records(f(x["comp_kv"][b]))
+        comp_recs.append(r); comp_vals.append(v)
+        r, v = oracle_records(f(x["swa"][b]))
+        swa_recs.append(r); swa_vals.append(v)
+    comp = torch.from_numpy(np.stack(comp_recs)).to(DEV)
+    swa = torch.from_numpy(np.stack(swa_recs)).to(DEV)
+    kc0, ks0 = numfmt.quantize_e4m3_rows(f(x["idx_keys"].reshape(-1, 128)).astype(np.float32))
+    kc0, ks0 = kc0.reshape(B, 1000, 128), ks0.reshape(B, 1000)
+    kc, ks = torch.from_numpy(kc0.copy()).to(DEV), dev_f32(ks0)
+    qi = g.standard_normal((B, 64, 128), dtype=np.float32) / np.float32(np.sqrt(128))
+    qc, qs = numfmt.quantize_e4m3_rows(qi.reshape(-1, 128))
+    qc = qc.reshape(B, 64, 128)
+    w8 = (x["w_idx"] * qs.reshape(B, 64)).astype(np.float32)
+    rc, rs = rope_tables(pos + 4)
+    cc, cs = rope_tables(1001, offset=0.25, base=500.0)
+    L = csa.make_layer_desc(comp_kv=comp, idx_keys=kc, idx_scales=ks, swa=swa, main_bias=dev_f32(x["main_bias"]),
+                            idx_bias=dev_f32(x["idx_bias"]), sink=dev_f32(x["sink"]), n_comp=x["n_comp"],
+                            swa_head=x["swa_head"], swa_len=x["swa_len"], h=64, h_i=64, top_k=shape.top_k,
+                            rope=(dev_f32(rc), dev_f32(rs)), comp_rope=(dev_f32(cc), dev_f32(cs)))
+    K, W = shape.top_k, shape.w
+    outs = dict(scores=torch.empty(B, 1000, device=DEV), topk_idx=torch.empty(B, K, dtype=torch.int32, device=DEV),
+                topk_count=torch.empty(B, dtype=torch.int32, device=DEV),
+                gather_buf=torch.zeros(B, K + W, REC, dtype=torch.uint8, device=DEV),
+                n_valid=torch.empty(B, dtype=torch.int32, device=DEV),
+                out=torch.empty(B, 64, 512, dtype=torch.bfloat16, device=DEV), lse=torch.empty(B, 64, device=DEV))
+    io = csa.make_step_io(pos=pos, q=dev_bf16(x["q"]), q_idx=torch.from_numpy(qc).to(DEV), w_idx=dev_f32(w8),
+                          kv_new=dev_bf16(x["kv_new"]), z_main=dev_f32(x["z_main"]), c_main=dev_f32(x["c_main"]),
+                          z_idx=dev_f32(x["z_idx"]), c_idx=dev_f32(x["c_idx"]), **outs)
+    ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+    csa.csa_decode_step(L, io, ws)
+    torch.cuda.synchronize()
+    N = x["n_comp"] + 1
+    for b in range(B):
+        ost = oracle.LayerState(comp_kv=comp_vals[b].copy(), idx_keys=np.zeros((1000, 128)), n_comp=x["n_comp"],
+                                swa=oracle.SwaRing(swa_vals[b].copy(), x["swa_head"], x["swa_len"]),
+                                main_bias=x["main_bias"], idx_bias=x["idx_bias"], sink=x["sink"],
+                                idx_codes=kc0[b].copy(), idx_scales=ks0[b].copy(), kv_mixed=True, rope_dim=ROPE,
+                                rope_cos=rc.astype(np.float64), rope_sin=rs.astype(np.float64),
+                                comp_rope_cos=cc.astype(np.float64), comp_rope_sin=cs.astype(np.float64))
+        oracle.decode_step(ost, q=f(x["q"][b]), q_idx=qc[b], w_idx=w8[b], kv_new=f(x["kv_new"][b]), pos=pos,
+                           top_k=K, z_main=x["z_main"][b], c_main=x["c_main"][b], z_idx=x["z_idx"][b],
+                           c_idx=x["c_idx"][b], scale=1 / np.sqrt(512))
+        # the new records: the ring one bit-exact, the entry within rounding; the key within E4M3 rounding
+        c_, s_, rp_, _ = oracle.mixed_kv_row(f(x["kv_new"][b]), ROPE)
+        np.testing.assert_array_equal(swa[b, x["swa_head"]].cpu().numpy(), record_of(c_, s_, rp_))
+        _assert_entry_close(comp[b, N - 1].cpu().numpy(), ost.comp_kv[N - 1])
+        gk, gs = kc[b, N - 1].cpu().numpy(), float(ks[b, N - 1])
+        yi = oracle.compress(x["z_idx"][b], x["c_idx"][b], x["idx_bias"], 4)[-1]
+        assert gs == pytest.approx(np.abs(yi).max() / 448, rel=1e-5)
+        ost.comp_kv[:N] = decode_records(comp[b, :N].cpu().numpy())
+        ost.idx_codes[:N], ost.idx_scales[:N] = kc[b, :N].cpu().numpy(), ks[b, :N].cpu().numpy()
+        ref_s = oracle.index_score_fp8(qc[b][None], w8[b][None], ost.idx_codes[:N], ost.idx_scales[:N])[0]
+        got_s = outs["scores"][b, :N].cpu().numpy().astype(np.float64)
+        assert rel_err(got_s, ref_s) <= 1e-4
+        gi, gc = outs["topk_idx"][b].cpu().numpy(), int(outs["topk_count"][b])
+        np.testing.assert_array_equal(gi, oracle.topk(got_s[None], K)[0][0])
+        assert_topk_gap_rule(gi, gc, ref_s, K)
+        recs, ring = comp[b].cpu().numpy(), swa[b].cpu().numpy()
+        head, ln = (x["swa_head"] + 1) % W, min(x["swa_len"] + 1, W)
+        want_buf = np.stack([recs[i] for i in gi[:gc]] + [ring[(head - ln + j) % W] for j in range(ln)])
+        nv = int(outs["n_valid"][b])
+        assert nv == len(want_buf)
+        np.testing.assert_array_equal(outs["gather_buf"][b, :nv].cpu().numpy(), want_buf)
+        ro, rl = oracle.sparse_attn(f(x["q"][b]), decode_records(want_buf), x["sink"], 1 / np.sqrt(512))
+        ro = oracle.rope_rotate(ro, rc[pos].astype(np.float64), rs[pos].astype(np.float64), inverse=True)
+        assert rel_err(host_f64(outs["out"][b]), ro) <= 2e-2
+        assert np.abs(outs["lse"][b].cpu().numpy() - rl).max() <= 1e-2
