@@ -54,11 +54,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
                                                              int out_bf16, float* __restrict__ lse,
                                                              long long out_stride_b, const float* inv_cos,
                                                              const float* inv_sin, int rope_start,
-                                                             const DevState* dev, const float* rope_cos,
-                                                             const float* rope_sin, int rope_rows) {
+                                                             const int* dev_pos, const float* rope_cos,
+                                                             const float* rope_sin, int rope_rows, DevState* adv,
+                                                             int adv_m, int adv_w, int adv_max_comp) {
     __shared__ float2 part[kMergeWaves][kWave];
-    if (dev && rope_cos) {  // the inverse-RoPE row of the position on the device
-        const int p = dev->pos < 0 ? 0 : (dev->pos < rope_rows ? dev->pos : rope_rows - 1);
+    if (dev_pos && rope_cos) {  // the inverse-RoPE row of the step's position (device counters)
+        const int p = *dev_pos < rope_rows ? *dev_pos : rope_rows - 1;
         const long long row = static_cast<long long>(p) * (kMixRope / 2);
         inv_cos = rope_cos + row;
         inv_sin = rope_sin + row;
@@ -161,6 +162,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
     }
     if (lse && cb == 0 && lane == 0)
         lse[static_cast<long long>(b) * h + hh] = den > 0.f ? M + logf(den) : -INFINITY;
+    // device counters: the step's other kernels have read them (stream order)
+    // and no workgroup of this one does
+    if (adv && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) dev_advance(adv, adv_m, adv_w, adv_max_comp);
 }
 
 // float32 path
@@ -245,30 +249,6 @@ size_t attn_workspace_bytes(bool bf16, int batch, int h, int d, int n_max) {
     return sizeof(float) * static_cast<size_t>(batch) * h * ns * (static_cast<size_t>(d) + 2);
 }
 
-namespace {
-
-// Move the device counters past the step that just ran (its kernels read
-// them before this one starts: stream order).
-__global__ void k_step_advance(DevState* st, int m, int w, int max_comp) {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    DevState s = dev_load(st, w, max_comp);
-    if (s.pos % m == m - 1) {
-        if (s.n_comp < max_comp) s.n_comp += 1;
-        else s.flags |= kDevFlagCacheFull;
-    }
-    s.pos += 1;
-    s.swa_head = (s.swa_head + 1) % w;
-    s.swa_len = s.swa_len + 1 < w ? s.swa_len + 1 : w;
-    *st = s;
-}
-
-}  // namespace
-
-hipError_t launch_step_advance(DevState* st, int m, int w, int max_comp, hipStream_t s) {
-    hipLaunchKernelGGL(k_step_advance, dim3(1), dim3(kWave), 0, s, st, m, w, max_comp);
-    return hipGetLastError();
-}
-
 int attn_max_splits() { return kMaxSplits; }
 
 int attn_max_rows() { return kMaxSplits * 32; }
@@ -287,7 +267,8 @@ hipError_t launch_attn_merge(const AttnArgs& a, int ns, hipStream_t s) {
     hipLaunchKernelGGL(k_attn_merge, dim3(a.h * col_blocks, a.batch), dim3(kAttnThreads), 0, s, a.ws_o, a.ws_ml,
                        a.sink, a.h,
                        a.d, ns, a.out, a.out_bf16 ? 1 : 0, a.lse, a.out_stride_b, a.inv_cos, a.inv_sin,
-                       a.d - kMixRope, a.dev, a.kv_mixed ? a.rope_cos : nullptr, a.rope_sin, a.rope_rows);
+                       a.d - kMixRope, a.dev_pos, a.kv_mixed ? a.rope_cos : nullptr, a.rope_sin, a.rope_rows,
+                       a.dev_adv, a.m, a.w, a.max_comp);
     return hipGetLastError();
 }
 

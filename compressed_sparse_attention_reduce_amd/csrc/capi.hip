@@ -573,10 +573,13 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
             a.rope_cos = L->rope_cos;
             a.rope_sin = L->rope_sin;
             a.rope_rows = L->rope_rows;
+            // one int past the attention workspace (inside the step's slack)
+            a.dev_pos = reinterpret_cast<int*>(static_cast<char*>(aws) +
+                                               align256(csa::attn_workspace_bytes(true, L->batch, L->h, L->d, n_max)));
+            a.dev_adv = dev;
         }
         e = fuse ? csa::launch_topk_attn(ta, ca.lists ? &ca : nullptr, a, s) : csa::launch_attn_bf16(a, s);
-        if (e != hipSuccess || !dev) return launched(e, "csa_decode_step/attention");
-        return launched(csa::launch_step_advance(dev, L->m, L->w, L->max_comp, s), "csa_decode_step_dev/advance");
+        return launched(e, "csa_decode_step/attention");
     }
     e = csa::launch_gather(L->comp_kv, N, io->topk_idx, io->topk_count, L->top_k, L->swa, swa_head,
                            swa_len, L->w, io->gather_buf, io->n_valid, es, L->batch, L->d,

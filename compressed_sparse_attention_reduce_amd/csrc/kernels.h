@@ -60,7 +60,19 @@ __host__ __device__ inline DevState dev_load(const DevState* p, int w, int max_c
 __host__ __device__ inline bool dev_completes(const DevState& s, int m, int max_comp) {
     return s.pos % m == m - 1 && s.n_comp < max_comp;
 }
-hipError_t launch_step_advance(DevState* st, int m, int w, int max_comp, hipStream_t s);
+// Move the counters past the step that read them (one thread, after every
+// reader of this step is done).
+__host__ __device__ inline void dev_advance(DevState* st, int m, int w, int max_comp) {
+    DevState s = dev_load(st, w, max_comp);
+    if (s.pos % m == m - 1) {
+        if (s.n_comp < max_comp) s.n_comp += 1;
+        else s.flags |= kDevFlagCacheFull;
+    }
+    s.pos += 1;
+    s.swa_head = (s.swa_head + 1) % w;
+    s.swa_len = s.swa_len + 1 < w ? s.swa_len + 1 : w;
+    *st = s;
+}
 
 // ---- lightning-indexer score -------------------------------------------------
 struct ScoreArgs {
@@ -201,6 +213,11 @@ struct AttnArgs {
     const float* rope_cos;
     const float* rope_sin;
     int rope_rows;  // positions past the table use its last row
+    // the fused top-k attention stores the step's position here for the
+    // merge, which then advances *dev_adv (so no reader of the counters runs
+    // after the advance within the step)
+    int* dev_pos;
+    DevState* dev_adv;
 };
 size_t attn_workspace_bytes(bool bf16, int batch, int h, int d, int n_max);
 int attn_max_splits();

@@ -23,6 +23,7 @@ __host__ __device__ inline size_t topk_attn_lds_bytes() {
 __global__ __launch_bounds__(kFinalThreads) void k_topk_attn(TopkArgs ta, CandArgs c, AttnArgs a, int n_splits) {
     if (a.dev) {  // counters on the device: the step's view of them after its jobs
         const DevState st = dev_load(a.dev, a.w, a.max_comp);
+        if (a.dev_pos && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *a.dev_pos = st.pos;
         const int n = st.n_comp + (dev_completes(st, a.m, a.max_comp) ? 1 : 0);
         ta.n = n;
         a.n_comp = n;
