@@ -353,8 +353,8 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
         CHECK(ring_bytes >= csa_decode_step_dev_ring_size(L), "csa_decode_step_dev: ring %zu < %zu bytes",
               ring_bytes, csa_decode_step_dev_ring_size(L));
         CHECK(L->max_comp >= 1, "csa_decode_step_dev: max_comp must be positive");
-        if (L->dtype != CSA_BF16 || L->idx_dtype == CSA_FP8_E4M3)
-            return fail(CSA_ERR_UNSUPPORTED, "csa_decode_step_dev: bfloat16 caches and indexer keys only");
+        if (L->dtype != CSA_BF16)
+            return fail(CSA_ERR_UNSUPPORTED, "csa_decode_step_dev: bfloat16 caches only");
     } else {
         CHECK(io->pos >= 0, "csa_decode_step: pos < 0");
         CHECK(L->n_comp >= 0 && L->n_comp <= L->max_comp, "csa_decode_step: n_comp %d outside 0..max_comp %d",
@@ -512,7 +512,7 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
         const csa::Fp8ScoreArgs fa{static_cast<const uint8_t*>(io->q_idx), io->w_idx,
                                    static_cast<const uint8_t*>(L->idx_keys), L->idx_scales, io->scores,
                                    L->batch, 1, n_scan, nullptr, L->m, io->q_idx_stride_b, io->w_stride_b,
-                                   L->idx_keys_stride_b, L->idx_scales_stride_b, io->scores_stride_b, N, ca};
+                                   L->idx_keys_stride_b, L->idx_scales_stride_b, io->scores_stride_b, N, ca, dev};
         e = csa::launch_index_score_fp8(fa, &pa, s);
     } else {
         e = bf ? csa::launch_index_score_bf16(sa, &pa, s) : csa::launch_index_score_f32(sa, s);

@@ -126,9 +126,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
         float* ybuf = lds;
         float* key = lds + kPrepMaxD;
         step_prep_role(p, blockIdx.x, b, ybuf, ws, key);
-        if (blockIdx.x == 2 && p.completes) {
+        const bool completes = p.dev ? dev_completes(dev_load(p.dev, p.swa_w, p.max_comp), p.m, p.max_comp)
+                                     : p.completes != 0;
+        if (blockIdx.x == 2 && !completes && kCands && p.dev && threadIdx.x <= a.cands.m)  // an empty last slot
+            a.cands.lists[(static_cast<long long>(row) * a.cands.slots + a.cands.slots - 1) * (a.cands.m + 1) +
+                          threadIdx.x] = 0ull;
+        if (blockIdx.x == 2 && completes) {
             float sc = score_one_key_fp8(a, b, tt, key, ws + 8);
-            const int kidx = a.n;
+            const int kidx = p.dev ? dev_load(p.dev, p.swa_w, p.max_comp).n_comp : a.n;
             if (a.q_pos && static_cast<long long>(a.ratio) * kidx + a.ratio - 1 > a.q_pos[row]) sc = -INFINITY;
             if (threadIdx.x == 0) a.scores[b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s + kidx] = sc;
             if (kCands && threadIdx.x <= a.cands.m) {
@@ -145,7 +150,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
     const int scan_wgs = gridDim.x - prep_wgs;
     const int li = lane & 15;
     const int lg = lane >> 4;
-    const int n = a.n;
+    const int n = a.dev ? dev_load(a.dev, p.swa_w > 0 ? p.swa_w : 1, a.n).n_comp : a.n;
+    if (a.dev) tiles_per_row = (n + kTileKeys - 1) / kTileKeys;
     if (n <= 0) {  // nothing to scan: an empty candidate list
         if (kCands && threadIdx.x <= a.cands.m)
             a.cands.lists[(static_cast<long long>(row) * a.cands.slots + wg) * (a.cands.m + 1) + threadIdx.x] = 0ull;

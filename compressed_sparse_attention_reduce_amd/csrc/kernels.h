@@ -120,6 +120,8 @@ struct Fp8ScoreArgs {
     long long q_stride_b, w_stride_b, k_stride_b, ks_stride_b, s_stride_b, ld_s;
     // optional top-k candidates, as in ScoreArgs
     CandArgs cands;
+    // decode step with device counters, as in ScoreArgs
+    const DevState* dev;
 };
 // Scan workgroups per row and keys per scan workgroup of the FP8 scan.
 int index_score_fp8_wgs(int rows, int n, int extra);

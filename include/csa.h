@@ -364,8 +364,8 @@ int csa_decode_step(const csa_layer_desc *layer, const csa_step_io *io, void *ws
  *     writes nothing and sets bit 0 of state->flags;
  *   - with mixed KV, positions and blocks past the RoPE tables use the
  *     tables' last rows;
- *   - bfloat16 caches and bfloat16 indexer keys only (CSA_ERR_UNSUPPORTED
- *     otherwise).
+ *   - bfloat16 caches only (CSA_ERR_UNSUPPORTED otherwise); E4M3 indexer
+ *     keys and mixed main KV as for csa_decode_step.
  * The workspace is csa_decode_step_workspace_size(layer) bytes.
  * ------------------------------------------------------------------------ */
 typedef struct csa_dev_state {

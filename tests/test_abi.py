@@ -358,8 +358,8 @@ def test_dev_step_validation(csa):
     assert call(L, state=FAKE + 4) == B.CSA_ERR_INVALID_ARG
     L2 = _desc(csa, dtype=csa.CSA_F32)
     assert call(L2, ring_bytes=1 << 30) == B.CSA_ERR_UNSUPPORTED
-    L3 = _desc(csa, idx_dtype=csa.CSA_FP8_E4M3, idx_scales=FAKE)
-    assert call(L3) == B.CSA_ERR_UNSUPPORTED
+    L3 = _desc(csa, idx_dtype=csa.CSA_FP8_E4M3, idx_scales=FAKE, h_i=32)
+    assert call(L3) == B.CSA_ERR_UNSUPPORTED  # E4M3 keys need the 64 x 128 indexer
     io.z_idx = None
     assert call(L) == B.CSA_ERR_INVALID_ARG
     assert "Z/C" in csa.csa_last_error()

@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import synth
+from oracle import numfmt
 from tests.gpu_util import DEV, dev_bf16, dev_f32
 
 pytestmark = pytest.mark.gpu
@@ -34,7 +35,7 @@ def _tables(rows, offset, base):
     return dev_f32(np.cos(ang).astype(np.float32)), dev_f32(np.sin(ang).astype(np.float32))
 
 
-def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64):
+def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64, fp8=False):
     g = _g(seed)
     D, Di, H = 512, 128, 64
     m = 4
@@ -48,8 +49,12 @@ def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64):
     rope = _tables(pos0 + steps + 4, 0.5, 10000.0) if mixed else None
     comp_rope = _tables(max_comp + 2, 0.25, 500.0) if mixed else None
 
+    if fp8:
+        kc0, ks0 = numfmt.quantize_e4m3_rows(numfmt.bf16_bits_to_f64(keys_bits).reshape(-1, Di).astype(np.float32))
+        kc0, ks0 = kc0.reshape(B, max_comp, Di), ks0.reshape(B, max_comp)
+
     def caches():
-        keys = dev_bf16(keys_bits)
+        keys = (torch.from_numpy(kc0.copy()).to(DEV), dev_f32(ks0)) if fp8 else dev_bf16(keys_bits)
         if mixed:
             comp = torch.empty(B, max_comp, REC, dtype=torch.uint8, device=DEV)
             swa = torch.empty(B, W, REC, dtype=torch.uint8, device=DEV)
@@ -60,7 +65,9 @@ def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64):
         return comp, keys, swa
 
     def layer(comp, keys, swa):
-        return csa.make_layer_desc(comp_kv=comp, idx_keys=keys, swa=swa, main_bias=mb, idx_bias=ib, sink=sink,
+        keys, scales = keys if fp8 else (keys, None)
+        return csa.make_layer_desc(comp_kv=comp, idx_keys=keys, idx_scales=scales, swa=swa, main_bias=mb,
+                                   idx_bias=ib, sink=sink,
                                    n_comp=n0, swa_head=pos0 % W, swa_len=min(pos0, W), h=H, h_i=64, top_k=K,
                                    overlap=overlap, rope=rope, comp_rope=comp_rope)
 
@@ -80,7 +87,7 @@ def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64):
     Ld = layer(cd, kd, sd)
     # static inputs of the captured step
     st_in = dict(q=torch.zeros(B, H, D, dtype=torch.bfloat16, device=DEV),
-                 q_idx=torch.zeros(B, 64, Di, dtype=torch.bfloat16, device=DEV),
+                 q_idx=torch.zeros(B, 64, Di, dtype=torch.uint8 if fp8 else torch.bfloat16, device=DEV),
                  w_idx=torch.zeros(B, 64, device=DEV),
                  kv_new=torch.zeros(B, D, dtype=torch.bfloat16, device=DEV),
                  z_main=torch.zeros(B, wm, device=DEV), c_main=torch.zeros(B, wm, device=DEV),
@@ -109,8 +116,14 @@ def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64):
         for k in hist_z:
             hist_z[k].append(x[k])
         # the captured step: new inputs into its static buffers, one replay
-        for k, v in x.items():
-            st_in[k].copy_(dev_bf16(v) if v.dtype == np.uint16 else dev_f32(v))
+        if fp8:  # E4M3 query, its per-head scales folded into the weights
+            qc, qs = numfmt.quantize_e4m3_rows(numfmt.bf16_bits_to_f64(x["q_idx"]).reshape(-1, Di).astype(np.float32))
+            x["q_idx"] = qc.reshape(B, 64, Di)
+            x["w_idx"] = (x["w_idx"] * qs.reshape(B, 64)).astype(np.float32)
+        dev_in = {k: (torch.from_numpy(v).to(DEV) if v.dtype == np.uint8 else
+                      dev_bf16(v) if v.dtype == np.uint16 else dev_f32(v)) for k, v in x.items()}
+        for k, v in dev_in.items():
+            st_in[k].copy_(v)
         print(f"dev step pos={pos}", flush=True)
         graph.replay()
         torch.cuda.synchronize()
@@ -123,8 +136,8 @@ def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64):
                 rows = np.stack(hist_z[k][-2 * m:], axis=1)           # previous block then this one
             blk[k] = dev_f32(np.ascontiguousarray(rows)) if completes else dev_f32(np.zeros((B, m, rows.shape[2]), np.float32))
         oh = outs()
-        ioh = csa.make_step_io(pos=pos, q=dev_bf16(x["q"]), q_idx=dev_bf16(x["q_idx"]), w_idx=dev_f32(x["w_idx"]),
-                               kv_new=dev_bf16(x["kv_new"]), **blk, **oh)
+        ioh = csa.make_step_io(pos=pos, q=dev_in["q"], q_idx=dev_in["q_idx"], w_idx=dev_in["w_idx"],
+                               kv_new=dev_in["kv_new"], **blk, **oh)
         csa.csa_decode_step(Lh, ioh, wsh)
         csa.csa_layer_advance(Lh, pos)
         torch.cuda.synchronize()
@@ -136,7 +149,11 @@ def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64):
             assert torch.equal(od[k], oh[k]), (pos, k)
         nv = int(oh["n_valid"].min())
         assert torch.equal(od["gather_buf"][:, :nv], oh["gather_buf"][:, :nv])
-        assert torch.equal(cd[:, :N], ch[:, :N]) and torch.equal(kd[:, :N], kh[:, :N]) and torch.equal(sd, sh)
+        if fp8:
+            assert torch.equal(kd[0][:, :N], kh[0][:, :N]) and torch.equal(kd[1][:, :N], kh[1][:, :N])
+        else:
+            assert torch.equal(kd[:, :N], kh[:, :N])
+        assert torch.equal(cd[:, :N], ch[:, :N]) and torch.equal(sd, sh)
     return state, cd, ch
 
 
@@ -149,6 +166,11 @@ def test_dev_step_overlap_and_mixed_kv(csa):
     """The overlapped compressor (the ring keeps the previous block) and mixed
     main KV (RoPE rows from the device position), from the first token."""
     _run(csa, mixed=True, overlap=1, B=1, n0=0, pos0=0, max_comp=16, steps=13, seed=8102)
+
+
+def test_dev_step_fp8_keys(csa):
+    """E4M3 indexer keys (the new key quantised in the step), batch 2."""
+    _run(csa, mixed=False, overlap=0, B=2, n0=150, pos0=600, max_comp=200, steps=9, seed=8104, fp8=True)
 
 
 def test_dev_step_full_cache_sets_flag(csa):
