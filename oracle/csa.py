@@ -536,18 +536,28 @@ def hca_decode_step(L: LayerState, *, q, kv_new, pos: int, z_main=None, c_main=N
     in the mixed-precision gather, ``gather_mixed_all``).  The compressor is the
     plain, non-overlapped ratio-``m`` reduce (page 1,
     ``hca_compress_reduce_kernel``), run when the token completes a block.
-    ``L.idx_keys`` is not used.  Mutates ``L``; returns the new entry, the
-    attended rows and ``out``/``lse``.
+    ``L.idx_keys`` is not used.  With mixed main KV (``L.kv_mixed``) the rows
+    are stored, rotated and rotated back as in :func:`decode_step` (the
+    pages' ``gather_mixed_all`` is the mixed gather of this branch).
+    Mutates ``L``; returns the new entry, the attended rows and
+    ``out``/``lse``.
     """
     m = L.m
-    L.swa.append(np.asarray(kv_new, dtype=np.float64))
+    if L.kv_mixed:
+        L.swa.append(mixed_kv_row(kv_new, L.rope_dim)[3])
+    else:
+        L.swa.append(np.asarray(kv_new, dtype=np.float64))
     rnd = L.round_cache if L.round_cache is not None else (lambda a: a)
     new_entry = None
     if pos % m == m - 1:
         ym = compress(z_main, c_main, L.main_bias, m, overlap=False)[-1]
         if L.main_norm is not None:
             ym = kv_norm(ym, L.main_norm)
-        L.comp_kv[L.n_comp] = rnd(ym)
+        if L.kv_mixed:
+            blk = pos // m
+            L.comp_kv[L.n_comp] = mixed_kv_row(ym, L.rope_dim, L.comp_rope_cos[blk], L.comp_rope_sin[blk])[3]
+        else:
+            L.comp_kv[L.n_comp] = rnd(ym)
         new_entry = ym
         L.n_comp += 1
     N = L.n_comp
@@ -557,6 +567,8 @@ def hca_decode_step(L: LayerState, *, q, kv_new, pos: int, z_main=None, c_main=N
     rows = np.concatenate([np.asarray(L.comp_kv[:N], dtype=np.float64),
                            np.stack(win) if win else np.zeros((0, D))], axis=0)
     out, lse = sparse_attn(q, rows, L.sink, scale)
+    if L.kv_mixed:
+        out = rope_rotate(out, L.rope_cos[pos], L.rope_sin[pos], inverse=True)
     return {"new_entry": new_entry, "rows": rows, "n_valid": rows.shape[0], "out": out, "lse": lse}
 
 

@@ -784,6 +784,28 @@ def test_hca_step_equals_csa_step_with_top_k_covering_all():
         np.testing.assert_allclose(rh["lse"], rc["lse"], rtol=1e-13)
 
 
+def test_hca_step_mixed_kv_equals_csa_step_mixed_kv_with_top_k_covering_all():
+    """With mixed main KV too, an HCA step equals a CSA step whose top-k
+    covers every entry: the same stored rows, rotations and output."""
+    g = _g(32)
+    m, W, D, H, rd = 8, 6, 16, 4, 4
+    Lh = _empty_state(g, D=D, W=W, H=H, m=m)
+    Lc = _empty_state(g, D=D, W=W, H=H, m=m)
+    Lc.main_bias, Lc.sink = Lh.main_bias, Lh.sink
+    cos, sin = _rope_tables(64, rd)
+    ccos, csin = _rope_tables(16, rd, base=9.0, offset=0.5)
+    for L in (Lh, Lc):
+        L.kv_mixed, L.rope_dim = True, rd
+        L.rope_cos, L.rope_sin, L.comp_rope_cos, L.comp_rope_sin = cos, sin, ccos, csin
+    for pos in range(27):
+        inp = _step_inputs(g, D=D, H=H, m=m)
+        rh = oracle.hca_decode_step(Lh, q=inp["q"], kv_new=inp["kv_new"], pos=pos,
+                                    z_main=inp["z_main"], c_main=inp["c_main"])
+        rc = oracle.decode_step(Lc, pos=pos, top_k=64, **inp)
+        np.testing.assert_array_equal(Lh.comp_kv[:Lh.n_comp], Lc.comp_kv[:Lc.n_comp])
+        np.testing.assert_allclose(rh["out"], rc["out"], rtol=1e-12, atol=1e-13)
+
+
 def test_hca_step_rows_are_cache_then_window():
     g = _g(25)
     L = _empty_state(g, W=4, m=2)
