@@ -606,14 +606,32 @@ int csa_decode_step_dev(const csa_layer_desc* L, const csa_step_io* io, csa_dev_
 size_t csa_hca_decode_step_workspace_size(const csa_layer_desc* L) {
     if (!L || L->batch < 1 || L->max_comp < 0 || L->w < 1 || L->h < 1 || L->d < 1) return 0;
     const size_t ns = static_cast<size_t>(csa::attn_dense_splits(L->max_comp + L->w));
-    return align256(sizeof(float) * static_cast<size_t>(L->batch) * L->h * ns * (static_cast<size_t>(L->d) + 2)) + 256;
+    // split partials, then (mixed KV) the new entry in float32 per sequence
+    return align256(sizeof(float) * static_cast<size_t>(L->batch) * L->h * ns * (static_cast<size_t>(L->d) + 2)) +
+           align256(sizeof(float) * static_cast<size_t>(L->batch) * L->d) + 256;
 }
 
 int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes,
                         csa_stream stream) {
     CHECK(L && io, "csa_hca_decode_step: null layer or io");
-    if (L->dtype != CSA_BF16 || L->kv_dtype == CSA_FP8_E4M3)
-        return fail(CSA_ERR_UNSUPPORTED, "csa_hca_decode_step: bfloat16 caches only (no mixed KV)");
+    if (L->dtype != CSA_BF16)
+        return fail(CSA_ERR_UNSUPPORTED, "csa_hca_decode_step: bfloat16 caches only");
+    const bool mixed = L->kv_dtype == CSA_FP8_E4M3;
+    if (mixed) {
+        if (L->d != csa::kMixD || L->rope_dim != csa::kMixRope || L->main_norm)
+            return fail(CSA_ERR_UNSUPPORTED, "csa_hca_decode_step: mixed KV needs d = %d, rope_dim = %d, no main norm",
+                        csa::kMixD, csa::kMixRope);
+        CHECK(L->rope_cos && L->rope_sin && L->comp_rope_cos && L->comp_rope_sin && L->rope_rows >= 1 &&
+                  L->comp_rope_rows >= 1,
+              "csa_hca_decode_step: mixed KV needs both RoPE tables");
+        CHECK(io->pos < L->rope_rows, "csa_hca_decode_step: pos %d outside the RoPE table (%d rows)", io->pos,
+              L->rope_rows);
+        CHECK(io->pos % L->m != L->m - 1 || io->pos / L->m < L->comp_rope_rows,
+              "csa_hca_decode_step: block %d outside the compressed-entry RoPE table (%d rows)", io->pos / L->m,
+              L->comp_rope_rows);
+        CHECK(L->comp_kv_stride_b % 16 == 0 && L->swa_stride_b % 16 == 0,
+              "csa_hca_decode_step: mixed records' batch strides must be multiples of 16 bytes");
+    }
     CHECK(dtype_ok(L->out_dtype), "csa_hca_decode_step: bad out_dtype");
     CHECK(L->batch >= 1 && L->m >= 1 && L->w >= 1, "csa_hca_decode_step: bad batch/m/w");
     CHECK(L->overlap == 0, "csa_hca_decode_step: the HCA compressor is not overlapped (overlap must be 0)");
@@ -672,6 +690,12 @@ int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws
     pa.idx_keys = nullptr;
     // long blocks without a norm: channel slices over several workgroups
     pa.main_wgs = (L->m >= 32 && !L->main_norm) ? (L->d + 31) / 32 : 1;
+    pa.kv_mixed = mixed ? 1 : 0;
+    if (mixed && completes) {
+        const long long row = static_cast<long long>(io->pos / L->m) * (csa::kMixRope / 2);
+        pa.entry_cos = L->comp_rope_cos + row;
+        pa.entry_sin = L->comp_rope_sin + row;
+    }
 
     // c. attention over the rows before the step — the entries before it and
     //    the window rows that stay (the new token's slot is being written) —
@@ -700,8 +724,15 @@ int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws
     a.d = L->d;
     a.n_max = n_max;
     a.ws = ws;
-    const void* x0 = completes ? static_cast<const char*>(L->comp_kv) + 2 * static_cast<long long>(L->n_comp) * L->d
-                               : nullptr;
+    if (mixed) {
+        const long long row = static_cast<long long>(io->pos) * (csa::kMixRope / 2);
+        a.kv_mixed = true;
+        a.inv_cos = L->rope_cos + row;
+        a.inv_sin = L->rope_sin + row;
+    }
+    const void* x0 = completes && !mixed
+                         ? static_cast<const char*>(L->comp_kv) + 2 * static_cast<long long>(L->n_comp) * L->d
+                         : nullptr;
     return launched(csa::launch_attn_dense_bf16(a, pa, x0, L->comp_kv_stride_b, io->kv_new, io->kv_new_stride_b, s),
                     "csa_hca_decode_step");
 }

@@ -20,6 +20,7 @@
 #include "attn_split.h"
 #include "common.h"
 #include "kernels.h"
+#include "mixed_kv.h"
 #include "step_prep.h"
 
 namespace csa {
@@ -42,8 +43,11 @@ __host__ __device__ inline size_t dense_lds_bytes(int d) {
                                static_cast<size_t>(kHeadGroup) * kDensePPitch);
 }
 
+// mixed: the rows are mixed records (mixed_kv.h), decoded to bfloat16 on
+// load, and the folded compression writes the block's entry in float32 to
+// entry_f32 ([B][512]) for the merge to pack.
 __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, int n_splits, int prep_wgs, PrepArgs p,
-                                                                    int extra_rows, int fold_ch) {
+                                                                    int extra_rows, int fold_ch, float* entry_f32) {
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     __shared__ float wmax[kDenseWaves][kHeadGroup];
     __shared__ float wsum[kDenseWaves][kHeadGroup];
@@ -80,8 +84,13 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
     auto fold_block = [&](float* scratch) {
         const float* z = p.z_main + b * p.zc_main_stride_b;
         const float* c = p.c_main + b * p.zc_main_stride_b;
-        char* out = static_cast<char*>(p.comp_kv) + (b * p.comp_kv_stride_b + static_cast<long long>(p.n_comp) * p.d) * p.es;
         const int ch0 = id * fold_ch;
+        if (entry_f32) {
+            compress_block_slice(z, c, p.main_bias, entry_f32 + static_cast<long long>(b) * p.d, false, p.m, p.d, ch0,
+                                 min(fold_ch, p.d - ch0), scratch);
+            return;
+        }
+        char* out = static_cast<char*>(p.comp_kv) + (b * p.comp_kv_stride_b + static_cast<long long>(p.n_comp) * p.d) * p.es;
         compress_block_slice(z, c, p.main_bias, out, p.es == 2, p.m, p.d, ch0, min(fold_ch, p.d - ch0), scratch);
     };
     const int lane = threadIdx.x & (kWave - 1);
@@ -125,6 +134,30 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
         const int c = threadIdx.x + u * kDenseThreads;
         const int r = c / cpr;
         const int j = r0 + r;
+        if (a.kv_mixed) {  // records (d = 512): 8 codes + the scale, or 16 bytes of the RoPE part
+            const uint8_t* rec = nullptr;
+            if (c < kDenseRows * cpr && r < rows) {
+                if (j < cnt) {
+                    rec = reinterpret_cast<const uint8_t*>(a.comp_kv) + b * a.comp_kv_stride_b +
+                          static_cast<long long>(j) * kMixRec;
+                } else {
+                    int slot = (a.swa_head - a.swa_len + (j - cnt)) % a.w;
+                    if (slot < 0) slot += a.w;
+                    rec = reinterpret_cast<const uint8_t*>(a.swa) + b * a.swa_stride_b +
+                          static_cast<long long>(slot) * kMixRec;
+                }
+            }
+            const int cc = c % cpr;
+            if (!rec) {
+                v[u] = make_uint4(0, 0, 0, 0);
+            } else if (cc < kMixNope / 8) {
+                const uint2 cw = *reinterpret_cast<const uint2*>(rec + 8 * cc);
+                v[u] = make_uint4(cw.x, cw.y, __float_as_uint(*reinterpret_cast<const float*>(rec + kMixScaleOff)), 1u);
+            } else {
+                v[u] = *reinterpret_cast<const uint4*>(rec + kMixNope + 16 * (cc - kMixNope / 8));
+            }
+            continue;
+        }
         const uint16_t* src = nullptr;
         if (c < kDenseRows * cpr && r < rows) {
             if (j < cnt) {
@@ -136,6 +169,13 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
             }
         }
         v[u] = src ? *reinterpret_cast<const uint4*>(src + (c % cpr) * 8) : make_uint4(0, 0, 0, 0);
+    }
+    if (a.kv_mixed) {  // decode the NoPE pieces (w = 1 marks a loaded one)
+#pragma unroll
+        for (int u = 0; u < kDenseRowPer; ++u) {
+            const int c = threadIdx.x + u * kDenseThreads;
+            if ((c % cpr) < kMixNope / 8 && v[u].w == 1u) v[u] = decode8_bf16(v[u].x, v[u].y, __uint_as_float(v[u].z));
+        }
     }
     // the block's channels while the rows are in flight (LDS as scratch first)
     if (fold) {
@@ -246,11 +286,20 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
 constexpr int kMergeThreads = 256;
 constexpr int kMergeWaves = kMergeThreads / kWave;
 constexpr int kMergeCols = 2 * kWave;  // columns per workgroup: a column pair per lane
+// Mixed main KV (a.kv_mixed, d = 512): x0f is the new entry in float32
+// ([B][512], from the attention kernel, or nullptr) and x1 the new token's
+// row; both take part as the caches now hold them (packed, then decoded as
+// the attention's loader decodes), and workgroup 0 of each sequence writes
+// the entry's record to rec0 (entry_cos / entry_sin: its RoPE row); the
+// output's RoPE dims are rotated back with a.inv_cos / a.inv_sin.
 __global__ __launch_bounds__(kMergeThreads) void k_attn_merge_rows(AttnArgs a, int n_splits, const uint16_t* x0,
                                                                    long long x0_stride_b, const uint16_t* x1,
-                                                                   long long x1_stride_b) {
+                                                                   long long x1_stride_b, const float* x0f,
+                                                                   uint8_t* rec0, long long rec0_stride_b,
+                                                                   const float* entry_cos, const float* entry_sin) {
     __shared__ float red[2][kMergeWaves];
     __shared__ float2 part[kMergeWaves][kWave];
+    __shared__ float xv[2][kMixD];  // mixed: the new rows' values as stored
     const int d = a.d;
     const int col_blocks = (d + kMergeCols - 1) / kMergeCols;
     const int hh = blockIdx.x / col_blocks;
@@ -271,7 +320,70 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge_rows(AttnArgs a, i
         hi = __uint_as_float(v & 0xffff0000u);
     };
     float d0 = 0.f, d1 = 0.f;
-    {
+    if (a.kv_mixed) {
+        // the new rows packed as the caches hold them: E4M3 NoPE with the
+        // row's scale (block maxima first), bf16 RoPE (the entry rotated)
+        const int col = 2 * threadIdx.x;  // d = 512: every column pair once
+        float q0, q1, u0 = 0.f, u1 = 0.f, v0, v1;
+        pair(qh, col, q0, q1);
+        if (x0f) {
+            u0 = x0f[static_cast<long long>(b) * kMixD + col];
+            u1 = x0f[static_cast<long long>(b) * kMixD + col + 1];
+        }
+        pair(x1b, col, v0, v1);
+        const bool nope = col < kMixNope;
+        float m0 = nope ? fmaxf(fabsf(u0), fabsf(u1)) : 0.f;
+        float m1 = nope ? fmaxf(fabsf(v0), fabsf(v1)) : 0.f;
+        m0 = wave_max(m0);
+        m1 = wave_max(m1);
+        if (lane == 0) {
+            red[0][wv] = m0;
+            red[1][wv] = m1;
+        }
+        __syncthreads();
+        m0 = red[0][0];
+        m1 = red[1][0];
+#pragma unroll
+        for (int w = 1; w < kMergeWaves; ++w) {
+            m0 = fmaxf(m0, red[0][w]);
+            m1 = fmaxf(m1, red[1][w]);
+        }
+        __syncthreads();  // red is reused for the logits
+        const float s0 = m0 > 0.f ? m0 / 448.0f : 1.0f;
+        const float s1 = m1 > 0.f ? m1 / 448.0f : 1.0f;
+        uint8_t* rec = (rec0 && blockIdx.x == 0) ? rec0 + b * rec0_stride_b : nullptr;
+        if (nope) {
+            const uint8_t c0 = e4m3_encode_rne(u0 / s0), c1 = e4m3_encode_rne(u1 / s0);
+            u0 = bf16_round(e4m3_decode(c0) * s0);
+            u1 = bf16_round(e4m3_decode(c1) * s0);
+            v0 = bf16_round(e4m3_decode(e4m3_encode_rne(v0 / s1)) * s1);
+            v1 = bf16_round(e4m3_decode(e4m3_encode_rne(v1 / s1)) * s1);
+            if (rec && x0f) {
+                rec[col] = c0;
+                rec[col + 1] = c1;
+            }
+        } else {
+            u0 = bf16_round(u0);
+            u1 = bf16_round(u1);
+            const int pr = (col - kMixNope) / 2;
+            if (x0f) {
+                rope_pair(u0, u1, entry_cos[pr], entry_sin[pr], false);
+                u0 = bf16_round(u0);
+                u1 = bf16_round(u1);
+            }
+            if (rec && x0f)
+                *reinterpret_cast<uint32_t*>(rec + kMixNope + 4 * pr) =
+                    static_cast<uint32_t>(f32_to_bf16(u0)) | (static_cast<uint32_t>(f32_to_bf16(u1)) << 16);
+        }
+        if (rec && x0f && threadIdx.x == 0)
+            *reinterpret_cast<uint4*>(rec + kMixScaleOff) = make_uint4(__float_as_uint(s0), 0u, 0u, 0u);
+        xv[0][col] = u0;
+        xv[0][col + 1] = u1;
+        xv[1][col] = v0;
+        xv[1][col + 1] = v1;
+        d0 = q0 * u0 + q1 * u1;
+        d1 = q0 * v0 + q1 * v1;
+    } else {
         const int col = 2 * threadIdx.x;
         if (col < d) {
             float q0, q1, u0 = 0.f, u1 = 0.f, v0, v1;
@@ -312,7 +424,8 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge_rows(AttnArgs a, i
         d0 += red[0][w];
         d1 += red[1][w];
     }
-    const float s0 = x0 ? d0 * a.scale : -INFINITY;
+    const bool has_x0 = x0 != nullptr || x0f != nullptr;
+    const float s0 = has_x0 ? d0 * a.scale : -INFINITY;
     const float s1 = d1 * a.scale;
     M = fmaxf(M, fmaxf(s0, s1));
     const float sk = a.sink ? a.sink[hh] : -INFINITY;
@@ -331,28 +444,42 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge_rows(AttnArgs a, i
     part[wv][lane] = make_float2(acc0, acc1);
     __syncthreads();
     if (wv != 0) return;
-    const float e0 = x0 ? expf(s0 - M) : 0.f;
+    const float e0 = has_x0 ? expf(s0 - M) : 0.f;
     const float e1 = expf(s1 - M);
     const float es = a.sink ? expf(sk - M) : 0.f;
     const float den = wave_sum(wsp * ls) + e0 + e1 + es;
     const float inv = 1.0f / den;
     if (has_col) {
         float u0 = 0.f, u1 = 0.f, w0, w1;
-        if (x0b) pair(x0b, col2, u0, u1);
-        pair(x1b, col2, w0, w1);
+        if (a.kv_mixed) {
+            u0 = xv[0][col2];
+            u1 = xv[0][col2 + 1];
+            w0 = xv[1][col2];
+            w1 = xv[1][col2 + 1];
+        } else {
+            if (x0b) pair(x0b, col2, u0, u1);
+            pair(x1b, col2, w0, w1);
+        }
         float o0 = e0 * u0 + e1 * w0, o1 = e0 * u1 + e1 * w1;
 #pragma unroll
         for (int w = 0; w < kMergeWaves; ++w) {
             o0 += part[w][lane].x;
             o1 += part[w][lane].y;
         }
+        o0 *= inv;
+        o1 *= inv;
+        // mixed KV: the RoPE dims rotated back at the token's position
+        if (a.inv_cos && col2 >= d - kMixRope) {
+            const int pr = (col2 - (d - kMixRope)) / 2;
+            rope_pair(o0, o1, a.inv_cos[pr], a.inv_sin[pr], true);
+        }
         const long long o = b * a.out_stride_b + static_cast<long long>(hh) * d + col2;
         if (a.out_bf16) {
-            static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(o0 * inv);
-            static_cast<uint16_t*>(a.out)[o + 1] = f32_to_bf16(o1 * inv);
+            static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(o0);
+            static_cast<uint16_t*>(a.out)[o + 1] = f32_to_bf16(o1);
         } else {
-            static_cast<float*>(a.out)[o] = o0 * inv;
-            static_cast<float*>(a.out)[o + 1] = o1 * inv;
+            static_cast<float*>(a.out)[o] = o0;
+            static_cast<float*>(a.out)[o + 1] = o1;
         }
     }
     if (a.lse && cb == 0 && lane == 0) a.lse[static_cast<long long>(b) * a.h + hh] = M + logf(den);
@@ -382,21 +509,27 @@ hipError_t launch_attn_dense_bf16(AttnArgs a, const PrepArgs& prep, const void* 
     }
     const int groups = a.h / kHeadGroup;
     const int att_wgs = groups * ns;
-    // a long main block (main_wgs > 1) is folded into the attention
-    // workgroups; otherwise one job workgroup compresses it
-    const bool fold = prep.completes && prep.main_wgs > 1;
+    // a long main block (main_wgs > 1), or any block with mixed KV, is
+    // folded into the attention workgroups; otherwise one job workgroup
+    // compresses it.  With mixed KV the entry goes to the workspace in
+    // float32 and the merge packs it (its row scale spans every slice).
+    const bool fold = prep.completes && (prep.main_wgs > 1 || a.kv_mixed);
+    float* entry_f32 = a.kv_mixed && prep.completes ? a.ws_ml + static_cast<size_t>(a.batch) * a.h * ns * 2 : nullptr;
+    uint8_t* rec0 = entry_f32 ? static_cast<uint8_t*>(prep.comp_kv) + static_cast<long long>(prep.n_comp) * kMixRec
+                              : nullptr;
     const int prep_wgs = prep.completes && !fold ? 2 : 1;
     int fold_ch = 0;
     if (fold) {  // a power of two, so the slices of a channel merge by lane swaps
         fold_ch = kFoldMinCh;
         while (fold_ch * att_wgs < a.d) fold_ch *= 2;
     }
-    const int extra = 1 + (x0 ? 1 : 0);
+    const int extra = 1 + (x0 || entry_f32 ? 1 : 0);
     hipLaunchKernelGGL(k_attn_dense_bf16, dim3(att_wgs + prep_wgs, a.batch), dim3(kDenseThreads), lds, s, a, ns,
-                       prep_wgs, prep, extra, fold_ch);
+                       prep_wgs, prep, extra, fold_ch, entry_f32);
     const int col_blocks = (a.d + kMergeCols - 1) / kMergeCols;
     hipLaunchKernelGGL(k_attn_merge_rows, dim3(a.h * col_blocks, a.batch), dim3(kMergeThreads), 0, s, a, ns,
-                       static_cast<const uint16_t*>(x0), x0_stride_b, static_cast<const uint16_t*>(x1), x1_stride_b);
+                       static_cast<const uint16_t*>(x0), x0_stride_b, static_cast<const uint16_t*>(x1), x1_stride_b,
+                       entry_f32, rec0, prep.comp_kv_stride_b, prep.entry_cos, prep.entry_sin);
     return hipGetLastError();
 }
 

@@ -422,6 +422,12 @@ int csa_pack_kv_mixed(const void *x, csa_dtype x_dtype, unsigned char *rec, long
  * bfloat16 caches only (CSA_ERR_UNSUPPORTED otherwise); h a multiple of 16,
  * d a multiple of 32 up to 512, max_comp + w <= 8192.  The host integers are
  * advanced by the caller (csa_layer_advance) as for csa_decode_step.
+ * Mixed main KV (kv_dtype = CSA_FP8_E4M3, section 6c): the records, tables
+ * and checks of csa_decode_step's mixed form, without a main norm
+ * (main_norm must be null: CSA_ERR_UNSUPPORTED); the ring record and the
+ * entry's record (rotated at block pos / m) are packed as there, every row
+ * is decoded to bfloat16 for the softmax, and out's RoPE dims are rotated
+ * back at pos.
  * Workspace: csa_hca_decode_step_workspace_size(layer) bytes, 16-byte aligned.
  * ------------------------------------------------------------------------ */
 size_t csa_hca_decode_step_workspace_size(const csa_layer_desc *layer);

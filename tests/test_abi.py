@@ -299,7 +299,8 @@ def test_decode_step_fp8_keys_validation(csa):
 
 def test_mixed_kv_validation(csa):
     """Mixed main KV: bfloat16, d = 512, rope_dim = 64, both tables, table
-    rows for the position and the block, 16-byte records; no HCA form."""
+    rows for the position and the block, 16-byte records; the same for the
+    HCA step, which also takes no main norm."""
     B = csa.binding
     lib = csa.lib()
     L = _desc(csa, kv_dtype=csa.CSA_FP8_E4M3, rope_dim=64, rope_rows=5000, comp_rope_rows=1000)
@@ -327,8 +328,24 @@ def test_mixed_kv_validation(csa):
     L.dtype = csa.CSA_F32
     assert call(L) == B.CSA_ERR_UNSUPPORTED
     L.dtype = csa.CSA_BF16
+    # the HCA step over mixed records: no main norm, both tables, the position's row
     L.m = 128
-    assert lib.csa_hca_decode_step(ctypes.byref(L), ctypes.byref(io), FAKE, 1 << 40, None) == B.CSA_ERR_UNSUPPORTED
+
+    def hca():
+        return lib.csa_hca_decode_step(ctypes.byref(L), ctypes.byref(io), FAKE, 1 << 40, None)
+
+    L.main_norm = FAKE
+    assert hca() == B.CSA_ERR_UNSUPPORTED
+    L.main_norm = None
+    L.comp_rope_sin = None
+    assert hca() == B.CSA_ERR_INVALID_ARG
+    L.comp_rope_sin = FAKE
+    L.rope_rows = 3999
+    assert hca() == B.CSA_ERR_INVALID_ARG
+    L.rope_rows = 5000
+    L.comp_kv_stride_b = 592 * 1000 + 4
+    assert hca() == B.CSA_ERR_INVALID_ARG
+    L.comp_kv_stride_b = 0
     assert lib.csa_pack_kv_mixed(FAKE, csa.CSA_BF16, FAKE, 10, 256, 64, None) == B.CSA_ERR_UNSUPPORTED
     assert lib.csa_pack_kv_mixed(FAKE, csa.CSA_FP8_E4M3, FAKE, 10, 512, 64, None) == B.CSA_ERR_INVALID_ARG
     assert lib.csa_pack_kv_mixed(FAKE + 8, csa.CSA_BF16, FAKE + 8, 10, 512, 64, None) == B.CSA_ERR_INVALID_ARG

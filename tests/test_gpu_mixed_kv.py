@@ -371,3 +371,73 @@ def test_decode_step_mixed_kv_fp8_keys_batched(csa):
         ro = oracle.rope_rotate(ro, rc[pos].astype(np.float64), rs[pos].astype(np.float64), inverse=True)
         assert rel_err(host_f64(outs["out"][b]), ro) <= 2e-2
         assert np.abs(outs["lse"][b].cpu().numpy() - rl).max() <= 1e-2
+
+
+HCA_MIXED_CASES = [
+    # name, ratio m, heads, entries before, cache capacity, window
+    ("ratio8_h64", 8, 64, 37, 48, 8),           # a short block, folded since its scale spans every channel
+    ("ratio64_h16_fold", 64, 16, 5, 40, 8),     # the block folded into the one attention workgroup
+    ("ratio32_h32_fold", 32, 32, 20, 300, 16),  # folded over workgroups of empty splits too
+]
+
+
+@pytest.mark.parametrize("case", HCA_MIXED_CASES, ids=[c[0] for c in HCA_MIXED_CASES])
+def test_hca_steps_in_sequence_mixed_kv(csa, case):
+    """Twenty HCA steps over mixed caches (block completions, ring wrap),
+    each against the oracle's evolving state: the ring record bit-exact, the
+    compressed entry within E4M3 / bfloat16 rounding of the oracle's (then
+    adopted), output and lse over every entry and the window."""
+    name, m, H, n0, max_comp, W = case
+    D = 512
+    g = _g(7501 + m)
+    f = numfmt.bf16_bits_to_f64
+    pos0 = n0 * m + (5 if m == 8 else m - 10)
+    comp_rec, comp_val = oracle_records(f(synth.to_bf16_bits(g.standard_normal((max_comp, D), dtype=np.float32))))
+    swa_rec, swa_val = oracle_records(f(synth.to_bf16_bits(g.standard_normal((W, D), dtype=np.float32))))
+    comp = torch.from_numpy(comp_rec[None].copy()).to(DEV)
+    swa = torch.from_numpy(swa_rec[None].copy()).to(DEV)
+    mb = g.standard_normal((m, D), dtype=np.float32) * np.float32(0.1)
+    sink = g.standard_normal(H, dtype=np.float32)
+    rc, rs = rope_tables(pos0 + 20)
+    cc, cs = rope_tables((pos0 + 20) // m + 1, offset=0.25, base=500.0)
+    L = csa.make_layer_desc(comp_kv=comp, idx_keys=None, swa=swa, main_bias=dev_f32(mb), idx_bias=None,
+                            sink=dev_f32(sink), n_comp=n0, swa_head=pos0 % W, swa_len=W, h=H, h_i=0, m=m, top_k=0,
+                            rope=(dev_f32(rc), dev_f32(rs)), comp_rope=(dev_f32(cc), dev_f32(cs)))
+    assert L.kv_dtype == csa.CSA_FP8_E4M3
+    ost = oracle.LayerState(comp_kv=comp_val, idx_keys=np.zeros((max_comp, 1)), n_comp=n0,
+                            swa=oracle.SwaRing(swa_val, pos0 % W, W), main_bias=mb.astype(np.float64),
+                            idx_bias=np.zeros((m, 1)), sink=sink.astype(np.float64), m=m,
+                            round_cache=numfmt.bf16_round_f64, kv_mixed=True, rope_dim=ROPE,
+                            rope_cos=rc.astype(np.float64), rope_sin=rs.astype(np.float64),
+                            comp_rope_cos=cc.astype(np.float64), comp_rope_sin=cs.astype(np.float64))
+    ws = torch.empty(csa.csa_hca_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+    for pos in range(pos0, pos0 + 20):
+        q = synth.to_bf16_bits(g.standard_normal((1, H, D), dtype=np.float32))
+        kvn = synth.to_bf16_bits(g.standard_normal((1, D), dtype=np.float32))
+        zm, cm = g.standard_normal((2, 1, m, D), dtype=np.float32)
+        out = torch.empty(1, H, D, dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty(1, H, device=DEV)
+        n_valid = torch.empty(1, dtype=torch.int32, device=DEV)
+        io = csa.make_step_io(pos=pos, q=dev_bf16(q), kv_new=dev_bf16(kvn), z_main=dev_f32(zm), c_main=dev_f32(cm),
+                              out=out, lse=lse, n_valid=n_valid)
+        print(f"mixed-KV HCA {name} pos={pos}", flush=True)
+        slot = L.swa_head
+        csa.csa_hca_decode_step(L, io, ws)
+        csa.csa_layer_advance(L, pos)
+        torch.cuda.synchronize()
+        nprev = ost.n_comp
+        r = oracle.hca_decode_step(ost, q=f(q[0]), kv_new=f(kvn[0]), pos=pos, z_main=zm[0], c_main=cm[0],
+                                   scale=1 / np.sqrt(D))
+        assert (L.n_comp, L.swa_head, L.swa_len) == (ost.n_comp, ost.swa.head, ost.swa.length)
+        c_, s_, rp_, _ = oracle.mixed_kv_row(f(kvn[0]), ROPE)
+        np.testing.assert_array_equal(swa[0, slot].cpu().numpy(), record_of(c_, s_, rp_))
+        if pos % m == m - 1:  # the new entry within rounding, then adopt the GPU's record
+            _assert_entry_close(comp[0, nprev].cpu().numpy(), ost.comp_kv[nprev])
+            ost.comp_kv[nprev] = decode_records(comp[0, nprev].cpu().numpy())
+            ro, rl = oracle.sparse_attn(f(q[0]), np.concatenate([ost.comp_kv[:ost.n_comp], r["rows"][ost.n_comp:]]),
+                                        sink.astype(np.float64), 1 / np.sqrt(D))
+            ro = oracle.rope_rotate(ro, ost.rope_cos[pos], ost.rope_sin[pos], inverse=True)
+            r = {"out": ro, "lse": rl, "n_valid": ost.n_comp + ost.swa.length}
+        assert int(n_valid[0]) == r["n_valid"]
+        assert rel_err(host_f64(out[0]), r["out"]) <= 2e-2
+        assert np.abs(lse[0].cpu().numpy() - r["lse"]).max() <= 1e-2
