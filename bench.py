@@ -469,42 +469,72 @@ def time_hca(csa, reps: int):
     """HCA layers at 1M context (ratio 128, 7813 compressed entries after the
     step, window 128, 64 heads x 512): 30 independent layer caches, one
     csa_hca_decode_step each, captured in one graph and replayed `reps`
-    times.  Returns the mean per-layer time and its algorithmic bytes."""
+    times; then the same over mixed main KV (the caches packed once with
+    csa_pack_kv_mixed).  Returns the mean per-layer times and their
+    algorithmic bytes."""
+    import numpy as np
     import torch
     import synth
 
     shape = synth.SHAPES["hca1m"]
     xs = synth.make_decode_inputs_torch(shape, seed=None, device="cuda")
-    steps = []
-    for x in xs:
-        L = csa.make_layer_desc(comp_kv=x["comp_kv"], idx_keys=None, swa=x["swa"], main_bias=x["main_bias"],
-                                idx_bias=None, sink=x["sink"], n_comp=x["n_comp"], swa_head=x["swa_head"],
-                                swa_len=x["swa_len"], h=shape.h, h_i=0, m=shape.m, top_k=0)
-        out = torch.empty(1, shape.h, shape.d, dtype=torch.bfloat16, device="cuda")
-        io = csa.make_step_io(pos=x["pos"], q=x["q"], kv_new=x["kv_new"], z_main=x["z_main"], c_main=x["c_main"],
-                              out=out)
-        ws = torch.empty(csa.csa_hca_decode_step_workspace_size(L), dtype=torch.uint8, device="cuda")
-        steps.append((L, io, ws))
-    stream = torch.cuda.Stream()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(g, stream=stream):
-            for L, io, ws in steps:
-                csa.csa_hca_decode_step(L, io, ws, stream=stream)
-        g.replay()
-        stream.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
+
+    def replay(steps):
+        stream = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for L, io, ws in steps:
+                    csa.csa_hca_decode_step(L, io, ws, stream=stream)
             g.replay()
-        e1.record(stream)
-    stream.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (reps * len(steps))
+            stream.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        stream.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * len(steps))
+
+    def tables(rows, offset, base):
+        ang = (np.arange(rows)[:, None] + offset) * base ** (-2.0 * np.arange(32)[None, :] / 64)
+        return (torch.from_numpy(np.cos(ang).astype(np.float32)).cuda(),
+                torch.from_numpy(np.sin(ang).astype(np.float32)).cuda())
+
+    def layer_steps(mixed):
+        steps = []
+        rope = tables(shape.ctx + 8, 0.5, 10000.0) if mixed else None
+        comp_rope = tables(shape.max_comp + 1, 0.25, 500.0) if mixed else None
+        for x in xs:
+            comp, swa = x["comp_kv"], x["swa"]
+            if mixed:
+                comp = torch.empty(1, shape.max_comp, csa.MIX_REC_BYTES, dtype=torch.uint8, device="cuda")
+                swa = torch.empty(1, shape.w, csa.MIX_REC_BYTES, dtype=torch.uint8, device="cuda")
+                csa.csa_pack_kv_mixed(x["comp_kv"], comp)
+                csa.csa_pack_kv_mixed(x["swa"], swa)
+            L = csa.make_layer_desc(comp_kv=comp, idx_keys=None, swa=swa, main_bias=x["main_bias"],
+                                    idx_bias=None, sink=x["sink"], n_comp=x["n_comp"], swa_head=x["swa_head"],
+                                    swa_len=x["swa_len"], h=shape.h, h_i=0, m=shape.m, top_k=0, rope=rope,
+                                    comp_rope=comp_rope)
+            out = torch.empty(1, shape.h, shape.d, dtype=torch.bfloat16, device="cuda")
+            io = csa.make_step_io(pos=x["pos"], q=x["q"], kv_new=x["kv_new"], z_main=x["z_main"],
+                                  c_main=x["c_main"], out=out)
+            ws = torch.empty(csa.csa_hca_decode_step_workspace_size(L), dtype=torch.uint8, device="cuda")
+            steps.append((L, io, ws))
+        torch.cuda.synchronize()
+        return steps
+
+    us = replay(layer_steps(False))
+    torch.cuda.empty_cache()
+    us_mixed = replay(layer_steps(True))
     n, d, w, h, m = shape.n_comp, shape.d, shape.w, shape.h, shape.m
     # cache rows + window + q read, out written; the block's Z/C read and the entry written; the new row appended
     alg = (n + w) * d * 2 + h * d * 2 + h * d * 2 + 2 * m * d * 4 + d * 2 + 2 * d * 2
-    del steps, xs
+    # the same with 592-byte records for the rows, the entry and the appended row (kv_new read as bf16)
+    rec = csa.MIX_REC_BYTES
+    alg_mixed = (n + w) * rec + h * d * 2 + h * d * 2 + 2 * m * d * 4 + rec + d * 2 + rec
+    del xs
     torch.cuda.empty_cache()
     return {
         "workload": "hca1m: one decode token through 30 HCA layers (ratio 128, no indexer), context 1,000,064 "
@@ -515,6 +545,13 @@ def time_hca(csa, reps: int):
         "alg_bytes_per_layer": alg,
         "achieved_gbps": round(alg / (us * 1e-6) / 1e9, 1),
         "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "mixed_kv": {
+            "us_per_layer": round(us_mixed, 3),
+            "steps_per_s_30_layers": round(1e6 / (us_mixed * 30), 1),
+            "alg_bytes_per_layer": alg_mixed,
+            "achieved_gbps": round(alg_mixed / (us_mixed * 1e-6) / 1e9, 1),
+            "frac": round(alg_mixed / (us_mixed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        },
     }
 
 

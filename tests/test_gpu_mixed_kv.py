@@ -441,3 +441,50 @@ def test_hca_steps_in_sequence_mixed_kv(csa, case):
         assert int(n_valid[0]) == r["n_valid"]
         assert rel_err(host_f64(out[0]), r["out"]) <= 2e-2
         assert np.abs(lse[0].cpu().numpy() - r["lse"]).max() <= 1e-2
+
+
+def test_hca_step_full_size_mixed_kv(csa):
+    """One HCA layer at 1M context (ratio 128: 7812 entries + the one this
+    step completes, window 128 with wrap) over mixed caches packed on the
+    GPU: the entry's record within rounding, output and lse against the
+    oracle's attention over all 7941 decoded rows with the inverse rotation."""
+    shape = synth.SHAPES["hca1m"]
+    x = synth.make_decode_inputs_torch(shape, seed=None, device=DEV, layers=1)[0]
+    H, W, m = shape.h, shape.w, shape.m
+    comp = torch.empty(1, shape.max_comp, REC, dtype=torch.uint8, device=DEV)
+    swa = torch.empty(1, W, REC, dtype=torch.uint8, device=DEV)
+    csa.csa_pack_kv_mixed(x["comp_kv"], comp)
+    csa.csa_pack_kv_mixed(x["swa"], swa)
+    pos = x["pos"]
+    rc, rs = rope_tables(pos + 1)
+    cc, cs = rope_tables(shape.max_comp + 1, offset=0.25, base=500.0)
+    L = csa.make_layer_desc(comp_kv=comp, idx_keys=None, swa=swa, main_bias=x["main_bias"], idx_bias=None,
+                            sink=x["sink"], n_comp=x["n_comp"], swa_head=x["swa_head"], swa_len=x["swa_len"],
+                            h=H, h_i=0, m=m, top_k=0, rope=(dev_f32(rc), dev_f32(rs)),
+                            comp_rope=(dev_f32(cc), dev_f32(cs)))
+    out = torch.empty(1, H, 512, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(1, H, device=DEV)
+    n_valid = torch.empty(1, dtype=torch.int32, device=DEV)
+    io = csa.make_step_io(pos=pos, q=x["q"], kv_new=x["kv_new"], z_main=x["z_main"], c_main=x["c_main"], out=out,
+                          lse=lse, n_valid=n_valid)
+    ws = torch.empty(csa.csa_hca_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+    slot = x["swa_head"]
+    csa.csa_hca_decode_step(L, io, ws)
+    torch.cuda.synchronize()
+    N = x["n_comp"] + 1
+    assert N == shape.n_comp and pos % m == m - 1
+    ym = oracle.compress(host_f64(x["z_main"][0]), host_f64(x["c_main"][0]), host_f64(x["main_bias"]), m)[-1]
+    blk = pos // m
+    _, _, _, want = oracle.mixed_kv_row(ym, ROPE, cc[blk].astype(np.float64), cs[blk].astype(np.float64))
+    _assert_entry_close(comp[0, N - 1].cpu().numpy(), want)
+    c_, s_, rp_, _ = oracle.mixed_kv_row(host_f64(x["kv_new"][0]), ROPE)
+    np.testing.assert_array_equal(swa[0, slot].cpu().numpy(), record_of(c_, s_, rp_))
+    ring = swa[0].cpu().numpy()
+    head = (x["swa_head"] + 1) % W
+    rows = decode_records(np.concatenate([comp[0, :N].cpu().numpy(),
+                                          np.stack([ring[(head - W + j) % W] for j in range(W)])]))
+    assert int(n_valid[0]) == N + W
+    ro, rl = oracle.sparse_attn(host_f64(x["q"][0]), rows, host_f64(x["sink"]), 1 / np.sqrt(512))
+    ro = oracle.rope_rotate(ro, rc[pos].astype(np.float64), rs[pos].astype(np.float64), inverse=True)
+    assert rel_err(host_f64(out[0]), ro) <= 2e-2
+    assert np.abs(lse[0].cpu().numpy() - rl).max() <= 1e-2
