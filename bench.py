@@ -372,6 +372,21 @@ def time_prefill(csa, reps: int):
 
     topk_ms = timed(topk, reps)
     attn_ms = timed(attn, reps)
+    # the attention over mixed main-KV records (packed once, outside the timed region)
+    comp_rec = torch.empty(N, csa.MIX_REC_BYTES, dtype=torch.uint8, device="cuda")
+    win_rec = torch.empty(x["win_kv"].shape[0], csa.MIX_REC_BYTES, dtype=torch.uint8, device="cuda")
+    csa.csa_pack_kv_mixed(x["comp_kv"], comp_rec)
+    csa.csa_pack_kv_mixed(x["win_kv"], win_rec)
+    ang = (np.arange(x["pos0"] + T)[:, None] + 0.5) * 10000.0 ** (-2.0 * np.arange(32)[None, :] / 64)
+    rope = (torch.from_numpy(np.cos(ang).astype(np.float32)).cuda(),
+            torch.from_numpy(np.sin(ang).astype(np.float32)).cuda())
+
+    def attn_mixed():
+        csa.csa_prefill_attn_mixed(x["q"], comp_rec, idx, cnt, win_rec, W, x["pos0"], rope, x["sink"], scale, out,
+                                   lse=lse)
+
+    attn_mixed_ms = timed(attn_mixed, reps)
+    del comp_rec, win_rec, rope
     # the score kernel alone: the chunks' launches back to back in a graph
     rows = 256
     sc = torch.empty(1, rows, N, device="cuda")
@@ -447,6 +462,7 @@ def time_prefill(csa, reps: int):
             "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
         },
         "attn_tflops": round(attn_flop / (attn_ms * 1e-3) / 1e12, 1),
+        "mixed_kv_attn_ms": round(attn_mixed_ms, 4),
         "fp8_keys": {
             "index_topk_ms": round(topk8_ms, 4),
             "chunk_ms": round(topk8_ms + attn_ms, 4),

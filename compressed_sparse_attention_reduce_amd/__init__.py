@@ -31,6 +31,7 @@ from .binding import (  # noqa: F401
     csa_last_error,
     csa_layer_advance,
     csa_prefill_attn,
+    csa_prefill_attn_mixed,
     csa_quantize_fp8,
     csa_sparse_attn,
     csa_sparse_attn_workspace_size,

@@ -104,6 +104,8 @@ _SIGS = {
     "csa_index_topk_fp8": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _ll, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "csa_prefill_attn": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _ll, _vp, _f, _vp, _i, _vp, _i, _i, _i,
                               _vp]),
+    "csa_prefill_attn_mixed": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _ll, _vp, _vp, _i, _vp, _f, _vp, _i,
+                                    _vp, _i, _i, _vp]),
 }
 
 _lib = None
@@ -446,3 +448,22 @@ def csa_prefill_attn(q, comp_kv, idx, count, win_kv, window: int, pos0: int, sin
     _check(lib().csa_prefill_attn(_ptr(q), _ptr(comp_kv), n_comp, _ptr(idx), _ptr(count), idx.shape[1],
                                   _ptr(win_kv), window, pos0, _ptr(sink), scale, _ptr(out), _dt(out), _ptr(lse),
                                   t, h, d, _stream(stream)))
+
+
+def csa_prefill_attn_mixed(q, comp_rec, idx, count, win_rec, window: int, pos0: int, rope, sink, scale: float, out,
+                           lse=None, n_comp: Optional[int] = None, stream=None) -> None:
+    """csa_prefill_attn over mixed main-KV records: q [t, h, 512] bf16;
+    comp_rec [N, 592] and win_rec [t + window - 1, 592] uint8 records;
+    rope = (cos, sin) float32 [rows, 32] tables (out's RoPE dims rotated back
+    at each query's position); the rest as csa_prefill_attn."""
+    for t_, nm in ((q, "q"), (comp_rec, "comp_rec"), (idx, "idx"), (win_rec, "win_rec"), (out, "out")):
+        if not t_.is_contiguous():
+            raise ValueError(f"{nm}: must be contiguous")
+    cos, sin = rope
+    if cos.shape != sin.shape or cos.dim() != 2 or not (cos.is_contiguous() and sin.is_contiguous()):
+        raise ValueError("rope: two contiguous [rows, 32] tables")
+    t, h, _ = q.shape
+    n_comp = comp_rec.shape[0] if n_comp is None else n_comp
+    _check(lib().csa_prefill_attn_mixed(_ptr(q), _ptr(comp_rec), n_comp, _ptr(idx), _ptr(count), idx.shape[1],
+                                        _ptr(win_rec), window, pos0, _ptr(cos), _ptr(sin), cos.shape[0], _ptr(sink),
+                                        scale, _ptr(out), _dt(out), _ptr(lse), t, h, _stream(stream)))

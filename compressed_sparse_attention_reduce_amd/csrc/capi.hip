@@ -824,4 +824,26 @@ int csa_prefill_attn(const void* q, const void* comp_kv, int n_comp, const int* 
     return launched(csa::launch_prefill_attn(a, static_cast<hipStream_t>(stream)), "csa_prefill_attn");
 }
 
+int csa_prefill_attn_mixed(const void* q, const unsigned char* comp_rec, int n_comp, const int* idx, const int* count,
+                           int k, const unsigned char* win_rec, int window, long long pos0, const float* rope_cos,
+                           const float* rope_sin, int rope_rows, const float* sink, float scale, void* out,
+                           csa_dtype out_dtype, float* lse, int t, int h, csa_stream stream) {
+    CHECK(q && idx && win_rec && out && (comp_rec || n_comp == 0), "csa_prefill_attn_mixed: null pointer argument");
+    CHECK(rope_cos && rope_sin, "csa_prefill_attn_mixed: null RoPE table");
+    CHECK(t >= 1 && n_comp >= 0, "csa_prefill_attn_mixed: t %d n_comp %d", t, n_comp);
+    CHECK(k >= 1 && k <= csa::kTopkMaxK, "csa_prefill_attn_mixed: k=%d out of 1..%d", k, csa::kTopkMaxK);
+    CHECK(window >= 1 && pos0 >= 0, "csa_prefill_attn_mixed: window %d / pos0 %lld", window, pos0);
+    CHECK(pos0 + t <= rope_rows, "csa_prefill_attn_mixed: positions up to %lld outside the RoPE table (%d rows)",
+          pos0 + t - 1, rope_rows);
+    CHECK(out_dtype == CSA_F32 || out_dtype == CSA_BF16, "csa_prefill_attn_mixed: bad out_dtype %d", (int)out_dtype);
+    if (!csa::prefill_attn_supported(h, csa::kMixD))
+        return fail(CSA_ERR_UNSUPPORTED, "csa_prefill_attn_mixed: needs h a multiple of 16 up to 64 (got %d)", h);
+    CHECK(aligned16(q) && aligned16(win_rec) && aligned16(out) && (n_comp == 0 || aligned16(comp_rec)),
+          "csa_prefill_attn_mixed: q, comp_rec, win_rec and out must be 16-byte aligned");
+    csa::PrefillAttnArgs a{static_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(comp_rec), n_comp, idx,
+                           count, k, reinterpret_cast<const uint16_t*>(win_rec), window, pos0, sink, scale, out,
+                           out_dtype == CSA_BF16, lse, t, h, csa::kMixD, true, rope_cos, rope_sin};
+    return launched(csa::launch_prefill_attn(a, static_cast<hipStream_t>(stream)), "csa_prefill_attn_mixed");
+}
+
 }  // extern "C"

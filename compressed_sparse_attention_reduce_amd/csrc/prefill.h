@@ -59,6 +59,12 @@ struct PrefillAttnArgs {
     bool out_bf16;
     float* lse;               // [t][h] or nullptr
     int t, h, d;
+    // mixed main KV (d = 512): comp_kv and win_kv hold 592-byte records
+    // (mixed_kv.h), and out's RoPE dims are rotated back at each query's
+    // position with rows pos0 + r of the tables (kMixRope / 2 values a row)
+    bool kv_mixed;
+    const float* inv_cos;
+    const float* inv_sin;
 };
 bool prefill_attn_supported(int h, int d);
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s);

@@ -34,6 +34,7 @@
 // loaded into registers while the current one is computed.
 #include "common.h"
 #include "kernels.h"
+#include "mixed_kv.h"
 #include "prefill.h"
 #include "score_tile.h"
 
@@ -266,10 +267,14 @@ struct PaCfg {
                                                           static_cast<size_t>(D) * kVtPitch);
 };
 
-template <int D>
 // Two workgroups per CU: one's loads and barriers overlap the other's
 // matrix work (at D = 512 a few registers spill to scratch: measured 10%
 // faster than one workgroup per CU with 64-row chunks all the same).
+// kMixed (D = 512): the rows are mixed records; a NoPE item loads its 8 codes
+// and the row scale and is decoded to bfloat16 before the LDS stores, a RoPE
+// item is 16 bytes of the record's bf16 part, and the output's RoPE pairs are
+// rotated back at the query's position.
+template <int D, bool kMixed>
 __global__ __launch_bounds__(kPaThreads, 2) void k_prefill_attn(PrefillAttnArgs a) {
     using C = PaCfg<D>;
     constexpr int R = C::kRows;
@@ -289,7 +294,11 @@ __global__ __launch_bounds__(kPaThreads, 2) void k_prefill_attn(PrefillAttnArgs 
     if (a.n_comp <= 0) cnt = 0;
     const int nv = cnt + wl;
     const bool active = 16 * wv < a.h;
-    const uint16_t* win = a.win_kv + (static_cast<long long>(tq) + a.window - wl) * D;
+    // the token's first window row (element or record units)
+    const long long win_row0 = static_cast<long long>(tq) + a.window - wl;
+    const uint16_t* win = a.win_kv + win_row0 * D;
+    const uint8_t* comp_rec = reinterpret_cast<const uint8_t*>(a.comp_kv);
+    const uint8_t* win_rec = reinterpret_cast<const uint8_t*>(a.win_kv) + win_row0 * kMixRec;
 
     // this token's selected indices to LDS; the query tile's B operands
     const int* idx = a.idx + static_cast<long long>(tq) * a.k;
@@ -314,6 +323,8 @@ __global__ __launch_bounds__(kPaThreads, 2) void k_prefill_attn(PrefillAttnArgs 
     // probabilities are exactly 0 and their values finite, so they add
     // nothing, and every load is unconditional.
     const uint16_t* last_row = win + static_cast<long long>(wl - 1) * D;
+    const uint8_t* last_rec = win_rec + static_cast<long long>(wl - 1) * kMixRec;
+    constexpr int kNopeItems = kMixNope / 8;  // mixed: 16-byte output columns decoded from codes
     uint4 v[C::kIpt][4];
     auto load_chunk = [&](int j0) {
 #pragma unroll
@@ -324,9 +335,21 @@ __global__ __launch_bounds__(kPaThreads, 2) void k_prefill_attn(PrefillAttnArgs 
 #pragma unroll
             for (int u2 = 0; u2 < 4; ++u2) {
                 const int j = j0 + 4 * rg + u2;
-                const uint16_t* src = j < cnt ? a.comp_kv + static_cast<long long>(sidx[j]) * D
-                                              : (j < nv ? win + static_cast<long long>(j - cnt) * D : last_row);
-                v[u][u2] = *reinterpret_cast<const uint4*>(src + 8 * cc);
+                if constexpr (kMixed) {
+                    const uint8_t* src = j < cnt ? comp_rec + static_cast<long long>(sidx[j]) * kMixRec
+                                                 : (j < nv ? win_rec + static_cast<long long>(j - cnt) * kMixRec
+                                                           : last_rec);
+                    if (cc < kNopeItems) {  // 8 codes and the row scale, decoded at the LDS store
+                        const uint2 cw = *reinterpret_cast<const uint2*>(src + 8 * cc);
+                        v[u][u2] = make_uint4(cw.x, cw.y, *reinterpret_cast<const uint32_t*>(src + kMixScaleOff), 0u);
+                    } else {
+                        v[u][u2] = *reinterpret_cast<const uint4*>(src + kMixNope + 16 * (cc - kNopeItems));
+                    }
+                } else {
+                    const uint16_t* src = j < cnt ? a.comp_kv + static_cast<long long>(sidx[j]) * D
+                                                  : (j < nv ? win + static_cast<long long>(j - cnt) * D : last_row);
+                    v[u][u2] = *reinterpret_cast<const uint4*>(src + 8 * cc);
+                }
             }
         }
     };
@@ -337,6 +360,13 @@ __global__ __launch_bounds__(kPaThreads, 2) void k_prefill_attn(PrefillAttnArgs 
             if (C::kItems % kPaThreads != 0 && it >= C::kItems) continue;
             const int cc = it % (D / 8);
             const int rg = it / (D / 8);
+            if constexpr (kMixed) {
+                if (cc < kNopeItems) {
+#pragma unroll
+                    for (int u2 = 0; u2 < 4; ++u2)
+                        v[u][u2] = decode8_bf16(v[u][u2].x, v[u][u2].y, __uint_as_float(v[u][u2].z));
+                }
+            }
 #pragma unroll
             for (int u2 = 0; u2 < 4; ++u2)
                 *reinterpret_cast<uint4*>(kr + (4 * rg + u2) * C::kKrPitch + 8 * cc) = v[u][u2];
@@ -447,6 +477,18 @@ __global__ __launch_bounds__(kPaThreads, 2) void k_prefill_attn(PrefillAttnArgs 
     const float es = sk == -INFINITY ? 0.f : expf(sk - M);
     const float den = l_run * em + es;
     const float f = em / den;
+    if constexpr (kMixed) {  // columns 16 md + 4 lg + (0, 1) and (2, 3) are RoPE pairs past the NoPE part
+        const float* cs = a.inv_cos + p * (kMixRope / 2);
+        const float* sn = a.inv_sin + p * (kMixRope / 2);
+#pragma unroll
+        for (int md = kMixNope / 16; md < C::kMd; ++md) {
+            const int pr = (16 * md + 4 * lg - kMixNope) / 2;
+            float e0 = o[md][0], o0 = o[md][1], e1 = o[md][2], o1 = o[md][3];
+            rope_pair(e0, o0, cs[pr], sn[pr], true);
+            rope_pair(e1, o1, cs[pr + 1], sn[pr + 1], true);
+            o[md] = f32x4{e0, o0, e1, o1};
+        }
+    }
     const long long ob = (static_cast<long long>(tq) * a.h + hh) * D + 4 * lg;
     if (a.out_bf16) {
 #pragma unroll
@@ -469,7 +511,7 @@ size_t prefill_attn_lds(int k) {
     return PaCfg<D>::kLdsRows + sizeof(int) * static_cast<size_t>(k);
 }
 
-template <int D>
+template <int D, bool kMixed = false>
 hipError_t launch_prefill_attn_d(const PrefillAttnArgs& a, hipStream_t s) {
     const size_t lds = prefill_attn_lds<D>(a.k);
     if (lds > 64 * 1024) {
@@ -477,14 +519,14 @@ hipError_t launch_prefill_attn_d(const PrefillAttnArgs& a, hipStream_t s) {
         if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
         static size_t opted[64] = {};
         if (opted[dev] < lds) {
-            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<D>),
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill_attn<D, kMixed>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      static_cast<int>(prefill_attn_lds<D>(kTopkMaxK)));
             if (e != hipSuccess) return e;
             opted[dev] = prefill_attn_lds<D>(kTopkMaxK);
         }
     }
-    hipLaunchKernelGGL(k_prefill_attn<D>, dim3(a.t), dim3(kPaThreads), lds, s, a);
+    hipLaunchKernelGGL((k_prefill_attn<D, kMixed>), dim3(a.t), dim3(kPaThreads), lds, s, a);
     return hipGetLastError();
 }
 
@@ -586,6 +628,7 @@ bool prefill_attn_supported(int h, int d) {
 
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
     if (a.t <= 0) return hipSuccess;
+    if (a.kv_mixed) return a.d == kMixD ? launch_prefill_attn_d<kMixD, true>(a, s) : hipErrorInvalidValue;
     switch (a.d) {
         case 128: return launch_prefill_attn_d<128>(a, s);
         case 256: return launch_prefill_attn_d<256>(a, s);

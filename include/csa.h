@@ -493,6 +493,23 @@ int csa_prefill_attn(const void *q, const void *comp_kv, int n_comp, const int *
                      const float *sink, float scale, void *out, csa_dtype out_dtype, float *lse,
                      int t, int h, int d, csa_stream stream);
 
+/* csa_prefill_attn_mixed: csa_prefill_attn over mixed main KV (section 6c;
+ *   page 2, single_shot_inference.py, eager_attention, the storage-native
+ *   mixed gather, and its inverse RoPE on the output).  d = 512.
+ *   comp_rec: [n_comp][592] records; win_rec: [t + window - 1][592] records,
+ *   row i holding position pos0 - window + 1 + i; every row attended is the
+ *   record's decoded value (E4M3 code times the row scale, bf16 RoPE part).
+ *   rope_cos / rope_sin: float32 [rope_rows][32]; out's RoPE dims (the last
+ *   64, (even, odd) pairs) are rotated back by row pos0 + r for query row r,
+ *   so pos0 + t <= rope_rows.  Other arguments, limits and errors as
+ *   csa_prefill_attn (h a multiple of 16 up to 64); null tables or
+ *   misaligned records: CSA_ERR_INVALID_ARG.  No workspace. */
+int csa_prefill_attn_mixed(const void *q, const unsigned char *comp_rec, int n_comp, const int *idx,
+                           const int *count, int k, const unsigned char *win_rec, int window,
+                           long long pos0, const float *rope_cos, const float *rope_sin, int rope_rows,
+                           const float *sink, float scale, void *out, csa_dtype out_dtype, float *lse,
+                           int t, int h, csa_stream stream);
+
 /* ------------------------------------------------------------------------
  * 8. Calibration (not a step of the method).
  *

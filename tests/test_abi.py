@@ -180,6 +180,20 @@ def test_prefill_entry_points_reject_bad_args(csa):
     assert lib.csa_prefill_attn(*a) == B.CSA_ERR_INVALID_ARG
     a = list(attn); a[3] = None
     assert lib.csa_prefill_attn(*a) == B.CSA_ERR_INVALID_ARG
+    # over mixed records: d is 512; the RoPE tables must cover every query position
+    mixed = [FAKE, FAKE, 65536, FAKE, FAKE, 512, FAKE, 128, 260096, FAKE, FAKE, 262144, FAKE, 0.04, FAKE,
+             B.CSA_BF16, None, 2048, 64, None]
+    a = list(mixed); a[11] = 262143             # the last query's row missing
+    assert lib.csa_prefill_attn_mixed(*a) == B.CSA_ERR_INVALID_ARG
+    assert "RoPE" in csa.csa_last_error()
+    a = list(mixed); a[10] = None
+    assert lib.csa_prefill_attn_mixed(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(mixed); a[18] = 80                 # heads above 64
+    assert lib.csa_prefill_attn_mixed(*a) == B.CSA_ERR_UNSUPPORTED
+    a = list(mixed); a[1] = FAKE + 8            # misaligned records
+    assert lib.csa_prefill_attn_mixed(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(mixed); a[7] = 0
+    assert lib.csa_prefill_attn_mixed(*a) == B.CSA_ERR_INVALID_ARG
 
 
 def test_topk_rejects_bad_args_and_sizes_workspace(csa):

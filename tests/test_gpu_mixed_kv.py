@@ -488,3 +488,50 @@ def test_hca_step_full_size_mixed_kv(csa):
     ro = oracle.rope_rotate(ro, rc[pos].astype(np.float64), rs[pos].astype(np.float64), inverse=True)
     assert rel_err(host_f64(out[0]), ro) <= 2e-2
     assert np.abs(lse[0].cpu().numpy() - rl).max() <= 1e-2
+
+
+PREFILL_MIXED_CASES = [
+    # name, t, h, n_comp, k, window, pos0, sink, bf16 out, counts all k
+    ("h64_ragged_counts", 40, 64, 300, 64, 16, 700, True, True, False),
+    ("h32_f32_from_position0", 24, 32, 50, 40, 8, 0, False, False, True),
+    ("h64_k512_window128", 6, 64, 2000, 512, 128, 9000, True, True, True),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_MIXED_CASES, ids=[c[0] for c in PREFILL_MIXED_CASES])
+def test_prefill_attn_mixed_kv(csa, case):
+    """csa_prefill_attn_mixed against the oracle: per query row, the softmax
+    over the decoded records of its selected rows then its window rows, and
+    the inverse rotation of the RoPE dims at the row's position."""
+    name, t, h, n_comp, k, window, pos0, use_sink, out_bf16, full = case
+    g = _g(7601 + t + h + n_comp)
+    f = numfmt.bf16_bits_to_f64
+    qn = synth.to_bf16_bits(g.standard_normal((t, h, 512), dtype=np.float32))
+    comp_rec, comp_val = oracle_records(f(synth.to_bf16_bits(g.standard_normal((n_comp, 512), dtype=np.float32))))
+    win_rec, win_val = oracle_records(f(synth.to_bf16_bits(g.standard_normal((t + window - 1, 512),
+                                                                            dtype=np.float32))))
+    sink = g.standard_normal(h, dtype=np.float32) if use_sink else None
+    idx = np.stack([g.choice(n_comp, size=k, replace=False) for _ in range(t)]).astype(np.int32)
+    cnt = np.full(t, k, dtype=np.int32) if full else g.integers(0, k + 1, size=t).astype(np.int32)
+    for r in range(t):
+        idx[r, cnt[r]:] = -1
+    rc, rs = rope_tables(pos0 + t)
+    out = torch.full((t, h, 512), 7.0, dtype=torch.bfloat16 if out_bf16 else torch.float32, device=DEV)
+    lse = torch.empty(t, h, device=DEV)
+    scale = 1.0 / np.sqrt(512)
+    print(f"prefill mixed {name}", flush=True)
+    csa.csa_prefill_attn_mixed(dev_bf16(qn), torch.from_numpy(comp_rec).to(DEV), torch.from_numpy(idx).to(DEV),
+                               torch.from_numpy(cnt).to(DEV), torch.from_numpy(win_rec).to(DEV), window, pos0,
+                               (dev_f32(rc), dev_f32(rs)), None if sink is None else dev_f32(sink), scale, out,
+                               lse=lse)
+    torch.cuda.synchronize()
+    got, got_lse = host_f64(out), lse.cpu().numpy()
+    for r in range(t):
+        p = pos0 + r
+        first = max(0, p - window + 1)
+        wrows = [win_val[x - (pos0 - window + 1)] for x in range(first, p + 1)]
+        rows = np.stack([comp_val[i] for i in idx[r, :cnt[r]]] + wrows)
+        ro, rl = oracle.sparse_attn(f(qn[r]), rows, None if sink is None else sink.astype(np.float64), scale)
+        ro = oracle.rope_rotate(ro, rc[p].astype(np.float64), rs[p].astype(np.float64), inverse=True)
+        assert rel_err(got[r], ro) <= 2e-2, r
+        assert np.abs(got_lse[r] - rl).max() <= 1e-2, r
