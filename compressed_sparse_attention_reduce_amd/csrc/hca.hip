@@ -118,69 +118,65 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
         if (fold) fold_block(reinterpret_cast<float*>(smem));
         return;
     }
-    // 1. query group and the split's rows to LDS, all loads in one batch
+    // 1. the split's rows and the query group to LDS, all loads in one batch
     const uint16_t* qg = a.q + b * a.q_stride_b + static_cast<long long>(hg * kHeadGroup) * d;
     const uint16_t* comp = a.comp_kv + b * a.comp_kv_stride_b;
     const uint16_t* swa = a.swa + b * a.swa_stride_b;
     uint4 qv[kDenseQPer], v[kDenseRowPer];
-#pragma unroll
-    for (int u = 0; u < kDenseQPer; ++u) {
-        const int c = threadIdx.x + u * kDenseThreads;
-        qv[u] = c < kHeadGroup * cpr ? *reinterpret_cast<const uint4*>(qg + (c / cpr) * d + (c % cpr) * 8)
-                                     : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < kDenseRowPer; ++u) {
-        const int c = threadIdx.x + u * kDenseThreads;
-        const int r = c / cpr;
-        const int j = r0 + r;
-        if (a.kv_mixed) {  // records (d = 512): 8 codes + the scale, or 16 bytes of the RoPE part
-            const uint8_t* rec = nullptr;
-            if (c < kDenseRows * cpr && r < rows) {
-                if (j < cnt) {
-                    rec = reinterpret_cast<const uint8_t*>(a.comp_kv) + b * a.comp_kv_stride_b +
-                          static_cast<long long>(j) * kMixRec;
-                } else {
-                    int slot = (a.swa_head - a.swa_len + (j - cnt)) % a.w;
-                    if (slot < 0) slot += a.w;
-                    rec = reinterpret_cast<const uint8_t*>(a.swa) + b * a.swa_stride_b +
-                          static_cast<long long>(slot) * kMixRec;
-                }
-            }
-            const int cc = c % cpr;
-            if (!rec) {
-                v[u] = make_uint4(0, 0, 0, 0);
-            } else if (cc < kMixNope / 8) {
-                const uint2 cw = *reinterpret_cast<const uint2*>(rec + 8 * cc);
-                v[u] = make_uint4(cw.x, cw.y, __float_as_uint(*reinterpret_cast<const float*>(rec + kMixScaleOff)), 1u);
-            } else {
-                v[u] = *reinterpret_cast<const uint4*>(rec + kMixNope + 16 * (cc - kMixNope / 8));
-            }
-            continue;
-        }
-        const uint16_t* src = nullptr;
-        if (c < kDenseRows * cpr && r < rows) {
-            if (j < cnt) {
-                src = comp + static_cast<long long>(j) * d;
-            } else {
-                int slot = (a.swa_head - a.swa_len + (j - cnt)) % a.w;
-                if (slot < 0) slot += a.w;
-                src = swa + static_cast<long long>(slot) * d;
-            }
-        }
-        v[u] = src ? *reinterpret_cast<const uint4*>(src + (c % cpr) * 8) : make_uint4(0, 0, 0, 0);
-    }
-    if (a.kv_mixed) {  // decode the NoPE pieces (w = 1 marks a loaded one)
+    float vsc[kDenseRowPer];  // mixed: the row scale of each piece
+    if (a.kv_mixed) {  // records (d = 512): one 16-byte read and the row scale per piece, no branch on the
+                       // piece kind; pieces past the split's rows read its first row (rows >= 1)
 #pragma unroll
         for (int u = 0; u < kDenseRowPer; ++u) {
             const int c = threadIdx.x + u * kDenseThreads;
-            if ((c % cpr) < kMixNope / 8 && v[u].w == 1u) v[u] = decode8_bf16(v[u].x, v[u].y, __uint_as_float(v[u].z));
+            const int r = c / cpr;
+            const int jj = (c < kDenseRows * cpr && r < rows) ? r0 + r : r0;
+            int slot = (a.swa_head - a.swa_len + (jj - cnt)) % a.w;
+            if (slot < 0) slot += a.w;
+            const uint8_t* rec = jj < cnt ? reinterpret_cast<const uint8_t*>(a.comp_kv) + b * a.comp_kv_stride_b +
+                                                static_cast<long long>(jj) * kMixRec
+                                          : reinterpret_cast<const uint8_t*>(a.swa) + b * a.swa_stride_b +
+                                                static_cast<long long>(slot) * kMixRec;
+            v[u] = mixed_piece_load(mixed_piece_ptr(rec, c % cpr));
+            vsc[u] = *reinterpret_cast<const float*>(rec + kMixScaleOff);
         }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kDenseRowPer; ++u) {
+            const int c = threadIdx.x + u * kDenseThreads;
+            const int r = c / cpr;
+            const int j = r0 + r;
+            const uint16_t* src = nullptr;
+            if (c < kDenseRows * cpr && r < rows) {
+                if (j < cnt) {
+                    src = comp + static_cast<long long>(j) * d;
+                } else {
+                    int slot = (a.swa_head - a.swa_len + (j - cnt)) % a.w;
+                    if (slot < 0) slot += a.w;
+                    src = swa + static_cast<long long>(slot) * d;
+                }
+            }
+            v[u] = src ? *reinterpret_cast<const uint4*>(src + (c % cpr) * 8) : make_uint4(0, 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kDenseQPer; ++u) {  // the query group after the rows (used only at the LDS staging)
+        const int c = threadIdx.x + u * kDenseThreads;
+        qv[u] = c < kHeadGroup * cpr ? *reinterpret_cast<const uint4*>(qg + (c / cpr) * d + (c % cpr) * 8)
+                                     : make_uint4(0, 0, 0, 0);
     }
     // the block's channels while the rows are in flight (LDS as scratch first)
     if (fold) {
         fold_block(reinterpret_cast<float*>(smem));
         __syncthreads();
+    }
+    if (a.kv_mixed) {  // decode the pieces (the first use of the loaded bytes); rows past the split's are zero
+#pragma unroll
+        for (int u = 0; u < kDenseRowPer; ++u) {
+            const int c = threadIdx.x + u * kDenseThreads;
+            v[u] = (c < kDenseRows * cpr && c / cpr < rows) ? mixed_piece_value(v[u], vsc[u], c % cpr)
+                                                            : make_uint4(0, 0, 0, 0);
+        }
     }
 #pragma unroll
     for (int u = 0; u < kDenseQPer; ++u) {

@@ -73,6 +73,24 @@ __device__ inline void wave_pack_mixed(Get get, uint8_t* rec, const float* cos, 
 // (nearest even) in a 16-byte piece: v_cvt_pk_f32_fp8 decodes two codes
 // exactly (gfx950 reads OCP E4M3), one float32 multiply each, and
 // v_cvt_pk_bf16_f32 rounds a pair.
+// Loaders read a 16-byte output piece cc of a record in two steps, so that
+// every piece's loads are issued before any of them is used (a load whose
+// result is chosen between branches makes the compiler wait for it at the
+// join): mixed_piece_ptr gives the bytes to read without branching on the
+// piece kind (piece cc < kMixNope / 8: its 8 codes, read as the 16 bytes at
+// 8 * cc, which the record holds; otherwise 16 bytes of the RoPE part), and
+// after the loads mixed_piece_value turns them and the row scale into 8
+// bfloat16 values.
+__device__ __forceinline__ const uint8_t* mixed_piece_ptr(const uint8_t* rec, int cc) {
+    const bool code = cc < kMixNope / 8;
+    return rec + (code ? 8 * cc : kMixNope + 16 * (cc - kMixNope / 8));
+}
+__device__ __forceinline__ uint4 mixed_piece_load(const uint8_t* p) {  // p: 8-byte aligned
+    uint4 v;
+    __builtin_memcpy(&v, __builtin_assume_aligned(p, 8), sizeof(v));
+    return v;
+}
+
 __device__ __forceinline__ uint4 decode8_bf16(uint32_t lo, uint32_t hi, float scale) {
     auto pack = [scale](decltype(__builtin_amdgcn_cvt_pk_f32_fp8(0, false)) f) -> uint32_t {
         const __bf16 a = static_cast<__bf16>(f[0] * scale);
@@ -84,6 +102,10 @@ __device__ __forceinline__ uint4 decode8_bf16(uint32_t lo, uint32_t hi, float sc
                       pack(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), true)),
                       pack(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), false)),
                       pack(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), true)));
+}
+
+__device__ __forceinline__ uint4 mixed_piece_value(const uint4& raw, float scale, int cc) {
+    return cc < kMixNope / 8 ? decode8_bf16(raw.x, raw.y, scale) : raw;
 }
 
 }  // namespace
