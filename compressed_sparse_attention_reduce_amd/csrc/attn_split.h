@@ -117,37 +117,28 @@ __device__ inline void attn_split(const AttnArgs& a, int n_splits, int split, in
     //    gather_buf); query -> LDS
     uint4 v[G::kChunks];
     if (a.kv_mixed) {
-        // mixed records (d = 512): chunk cc < 56 is 8 codes (+ the row scale),
-        // decoded to bfloat16; chunk cc >= 56 is 16 bytes of the RoPE part
+        // mixed records (d = 512): one 16-byte read and the row scale per chunk, with no branch on the
+        // chunk kind (a load chosen between branches makes the compiler wait for it at the join);
+        // chunks past the split's rows read the ring's first record.  Chunk cc < 56 decodes 8 codes
+        // to bfloat16, chunk cc >= 56 is 16 bytes of the RoPE part.
         constexpr int kNopeChunks = kMixNope / 8;
         const uint8_t* cbase = reinterpret_cast<const uint8_t*>(a.comp_kv) + b * a.comp_kv_stride_b;
         const uint8_t* sbase = reinterpret_cast<const uint8_t*>(a.swa) + b * a.swa_stride_b;
+        float vsc[G::kChunks];
 #pragma unroll
         for (int u = 0; u < G::kChunks; ++u) {
             const int c = u * NT + threadIdx.x;
             const int r = c / cpr;
             const int j = r0 + r;
-            const int cc = c % cpr;
-            const uint8_t* rec = nullptr;
-            if (c < n_chunks && r < rows) {
-                if (j < cnt) {
-                    const int ri = my_idx[u] < 0 ? 0 : (my_idx[u] >= a.n_comp ? a.n_comp - 1 : my_idx[u]);
-                    rec = cbase + static_cast<long long>(ri) * kMixRec;
-                } else {
-                    int slot = (a.swa_head - a.swa_len + (j - cnt)) % a.w;
-                    if (slot < 0) slot += a.w;
-                    rec = sbase + static_cast<long long>(slot) * kMixRec;
-                }
-            }
-            if (!rec) {
-                v[u] = make_uint4(0, 0, 0, 0);
-            } else if (cc < kNopeChunks) {
-                const uint2 cw = *reinterpret_cast<const uint2*>(rec + 8 * cc);
-                const float sc = *reinterpret_cast<const float*>(rec + kMixScaleOff);
-                v[u] = make_uint4(cw.x, cw.y, __float_as_uint(sc), 0u);
-            } else {
-                v[u] = *reinterpret_cast<const uint4*>(rec + kMixNope + 16 * (cc - kNopeChunks));
-            }
+            const bool live = c < n_chunks && r < rows;
+            int slot = (a.swa_head - a.swa_len + (j - cnt)) % a.w;
+            if (slot < 0) slot += a.w;
+            const int ri = my_idx[u] < 0 ? 0 : (my_idx[u] >= a.n_comp ? a.n_comp - 1 : my_idx[u]);
+            const uint8_t* rec = !live ? sbase
+                                       : (j < cnt ? cbase + static_cast<long long>(ri) * kMixRec
+                                                  : sbase + static_cast<long long>(slot) * kMixRec);
+            v[u] = mixed_piece_load(mixed_piece_ptr(rec, c % cpr));
+            vsc[u] = *reinterpret_cast<const float*>(rec + kMixScaleOff);
         }
         const bool write_rec = a.idx && a.gather_buf && hg == 0;
         uint8_t* gbase = reinterpret_cast<uint8_t*>(a.gather_buf) + b * a.buf_stride_b;
@@ -156,16 +147,17 @@ __device__ inline void attn_split(const AttnArgs& a, int n_splits, int split, in
             const int c = u * NT + threadIdx.x;
             const int r = c / cpr;
             const int cc = c % cpr;
-            if (c < n_chunks && r < rows && write_rec) {  // the record's own bytes to gather_buf
+            const bool live = c < n_chunks && r < rows;
+            if (live && write_rec) {  // the record's own bytes to gather_buf
                 uint8_t* out = gbase + static_cast<long long>(r0 + r) * kMixRec;
                 if (cc < kNopeChunks) {
                     *reinterpret_cast<uint2*>(out + 8 * cc) = make_uint2(v[u].x, v[u].y);
-                    if (cc == 0) *reinterpret_cast<uint4*>(out + kMixScaleOff) = make_uint4(v[u].z, 0u, 0u, 0u);
+                    if (cc == 0) *reinterpret_cast<uint4*>(out + kMixScaleOff) = make_uint4(__float_as_uint(vsc[u]), 0u, 0u, 0u);
                 } else {
                     *reinterpret_cast<uint4*>(out + kMixNope + 16 * (cc - kNopeChunks)) = v[u];
                 }
             }
-            if (c < n_chunks && cc < kNopeChunks) v[u] = decode8_bf16(v[u].x, v[u].y, __uint_as_float(v[u].z));
+            v[u] = live ? mixed_piece_value(v[u], vsc[u], cc) : make_uint4(0, 0, 0, 0);
         }
     } else {
 #pragma unroll

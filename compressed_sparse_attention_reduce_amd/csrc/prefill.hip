@@ -270,7 +270,7 @@ struct PaCfg {
 // Two workgroups per CU: one's loads and barriers overlap the other's
 // matrix work (at D = 512 a few registers spill to scratch: measured 10%
 // faster than one workgroup per CU with 64-row chunks all the same).
-// kMixed (D = 512): the rows are mixed records; a NoPE item loads its 8 codes
+// kMixed (D = 512): the rows are mixed records; a NoPE item reads its 8 codes
 // and the row scale and is decoded to bfloat16 before the LDS stores, a RoPE
 // item is 16 bytes of the record's bf16 part, and the output's RoPE pairs are
 // rotated back at the query's position.
@@ -324,8 +324,8 @@ __global__ __launch_bounds__(kPaThreads, 2) void k_prefill_attn(PrefillAttnArgs 
     // nothing, and every load is unconditional.
     const uint16_t* last_row = win + static_cast<long long>(wl - 1) * D;
     const uint8_t* last_rec = win_rec + static_cast<long long>(wl - 1) * kMixRec;
-    constexpr int kNopeItems = kMixNope / 8;  // mixed: 16-byte output columns decoded from codes
     uint4 v[C::kIpt][4];
+    float vsc[C::kIpt][4];  // mixed: the row scale of each item (unused otherwise)
     auto load_chunk = [&](int j0) {
 #pragma unroll
         for (int u = 0; u < C::kIpt; ++u) {
@@ -339,12 +339,10 @@ __global__ __launch_bounds__(kPaThreads, 2) void k_prefill_attn(PrefillAttnArgs 
                     const uint8_t* src = j < cnt ? comp_rec + static_cast<long long>(sidx[j]) * kMixRec
                                                  : (j < nv ? win_rec + static_cast<long long>(j - cnt) * kMixRec
                                                            : last_rec);
-                    if (cc < kNopeItems) {  // 8 codes and the row scale, decoded at the LDS store
-                        const uint2 cw = *reinterpret_cast<const uint2*>(src + 8 * cc);
-                        v[u][u2] = make_uint4(cw.x, cw.y, *reinterpret_cast<const uint32_t*>(src + kMixScaleOff), 0u);
-                    } else {
-                        v[u][u2] = *reinterpret_cast<const uint4*>(src + kMixNope + 16 * (cc - kNopeItems));
-                    }
+                    // one 16-byte read (8 codes, or 16 bytes of the RoPE part) and the row scale, with
+                    // no branch on the item kind; decoded at the LDS store
+                    v[u][u2] = mixed_piece_load(mixed_piece_ptr(src, cc));
+                    vsc[u][u2] = *reinterpret_cast<const float*>(src + kMixScaleOff);
                 } else {
                     const uint16_t* src = j < cnt ? a.comp_kv + static_cast<long long>(sidx[j]) * D
                                                   : (j < nv ? win + static_cast<long long>(j - cnt) * D : last_row);
@@ -361,11 +359,8 @@ __global__ __launch_bounds__(kPaThreads, 2) void k_prefill_attn(PrefillAttnArgs 
             const int cc = it % (D / 8);
             const int rg = it / (D / 8);
             if constexpr (kMixed) {
-                if (cc < kNopeItems) {
 #pragma unroll
-                    for (int u2 = 0; u2 < 4; ++u2)
-                        v[u][u2] = decode8_bf16(v[u][u2].x, v[u][u2].y, __uint_as_float(v[u][u2].z));
-                }
+                for (int u2 = 0; u2 < 4; ++u2) v[u][u2] = mixed_piece_value(v[u][u2], vsc[u][u2], cc);
             }
 #pragma unroll
             for (int u2 = 0; u2 < 4; ++u2)
