@@ -571,6 +571,52 @@ def time_hca(csa, reps: int):
     }
 
 
+def time_batch128k(csa, reps: int, n_caches: int = 8):
+    """Batched decode at 128K context: 8 independent sequences (n_comp 32768
+    each) through one csa_decode_step per layer, over `n_caches` independent
+    layer caches (about 336 MB each, so successive layers read from HBM, not
+    the 256 MB last-level cache), captured in one graph and replayed `reps`
+    times.  Returns the mean time per layer step (all 8 sequences) and its
+    algorithmic bytes."""
+    import torch
+    import synth
+
+    shape = synth.with_(synth.SHAPES["batch128k"], layers=n_caches)
+    layers = build_layers(csa, shape, torch.device("cuda:0"))
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        for ly in layers:  # eager once, then capture
+            csa.csa_decode_step(ly["L"], ly["io"], ly["ws"], stream=stream)
+        with torch.cuda.graph(g, stream=stream):
+            for ly in layers:
+                csa.csa_decode_step(ly["L"], ly["io"], ly["ws"], stream=stream)
+        g.replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    stream.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(layers))
+    alg = algorithmic_bytes(shape)["per_layer"] * shape.batch
+    del layers
+    torch.cuda.empty_cache()
+    return {
+        "workload": "batch128k: 8 independent sequences at context 131,072 (n_comp 32,768 each, SWA 128), one "
+                    "decode token each through one CSA layer; indexer 64x128 bf16, top_k 512, main attention "
+                    f"64 heads x 512 bf16 with sink; {n_caches} independent layer caches replayed in turn",
+        "us_per_layer_step": round(us, 3),
+        "layer_steps_per_s": round(1e6 / us, 1),
+        "sequence_tokens_per_s_per_layer": round(shape.batch * 1e6 / us, 1),
+        "alg_bytes_per_layer_step": alg,
+        "achieved_gbps": round(alg / (us * 1e-6) / 1e9, 1),
+        "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
 def cpu_baseline(layers, shape, budget_s: float):
     """The float64 oracle on the host, layer by layer, until the budget is spent."""
     import numpy as np
@@ -708,6 +754,7 @@ def main() -> int:
     torch.cuda.empty_cache()
     prefill = time_prefill(csa, max(2, args.scan_reps // 2))
     hca = time_hca(csa, args.scan_reps)
+    batch = time_batch128k(csa, max(10, args.steps // 4))
 
     res = {
         "metric": "CSA decode steps/s and indexer-scan HBM GB/s at 1M ctx (250K comp entries)",
@@ -774,6 +821,7 @@ def main() -> int:
         },
         "prefill": prefill,
         "hca": hca,
+        "batch128k": batch,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -241,6 +241,8 @@ hipError_t launch_attn_dense_bf16(AttnArgs a, const PrepArgs& prep, const void* 
 // workgroup selects the top k itself (from cands when given, else the
 // exact path over the scores), then attends; topk idx / count written too.
 hipError_t launch_topk_attn(const TopkArgs& t, const CandArgs* cands, AttnArgs a, hipStream_t s);
+// workgroups launch_topk_attn starts (one 1024-thread workgroup per compute unit fits)
+int topk_attn_workgroups(int batch, int h, int n_max);
 hipError_t launch_attn_f32(const void* q, const void* kv, const int* n_valid, const float* sink,
                            float scale, void* out, bool out_bf16, float* lse, int batch, int h,
                            int d, int n_max, long long q_stride_b, long long kv_stride_b,

@@ -60,6 +60,8 @@ static_assert(sizeof(FinalSmem) >= sizeof(uint16_t) * ((kR + kHeadGroup) * (512 
 
 }  // namespace
 
+int topk_attn_workgroups(int batch, int h, int n_max) { return attn_splits(n_max) * (h / kHeadGroup) * batch; }
+
 hipError_t launch_topk_attn(const TopkArgs& ta, const CandArgs* cands, AttnArgs a, hipStream_t s) {
     if (ta.t != 1 || a.d > 512 || a.batch != ta.batch) return hipErrorInvalidValue;
     int dev = 0;
