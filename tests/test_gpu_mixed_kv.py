@@ -291,11 +291,13 @@ def test_decode_step_ctx1m_mixed_kv_full_size(csa):
     assert np.abs(outs["lse"][0].cpu().numpy() - rl).max() <= 1e-2
 
 
-def test_decode_step_mixed_kv_fp8_keys_batched(csa):
-    """Three sequences, E4M3 indexer keys and mixed main KV together, a step
+@pytest.mark.parametrize("B", [3, 5])
+def test_decode_step_mixed_kv_fp8_keys_batched(csa, B):
+    """Several sequences, E4M3 indexer keys and mixed main KV together, a step
     that completes a block: each sequence's new records, scores, selection,
-    gather_buf and output against the oracle."""
-    B = 3
+    gather_buf and output against the oracle.  Three sequences take the fused
+    top-k + attention (240 workgroups fit one round of 256 compute units);
+    five take one top-k launch per sequence and the separate attention."""
     shape = synth.with_(synth.SHAPES["ctx8k"], batch=B, ctx=4000, n_comp=999)
     x = synth.make_decode_inputs(shape, 7401, max_comp=1000)
     g = _g(7402)
