@@ -522,11 +522,11 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
                      io->topk_count, tws};
     // bf16 with candidate lists (or a short row): every attention workgroup
     // selects the top k itself, no separate top-k launch, as long as those
-    // workgroups run in one round (one per compute unit); a larger batch
+    // workgroups are all resident at once (one per compute unit); a larger batch
     // selects once per sequence and attends with smaller workgroups.  The
     // device-counter step always fuses (its top-k length is on the device).
-    const bool one_round = csa::topk_attn_workgroups(L->batch, L->h, n_max) <= csa::device_cu_count();
-    const bool fuse = bf && (dev || ((ca.lists || N <= kFuseExactMaxN) && one_round));
+    const bool all_resident = csa::topk_attn_workgroups(L->batch, L->h, n_max) <= csa::device_cu_count();
+    const bool fuse = bf && (dev || ((ca.lists || N <= kFuseExactMaxN) && all_resident));
     if (!fuse) {
         e = csa::launch_topk(ta, ca.lists ? &ca : nullptr, s);
         if (e != hipSuccess) return launched(e, "csa_decode_step/topk");

@@ -296,7 +296,7 @@ def test_decode_step_mixed_kv_fp8_keys_batched(csa, B):
     """Several sequences, E4M3 indexer keys and mixed main KV together, a step
     that completes a block: each sequence's new records, scores, selection,
     gather_buf and output against the oracle.  Three sequences take the fused
-    top-k + attention (240 workgroups fit one round of 256 compute units);
+    top-k + attention (240 workgroups, all resident on 256 compute units);
     five take one top-k launch per sequence and the separate attention."""
     shape = synth.with_(synth.SHAPES["ctx8k"], batch=B, ctx=4000, n_comp=999)
     x = synth.make_decode_inputs(shape, 7401, max_comp=1000)

@@ -529,7 +529,7 @@ STEP_CASES = [
     ("overlap_bf16", synth.with_(synth.SHAPES["ctx8k"], ctx=4000, n_comp=1000, overlap=True), 2005, None),
     ("k_covers_all", synth.with_(synth.SHAPES["ctx8k"], ctx=800, n_comp=200), 2006, 256),
     ("tiny_f32_batch3", synth.with_(synth.SHAPES["tiny"], batch=3), 1002, None),
-    # 5 x 80 fused workgroups would not fit one round of the chip: one top-k launch per
+    # 5 x 80 fused workgroups would not all be resident at once: one top-k launch per
     # sequence and the separate attention, with the scan's candidate lists (n_comp 4000)
     # and without them (n_comp 1000 <= 4 top_k)
     ("bf16_batch5_lists", synth.with_(synth.SHAPES["ctx8k"], batch=5, ctx=16000, n_comp=3999), 2007, None),
