@@ -73,6 +73,19 @@ __device__ inline void wave_pack_mixed(Get get, uint8_t* rec, const float* cos, 
 // (nearest even) in a 16-byte piece: v_cvt_pk_f32_fp8 decodes two codes
 // exactly (gfx950 reads OCP E4M3), one float32 multiply each, and
 // v_cvt_pk_bf16_f32 rounds a pair.
+__device__ __forceinline__ uint4 decode8_bf16(uint32_t lo, uint32_t hi, float scale) {
+    auto pack = [scale](decltype(__builtin_amdgcn_cvt_pk_f32_fp8(0, false)) f) -> uint32_t {
+        const __bf16 a = static_cast<__bf16>(f[0] * scale);
+        const __bf16 b = static_cast<__bf16>(f[1] * scale);
+        return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+    };
+    return make_uint4(pack(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), false)),
+                      pack(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), true)),
+                      pack(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), false)),
+                      pack(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), true)));
+}
+
 // Loaders read a 16-byte output piece cc of a record in two steps, so that
 // every piece's loads are issued before any of them is used (a load whose
 // result is chosen between branches makes the compiler wait for it at the
@@ -89,19 +102,6 @@ __device__ __forceinline__ uint4 mixed_piece_load(const uint8_t* p) {  // p: 8-b
     uint4 v;
     __builtin_memcpy(&v, __builtin_assume_aligned(p, 8), sizeof(v));
     return v;
-}
-
-__device__ __forceinline__ uint4 decode8_bf16(uint32_t lo, uint32_t hi, float scale) {
-    auto pack = [scale](decltype(__builtin_amdgcn_cvt_pk_f32_fp8(0, false)) f) -> uint32_t {
-        const __bf16 a = static_cast<__bf16>(f[0] * scale);
-        const __bf16 b = static_cast<__bf16>(f[1] * scale);
-        return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
-    };
-    return make_uint4(pack(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), false)),
-                      pack(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), true)),
-                      pack(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), false)),
-                      pack(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), true)));
 }
 
 __device__ __forceinline__ uint4 mixed_piece_value(const uint4& raw, float scale, int cc) {
