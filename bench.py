@@ -180,15 +180,17 @@ def time_fp8(csa, layers, shape, reps: int, steps: int):
         kc = torch.zeros(1, shape.max_comp, 128, dtype=torch.uint8, device="cuda")
         ks = torch.zeros(1, shape.max_comp, dtype=torch.float32, device="cuda")
         csa.csa_quantize_fp8(x["idx_keys"][:, :n].contiguous(), kc[:, :n], ks[:, :n])
+        # the standalone scan takes query codes with the scales folded into w
+        # (the library's query quantiser); the decode step quantises the bf16
+        # query itself, inside its timed region
         qc = torch.empty(1, 64, 128, dtype=torch.uint8, device="cuda")
-        qs = torch.empty(1, 64, dtype=torch.float32, device="cuda")
-        csa.csa_quantize_fp8(x["q_idx"].contiguous(), qc, qs)
-        w8 = (x["w_idx"] * qs).contiguous()
+        w8 = torch.empty(1, 64, dtype=torch.float32, device="cuda")
+        csa.csa_quantize_query_fp8(x["q_idx"].contiguous(), x["w_idx"].contiguous(), qc, w8)
         L = csa.make_layer_desc(comp_kv=x["comp_kv"], idx_keys=kc, idx_scales=ks, swa=x["swa"],
                                 main_bias=x["main_bias"], idx_bias=x["idx_bias"], sink=x["sink"],
                                 n_comp=x["n_comp"], swa_head=x["swa_head"], swa_len=x["swa_len"],
                                 h=shape.h, h_i=shape.h_i, m=shape.m, top_k=shape.top_k)
-        io = csa.make_step_io(pos=x["pos"], q=x["q"], q_idx=qc, w_idx=w8, kv_new=x["kv_new"],
+        io = csa.make_step_io(pos=x["pos"], q=x["q"], q_idx=x["q_idx"], w_idx=x["w_idx"], kv_new=x["kv_new"],
                               z_main=x["z_main"], c_main=x["c_main"], z_idx=x["z_idx"], c_idx=x["c_idx"],
                               **ly["outs"])
         fl.append({"L": L, "io": io, "ws": ly["ws"], "qc": qc, "w8": w8, "kc": kc, "ks": ks, "outs": ly["outs"]})
@@ -419,12 +421,11 @@ def time_prefill(csa, reps: int):
     ks = torch.empty(N, dtype=torch.float32, device="cuda")
     csa.csa_quantize_fp8(x["idx_keys"], kc, ks)
     qc = torch.empty(T, 64, 128, dtype=torch.uint8, device="cuda")
-    qs = torch.empty(T, 64, dtype=torch.float32, device="cuda")
-    csa.csa_quantize_fp8(x["q_idx"], qc, qs)
-    w8 = (x["w_idx"] * qs).contiguous()
+    w8 = torch.empty(T, 64, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
 
-    def topk8():
+    def topk8():  # the chunk's queries quantised (scales folded into w), then score + top-k
+        csa.csa_quantize_query_fp8(x["q_idx"], x["w_idx"], qc, w8)
         csa.csa_index_topk_fp8(qc, w8, kc, ks, idx, cnt, ws, pos0=x["pos0"])
 
     topk8_ms = timed(topk8, reps)

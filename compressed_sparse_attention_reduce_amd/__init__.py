@@ -33,6 +33,7 @@ from .binding import (  # noqa: F401
     csa_prefill_attn,
     csa_prefill_attn_mixed,
     csa_quantize_fp8,
+    csa_quantize_query_fp8,
     csa_sparse_attn,
     csa_sparse_attn_workspace_size,
     csa_topk,

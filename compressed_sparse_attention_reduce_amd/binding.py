@@ -81,6 +81,7 @@ _SIGS = {
     "csa_index_score": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _ll, _ll, _ll,
                              _ll, _ll, _vp]),
     "csa_quantize_fp8": (_i, [_vp, _i, _vp, _vp, _ll, _i, _vp]),
+    "csa_quantize_query_fp8": (_i, [_vp, _i, _vp, _vp, _vp, _ll, _i, _i, _vp]),
     "csa_pack_kv_mixed": (_i, [_vp, _i, _vp, _ll, _i, _i, _vp]),
     "csa_read_probe": (_i, [_vp, _ll, _vp, _vp]),
     "csa_index_score_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _ll, _ll, _ll,
@@ -199,6 +200,23 @@ def csa_quantize_fp8(x, codes, scales, stream=None) -> None:
     if codes.shape != x.shape or scales.numel() != rows:
         raise ValueError("codes must match x and scales hold one value per row")
     _check(lib().csa_quantize_fp8(_ptr(x), _dt(x), _ptr(codes), _ptr(scales), rows, d, _stream(stream)))
+
+
+def csa_quantize_query_fp8(q, w, q_codes, w_folded, stream=None) -> None:
+    """q [..., h, d] float32 / bfloat16 and w [..., h] float32 (contiguous) ->
+    q_codes [..., h, d] uint8 E4M3 and w_folded [..., h] float32 (w times each
+    head row's scale)."""
+    for t_, nm in ((q, "q"), (w, "w"), (q_codes, "q_codes"), (w_folded, "w_folded")):
+        if not t_.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if q_codes.dtype != torch.uint8 or w.dtype != torch.float32 or w_folded.dtype != torch.float32:
+        raise TypeError("q_codes must be uint8, w and w_folded float32")
+    h, d = q.shape[-2], q.shape[-1]
+    rows = q.numel() // (h * d) if h * d else 0
+    if q_codes.shape != q.shape or w.shape != q.shape[:-1] or w_folded.shape != w.shape:
+        raise ValueError("q_codes must match q, w and w_folded be q's shape without d")
+    _check(lib().csa_quantize_query_fp8(_ptr(q), _dt(q), _ptr(w), _ptr(q_codes), _ptr(w_folded), rows, h, d,
+                                        _stream(stream)))
 
 
 def csa_read_probe(buf, sink, stream=None) -> None:

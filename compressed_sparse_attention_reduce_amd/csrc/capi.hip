@@ -161,6 +161,18 @@ static int check_fp8_score_args(const void* q, const float* w, const void* k, co
     return CSA_OK;
 }
 
+int csa_quantize_query_fp8(const void* q, csa_dtype q_dtype, const float* w, unsigned char* q_codes, float* w_folded,
+                           long long rows, int h, int d, csa_stream stream) {
+    CHECK((q && w && q_codes && w_folded) || rows == 0, "csa_quantize_query_fp8: null pointer argument");
+    CHECK(q_dtype == CSA_F32 || q_dtype == CSA_BF16, "csa_quantize_query_fp8: q must be float32 or bfloat16");
+    CHECK(rows >= 0 && h >= 1 && static_cast<long long>(rows) * h <= (1LL << 31) * 64,
+          "csa_quantize_query_fp8: rows %lld h %d", rows, h);
+    CHECK(d >= 1 && d <= 65536, "csa_quantize_query_fp8: d=%d out of 1..65536", d);
+    return launched(csa::launch_quantize_fp8(q, q_dtype == CSA_BF16, q_codes, nullptr, rows * h, d,
+                                             static_cast<hipStream_t>(stream), w, w_folded),
+                    "csa_quantize_query_fp8");
+}
+
 int csa_read_probe(const void* buf, long long bytes, unsigned* sink, csa_stream stream) {
     CHECK((buf && sink) || bytes < 16, "csa_read_probe: null pointer argument");
     CHECK(bytes >= 0 && aligned16(buf), "csa_read_probe: bytes %lld / unaligned buffer", bytes);
@@ -378,8 +390,9 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
     const bool fp8 = L->idx_dtype == CSA_FP8_E4M3;
     if (fp8 && L->dtype != CSA_BF16)
         return fail(CSA_ERR_UNSUPPORTED, "csa_decode_step: E4M3 indexer keys need bfloat16 caches");
+    // (the E4M3 step takes a bfloat16 query and quantises it: its stride is in bfloat16 elements)
     const int rc_s = fp8 ? check_fp8_score_args(io->q_idx, io->w_idx, L->idx_keys, L->idx_scales, io->scores,
-                                                L->batch, 1, L->h_i, L->d_i, N, L->m, io->q_idx_stride_b,
+                                                L->batch, 1, L->h_i, L->d_i, N, L->m, 2 * io->q_idx_stride_b,
                                                 io->w_stride_b, L->idx_keys_stride_b, L->idx_scales_stride_b,
                                                 io->scores_stride_b, N, "csa_decode_step")
                          : check_score_args(io->q_idx, io->w_idx, L->idx_keys, io->scores, L->dtype, L->batch,
@@ -511,8 +524,9 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
     if (fp8) {
         const csa::Fp8ScoreArgs fa{static_cast<const uint8_t*>(io->q_idx), io->w_idx,
                                    static_cast<const uint8_t*>(L->idx_keys), L->idx_scales, io->scores,
-                                   L->batch, 1, n_scan, nullptr, L->m, io->q_idx_stride_b, io->w_stride_b,
-                                   L->idx_keys_stride_b, L->idx_scales_stride_b, io->scores_stride_b, N, ca, dev};
+                                   L->batch, 1, n_scan, nullptr, L->m, 2 * io->q_idx_stride_b, io->w_stride_b,
+                                   L->idx_keys_stride_b, L->idx_scales_stride_b, io->scores_stride_b, N, ca, dev,
+                                   static_cast<const uint16_t*>(io->q_idx), io->q_idx_stride_b};
         e = csa::launch_index_score_fp8(fa, &pa, s);
     } else {
         e = bf ? csa::launch_index_score_bf16(sa, &pa, s) : csa::launch_index_score_f32(sa, s);

@@ -35,9 +35,13 @@ namespace {
 constexpr int kQuantThreads = 256;
 constexpr int kQuantRowsPerWg = kQuantThreads / kWave;
 
+// w_in / w_out (a query's head weights, nullable): w_out[row] = w_in[row] *
+// scale instead of scales[row] = scale (the scale folded into the weight).
 __global__ __launch_bounds__(kQuantThreads) void k_quantize_fp8(const void* __restrict__ x, int x_bf16,
                                                                 uint8_t* __restrict__ codes,
-                                                                float* __restrict__ scales, long long rows, int d) {
+                                                                float* __restrict__ scales, long long rows, int d,
+                                                                const float* __restrict__ w_in,
+                                                                float* __restrict__ w_out) {
     const int lane = threadIdx.x & (kWave - 1);
     const long long row = static_cast<long long>(blockIdx.x) * kQuantRowsPerWg + threadIdx.x / kWave;
     if (row >= rows) return;  // wave-uniform
@@ -50,7 +54,10 @@ __global__ __launch_bounds__(kQuantThreads) void k_quantize_fp8(const void* __re
     amax = wave_max(amax);
     const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
     for (int j = lane; j < d; j += kWave) codes[row * d + j] = e4m3_encode_rne(get(j) / scale);
-    if (lane == 0) scales[row] = scale;
+    if (lane == 0) {
+        if (w_out) w_out[row] = w_in[row] * scale;
+        else scales[row] = scale;
+    }
 }
 
 // ---- FP8 index score ------------------------------------------------------------
@@ -79,21 +86,48 @@ constexpr int kFp8WgsPerCu = 2;  // one per CU measured slower (11.3 vs 10.9 us 
 // Returns the score in every thread; red: kWaves floats of LDS.
 __device__ inline float score_one_key_fp8(const Fp8ScoreArgs& a, int b, int tt, const float* key, float* red) {
     constexpr int kPer = kDi * kHeads / kThreads;  // key elements per thread
+    static_assert(kDi / kPer == 4, "four lanes per head");
     const int h = threadIdx.x / (kDi / kPer);
     const int part = threadIdx.x % (kDi / kPer);
-    const uint8_t* qh = a.q + b * a.q_stride_b + (static_cast<long long>(tt) * kHeads + h) * kDi + kPer * part;
+    float wh = a.w[b * a.w_stride_b + static_cast<long long>(tt) * kHeads + h];
     float dot = 0.f;
+    if (a.q_raw) {
+        // bfloat16 query: the head row quantised here (quantise_head_row's
+        // rule over the four lanes of the head), its scale folded into wh
+        const uint16_t* qh = a.q_raw + b * a.q_raw_stride_b + (static_cast<long long>(tt) * kHeads + h) * kDi + kPer * part;
+        float x[kPer];
 #pragma unroll
-    for (int u = 0; u < kPer / 16; ++u) {
-        const uint4 v = *reinterpret_cast<const uint4*>(qh + 16 * u);
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        for (int u = 0; u < kPer / 8; ++u) {
+            const uint4 v = *reinterpret_cast<const uint4*>(qh + 8 * u);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            dot += e4m3_decode((w4[e >> 2] >> (8 * (e & 3))) & 0xffu) * key[kPer * part + 16 * u + e];
+            for (int e = 0; e < 4; ++e) {
+                x[8 * u + 2 * e] = bf16_to_f32(static_cast<uint16_t>(w4[e] & 0xffffu));
+                x[8 * u + 2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(w4[e] >> 16));
+            }
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) amax = fmaxf(amax, fabsf(x[e]));
+        amax = fmaxf(amax, xor_lanes_f32<1>(amax));
+        amax = fmaxf(amax, xor_lanes_f32<2>(amax));
+        const float qscale = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) dot += e4m3_decode(e4m3_encode_rne(x[e] / qscale)) * key[kPer * part + e];
+        wh = wh * qscale;
+    } else {
+        const uint8_t* qh = a.q + b * a.q_stride_b + (static_cast<long long>(tt) * kHeads + h) * kDi + kPer * part;
+#pragma unroll
+        for (int u = 0; u < kPer / 16; ++u) {
+            const uint4 v = *reinterpret_cast<const uint4*>(qh + 16 * u);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                dot += e4m3_decode((w4[e >> 2] >> (8 * (e & 3))) & 0xffu) * key[kPer * part + 16 * u + e];
+        }
     }
     dot += xor_lanes_f32<1>(dot);
     dot += xor_lanes_f32<2>(dot);
-    const float wh = a.w[b * a.w_stride_b + static_cast<long long>(tt) * kHeads + h];
     float sc = part == 0 ? wh * fmaxf(dot * key[kDi], 0.f) : 0.f;
     sc = wave_sum(sc);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = sc;
@@ -112,6 +146,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
     static_assert(kHeads * kQPitch <= kLdsFloats * sizeof(float), "query fits the shared area");
     __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
     __shared__ __attribute__((aligned(16))) float ws[kHeads];
+    __shared__ __attribute__((aligned(16))) float qsc[kHeads];  // a bfloat16 query's head scales
     __shared__ CandSmem cs;
     uint8_t* qs = reinterpret_cast<uint8_t*>(lds);
     const int lane = threadIdx.x & (kWave - 1);
@@ -171,11 +206,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
         ks = sbase[key];
     };
 
-    // 1. query (8 KB: two 16-byte pieces per thread) and head weights, then the ring
-    const uint8_t* qrow = a.q + b * a.q_stride_b + static_cast<long long>(tt) * kHeads * kDi;
+    // 1. query (8 KB of codes: two 16-byte pieces per thread; or 16 KB of
+    //    bfloat16: four) and head weights, then the ring
     static_assert(kHeads * kDi / 16 == 2 * kThreads, "two 16-byte query pieces per thread");
-    const uint4 qv0 = *reinterpret_cast<const uint4*>(qrow + 16 * threadIdx.x);
-    const uint4 qv1 = *reinterpret_cast<const uint4*>(qrow + 16 * (threadIdx.x + kThreads));
+    static_assert(kHeads * kDi / 8 == 4 * kThreads, "four 16-byte bfloat16 query pieces per thread");
+    const uint8_t* qrow = a.q + b * a.q_stride_b + static_cast<long long>(tt) * kHeads * kDi;
+    const uint16_t* qraw = a.q_raw + b * a.q_raw_stride_b + static_cast<long long>(tt) * kHeads * kDi;
+    uint4 qv[4];
+    if (a.q_raw) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) qv[u] = *reinterpret_cast<const uint4*>(qraw + 8 * (threadIdx.x + u * kThreads));
+    } else {
+        qv[0] = *reinterpret_cast<const uint4*>(qrow + 16 * threadIdx.x);
+        qv[1] = *reinterpret_cast<const uint4*>(qrow + 16 * (threadIdx.x + kThreads));
+    }
     const float* wrow = a.w + b * a.w_stride_b + static_cast<long long>(tt) * kHeads;
     const float4 wv4 = *reinterpret_cast<const float4*>(wrow + 4 * (threadIdx.x & 15));
     __builtin_amdgcn_sched_barrier(0);
@@ -184,12 +228,45 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
 #pragma unroll
     for (int i = 0; i < kRing; ++i) load_tile(i, kb[i], ksc[i]);
 
-    // 2. stage the query and weights through LDS into registers
-    auto qstage = [&](int c, const uint4& v) {
-        *reinterpret_cast<uint4*>(qs + (c / (kDi / 16)) * kQPitch + (c % (kDi / 16)) * 16) = v;
-    };
-    qstage(threadIdx.x, qv0);
-    qstage(threadIdx.x + kThreads, qv1);
+    // 2. stage the query and weights through LDS into registers; a bfloat16
+    //    query is quantised on the way, one head row per 16 lanes (each lane
+    //    8 elements): the row maximum by lane swaps, then csa_quantize_fp8's
+    //    rule, and the row's scale folded into its head weight
+    if (a.q_raw) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = threadIdx.x + u * kThreads;  // head c / 16, elements 8 (c % 16) ..
+            const uint32_t w4[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[2 * e] = bf16_to_f32(static_cast<uint16_t>(w4[e] & 0xffffu));
+                x[2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(w4[e] >> 16));
+            }
+            float amax = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+            amax = fmaxf(amax, xor_lanes_f32<1>(amax));
+            amax = fmaxf(amax, xor_lanes_f32<2>(amax));
+            amax = fmaxf(amax, xor_lanes_f32<4>(amax));
+            amax = fmaxf(amax, xor_lanes_f32<8>(amax));
+            const float qscale = amax > 0.f ? amax / 448.0f : 1.0f;
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lo |= static_cast<uint32_t>(e4m3_encode_rne(x[e] / qscale)) << (8 * e);
+                hi |= static_cast<uint32_t>(e4m3_encode_rne(x[4 + e] / qscale)) << (8 * e);
+            }
+            *reinterpret_cast<uint2*>(qs + (c / 16) * kQPitch + (c % 16) * 8) = make_uint2(lo, hi);
+            if ((c & 15) == 0) qsc[c / 16] = qscale;
+        }
+    } else {
+        auto qstage = [&](int c, const uint4& v) {
+            *reinterpret_cast<uint4*>(qs + (c / (kDi / 16)) * kQPitch + (c % (kDi / 16)) * 16) = v;
+        };
+        qstage(threadIdx.x, qv[0]);
+        qstage(threadIdx.x + kThreads, qv[1]);
+    }
     if (threadIdx.x < 16) *reinterpret_cast<float4*>(ws + 4 * threadIdx.x) = wv4;
     __syncthreads();
     i32x8 qa[kMTiles];
@@ -206,6 +283,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
     for (int mt = 0; mt < kMTiles; ++mt) {
         const float4 v = *reinterpret_cast<const float4*>(ws + 16 * mt + 4 * lg);
         wr[mt][0] = v.x; wr[mt][1] = v.y; wr[mt][2] = v.z; wr[mt][3] = v.w;
+        if (a.q_raw) {
+            const float4 sc4 = *reinterpret_cast<const float4*>(qsc + 16 * mt + 4 * lg);
+            wr[mt][0] *= sc4.x; wr[mt][1] *= sc4.y; wr[mt][2] *= sc4.z; wr[mt][3] *= sc4.w;
+        }
     }
 
     float* srow = a.scores + b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s;
@@ -264,11 +345,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
 }  // namespace
 
 hipError_t launch_quantize_fp8(const void* x, bool x_bf16, uint8_t* codes, float* scales, long long rows, int d,
-                               hipStream_t s) {
+                               hipStream_t s, const float* w_in, float* w_out) {
     if (rows == 0) return hipSuccess;
     const long long wgs = (rows + kQuantRowsPerWg - 1) / kQuantRowsPerWg;
     hipLaunchKernelGGL(k_quantize_fp8, dim3(static_cast<unsigned>(wgs)), dim3(kQuantThreads), 0, s, x,
-                       x_bf16 ? 1 : 0, codes, scales, rows, d);
+                       x_bf16 ? 1 : 0, codes, scales, rows, d, w_in, w_out);
     return hipGetLastError();
 }
 

@@ -106,11 +106,13 @@ hipError_t launch_index_score_bf16(const ScoreArgs& a, const PrepArgs* fold, hip
 hipError_t launch_index_score_f32(const ScoreArgs& a, hipStream_t s);
 
 // ---- FP8 E4M3 indexer keys ------------------------------------------------------
+// w_in / w_out non-null: the rows are a query's head rows and w_out[r] =
+// w_in[r] * scale_r replaces scales[r] (the scale folded into the weight)
 hipError_t launch_quantize_fp8(const void* x, bool x_bf16, uint8_t* codes, float* scales, long long rows, int d,
-                               hipStream_t s);
+                               hipStream_t s, const float* w_in = nullptr, float* w_out = nullptr);
 struct Fp8ScoreArgs {
     const uint8_t* q;      // [B][t][64][128] E4M3
-    const float* w;        // [B][t][64], query scales folded in
+    const float* w;        // [B][t][64], query scales folded in (unless q_raw)
     const uint8_t* k;      // [B][n][128] E4M3
     const float* k_scale;  // [B][n]
     float* scores;
@@ -122,6 +124,11 @@ struct Fp8ScoreArgs {
     CandArgs cands;
     // decode step with device counters, as in ScoreArgs
     const DevState* dev;
+    // non-null (decode step, t = 1): the query as bfloat16 [B][t][64][128]
+    // (stride in elements) instead of q; every workgroup quantises each head
+    // row as csa_quantize_fp8 does and multiplies w by the row's scale
+    const uint16_t* q_raw;
+    long long q_raw_stride_b;
 };
 // Scan workgroups per row and keys per scan workgroup of the FP8 scan.
 int index_score_fp8_wgs(int rows, int n, int extra);

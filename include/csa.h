@@ -140,6 +140,14 @@ int csa_index_score(const void *q, const float *w, const void *k, float *scores,
  *   rounded to nearest, ties to the even code, saturating at +-448; -0 keeps
  *   its sign.  NaN inputs are out of contract.  Limits: 1 <= d <= 65536.
  *
+ * csa_quantize_query_fp8: a query for the E4M3 score.  q [rows][h][d]
+ *   float32 or bfloat16 (q_dtype), contiguous; w [rows][h] float32 head
+ *   weights -> q_codes [rows][h][d] uint8 (every head row quantised as
+ *   csa_quantize_fp8 quantises a row) and w_folded [rows][h] = w * that head
+ *   row's scale (one binary32 multiply; since ReLU(c x) = c ReLU(x) for
+ *   c > 0 this carries the query's scale into the score).  Limits as
+ *   csa_quantize_fp8, h >= 1.
+ *
  * csa_index_score_fp8:
  *   I[t,s] = sum_h w[t,h] * ReLU(k_scale[s] * (e4m3(q[t,h]) . e4m3(k[s])))
  *   q:       [B][t][h_i][d_i] uint8 codes, stride_b = q_stride_b bytes.
@@ -158,6 +166,8 @@ int csa_index_score(const void *q, const float *w, const void *k, float *scores,
  * ------------------------------------------------------------------------ */
 int csa_quantize_fp8(const void *x, csa_dtype x_dtype, unsigned char *codes, float *scales,
                      long long rows, int d, csa_stream stream);
+int csa_quantize_query_fp8(const void *q, csa_dtype q_dtype, const float *w, unsigned char *q_codes,
+                           float *w_folded, long long rows, int h, int d, csa_stream stream);
 int csa_index_score_fp8(const unsigned char *q, const float *w, const unsigned char *k,
                         const float *k_scale, float *scores, int batch, int t, int h_i, int d_i,
                         int n, const int *q_pos, int ratio, long long q_stride_b,
@@ -263,8 +273,10 @@ int csa_sparse_attn(const void *q, const void *kv, const int *n_valid, const flo
  * records (gather_stride_b in bytes).
  * With E4M3 indexer keys (idx_dtype = CSA_FP8_E4M3; bfloat16 caches, h_i = 64,
  * d_i = 128) step b stores the compressed key as csa_quantize_fp8 would
- * (codes into idx_keys[n_comp], its scale into idx_scales[n_comp]) and step c
- * scores as csa_index_score_fp8 does.
+ * (codes into idx_keys[n_comp], its scale into idx_scales[n_comp]); step c
+ * takes the bfloat16 q_idx and plain w_idx, quantises every head row of
+ * q_idx and folds its scale into that head's weight exactly as
+ * csa_quantize_query_fp8 does, and scores as csa_index_score_fp8 does.
  * It does NOT update the host integers: afterwards the caller sets
  * swa_head = (swa_head + 1) % w, swa_len = min(swa_len + 1, w) and, if a block
  * completed, n_comp += 1 (csa_layer_advance does exactly this).
@@ -295,9 +307,9 @@ typedef struct csa_layer_desc {
     /* E4M3 indexer keys (section 2b; appended, so a zero-filled descriptor
      * keeps keys of `dtype`): idx_dtype = CSA_FP8_E4M3 makes idx_keys
      * [B][max_comp][d_i] uint8 codes (idx_keys_stride_b in bytes) with row
-     * scales idx_scales [B][max_comp] float32 (stride idx_scales_stride_b),
-     * and q_idx [B][h_i][d_i] E4M3 codes whose per-head scales the caller has
-     * folded into w_idx.  Any other value: keys stored as `dtype`. */
+     * scales idx_scales [B][max_comp] float32 (stride idx_scales_stride_b);
+     * q_idx stays bfloat16 [B][h_i][d_i] (the step quantises it).  Any other
+     * value: keys stored as `dtype`. */
     csa_dtype idx_dtype;
     float *idx_scales; long long idx_scales_stride_b;
     /* Mixed main KV (section 6c; appended: zero keeps comp_kv / swa rows of
@@ -337,6 +349,7 @@ typedef struct csa_step_io {
 size_t csa_decode_step_workspace_size(const csa_layer_desc *layer);
 int csa_decode_step(const csa_layer_desc *layer, const csa_step_io *io, void *ws,
                     size_t ws_bytes, csa_stream stream);
+
 
 /* ------------------------------------------------------------------------
  * 6d. The decode step with its counters on the device (graph replay).

@@ -456,8 +456,11 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
     With E4M3 indexer keys (``L.idx_codes`` set) the compressed key is taken
     to float32 and quantised per row (:func:`numfmt.quantize_e4m3_rows`) into
     ``L.idx_codes`` / ``L.idx_scales``, and the scores are
-    :func:`index_score_fp8` with ``q_idx`` the query's E4M3 codes and
-    ``w_idx`` the head weights with the query's scales folded in.
+    :func:`index_score_fp8`.  A real-valued ``q_idx`` is quantised the same
+    way, one row per head, and each head's scale is folded into its weight
+    with one binary32 product (reading R20: ReLU(s x) = s ReLU(x) for s > 0);
+    a uint8 ``q_idx`` is taken as codes whose scales ``w_idx`` already
+    carries.
 
     With mixed main KV (``L.kv_mixed``) the new token's row (already rotated
     by the caller, as the pages' ``kv_roped``) and each compressed entry
@@ -500,8 +503,11 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
         L.n_comp += 1
     N = L.n_comp
     if fp8:
-        scores = index_score_fp8(np.asarray(q_idx, dtype=np.uint8)[None], np.asarray(w_idx)[None],
-                                 L.idx_codes[:N], L.idx_scales[:N])[0]
+        q_codes, w_fold = np.asarray(q_idx), np.asarray(w_idx)
+        if q_codes.dtype != np.uint8:
+            q_codes, q_scale = quantize_e4m3_rows(q_codes.astype(np.float32))
+            w_fold = (w_fold.astype(np.float32) * q_scale).astype(np.float32)
+        scores = index_score_fp8(q_codes[None], w_fold[None], L.idx_codes[:N], L.idx_scales[:N])[0]
     else:
         scores = index_score(np.asarray(q_idx)[None], np.asarray(w_idx)[None], L.idx_keys[:N])[0]
     idx, count = topk(scores[None], top_k)

@@ -1,22 +1,29 @@
 """GPU: the decode step with its counters on the device (csa_decode_step_dev)
-captured once in a HIP graph and replayed step after step, against the
-host-counter step (csa_decode_step, itself checked against the oracle in
-test_gpu_parity.py / test_gpu_mixed_kv.py) on the same inputs.  Every output
-must match bit for bit: the two run the same kernels, only where the
-counters come from differs.  Each replay is checked, with eager work and
-synchronisations between replays."""
+captured once in a HIP graph and replayed step after step.  Every replay is
+checked against the float64 oracle's evolving layer state (the compressed
+entry and key within rounding of the oracle's, then adopted; scores, the
+top-k by the gap rule, gather_buf and the attention output within the
+stated tolerances), and, bit for bit, against the host-counter step
+(csa_decode_step) on the same inputs: the two run the same kernels, only
+where the counters come from differs.  Eager work and synchronisations run
+between replays."""
 
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 from oracle import numfmt
-from tests.gpu_util import DEV, dev_bf16, dev_f32
+from tests.gpu_util import (DEV, assert_bf16_close, assert_topk_gap_rule, dev_bf16, dev_f32, host_bits, host_f64,
+                            rel_err)
+from tests.test_gpu_mixed_kv import _assert_entry_close, decode_records, oracle_records, record_of
+from tests.test_gpu_parity import _assert_e4m3_key_close
 
 pytestmark = pytest.mark.gpu
 
 REC = 592
+ROPE = 64
 
 
 @pytest.fixture(scope="module")
@@ -30,27 +37,32 @@ def _g(seed):
     return np.random.Generator(np.random.PCG64(seed))
 
 
-def _tables(rows, offset, base):
+def _tables_np(rows, offset, base):
     ang = (np.arange(rows)[:, None] + offset) * base ** (-2.0 * np.arange(32)[None, :] / 64)
-    return dev_f32(np.cos(ang).astype(np.float32)), dev_f32(np.sin(ang).astype(np.float32))
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
 
 
 def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64, fp8=False):
     g = _g(seed)
     D, Di, H = 512, 128, 64
     m = 4
+    f = numfmt.bf16_bits_to_f64
+    scale = 1 / np.sqrt(D)
     wm, wi = (2 * D, 2 * Di) if overlap else (D, Di)
     comp_bits = synth.to_bf16_bits(g.standard_normal((B, max_comp, D), dtype=np.float32))
     keys_bits = synth.to_bf16_bits(g.standard_normal((B, max_comp, Di), dtype=np.float32))
     swa_bits = synth.to_bf16_bits(g.standard_normal((B, W, D), dtype=np.float32))
-    mb = dev_f32(g.standard_normal((m, wm), dtype=np.float32) * np.float32(0.1))
-    ib = dev_f32(g.standard_normal((m, wi), dtype=np.float32) * np.float32(0.1))
-    sink = dev_f32(g.standard_normal(H, dtype=np.float32))
-    rope = _tables(pos0 + steps + 4, 0.5, 10000.0) if mixed else None
-    comp_rope = _tables(max_comp + 2, 0.25, 500.0) if mixed else None
+    mb_np = g.standard_normal((m, wm), dtype=np.float32) * np.float32(0.1)
+    ib_np = g.standard_normal((m, wi), dtype=np.float32) * np.float32(0.1)
+    sink_np = g.standard_normal(H, dtype=np.float32)
+    mb, ib, sink = dev_f32(mb_np), dev_f32(ib_np), dev_f32(sink_np)
+    rope_np = _tables_np(pos0 + steps + 4, 0.5, 10000.0) if mixed else None
+    comp_rope_np = _tables_np(max_comp + 2, 0.25, 500.0) if mixed else None
+    rope = tuple(dev_f32(t) for t in rope_np) if mixed else None
+    comp_rope = tuple(dev_f32(t) for t in comp_rope_np) if mixed else None
 
     if fp8:
-        kc0, ks0 = numfmt.quantize_e4m3_rows(numfmt.bf16_bits_to_f64(keys_bits).reshape(-1, Di).astype(np.float32))
+        kc0, ks0 = numfmt.quantize_e4m3_rows(f(keys_bits).reshape(-1, Di).astype(np.float32))
         kc0, ks0 = kc0.reshape(B, max_comp, Di), ks0.reshape(B, max_comp)
 
     def caches():
@@ -81,13 +93,35 @@ def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64, 
                     out=torch.zeros(B, H, D, dtype=torch.bfloat16, device=DEV),
                     lse=torch.zeros(B, H, device=DEV))
 
+    # one oracle layer state per sequence, from the same cache values
+    osts = []
+    for b in range(B):
+        if mixed:
+            comp_rec, comp_val = oracle_records(f(comp_bits[b]))
+            _, swa_val = oracle_records(f(swa_bits[b]))
+        else:
+            comp_val, swa_val = f(comp_bits[b]), f(swa_bits[b])
+        osts.append(oracle.LayerState(
+            comp_kv=comp_val.copy(), idx_keys=np.zeros((max_comp, Di)) if fp8 else f(keys_bits[b]), n_comp=n0,
+            swa=oracle.SwaRing(swa_val.copy(), pos0 % W, min(pos0, W)), main_bias=mb_np.astype(np.float64),
+            idx_bias=ib_np.astype(np.float64), sink=sink_np.astype(np.float64), overlap=bool(overlap),
+            round_cache=numfmt.bf16_round_f64,
+            idx_codes=kc0[b].copy() if fp8 else None, idx_scales=ks0[b].copy() if fp8 else None,
+            kv_mixed=mixed, rope_dim=ROPE,
+            rope_cos=rope_np[0].astype(np.float64) if mixed else None,
+            rope_sin=rope_np[1].astype(np.float64) if mixed else None,
+            comp_rope_cos=comp_rope_np[0].astype(np.float64) if mixed else None,
+            comp_rope_sin=comp_rope_np[1].astype(np.float64) if mixed else None))
+
     ch, kh, sh = caches()
     Lh = layer(ch, kh, sh)
     cd, kd, sd = caches()
     Ld = layer(cd, kd, sd)
-    # static inputs of the captured step
+    if mixed:  # the library packs the caches as the oracle does
+        np.testing.assert_array_equal(cd[0].cpu().numpy(), oracle_records(f(comp_bits[0]))[0])
+    # static inputs of the captured step (the E4M3 step takes the bf16 query too)
     st_in = dict(q=torch.zeros(B, H, D, dtype=torch.bfloat16, device=DEV),
-                 q_idx=torch.zeros(B, 64, Di, dtype=torch.uint8 if fp8 else torch.bfloat16, device=DEV),
+                 q_idx=torch.zeros(B, 64, Di, dtype=torch.bfloat16, device=DEV),
                  w_idx=torch.zeros(B, 64, device=DEV),
                  kv_new=torch.zeros(B, D, dtype=torch.bfloat16, device=DEV),
                  z_main=torch.zeros(B, wm, device=DEV), c_main=torch.zeros(B, wm, device=DEV),
@@ -116,12 +150,7 @@ def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64, 
         for k in hist_z:
             hist_z[k].append(x[k])
         # the captured step: new inputs into its static buffers, one replay
-        if fp8:  # E4M3 query, its per-head scales folded into the weights
-            qc, qs = numfmt.quantize_e4m3_rows(numfmt.bf16_bits_to_f64(x["q_idx"]).reshape(-1, Di).astype(np.float32))
-            x["q_idx"] = qc.reshape(B, 64, Di)
-            x["w_idx"] = (x["w_idx"] * qs.reshape(B, 64)).astype(np.float32)
-        dev_in = {k: (torch.from_numpy(v).to(DEV) if v.dtype == np.uint8 else
-                      dev_bf16(v) if v.dtype == np.uint16 else dev_f32(v)) for k, v in x.items()}
+        dev_in = {k: (dev_bf16(v) if v.dtype == np.uint16 else dev_f32(v)) for k, v in x.items()}
         for k, v in dev_in.items():
             st_in[k].copy_(v)
         print(f"dev step pos={pos}", flush=True)
@@ -129,21 +158,86 @@ def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64, 
         torch.cuda.synchronize()
         # the host-counter step on the same inputs (block rows from the history)
         completes = pos % m == m - 1
-        blk = {}
+        blk_np = {}
         for k in hist_z:
             rows = np.stack(hist_z[k][-m:], axis=1)                   # [B, m, w]
             if overlap and pos // m > 0:
                 rows = np.stack(hist_z[k][-2 * m:], axis=1)           # previous block then this one
-            blk[k] = dev_f32(np.ascontiguousarray(rows)) if completes else dev_f32(np.zeros((B, m, rows.shape[2]), np.float32))
+            blk_np[k] = np.ascontiguousarray(rows)
+        blk = {k: dev_f32(v) if completes else dev_f32(np.zeros((B, m, v.shape[2]), np.float32))
+               for k, v in blk_np.items()}
         oh = outs()
         ioh = csa.make_step_io(pos=pos, q=dev_in["q"], q_idx=dev_in["q_idx"], w_idx=dev_in["w_idx"],
                                kv_new=dev_in["kv_new"], **blk, **oh)
+        slot = Lh.swa_head
         csa.csa_decode_step(Lh, ioh, wsh)
         csa.csa_layer_advance(Lh, pos)
         torch.cuda.synchronize()
         N = Lh.n_comp
         sv = state.cpu().numpy()
         assert (sv[0], sv[1], sv[2], sv[3], sv[4]) == (pos + 1, N, Lh.swa_head, Lh.swa_len, 0)
+
+        # 1. against the oracle, sequence by sequence
+        for b in range(B):
+            ost = osts[b]
+            nb = ost.n_comp
+            r = oracle.decode_step(ost, q=f(x["q"][b]), q_idx=f(x["q_idx"][b]), w_idx=x["w_idx"][b],
+                                   kv_new=f(x["kv_new"][b]), pos=pos, top_k=K,
+                                   **{k: v[b] for k, v in blk_np.items()}, scale=scale)
+            assert (ost.n_comp, ost.swa.head, ost.swa.length) == (N, Lh.swa_head, Lh.swa_len)
+            # the new token's ring row
+            if mixed:
+                c_, s_, rp_, _ = oracle.mixed_kv_row(f(x["kv_new"][b]), ROPE)
+                np.testing.assert_array_equal(sd[b, slot].cpu().numpy(), record_of(c_, s_, rp_))
+            else:
+                np.testing.assert_array_equal(host_bits(sd[b, slot]), x["kv_new"][b])
+            # the compressed entry and key within rounding of the oracle's, then the GPU's adopted
+            if completes:
+                ym, yi = r["new_entry"]
+                if mixed:
+                    _assert_entry_close(cd[b, nb].cpu().numpy(), ost.comp_kv[nb])
+                else:
+                    assert_bf16_close(host_bits(cd[b, nb]), ym)
+                if fp8:
+                    _assert_e4m3_key_close(kd[0][b, nb].cpu().numpy(), float(kd[1][b, nb]), yi)
+                else:
+                    assert_bf16_close(host_bits(kd[b, nb]), yi)
+            ost.comp_kv[:N] = decode_records(cd[b, :N].cpu().numpy()) if mixed else host_f64(cd[b, :N])
+            if fp8:
+                ost.idx_codes[:N], ost.idx_scales[:N] = kd[0][b, :N].cpu().numpy(), kd[1][b, :N].cpu().numpy()
+                qc, qs = numfmt.quantize_e4m3_rows(f(x["q_idx"][b]).astype(np.float32))
+                w8 = (x["w_idx"][b] * qs).astype(np.float32)
+                ref_s = oracle.index_score_fp8(qc[None], w8[None], ost.idx_codes[:N], ost.idx_scales[:N])[0]
+            else:
+                ost.idx_keys[:N] = host_f64(kd[b, :N])
+                ref_s = oracle.index_score(f(x["q_idx"][b])[None], x["w_idx"][b][None], ost.idx_keys[:N])[0]
+            got_s = od["scores"][b, :N].cpu().numpy().astype(np.float64)
+            assert rel_err(got_s, ref_s) <= 1e-4, (pos, b)
+            gi, gc = od["topk_idx"][b].cpu().numpy(), int(od["topk_count"][b])
+            np.testing.assert_array_equal(gi, oracle.topk(got_s[None], K)[0][0])
+            assert_topk_gap_rule(gi, gc, ref_s, K)
+            nv = int(od["n_valid"][b])
+            if mixed:
+                recs, ringr = cd[b].cpu().numpy(), sd[b].cpu().numpy()
+                want_buf = np.stack([recs[i] for i in gi[:gc]] +
+                                    [ringr[(ost.swa.head - ost.swa.length + j) % W] for j in range(ost.swa.length)])
+                assert nv == len(want_buf)
+                np.testing.assert_array_equal(od["gather_buf"][b, :nv].cpu().numpy(), want_buf)
+                rows = decode_records(want_buf)
+                np.testing.assert_array_equal(rows[gc:], oracle.gather(ost.comp_kv[:N], gi, gc, ost.swa.rows,
+                                                                       ost.swa.head, ost.swa.length)[0][gc:])
+            else:
+                rows, n_valid = oracle.gather(ost.comp_kv[:N], gi, gc, ost.swa.rows, ost.swa.head, ost.swa.length)
+                assert nv == n_valid
+                np.testing.assert_array_equal(host_f64(od["gather_buf"][b, :nv]), rows)
+            ro, rl = oracle.sparse_attn(f(x["q"][b]), rows, ost.sink, scale)
+            if mixed:
+                ro = oracle.rope_rotate(ro, ost.rope_cos[pos], ost.rope_sin[pos], inverse=True)
+            assert rel_err(host_f64(od["out"][b]), ro) <= 2e-2, (pos, b)
+            gl = od["lse"][b].cpu().numpy()
+            assert rel_err(gl, rl) <= 2e-2 and np.abs(gl - rl).max() <= 1e-2, (pos, b)
+
+        # 2. bit for bit against the host-counter step
         assert torch.equal(od["scores"][:, :N], oh["scores"][:, :N])
         for k in ("topk_idx", "topk_count", "n_valid", "out", "lse"):
             assert torch.equal(od[k], oh[k]), (pos, k)

@@ -315,8 +315,9 @@ def test_decode_step_mixed_kv_fp8_keys_batched(csa, B):
     kc0, ks0 = numfmt.quantize_e4m3_rows(f(x["idx_keys"].reshape(-1, 128)).astype(np.float32))
     kc0, ks0 = kc0.reshape(B, 1000, 128), ks0.reshape(B, 1000)
     kc, ks = torch.from_numpy(kc0.copy()).to(DEV), dev_f32(ks0)
-    qi = g.standard_normal((B, 64, 128), dtype=np.float32) / np.float32(np.sqrt(128))
-    qc, qs = numfmt.quantize_e4m3_rows(qi.reshape(-1, 128))
+    # the step takes the bf16 query and quantises it; the oracle's codes and folded weights from the host
+    qi = synth.to_bf16_bits(g.standard_normal((B, 64, 128), dtype=np.float32) / np.float32(np.sqrt(128)))
+    qc, qs = numfmt.quantize_e4m3_rows(f(qi).reshape(-1, 128).astype(np.float32))
     qc = qc.reshape(B, 64, 128)
     w8 = (x["w_idx"] * qs.reshape(B, 64)).astype(np.float32)
     rc, rs = rope_tables(pos + 4)
@@ -331,7 +332,7 @@ def test_decode_step_mixed_kv_fp8_keys_batched(csa, B):
                 gather_buf=torch.zeros(B, K + W, REC, dtype=torch.uint8, device=DEV),
                 n_valid=torch.empty(B, dtype=torch.int32, device=DEV),
                 out=torch.empty(B, 64, 512, dtype=torch.bfloat16, device=DEV), lse=torch.empty(B, 64, device=DEV))
-    io = csa.make_step_io(pos=pos, q=dev_bf16(x["q"]), q_idx=torch.from_numpy(qc).to(DEV), w_idx=dev_f32(w8),
+    io = csa.make_step_io(pos=pos, q=dev_bf16(x["q"]), q_idx=dev_bf16(qi), w_idx=dev_f32(x["w_idx"]),
                           kv_new=dev_bf16(x["kv_new"]), z_main=dev_f32(x["z_main"]), c_main=dev_f32(x["c_main"]),
                           z_idx=dev_f32(x["z_idx"]), c_idx=dev_f32(x["c_idx"]), **outs)
     ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
@@ -345,7 +346,7 @@ def test_decode_step_mixed_kv_fp8_keys_batched(csa, B):
                                 idx_codes=kc0[b].copy(), idx_scales=ks0[b].copy(), kv_mixed=True, rope_dim=ROPE,
                                 rope_cos=rc.astype(np.float64), rope_sin=rs.astype(np.float64),
                                 comp_rope_cos=cc.astype(np.float64), comp_rope_sin=cs.astype(np.float64))
-        oracle.decode_step(ost, q=f(x["q"][b]), q_idx=qc[b], w_idx=w8[b], kv_new=f(x["kv_new"][b]), pos=pos,
+        oracle.decode_step(ost, q=f(x["q"][b]), q_idx=f(qi[b]), w_idx=x["w_idx"][b], kv_new=f(x["kv_new"][b]), pos=pos,
                            top_k=K, z_main=x["z_main"][b], c_main=x["c_main"][b], z_idx=x["z_idx"][b],
                            c_idx=x["c_idx"][b], scale=1 / np.sqrt(512))
         # the new records: the ring one bit-exact, the entry within rounding; the key within E4M3 rounding

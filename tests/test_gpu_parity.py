@@ -247,9 +247,12 @@ def test_index_score_fp8_full_size_sampled_and_recall(csa):
     csa.csa_quantize_fp8(keys, kc, ks)
     q = x["q_idx"][:, None].contiguous()               # [1, 1, 64, 128] bf16
     qc = torch.empty(1, 1, 64, 128, dtype=torch.uint8, device=DEV)
-    qs = torch.empty(1, 1, 64, dtype=torch.float32, device=DEV)
-    csa.csa_quantize_fp8(q, qc, qs)
-    w8 = (x["w_idx"][:, None] * qs).contiguous()
+    w8 = torch.empty(1, 1, 64, dtype=torch.float32, device=DEV)
+    csa.csa_quantize_query_fp8(q, x["w_idx"][:, None].contiguous(), qc, w8)
+    # the library's query codes and folded weights are the oracle's, bit for bit
+    hqc, hw8 = _fp8_query(host_f64(q[0, 0]).astype(np.float32), x["w_idx"][0].cpu().numpy())
+    np.testing.assert_array_equal(qc[0, 0].cpu().numpy(), hqc)
+    np.testing.assert_array_equal(w8[0, 0].cpu().numpy().view(np.uint32), hw8.view(np.uint32))
     s8 = torch.empty(1, 1, n, device=DEV)
     csa.csa_index_score_fp8(qc, w8, kc, ks, s8)
     s16 = torch.empty(1, 1, n, device=DEV)
@@ -258,8 +261,7 @@ def test_index_score_fp8_full_size_sampled_and_recall(csa):
     g = _g(45)
     sample = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n), g.integers(0, n, 4096)]))
     idx = torch.from_numpy(sample).to(DEV)
-    ref = oracle.index_score_fp8(qc[0].cpu().numpy(), w8[0].cpu().numpy(), kc[0, idx].cpu().numpy(),
-                                 ks[0, idx].cpu().numpy())[0]
+    ref = oracle.index_score_fp8(hqc[None], hw8[None], kc[0, idx].cpu().numpy(), ks[0, idx].cpu().numpy())[0]
     assert rel_err(s8[0, 0].cpu().numpy().astype(np.float64)[sample], ref) <= 1e-4
     top8 = set(torch.topk(s8[0, 0], 512).indices.cpu().tolist())
     top16 = set(torch.topk(s16[0, 0], 512).indices.cpu().tolist())
@@ -733,8 +735,10 @@ def test_decode_steps_in_sequence_fp8_keys(csa):
     ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
     for pos in range(x["pos"], x["pos"] + 9):
         q = synth.to_bf16_bits(g.standard_normal((1, 64, 512), dtype=np.float32))
-        qc, w8 = _fp8_query(g.standard_normal((1, 64, 128), dtype=np.float32) / np.float32(np.sqrt(128)),
-                            g.standard_normal((1, 64), dtype=np.float32))
+        # the step takes the bf16 query and plain weights and quantises the query itself
+        qi = synth.to_bf16_bits(g.standard_normal((1, 64, 128), dtype=np.float32) / np.float32(np.sqrt(128)))
+        wi = g.standard_normal((1, 64), dtype=np.float32)
+        qc, w8 = _fp8_query(f(qi).astype(np.float32), wi)
         kvn = synth.to_bf16_bits(g.standard_normal((1, 512), dtype=np.float32))
         zm, cm = g.standard_normal((2, 1, 4, 512), dtype=np.float32)
         zi, ci = g.standard_normal((2, 1, 4, 128), dtype=np.float32)
@@ -743,7 +747,7 @@ def test_decode_steps_in_sequence_fp8_keys(csa):
                     gather_buf=torch.zeros(1, 72, 512, dtype=dt, device=DEV),
                     n_valid=torch.empty(1, dtype=torch.int32, device=DEV),
                     out=torch.empty(1, 64, 512, dtype=dt, device=DEV))
-        io = csa.make_step_io(pos=pos, q=dev_bf16(q), q_idx=torch.from_numpy(qc).to(DEV), w_idx=dev_f32(w8),
+        io = csa.make_step_io(pos=pos, q=dev_bf16(q), q_idx=dev_bf16(qi), w_idx=dev_f32(wi),
                               kv_new=dev_bf16(kvn), z_main=dev_f32(zm), c_main=dev_f32(cm), z_idx=dev_f32(zi),
                               c_idx=dev_f32(ci), **outs)
         print(f"fp8-key step pos={pos}", flush=True)
@@ -752,7 +756,7 @@ def test_decode_steps_in_sequence_fp8_keys(csa):
         torch.cuda.synchronize()
         completes = pos % 4 == 3
         n0 = ost.n_comp
-        oracle.decode_step(ost, q=f(q[0]), q_idx=qc[0], w_idx=w8[0], kv_new=f(kvn[0]), pos=pos, top_k=64,
+        oracle.decode_step(ost, q=f(q[0]), q_idx=f(qi[0]), w_idx=wi[0], kv_new=f(kvn[0]), pos=pos, top_k=64,
                            z_main=zm[0], c_main=cm[0], z_idx=zi[0], c_idx=ci[0], scale=1 / np.sqrt(512))
         assert (L.n_comp, L.swa_head, L.swa_len) == (ost.n_comp, ost.swa.head, ost.swa.length)
         N = ost.n_comp
@@ -789,11 +793,8 @@ def test_decode_step_ctx1m_fp8_keys_full_size(csa):
     kc = torch.zeros(B, shape.max_comp, 128, dtype=torch.uint8, device=DEV)
     ks = torch.zeros(B, shape.max_comp, dtype=torch.float32, device=DEV)
     csa.csa_quantize_fp8(x["idx_keys"][:, :n0].contiguous(), kc[:, :n0], ks[:, :n0])
-    q = x["q_idx"].contiguous()                        # [1, 64, 128] bf16
-    qc = torch.empty(1, 64, 128, dtype=torch.uint8, device=DEV)
-    qs = torch.empty(1, 64, dtype=torch.float32, device=DEV)
-    csa.csa_quantize_fp8(q, qc, qs)
-    w8 = (x["w_idx"] * qs).contiguous()
+    # the step quantises the bf16 query itself; the oracle's codes and folded weights from the host
+    qc, w8 = _fp8_query(host_f64(x["q_idx"]).astype(np.float32), x["w_idx"].cpu().numpy())
     torch.cuda.synchronize()
     pristine = kc[0, :n0].clone()
     L = csa.make_layer_desc(comp_kv=x["comp_kv"], idx_keys=kc, idx_scales=ks, swa=x["swa"],
@@ -807,7 +808,7 @@ def test_decode_step_ctx1m_fp8_keys_full_size(csa):
                 n_valid=torch.empty(B, dtype=torch.int32, device=DEV),
                 out=torch.empty(B, shape.h, D, dtype=torch.bfloat16, device=DEV),
                 lse=torch.empty(B, shape.h, device=DEV))
-    io = csa.make_step_io(pos=x["pos"], q=x["q"], q_idx=qc, w_idx=w8, kv_new=x["kv_new"],
+    io = csa.make_step_io(pos=x["pos"], q=x["q"], q_idx=x["q_idx"], w_idx=x["w_idx"], kv_new=x["kv_new"],
                           z_main=x["z_main"], c_main=x["c_main"], z_idx=x["z_idx"], c_idx=x["c_idx"], **outs)
     ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
     csa.csa_decode_step(L, io, ws)
@@ -819,7 +820,7 @@ def test_decode_step_ctx1m_fp8_keys_full_size(csa):
                          x["idx_bias"].cpu().numpy(), 4)[-1]
     codes, scales = kc[0, :N].cpu().numpy(), ks[0, :N].cpu().numpy()
     _assert_e4m3_key_close(codes[n0], float(scales[n0]), yi)
-    ref_s = oracle.index_score_fp8(qc.cpu().numpy(), w8.cpu().numpy(), codes, scales)[0]
+    ref_s = oracle.index_score_fp8(qc, w8, codes, scales)[0]
     got_s = outs["scores"][0, :N].cpu().numpy().astype(np.float64)
     assert rel_err(got_s, ref_s) <= 1e-4
     gi = outs["topk_idx"][0].cpu().numpy()

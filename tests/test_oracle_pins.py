@@ -647,6 +647,42 @@ def test_decode_step_fp8_key_within_e4m3_rounding():
     assert L.n_comp == 4
 
 
+def test_decode_step_fp8_float_query_quantised_and_folded():
+    """Over E4M3 keys a real-valued query is quantised per head row and each
+    row's scale folded into its head weight (reading R20).  Head rows that are
+    E4M3 values times a power of two p_h, with +-448 present, quantise exactly
+    (codes = those values, scale = p_h): the step must equal the step given
+    those codes and w * p_h.  And doubling the query doubles every score (a
+    step that dropped the scale would not move)."""
+    g = _g(29)
+    D, di, H, W, Hi = 16, 8, 4, 6, 4
+    states = []
+    for _ in range(3):
+        L = _empty_state(g, D=D, di=di, H=H, W=W)
+        L.idx_codes = np.zeros((64, di), dtype=np.uint8)
+        L.idx_scales = np.zeros(64, dtype=np.float32)
+        states.append(L)
+    for L in states[1:]:
+        L.main_bias, L.idx_bias, L.sink = states[0].main_bias, states[0].idx_bias, states[0].sink
+    La, Lb, Lc = states
+    for pos in range(14):
+        inp = _step_inputs(g, D=D, di=di, H=H, Hi=Hi)
+        qc = _e4m3_codes(g, (Hi, di))
+        qc[np.arange(Hi), (pos + np.arange(Hi)) % di] = 0x7E | (0x80 * (np.arange(Hi) % 2)).astype(np.uint8)
+        p = np.float32(2.0) ** g.integers(-6, 3, size=Hi).astype(np.float32)
+        qv = numfmt.e4m3_decode(qc) * p[:, None].astype(np.float64)
+        w = inp["w_idx"].astype(np.float32)
+        ra = oracle.decode_step(La, pos=pos, top_k=5, **{**inp, "q_idx": qv, "w_idx": w})
+        rb = oracle.decode_step(Lb, pos=pos, top_k=5, **{**inp, "q_idx": qc, "w_idx": (w * p).astype(np.float32)})
+        rc = oracle.decode_step(Lc, pos=pos, top_k=5, **{**inp, "q_idx": 2 * qv, "w_idx": w})
+        np.testing.assert_array_equal(ra["scores"], rb["scores"])
+        np.testing.assert_array_equal(rc["scores"], 2 * ra["scores"])
+        np.testing.assert_array_equal(ra["idx"], rb["idx"])
+        if La.n_comp:
+            assert np.abs(ra["scores"]).max() > 0
+    assert La.n_comp == 3
+
+
 def _rope_tables(n_pos, rd, base=10000.0, offset=0.0):
     """cos / sin rows of angle (p + offset) * base^(-2j/rd) (a test table)."""
     ang = (np.arange(n_pos)[:, None] + offset) * base ** (-2.0 * np.arange(rd // 2)[None, :] / rd)
