@@ -95,6 +95,8 @@ _SIGS = {
                              _ll, _vp, _sz, _vp]),
     "csa_decode_step_workspace_size": (_sz, [ctypes.POINTER(LayerDesc)]),
     "csa_decode_step": (_i, [ctypes.POINTER(LayerDesc), ctypes.POINTER(StepIO), _vp, _sz, _vp]),
+    "csa_decode_step_noalloc_max_bytes": (_sz, []),
+    "csa_decode_step_noalloc": (_i, [ctypes.POINTER(LayerDesc), ctypes.POINTER(StepIO), _vp]),
     "csa_layer_advance": (_i, [ctypes.POINTER(LayerDesc), _i]),
     "csa_decode_step_dev_ring_size": (_sz, [ctypes.POINTER(LayerDesc)]),
     "csa_decode_step_dev": (_i, [ctypes.POINTER(LayerDesc), ctypes.POINTER(StepIO), _vp, _vp, _sz, _vp, _sz, _vp]),
@@ -307,6 +309,15 @@ def csa_decode_step_workspace_size(layer: LayerDesc) -> int:
 def csa_decode_step(layer: LayerDesc, io: StepIO, ws, stream=None) -> None:
     _check(lib().csa_decode_step(ctypes.byref(layer), ctypes.byref(io), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def csa_decode_step_noalloc_max_bytes() -> int:
+    return int(lib().csa_decode_step_noalloc_max_bytes())
+
+
+def csa_decode_step_noalloc(layer: LayerDesc, io: StepIO, stream=None) -> None:
+    """csa_decode_step with the library's own fixed scratch (no workspace)."""
+    _check(lib().csa_decode_step_noalloc(ctypes.byref(layer), ctypes.byref(io), _stream(stream)))
 
 
 def csa_decode_step_dev_ring_size(layer: LayerDesc) -> int:

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/csa.h"
 #include "kernels.h"
@@ -612,6 +613,68 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
 int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes,
                     csa_stream stream) {
     return decode_step(L, io, ws, ws_bytes, stream, nullptr, nullptr, 0);
+}
+
+}  // extern "C"
+
+// ---- the decode step without a caller workspace ----------------------------------------
+//
+// For callers that cannot allocate (graph capture, serving loops): the
+// step's scratch (candidate lists, split partials) lives in this file-scope
+// device array, one copy per GPU, held until the process ends.  On the host
+// the array's name is only a stand-in: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is handed to
+// kernels.  Nothing in the array has to start at zero: every byte the step
+// reads back is written by the same step first.
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = size_t{32} << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (nullptr and a message on failure).
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        fail(CSA_ERR_LAUNCH, "csa_decode_step_noalloc: no current device (or device id %d above %d)", dev,
+             kMaxDevices - 1);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            fail(CSA_ERR_LAUNCH, "csa_decode_step_noalloc: hipGetSymbolAddress(scratch) failed: %s",
+                 hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t csa_decode_step_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+int csa_decode_step_noalloc(const csa_layer_desc* L, const csa_step_io* io, csa_stream stream) {
+    CHECK(L && io, "csa_decode_step_noalloc: null layer or io");
+    const size_t need = csa_decode_step_workspace_size(L);
+    CHECK(need > 0, "csa_decode_step_noalloc: bad layer sizes");
+    if (need > kNoAllocScratchBytes)
+        return fail(CSA_ERR_WORKSPACE,
+                    "csa_decode_step_noalloc: the step needs %zu bytes of scratch, above the fixed %zu "
+                    "(use csa_decode_step with a workspace)",
+                    need, kNoAllocScratchBytes);
+    void* ws = device_scratch();
+    if (!ws) return CSA_ERR_LAUNCH;
+    return decode_step(L, io, ws, kNoAllocScratchBytes, stream, nullptr, nullptr, 0);
 }
 
 int csa_decode_step_dev(const csa_layer_desc* L, const csa_step_io* io, csa_dev_state* state, float* ring,

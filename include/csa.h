@@ -350,6 +350,27 @@ size_t csa_decode_step_workspace_size(const csa_layer_desc *layer);
 int csa_decode_step(const csa_layer_desc *layer, const csa_step_io *io, void *ws,
                     size_t ws_bytes, csa_stream stream);
 
+/* ------------------------------------------------------------------------
+ * 6e. The decode step with no workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).
+ *
+ * csa_decode_step_noalloc runs exactly csa_decode_step (same kernels, same
+ * results) with its scratch in a fixed device array inside the library:
+ * csa_decode_step_noalloc_max_bytes() bytes (32 MiB), one copy per GPU,
+ * held from the first call on that GPU until the process ends.  The caller
+ * still owns and passes every input and output (layer caches, io).  It
+ * calls no allocating routine.  A layer whose step needs more scratch than
+ * that (csa_decode_step_workspace_size(layer) > the maximum, e.g. more
+ * than 8 sequences at top_k 512 + window 128, d 512) is rejected with
+ * CSA_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different host threads without stream
+ * ordering between them) race on it and give undefined results.  Nothing
+ * in the array needs to start at zero.
+ * ------------------------------------------------------------------------ */
+size_t csa_decode_step_noalloc_max_bytes(void);
+int csa_decode_step_noalloc(const csa_layer_desc *layer, const csa_step_io *io, csa_stream stream);
 
 /* ------------------------------------------------------------------------
  * 6d. The decode step with its counters on the device (graph replay).

@@ -284,6 +284,21 @@ def test_decode_step_validation_and_advance(csa):
         csa.csa_layer_advance(L4, 3)
 
 
+def test_decode_step_noalloc_rejects_oversize_scratch(csa):
+    """The fixed-scratch step refuses layers whose scratch exceeds its array
+    (before any device call), and validates like csa_decode_step."""
+    B = csa.binding
+    lib = csa.lib()
+    cap = csa.csa_decode_step_noalloc_max_bytes()
+    assert cap == 32 << 20
+    io = _io(csa, pos=3999)
+    big = _desc(csa, batch=16)
+    assert csa.csa_decode_step_workspace_size(big) > cap
+    assert lib.csa_decode_step_noalloc(ctypes.byref(big), ctypes.byref(io), None) == B.CSA_ERR_WORKSPACE
+    assert "scratch" in csa.csa_last_error()
+    assert lib.csa_decode_step_noalloc(None, ctypes.byref(io), None) == B.CSA_ERR_INVALID_ARG
+
+
 def test_decode_step_fp8_keys_validation(csa):
     """E4M3 indexer keys: bfloat16 caches, 64 x 128 indexer, row scales given."""
     B = csa.binding
