@@ -73,7 +73,7 @@ constexpr int kQPitch = kDi + 16;   // LDS row pitch of the staged query (bytes)
 
 constexpr int kLaneTop = 4;         // composites a lane keeps (candidate lists)
 constexpr int kMaxTilesPerWave = 32;  // with candidates: at most 8 keys per lane list
-static_assert(kRing % 4 == 0, "ring slot i feeds the lists of lane group i % 4");
+static_assert(kRing % 4 == 0, "each run of four ring slots feeds the four lane groups' lists");
 
 static_assert(kWaves == kScoreWavesPerWg, "waves per workgroup as the host assumes");
 
@@ -295,6 +295,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
     u64 drop = 0;
 #pragma unroll
     for (int i = 0; i < kLaneTop; ++i) top[i] = 0;
+    // every lane holds the score of key li of each tile; each run of four
+    // tiles waits here and lane group lg inserts the one of tile lg
+    u64 pend[4];
 
     // 3. stream (the same ring discipline as the bf16 scan)
     auto step = [&](int i, int j, bool refill) {
@@ -320,8 +323,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
         if (live && lg == 0) srow[key] = sc;
         if (kCands) {
             const uint32_t kk = score_key(sc);
-            const bool mine = live && lg == (i & 3) && key_valid(kk, sc);
-            lane_insert(top, drop, mine ? composite(kk, static_cast<uint32_t>(key)) : 0ull);
+            pend[i & 3] = (live && key_valid(kk, sc)) ? composite(kk, static_cast<uint32_t>(key)) : 0ull;
+            if ((i & 3) == 3)
+                lane_insert(top, drop, lg == 0 ? pend[0] : lg == 1 ? pend[1] : lg == 2 ? pend[2] : pend[3]);
         }
     };
     int j0 = 0;

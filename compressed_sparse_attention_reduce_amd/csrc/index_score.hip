@@ -46,7 +46,7 @@ constexpr int kRing = 4;           // key tiles in flight per wave
 constexpr int kQPitch = kDi + 8;   // LDS row pitch of the staged query (bank spread)
 constexpr int kMaxTilesPerWave = 32;  // with candidates: at most 8 keys per lane list
 constexpr int kLaneTop = 4;           // composites a lane keeps
-static_assert(kRing % 4 == 0, "ring slot i feeds the lists of lane group i % 4");
+static_assert(kRing == 4, "ring slot i feeds the list of lane group i");
 
 static_assert(kHeads * kQPitch * sizeof(uint16_t) >= kPrepMaxD * sizeof(float), "prep roles reuse the query LDS");
 
@@ -198,6 +198,9 @@ __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs
     u64 drop = 0;
 #pragma unroll
     for (int i = 0; i < kLaneTop; ++i) top[i] = 0;
+    // every lane holds the score of key li of each tile; the four tiles of a
+    // ring cycle wait here and lane group lg inserts the one of tile lg
+    u64 pend[kRing];
 
     // 3. stream: consume a tile, refill its ring slot kRing tiles ahead.
     //    The steady loop only refills tiles that exist; one more group may
@@ -222,8 +225,9 @@ __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs
         if (live && lg == 0) srow[key] = sc;
         if (kCands) {
             const uint32_t kk = score_key(sc);
-            const bool mine = live && lg == (i & 3) && key_valid(kk, sc);
-            lane_insert(top, drop, mine ? composite(kk, static_cast<uint32_t>(key)) : 0ull);
+            pend[i] = (live && key_valid(kk, sc)) ? composite(kk, static_cast<uint32_t>(key)) : 0ull;
+            if (i == kRing - 1)
+                lane_insert(top, drop, lg == 0 ? pend[0] : lg == 1 ? pend[1] : lg == 2 ? pend[2] : pend[3]);
         }
     };
     int j0 = 0;

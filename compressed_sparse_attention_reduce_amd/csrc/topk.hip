@@ -146,7 +146,7 @@ int topk_cand_m(int n, int k, int keys_per_slot) {
     // and falls back to the exact path if a slot held more)
     if (n <= 0 || keys_per_slot <= 0) return -1;
     const double e = static_cast<double>(k) * keys_per_slot / n;
-    const int m = static_cast<int>(e + 6.0 * sqrt(e) + 4.0 + 0.999);
+    const int m = static_cast<int>(e + 4.0 * sqrt(e) + 3.0 + 0.999);
     return m + 1 <= kMaxCandM1 ? m : -1;
 }
 
