@@ -8,9 +8,14 @@ attention of 64 heads x 512 with a sink.  The 30-layer step is captured once
 in a HIP graph and replayed; every replay redoes all the work (same token
 position, so each replay rewrites the same cache slots with the same values).
 
-Prints one JSON line.  `roofline` is for the dominant kernel (the indexer
-scan), timed with HIP events on its launch stream; `cpu_baseline` is the
-float64 CPU oracle timed on the host over a bounded sample of the same step.
+Prints one JSON line.  `roofline` is for the dominant kernel, the step's
+first kernel (the indexer scan with its candidate lists and the folded SWA
+append / block compression) as the step launches it (csa_decode_step_scan),
+timed with HIP events on its launch stream; `cpu_baseline` is the float64
+CPU oracle timed on the host over a bounded sample of the same step.  The
+other workloads (tiny, ctx8k, batch128k, prefill, HCA layers, E4M3 keys,
+mixed main KV, device counters) and the oracle's timings on them are extra
+fields; `--legs` selects a subset (the headline step always runs).
 """
 
 from __future__ import annotations
@@ -32,21 +37,29 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 matrix peak, TFLOP/s
 
 
 def algorithmic_bytes(shape) -> dict:
-    """Bytes each step of one layer must move at minimum (bf16 caches)."""
+    """Bytes each step of one layer must move at minimum (element size of the
+    workload's storage type: 2 for bf16 caches, 4 for float32)."""
     N, di, hi, D, H, K, W, m = (shape.n_comp, shape.d_i, shape.h_i, shape.d, shape.h, shape.top_k,
                                 shape.w, shape.m)
-    scan = N * di * 2 + hi * di * 2 + hi * 4            # keys + q_idx + head weights
+    es = 4 if shape.dtype == "f32" else 2
+    K = min(K, N)
+    scan = N * di * es + hi * di * es + hi * 4          # keys + q_idx + head weights
     topk = K * 4 + 4                                    # indices + count
-    gather = 2 * (K + W) * D * 2                        # read + write rows
-    attn = (K + W) * D * 2 + H * D * 2 + H * 4 + H * D * 2 + H * 4  # rows, q, sink, out, lse
-    compress = (2 * m * D * 4 + m * D * 4 + D * 2) + (2 * m * di * 4 + m * di * 4 + di * 2)
-    swa = 2 * D * 2
+    gather = 2 * (K + W) * D * es                       # read + write rows
+    attn = (K + W) * D * es + H * D * es + H * 4 + H * D * es + H * 4  # rows, q, sink, out, lse
+    compress = (2 * m * D * 4 + m * D * 4 + D * es) + (2 * m * di * 4 + m * di * 4 + di * es)
+    swa = 2 * D * es
     per_layer = scan + topk + gather + attn + compress + swa
     # the standalone scan launch (csa_index_score) also writes its fp32 scores:
     # its own output, though materialising them is no part of the step's minimum
     scan_launch = scan + N * 4
+    # the step's first kernel: the scan plus the jobs folded into it (SWA
+    # append, compression of the completed block); scores and candidate lists
+    # are implementation overhead, not counted
+    step_scan_launch = scan + compress + swa
     return {"scan": scan, "topk": topk, "gather": gather, "attn": attn, "compress": compress,
-            "swa": swa, "per_layer": per_layer, "scan_launch": scan_launch}
+            "swa": swa, "per_layer": per_layer, "scan_launch": scan_launch,
+            "step_scan_launch": step_scan_launch}
 
 
 def build_layers(csa, shape, dev):
@@ -108,6 +121,62 @@ def time_scan_kernel(csa, layers, shape, reps: int):
     stream.synchronize()
     n = reps * len(layers)
     return e0.elapsed_time(e1) / n, n
+
+
+def time_step_scan(csa, layers, reps: int):
+    """Average duration of the decode step's first kernel (k_index_score_bf16
+    with candidate lists and the folded SWA append / block compression) as the
+    step launches it: csa_decode_step_scan for the 30 layers (one launch per
+    layer cache) captured back to back in a HIP graph, replayed `reps` times
+    between two HIP events on the graph's stream."""
+    import torch
+
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for ly in layers:
+                csa.csa_decode_step_scan(ly["L"], ly["io"], ly["ws"], stream=stream)
+        g.replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    stream.synchronize()
+    n = reps * len(layers)
+    return e0.elapsed_time(e1) / n, n
+
+
+def time_steady_read(csa, reps: int, gib: int = 1):
+    """Sustained HBM read rate: csa_read_probe (plain streaming loads) over a
+    `gib` GiB buffer in one launch, graph-replayed; separates the per-launch
+    ramp of a 64 MB read from the steady rate.  Returns (us, bytes)."""
+    import torch
+
+    buf = torch.ones(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            csa.csa_read_probe(buf, sink, stream=stream)
+        g.replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    stream.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = buf.numel()
+    del buf
+    torch.cuda.empty_cache()
+    return us, nbytes
 
 
 def time_read_ceiling(csa, layers, reps: int):
@@ -484,7 +553,7 @@ def time_prefill(csa, reps: int):
 
 def time_hca(csa, reps: int):
     """HCA layers at 1M context (ratio 128, 7813 compressed entries after the
-    step, window 128, 64 heads x 512): 30 independent layer caches, one
+    step, window 128, 64 heads x 512): 64 independent layer caches, one
     csa_hca_decode_step each, captured in one graph and replayed `reps`
     times; then the same over mixed main KV (the caches packed once with
     csa_pack_kv_mixed).  Returns the mean per-layer times and their
@@ -493,7 +562,9 @@ def time_hca(csa, reps: int):
     import torch
     import synth
 
-    shape = synth.SHAPES["hca1m"]
+    # 64 independent layer caches (512 MB of bf16 entries, 296 MB as mixed
+    # records) so successive layers read from HBM, not the 256 MB last-level cache
+    shape = synth.with_(synth.SHAPES["hca1m"], layers=64)
     xs = synth.make_decode_inputs_torch(shape, seed=None, device="cuda")
 
     def replay(steps):
@@ -554,9 +625,10 @@ def time_hca(csa, reps: int):
     del xs
     torch.cuda.empty_cache()
     return {
-        "workload": "hca1m: one decode token through 30 HCA layers (ratio 128, no indexer), context 1,000,064 "
+        "workload": "hca1m: one decode token through HCA layers (ratio 128, no indexer), context 1,000,064 "
                     "(7813 compressed entries incl. the one this step completes, SWA 128 with wrap), batch 1, "
-                    "main attention 64 heads x 512 bf16 with sink over every entry + the window",
+                    "main attention 64 heads x 512 bf16 with sink over every entry + the window; 64 independent "
+                    "layer caches replayed in turn (steps/s counts 30 layers)",
         "us_per_layer": round(us, 3),
         "steps_per_s_30_layers": round(1e6 / (us * 30), 1),
         "alg_bytes_per_layer": alg,
@@ -618,18 +690,153 @@ def time_batch128k(csa, reps: int, n_caches: int = 8):
     }
 
 
+def time_one_layer_config(csa, name: str, reps: int):
+    """A latency-sized decode workload (tiny: context 1024, float32; ctx8k:
+    context 8192, bf16): one layer's csa_decode_step on the workload's seeded
+    inputs, captured in a graph and replayed `reps` times (each replay redoes
+    the whole step at the same position)."""
+    import numpy as np
+    import torch
+    import synth
+
+    shape = synth.SHAPES[name]
+    x = synth.make_decode_inputs(shape, synth.seed_for(shape))
+    B, K, W, D = shape.batch, shape.top_k, shape.w, shape.d
+
+    def st(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    dt = torch.float32 if shape.dtype == "f32" else torch.bfloat16
+    L = csa.make_layer_desc(comp_kv=st(x["comp_kv"]), idx_keys=st(x["idx_keys"]), swa=st(x["swa"]),
+                            main_bias=st(x["main_bias"]), idx_bias=st(x["idx_bias"]), sink=st(x["sink"]),
+                            n_comp=x["n_comp"], swa_head=x["swa_head"], swa_len=x["swa_len"], h=shape.h,
+                            h_i=shape.h_i, top_k=K)
+    outs = dict(scores=torch.empty(B, shape.max_comp, device="cuda"),
+                topk_idx=torch.empty(B, K, dtype=torch.int32, device="cuda"),
+                topk_count=torch.empty(B, dtype=torch.int32, device="cuda"),
+                gather_buf=torch.zeros(B, K + W, D, dtype=dt, device="cuda"),
+                n_valid=torch.empty(B, dtype=torch.int32, device="cuda"),
+                out=torch.empty(B, shape.h, D, dtype=dt, device="cuda"),
+                lse=torch.empty(B, shape.h, device="cuda"))
+    io = csa.make_step_io(pos=x["pos"], q=st(x["q"]), q_idx=st(x["q_idx"]), w_idx=st(x["w_idx"]),
+                          kv_new=st(x["kv_new"]), z_main=st(x["z_main"]), c_main=st(x["c_main"]),
+                          z_idx=st(x["z_idx"]), c_idx=st(x["c_idx"]), **outs)
+    ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        csa.csa_decode_step(L, io, ws, stream=stream)
+        with torch.cuda.graph(g, stream=stream):
+            csa.csa_decode_step(L, io, ws, stream=stream)
+        g.replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    stream.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    alg = algorithmic_bytes(shape)["per_layer"] * B
+    return {
+        "us_per_step": round(us, 3),
+        "steps_per_s": round(1e6 / us, 1),
+        "alg_bytes_per_step": alg,
+        "achieved_gbps": round(alg / (us * 1e-6) / 1e9, 1),
+        "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "bound": "latency (the caches fit the last-level cache)",
+    }
+
+
+def host_info() -> dict:
+    """The host the CPU oracle runs on: CPU model, usable cores, BLAS threads."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")} for i in threadpool_info()]
+    except Exception:  # pragma: no cover
+        pass
+    cores = len(os.sched_getaffinity(0))
+    threads = max([b["threads"] or 1 for b in blas] + [1])
+    return {"cpu_model": model, "cores_available": cores, "blas": blas, "threads_used": min(threads, cores)}
+
+
+def cpu_configs(budget_s: float) -> dict:
+    """The float64 CPU oracle (a correctness reference, not a tuned CPU
+    implementation) timed on this host on the other workloads, each on a
+    bounded sample of its own seeded inputs: the tiny and ctx8k steps whole;
+    one of batch128k's eight sequences (they are independent; the layer
+    step is eight of them); eight query rows of the prefill chunk (its last
+    eight, positions 262136..262143; every row scores all 65,536 blocks, so
+    the chunk is 256 such samples)."""
+    import numpy as np
+    import oracle
+    import synth
+    from oracle import numfmt
+
+    f = numfmt.bf16_bits_to_f64
+
+    def val(a):
+        return f(a) if a.dtype == np.uint16 else np.asarray(a, dtype=np.float64)
+
+    def one_step(shape, seed, b=0):
+        x = synth.make_decode_inputs(shape, seed)
+        rnd = numfmt.bf16_round_f64 if shape.dtype == "bf16" else None
+        st = oracle.LayerState(comp_kv=val(x["comp_kv"][b]), idx_keys=val(x["idx_keys"][b]), n_comp=x["n_comp"],
+                               swa=oracle.SwaRing(val(x["swa"][b]), x["swa_head"], x["swa_len"]),
+                               main_bias=val(x["main_bias"]), idx_bias=val(x["idx_bias"]), sink=val(x["sink"]),
+                               round_cache=rnd)
+        t0 = time.perf_counter()
+        oracle.decode_step(st, q=val(x["q"][b]), q_idx=val(x["q_idx"][b]), w_idx=val(x["w_idx"][b]),
+                           kv_new=val(x["kv_new"][b]), pos=x["pos"], top_k=shape.top_k, z_main=x["z_main"][b],
+                           c_main=x["c_main"][b], z_idx=x["z_idx"][b], c_idx=x["c_idx"][b],
+                           scale=1.0 / np.sqrt(shape.d))
+        return time.perf_counter() - t0
+
+    res = {"note": "float64 numpy oracle; a correctness reference, not a tuned CPU implementation"}
+    res.update(host_info())
+    t = one_step(synth.SHAPES["tiny"], synth.seed_for(synth.SHAPES["tiny"]))
+    res["tiny"] = {"s_per_step": round(t, 4), "steps_per_s": round(1 / t, 2), "sample": "one whole step"}
+    t = one_step(synth.SHAPES["ctx8k"], synth.seed_for(synth.SHAPES["ctx8k"]))
+    res["ctx8k"] = {"s_per_step": round(t, 4), "steps_per_s": round(1 / t, 2), "sample": "one whole step"}
+    b1 = synth.with_(synth.SHAPES["batch128k"], batch=1)
+    t = one_step(b1, synth.seed_for(synth.SHAPES["batch128k"]))
+    res["batch128k"] = {"s_per_layer_step": round(8 * t, 3), "layer_steps_per_s": round(1 / (8 * t), 3),
+                        "sample": f"one sequence's step ({t:.3f} s) x 8 sequences"}
+    if budget_s > 0:
+        sh = synth.with_(synth.SHAPES["prefill"], t=8)
+        x = synth.make_prefill_inputs(sh, synth.seed_for(synth.SHAPES["prefill"]))
+        t0 = time.perf_counter()
+        oracle.prefill_chunk(q=val(x["q"]), q_idx=val(x["q_idx"]), w_idx=x["w_idx"], idx_keys=val(x["idx_keys"]),
+                             comp_kv=val(x["comp_kv"]), win_kv=val(x["win_kv"]), pos0=x["pos0"], top_k=sh.top_k,
+                             window=sh.w, sink=x["sink"], scale=1.0 / np.sqrt(sh.d))
+        t = time.perf_counter() - t0
+        res["prefill"] = {"s_per_chunk": round(t * 2048 / 8, 2), "queries_per_s": round(8 / t, 1),
+                          "sample": f"8 of 2048 query rows ({t:.2f} s) x 256"}
+    return res
+
+
 def cpu_baseline(layers, shape, budget_s: float):
-    """The float64 oracle on the host, layer by layer, until the budget is spent."""
+    """The float64 oracle on the host, layer by layer of the 1M-context step,
+    until the budget is spent.  Converting a layer's caches to float64 on the
+    host (outside the timed region) is reported separately."""
     import numpy as np
     import oracle
     from oracle import numfmt
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    cores = len(os.sched_getaffinity(0))
+    info = host_info()
 
     def f64(t):
         import torch
@@ -637,32 +844,36 @@ def cpu_baseline(layers, shape, budget_s: float):
             return numfmt.bf16_bits_to_f64(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
         return t.cpu().numpy().astype(np.float64)
 
-    times = []
+    times, prep = [], []
     for ly in layers:
         x = ly["x"]
+        p0 = time.perf_counter()
         st = oracle.LayerState(comp_kv=f64(x["comp_kv"][0]), idx_keys=f64(x["idx_keys"][0]),
-                               n_comp=x["n_comp"] - 0, swa=oracle.SwaRing(f64(x["swa"][0]), x["swa_head"],
-                                                                        x["swa_len"]),
+                               n_comp=x["n_comp"], swa=oracle.SwaRing(f64(x["swa"][0]), x["swa_head"],
+                                                                      x["swa_len"]),
                                main_bias=f64(x["main_bias"]), idx_bias=f64(x["idx_bias"]),
                                sink=f64(x["sink"]), round_cache=numfmt.bf16_round_f64)
-        # the GPU step already wrote this step's block into the caches; the
-        # oracle recomputes it into the same slot
-        st.n_comp = x["n_comp"]
         args = dict(q=f64(x["q"][0]), q_idx=f64(x["q_idx"][0]), w_idx=f64(x["w_idx"][0]),
                     kv_new=f64(x["kv_new"][0]), pos=x["pos"], top_k=shape.top_k,
                     z_main=f64(x["z_main"][0]), c_main=f64(x["c_main"][0]), z_idx=f64(x["z_idx"][0]),
                     c_idx=f64(x["c_idx"][0]), scale=1.0 / np.sqrt(shape.d))
+        prep.append(time.perf_counter() - p0)
         t0 = time.perf_counter()
         oracle.decode_step(st, **args)
         times.append(time.perf_counter() - t0)
         del st
-        if sum(times) > budget_s:
+        if sum(times) + sum(prep) > budget_s:
             break
     per_layer = sum(times) / len(times)
-    return {"value": 1.0 / (per_layer * shape.layers), "unit": "steps/s", "cores": min(threads, cores),
+    return {"value": 1.0 / (per_layer * shape.layers), "unit": "steps/s", "cores": info["threads_used"],
             "kind": "oracle",
             "sample": f"{len(times)} of {shape.layers} layers of one decode step at n_comp={shape.n_comp} "
-                      f"(float64 numpy oracle, mean {per_layer:.3f} s/layer; steps/s = 1/(30 x mean))"}
+                      f"(float64 numpy oracle, mean {per_layer:.3f} s/layer; steps/s = 1/(30 x mean)); "
+                      f"host prep outside the timed region (caches to float64) {sum(prep) / len(prep):.2f} s/layer",
+            "cpu_model": info["cpu_model"], "cores_available": info["cores_available"], "blas": info["blas"]}
+
+
+LEGS = ("main", "fp8", "mixed", "dev", "configs", "prefill", "hca", "batch", "cpu")
 
 
 def main() -> int:
@@ -673,10 +884,17 @@ def main() -> int:
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--scan-reps", type=int, default=10)
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help="comma-separated subset of " + ",".join(LEGS) + " (the headline step always runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode path runs "
               "on a single MI355X (multi-GPU sharding is not implemented)", file=sys.stderr)
+        return 2
+    legs = set(x.strip() for x in args.legs.split(",") if x.strip())
+    bad = legs - set(LEGS)
+    if bad:
+        print(f"unknown legs {sorted(bad)}", file=sys.stderr)
         return 2
 
     import torch
@@ -735,27 +953,16 @@ def main() -> int:
     ms_per_step = e0.elapsed_time(e1) / args.steps
     assert torch.equal(layers[0]["outs"]["out"], ref_out), "timed replays differ from eager"
 
+    ab = algorithmic_bytes(shape)
+    # the dominant kernel as the step launches it, then the standalone scan and the read ceilings
+    step_scan_ms, step_scan_launches = time_step_scan(csa, layers, args.scan_reps)
+    step_scan_gbs = ab["step_scan_launch"] / (step_scan_ms * 1e-3) / 1e9
     scan_ms, scan_launches = time_scan_kernel(csa, layers, shape, args.scan_reps)
+    scan_gbs = ab["scan_launch"] / (scan_ms * 1e-3) / 1e9
     ceil_us, ceil_bytes = time_read_ceiling(csa, layers, args.scan_reps)
     ceil_gbs = ceil_bytes / (ceil_us * 1e-6) / 1e9
-    ab = algorithmic_bytes(shape)
-    scan_gbs = ab["scan_launch"] / (scan_ms * 1e-3) / 1e9
     step_bytes = ab["per_layer"] * shape.layers
     step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-
-    fp8_ms, fp8_bytes, fp8_step_ms = time_fp8(csa, layers, shape, args.scan_reps, max(20, args.steps // 2))
-    fp8_gbs = fp8_bytes / (fp8_ms * 1e-3) / 1e9
-    mixed_ms = time_mixed_kv(csa, layers, shape, max(20, args.steps // 2))
-    dev_ms = time_dev_step(csa, layers, shape, max(20, args.steps // 2), 4)
-
-    cpu = None
-    if args.cpu_budget > 0:
-        cpu = cpu_baseline(layers, shape, args.cpu_budget)
-    del layers  # the 1M-context caches make room for the prefill workload
-    torch.cuda.empty_cache()
-    prefill = time_prefill(csa, max(2, args.scan_reps // 2))
-    hca = time_hca(csa, args.scan_reps)
-    batch = time_batch128k(csa, max(10, args.steps // 4))
 
     res = {
         "metric": "CSA decode steps/s and indexer-scan HBM GB/s at 1M ctx (250K comp entries)",
@@ -777,28 +984,44 @@ def main() -> int:
             "layers": shape.layers, "n_comp": shape.n_comp, "top_k": shape.top_k,
             "swa": shape.w, "batch": shape.batch, "mode": args.mode,
         },
-        "scan_gbps": round(scan_gbs, 1),
+        "scan_gbps": round(step_scan_gbs, 1),
         "step_gbps": round(step_gbs, 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "step_alg_bytes": step_bytes,
         "eager_ms_per_step": round(eager_ms, 4),
         "wall_ms_timed": round(wall_ms, 2),
         "roofline": {
-            "kernel": "k_index_score_bf16",
+            "kernel": "k_index_score_bf16<true> (the decode step's first kernel: scan with candidate lists, "
+                      "SWA append and block compression folded in)",
             "bound": "hbm",
-            "achieved": round(scan_gbs, 1),
+            "achieved": round(step_scan_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
+            "frac": round(step_scan_gbs / HBM_PEAK_GBS, 4),
             "traffic": scan_traffic(),
-            "alg_bytes_per_launch": ab["scan_launch"],
-            "avg_launch_us": round(scan_ms * 1e3, 3),
-            "launches_timed": scan_launches,
-            # context: a plain streaming read of the same caches, one launch each
+            "alg_bytes_per_launch": ab["step_scan_launch"],
+            "avg_launch_us": round(step_scan_ms * 1e3, 3),
+            "launches_timed": step_scan_launches,
+            "standalone_scan": {
+                "kernel": "k_index_score_bf16<false> (csa_index_score: scores only, no lists, no jobs)",
+                "avg_launch_us": round(scan_ms * 1e3, 3),
+                "alg_bytes_per_launch": ab["scan_launch"],
+                "achieved_gbps": round(scan_gbs, 1),
+                "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
+            },
+            # context: plain streaming reads, one launch per 64 MB cache, and one 1 GiB launch
             "read_ceiling_gbps": round(ceil_gbs, 1),
             "read_ceiling_us": round(ceil_us, 3),
-            "frac_of_read_ceiling": round(scan_gbs / ceil_gbs, 4),
+            "frac_of_read_ceiling": round(step_scan_gbs / ceil_gbs, 4),
         },
-        "fp8_scan": {
+    }
+    sr_us, sr_bytes = time_steady_read(csa, max(3, args.scan_reps // 2))
+    res["roofline"]["steady_read_gbps_1gib"] = round(sr_bytes / (sr_us * 1e-6) / 1e9, 1)
+
+    if "fp8" in legs:
+        fp8_ms, fp8_bytes, fp8_step_ms = time_fp8(csa, layers, shape, args.scan_reps, max(20, args.steps // 2))
+        fp8_gbs = fp8_bytes / (fp8_ms * 1e-3) / 1e9
+        res["fp8_scan"] = {
             "kernel": "k_index_score_fp8",
             "avg_launch_us": round(fp8_ms * 1e3, 3),
             "alg_bytes_per_launch": fp8_bytes,
@@ -806,25 +1029,46 @@ def main() -> int:
             "frac": round(fp8_gbs / HBM_PEAK_GBS, 4),
             "decode_steps_per_s": round(1e3 / fp8_step_ms, 2),
             "decode_ms_per_step": round(fp8_step_ms, 5),
-        },
-        "device_counters": {
-            "workload": "ctx1m decode step as above through csa_decode_step_dev: one graph replayed, each replay "
-                        "the next token (positions, block completions and the SWA ring advanced on the device)",
-            "decode_steps_per_s": round(1e3 / dev_ms, 2),
-            "decode_ms_per_step": round(dev_ms, 5),
-        },
-        "mixed_kv": {
+            "decode_note": "the step takes the bf16 query and quantises it in its scan workgroups",
+        }
+    if "mixed" in legs:
+        mixed_ms = time_mixed_kv(csa, layers, shape, max(20, args.steps // 2))
+        res["mixed_kv"] = {
             "workload": "ctx1m decode step as above with mixed main KV: every compressed entry and window row "
                         "a 592-byte record (448 E4M3 NoPE codes + scale, 64 bf16 RoPE values), RoPE on the new "
                         "entry, inverse RoPE on the output",
             "decode_steps_per_s": round(1e3 / mixed_ms, 2),
             "decode_ms_per_step": round(mixed_ms, 5),
-        },
-        "prefill": prefill,
-        "hca": hca,
-        "batch128k": batch,
-        "cpu_baseline": cpu,
-    }
+        }
+    if "dev" in legs:
+        dev_ms = time_dev_step(csa, layers, shape, max(20, args.steps // 2), 4)
+        res["device_counters"] = {
+            "workload": "ctx1m decode step as above through csa_decode_step_dev: one graph replayed, each replay "
+                        "the next token (positions, block completions and the SWA ring advanced on the device)",
+            "decode_steps_per_s": round(1e3 / dev_ms, 2),
+            "decode_ms_per_step": round(dev_ms, 5),
+        }
+    cpu = None
+    if "cpu" in legs and args.cpu_budget > 0:
+        cpu = cpu_baseline(layers, shape, args.cpu_budget)
+    del layers  # the 1M-context caches make room for the other workloads
+    torch.cuda.empty_cache()
+    if "configs" in legs:
+        res["tiny"] = dict(workload="tiny: context 1024 (n_comp 256), batch 1, float32, indexer 64x128, top_k 64, "
+                                    "SWA 128, main attention 16 heads x 128 with sink",
+                           **time_one_layer_config(csa, "tiny", max(50, args.steps)))
+        res["ctx8k"] = dict(workload="ctx8k: context 8192 (n_comp 2048), batch 1, bf16, indexer 64x128, top_k 512, "
+                                     "SWA 128 (gather_buf 640 x 512), main attention 64 heads x 512 with sink",
+                            **time_one_layer_config(csa, "ctx8k", max(50, args.steps)))
+    if "prefill" in legs:
+        res["prefill"] = time_prefill(csa, max(2, args.scan_reps // 2))
+    if "hca" in legs:
+        res["hca"] = time_hca(csa, args.scan_reps)
+    if "batch" in legs:
+        res["batch128k"] = time_batch128k(csa, max(10, args.steps // 4))
+    if "cpu" in legs and args.cpu_budget > 0:
+        res["cpu_other_configs"] = cpu_configs(args.cpu_budget)
+    res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
     return 0
 

@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     csa_decode_step,
     csa_decode_step_workspace_size,
     csa_decode_step_noalloc,
+    csa_decode_step_scan,
+    csa_decode_step_attend,
     csa_decode_step_noalloc_max_bytes,
     csa_gather,
     csa_hca_decode_step,

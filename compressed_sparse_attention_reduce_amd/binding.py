@@ -95,6 +95,8 @@ _SIGS = {
                              _ll, _vp, _sz, _vp]),
     "csa_decode_step_workspace_size": (_sz, [ctypes.POINTER(LayerDesc)]),
     "csa_decode_step": (_i, [ctypes.POINTER(LayerDesc), ctypes.POINTER(StepIO), _vp, _sz, _vp]),
+    "csa_decode_step_scan": (_i, [ctypes.POINTER(LayerDesc), ctypes.POINTER(StepIO), _vp, _sz, _vp]),
+    "csa_decode_step_attend": (_i, [ctypes.POINTER(LayerDesc), ctypes.POINTER(StepIO), _vp, _sz, _vp]),
     "csa_decode_step_noalloc_max_bytes": (_sz, []),
     "csa_decode_step_noalloc": (_i, [ctypes.POINTER(LayerDesc), ctypes.POINTER(StepIO), _vp]),
     "csa_layer_advance": (_i, [ctypes.POINTER(LayerDesc), _i]),
@@ -309,6 +311,18 @@ def csa_decode_step_workspace_size(layer: LayerDesc) -> int:
 def csa_decode_step(layer: LayerDesc, io: StepIO, ws, stream=None) -> None:
     _check(lib().csa_decode_step(ctypes.byref(layer), ctypes.byref(io), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def csa_decode_step_scan(layer: LayerDesc, io: StepIO, ws, stream=None) -> None:
+    """The first part of csa_decode_step (jobs + scan with candidates)."""
+    _check(lib().csa_decode_step_scan(ctypes.byref(layer), ctypes.byref(io), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def csa_decode_step_attend(layer: LayerDesc, io: StepIO, ws, stream=None) -> None:
+    """The rest of csa_decode_step (top-k, gather, attention), after csa_decode_step_scan."""
+    _check(lib().csa_decode_step_attend(ctypes.byref(layer), ctypes.byref(io), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def csa_decode_step_noalloc_max_bytes() -> int:

@@ -344,10 +344,17 @@ size_t csa_decode_step_dev_ring_size(const csa_layer_desc* L) {
     return sizeof(float) * static_cast<size_t>(L->batch) * 4 * L->m * (wm + wi);
 }
 
+// Which kernels of the step an entry point enqueues: all of them, or the
+// first (jobs + scan) or the rest (top-k + gather + attention) of the
+// two-call form.  Both calls validate everything and size every launch the
+// same way, so their candidate slots agree.
+enum StepPhase { kStepAll = 0, kStepScan = 1, kStepAttend = 2 };
+
 // The decode step; dev != nullptr: the counters are read from and advanced
 // on the device (csa_decode_step_dev), the block rows kept in `ring`.
 static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes,
-                       csa_stream stream, csa::DevState* dev, float* ring, size_t ring_bytes) {
+                       csa_stream stream, csa::DevState* dev, float* ring, size_t ring_bytes,
+                       StepPhase phase = kStepAll) {
     CHECK(L && io, "csa_decode_step: null layer or io");
     CHECK(dtype_ok(L->dtype) && dtype_ok(L->out_dtype), "csa_decode_step: bad dtype");
     CHECK(L->batch >= 1 && L->m >= 1 && L->w >= 1 && L->top_k >= 1 && L->top_k <= csa::kTopkMaxK,
@@ -500,7 +507,9 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
     // scores the new key itself); the float32 path launches them first.
     const int n_scan = dev ? L->max_comp : (bf ? L->n_comp : N);
     const int prep_wgs = bf ? (completes ? 3 : 1) : 0;
-    if (!bf) {
+    const bool do_scan = phase != kStepAttend;
+    const bool do_rest = phase != kStepScan;
+    if (!bf && do_scan) {
         e = csa::launch_step_prep(pa, s);
         if (e != hipSuccess) return launched(e, "csa_decode_step/prep");
     }
@@ -522,7 +531,9 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
     csa::ScoreArgs sa{io->q_idx, io->w_idx, L->idx_keys, io->scores, L->batch, 1, L->h_i, L->d_i, n_scan,
                       nullptr, L->m, io->q_idx_stride_b, io->w_stride_b, L->idx_keys_stride_b,
                       io->scores_stride_b, N, ca, dev};
-    if (fp8) {
+    if (!do_scan) {
+        e = hipSuccess;
+    } else if (fp8) {
         const csa::Fp8ScoreArgs fa{static_cast<const uint8_t*>(io->q_idx), io->w_idx,
                                    static_cast<const uint8_t*>(L->idx_keys), L->idx_scales, io->scores,
                                    L->batch, 1, n_scan, nullptr, L->m, 2 * io->q_idx_stride_b, io->w_stride_b,
@@ -533,6 +544,7 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
         e = bf ? csa::launch_index_score_bf16(sa, &pa, s) : csa::launch_index_score_f32(sa, s);
     }
     if (e != hipSuccess) return launched(e, "csa_decode_step/index_score");
+    if (!do_rest) return ok();
     csa::TopkArgs ta{io->scores, L->batch, 1, N, N, io->scores_stride_b, L->top_k, io->topk_idx,
                      io->topk_count, tws};
     // bf16 with candidate lists (or a short row): every attention workgroup
@@ -613,6 +625,16 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
 int csa_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes,
                     csa_stream stream) {
     return decode_step(L, io, ws, ws_bytes, stream, nullptr, nullptr, 0);
+}
+
+int csa_decode_step_scan(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes,
+                         csa_stream stream) {
+    return decode_step(L, io, ws, ws_bytes, stream, nullptr, nullptr, 0, kStepScan);
+}
+
+int csa_decode_step_attend(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes,
+                           csa_stream stream) {
+    return decode_step(L, io, ws, ws_bytes, stream, nullptr, nullptr, 0, kStepAttend);
 }
 
 }  // extern "C"

@@ -351,6 +351,28 @@ int csa_decode_step(const csa_layer_desc *layer, const csa_step_io *io, void *ws
                     size_t ws_bytes, csa_stream stream);
 
 /* ------------------------------------------------------------------------
+ * 6f. The decode step in two calls.
+ *
+ * Source: as section 6 (page 2, single_shot_inference.py, eager_attention):
+ * the step's first part reads the new token's inputs and the indexer keys,
+ * its second part the selected compressed rows and the window.
+ *
+ * csa_decode_step_scan enqueues steps a and b and the index score of step c
+ * (one kernel on the bfloat16 paths: the SWA append, the compression of a
+ * completed block, the scan over every key with each workgroup's top-k
+ * candidates written to the workspace); csa_decode_step_attend enqueues the
+ * rest of step c (top-k, gather, attention).  Called in that order on one
+ * stream with the same layer, io and workspace (the candidates pass through
+ * it), they do exactly what one csa_decode_step call does, with the same
+ * validation and errors.  Independent work may be enqueued between them; the
+ * workspace must not be touched in between.
+ * ------------------------------------------------------------------------ */
+int csa_decode_step_scan(const csa_layer_desc *layer, const csa_step_io *io, void *ws,
+                         size_t ws_bytes, csa_stream stream);
+int csa_decode_step_attend(const csa_layer_desc *layer, const csa_step_io *io, void *ws,
+                           size_t ws_bytes, csa_stream stream);
+
+/* ------------------------------------------------------------------------
  * 6e. The decode step with no workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc).

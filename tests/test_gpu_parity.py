@@ -969,3 +969,66 @@ def test_fp8_scans_decode_every_code_pair(csa):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(s1[0].cpu().numpy().astype(np.float64), want)
     np.testing.assert_array_equal(s2[:, 0].cpu().numpy().astype(np.float64), want)
+
+
+SPLIT_CASES = [
+    # name, shape, fp8 keys
+    ("ctx8k_bf16", synth.with_(synth.SHAPES["ctx8k"], n_comp=2048, ctx=8192), False),
+    ("batch5_split_topk", synth.with_(synth.SHAPES["ctx8k"], batch=5, n_comp=3000, ctx=12000), False),
+    ("tiny_f32", synth.SHAPES["tiny"], False),
+    ("ctx8k_fp8_keys", synth.with_(synth.SHAPES["ctx8k"], n_comp=2048, ctx=8192), True),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_decode_step_two_calls_equal_one(csa, case):
+    """csa_decode_step_scan then csa_decode_step_attend (the step's two parts,
+    on one stream, one workspace) give bit for bit what csa_decode_step
+    gives: scores, top-k, gather_buf, output, lse and the cache writes."""
+    name, shape, fp8 = case
+    x = synth.make_decode_inputs(shape, 9301 + len(name))
+    B, K, W, D = shape.batch, shape.top_k, shape.w, shape.d
+    res = []
+    for split in (False, True):
+        st = dev_store
+        comp, swa = st(x["comp_kv"]), st(x["swa"])
+        if fp8:
+            kc, ks = numfmt.quantize_e4m3_rows(as_f64(x["idx_keys"]).reshape(-1, shape.d_i).astype(np.float32))
+            keys = torch.from_numpy(kc.reshape(B, -1, shape.d_i)).to(DEV)
+            scales = dev_f32(ks.reshape(B, -1))
+        else:
+            keys, scales = st(x["idx_keys"]), None
+        L = csa.make_layer_desc(comp_kv=comp, idx_keys=keys, idx_scales=scales, swa=swa,
+                                main_bias=dev_f32(x["main_bias"]), idx_bias=dev_f32(x["idx_bias"]),
+                                sink=dev_f32(x["sink"]), n_comp=x["n_comp"], swa_head=x["swa_head"],
+                                swa_len=x["swa_len"], h=shape.h, h_i=shape.h_i, top_k=K)
+        dt = torch.float32 if shape.dtype == "f32" else torch.bfloat16
+        outs = dict(scores=torch.full((B, shape.max_comp), 5.0, device=DEV),
+                    topk_idx=torch.full((B, K), -3, dtype=torch.int32, device=DEV),
+                    topk_count=torch.full((B,), -3, dtype=torch.int32, device=DEV),
+                    gather_buf=torch.zeros(B, K + W, D, dtype=dt, device=DEV),
+                    n_valid=torch.full((B,), -3, dtype=torch.int32, device=DEV),
+                    out=torch.zeros(B, shape.h, D, dtype=dt, device=DEV), lse=torch.zeros(B, shape.h, device=DEV))
+        io = csa.make_step_io(pos=x["pos"], q=st(x["q"]), q_idx=st(x["q_idx"]), w_idx=dev_f32(x["w_idx"]),
+                              kv_new=st(x["kv_new"]), z_main=dev_f32(x["z_main"]), c_main=dev_f32(x["c_main"]),
+                              z_idx=dev_f32(x["z_idx"]), c_idx=dev_f32(x["c_idx"]), **outs)
+        ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+        print(f"two-call step {name}: split={split}", flush=True)
+        if split:
+            csa.csa_decode_step_scan(L, io, ws)
+            csa.csa_decode_step_attend(L, io, ws)
+        else:
+            csa.csa_decode_step(L, io, ws)
+        torch.cuda.synchronize()
+        res.append((outs, comp, keys, scales, swa))
+    (o1, *c1), (o2, *c2) = res
+    N = shape.n_comp
+    assert torch.equal(o1["scores"][:, :N], o2["scores"][:, :N])
+    for k in ("topk_idx", "topk_count", "n_valid", "out", "lse"):
+        assert torch.equal(o1[k], o2[k]), k
+    nv = int(o1["n_valid"].min())
+    assert nv == min(K, N) + W
+    assert torch.equal(o1["gather_buf"][:, :nv], o2["gather_buf"][:, :nv])
+    for a, b in zip(c1, c2):
+        if a is not None:
+            assert torch.equal(a, b)
