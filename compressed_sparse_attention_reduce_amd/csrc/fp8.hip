@@ -92,8 +92,8 @@ __device__ inline float score_one_key_fp8(const Fp8ScoreArgs& a, int b, int tt, 
     float wh = a.w[b * a.w_stride_b + static_cast<long long>(tt) * kHeads + h];
     float dot = 0.f;
     if (a.q_raw) {
-        // bfloat16 query: the head row quantised here (quantise_head_row's
-        // rule over the four lanes of the head), its scale folded into wh
+        // bfloat16 query: the head row quantised as the scan quantises it (the
+        // row maximum over the head's four lanes), its scale folded into wh
         const uint16_t* qh = a.q_raw + b * a.q_raw_stride_b + (static_cast<long long>(tt) * kHeads + h) * kDi + kPer * part;
         float x[kPer];
 #pragma unroll
@@ -111,10 +111,14 @@ __device__ inline float score_one_key_fp8(const Fp8ScoreArgs& a, int b, int tt, 
         for (int e = 0; e < kPer; ++e) amax = fmaxf(amax, fabsf(x[e]));
         amax = fmaxf(amax, xor_lanes_f32<1>(amax));
         amax = fmaxf(amax, xor_lanes_f32<2>(amax));
-        const float qscale = amax > 0.f ? amax / 448.0f : 1.0f;
+        const E4m3Row rs = e4m3_row(amax);
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) dot += e4m3_decode(e4m3_encode_rne(x[e] / qscale)) * key[kPer * part + e];
-        wh = wh * qscale;
+        for (int e = 0; e < kPer; e += 2) {
+            const uint32_t c2 = e4m3_encode2(e4m3_quot(x[e], rs), e4m3_quot(x[e + 1], rs));
+            dot += e4m3_decode(c2 & 0xffu) * key[kPer * part + e];
+            dot += e4m3_decode(c2 >> 8) * key[kPer * part + e + 1];
+        }
+        wh = wh * rs.s;
     } else {
         const uint8_t* qh = a.q + b * a.q_stride_b + (static_cast<long long>(tt) * kHeads + h) * kDi + kPer * part;
 #pragma unroll
@@ -250,15 +254,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
             amax = fmaxf(amax, xor_lanes_f32<2>(amax));
             amax = fmaxf(amax, xor_lanes_f32<4>(amax));
             amax = fmaxf(amax, xor_lanes_f32<8>(amax));
-            const float qscale = amax > 0.f ? amax / 448.0f : 1.0f;
-            uint32_t lo = 0, hi = 0;
+            const E4m3Row rs = e4m3_row(amax);
+            float y[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                lo |= static_cast<uint32_t>(e4m3_encode_rne(x[e] / qscale)) << (8 * e);
-                hi |= static_cast<uint32_t>(e4m3_encode_rne(x[4 + e] / qscale)) << (8 * e);
-            }
+            for (int e = 0; e < 8; ++e) y[e] = e4m3_quot(x[e], rs);
+            const uint32_t lo = e4m3_encode2(y[0], y[1]) | (e4m3_encode2(y[2], y[3]) << 16);
+            const uint32_t hi = e4m3_encode2(y[4], y[5]) | (e4m3_encode2(y[6], y[7]) << 16);
             *reinterpret_cast<uint2*>(qs + (c / 16) * kQPitch + (c % 16) * 8) = make_uint2(lo, hi);
-            if ((c & 15) == 0) qsc[c / 16] = qscale;
+            if ((c & 15) == 0) qsc[c / 16] = rs.s;
         }
     } else {
         auto qstage = [&](int c, const uint4& v) {

@@ -40,6 +40,41 @@ __device__ inline uint8_t e4m3_encode_rne(float y) {
     return static_cast<uint8_t>(sign | m);
 }
 
+// A row's E4M3 scale (s = amax / 448, 1 for an all-zero row) and what the
+// fast quotient below needs: y = 1 / s (both binary32, correctly rounded).
+struct E4m3Row {
+    float s, y;
+    bool recip;  // the reciprocal form is exact for this row
+};
+__device__ inline E4m3Row e4m3_row(float amax) {
+    E4m3Row r;
+    r.s = amax > 0.f ? amax / 448.0f : 1.0f;
+    r.y = 1.0f / r.s;
+    r.recip = amax >= 0x1p-90f || amax == 0.f;
+    return r;
+}
+// RN(x / s) for a bfloat16 value x of the row (|x| <= amax): q = RN(x y),
+// then one correction with the exact residual x - s q (Markstein's theorem
+// for a correctly rounded reciprocal).  It equals the binary32 division for
+// every pair of bfloat16 x and bfloat16 amax >= 2^-90 (an exhaustive host
+// check of all 1.06e9 pairs); smaller rows take the division, where the
+// residual could underflow.  The quotient has x's sign (also for -0).
+__device__ inline float e4m3_quot(float x, const E4m3Row& r) {
+    if (!r.recip) return x / r.s;
+    float q = x * r.y;
+    const float res = __builtin_fmaf(-r.s, q, x);
+    q = __builtin_fmaf(res, r.y, q);
+    return __builtin_copysignf(q, x);
+}
+// Codes of two quotients by the conversion instruction (round to nearest
+// even): equal to e4m3_encode_rne for every binary32 value of magnitude up
+// to 448.0001 (all 2.28e9 of them compared on gfx950), which covers every
+// x / s of a row (at most 448 / (1 - 2^-24)).  The low byte is a's code,
+// the next b's.
+__device__ inline uint32_t e4m3_encode2(float a, float b) {
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xffffu;
+}
+
 // The exact value of an E4M3 code (never NaN here: the encoder saturates).
 __device__ inline float e4m3_decode(uint32_t c) {
     const uint32_t e = (c >> 3) & 15u;

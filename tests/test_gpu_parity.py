@@ -823,6 +823,16 @@ def test_decode_step_ctx1m_fp8_keys_full_size(csa):
     ref_s = oracle.index_score_fp8(qc, w8, codes, scales)[0]
     got_s = outs["scores"][0, :N].cpu().numpy().astype(np.float64)
     assert rel_err(got_s, ref_s) <= 1e-4
+    # the step's own query quantisation is the host's bit for bit: the
+    # standalone FP8 scan over the host's codes and folded weights gives the
+    # step's scores exactly for every key the scan covered (the new key is
+    # scored apart, by the workgroup that quantised it)
+    s8 = torch.empty(1, 1, N, device=DEV)
+    csa.csa_index_score_fp8(torch.from_numpy(qc[None]).to(DEV), dev_f32(w8[None]), kc[:, :N], ks[:, :N], s8)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(s8[0, 0, :n0].cpu().numpy().view(np.uint32),
+                                  outs["scores"][0, :n0].cpu().numpy().view(np.uint32))
+    assert abs(float(s8[0, 0, n0]) - got_s[n0]) <= 1e-5 * np.abs(got_s).max()
     gi = outs["topk_idx"][0].cpu().numpy()
     oi, _ = oracle.topk(got_s[None], K)
     np.testing.assert_array_equal(gi, oi[0])
