@@ -22,6 +22,7 @@ from .csa import (
     kv_norm,
     mixed_kv_row,
     prefill_chunk,
+    rescored_topk,
     rope_rotate,
     sparse_attn,
     topk,
@@ -36,6 +37,7 @@ __all__ = [
     "index_score",
     "index_score_fp8",
     "topk",
+    "rescored_topk",
     "gather",
     "sparse_attn",
     "SwaRing",

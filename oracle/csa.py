@@ -28,6 +28,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
+    "rescored_topk",
     "compress",
     "kv_norm",
     "index_score",
@@ -240,6 +241,36 @@ def topk(scores, k: int):
     return idx, count
 
 
+def rescored_topk(scores_fp8, scores_exact, k: int, k_cand: int):
+    """Two-stage selection of an E4M3 indexer whose recall must meet the exact
+    one's (reading R29: page 1, ``ARCHITECTURE_AND_MEMORY_AUDIT.md``, the
+    recall test of Tier 1, gate 4, against an exact-score reference, with the
+    keys kept as FP8_E4M3 for the FP8 scoring path of page 1,
+    ``single_shot_inference.py``, "B2").
+
+    Stage 1: the ``k_cand`` best entries of each row by ``scores_fp8``
+    (:func:`topk`'s rules).  Stage 2: of those, the ``k`` best by
+    ``scores_exact`` (same rules: score descending, lower index first).
+    ``scores_exact`` need only be meaningful at the stage-1 entries.  Returns
+    ``idx [T, k]`` (unused slots -1) and ``count [T]`` = ``min(k, stage-1
+    count)``, like :func:`topk`.
+    """
+    e = np.asarray(scores_exact, dtype=np.float64)
+    if e.ndim == 1:
+        e = e[None, :]
+    cand, ccount = topk(scores_fp8, k_cand)
+    T = cand.shape[0]
+    idx = np.full((T, k), -1, dtype=np.int32)
+    count = np.zeros(T, dtype=np.int32)
+    for t in range(T):
+        c = cand[t, :ccount[t]].astype(np.int64)
+        order = c[np.lexsort((c, -e[t, c]))]
+        k_eff = min(k, c.size)
+        idx[t, :k_eff] = order[:k_eff]
+        count[t] = k_eff
+    return idx, count
+
+
 # ---------------------------------------------------------------------------
 # (4) gather into gather_buf
 # ---------------------------------------------------------------------------
@@ -429,6 +460,12 @@ class LayerState:
     # get RoPE from the comp tables at their block index, the output inverse
     # RoPE from the token tables at the token's position.  Tables:
     # [rows, rope_dim / 2].
+    # Recall-restored E4M3 keys (reading R29): with ``fp8_rescore`` = k_cand
+    # > 0 the layer keeps its keys twice, as codes (``idx_codes`` /
+    # ``idx_scales``) and in ``idx_keys`` (rounded by ``round_cache``), and
+    # the top-k is :func:`rescored_topk` of the E4M3 scores and the exact
+    # scores over ``idx_keys``
+    fp8_rescore: int = 0
     kv_mixed: bool = False
     rope_dim: int = 64
     rope_cos: Optional[np.ndarray] = None
@@ -452,6 +489,10 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
     rounding) is applied to entries written into the caches, which is what a
     later step reads back.  Mutates ``L`` and returns a dict of every
     intermediate.
+
+    With ``L.fp8_rescore`` set as well (reading R29) the new key is also
+    stored in ``idx_keys`` and the selection is :func:`rescored_topk`; ``q_idx``
+    must then be real-valued (the exact scores use it unquantised).
 
     With E4M3 indexer keys (``L.idx_codes`` set) the compressed key is taken
     to float32 and quantised per row (:func:`numfmt.quantize_e4m3_rows`) into
@@ -497,7 +538,7 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
             codes, kscale = quantize_e4m3_rows(np.asarray(yi, dtype=np.float32)[None])
             L.idx_codes[L.n_comp] = codes[0]
             L.idx_scales[L.n_comp] = kscale[0]
-        else:
+        if not fp8 or L.fp8_rescore:
             L.idx_keys[L.n_comp] = rnd(yi)
         new_entry = (ym, yi)
         L.n_comp += 1
@@ -510,7 +551,11 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
         scores = index_score_fp8(q_codes[None], w_fold[None], L.idx_codes[:N], L.idx_scales[:N])[0]
     else:
         scores = index_score(np.asarray(q_idx)[None], np.asarray(w_idx)[None], L.idx_keys[:N])[0]
-    idx, count = topk(scores[None], top_k)
+    if fp8 and L.fp8_rescore:
+        exact = index_score(np.asarray(q_idx, dtype=np.float64)[None], np.asarray(w_idx)[None], L.idx_keys[:N])[0]
+        idx, count = rescored_topk(scores[None], exact[None], top_k, L.fp8_rescore)
+    else:
+        idx, count = topk(scores[None], top_k)
     rows, n_valid = gather(L.comp_kv[:N], idx[0], int(count[0]), L.swa.rows, L.swa.head, L.swa.length)
     out, lse = sparse_attn(q, rows, L.sink, scale)
     if L.kv_mixed:  # inverse RoPE of the output at the token's position
