@@ -293,9 +293,22 @@ def time_fp8(csa, layers, shape, reps: int, steps: int):
 
     scan_ms = timed(scans, reps) / len(fl)
     step_ms = timed(step, steps)
+
+    # the two-stage selection: the same E4M3 caches plus the bf16 keys, the
+    # top-512 of the E4M3 best 1024 by exact score
+    for ly, f in zip(layers, fl):
+        x = ly["x"]
+        f["L"] = csa.make_layer_desc(comp_kv=x["comp_kv"], idx_keys=f["kc"], idx_scales=f["ks"], swa=x["swa"],
+                                     main_bias=x["main_bias"], idx_bias=x["idx_bias"], sink=x["sink"],
+                                     n_comp=x["n_comp"], swa_head=x["swa_head"], swa_len=x["swa_len"], h=shape.h,
+                                     h_i=shape.h_i, m=shape.m, top_k=shape.top_k, idx_keys_exact=x["idx_keys"],
+                                     idx_rescore=2 * shape.top_k)
+        f["ws"] = torch.empty(csa.csa_decode_step_workspace_size(f["L"]), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    rescored_ms = timed(step, steps)
     alg = n * 128 + n * 4 + 64 * 128 + 64 * 4 + n * 4  # keys + key scales + q + w read, scores written
     del fl
-    return scan_ms, alg, step_ms
+    return scan_ms, alg, step_ms, rescored_ms
 
 
 def time_mixed_kv(csa, layers, shape, steps: int):
@@ -498,6 +511,17 @@ def time_prefill(csa, reps: int):
         csa.csa_index_topk_fp8(qc, w8, kc, ks, idx, cnt, ws, pos0=x["pos0"])
 
     topk8_ms = timed(topk8, reps)
+    # the two-stage selection over the same E4M3 keys plus the bf16 keys
+    kcand = 2 * k
+    ws_r = torch.empty(csa.csa_index_topk_fp8_rescored_workspace_size(T, N, k, kcand), dtype=torch.uint8,
+                       device="cuda")
+
+    def topk8r():
+        csa.csa_index_topk_fp8_rescored(x["q_idx"], x["w_idx"], kc, ks, x["idx_keys"], idx, cnt, ws_r, kcand,
+                                        pos0=x["pos0"])
+
+    topk8r_ms = timed(topk8r, reps)
+    del ws_r
     g8 = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
         with torch.cuda.graph(g8, stream=stream):
@@ -537,6 +561,10 @@ def time_prefill(csa, reps: int):
             "index_topk_ms": round(topk8_ms, 4),
             "chunk_ms": round(topk8_ms + attn_ms, 4),
             "queries_per_s": round(T / ((topk8_ms + attn_ms) * 1e-3), 1),
+            "rescored_index_topk_ms": round(topk8r_ms, 4),
+            "rescored_chunk_ms": round(topk8r_ms + attn_ms, 4),
+            "rescored_note": "query quantised, the best 1024 by E4M3 score per query, then the top-512 of those "
+                             "by exact score from the bf16 keys",
             "score_kernel": {
                 "kernel": "k_index_score_mq_fp8",
                 "bound": "mfma",
@@ -1019,7 +1047,8 @@ def main() -> int:
     res["roofline"]["steady_read_gbps_1gib"] = round(sr_bytes / (sr_us * 1e-6) / 1e9, 1)
 
     if "fp8" in legs:
-        fp8_ms, fp8_bytes, fp8_step_ms = time_fp8(csa, layers, shape, args.scan_reps, max(20, args.steps // 2))
+        fp8_ms, fp8_bytes, fp8_step_ms, rescored_ms = time_fp8(csa, layers, shape, args.scan_reps,
+                                                              max(20, args.steps // 2))
         fp8_gbs = fp8_bytes / (fp8_ms * 1e-3) / 1e9
         res["fp8_scan"] = {
             "kernel": "k_index_score_fp8",
@@ -1030,6 +1059,13 @@ def main() -> int:
             "decode_steps_per_s": round(1e3 / fp8_step_ms, 2),
             "decode_ms_per_step": round(fp8_step_ms, 5),
             "decode_note": "the step takes the bf16 query and quantises it in its scan workgroups",
+            "rescored": {
+                "workload": "the E4M3 step with the two-stage selection: the top-512 by exact score (bf16 keys "
+                            "kept as well) of the best 1024 by E4M3 score; top-512 recall 1.0 against the "
+                            "float64 indexer where E4M3 alone reaches 0.936",
+                "decode_steps_per_s": round(1e3 / rescored_ms, 2),
+                "decode_ms_per_step": round(rescored_ms, 5),
+            },
         }
     if "mixed" in legs:
         mixed_ms = time_mixed_kv(csa, layers, shape, max(20, args.steps // 2))

@@ -54,6 +54,7 @@ class LayerDesc(ctypes.Structure):
         ("kv_dtype", _i), ("rope_dim", _i),
         ("rope_cos", _vp), ("rope_sin", _vp), ("rope_rows", _i),
         ("comp_rope_cos", _vp), ("comp_rope_sin", _vp), ("comp_rope_rows", _i),
+        ("idx_rescore", _i), ("idx_keys_exact", _vp), ("idx_keys_exact_stride_b", _ll),
     ]
 
 
@@ -107,6 +108,9 @@ _SIGS = {
     "csa_index_topk_workspace_size": (_sz, [_i, _i, _i]),
     "csa_index_topk": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _ll, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_topk_fp8": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _ll, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "csa_index_topk_fp8_rescored_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "csa_index_topk_fp8_rescored": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _ll, _i, _i, _i, _vp, _vp, _vp, _sz,
+                                         _vp]),
     "csa_prefill_attn": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _ll, _vp, _f, _vp, _i, _vp, _i, _i, _i,
                               _vp]),
     "csa_prefill_attn_mixed": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _ll, _vp, _vp, _i, _vp, _f, _vp, _i,
@@ -364,15 +368,18 @@ def csa_layer_advance(layer: LayerDesc, pos: int) -> None:
 def make_layer_desc(*, comp_kv, idx_keys, swa, main_bias, idx_bias, sink, n_comp: int,
                     swa_head: int, swa_len: int, h: int, h_i: int, m: int = 4, top_k: int,
                     overlap: int = 0, out_dtype=None, scale: Optional[float] = None,
-                    main_norm=None, idx_norm=None, idx_scales=None, rope=None, comp_rope=None) -> LayerDesc:
+                    main_norm=None, idx_norm=None, idx_scales=None, rope=None, comp_rope=None,
+                    idx_keys_exact=None, idx_rescore: int = 0) -> LayerDesc:
     """Fill a LayerDesc from cache tensors: comp_kv [B, max_comp, d], idx_keys
     [B, max_comp, d_i] (None for an HCA layer, with idx_bias None, h_i and
     top_k 0), swa [B, W, d].  idx_keys of torch.uint8 are E4M3 codes, with
     their row scales in idx_scales [B, max_comp] float32.  comp_kv and swa of
     torch.uint8 [B, rows, 592] are mixed main-KV records (d = 512), with
     rope = (cos, sin) and comp_rope = (cos, sin) float32 tables
-    [rows, 32] of token positions and of block indices.  The returned struct
-    keeps references to every tensor it points at."""
+    [rows, 32] of token positions and of block indices.  E4M3 keys with
+    idx_rescore = k_cand > 0 also keep idx_keys_exact [B, max_comp, d_i]
+    bf16 (the two-stage selection).  The returned struct keeps references to
+    every tensor it points at."""
     B, max_comp, d = comp_kv.shape
     mixed = comp_kv.dtype == torch.uint8
     if mixed:
@@ -408,8 +415,13 @@ def make_layer_desc(*, comp_kv, idx_keys, swa, main_bias, idx_bias, sink, n_comp
         L.idx_scales, L.idx_scales_stride_b = idx_scales.data_ptr(), idx_scales.stride(0)
     else:
         L.idx_dtype = L.dtype
+    if idx_rescore:
+        L.idx_rescore = idx_rescore
+        L.idx_keys_exact, L.idx_keys_exact_stride_b = _ptr(idx_keys_exact), (
+            idx_keys_exact.stride(0) if idx_keys_exact is not None else 0)
     # the struct holds raw device pointers: keep the tensors alive with it
-    L._keep = (comp_kv, idx_keys, swa, main_bias, idx_bias, sink, main_norm, idx_norm, idx_scales, rope, comp_rope)
+    L._keep = (comp_kv, idx_keys, swa, main_bias, idx_bias, sink, main_norm, idx_norm, idx_scales, rope, comp_rope,
+               idx_keys_exact)
     return L
 
 
@@ -475,6 +487,27 @@ def csa_index_topk_fp8(q, w, k, k_scale, idx, count, ws, pos0: int = -1, ratio: 
     _check(lib().csa_index_topk_fp8(_ptr(q), _ptr(w), _ptr(k), _ptr(k_scale), t, h_i, d_i, n, pos0, ratio,
                                     idx.shape[1], _ptr(idx), _ptr(count), _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream(stream)))
+
+
+def csa_index_topk_fp8_rescored_workspace_size(t: int, n: int, top_k: int, k_cand: int) -> int:
+    return lib().csa_index_topk_fp8_rescored_workspace_size(t, n, top_k, k_cand)
+
+
+def csa_index_topk_fp8_rescored(q, w, k8, k_scale, k16, idx, count, ws, k_cand: int, pos0: int = -1, ratio: int = 4,
+                                n: Optional[int] = None, stream=None) -> None:
+    """q [t, 64, 128] bf16; w [t, 64] float32 (plain weights); k8 [N, 128]
+    uint8 E4M3, k_scale [N] float32 and k16 [N, 128] bf16 (the same keys);
+    idx [t, top_k] int32; count [t] int32 or None; pos0 as csa_index_topk."""
+    for t_, nm in ((q, "q"), (w, "w"), (k8, "k8"), (k_scale, "k_scale"), (k16, "k16"), (idx, "idx")):
+        if not t_.is_contiguous():
+            raise ValueError(f"{nm}: must be contiguous")
+    if q.dtype != torch.bfloat16 or k16.dtype != torch.bfloat16 or k8.dtype != torch.uint8:
+        raise TypeError("q and k16 must be bfloat16, k8 uint8 E4M3 codes")
+    t, h_i, d_i = q.shape
+    n = k8.shape[0] if n is None else n
+    _check(lib().csa_index_topk_fp8_rescored(_ptr(q), _ptr(w), _ptr(k8), _ptr(k_scale), _ptr(k16), t, h_i, d_i, n,
+                                             pos0, ratio, idx.shape[1], k_cand, _ptr(idx), _ptr(count), _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def csa_prefill_attn(q, comp_kv, idx, count, win_kv, window: int, pos0: int, sink, scale: float, out,

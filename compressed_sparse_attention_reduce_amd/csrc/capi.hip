@@ -330,11 +330,18 @@ static size_t step_topk_bytes(const csa_layer_desc* L) {
     return align256(static_cast<size_t>(L->batch) * kStepMaxSlots * csa::kMaxCandM1 * sizeof(unsigned long long));
 }
 
+// the two-stage E4M3 selection's list of exact candidates (one per sequence)
+static size_t step_rescore_bytes(const csa_layer_desc* L) {
+    if (L->idx_dtype != CSA_FP8_E4M3 || L->idx_rescore <= 0) return 0;
+    return align256(static_cast<size_t>(L->batch) * (static_cast<size_t>(L->idx_rescore) + 1) *
+                    sizeof(unsigned long long));
+}
+
 size_t csa_decode_step_workspace_size(const csa_layer_desc* L) {
     if (!L || L->batch < 1 || L->max_comp < 0 || L->top_k < 1) return 0;
     return step_topk_bytes(L) +
            align256(csa::attn_workspace_bytes(L->dtype == CSA_BF16, L->batch, L->h, L->d, L->top_k + L->w)) +
-           256;
+           256 + step_rescore_bytes(L);
 }
 
 size_t csa_decode_step_dev_ring_size(const csa_layer_desc* L) {
@@ -398,6 +405,20 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
     const bool fp8 = L->idx_dtype == CSA_FP8_E4M3;
     if (fp8 && L->dtype != CSA_BF16)
         return fail(CSA_ERR_UNSUPPORTED, "csa_decode_step: E4M3 indexer keys need bfloat16 caches");
+    // the two-stage E4M3 selection: the k_cand best by E4M3 score, rescored from bfloat16 keys
+    const bool rescore = fp8 && L->idx_rescore > 0;
+    if (L->idx_rescore != 0) {
+        if (!fp8)
+            return fail(CSA_ERR_UNSUPPORTED, "csa_decode_step: idx_rescore needs E4M3 indexer keys");
+        if (dev)
+            return fail(CSA_ERR_UNSUPPORTED, "csa_decode_step_dev: the two-stage E4M3 selection needs host counters");
+        CHECK(L->idx_rescore >= L->top_k && L->idx_rescore <= csa::kTopkMaxK,
+              "csa_decode_step: idx_rescore %d outside top_k %d .. %d", L->idx_rescore, L->top_k, csa::kTopkMaxK);
+        CHECK(L->idx_keys_exact && aligned16(L->idx_keys_exact) && L->idx_keys_exact_stride_b % 8 == 0 &&
+                  L->idx_keys_exact_stride_b >= 0,
+              "csa_decode_step: idx_keys_exact missing, misaligned or with a bad batch stride");
+    }
+    const int kc = rescore ? L->idx_rescore : L->top_k;  // the first stage's k
     // (the E4M3 step takes a bfloat16 query and quantises it: its stride is in bfloat16 elements)
     const int rc_s = fp8 ? check_fp8_score_args(io->q_idx, io->w_idx, L->idx_keys, L->idx_scales, io->scores,
                                                 L->batch, 1, L->h_i, L->d_i, N, L->m, 2 * io->q_idx_stride_b,
@@ -483,6 +504,8 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
     pa.idx_fp8 = fp8 ? 1 : 0;
     pa.idx_scales = fp8 ? L->idx_scales : nullptr;
     pa.idx_scales_stride_b = fp8 ? L->idx_scales_stride_b : 0;
+    pa.idx_keys_exact = rescore ? static_cast<uint16_t*>(L->idx_keys_exact) : nullptr;
+    pa.idx_keys_exact_stride_b = rescore ? L->idx_keys_exact_stride_b : 0;
     if (dev) {  // the token's own rows; the kernels keep the block in the ring
         pa.z_main = io->z_main;
         pa.c_main = io->c_main;
@@ -523,9 +546,9 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
                           (completes ? 1 : 0);
         const int kpw = fp8 ? csa::index_score_fp8_keys_per_wg(L->batch, n_scan, prep_wgs)
                             : csa::index_score_bf16_keys_per_wg(L->batch, n_scan, prep_wgs);
-        const int m = kpw > 0 ? csa::topk_cand_m(N, L->top_k, kpw) : -1;
-        const int mw = kpw > 0 ? csa::topk_cand_m(N, L->top_k, kpw / csa::kScoreWavesPerWg) : -1;
-        if (m > 0 && slots <= kStepMaxSlots && (dev || N > 4 * L->top_k))
+        const int m = kpw > 0 ? csa::topk_cand_m(N, kc, kpw) : -1;
+        const int mw = kpw > 0 ? csa::topk_cand_m(N, kc, kpw / csa::kScoreWavesPerWg) : -1;
+        if (m > 0 && slots <= kStepMaxSlots && (dev || N > 4 * kc))
             ca = csa::CandArgs{static_cast<unsigned long long*>(tws), slots, m, mw < m ? mw : m};
     }
     csa::ScoreArgs sa{io->q_idx, io->w_idx, L->idx_keys, io->scores, L->batch, 1, L->h_i, L->d_i, n_scan,
@@ -547,6 +570,20 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
     if (!do_rest) return ok();
     csa::TopkArgs ta{io->scores, L->batch, 1, N, N, io->scores_stride_b, L->top_k, io->topk_idx,
                      io->topk_count, tws};
+    // two-stage E4M3 selection: the first stage and the exact scores make one
+    // list per sequence that the top-k below selects from
+    if (rescore) {
+        auto* ex = reinterpret_cast<unsigned long long*>(
+            static_cast<char*>(ws) + csa_decode_step_workspace_size(L) - step_rescore_bytes(L));
+        csa::TopkArgs tc = ta;
+        tc.k = kc;
+        const csa::RescoreArgs ra{static_cast<const uint16_t*>(io->q_idx), io->q_idx_stride_b, io->w_idx,
+                                  io->w_stride_b, static_cast<const uint16_t*>(L->idx_keys_exact),
+                                  L->idx_keys_exact_stride_b, N, ex};
+        e = csa::launch_fp8_rescore(tc, ca.lists ? &ca : nullptr, ra, s);
+        if (e != hipSuccess) return launched(e, "csa_decode_step/rescore");
+        ca = csa::CandArgs{ex, 1, kc, kc};
+    }
     // bf16 with candidate lists (or a short row): every attention workgroup
     // selects the top k itself, no separate top-k launch, as long as those
     // workgroups are all resident at once (one per compute unit); a larger batch
@@ -906,6 +943,73 @@ int csa_index_topk_fp8(const unsigned char* q, const float* w, const unsigned ch
     static const float kNoKeys = 1.f;
     a.k_scale = n > 0 ? k_scale : &kNoKeys;
     return launched(csa::launch_index_topk(a, static_cast<hipStream_t>(stream)), "csa_index_topk_fp8");
+}
+
+// workspace of the two-stage E4M3 selection of a chunk: query codes, folded
+// weights, the first stage's candidates and counts, then csa_index_topk's
+static size_t rescored_parts(int t, int n, int k_cand, size_t* off) {
+    const size_t tt = static_cast<size_t>(t);
+    off[0] = 0;                                                      // codes [t][64][128]
+    off[1] = off[0] + align256(tt * 64 * 128);                       // folded w [t][64]
+    off[2] = off[1] + align256(tt * 64 * sizeof(float));             // candidates [t][k_cand]
+    off[3] = off[2] + align256(tt * static_cast<size_t>(k_cand) * sizeof(int));  // counts [t]
+    off[4] = off[3] + align256(tt * sizeof(int));                    // the first stage's workspace
+    return off[4] + csa::index_topk_workspace_bytes(t, n, k_cand);
+}
+
+size_t csa_index_topk_fp8_rescored_workspace_size(int t, int n, int top_k, int k_cand) {
+    if (t < 1 || n < 0 || top_k < 1 || k_cand < top_k) return 0;
+    size_t off[5];
+    return rescored_parts(t, n, k_cand, off);
+}
+
+int csa_index_topk_fp8_rescored(const void* q, const float* w, const unsigned char* k8, const float* k_scale,
+                                const void* k16, int t, int h_i, int d_i, int n, long long pos0, int ratio, int top_k,
+                                int k_cand, int* idx, int* count, void* ws, size_t ws_bytes, csa_stream stream) {
+    CHECK(q && w && idx && ws && ((k8 && k_scale && k16) || n == 0), "csa_index_topk_fp8_rescored: null pointer argument");
+    CHECK(t >= 1 && n >= 0, "csa_index_topk_fp8_rescored: t %d n %d", t, n);
+    CHECK(ratio >= 1, "csa_index_topk_fp8_rescored: ratio %d", ratio);
+    CHECK(top_k >= 1 && k_cand >= top_k && k_cand <= csa::kTopkMaxK,
+          "csa_index_topk_fp8_rescored: top_k %d / k_cand %d (need 1 <= top_k <= k_cand <= %d)", top_k, k_cand,
+          csa::kTopkMaxK);
+    if (h_i != 64 || d_i != 128)
+        return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk_fp8_rescored: needs h_i=64, d_i=128 (got %d, %d)", h_i, d_i);
+    CHECK(aligned16(q) && aligned16(w) && aligned16(ws) && (n == 0 || (aligned16(k8) && aligned16(k16))),
+          "csa_index_topk_fp8_rescored: q, w, keys and ws must be 16-byte aligned");
+    size_t off[5];
+    const size_t need = rescored_parts(t, n, k_cand, off);
+    if (ws_bytes < need)
+        return fail(CSA_ERR_WORKSPACE, "csa_index_topk_fp8_rescored: workspace %zu < %zu bytes", ws_bytes, need);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    char* base = static_cast<char*>(ws);
+    auto* qc = reinterpret_cast<uint8_t*>(base + off[0]);
+    auto* wf = reinterpret_cast<float*>(base + off[1]);
+    auto* cand = reinterpret_cast<int*>(base + off[2]);
+    auto* ccount = reinterpret_cast<int*>(base + off[3]);
+    // 1. the query's codes and folded weights
+    hipError_t e = csa::launch_quantize_fp8(q, true, qc, nullptr, static_cast<long long>(t) * 64, 128, s, w, wf);
+    if (e != hipSuccess) return launched(e, "csa_index_topk_fp8_rescored/quantise");
+    // 2. the k_cand best by E4M3 score per query
+    csa::IndexTopkArgs a{};
+    a.w = wf;
+    a.t = t;
+    a.n = n;
+    a.pos0 = pos0;
+    a.ratio = ratio;
+    a.top_k = k_cand;
+    a.idx = cand;
+    a.count = ccount;
+    a.ws = base + off[4];
+    a.q8 = qc;
+    a.k8 = k8;
+    static const float kNoKeys = 1.f;
+    a.k_scale = n > 0 ? k_scale : &kNoKeys;
+    e = csa::launch_index_topk(a, s);
+    if (e != hipSuccess) return launched(e, "csa_index_topk_fp8_rescored/first stage");
+    // 3. their exact scores and the top_k of them
+    const csa::RescoreRowsArgs r{static_cast<const uint16_t*>(q), w, static_cast<const uint16_t*>(k16), n, cand, ccount,
+                                 k_cand, t, top_k, idx, count};
+    return launched(csa::launch_rescore_rows(r, s), "csa_index_topk_fp8_rescored");
 }
 
 int csa_prefill_attn(const void* q, const void* comp_kv, int n_comp, const int* idx, const int* count, int k,

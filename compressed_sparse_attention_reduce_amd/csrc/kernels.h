@@ -244,6 +244,40 @@ struct PrepArgs;
 int attn_dense_splits(int n_max);
 hipError_t launch_attn_dense_bf16(AttnArgs a, const PrepArgs& prep, const void* x0, long long x0_stride_b,
                                   const void* x1, long long x1_stride_b, hipStream_t s);
+// The two-stage E4M3 selection (decode step, one query row per sequence):
+// the k_cand best by E4M3 score (t.k = k_cand; from cands when given, else
+// the exact path over t.scores), their exact scores from the bfloat16 keys
+// and query (the bfloat16 scan's arithmetic), written as one candidate list
+// per sequence: out[b][0 .. k_cand) composites (zero padded) and out[b][k_cand]
+// = 0, for launch_topk_attn / launch_topk with CandArgs{out, 1, k_cand, k_cand}.
+struct RescoreArgs {
+    const uint16_t* q;      // [B][64][128] bfloat16
+    long long q_stride_b;
+    const float* w;         // [B][64]
+    long long w_stride_b;
+    const uint16_t* keys;   // [B][max_comp][128] bfloat16
+    long long keys_stride_b;
+    int n;                  // keys in the cache (indices are clamped below it)
+    unsigned long long* out;
+};
+hipError_t launch_fp8_rescore(const TopkArgs& t, const CandArgs* cands, const RescoreArgs& r, hipStream_t s);
+// The second stage for many query rows (a prefill chunk): row r's candidates
+// cand[r][0 .. cand_count[r]) (kc a row), their exact scores from the
+// bfloat16 row q[r] (64 x 128), w[r] (64) and keys [n][128], the k best of
+// them sorted into idx[r] (-1 past the count) and count[r] (nullable).
+struct RescoreRowsArgs {
+    const uint16_t* q;
+    const float* w;
+    const uint16_t* keys;
+    int n;
+    const int* cand;
+    const int* cand_count;
+    int kc;
+    int t, k;
+    int* idx;
+    int* count;
+};
+hipError_t launch_rescore_rows(const RescoreRowsArgs& a, hipStream_t s);
 // decode step, bf16 gather mode, one query row per sequence: every attention
 // workgroup selects the top k itself (from cands when given, else the
 // exact path over the scores), then attends; topk idx / count written too.
@@ -263,6 +297,8 @@ struct PrepArgs {
     int idx_fp8;   // the indexer keys are E4M3 codes with per-row scales (role 2 quantises the new key)
     float* idx_scales;
     long long idx_scales_stride_b;
+    uint16_t* idx_keys_exact;  // E4M3 keys: also the bfloat16 key here (nullable)
+    long long idx_keys_exact_stride_b;
     long long block;
     const void* kv_new;
     long long kv_new_stride_b;

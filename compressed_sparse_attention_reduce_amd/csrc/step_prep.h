@@ -88,6 +88,10 @@ __device__ inline void step_prep_role_at(const PrepArgs& a, int role, int b, flo
         const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
         uint8_t* codes = static_cast<uint8_t*>(a.idx_keys) + b * a.idx_keys_stride_b +
                          static_cast<long long>(a.n_comp) * a.d_i;
+        if (a.idx_keys_exact) {  // the key in bfloat16 too (the bfloat16 step's rounding)
+            uint16_t* ex = a.idx_keys_exact + b * a.idx_keys_exact_stride_b + static_cast<long long>(a.n_comp) * a.d_i;
+            for (int j = threadIdx.x; j < a.d_i; j += blockDim.x) ex[j] = f32_to_bf16(key[j]);
+        }
         __syncthreads();  // every thread has read red
         for (int j = threadIdx.x; j < a.d_i; j += blockDim.x) {
             const uint8_t q = e4m3_encode_rne(key[j] / scale);

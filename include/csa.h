@@ -277,6 +277,17 @@ int csa_sparse_attn(const void *q, const void *kv, const int *n_valid, const flo
  * takes the bfloat16 q_idx and plain w_idx, quantises every head row of
  * q_idx and folds its scale into that head's weight exactly as
  * csa_quantize_query_fp8 does, and scores as csa_index_score_fp8 does.
+ * Section 2c (idx_rescore = k_cand > 0, E4M3 keys only): step b also stores
+ * the new key in bfloat16 in idx_keys_exact[n_comp] (the bfloat16 step's
+ * rounding); step c writes the E4M3 scores to io->scores, takes the k_cand
+ * best of them (the top-k rules), computes their exact scores from
+ * idx_keys_exact and the bfloat16 query (the same values the bfloat16 step
+ * computes for those keys) and selects the top_k best of those (score
+ * descending, lower index first).  Source of the two stages: the recall
+ * gate of page 1, ARCHITECTURE_AND_MEMORY_AUDIT.md (Tier 1 gate 4: the
+ * selection must keep 99% of the exact top-512), which per-row E4M3 alone
+ * misses on crowded scores (93.6% on the 1M-context workload).  Host
+ * counters only (csa_decode_step_dev: CSA_ERR_UNSUPPORTED).
  * It does NOT update the host integers: afterwards the caller sets
  * swa_head = (swa_head + 1) % w, swa_len = min(swa_len + 1, w) and, if a block
  * completed, n_comp += 1 (csa_layer_advance does exactly this).
@@ -323,6 +334,13 @@ typedef struct csa_layer_desc {
     int rope_dim;
     const float *rope_cos, *rope_sin; int rope_rows;
     const float *comp_rope_cos, *comp_rope_sin; int comp_rope_rows;
+    /* Recall-restored E4M3 keys (section 2c; appended: zero = off): with
+     * idx_dtype = CSA_FP8_E4M3 and idx_rescore = k_cand (top_k <= k_cand <=
+     * 2048) the layer also keeps its keys as bfloat16 in idx_keys_exact
+     * [B][max_comp][d_i] (stride idx_keys_exact_stride_b elements, 16-byte
+     * aligned rows). */
+    int idx_rescore;
+    void *idx_keys_exact; long long idx_keys_exact_stride_b;
 } csa_layer_desc;
 
 typedef struct csa_step_io {
@@ -520,6 +538,18 @@ int csa_hca_decode_step(const csa_layer_desc *layer, const csa_step_io *io, void
  *   scales; scores as csa_index_score_fp8 computes them.  The same workspace
  *   size, outputs and limits as csa_index_topk.
  *
+ * csa_index_topk_fp8_rescored: the two-stage E4M3 selection of section 2c
+ *   for every query: q [t][64][128] bf16 and w [t][64] float32 (plain
+ *   weights; the query is quantised as csa_quantize_query_fp8 does), k8 /
+ *   k_scale [n][128] codes and [n] scales, k16 [n][128] the same keys in
+ *   bfloat16.  Per query, the k_cand best by E4M3 score (csa_index_topk_fp8),
+ *   then their exact scores from k16 and the bfloat16 query (the values
+ *   csa_index_score computes) and the top_k best of those: idx [t][top_k]
+ *   (score descending, lower index first, -1 past the count), count [t]
+ *   (nullable) = min(top_k, visible blocks).  top_k <= k_cand <= 2048.
+ *   ws: csa_index_topk_fp8_rescored_workspace_size(t, n, top_k, k_cand)
+ *   bytes, 16-byte aligned.
+ *
  * csa_prefill_attn: per query row r, one softmax (scale, then the sink in the
  *   denominator only) over comp_kv[idx[r][0 .. count[r])] followed by its
  *   window rows.  q: [t][h][d] bf16; comp_kv: [n_comp][d] bf16; idx/count as
@@ -544,6 +574,11 @@ int csa_index_topk_fp8(const unsigned char *q, const float *w, const unsigned ch
                        const float *k_scale, int t, int h_i, int d_i, int n, long long pos0,
                        int ratio, int top_k, int *idx, int *count, void *ws, size_t ws_bytes,
                        csa_stream stream);
+size_t csa_index_topk_fp8_rescored_workspace_size(int t, int n, int top_k, int k_cand);
+int csa_index_topk_fp8_rescored(const void *q, const float *w, const unsigned char *k8, const float *k_scale,
+                                const void *k16, int t, int h_i, int d_i, int n, long long pos0, int ratio,
+                                int top_k, int k_cand, int *idx, int *count, void *ws, size_t ws_bytes,
+                                csa_stream stream);
 int csa_prefill_attn(const void *q, const void *comp_kv, int n_comp, const int *idx,
                      const int *count, int k, const void *win_kv, int window, long long pos0,
                      const float *sink, float scale, void *out, csa_dtype out_dtype, float *lse,

@@ -236,8 +236,11 @@ def test_index_score_fp8(csa, case):
 def test_index_score_fp8_full_size_sampled_and_recall(csa):
     """n = 250,000 FP8 keys quantised on the GPU from the 1M-context bf16
     cache: scores on a sample against the oracle; the FP8 top-512 against the
-    bf16 scores' top-512 (recall is reported, not a parity bar: E4M3's
-    3-bit significand moves scores near the threshold)."""
+    bf16 scores' top-512.  That recall is a property of the format (E4M3's
+    3-bit significand moves crowded scores across the threshold: 0.936 here,
+    as the float64 study in test_fp8_recall.py finds), checked to stay at the
+    format's figure; the 0.99 gate is met by the two-stage selection
+    (test_decode_step_ctx1m_fp8_rescored_full_size_recall)."""
     shape = synth.SHAPES["ctx1m"]
     x = synth.make_decode_inputs_torch(shape, seed=None, device=DEV, layers=1)[0]
     n = shape.n_comp
@@ -267,7 +270,7 @@ def test_index_score_fp8_full_size_sampled_and_recall(csa):
     top16 = set(torch.topk(s16[0, 0], 512).indices.cpu().tolist())
     recall = len(top8 & top16) / 512
     print(f"fp8 top-512 recall vs bf16 keys at n=250000: {recall:.4f}")
-    assert recall >= 0.9
+    assert recall >= 0.93  # the format's own figure (0.9355); the gate needs the two-stage selection
 
 
 # ---------------------------------------------------------------------------
@@ -1042,3 +1045,160 @@ def test_decode_step_two_calls_equal_one(csa, case):
     for a, b in zip(c1, c2):
         if a is not None:
             assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# E4M3 keys with the two-stage selection (E4M3 top-k_cand, then exact top-k)
+# ---------------------------------------------------------------------------
+
+def _rescored_layer(csa, x, B, max_comp, K, kc):
+    f = numfmt.bf16_bits_to_f64
+    kc0, ks0 = numfmt.quantize_e4m3_rows(f(x["idx_keys"]).reshape(-1, 128).astype(np.float32))
+    codes = torch.from_numpy(kc0.reshape(B, max_comp, 128)).to(DEV)
+    scales = dev_f32(ks0.reshape(B, max_comp))
+    exact_keys = dev_bf16(x["idx_keys"])
+    comp, swa = dev_bf16(x["comp_kv"]), dev_bf16(x["swa"])
+    L = csa.make_layer_desc(comp_kv=comp, idx_keys=codes, idx_scales=scales, swa=swa,
+                            main_bias=dev_f32(x["main_bias"]), idx_bias=dev_f32(x["idx_bias"]),
+                            sink=dev_f32(x["sink"]), n_comp=x["n_comp"], swa_head=x["swa_head"],
+                            swa_len=x["swa_len"], h=64, h_i=64, top_k=K, idx_keys_exact=exact_keys,
+                            idx_rescore=kc)
+    return L, codes, scales, exact_keys, comp, swa
+
+
+def _check_rescored_selection(csa, qi_dev, wi_dev, exact_keys, N, got_s8, gi, gc, exact_ref, K, kc, b=0):
+    """The selection of the two-stage step: bit for bit the oracle's two
+    stages applied to the GPU's own E4M3 scores and to the bfloat16 scan's
+    scores (which the rescoring reproduces exactly); and by the gap rule
+    against the float64 exact scores inside the first stage's set."""
+    s16 = torch.empty(1, 1, N, device=DEV)
+    csa.csa_index_score(qi_dev[b:b + 1, None].contiguous(), wi_dev[b:b + 1, None].contiguous(),
+                        exact_keys[b:b + 1, :N].contiguous(), s16)
+    torch.cuda.synchronize()
+    s16 = s16[0, 0].cpu().numpy().astype(np.float64)
+    want, wc = oracle.rescored_topk(got_s8[None], s16[None], K, kc)
+    np.testing.assert_array_equal(gi, want[0])
+    assert gc == wc[0]
+    stage1 = oracle.topk(got_s8[None], kc)[0][0]
+    inside = np.full(N, -np.inf)
+    inside[stage1[stage1 >= 0]] = exact_ref[stage1[stage1 >= 0]]
+    assert_topk_gap_rule(gi, gc, inside, K)
+
+
+@pytest.mark.parametrize("B", [1, 5])
+def test_decode_steps_in_sequence_fp8_rescored(csa, B):
+    """Steps over E4M3 keys with the two-stage selection (top_k 64 out of the
+    E4M3 best 128, two block completions; batch 5 takes the separate top-k):
+    new key in both forms within rounding of the oracle's, then adopted;
+    E4M3 scores against the oracle; the selection exactly as above; gather
+    and attention against the oracle."""
+    K, kc, W = 64, 128, 8
+    shape = synth.with_(synth.SHAPES["ctx8k"], batch=B, ctx=12000, n_comp=3000, top_k=K, w=W)
+    x = synth.make_decode_inputs(shape, 4201 + B, max_comp=3100)
+    g = _g(4202 + B)
+    f = numfmt.bf16_bits_to_f64
+    L, codes, scales, exact_keys, comp, swa = _rescored_layer(csa, x, B, 3100, K, kc)
+    osts = []
+    for b in range(B):
+        kc0, ks0 = codes[b].cpu().numpy(), scales[b].cpu().numpy()
+        osts.append(oracle.LayerState(comp_kv=f(x["comp_kv"][b]), idx_keys=f(x["idx_keys"][b]), n_comp=x["n_comp"],
+                                      swa=oracle.SwaRing(f(x["swa"][b]), x["swa_head"], x["swa_len"]),
+                                      main_bias=x["main_bias"], idx_bias=x["idx_bias"], sink=x["sink"],
+                                      round_cache=numfmt.bf16_round_f64, idx_codes=kc0.copy(), idx_scales=ks0.copy(),
+                                      fp8_rescore=kc))
+    ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+    for pos in range(x["pos"], x["pos"] + 6):
+        q = synth.to_bf16_bits(g.standard_normal((B, 64, 512), dtype=np.float32))
+        qi = synth.to_bf16_bits(g.standard_normal((B, 64, 128), dtype=np.float32) / np.float32(np.sqrt(128)))
+        wi = g.standard_normal((B, 64), dtype=np.float32)
+        kvn = synth.to_bf16_bits(g.standard_normal((B, 512), dtype=np.float32))
+        zm, cm = g.standard_normal((2, B, 4, 512), dtype=np.float32)
+        zi, ci = g.standard_normal((2, B, 4, 128), dtype=np.float32)
+        outs = dict(scores=torch.empty(B, 3100, device=DEV), topk_idx=torch.empty(B, K, dtype=torch.int32, device=DEV),
+                    topk_count=torch.empty(B, dtype=torch.int32, device=DEV),
+                    gather_buf=torch.zeros(B, K + W, 512, dtype=torch.bfloat16, device=DEV),
+                    n_valid=torch.empty(B, dtype=torch.int32, device=DEV),
+                    out=torch.empty(B, 64, 512, dtype=torch.bfloat16, device=DEV), lse=torch.empty(B, 64, device=DEV))
+        qi_dev, wi_dev = dev_bf16(qi), dev_f32(wi)
+        io = csa.make_step_io(pos=pos, q=dev_bf16(q), q_idx=qi_dev, w_idx=wi_dev, kv_new=dev_bf16(kvn),
+                              z_main=dev_f32(zm), c_main=dev_f32(cm), z_idx=dev_f32(zi), c_idx=dev_f32(ci), **outs)
+        print(f"rescored fp8-key step pos={pos} B={B}", flush=True)
+        csa.csa_decode_step(L, io, ws)
+        csa.csa_layer_advance(L, pos)
+        torch.cuda.synchronize()
+        completes = pos % 4 == 3
+        for b in range(B):
+            ost = osts[b]
+            n0 = ost.n_comp
+            oracle.decode_step(ost, q=f(q[b]), q_idx=f(qi[b]), w_idx=wi[b], kv_new=f(kvn[b]), pos=pos, top_k=K,
+                               z_main=zm[b], c_main=cm[b], z_idx=zi[b], c_idx=ci[b], scale=1 / np.sqrt(512))
+            N = ost.n_comp
+            assert L.n_comp == N
+            if completes:
+                yi = oracle.compress(zi[b], ci[b], x["idx_bias"], 4)[0]
+                _assert_e4m3_key_close(codes[b, n0].cpu().numpy(), float(scales[b, n0]), yi)
+                assert_bf16_close(host_bits(exact_keys[b, n0]), yi)
+                assert_bf16_close(host_bits(comp[b, n0]), oracle.compress(zm[b], cm[b], x["main_bias"], 4)[0])
+            ost.comp_kv[:N] = host_f64(comp[b, :N])
+            ost.idx_keys[:N] = host_f64(exact_keys[b, :N])
+            ost.idx_codes[:N], ost.idx_scales[:N] = codes[b, :N].cpu().numpy(), scales[b, :N].cpu().numpy()
+            qc, w8 = _fp8_query(f(qi[b:b + 1]).astype(np.float32), wi[b:b + 1])
+            ref_s8 = oracle.index_score_fp8(qc, w8, ost.idx_codes[:N], ost.idx_scales[:N])[0]
+            got_s8 = outs["scores"][b, :N].cpu().numpy().astype(np.float64)
+            assert rel_err(got_s8, ref_s8) <= 1e-4
+            exact_ref = oracle.index_score(f(qi[b])[None], wi[b][None].astype(np.float64), ost.idx_keys[:N])[0]
+            gi, gc = outs["topk_idx"][b].cpu().numpy(), int(outs["topk_count"][b])
+            _check_rescored_selection(csa, qi_dev, wi_dev, exact_keys, N, got_s8, gi, gc, exact_ref, K, kc, b)
+            rows, n_valid = oracle.gather(ost.comp_kv[:N], gi, gc, ost.swa.rows, ost.swa.head, ost.swa.length)
+            assert int(outs["n_valid"][b]) == n_valid
+            np.testing.assert_array_equal(host_f64(outs["gather_buf"][b, :n_valid]), rows)
+            ro, rl = oracle.sparse_attn(f(q[b]), rows, x["sink"], 1 / np.sqrt(512))
+            assert rel_err(host_f64(outs["out"][b]), ro) <= 2e-2
+            assert rel_err(outs["lse"][b].cpu().numpy(), rl) <= 2e-2
+
+
+def test_decode_step_ctx1m_fp8_rescored_full_size_recall(csa):
+    """One 1M-context layer over E4M3 keys with the two-stage selection
+    (top-512 of the E4M3 best 1024): the selection exactly as the oracle's
+    two stages on the GPU's scores, and top-512 recall against the float64
+    exact indexer of at least 0.99 (the gate of page 1,
+    ARCHITECTURE_AND_MEMORY_AUDIT.md, Tier 1 gate 4)."""
+    shape = synth.SHAPES["ctx1m"]
+    x = synth.make_decode_inputs_torch(shape, seed=None, device=DEV, layers=1)[0]
+    B, K, W, D, kc = 1, shape.top_k, shape.w, shape.d, 2 * shape.top_k
+    n0 = x["n_comp"]
+    codes = torch.zeros(B, shape.max_comp, 128, dtype=torch.uint8, device=DEV)
+    scales = torch.zeros(B, shape.max_comp, dtype=torch.float32, device=DEV)
+    csa.csa_quantize_fp8(x["idx_keys"][:, :n0].contiguous(), codes[:, :n0], scales[:, :n0])
+    exact_keys = x["idx_keys"]
+    L = csa.make_layer_desc(comp_kv=x["comp_kv"], idx_keys=codes, idx_scales=scales, swa=x["swa"],
+                            main_bias=x["main_bias"], idx_bias=x["idx_bias"], sink=x["sink"], n_comp=n0,
+                            swa_head=x["swa_head"], swa_len=x["swa_len"], h=shape.h, h_i=shape.h_i, top_k=K,
+                            idx_keys_exact=exact_keys, idx_rescore=kc)
+    outs = dict(scores=torch.empty(B, shape.max_comp, device=DEV),
+                topk_idx=torch.empty(B, K, dtype=torch.int32, device=DEV),
+                topk_count=torch.empty(B, dtype=torch.int32, device=DEV),
+                gather_buf=torch.zeros(B, K + W, D, dtype=torch.bfloat16, device=DEV),
+                n_valid=torch.empty(B, dtype=torch.int32, device=DEV),
+                out=torch.empty(B, shape.h, D, dtype=torch.bfloat16, device=DEV),
+                lse=torch.empty(B, shape.h, device=DEV))
+    io = csa.make_step_io(pos=x["pos"], q=x["q"], q_idx=x["q_idx"], w_idx=x["w_idx"], kv_new=x["kv_new"],
+                          z_main=x["z_main"], c_main=x["c_main"], z_idx=x["z_idx"], c_idx=x["c_idx"], **outs)
+    ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+    csa.csa_decode_step(L, io, ws)
+    torch.cuda.synchronize()
+    N = shape.n_comp
+    got_s8 = outs["scores"][0, :N].cpu().numpy().astype(np.float64)
+    exact_ref = oracle.index_score(host_f64(x["q_idx"][0])[None], x["w_idx"][0].cpu().numpy()[None].astype(np.float64),
+                                   host_f64(exact_keys[0, :N]))[0]
+    gi, gc = outs["topk_idx"][0].cpu().numpy(), int(outs["topk_count"][0])
+    _check_rescored_selection(csa, x["q_idx"], x["w_idx"], exact_keys, N, got_s8, gi, gc, exact_ref, K, kc)
+    ref = set(oracle.topk(exact_ref[None], K)[0][0].tolist())
+    recall = len(ref & set(gi.tolist())) / K
+    plain = len(ref & set(oracle.topk(got_s8[None], K)[0][0].tolist())) / K
+    print(f"top-512 recall at n=250000: two-stage {recall:.4f}, E4M3 alone {plain:.4f}")
+    assert recall >= 0.99
+    sel = host_f64(x["comp_kv"][0, torch.from_numpy(gi).to(DEV).long()])
+    nv = int(outs["n_valid"][0])
+    np.testing.assert_array_equal(host_f64(outs["gather_buf"][0, :gc]), sel)
+    assert nv == gc + W

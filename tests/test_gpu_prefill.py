@@ -278,7 +278,9 @@ def test_prefill_fp8_keys_full_size_sampled(csa):
     counts, the top-512 of 16 sampled rows bit-exact against the oracle's
     top-k of the same kernel's scores, the gap rule and the scores against
     the oracle's FP8 score on two rows; the overlap with the bf16 top-512 is
-    printed (E4M3 moves scores near the threshold: no parity bar)."""
+    the format's own figure (E4M3 moves crowded scores across the threshold;
+    the 0.99 gate is met by the two-stage selection,
+    test_prefill_fp8_rescored_full_size_recall)."""
     shape = synth.SHAPES["prefill"]
     x = synth.make_prefill_inputs_torch(shape, None, DEV)
     T, N, k = shape.t, shape.n_comp, shape.top_k
@@ -286,9 +288,8 @@ def test_prefill_fp8_keys_full_size_sampled(csa):
     ks = torch.empty(N, dtype=torch.float32, device=DEV)
     csa.csa_quantize_fp8(x["idx_keys"], kc, ks)
     qc = torch.empty(T, 64, 128, dtype=torch.uint8, device=DEV)
-    qs = torch.empty(T, 64, dtype=torch.float32, device=DEV)
-    csa.csa_quantize_fp8(x["q_idx"], qc, qs)
-    w8 = (x["w_idx"] * qs).contiguous()
+    w8 = torch.empty(T, 64, dtype=torch.float32, device=DEV)
+    csa.csa_quantize_query_fp8(x["q_idx"], x["w_idx"], qc, w8)
     idx, cnt = _run_index_topk_fp8(csa, qc, w8, kc, ks, k, x["pos0"])
     idx16, _ = _run_index_topk(csa, x["q_idx"], x["w_idx"], x["idx_keys"], k, x["pos0"])
     torch.cuda.synchronize()
@@ -316,7 +317,7 @@ def test_prefill_fp8_keys_full_size_sampled(csa):
     i16 = idx16.cpu().numpy()
     overlap = np.mean([len(set(gi[r]) & set(i16[r])) / k for r in range(0, T, 64)])
     print(f"fp8 vs bf16 top-512 overlap over 32 sampled queries: {overlap:.4f}")
-    assert overlap >= 0.85
+    assert overlap >= 0.85  # the format's figure; the gate needs the two-stage selection
 
 
 # ---------------------------------------------------------------------------
@@ -450,3 +451,117 @@ def test_prefill_full_size_sampled(csa):
         o, l = oracle.sparse_attn(qh[i], kv, sink, 1.0 / np.sqrt(shape.d))
         assert rel_err(outs[i], o) <= 2e-2
         assert np.abs(lse[r].cpu().numpy() - l).max() <= 1e-2
+
+
+# ---------------------------------------------------------------------------
+# E4M3 keys with the two-stage selection (E4M3 top-k_cand, then exact top-k)
+# ---------------------------------------------------------------------------
+
+RESCORED_CASES = [
+    # name, t, n, k, k_cand, pos0
+    ("two_chunks_causal", 300, 5000, 64, 128, 4 * 5000 - 400),
+    ("fewer_visible_than_cand", 40, 1000, 32, 96, 4 * 30),
+    ("no_mask_k_equal_cand", 20, 3000, 100, 100, -1),
+    ("ragged_chunk_k512", 270, 9000, 512, 1024, -1),
+]
+
+
+def _rescored_inputs(g, t, n):
+    f = numfmt.bf16_bits_to_f64
+    q = synth.to_bf16_bits((g.standard_normal((t, 64, 128)) / np.sqrt(128)).astype(np.float32))
+    w = g.standard_normal((t, 64)).astype(np.float32)
+    K = synth.to_bf16_bits(g.standard_normal((n, 128)).astype(np.float32))
+    kc, ks = numfmt.quantize_e4m3_rows(f(K).astype(np.float32))
+    qc, qs = numfmt.quantize_e4m3_rows(f(q).reshape(-1, 128).astype(np.float32))
+    return q, w, K, kc, ks, qc.reshape(t, 64, 128), (w * qs.reshape(t, 64)).astype(np.float32)
+
+
+def _check_rescored_rows(csa, rows, qd, wd, k16, kc_dev, ks_dev, qc, w8, pos0, n, k, kcand, gi, gc, exact_rows):
+    """Rows of the two-stage chunk selection: bit for bit the oracle's two
+    stages over the GPU's E4M3 and bf16 scan scores of those rows; the gap
+    rule against the float64 exact scores inside the first stage's set."""
+    # at least 16 rows per call, so the E4M3 scores come from the multi-query
+    # kernel the chunk's first stage uses (its float32 order is its own)
+    ext = list(rows) + [r for r in range(qc.shape[0]) if r not in rows][:max(0, 16 - len(rows))]
+    sel = torch.tensor(ext, device=DEV)
+    pos = None if pos0 < 0 else torch.from_numpy((pos0 + np.asarray(ext)).astype(np.int32)).to(DEV)[None]
+    s8 = torch.empty(1, len(ext), n, device=DEV)
+    s16 = torch.empty(1, len(ext), n, device=DEV)
+    csa.csa_index_score_fp8(torch.from_numpy(qc[ext]).to(DEV)[None], dev_f32(w8[ext])[None], kc_dev[None],
+                            ks_dev[None], s8, q_pos=pos)
+    csa.csa_index_score(qd[sel][None], wd[sel][None], k16[None], s16, q_pos=pos)
+    torch.cuda.synchronize()
+    s8 = s8[0, :len(rows)].cpu().numpy().astype(np.float64)
+    s16 = s16[0, :len(rows)].cpu().numpy().astype(np.float64)
+    want, wc = oracle.rescored_topk(s8, s16, k, kcand)
+    np.testing.assert_array_equal(gi[rows], want)
+    np.testing.assert_array_equal(gc[rows], wc)
+    for i, r in enumerate(rows):
+        stage1 = oracle.topk(s8[i][None], kcand)[0][0]
+        stage1 = stage1[stage1 >= 0]
+        inside = np.full(n, -np.inf)
+        inside[stage1] = exact_rows[i][stage1]
+        assert_topk_gap_rule(gi[r], int(gc[r]), inside, k)
+
+
+@pytest.mark.parametrize("case", RESCORED_CASES, ids=[c[0] for c in RESCORED_CASES])
+def test_index_topk_fp8_rescored(csa, case):
+    name, t, n, k, kcand, pos0 = case
+    g = _g(t * 3 + n + k + kcand)
+    q, w, K, kcn, ksn, qc, w8 = _rescored_inputs(g, t, n)
+    qd, wd, k16 = dev_bf16(q), dev_f32(w), dev_bf16(K)
+    kc_dev, ks_dev = torch.from_numpy(kcn).to(DEV), dev_f32(ksn)
+    idx = torch.full((t, k), -5, dtype=torch.int32, device=DEV)
+    cnt = torch.full((t,), -5, dtype=torch.int32, device=DEV)
+    ws = torch.empty(csa.csa_index_topk_fp8_rescored_workspace_size(t, n, k, kcand), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xCD)
+    print(f"rescored chunk {name}", flush=True)
+    csa.csa_index_topk_fp8_rescored(qd, wd, kc_dev, ks_dev, k16, idx, cnt, ws, kcand, pos0=pos0)
+    torch.cuda.synchronize()
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    if pos0 >= 0:
+        np.testing.assert_array_equal(gc, np.minimum(k, _visible(pos0 + np.arange(t), n)))
+    else:
+        assert (gc == min(k, n)).all()
+    rows = sorted({0, 1, t // 2, t - 1})
+    f = numfmt.bf16_bits_to_f64
+    qpos = None if pos0 < 0 else pos0 + np.asarray(rows)
+    exact = oracle.index_score(f(q[rows]), w[rows].astype(np.float64), f(K), q_pos=qpos)
+    _check_rescored_rows(csa, rows, qd, wd, k16, kc_dev, ks_dev, qc, w8, pos0, n, k, kcand, gi, gc, exact)
+
+
+def test_prefill_fp8_rescored_full_size_recall(csa):
+    """The 2048 x 65536 chunk over E4M3 keys with the two-stage selection
+    (top-512 of the E4M3 best 1024): sampled rows' selection exactly the
+    oracle's two stages, and top-512 recall against the float64 exact
+    indexer of at least 0.99 on each sampled row (the gate of page 1,
+    ARCHITECTURE_AND_MEMORY_AUDIT.md, Tier 1 gate 4)."""
+    shape = synth.SHAPES["prefill"]
+    x = synth.make_prefill_inputs_torch(shape, None, DEV)
+    T, N, k, kcand = shape.t, shape.n_comp, shape.top_k, 2 * shape.top_k
+    kc_dev = torch.empty(N, 128, dtype=torch.uint8, device=DEV)
+    ks_dev = torch.empty(N, dtype=torch.float32, device=DEV)
+    csa.csa_quantize_fp8(x["idx_keys"], kc_dev, ks_dev)
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    cnt = torch.empty(T, dtype=torch.int32, device=DEV)
+    ws = torch.empty(csa.csa_index_topk_fp8_rescored_workspace_size(T, N, k, kcand), dtype=torch.uint8, device=DEV)
+    csa.csa_index_topk_fp8_rescored(x["q_idx"], x["w_idx"], kc_dev, ks_dev, x["idx_keys"], idx, cnt, ws, kcand,
+                                    pos0=x["pos0"])
+    torch.cuda.synchronize()
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    pos = x["pos0"] + np.arange(T)
+    np.testing.assert_array_equal(gc, np.minimum(k, _visible(pos, N)))
+    rows = [0, 1, 255, 256, 1027, 2046, 2047]
+    f64q = host_f64(x["q_idx"][torch.tensor(rows, device=DEV)])
+    wq = x["w_idx"][torch.tensor(rows, device=DEV)].cpu().numpy()
+    exact = oracle.index_score(f64q, wq.astype(np.float64), host_f64(x["idx_keys"]), q_pos=pos[rows])
+    qc, qs = numfmt.quantize_e4m3_rows(host_f64(x["q_idx"]).reshape(-1, 128).astype(np.float32))
+    w8 = (x["w_idx"].cpu().numpy() * qs.reshape(T, 64)).astype(np.float32)
+    _check_rescored_rows(csa, rows, x["q_idx"], x["w_idx"], x["idx_keys"], kc_dev, ks_dev, qc.reshape(T, 64, 128), w8,
+                         x["pos0"], N, k, kcand, gi, gc, exact)
+    recalls = []
+    for i, r in enumerate(rows):
+        ref = set(oracle.topk(exact[i][None], k)[0][0][:gc[r]].tolist())
+        recalls.append(len(ref & set(gi[r, :gc[r]].tolist())) / max(len(ref), 1))
+    print("two-stage top-512 recall on sampled chunk rows:", [round(v, 4) for v in recalls])
+    assert min(recalls) >= 0.99
