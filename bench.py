@@ -643,6 +643,42 @@ def time_hca(csa, reps: int):
 
     us = replay(layer_steps(False))
     torch.cuda.empty_cache()
+    # the same bf16 layers through csa_hca_decode_step_dev: one graph, each
+    # replay the next token (counters on the device, from a block's first
+    # token, so no replay here completes into a full cache)
+    dev_steps = []
+    for x in xs:
+        L = csa.make_layer_desc(comp_kv=x["comp_kv"], idx_keys=None, swa=x["swa"], main_bias=x["main_bias"],
+                                idx_bias=None, sink=x["sink"], n_comp=x["n_comp"], swa_head=x["swa_head"],
+                                swa_len=x["swa_len"], h=shape.h, h_i=0, m=shape.m, top_k=0)
+        out = torch.empty(1, shape.h, shape.d, dtype=torch.bfloat16, device="cuda")
+        io = csa.make_step_io(pos=0, q=x["q"], kv_new=x["kv_new"], z_main=x["z_main"][:, 0].contiguous(),
+                              c_main=x["c_main"][:, 0].contiguous(), out=out)
+        first = x["pos"] - shape.m + 1
+        state = torch.tensor([first, x["n_comp"], first % shape.w, min(first, shape.w), 0], dtype=torch.int32,
+                             device="cuda")
+        ring = torch.zeros(csa.csa_hca_decode_step_dev_ring_size(L) // 4, device="cuda")
+        ws = torch.empty(csa.csa_hca_decode_step_workspace_size(L), dtype=torch.uint8, device="cuda")
+        dev_steps.append((L, io, state, ring, ws))
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for L, io, state, ring, ws in dev_steps:
+                csa.csa_hca_decode_step_dev(L, io, state, ring, ws, stream=stream)
+        g.replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(min(reps, shape.m - 2)):
+            g.replay()
+        e1.record(stream)
+    stream.synchronize()
+    us_dev = e0.elapsed_time(e1) * 1e3 / (min(reps, shape.m - 2) * len(dev_steps))
+    del dev_steps, g
+    torch.cuda.empty_cache()
     us_mixed = replay(layer_steps(True))
     n, d, w, h, m = shape.n_comp, shape.d, shape.w, shape.h, shape.m
     # cache rows + window + q read, out written; the block's Z/C read and the entry written; the new row appended
@@ -662,6 +698,10 @@ def time_hca(csa, reps: int):
         "alg_bytes_per_layer": alg,
         "achieved_gbps": round(alg / (us * 1e-6) / 1e9, 1),
         "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "device_counters": {
+            "workload": "the bf16 layers through csa_hca_decode_step_dev, one graph replayed token after token",
+            "us_per_layer": round(us_dev, 3),
+        },
         "mixed_kv": {
             "us_per_layer": round(us_mixed, 3),
             "steps_per_s_30_layers": round(1e6 / (us_mixed * 30), 1),

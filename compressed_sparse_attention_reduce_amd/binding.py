@@ -105,6 +105,9 @@ _SIGS = {
     "csa_decode_step_dev": (_i, [ctypes.POINTER(LayerDesc), ctypes.POINTER(StepIO), _vp, _vp, _sz, _vp, _sz, _vp]),
     "csa_hca_decode_step_workspace_size": (_sz, [ctypes.POINTER(LayerDesc)]),
     "csa_hca_decode_step": (_i, [ctypes.POINTER(LayerDesc), ctypes.POINTER(StepIO), _vp, _sz, _vp]),
+    "csa_hca_decode_step_dev_ring_size": (_sz, [ctypes.POINTER(LayerDesc)]),
+    "csa_hca_decode_step_dev": (_i, [ctypes.POINTER(LayerDesc), ctypes.POINTER(StepIO), _vp, _vp, _sz, _vp, _sz,
+                                     _vp]),
     "csa_index_topk_workspace_size": (_sz, [_i, _i, _i]),
     "csa_index_topk": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _ll, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_topk_fp8": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _ll, _i, _i, _vp, _vp, _vp, _sz, _vp]),
@@ -359,6 +362,20 @@ def csa_hca_decode_step_workspace_size(layer: LayerDesc) -> int:
 def csa_hca_decode_step(layer: LayerDesc, io: StepIO, ws, stream=None) -> None:
     _check(lib().csa_hca_decode_step(ctypes.byref(layer), ctypes.byref(io), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def csa_hca_decode_step_dev_ring_size(layer: LayerDesc) -> int:
+    return lib().csa_hca_decode_step_dev_ring_size(ctypes.byref(layer))
+
+
+def csa_hca_decode_step_dev(layer: LayerDesc, io: StepIO, state, ring, ws, stream=None) -> None:
+    """state: int32 [5] device tensor (pos, n_comp, swa_head, swa_len, flags);
+    ring: float32 device tensor of csa_hca_decode_step_dev_ring_size(layer) bytes."""
+    if state.dtype != torch.int32 or state.numel() < 5:
+        raise ValueError("state must be int32 [5]")
+    _check(lib().csa_hca_decode_step_dev(ctypes.byref(layer), ctypes.byref(io), _ptr(state), _ptr(ring),
+                                         ring.numel() * ring.element_size(), _ptr(ws), ws.numel() * ws.element_size(),
+                                         _stream(stream)))
 
 
 def csa_layer_advance(layer: LayerDesc, pos: int) -> None:

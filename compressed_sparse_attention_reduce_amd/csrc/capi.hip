@@ -746,63 +746,81 @@ int csa_decode_step_dev(const csa_layer_desc* L, const csa_step_io* io, csa_dev_
 size_t csa_hca_decode_step_workspace_size(const csa_layer_desc* L) {
     if (!L || L->batch < 1 || L->max_comp < 0 || L->w < 1 || L->h < 1 || L->d < 1) return 0;
     const size_t ns = static_cast<size_t>(csa::attn_dense_splits(L->max_comp + L->w));
-    // split partials, then (mixed KV) the new entry in float32 per sequence
+    // split partials, then (mixed KV) the new entry in float32 per sequence,
+    // then (device counters) the step's record for the merge
     return align256(sizeof(float) * static_cast<size_t>(L->batch) * L->h * ns * (static_cast<size_t>(L->d) + 2)) +
-           align256(sizeof(float) * static_cast<size_t>(L->batch) * L->d) + 256;
+           align256(sizeof(float) * static_cast<size_t>(L->batch) * L->d) + 256 + 256;
 }
 
-int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes,
-                        csa_stream stream) {
-    CHECK(L && io, "csa_hca_decode_step: null layer or io");
+size_t csa_hca_decode_step_dev_ring_size(const csa_layer_desc* L) {
+    if (!L || L->batch < 1 || L->m < 1 || L->d < 1) return 0;
+    return sizeof(float) * static_cast<size_t>(L->batch) * 4 * L->m * static_cast<size_t>(L->d);
+}
+
+// The HCA step; dev != nullptr: the counters are read from and advanced on
+// the device (csa_hca_decode_step_dev), the block's rows kept in `ring`.
+static int hca_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes, csa_stream stream,
+                    csa::DevState* dev, float* ring, size_t ring_bytes) {
+    const char* who = dev ? "csa_hca_decode_step_dev" : "csa_hca_decode_step";
+    CHECK(L && io, "%s: null layer or io", who);
     if (L->dtype != CSA_BF16)
-        return fail(CSA_ERR_UNSUPPORTED, "csa_hca_decode_step: bfloat16 caches only");
+        return fail(CSA_ERR_UNSUPPORTED, "%s: bfloat16 caches only", who);
     const bool mixed = L->kv_dtype == CSA_FP8_E4M3;
     if (mixed) {
         if (L->d != csa::kMixD || L->rope_dim != csa::kMixRope || L->main_norm)
-            return fail(CSA_ERR_UNSUPPORTED, "csa_hca_decode_step: mixed KV needs d = %d, rope_dim = %d, no main norm",
+            return fail(CSA_ERR_UNSUPPORTED, "%s: mixed KV needs d = %d, rope_dim = %d, no main norm", who,
                         csa::kMixD, csa::kMixRope);
         CHECK(L->rope_cos && L->rope_sin && L->comp_rope_cos && L->comp_rope_sin && L->rope_rows >= 1 &&
                   L->comp_rope_rows >= 1,
-              "csa_hca_decode_step: mixed KV needs both RoPE tables");
-        CHECK(io->pos < L->rope_rows, "csa_hca_decode_step: pos %d outside the RoPE table (%d rows)", io->pos,
+              "%s: mixed KV needs both RoPE tables", who);
+        CHECK(dev || io->pos < L->rope_rows, "%s: pos %d outside the RoPE table (%d rows)", who, io->pos,
               L->rope_rows);
-        CHECK(io->pos % L->m != L->m - 1 || io->pos / L->m < L->comp_rope_rows,
-              "csa_hca_decode_step: block %d outside the compressed-entry RoPE table (%d rows)", io->pos / L->m,
+        CHECK(dev || io->pos % L->m != L->m - 1 || io->pos / L->m < L->comp_rope_rows,
+              "%s: block %d outside the compressed-entry RoPE table (%d rows)", who, io->pos / L->m,
               L->comp_rope_rows);
         CHECK(L->comp_kv_stride_b % 16 == 0 && L->swa_stride_b % 16 == 0,
-              "csa_hca_decode_step: mixed records' batch strides must be multiples of 16 bytes");
+              "%s: mixed records' batch strides must be multiples of 16 bytes", who);
     }
-    CHECK(dtype_ok(L->out_dtype), "csa_hca_decode_step: bad out_dtype");
-    CHECK(L->batch >= 1 && L->m >= 1 && L->w >= 1, "csa_hca_decode_step: bad batch/m/w");
-    CHECK(L->overlap == 0, "csa_hca_decode_step: the HCA compressor is not overlapped (overlap must be 0)");
-    CHECK(L->comp_kv && L->swa && L->main_bias, "csa_hca_decode_step: null cache or bias pointer");
-    CHECK(io->q && io->kv_new && io->out, "csa_hca_decode_step: null io pointer");
-    CHECK(io->pos >= 0, "csa_hca_decode_step: pos < 0");
-    CHECK(L->n_comp >= 0 && L->n_comp <= L->max_comp, "csa_hca_decode_step: n_comp %d outside 0..max_comp %d",
-          L->n_comp, L->max_comp);
-    CHECK(L->swa_head >= 0 && L->swa_head < L->w && L->swa_len >= 0 && L->swa_len <= L->w,
-          "csa_hca_decode_step: bad SWA state");
-    const bool completes = io->pos % L->m == L->m - 1;
-    if (completes) {
-        CHECK(io->z_main && io->c_main, "csa_hca_decode_step: block rows missing");
-        CHECK(L->n_comp < L->max_comp, "csa_hca_decode_step: compressed cache full (max_comp %d)", L->max_comp);
+    CHECK(dtype_ok(L->out_dtype), "%s: bad out_dtype", who);
+    CHECK(L->batch >= 1 && L->m >= 1 && L->w >= 1, "%s: bad batch/m/w", who);
+    CHECK(L->overlap == 0, "%s: the HCA compressor is not overlapped (overlap must be 0)", who);
+    CHECK(L->comp_kv && L->swa && L->main_bias, "%s: null cache or bias pointer", who);
+    CHECK(io->q && io->kv_new && io->out, "%s: null io pointer", who);
+    if (dev) {
+        CHECK(aligned16(dev), "%s: state must be 16-byte aligned", who);
+        CHECK(io->z_main && io->c_main, "%s: the token's Z/C rows missing", who);
+        CHECK(ring && aligned16(ring), "%s: ring must be non-null and 16-byte aligned", who);
+        CHECK(ring_bytes >= csa_hca_decode_step_dev_ring_size(L), "%s: ring %zu < %zu bytes", who, ring_bytes,
+              csa_hca_decode_step_dev_ring_size(L));
+        CHECK(L->max_comp >= 1, "%s: max_comp must be positive", who);
+    } else {
+        CHECK(io->pos >= 0, "%s: pos < 0", who);
+        CHECK(L->n_comp >= 0 && L->n_comp <= L->max_comp, "%s: n_comp %d outside 0..max_comp %d", who, L->n_comp,
+              L->max_comp);
+        CHECK(L->swa_head >= 0 && L->swa_head < L->w && L->swa_len >= 0 && L->swa_len <= L->w,
+              "%s: bad SWA state", who);
+    }
+    // with device counters the launch is shaped for a completing step; the kernels decide
+    const bool completes = dev ? true : io->pos % L->m == L->m - 1;
+    if (completes && !dev) {
+        CHECK(io->z_main && io->c_main, "%s: block rows missing", who);
+        CHECK(L->n_comp < L->max_comp, "%s: compressed cache full (max_comp %d)", who, L->max_comp);
     }
     const int n_max = L->max_comp + L->w;
     if (n_max > csa::attn_max_rows())
-        return fail(CSA_ERR_UNSUPPORTED, "csa_hca_decode_step: max_comp + w = %d above %d rows", n_max,
-                    csa::attn_max_rows());
+        return fail(CSA_ERR_UNSUPPORTED, "%s: max_comp + w = %d above %d rows", who, n_max, csa::attn_max_rows());
     CHECK(L->h >= 16 && L->h % 16 == 0 && L->d >= 32 && L->d % 32 == 0 && L->d <= 512,
-          "csa_hca_decode_step: needs h a multiple of 16 and d a multiple of 32 up to 512");
-    CHECK(L->d <= csa::kPrepMaxD, "csa_hca_decode_step: head dim above %d", csa::kPrepMaxD);
+          "%s: needs h a multiple of 16 and d a multiple of 32 up to 512", who);
+    CHECK(L->d <= csa::kPrepMaxD, "%s: head dim above %d", who, csa::kPrepMaxD);
     CHECK(aligned16(io->q) && aligned16(L->comp_kv) && aligned16(L->swa) && aligned16(io->kv_new) &&
               aligned16(io->out),
-          "csa_hca_decode_step: q, caches, kv_new and out must be 16-byte aligned");
+          "%s: q, caches, kv_new and out must be 16-byte aligned", who);
     CHECK(io->q_stride_b % 8 == 0 && L->comp_kv_stride_b % 8 == 0 && L->swa_stride_b % 8 == 0 &&
               io->kv_new_stride_b % 8 == 0,
-          "csa_hca_decode_step: batch strides must keep 16-byte alignment");
-    if (!aligned16(ws)) return fail(CSA_ERR_INVALID_ARG, "csa_hca_decode_step: workspace must be 16-byte aligned");
+          "%s: batch strides must keep 16-byte alignment", who);
+    if (!aligned16(ws)) return fail(CSA_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", who);
     if (ws_bytes < csa_hca_decode_step_workspace_size(L))
-        return fail(CSA_ERR_WORKSPACE, "csa_hca_decode_step: workspace %zu < %zu bytes", ws_bytes,
+        return fail(CSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes,
                     csa_hca_decode_step_workspace_size(L));
     const hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -813,8 +831,8 @@ int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws
     pa.d = L->d;
     pa.m = L->m;
     pa.completes = completes ? 1 : 0;
-    pa.n_comp = L->n_comp;
-    pa.block = io->pos / L->m;
+    pa.n_comp = dev ? 0 : L->n_comp;
+    pa.block = dev ? 0 : io->pos / L->m;
     pa.kv_new = io->kv_new;
     pa.kv_new_stride_b = io->kv_new_stride_b;
     pa.swa = L->swa;
@@ -831,10 +849,20 @@ int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws
     // long blocks without a norm: channel slices over several workgroups
     pa.main_wgs = (L->m >= 32 && !L->main_norm) ? (L->d + 31) / 32 : 1;
     pa.kv_mixed = mixed ? 1 : 0;
-    if (mixed && completes) {
+    if (mixed && completes && !dev) {
         const long long row = static_cast<long long>(io->pos / L->m) * (csa::kMixRope / 2);
         pa.entry_cos = L->comp_rope_cos + row;
         pa.entry_sin = L->comp_rope_sin + row;
+    }
+    if (dev) {  // the token's own rows; the kernels keep the block in the ring
+        pa.dev = dev;
+        pa.max_comp = L->max_comp;
+        pa.swa_w = L->w;
+        pa.dev_ring = ring;
+        pa.ring_stride_b = static_cast<long long>(csa_hca_decode_step_dev_ring_size(L) / sizeof(float) / L->batch);
+        pa.comp_rope_cos = L->comp_rope_cos;
+        pa.comp_rope_sin = L->comp_rope_sin;
+        pa.comp_rope_rows = L->comp_rope_rows;
     }
 
     // c. attention over the rows before the step — the entries before it and
@@ -845,12 +873,12 @@ int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws
     a.q_stride_b = io->q_stride_b;
     a.comp_kv = static_cast<const uint16_t*>(L->comp_kv);
     a.comp_kv_stride_b = L->comp_kv_stride_b;
-    a.n_comp = L->n_comp;
+    a.n_comp = dev ? 0 : L->n_comp;
     a.dense = true;
     a.swa = static_cast<const uint16_t*>(L->swa);
     a.swa_stride_b = L->swa_stride_b;
-    a.swa_head = L->swa_head;
-    a.swa_len = (L->swa_len + 1 < L->w ? L->swa_len + 1 : L->w) - 1;
+    a.swa_head = dev ? 0 : L->swa_head;
+    a.swa_len = dev ? 0 : (L->swa_len + 1 < L->w ? L->swa_len + 1 : L->w) - 1;
     a.w = L->w;
     a.n_valid_out = io->n_valid;
     a.sink = L->sink;
@@ -865,16 +893,43 @@ int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws
     a.n_max = n_max;
     a.ws = ws;
     if (mixed) {
-        const long long row = static_cast<long long>(io->pos) * (csa::kMixRope / 2);
         a.kv_mixed = true;
-        a.inv_cos = L->rope_cos + row;
-        a.inv_sin = L->rope_sin + row;
+        if (!dev) {
+            const long long row = static_cast<long long>(io->pos) * (csa::kMixRope / 2);
+            a.inv_cos = L->rope_cos + row;
+            a.inv_sin = L->rope_sin + row;
+        }
     }
-    const void* x0 = completes && !mixed
+    if (dev) {
+        a.dev = dev;
+        a.m = L->m;
+        a.max_comp = L->max_comp;
+        a.rope_cos = L->rope_cos;
+        a.rope_sin = L->rope_sin;
+        a.rope_rows = L->rope_rows;
+        a.comp_rope_cos = L->comp_rope_cos;
+        a.comp_rope_sin = L->comp_rope_sin;
+        a.comp_rope_rows = L->comp_rope_rows;
+        // the step's record, in the last 256 bytes of the workspace
+        a.dev_pos = reinterpret_cast<int*>(static_cast<char*>(ws) + csa_hca_decode_step_workspace_size(L) - 256);
+        a.dev_adv = dev;
+    }
+    const void* x0 = completes && !mixed && !dev
                          ? static_cast<const char*>(L->comp_kv) + 2 * static_cast<long long>(L->n_comp) * L->d
                          : nullptr;
     return launched(csa::launch_attn_dense_bf16(a, pa, x0, L->comp_kv_stride_b, io->kv_new, io->kv_new_stride_b, s),
-                    "csa_hca_decode_step");
+                    who);
+}
+
+int csa_hca_decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws, size_t ws_bytes,
+                        csa_stream stream) {
+    return hca_step(L, io, ws, ws_bytes, stream, nullptr, nullptr, 0);
+}
+
+int csa_hca_decode_step_dev(const csa_layer_desc* L, const csa_step_io* io, csa_dev_state* state, float* ring,
+                            size_t ring_bytes, void* ws, size_t ws_bytes, csa_stream stream) {
+    CHECK(state, "csa_hca_decode_step_dev: null state");
+    return hca_step(L, io, ws, ws_bytes, stream, reinterpret_cast<csa::DevState*>(state), ring, ring_bytes);
 }
 
 int csa_layer_advance(csa_layer_desc* L, int pos) {

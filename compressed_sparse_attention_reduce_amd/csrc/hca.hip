@@ -76,22 +76,58 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
         hg = (id - n_full * groups) % groups;
     }
     const int b = blockIdx.y;
+    // device counters: the step's view of them (before its own append), and
+    // the record the merge reads instead of the state
+    bool dev_done = true;  // (host counters: whether a block completes is known on the host)
+    if (a.dev) {
+        const DevState st = dev_load(a.dev, a.w, a.max_comp);
+        dev_done = dev_completes(st, a.m, a.max_comp);
+        p.completes = dev_done ? 1 : 0;
+        p.n_comp = st.n_comp;
+        p.block = st.pos / a.m;
+        a.n_comp = st.n_comp;
+        a.swa_head = st.swa_head;
+        a.swa_len = (st.swa_len + 1 < a.w ? st.swa_len + 1 : a.w) - 1;
+        extra_rows = 1 + (dev_done ? 1 : 0);
+        if (a.dev_pos && id == 0 && b == 0 && threadIdx.x == 0) {
+            a.dev_pos[0] = st.pos;
+            a.dev_pos[1] = st.n_comp;
+            a.dev_pos[2] = dev_done ? 1 : 0;
+        }
+    }
     // A block this step completes is compressed here, fold_ch channels per
     // workgroup by the first ones (ratio-m blocks are long: one workgroup
     // alone would take longer than the attention).  Its rows are independent
     // of the attention's, which covers the entries before the step only.
-    const bool fold = fold_ch > 0 && id * fold_ch < p.d;  // uniform
+    // With device counters the block's rows come from the ring, to which
+    // each folding workgroup first adds its channels of the token's row.
+    const bool fold = fold_ch > 0 && id * fold_ch < p.d && dev_done;  // uniform
     auto fold_block = [&](float* scratch) {
         const float* z = p.z_main + b * p.zc_main_stride_b;
         const float* c = p.c_main + b * p.zc_main_stride_b;
         const int ch0 = id * fold_ch;
+        const int nch = min(fold_ch, p.d - ch0);
+        if (p.dev) {
+            const long long pos = p.block * p.m + p.m - 1;  // the completing token
+            float* rz = p.dev_ring + b * p.ring_stride_b;
+            float* rc = rz + 2LL * p.m * p.d;
+            const long long slot = pos % (2 * p.m);
+            for (int j = threadIdx.x; j < nch; j += blockDim.x) {
+                rz[slot * p.d + ch0 + j] = z[ch0 + j];
+                rc[slot * p.d + ch0 + j] = c[ch0 + j];
+            }
+            __syncthreads();
+            const long long cur = (p.block & 1) * static_cast<long long>(p.m) * p.d;
+            z = rz + cur;
+            c = rc + cur;
+        }
         if (entry_f32) {
             compress_block_slice(z, c, p.main_bias, entry_f32 + static_cast<long long>(b) * p.d, false, p.m, p.d, ch0,
-                                 min(fold_ch, p.d - ch0), scratch);
+                                 nch, scratch);
             return;
         }
         char* out = static_cast<char*>(p.comp_kv) + (b * p.comp_kv_stride_b + static_cast<long long>(p.n_comp) * p.d) * p.es;
-        compress_block_slice(z, c, p.main_bias, out, p.es == 2, p.m, p.d, ch0, min(fold_ch, p.d - ch0), scratch);
+        compress_block_slice(z, c, p.main_bias, out, p.es == 2, p.m, p.d, ch0, nch, scratch);
     };
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
@@ -297,6 +333,31 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge_rows(AttnArgs a, i
     __shared__ float2 part[kMergeWaves][kWave];
     __shared__ float xv[2][kMixD];  // mixed: the new rows' values as stored
     const int d = a.d;
+    if (a.dev) {
+        // device counters: the attention launch recorded (pos, n_comp,
+        // completes) as the step saw them; the new entry (if any), its
+        // record and the RoPE rows follow from it
+        const int pos = a.dev_pos[0];
+        const int n0 = a.dev_pos[1];
+        const bool done = a.dev_pos[2] != 0;
+        if (!done) {
+            x0 = nullptr;
+            x0f = nullptr;
+            rec0 = nullptr;
+        } else if (a.kv_mixed) {
+            rec0 = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(a.comp_kv)) + static_cast<long long>(n0) * kMixRec;
+        } else {
+            x0 = a.comp_kv + static_cast<long long>(n0) * d;
+        }
+        if (a.kv_mixed) {
+            const int blk = pos / a.m < a.comp_rope_rows ? pos / a.m : a.comp_rope_rows - 1;
+            entry_cos = a.comp_rope_cos + static_cast<long long>(blk) * (kMixRope / 2);
+            entry_sin = a.comp_rope_sin + static_cast<long long>(blk) * (kMixRope / 2);
+            const int pr = pos < a.rope_rows ? pos : a.rope_rows - 1;
+            a.inv_cos = a.rope_cos + static_cast<long long>(pr) * (kMixRope / 2);
+            a.inv_sin = a.rope_sin + static_cast<long long>(pr) * (kMixRope / 2);
+        }
+    }
     const int col_blocks = (d + kMergeCols - 1) / kMergeCols;
     const int hh = blockIdx.x / col_blocks;
     const int cb = blockIdx.x % col_blocks;
@@ -479,6 +540,8 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge_rows(AttnArgs a, i
         }
     }
     if (a.lse && cb == 0 && lane == 0) a.lse[static_cast<long long>(b) * a.h + hh] = M + logf(den);
+    // device counters: every reader of the state ran in the attention launch
+    if (a.dev_adv && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) dev_advance(a.dev_adv, a.m, a.w, a.max_comp);
 }
 
 }  // namespace

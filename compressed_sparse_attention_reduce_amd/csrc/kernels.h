@@ -227,6 +227,12 @@ struct AttnArgs {
     // after the advance within the step)
     int* dev_pos;
     DevState* dev_adv;
+    // HCA step with device counters: the entry RoPE tables by block index
+    // (mixed KV; blocks past the table use its last row); dev_pos then holds
+    // (pos, n_comp, completes) as the attention launch saw them
+    const float* comp_rope_cos;
+    const float* comp_rope_sin;
+    int comp_rope_rows;
 };
 size_t attn_workspace_bytes(bool bf16, int batch, int h, int d, int n_max);
 int attn_max_splits();

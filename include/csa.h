@@ -509,6 +509,31 @@ int csa_hca_decode_step(const csa_layer_desc *layer, const csa_step_io *io, void
                         size_t ws_bytes, csa_stream stream);
 
 /* ------------------------------------------------------------------------
+ * 6g. The HCA step with its counters on the device (graph replay).
+ *
+ * Source: page 3, GETTING+CUDAGRAPH_READY.md, Section C item 1 (the
+ * compressors' periodic host branch, 3/4 for CSA and 127/128 for HCA,
+ * becomes a persistent partial state with a device-side emit on the block
+ * boundary), items 2, 3 and 5, as for csa_decode_step_dev.
+ *
+ * csa_hca_decode_step_dev runs the same step as csa_hca_decode_step, with
+ * pos, n_comp, swa_head and swa_len read from `state` when its kernels run,
+ * the block boundary (pos % m == m - 1, with room in the cache) decided
+ * there, and the state advanced afterwards as csa_decode_step_dev advances
+ * it.  io->z_main, c_main are this token's rows only ([B][d]), every step;
+ * the step keeps the rows of the current and the previous block in `ring`
+ * (csa_hca_decode_step_dev_ring_size bytes of caller-owned device memory;
+ * the first block of a layer must be stepped from its first token).  A
+ * completed block that finds the cache full writes nothing and sets bit 0
+ * of state->flags.  With mixed KV, positions and blocks past the RoPE tables
+ * use the tables' last rows.  Other arguments, limits and errors as
+ * csa_hca_decode_step; the workspace is csa_hca_decode_step_workspace_size.
+ * ------------------------------------------------------------------------ */
+size_t csa_hca_decode_step_dev_ring_size(const csa_layer_desc *layer);
+int csa_hca_decode_step_dev(const csa_layer_desc *layer, const csa_step_io *io, csa_dev_state *state,
+                            float *ring, size_t ring_bytes, void *ws, size_t ws_bytes, csa_stream stream);
+
+/* ------------------------------------------------------------------------
  * 7. Prefill-shaped chunk: t query tokens at positions pos0, pos0+1, ...
  *    against one compressed history.
  *

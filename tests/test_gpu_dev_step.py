@@ -316,3 +316,200 @@ def test_dev_step_full_cache_sets_flag(csa):
     for k in ("scores", "topk_idx", "topk_count", "n_valid", "gather_buf", "out", "lse"):
         assert torch.equal(od[k], oh[k]), k
     assert torch.equal(sd, sh)
+
+
+# ---------------------------------------------------------------------------
+# HCA layers with device counters (csa_hca_decode_step_dev)
+# ---------------------------------------------------------------------------
+
+HCA_DEV_CASES = [
+    # name, ratio m, heads, entries before, capacity, window, batch, mixed KV, main norm, replays
+    ("ratio128_bf16_batch2", 128, 64, 20, 40, 16, 2, False, False, 130),
+    ("ratio8_mixed", 8, 16, 10, 60, 8, 1, True, False, 30),
+    ("ratio16_norm", 16, 32, 5, 30, 8, 1, False, True, 40),
+]
+
+
+@pytest.mark.parametrize("case", HCA_DEV_CASES, ids=[c[0] for c in HCA_DEV_CASES])
+def test_hca_dev_step_graph_replays(csa, case):
+    """One captured graph of csa_hca_decode_step_dev replayed step after step
+    from a block's first token across a block boundary (ratio 128: 130
+    replays, the block completing at the 128th); each replay against
+    oracle.hca_decode_step over the evolving state (the new entry within
+    rounding, then adopted; output and lse within the stated tolerances) and
+    bit for bit against csa_hca_decode_step with host counters."""
+    name, m, H, n0, max_comp, W, B, mixed, norm, steps = case
+    D = 512
+    g = _g(8201 + m + B)
+    f = numfmt.bf16_bits_to_f64
+    scale = 1 / np.sqrt(D)
+    pos0 = n0 * m  # a block's first token
+    comp_bits = synth.to_bf16_bits(g.standard_normal((B, max_comp, D), dtype=np.float32))
+    swa_bits = synth.to_bf16_bits(g.standard_normal((B, W, D), dtype=np.float32))
+    mb_np = g.standard_normal((m, D), dtype=np.float32) * np.float32(0.1)
+    sink_np = g.standard_normal(H, dtype=np.float32)
+    norm_np = (1 + 0.1 * g.standard_normal(D)).astype(np.float32) if norm else None
+    rope_np = _tables_np(pos0 + steps + 4, 0.5, 10000.0) if mixed else None
+    comp_rope_np = _tables_np(max_comp + 2, 0.25, 500.0) if mixed else None
+    rope = tuple(dev_f32(t) for t in rope_np) if mixed else None
+    comp_rope = tuple(dev_f32(t) for t in comp_rope_np) if mixed else None
+
+    def caches():
+        if mixed:
+            comp = torch.empty(B, max_comp, REC, dtype=torch.uint8, device=DEV)
+            swa = torch.empty(B, W, REC, dtype=torch.uint8, device=DEV)
+            csa.csa_pack_kv_mixed(dev_bf16(comp_bits), comp)
+            csa.csa_pack_kv_mixed(dev_bf16(swa_bits), swa)
+            return comp, swa
+        return dev_bf16(comp_bits), dev_bf16(swa_bits)
+
+    def layer(comp, swa):
+        return csa.make_layer_desc(comp_kv=comp, idx_keys=None, swa=swa, main_bias=dev_f32(mb_np), idx_bias=None,
+                                   sink=dev_f32(sink_np), n_comp=n0, swa_head=pos0 % W, swa_len=min(pos0, W), h=H,
+                                   h_i=0, m=m, top_k=0, main_norm=None if norm_np is None else dev_f32(norm_np),
+                                   rope=rope, comp_rope=comp_rope)
+
+    def outs():
+        return dict(out=torch.zeros(B, H, D, dtype=torch.bfloat16, device=DEV), lse=torch.zeros(B, H, device=DEV),
+                    n_valid=torch.zeros(B, dtype=torch.int32, device=DEV))
+
+    osts = []
+    for b in range(B):
+        if mixed:
+            _, comp_val = oracle_records(f(comp_bits[b]))
+            _, swa_val = oracle_records(f(swa_bits[b]))
+        else:
+            comp_val, swa_val = f(comp_bits[b]), f(swa_bits[b])
+        osts.append(oracle.LayerState(
+            comp_kv=comp_val.copy(), idx_keys=np.zeros((max_comp, 1)), n_comp=n0,
+            swa=oracle.SwaRing(swa_val.copy(), pos0 % W, min(pos0, W)), main_bias=mb_np.astype(np.float64),
+            idx_bias=np.zeros((m, 1)), sink=sink_np.astype(np.float64), m=m, round_cache=numfmt.bf16_round_f64,
+            main_norm=None if norm_np is None else norm_np.astype(np.float64), kv_mixed=mixed, rope_dim=ROPE,
+            rope_cos=rope_np[0].astype(np.float64) if mixed else None,
+            rope_sin=rope_np[1].astype(np.float64) if mixed else None,
+            comp_rope_cos=comp_rope_np[0].astype(np.float64) if mixed else None,
+            comp_rope_sin=comp_rope_np[1].astype(np.float64) if mixed else None))
+
+    ch, sh = caches()
+    Lh = layer(ch, sh)
+    cd, sd = caches()
+    Ld = layer(cd, sd)
+    st_in = dict(q=torch.zeros(B, H, D, dtype=torch.bfloat16, device=DEV),
+                 kv_new=torch.zeros(B, D, dtype=torch.bfloat16, device=DEV),
+                 z_main=torch.zeros(B, D, device=DEV), c_main=torch.zeros(B, D, device=DEV))
+    od = outs()
+    iod = csa.make_step_io(pos=0, **st_in, **od)
+    state = torch.tensor([pos0, n0, pos0 % W, min(pos0, W), 0], dtype=torch.int32, device=DEV)
+    ring = torch.zeros(csa.csa_hca_decode_step_dev_ring_size(Ld) // 4, device=DEV)
+    wsd = torch.empty(csa.csa_hca_decode_step_workspace_size(Ld), dtype=torch.uint8, device=DEV)
+    wsh = torch.empty(csa.csa_hca_decode_step_workspace_size(Lh), dtype=torch.uint8, device=DEV)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            csa.csa_hca_decode_step_dev(Ld, iod, state, ring, wsd, stream=stream)
+    torch.cuda.synchronize()
+
+    hist = {"z_main": [], "c_main": []}
+    completions = 0
+    for pos in range(pos0, pos0 + steps):
+        x = dict(q=synth.to_bf16_bits(g.standard_normal((B, H, D), dtype=np.float32)),
+                 kv_new=synth.to_bf16_bits(g.standard_normal((B, D), dtype=np.float32)),
+                 z_main=g.standard_normal((B, D), dtype=np.float32), c_main=g.standard_normal((B, D), dtype=np.float32))
+        for k in hist:
+            hist[k].append(x[k])
+        dev_in = {k: (dev_bf16(v) if v.dtype == np.uint16 else dev_f32(v)) for k, v in x.items()}
+        for k, v in dev_in.items():
+            st_in[k].copy_(v)
+        if pos % 16 == 0 or pos % m >= m - 2:
+            print(f"hca dev step {name} pos={pos}", flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        completes = pos % m == m - 1
+        blk_np = {k: np.ascontiguousarray(np.stack(hist[k][-m:], axis=1)) for k in hist}   # [B, <=m, D]
+        blk = {k: dev_f32(v) if completes else dev_f32(np.zeros((B, m, D), np.float32)) for k, v in blk_np.items()}
+        oh = outs()
+        ioh = csa.make_step_io(pos=pos, q=dev_in["q"], kv_new=dev_in["kv_new"], **blk, **oh)
+        slot = Lh.swa_head
+        csa.csa_hca_decode_step(Lh, ioh, wsh)
+        csa.csa_layer_advance(Lh, pos)
+        torch.cuda.synchronize()
+        N = Lh.n_comp
+        sv = state.cpu().numpy()
+        assert (sv[0], sv[1], sv[2], sv[3], sv[4]) == (pos + 1, N, Lh.swa_head, Lh.swa_len, 0), (pos, sv)
+        completions += int(completes)
+        for b in range(B):
+            ost = osts[b]
+            nb = ost.n_comp
+            r = oracle.hca_decode_step(ost, q=f(x["q"][b]), kv_new=f(x["kv_new"][b]), pos=pos,
+                                       z_main=blk_np["z_main"][b], c_main=blk_np["c_main"][b], scale=scale)
+            assert ost.n_comp == N
+            if mixed:
+                c_, s_, rp_, _ = oracle.mixed_kv_row(f(x["kv_new"][b]), ROPE)
+                np.testing.assert_array_equal(sd[b, slot].cpu().numpy(), record_of(c_, s_, rp_))
+            else:
+                np.testing.assert_array_equal(host_bits(sd[b, slot]), x["kv_new"][b])
+            if completes:  # the new entry within rounding of the oracle's, then the GPU's adopted
+                if mixed:
+                    _assert_entry_close(cd[b, nb].cpu().numpy(), ost.comp_kv[nb])
+                    ost.comp_kv[nb] = decode_records(cd[b, nb].cpu().numpy())
+                else:
+                    assert_bf16_close(host_bits(cd[b, nb]), r["new_entry"])  # (normalised when there is a norm)
+                    ost.comp_kv[nb] = host_f64(cd[b, nb])
+            win = r["rows"][nb + (1 if completes else 0):]
+            rows = np.concatenate([ost.comp_kv[:N], win])
+            ro, rl = oracle.sparse_attn(f(x["q"][b]), rows, ost.sink, scale)
+            if mixed:
+                ro = oracle.rope_rotate(ro, ost.rope_cos[pos], ost.rope_sin[pos], inverse=True)
+            assert int(od["n_valid"][b]) == rows.shape[0]
+            assert rel_err(host_f64(od["out"][b]), ro) <= 2e-2, (pos, b)
+            gl = od["lse"][b].cpu().numpy()
+            assert rel_err(gl, rl) <= 2e-2 and np.abs(gl - rl).max() <= 1e-2, (pos, b)
+        for k in ("out", "lse", "n_valid"):
+            assert torch.equal(od[k], oh[k]), (pos, k)
+        assert torch.equal(cd[:, :N], ch[:, :N]) and torch.equal(sd, sh)
+    assert completions >= 1
+
+
+def test_hca_dev_step_full_cache_sets_flag(csa):
+    """A ratio-8 block completing into a full cache writes nothing, keeps
+    n_comp and sets bit 0 of the flags; the attention is the host step's that
+    completes nothing (position one earlier, same state)."""
+    g = _g(8301)
+    B, D, H, W, m = 1, 512, 16, 8, 8
+    max_comp = n0 = 12
+    pos = n0 * m + m - 1
+    comp = dev_bf16(synth.to_bf16_bits(g.standard_normal((B, max_comp, D), dtype=np.float32)))
+    swa_bits = synth.to_bf16_bits(g.standard_normal((B, W, D), dtype=np.float32))
+    mb = dev_f32(g.standard_normal((m, D), dtype=np.float32))
+    sink = dev_f32(g.standard_normal(H, dtype=np.float32))
+    x = dict(q=dev_bf16(synth.to_bf16_bits(g.standard_normal((B, H, D), dtype=np.float32))),
+             kv_new=dev_bf16(synth.to_bf16_bits(g.standard_normal((B, D), dtype=np.float32))))
+    res = []
+    for dev in (True, False):
+        swa = dev_bf16(swa_bits)
+        L = csa.make_layer_desc(comp_kv=comp, idx_keys=None, swa=swa, main_bias=mb, idx_bias=None, sink=sink,
+                                n_comp=n0, swa_head=3, swa_len=W, h=H, h_i=0, m=m, top_k=0)
+        o = dict(out=torch.zeros(B, H, D, dtype=torch.bfloat16, device=DEV), lse=torch.zeros(B, H, device=DEV),
+                 n_valid=torch.zeros(B, dtype=torch.int32, device=DEV))
+        ws = torch.empty(csa.csa_hca_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+        before = comp.clone()
+        if dev:
+            io = csa.make_step_io(pos=0, **x, z_main=torch.ones(B, D, device=DEV), c_main=torch.ones(B, D, device=DEV),
+                                  **o)
+            state = torch.tensor([pos, n0, 3, W, 0], dtype=torch.int32, device=DEV)
+            ring = torch.zeros(csa.csa_hca_decode_step_dev_ring_size(L) // 4, device=DEV)
+            csa.csa_hca_decode_step_dev(L, io, state, ring, ws)
+            torch.cuda.synchronize()
+            assert state.cpu().tolist() == [pos + 1, n0, 4, W, 1]
+        else:
+            io = csa.make_step_io(pos=pos - 1, **x, z_main=torch.ones(B, m, D, device=DEV),
+                                  c_main=torch.ones(B, m, D, device=DEV), **o)
+            csa.csa_hca_decode_step(L, io, ws)
+            torch.cuda.synchronize()
+        assert torch.equal(comp, before)
+        res.append((o, swa))
+    (od, sd), (oh, sh) = res
+    for k in ("out", "lse", "n_valid"):
+        assert torch.equal(od[k], oh[k]), k
+    assert torch.equal(sd, sh)
