@@ -548,8 +548,11 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
                             : csa::index_score_bf16_keys_per_wg(L->batch, n_scan, prep_wgs);
         const int m = kpw > 0 ? csa::topk_cand_m(N, kc, kpw) : -1;
         const int mw = kpw > 0 ? csa::topk_cand_m(N, kc, kpw / csa::kScoreWavesPerWg) : -1;
+        // a scan workgroup's waves take consecutive 16-key tiles, the grid strides over the row
+        const int run = csa::kScoreWavesPerWg * 16;
+        const int scan_wgs = slots - (completes ? 1 : 0);
         if (m > 0 && slots <= kStepMaxSlots && (dev || N > 4 * kc))
-            ca = csa::CandArgs{static_cast<unsigned long long*>(tws), slots, m, mw < m ? mw : m};
+            ca = csa::CandArgs{static_cast<unsigned long long*>(tws), slots, m, mw < m ? mw : m, run, scan_wgs * run};
     }
     csa::ScoreArgs sa{io->q_idx, io->w_idx, L->idx_keys, io->scores, L->batch, 1, L->h_i, L->d_i, n_scan,
                       nullptr, L->m, io->q_idx_stride_b, io->w_stride_b, L->idx_keys_stride_b,

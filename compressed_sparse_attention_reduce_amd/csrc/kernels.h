@@ -33,6 +33,11 @@ struct CandArgs {
     int slots;
     int m;
     int mw;
+    // Which keys a slot lists (0: not stated): slot s < stride / run holds the
+    // keys whose position modulo stride lies in [s * run, (s + 1) * run); any
+    // slots past those list single keys in full (bound 0).
+    int run;
+    int stride;
 };
 // m for slots of keys_per_slot keys (also mw, for a wave's share of them),
 // or -1 if lists would be too long.

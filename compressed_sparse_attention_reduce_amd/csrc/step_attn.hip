@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_attn(TopkArgs ta, CandAr
     const bool done = c.lists && union_topk(fs, c, b, ta.k, sidx, k_eff);
     if (!done) {
         __syncthreads();  // the fast path's reads of LDS are over
-        k_eff = exact_row_topk(fs, score_row(ta, b), ta.n, ta.k, sidx);
+        k_eff = row_topk(fs, c, b, score_row(ta, b), ta.n, ta.k, sidx);
     }
     __syncthreads();  // sidx complete; the top-k LDS is free for the attention
     if (split == 0 && hg == 0) {
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_fp8_rescore(TopkArgs ta, Cand
     const bool done = c.lists && union_topk(fs, c, b, kc, sidx, k_eff);
     if (!done) {
         __syncthreads();
-        k_eff = exact_row_topk(fs, score_row(ta, b), ta.n, kc, sidx);
+        k_eff = row_topk(fs, c, b, score_row(ta, b), ta.n, kc, sidx);
     }
     __syncthreads();  // sidx complete
     unsigned long long* out = r.out + static_cast<long long>(b) * (kc + 1);

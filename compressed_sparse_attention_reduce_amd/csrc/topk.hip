@@ -19,12 +19,18 @@
 //     (entry m + 1 of a slot: at least the largest composite it did not
 //     keep).  If k entries remain they are provably the true top k; they are
 //     selected and sorted in one go (a radix digit placed where they differ,
-//     bin starts giving final positions, ranks inside each bin).  Otherwise
-//     (adversarial ties, or no candidates were produced) it runs an exact
-//     select over the whole row: 12-bit key histogram, threshold bin, further
-//     digits until the remaining candidates fit in LDS, then the same sorted
-//     select over them.
-// Either way the result is exact; only the time differs.
+//     bin starts giving final positions, ranks inside each bin).
+//   * otherwise, in order until one holds the candidates in LDS:
+//     - refine (the top k clustered in a few slots, e.g. recent blocks
+//       outscoring the cache): the k-th largest listed key bounds the answer
+//       from below; the slots whose bound reaches it are re-read from the
+//       score row, the others contribute their lists;
+//     - two streaming reads of the row (no lists, or many open slots): the
+//       k-th largest of the threads' maxima is the bound;
+//     - the exact select over the whole row (ties that keep more entries
+//       than LDS holds): 12-bit key histogram, threshold bin, further digits
+//       until the remaining candidates fit, then the same sorted select.
+// Every path is exact; only the time differs.
 #include <cmath>
 
 #include "common.h"
@@ -53,7 +59,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_topk_final(TopkArgs a, CandAr
     const bool done = c.lists && union_topk(sm, c, row, a.k, out, k_eff);
     if (!done) {
         __syncthreads();  // the fast path's reads of sm are over
-        k_eff = exact_row_topk(sm, score_row(a, row), a.n, a.k, out);
+        k_eff = row_topk(sm, c, row, score_row(a, row), a.n, a.k, out);
     }
     const int ns = static_cast<int>(k_eff);
     for (int j = ns + threadIdx.x; j < a.k; j += blockDim.x) out[j] = -1;
@@ -173,6 +179,8 @@ hipError_t launch_topk(const TopkArgs& a, const CandArgs* cands, hipStream_t s) 
             c.slots = slots;
             c.m = m;
             c.mw = mw < m ? mw : m;
+            c.run = kCandChunk;
+            c.stride = slots * kCandChunk;
             hipLaunchKernelGGL(k_topk_cands, dim3(slots, rows), dim3(kCandThreads), 0, s, a, c);
         }
     }

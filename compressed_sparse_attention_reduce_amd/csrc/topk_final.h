@@ -252,6 +252,236 @@ __device__ bool long_row_topk(FinalSmem& sm, const float* row, int n, int k, int
     return true;
 }
 
+// Rows of any length, in two streaming reads (long_row_topk's bound without
+// holding the row): thread t first takes the maximum of its elements t,
+// t + blockDim, ...; the k-th largest of those maxima bounds the k-th largest
+// score from below, so every entry in or above its 12-bit histogram bin is a
+// candidate; the second read compacts them into the pool for the sorted
+// select.  Strided elements spread a run of high scores over every thread, so
+// scores clustered by index (recent blocks) keep the candidates few.
+// Returns false (nothing written) when they overflow the pool (heavily tied
+// scores); the caller then takes the exact path.
+constexpr int kStreamBatch = 16;  // loads in flight per thread
+__device__ bool stream_row_topk(FinalSmem& sm, const float* row, int n, int k, int* out, uint32_t& k_eff) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int step = kStreamBatch * static_cast<int>(blockDim.x);
+    uint32_t tmax = 0;
+#pragma unroll 1
+    for (int base = 0; base < n; base += step) {
+        uint32_t key[kStreamBatch];
+#pragma unroll
+        for (int u = 0; u < kStreamBatch; ++u) key[u] = long_key(row, base + u * static_cast<int>(blockDim.x) + threadIdx.x, n);
+#pragma unroll
+        for (int u = 0; u < kStreamBatch; ++u) tmax = key[u] > tmax ? key[u] : tmax;
+    }
+    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) sm.hist[i] = 0;
+    if (threadIdx.x == 0) { sm.n_sel = 0; sm.n_pool = 0; }
+    __syncthreads();
+    if (tmax) atomicAdd(&sm.hist[tmax >> (32 - kHistBits)], 1u);
+    __syncthreads();
+    int tb;
+    uint32_t above, at, total;
+    block_threshold(sm.hist, kHistBins, static_cast<uint32_t>(k), tb, above, at, total);
+    // fewer than k thread maxima: every valid entry is a candidate
+    const uint32_t edge = tb >= 0 ? static_cast<uint32_t>(tb) << (32 - kHistBits) : 0u;
+    const uint32_t lo = edge > kKeyNegInf ? edge : kKeyNegInf + 1;
+#pragma unroll 1
+    for (int base = 0; base < n; base += step) {
+        uint32_t key[kStreamBatch];
+#pragma unroll
+        for (int u = 0; u < kStreamBatch; ++u) key[u] = long_key(row, base + u * static_cast<int>(blockDim.x) + threadIdx.x, n);
+        uint32_t c = 0;
+#pragma unroll
+        for (int u = 0; u < kStreamBatch; ++u) c += key[u] >= lo ? 1u : 0u;
+        uint32_t pre = c, sum = c;
+#define CSA_SCAN_STEP(o)                              \
+        {                                             \
+            const uint32_t other = xor_lanes<o>(sum); \
+            if (lane & (o)) pre += other;             \
+            sum += other;                             \
+        }
+        CSA_SCAN_STEP(1) CSA_SCAN_STEP(2) CSA_SCAN_STEP(4) CSA_SCAN_STEP(8) CSA_SCAN_STEP(16) CSA_SCAN_STEP(32)
+#undef CSA_SCAN_STEP
+        uint32_t wbase = 0;
+        if (lane == 0 && sum) wbase = atomicAdd(&sm.n_sel, sum);
+        wbase = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(wbase)));
+        uint32_t off = wbase + pre - c;
+        if (wbase + sum <= static_cast<uint32_t>(kUnionCap)) {  // else overflow: the total shows it
+#pragma unroll
+            for (int u = 0; u < kStreamBatch; ++u)
+                if (key[u] >= lo)
+                    sm.pool[off++] = composite(key[u], static_cast<uint32_t>(base + u * static_cast<int>(blockDim.x) +
+                                                                            threadIdx.x));
+        }
+    }
+    __syncthreads();
+    const uint32_t np = sm.n_sel;
+    if (np > static_cast<uint32_t>(kUnionCap)) return false;
+    u64 hi = 0, lo_c = 0;
+    for (uint32_t i = threadIdx.x; i < np; i += blockDim.x) {
+        hi = umax64(hi, sm.pool[i]);
+        lo_c = umax64(lo_c, ~sm.pool[i]);
+    }
+    block_max2(sm, hi, lo_c);
+    const int pb = np <= 1 ? 0 : __clzll(static_cast<long long>(hi ^ ~lo_c));
+    k_eff = select_sorted<kUnionRegs>(sm.pool, np, static_cast<uint32_t>(k), pb, out, sm.stage, sm.ss, &sm.n_pool);
+    return true;
+}
+
+// The candidate lists when they cannot prove the top k by themselves: the
+// k-th largest listed composite still bounds the k-th largest score from
+// below, so the top k lies among the listed entries at or above a lower bound
+// of it (two 12-bit digits of the key) and among the unlisted entries of the
+// slots whose bound reaches it ("open" slots).  The open slots' keys (as
+// c.run / c.stride lay them out) are read again from the score row; the
+// other slots contribute their lists, except entries whose key an open slot
+// covers (the new key's slot), so no index enters twice.  When the recent
+// keys outscore the rest of the cache, only the slots that hold them open and
+// a small part of the row is read.  Returns false (nothing written) when the
+// layout is not stated, the open slots cover more than a quarter of the row,
+// or the candidates overflow the pool.
+constexpr int kRefineMaxSlots = 2048;
+static_assert(sizeof(FinalSmem::stage) >= kRefineMaxSlots * sizeof(uint32_t), "open-slot list fits the stage");
+__device__ bool refine_topk(FinalSmem& sm, const CandArgs& c, int row, const float* srow, int n, int k, int* out,
+                            uint32_t& k_eff) {
+    if (!c.lists || c.run <= 0 || c.stride < c.run || c.stride % c.run != 0 || c.stride / c.run > c.slots ||
+        c.slots > kRefineMaxSlots)
+        return false;
+    const int m1 = c.m + 1;
+    const int total = c.slots * m1;
+    if (total > kUnionCap) return false;
+    const u64* lists = c.lists + static_cast<long long>(row) * total;
+    uint32_t* hist = sm.hist;
+    uint32_t* open_list = reinterpret_cast<uint32_t*>(sm.stage);
+    u64 v[kUnionRegs];
+#pragma unroll
+    for (int u = 0; u < kUnionRegs; ++u) {
+        const int i = threadIdx.x + u * kFinalThreads;
+        v[u] = i < total ? lists[i] : 0ull;
+    }
+    // 1. a lower bound of the k-th largest listed key: its top 12 bits, then the next 12
+    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) hist[i] = 0;
+    if (threadIdx.x == 0) { sm.n_sel = 0; sm.n_pool = 0; }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kUnionRegs; ++u) {
+        const int i = threadIdx.x + u * kFinalThreads;
+        const uint32_t hi = static_cast<uint32_t>(v[u] >> 32);
+        if (i % m1 != c.m && hi) atomicAdd(&hist[hi >> 20], 1u);
+    }
+    __syncthreads();
+    int tb;
+    uint32_t above, at, listed;
+    block_threshold(hist, kHistBins, static_cast<uint32_t>(k), tb, above, at, listed);
+    uint32_t edge = 0;
+    if (tb >= 0) {
+        for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kUnionRegs; ++u) {
+            const int i = threadIdx.x + u * kFinalThreads;
+            const uint32_t hi = static_cast<uint32_t>(v[u] >> 32);
+            if (i % m1 != c.m && hi && static_cast<int>(hi >> 20) == tb) atomicAdd(&hist[(hi >> 8) & 0xfffu], 1u);
+        }
+        __syncthreads();
+        int tb2;
+        uint32_t a2, t2, n2;
+        block_threshold(hist, kHistBins, static_cast<uint32_t>(k) - above, tb2, a2, t2, n2);
+        edge = (static_cast<uint32_t>(tb) << 20) | (static_cast<uint32_t>(tb2 < 0 ? 0 : tb2) << 8);
+    }
+    const uint32_t lo = edge > kKeyNegInf ? edge : kKeyNegInf + 1;
+    // 2. open slots: flags in hist (one word per slot), their indices in the stage
+    for (int i = threadIdx.x; i < c.slots; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    const int layout_slots = c.stride / c.run;  // slots past these list their keys in full
+    int unmapped = 0;                            // an open slot outside the layout
+#pragma unroll
+    for (int u = 0; u < kUnionRegs; ++u) {
+        const int i = threadIdx.x + u * kFinalThreads;
+        const bool reach = i < total && i % m1 == c.m && static_cast<uint32_t>(v[u] >> 32) >= lo;
+        const bool open = reach && i / m1 < layout_slots;
+        unmapped |= reach && !open;
+        const uint32_t p = wave_append_pos(open, &sm.n_pool);
+        if (open) {
+            hist[i / m1] = 1u;
+            open_list[p] = static_cast<uint32_t>(i / m1);
+        }
+    }
+    if (__syncthreads_or(unmapped)) return false;
+    const uint32_t n_open = sm.n_pool;
+    const uint32_t runs = static_cast<uint32_t>((static_cast<long long>(n) + c.stride - 1) / c.stride);
+    const uint32_t per_slot = runs * static_cast<uint32_t>(c.run);
+    const long long span_ll = static_cast<long long>(n_open) * per_slot;
+    if (span_ll > n / 4 + c.run) return false;  // the streaming reads are cheaper
+    const uint32_t span = static_cast<uint32_t>(span_ll);
+    // 3. candidates: listed entries at or above lo whose key no open slot covers ...
+#pragma unroll
+    for (int u = 0; u < kUnionRegs; ++u) {
+        const int i = threadIdx.x + u * kFinalThreads;
+        const uint32_t hi = static_cast<uint32_t>(v[u] >> 32);
+        bool keep = i < total && i % m1 != c.m && hi >= lo;
+        if (keep) {
+            const uint32_t idx = ~static_cast<uint32_t>(v[u]);
+            keep = hist[(idx % static_cast<uint32_t>(c.stride)) / static_cast<uint32_t>(c.run)] == 0u;
+        }
+        const uint32_t p = wave_append_pos(keep, &sm.n_sel);
+        if (keep && p < static_cast<uint32_t>(kUnionCap)) sm.pool[p] = v[u];
+    }
+    // ... and the open slots' keys at or above lo, read from the score row
+    const uint32_t run = static_cast<uint32_t>(c.run), stride = static_cast<uint32_t>(c.stride);
+#pragma unroll 1
+    for (uint32_t base = 0; base < span; base += kStreamBatch * blockDim.x) {
+        uint32_t key[kStreamBatch];
+        int at_i[kStreamBatch];
+#pragma unroll
+        for (int u = 0; u < kStreamBatch; ++u) {
+            const uint32_t f = base + u * blockDim.x + threadIdx.x;
+            int x = n;  // past the row: key 0
+            if (f < span) {
+                const uint32_t o = f / per_slot;
+                const uint32_t rest = f - o * per_slot;
+                const uint32_t j = rest / run;
+                x = static_cast<int>(open_list[o] * run + j * stride + (rest - j * run));
+            }
+            at_i[u] = x;
+            key[u] = long_key(srow, x, n);
+        }
+#pragma unroll
+        for (int u = 0; u < kStreamBatch; ++u) {
+            const bool keep = key[u] >= lo;
+            const uint32_t p = wave_append_pos(keep, &sm.n_sel);
+            if (keep && p < static_cast<uint32_t>(kUnionCap))
+                sm.pool[p] = composite(key[u], static_cast<uint32_t>(at_i[u]));
+        }
+    }
+    __syncthreads();
+    const uint32_t np = sm.n_sel;
+    if (np > static_cast<uint32_t>(kUnionCap)) return false;
+    // 4. the sorted select over them (it reuses the hist words and the stage)
+    u64 hi = 0, lo_c = 0;
+    for (uint32_t i = threadIdx.x; i < np; i += blockDim.x) {
+        hi = umax64(hi, sm.pool[i]);
+        lo_c = umax64(lo_c, ~sm.pool[i]);
+    }
+    block_max2(sm, hi, lo_c);
+    const int pb = np <= 1 ? 0 : __clzll(static_cast<long long>(hi ^ ~lo_c));
+    k_eff = select_sorted<kUnionRegs>(sm.pool, np, static_cast<uint32_t>(k), pb, out, sm.stage, sm.ss, &sm.n_pool);
+    return true;
+}
+
+// The exact top-k of a row once the candidate lists alone cannot prove it:
+// the lists refined by a partial re-read, else the two streaming reads of
+// stream_row_topk, else the exact radix path when tied scores overflow them.
+__device__ inline uint32_t row_topk(FinalSmem& sm, const CandArgs& c, int row, const float* srow, int n, int k,
+                                    int* out) {
+    uint32_t k_eff = 0;
+    if (refine_topk(sm, c, row, srow, n, k, out, k_eff)) return k_eff;
+    __syncthreads();
+    if (stream_row_topk(sm, srow, n, k, out, k_eff)) return k_eff;
+    __syncthreads();  // the streaming path's LDS reads are over
+    return exact_row_topk(sm, srow, n, k, out);
+}
+
 // Fast path: top-k of the union of per-slot candidates, as sorted indices
 // into out.  Returns false if the union cannot prove the answer.
 __device__ bool union_topk(FinalSmem& sm, const CandArgs& c, int row, int k, int* out, uint32_t& k_eff) {

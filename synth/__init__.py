@@ -287,3 +287,31 @@ def make_prefill_inputs_torch(shape: Shape, seed: Optional[int], device) -> dict
 def with_(shape: Shape, **kw) -> Shape:
     """A copy of ``shape`` with some fields changed (edge-case workloads)."""
     return replace(shape, **kw)
+
+
+def cluster_direction(q_idx, w_idx):
+    """Unit direction ``[B, d]`` of each sequence's indexer query heads with
+    positive weight (their weighted sum); keys along it score high."""
+    w = w_idx.float().clamp(min=0.0)
+    u = (w[..., None] * q_idx.float()).sum(dim=1)
+    return u / u.norm(dim=-1, keepdim=True).clamp(min=1e-30)
+
+
+def cluster_recent_keys(idx_keys, q_idx, w_idx, end: int, count: int, seed: int, strength: float = 20.0):
+    """Recent-context locality, in place: the ``count`` indexer keys before
+    block ``end`` of every sequence are redrawn as unit normal noise plus
+    ``strength`` times the unit direction of that sequence's query heads with
+    positive weight (their weighted sum).  Those keys then outscore the rest
+    of the cache, so the whole top-k falls in a few neighbouring blocks — the
+    case in which per-slice candidate lists cannot prove the selection.
+
+    ``idx_keys`` ``[B, N, d]``, ``q_idx`` ``[B, H, d]``, ``w_idx`` ``[B, H]``:
+    torch tensors on one device."""
+    import torch
+    B, _, di = idx_keys.shape
+    u = cluster_direction(q_idx, w_idx)
+    gen = torch.Generator(device=idx_keys.device)
+    gen.manual_seed(seed)
+    noise = torch.randn(B, count, di, generator=gen, device=idx_keys.device, dtype=torch.float32)
+    idx_keys[:, end - count:end] = (noise + strength * u[:, None, :]).to(idx_keys.dtype)
+    return idx_keys

@@ -551,12 +551,12 @@ def test_decode_step(csa, case):
         _check_step(x, shape, st, outs, b)
 
 
-def test_decode_step_clustered_scores_take_exact_path(csa):
+def test_decode_step_clustered_scores_refine_lists(csa):
     """600 consecutive indexer keys set to copies of the best key: every tile
     they fall in holds 16 of the top k, more than any candidate list keeps, so
-    the union cannot prove the answer and the top-k takes the exact select over
-    the score row.  The result must still be the oracle's, ties between the
-    copies broken by the lower index."""
+    the union cannot prove the answer; the top-k re-reads the slots whose
+    bound reaches the k-th largest listed key.  The result must still be the
+    oracle's, ties between the copies broken by the lower index."""
     shape = synth.with_(synth.SHAPES["ctx8k"], ctx=131072, n_comp=32768)
     x = synth.make_decode_inputs(shape, 4001)
     n0 = x["n_comp"]
@@ -567,6 +567,22 @@ def test_decode_step_clustered_scores_take_exact_path(csa):
     # the scenario happened: the selection is (all but possibly one of) the copies
     gi = outs["topk_idx"][0].cpu().numpy()
     assert np.isin(gi, np.arange(10000, 10600)).sum() >= shape.top_k - 1
+
+
+@pytest.mark.parametrize("n_comp", [2048, 32768])
+def test_decode_step_all_scores_tied(csa, n_comp):
+    """Every indexer key equal, so every score ties: the top k is the first k
+    blocks.  At 32,768 blocks neither the lists, their refinement nor the
+    streaming select can narrow the row to fewer than the pool holds, so the
+    exact radix select decides; at 2048 (no lists) the streaming select
+    holds the whole row."""
+    shape = synth.with_(synth.SHAPES["ctx8k"], ctx=4 * n_comp, n_comp=n_comp)
+    x = synth.make_decode_inputs(shape, 4004)
+    x["idx_keys"][0, :] = x["idx_keys"][0, 0]
+    x["c_idx"][0, :] = 0.0
+    x["idx_bias"][:] = 0.0
+    st, outs, _ = _run_step(csa, x, shape)
+    _check_step(x, shape, st, outs, 0)
 
 
 def test_decode_step_long_top_k_without_candidate_lists(csa):
@@ -586,11 +602,25 @@ def test_decode_step_batch128k_full_size(csa):
         _check_step(x, shape, st, outs, b)
 
 
-def test_decode_step_ctx1m_full_size(csa):
+CLUSTER_KEYS = 4096
+
+
+@pytest.mark.parametrize("clustered", [0, 1, 2], ids=["random_keys", "clustered_recent_keys", "clustered_new_key"])
+def test_decode_step_ctx1m_full_size(csa, clustered):
     """One layer of the 1M-context workload (n_comp 250,000, SWA wrap) through
-    csa_decode_step, as the benchmark runs it; the oracle scores every key."""
+    csa_decode_step, as the benchmark runs it; the oracle scores every key.
+    Clustered: the 4096 most recent keys outscore the rest of the cache, so
+    the candidate lists cannot prove the top-k and the step refines them by
+    re-reading the slots that hold those keys.  With the new key: the block
+    the step compresses lies along the same direction (every compressor row
+    of the indexer holds it), so it tops the selection from its own list
+    while the scan slot its position maps to is re-read."""
     shape = synth.SHAPES["ctx1m"]
     x = synth.make_decode_inputs_torch(shape, seed=None, device=DEV, layers=1)[0]
+    if clustered:
+        synth.cluster_recent_keys(x["idx_keys"], x["q_idx"], x["w_idx"], x["n_comp"], CLUSTER_KEYS, seed=4003)
+    if clustered == 2:
+        x["c_idx"][:] = 40.0 * synth.cluster_direction(x["q_idx"], x["w_idx"])[:, None, :]
     B, K, W, D = shape.batch, shape.top_k, shape.w, shape.d
     pristine_keys = x["idx_keys"][0, : x["n_comp"]].clone()
     L = csa.make_layer_desc(comp_kv=x["comp_kv"], idx_keys=x["idx_keys"], swa=x["swa"],
@@ -622,6 +652,10 @@ def test_decode_step_ctx1m_full_size(csa):
     oi, oc = oracle.topk(got_s[None], K)
     np.testing.assert_array_equal(gi, oi[0])
     assert_topk_gap_rule(gi, int(outs["topk_count"][0]), ref_s, K)
+    if clustered:  # the scenario happened: the whole selection lies in the recent keys
+        assert (gi >= x["n_comp"] - CLUSTER_KEYS).all()
+    if clustered == 2:
+        assert gi[0] == x["n_comp"]
     sel = host_f64(x["comp_kv"][0, torch.from_numpy(gi).to(DEV).long()])
     swa_rows = host_f64(x["swa"][0])
     head = (x["swa_head"] + 1) % W
