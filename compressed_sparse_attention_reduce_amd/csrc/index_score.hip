@@ -248,32 +248,59 @@ __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs
                 a.cands.lists + (static_cast<long long>(row) * a.cands.slots + wg) * (a.cands.m + 1), cs);
 }
 
-// float32 path (small correctness workloads): one thread per key, the query
-// and head weights staged in LDS and read as broadcasts.
+// float32 path (small correctness workloads): lane h of a wave takes indexer
+// head h (h_i <= 64), so a key's 64 dot products run side by side and one
+// wave-wide sum gives its score.  A workgroup stages the query (row pitch
+// d_i + 1: lanes reading one column hit distinct banks), the head weights and
+// its 16 keys in LDS; each wave scores 4 keys at once, reading every query
+// element once for all four.
 constexpr int kScoreF32Threads = 256;
+constexpr int kScoreF32Keys = 16;
+constexpr int kScoreF32PerWave = kScoreF32Keys / (kScoreF32Threads / kWave);
 
 __global__ __launch_bounds__(kScoreF32Threads) void k_index_score_f32(ScoreArgs a) {
-    extern __shared__ float qs[];  // [h_i * d_i] query, then [h_i] weights
+    extern __shared__ float qs[];  // [h_i][d_i + 1] query, [h_i] weights, [16][d_i] keys
     const int row = blockIdx.y;
     const int b = row / a.t;
     const int tt = row - b * a.t;
-    const int hd = a.h_i * a.d_i;
-    const float* qrow = static_cast<const float*>(a.q) + b * a.q_stride_b + static_cast<long long>(tt) * hd;
+    const int di = a.d_i;
+    const int qp = di + 1;
+    float* ws = qs + a.h_i * qp;
+    float* ks = ws + a.h_i;
+    const float* qrow = static_cast<const float*>(a.q) + b * a.q_stride_b + static_cast<long long>(tt) * a.h_i * di;
     const float* wrow = a.w + b * a.w_stride_b + static_cast<long long>(tt) * a.h_i;
-    for (int i = threadIdx.x; i < hd; i += blockDim.x) qs[i] = qrow[i];
-    for (int i = threadIdx.x; i < a.h_i; i += blockDim.x) qs[hd + i] = wrow[i];
+    for (int i = threadIdx.x; i < a.h_i * di; i += blockDim.x) qs[(i / di) * qp + i % di] = qrow[i];
+    for (int i = threadIdx.x; i < a.h_i; i += blockDim.x) ws[i] = wrow[i];
+    const int key0 = blockIdx.x * kScoreF32Keys;
+    const float* kbase = static_cast<const float*>(a.k) + b * a.k_stride_b;
+    for (int i = threadIdx.x; i < kScoreF32Keys * di; i += blockDim.x) {
+        const int key = key0 + i / di;
+        ks[i] = key < a.n ? kbase[static_cast<long long>(key) * di + i % di] : 0.f;
+    }
     __syncthreads();
-    const int key = blockIdx.x * blockDim.x + threadIdx.x;
-    if (key < a.n) {
-        const float* kr = static_cast<const float*>(a.k) + b * a.k_stride_b + static_cast<long long>(key) * a.d_i;
-        float sc = 0.f;
-        for (int h = 0; h < a.h_i; ++h) {
-            float dot = 0.f;
-            for (int d = 0; d < a.d_i; ++d) dot += qs[h * a.d_i + d] * kr[d];
-            sc += qs[hd + h] * fmaxf(dot, 0.f);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int j0 = (threadIdx.x / kWave) * kScoreF32PerWave;  // this wave's first key of the workgroup
+    const int h = lane < a.h_i ? lane : 0;
+    const float* qh = qs + h * qp;
+    const float* kj = ks + j0 * di;
+    float dot[kScoreF32PerWave] = {};
+    for (int d = 0; d < di; ++d) {
+        const float qv = qh[d];
+#pragma unroll
+        for (int u = 0; u < kScoreF32PerWave; ++u) dot[u] = fmaf(qv, kj[u * di + d], dot[u]);
+    }
+    float sc[kScoreF32PerWave];
+#pragma unroll
+    for (int u = 0; u < kScoreF32PerWave; ++u) sc[u] = wave_sum(lane < a.h_i ? ws[h] * fmaxf(dot[u], 0.f) : 0.f);
+    if (lane < kScoreF32PerWave) {
+        float v = sc[0];
+#pragma unroll
+        for (int u = 1; u < kScoreF32PerWave; ++u) v = lane == u ? sc[u] : v;
+        const int key = key0 + j0 + lane;
+        if (key < a.n) {
+            if (a.q_pos && static_cast<long long>(a.ratio) * key + a.ratio - 1 > a.q_pos[row]) v = -INFINITY;
+            a.scores[b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s + key] = v;
         }
-        if (a.q_pos && static_cast<long long>(a.ratio) * key + a.ratio - 1 > a.q_pos[row]) sc = -INFINITY;
-        a.scores[b * a.s_stride_b + static_cast<long long>(tt) * a.ld_s + key] = sc;
     }
 }
 
@@ -324,8 +351,10 @@ hipError_t launch_index_score_bf16(const ScoreArgs& a, const PrepArgs* fold, hip
 hipError_t launch_index_score_f32(const ScoreArgs& a, hipStream_t s) {
     if (a.n == 0) return hipSuccess;
     const int rows = a.batch * a.t;
-    const size_t lds = sizeof(float) * (static_cast<size_t>(a.h_i) * a.d_i + a.h_i);
-    hipLaunchKernelGGL(k_index_score_f32, dim3((a.n + kScoreF32Threads - 1) / kScoreF32Threads, rows),
+    if (a.h_i > kWave) return hipErrorInvalidValue;
+    const size_t lds =
+        sizeof(float) * (static_cast<size_t>(a.h_i) * (a.d_i + 1) + a.h_i + static_cast<size_t>(kScoreF32Keys) * a.d_i);
+    hipLaunchKernelGGL(k_index_score_f32, dim3((a.n + kScoreF32Keys - 1) / kScoreF32Keys, rows),
                        dim3(kScoreF32Threads), lds, s, a);
     return hipGetLastError();
 }
