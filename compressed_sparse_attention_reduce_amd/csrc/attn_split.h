@@ -3,6 +3,8 @@
 // step (step_attn.hip).  See attn.hip for the method and its sources.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "mixed_kv.h"
@@ -38,6 +40,99 @@ struct AttnSplit {
     static constexpr int kChunks = (kR * 64 + NT - 1) / NT;          // row pieces per thread at d = 512
     static_assert(kWaves >= kNt, "one wave per 16-row tile");
 };
+
+// Row and 16-byte chunk of the pieces c = threadIdx.x + u * NT (u < N) of a
+// tile with cpr chunks per row: shifts and adds when NT is a multiple of cpr
+// (power-of-two head dims), one division per piece otherwise.  (A division
+// per piece is tens of instructions on every lane; across a tile's pieces it
+// delays the issue of the row loads by microseconds.)
+template <int NT, int N>
+__device__ inline void piece_rows(int cpr, int (&r)[N], int (&p)[N]) {
+    if (NT % cpr == 0) {
+        const int rt = threadIdx.x / cpr;
+        const int pt = threadIdx.x - rt * cpr;
+        const int dr = NT / cpr;
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            r[u] = rt + u * dr;
+            p[u] = pt;
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const int c = threadIdx.x + u * NT;
+            r[u] = c / cpr;
+            p[u] = c - r[u] * cpr;
+        }
+    }
+}
+
+// Ring slot of window row i (0 = the oldest of the len live rows; 0 <= i <
+// len <= w, head < w): head - len + i lies in (-w, w).
+__device__ inline int swa_slot(int head, int len, int i, int w) {
+    const int s = head - len + i;
+    return s < 0 ? s + w : s;
+}
+
+// O = P V for a group of 16 * P columns of d starting at c_base (P = 2 or 4):
+// M = 16 heads, K = rows in 32-row steps, N = columns.  Lane (li, lg) reads
+// P adjacent columns (c_base + P li ..) of each of its 8 rows per step with
+// one LDS read per row (4 or 8 bytes); byte permutes (v_perm_b32) regroup
+// them into the B operands of P MFMAs (dword j: rows 2j and 2j + 1 of one
+// column), so P MFMAs share 8 reads instead of taking 8 two-byte reads each.
+// Accumulator t holds column c_base + P li + t; each head's P values leave as
+// one store of P floats to ob[head * ob_head_stride + column].  Columns at or
+// past d (a last, partial group) read column 0 and store nothing.
+template <int P>
+__device__ inline void pv_group(const uint16_t* tile, int pitch, const uint16_t* pl, int ppitch, int ksteps,
+                                int c_base, int d, float* ob, long long ob_head_stride) {
+    static_assert(P == 2 || P == 4, "two or four columns per lane");
+    using Piece = typename std::conditional<P == 2, uint32_t, uint2>::type;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+    const int cp = c_base + P * li;
+    const bool cv = cp < d;
+    const int cr = cv ? cp : 0;
+    f32x4 o[P];
+#pragma unroll
+    for (int t = 0; t < P; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < ksteps; ++ks) {
+        const bf16x8 pa = *reinterpret_cast<const bf16x8*>(pl + li * ppitch + 32 * ks + 8 * lg);
+        Piece rv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rv[e] = *reinterpret_cast<const Piece*>(tile + (32 * ks + 8 * lg + e) * pitch + cr);
+#pragma unroll
+        for (int t = 0; t < P; ++t) {
+            const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+            uint32_t wd[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t lo, hi;
+                if constexpr (P == 2) {
+                    lo = rv[2 * j];
+                    hi = rv[2 * j + 1];
+                } else {
+                    lo = t < 2 ? rv[2 * j].x : rv[2 * j].y;
+                    hi = t < 2 ? rv[2 * j + 1].x : rv[2 * j + 1].y;
+                }
+                wd[j] = __builtin_amdgcn_perm(hi, lo, sel);
+            }
+            bf16x8 vb;
+            __builtin_memcpy(&vb, wd, sizeof(vb));
+            o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[t], 0, 0, 0);
+        }
+    }
+    if (!cv) return;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float* dst = ob + static_cast<long long>(4 * lg + r) * ob_head_stride + cp;
+        if constexpr (P == 2)
+            *reinterpret_cast<float2*>(dst) = make_float2(o[0][r], o[1][r]);
+        else
+            *reinterpret_cast<float4*>(dst) = make_float4(o[0][r], o[1][r], o[2][r], o[3][r]);
+    }
+}
 
 // The query group's loads (independent of everything else: issued first).
 template <int NT>
@@ -79,13 +174,13 @@ __device__ inline void attn_split(const AttnArgs& a, int n_splits, int split, in
     // valid rows (gather mode: top-k count + window).  The top-k index of
     // every row a thread's chunks fall in is read alongside the count, so
     // the row loads wait for one round trip only.
-    const int n_chunks = kR * cpr;
+    int pr[G::kChunks], pc[G::kChunks];  // each piece's row of the split (kR and up: none) and chunk
+    piece_rows<NT>(cpr, pr, pc);
     int my_idx[G::kChunks];
 #pragma unroll
     for (int u = 0; u < G::kChunks; ++u) {
-        const int c = u * NT + threadIdx.x;
-        const int j = r0 + c / cpr;
-        my_idx[u] = a.dense ? j : ((a.idx && c < n_chunks && j < a.k) ? rows_idx[j] : 0);
+        const int j = r0 + pr[u];
+        my_idx[u] = a.dense ? j : ((a.idx && pr[u] < kR && j < a.k) ? rows_idx[j] : 0);
     }
     int cnt = 0, nv;
     if (a.idx || a.dense) {
@@ -127,27 +222,24 @@ __device__ inline void attn_split(const AttnArgs& a, int n_splits, int split, in
         float vsc[G::kChunks];
 #pragma unroll
         for (int u = 0; u < G::kChunks; ++u) {
-            const int c = u * NT + threadIdx.x;
-            const int r = c / cpr;
-            const int j = r0 + r;
-            const bool live = c < n_chunks && r < rows;
-            int slot = (a.swa_head - a.swa_len + (j - cnt)) % a.w;
-            if (slot < 0) slot += a.w;
+            const int j = r0 + pr[u];
+            const bool live = pr[u] < rows;
             const int ri = my_idx[u] < 0 ? 0 : (my_idx[u] >= a.n_comp ? a.n_comp - 1 : my_idx[u]);
-            const uint8_t* rec = !live ? sbase
-                                       : (j < cnt ? cbase + static_cast<long long>(ri) * kMixRec
-                                                  : sbase + static_cast<long long>(slot) * kMixRec);
-            v[u] = mixed_piece_load(mixed_piece_ptr(rec, c % cpr));
+            const uint8_t* rec =
+                !live ? sbase
+                      : (j < cnt ? cbase + static_cast<long long>(ri) * kMixRec
+                                 : sbase + static_cast<long long>(swa_slot(a.swa_head, a.swa_len, j - cnt, a.w)) *
+                                               kMixRec);
+            v[u] = mixed_piece_load(mixed_piece_ptr(rec, pc[u]));
             vsc[u] = *reinterpret_cast<const float*>(rec + kMixScaleOff);
         }
         const bool write_rec = a.idx && a.gather_buf && hg == 0;
         uint8_t* gbase = reinterpret_cast<uint8_t*>(a.gather_buf) + b * a.buf_stride_b;
 #pragma unroll
         for (int u = 0; u < G::kChunks; ++u) {
-            const int c = u * NT + threadIdx.x;
-            const int r = c / cpr;
-            const int cc = c % cpr;
-            const bool live = c < n_chunks && r < rows;
+            const int r = pr[u];
+            const int cc = pc[u];
+            const bool live = r < rows;
             if (live && write_rec) {  // the record's own bytes to gather_buf
                 uint8_t* out = gbase + static_cast<long long>(r0 + r) * kMixRec;
                 if (cc < kNopeChunks) {
@@ -162,23 +254,20 @@ __device__ inline void attn_split(const AttnArgs& a, int n_splits, int split, in
     } else {
 #pragma unroll
     for (int u = 0; u < G::kChunks; ++u) {
-        const int c = u * NT + threadIdx.x;
-        const int r = c / cpr;
-        const int j = r0 + r;
+        const int j = r0 + pr[u];
         const uint16_t* src = nullptr;
-        if (c < n_chunks && r < rows) {
+        if (pr[u] < rows) {
             if (!a.idx && !a.dense) {
                 src = a.kv + b * a.kv_stride_b + static_cast<long long>(j) * d;
             } else if (j < cnt) {
                 const int ri = my_idx[u] < 0 ? 0 : (my_idx[u] >= a.n_comp ? a.n_comp - 1 : my_idx[u]);
                 src = a.comp_kv + b * a.comp_kv_stride_b + static_cast<long long>(ri) * d;
             } else {
-                int slot = (a.swa_head - a.swa_len + (j - cnt)) % a.w;
-                if (slot < 0) slot += a.w;
-                src = a.swa + b * a.swa_stride_b + static_cast<long long>(slot) * d;
+                src = a.swa + b * a.swa_stride_b +
+                      static_cast<long long>(swa_slot(a.swa_head, a.swa_len, j - cnt, a.w)) * d;
             }
         }
-        v[u] = src ? *reinterpret_cast<const uint4*>(src + (c % cpr) * 8) : make_uint4(0, 0, 0, 0);
+        v[u] = src ? *reinterpret_cast<const uint4*>(src + pc[u] * 8) : make_uint4(0, 0, 0, 0);
     }
     }
 #pragma unroll
@@ -189,10 +278,9 @@ __device__ inline void attn_split(const AttnArgs& a, int n_splits, int split, in
     const bool write_buf = (a.idx || a.dense) && a.gather_buf && hg == 0 && !a.kv_mixed;
 #pragma unroll
     for (int u = 0; u < G::kChunks; ++u) {
-        const int c = u * NT + threadIdx.x;
-        if (c < n_chunks) {
-            const int r = c / cpr;
-            const int cc = c % cpr;
+        if (pr[u] < kR) {
+            const int r = pr[u];
+            const int cc = pc[u];
             *reinterpret_cast<uint4*>(tile + r * pitch + cc * 8) = v[u];
             if (write_buf && r < rows)
                 *reinterpret_cast<uint4*>(a.gather_buf + b * a.buf_stride_b + static_cast<long long>(r0 + r) * d + cc * 8) = v[u];
@@ -268,25 +356,13 @@ __device__ inline void attn_split(const AttnArgs& a, int n_splits, int split, in
         a.ws_ml[2 * (ml_base + static_cast<long long>(hh) * n_splits) + 1] = l;
     }
 
-    // 4. O = P V: M = 16 heads, K = kR rows (one MFMA step), N = d in 16-wide tiles
+    // 4. O = P V: M = 16 heads, K = kR rows, N = d in groups of 16 P columns
+    //    (P = 2 when the waves are many, so every wave gets a group at d = 512)
     float* ob = a.ws_o + (static_cast<long long>(b) * a.h + hg * kHeadGroup) * n_splits * d +
                 static_cast<long long>(split) * d;
-    for (int nt = wv; nt < d / 16; nt += G::kWaves) {
-        const int col = 16 * nt + li;
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < kR / 32; ++ks) {
-            const bf16x8 pa = *reinterpret_cast<const bf16x8*>(pl + li * kPPitch + 32 * ks + 8 * lg);
-            bf16x8 vb;
-            uint16_t tmp[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tmp[e] = tile[(32 * ks + 8 * lg + e) * pitch + col];
-            __builtin_memcpy(&vb, tmp, sizeof(vb));
-            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ob[static_cast<long long>(4 * lg + r) * n_splits * d + col] = o[r];
-    }
+    constexpr int kP = G::kWaves >= 16 ? 2 : 4;
+    for (int g = wv; 16 * kP * g < d; g += G::kWaves)
+        pv_group<kP>(tile, pitch, pl, kPPitch, kR / 32, 16 * kP * g, d, ob, static_cast<long long>(n_splits) * d);
 }
 
 }  // namespace

@@ -113,48 +113,27 @@ __device__ inline void compress_block(const float* __restrict__ z, const float* 
 // (max, denominator, weighted sum) are combined in LDS:
 // M = max_s mx_s, den = sum_s den_s e^(mx_s - M), acc likewise, y = acc / den.
 // part: 3 * blockDim.x floats of LDS.  Plain (non-overlapped) blocks only.
-__device__ inline void compress_block_slice(const float* __restrict__ z, const float* __restrict__ c,
-                                            const float* __restrict__ bias, void* __restrict__ out_row,
-                                            bool out_bf16, int m, int d, int ch0, int nch, float* part) {
+
+// One row of a slice into its running (max, denominator, weighted sum).
+__device__ inline void slice_row_update(float lz, float lc, float& mx, float& den, float& acc) {
+    if (lz > mx) {
+        const float sc = expf(mx - lz);  // 0 on the slice's first row
+        den *= sc;
+        acc *= sc;
+        mx = lz;
+    }
+    const float e = expf(lz - mx);
+    den += e;
+    acc += e * lc;
+}
+
+// The slices' running sums combined in LDS; the output channels written.
+__device__ inline void slice_merge(float mx, float den, float acc, void* __restrict__ out_row, bool out_bf16, int d,
+                                   int ch0, int nch, float* part) {
     const int slices = blockDim.x / nch;
     const int t = threadIdx.x % nch;
-    const int sl = threadIdx.x / nch;
     const int ch = ch0 + t;
-    const int per = (m + slices - 1) / slices;
-    const int r_lo = sl * per;
-    const int r_hi = min(m, r_lo + per);
-    float mx = -INFINITY, den = 0.f, acc = 0.f;
-    if (sl < slices && ch < d) {
-        constexpr int kBatch = 16;
-        for (int r0 = r_lo; r0 < r_hi; r0 += kBatch) {
-            float lz[kBatch], lc[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int r = r0 + u;
-                lz[u] = -INFINITY;
-                lc[u] = 0.f;
-                if (r < r_hi) {
-                    const long long o = static_cast<long long>(r) * d + ch;
-                    lz[u] = z[o] + bias[o];
-                    lc[u] = c[o];
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                if (r0 + u < r_hi) {
-                    if (lz[u] > mx) {
-                        const float sc = expf(mx - lz[u]);  // 0 on the slice's first row
-                        den *= sc;
-                        acc *= sc;
-                        mx = lz[u];
-                    }
-                    const float e = expf(lz[u] - mx);
-                    den += e;
-                    acc += e * lc[u];
-                }
-            }
-        }
-    }
+    const int sl = threadIdx.x / nch;
     part[threadIdx.x] = mx;
     part[blockDim.x + threadIdx.x] = den;
     part[2 * blockDim.x + threadIdx.x] = acc;
@@ -204,6 +183,46 @@ __device__ inline void compress_block_slice(const float* __restrict__ z, const f
         else
             static_cast<float*>(out_row)[ch] = y;
     }
+}
+
+// This thread's rows of the slice: [r_lo, r_hi) of channel ch (empty when
+// the thread has no slice or channel).
+__device__ inline void slice_rows(int m, int d, int ch0, int nch, int& ch, int& r_lo, int& r_hi) {
+    const int slices = blockDim.x / nch;
+    const int t = threadIdx.x % nch;
+    const int sl = threadIdx.x / nch;
+    ch = ch0 + t;
+    const int per = (m + slices - 1) / slices;
+    r_lo = sl * per;
+    r_hi = min(m, r_lo + per);
+    if (sl >= slices || ch >= d) r_hi = r_lo;
+}
+
+__device__ inline void compress_block_slice(const float* __restrict__ z, const float* __restrict__ c,
+                                            const float* __restrict__ bias, void* __restrict__ out_row,
+                                            bool out_bf16, int m, int d, int ch0, int nch, float* part) {
+    int ch, r_lo, r_hi;
+    slice_rows(m, d, ch0, nch, ch, r_lo, r_hi);
+    float mx = -INFINITY, den = 0.f, acc = 0.f;
+    constexpr int kBatch = 16;
+    for (int r0 = r_lo; r0 < r_hi; r0 += kBatch) {
+        float lz[kBatch], lc[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int r = r0 + u;
+            lz[u] = -INFINITY;
+            lc[u] = 0.f;
+            if (r < r_hi) {
+                const long long o = static_cast<long long>(r) * d + ch;
+                lz[u] = z[o] + bias[o];
+                lc[u] = c[o];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (r0 + u < r_hi) slice_row_update(lz[u], lc[u], mx, den, acc);
+    }
+    slice_merge(mx, den, acc, out_row, out_bf16, d, ch0, nch, part);
 }
 
 }  // namespace csa

@@ -160,39 +160,31 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
     const uint16_t* swa = a.swa + b * a.swa_stride_b;
     uint4 qv[kDenseQPer], v[kDenseRowPer];
     float vsc[kDenseRowPer];  // mixed: the row scale of each piece
+    int pr[kDenseRowPer], pc[kDenseRowPer];  // each piece's row of the split (kDenseRows and up: none) and chunk
+    piece_rows<kDenseThreads>(cpr, pr, pc);
     if (a.kv_mixed) {  // records (d = 512): one 16-byte read and the row scale per piece, no branch on the
                        // piece kind; pieces past the split's rows read its first row (rows >= 1)
 #pragma unroll
         for (int u = 0; u < kDenseRowPer; ++u) {
-            const int c = threadIdx.x + u * kDenseThreads;
-            const int r = c / cpr;
-            const int jj = (c < kDenseRows * cpr && r < rows) ? r0 + r : r0;
-            int slot = (a.swa_head - a.swa_len + (jj - cnt)) % a.w;
-            if (slot < 0) slot += a.w;
+            const int jj = pr[u] < rows ? r0 + pr[u] : r0;
             const uint8_t* rec = jj < cnt ? reinterpret_cast<const uint8_t*>(a.comp_kv) + b * a.comp_kv_stride_b +
                                                 static_cast<long long>(jj) * kMixRec
                                           : reinterpret_cast<const uint8_t*>(a.swa) + b * a.swa_stride_b +
-                                                static_cast<long long>(slot) * kMixRec;
-            v[u] = mixed_piece_load(mixed_piece_ptr(rec, c % cpr));
+                                                static_cast<long long>(swa_slot(a.swa_head, a.swa_len, jj - cnt, a.w)) *
+                                                    kMixRec;
+            v[u] = mixed_piece_load(mixed_piece_ptr(rec, pc[u]));
             vsc[u] = *reinterpret_cast<const float*>(rec + kMixScaleOff);
         }
     } else {
 #pragma unroll
         for (int u = 0; u < kDenseRowPer; ++u) {
-            const int c = threadIdx.x + u * kDenseThreads;
-            const int r = c / cpr;
-            const int j = r0 + r;
+            const int j = r0 + pr[u];
             const uint16_t* src = nullptr;
-            if (c < kDenseRows * cpr && r < rows) {
-                if (j < cnt) {
-                    src = comp + static_cast<long long>(j) * d;
-                } else {
-                    int slot = (a.swa_head - a.swa_len + (j - cnt)) % a.w;
-                    if (slot < 0) slot += a.w;
-                    src = swa + static_cast<long long>(slot) * d;
-                }
+            if (pr[u] < rows) {
+                src = j < cnt ? comp + static_cast<long long>(j) * d
+                              : swa + static_cast<long long>(swa_slot(a.swa_head, a.swa_len, j - cnt, a.w)) * d;
             }
-            v[u] = src ? *reinterpret_cast<const uint4*>(src + (c % cpr) * 8) : make_uint4(0, 0, 0, 0);
+            v[u] = src ? *reinterpret_cast<const uint4*>(src + pc[u] * 8) : make_uint4(0, 0, 0, 0);
         }
     }
 #pragma unroll
@@ -208,11 +200,8 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
     }
     if (a.kv_mixed) {  // decode the pieces (the first use of the loaded bytes); rows past the split's are zero
 #pragma unroll
-        for (int u = 0; u < kDenseRowPer; ++u) {
-            const int c = threadIdx.x + u * kDenseThreads;
-            v[u] = (c < kDenseRows * cpr && c / cpr < rows) ? mixed_piece_value(v[u], vsc[u], c % cpr)
-                                                            : make_uint4(0, 0, 0, 0);
-        }
+        for (int u = 0; u < kDenseRowPer; ++u)
+            v[u] = pr[u] < rows ? mixed_piece_value(v[u], vsc[u], pc[u]) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kDenseQPer; ++u) {
@@ -220,10 +209,8 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
         if (c < kHeadGroup * cpr) *reinterpret_cast<uint4*>(qs + (c / cpr) * pitch + (c % cpr) * 8) = qv[u];
     }
 #pragma unroll
-    for (int u = 0; u < kDenseRowPer; ++u) {
-        const int c = threadIdx.x + u * kDenseThreads;
-        if (c < kDenseRows * cpr) *reinterpret_cast<uint4*>(tile + (c / cpr) * pitch + (c % cpr) * 8) = v[u];
-    }
+    for (int u = 0; u < kDenseRowPer; ++u)
+        if (pr[u] < kDenseRows) *reinterpret_cast<uint4*>(tile + pr[u] * pitch + pc[u] * 8) = v[u];
     __syncthreads();
 
     // 2. S = q K^T: wave wv owns rows 16*wv .. 16*wv+15; per-head max of the wave
@@ -286,25 +273,13 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
         a.ws_ml[2 * (ml_base + static_cast<long long>(hh) * n_splits) + 0] = M;
         a.ws_ml[2 * (ml_base + static_cast<long long>(hh) * n_splits) + 1] = l;
     }
-    // 4. O = P V: M = 16 heads, K = the split's rows in 32-row steps, N = d in 16-wide tiles
+    // 4. O = P V: M = 16 heads, K = the split's rows in 32-row steps, N = d in
+    //    groups of 64 columns, one per wave
     float* ob = a.ws_o + (static_cast<long long>(b) * a.h + hg * kHeadGroup) * n_splits * d +
                 static_cast<long long>(split) * d;
     const int ksteps = (rows + 31) / 32;  // rows past the valid ones hold zeros and p = 0
-    for (int nt = wv; nt < d / 16; nt += kDenseWaves) {
-        const int col = 16 * nt + li;
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-        for (int ks = 0; ks < ksteps; ++ks) {
-            const bf16x8 pa = *reinterpret_cast<const bf16x8*>(pl + li * kDensePPitch + 32 * ks + 8 * lg);
-            bf16x8 vb;
-            uint16_t tmp[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tmp[e] = tile[(32 * ks + 8 * lg + e) * pitch + col];
-            __builtin_memcpy(&vb, tmp, sizeof(vb));
-            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ob[static_cast<long long>(4 * lg + r) * n_splits * d + col] = o[r];
-    }
+    for (int g = wv; 64 * g < d; g += kDenseWaves)
+        pv_group<4>(tile, pitch, pl, kDensePPitch, ksteps, 64 * g, d, ob, static_cast<long long>(n_splits) * d);
 }
 
 // Merge of the splits plus the step's new rows (the compressed entry of a
