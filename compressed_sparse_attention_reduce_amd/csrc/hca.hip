@@ -162,29 +162,52 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
     float vsc[kDenseRowPer];  // mixed: the row scale of each piece
     int pr[kDenseRowPer], pc[kDenseRowPer];  // each piece's row of the split (kDenseRows and up: none) and chunk
     piece_rows<kDenseThreads>(cpr, pr, pc);
+    // d = 512: piece u of wave wv is the whole row wv + 8 u (lane = chunk), so
+    // the row, its source and its bounds test are wave-uniform (scalar) and a
+    // load costs one address add
+    const bool wave_rows = cpr == kWave;
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    constexpr int kRowStep = kDenseThreads / kWave;
     if (a.kv_mixed) {  // records (d = 512): one 16-byte read and the row scale per piece, no branch on the
                        // piece kind; pieces past the split's rows read its first row (rows >= 1)
+        const uint8_t* cbase = reinterpret_cast<const uint8_t*>(a.comp_kv) + b * a.comp_kv_stride_b;
+        const uint8_t* sbase = reinterpret_cast<const uint8_t*>(a.swa) + b * a.swa_stride_b;
+        auto rec_of = [&](int jj) {
+            return jj < cnt ? cbase + static_cast<long long>(jj) * kMixRec
+                            : sbase + static_cast<long long>(swa_slot(a.swa_head, a.swa_len, jj - cnt, a.w)) * kMixRec;
+        };
+        if (wave_rows) {
 #pragma unroll
-        for (int u = 0; u < kDenseRowPer; ++u) {
-            const int jj = pr[u] < rows ? r0 + pr[u] : r0;
-            const uint8_t* rec = jj < cnt ? reinterpret_cast<const uint8_t*>(a.comp_kv) + b * a.comp_kv_stride_b +
-                                                static_cast<long long>(jj) * kMixRec
-                                          : reinterpret_cast<const uint8_t*>(a.swa) + b * a.swa_stride_b +
-                                                static_cast<long long>(swa_slot(a.swa_head, a.swa_len, jj - cnt, a.w)) *
-                                                    kMixRec;
-            v[u] = mixed_piece_load(mixed_piece_ptr(rec, pc[u]));
-            vsc[u] = *reinterpret_cast<const float*>(rec + kMixScaleOff);
+            for (int u = 0; u < kDenseRowPer; ++u) {
+                const int r = wvu + u * kRowStep;
+                const uint8_t* rec = rec_of(r < rows ? r0 + r : r0);
+                v[u] = mixed_piece_load(mixed_piece_ptr(rec, lane));
+                vsc[u] = *reinterpret_cast<const float*>(rec + kMixScaleOff);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kDenseRowPer; ++u) {
+                const uint8_t* rec = rec_of(pr[u] < rows ? r0 + pr[u] : r0);
+                v[u] = mixed_piece_load(mixed_piece_ptr(rec, pc[u]));
+                vsc[u] = *reinterpret_cast<const float*>(rec + kMixScaleOff);
+            }
         }
     } else {
+        auto row_of = [&](int j) {
+            return j < cnt ? comp + static_cast<long long>(j) * d
+                           : swa + static_cast<long long>(swa_slot(a.swa_head, a.swa_len, j - cnt, a.w)) * d;
+        };
+        if (wave_rows) {
 #pragma unroll
-        for (int u = 0; u < kDenseRowPer; ++u) {
-            const int j = r0 + pr[u];
-            const uint16_t* src = nullptr;
-            if (pr[u] < rows) {
-                src = j < cnt ? comp + static_cast<long long>(j) * d
-                              : swa + static_cast<long long>(swa_slot(a.swa_head, a.swa_len, j - cnt, a.w)) * d;
+            for (int u = 0; u < kDenseRowPer; ++u) {
+                const int r = wvu + u * kRowStep;
+                v[u] = r < rows ? *reinterpret_cast<const uint4*>(row_of(r0 + r) + lane * 8) : make_uint4(0, 0, 0, 0);
             }
-            v[u] = src ? *reinterpret_cast<const uint4*>(src + pc[u] * 8) : make_uint4(0, 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kDenseRowPer; ++u)
+                v[u] = pr[u] < rows ? *reinterpret_cast<const uint4*>(row_of(r0 + pr[u]) + pc[u] * 8)
+                                    : make_uint4(0, 0, 0, 0);
         }
     }
 #pragma unroll
