@@ -743,6 +743,9 @@ def time_batch128k(csa, reps: int, n_caches: int = 8):
     stream.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (reps * len(layers))
     alg = algorithmic_bytes(shape)["per_layer"] * shape.batch
+    # the same layers through csa_decode_step_dev (one graph, each replay the next token): 8 x 80 fused
+    # workgroups would not all be resident, so it selects once per sequence like the host-counter step
+    dev_us = time_dev_step(csa, layers, shape, reps, 4) * 1e3 / len(layers)
     del layers
     torch.cuda.empty_cache()
     return {
@@ -750,6 +753,7 @@ def time_batch128k(csa, reps: int, n_caches: int = 8):
                     "decode token each through one CSA layer; indexer 64x128 bf16, top_k 512, main attention "
                     f"64 heads x 512 bf16 with sink; {n_caches} independent layer caches replayed in turn",
         "us_per_layer_step": round(us, 3),
+        "device_counters_us_per_layer_step": round(dev_us, 3),
         "layer_steps_per_s": round(1e6 / us, 1),
         "sequence_tokens_per_s_per_layer": round(shape.batch * 1e6 / us, 1),
         "alg_bytes_per_layer_step": alg,

@@ -30,6 +30,7 @@ namespace csa {
 namespace {
 
 __global__ __launch_bounds__(kAttnThreads) void k_attn_partial_bf16(AttnArgs a, int n_splits) {
+    if (a.dev) attn_dev_view(a, blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0);
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint4 qv[AttnSplit<kAttnThreads>::kQBatch];
     attn_load_q<kAttnThreads>(a, blockIdx.y, blockIdx.z, qv);

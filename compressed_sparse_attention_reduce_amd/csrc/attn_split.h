@@ -134,6 +134,19 @@ __device__ inline void pv_group(const uint16_t* tile, int pitch, const uint16_t*
     }
 }
 
+// Decode step with device counters: the step's view of them after its own
+// jobs (the block it completes and the token's window row are in place);
+// one workgroup records the position for the merge.  Returns the entry count.
+__device__ inline int attn_dev_view(AttnArgs& a, bool record) {
+    const DevState st = dev_load(a.dev, a.w, a.max_comp);
+    if (record && a.dev_pos) *a.dev_pos = st.pos;
+    const int n = dev_step_entries(st, a.m, a.max_comp);
+    a.n_comp = n;
+    a.swa_head = (st.swa_head + 1) % a.w;
+    a.swa_len = st.swa_len + 1 < a.w ? st.swa_len + 1 : a.w;
+    return n;
+}
+
 // The query group's loads (independent of everything else: issued first).
 template <int NT>
 __device__ inline void attn_load_q(const AttnArgs& a, int hg, int b, uint4 (&qv)[AttnSplit<NT>::kQBatch]) {

@@ -573,6 +573,12 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
     if (!do_rest) return ok();
     csa::TopkArgs ta{io->scores, L->batch, 1, N, N, io->scores_stride_b, L->top_k, io->topk_idx,
                      io->topk_count, tws};
+    if (dev) {
+        ta.dev = dev;
+        ta.w = L->w;
+        ta.m = L->m;
+        ta.max_comp = L->max_comp;
+    }
     // two-stage E4M3 selection: the first stage and the exact scores make one
     // list per sequence that the top-k below selects from
     if (rescore) {
@@ -591,9 +597,12 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
     // selects the top k itself, no separate top-k launch, as long as those
     // workgroups are all resident at once (one per compute unit); a larger batch
     // selects once per sequence and attends with smaller workgroups.  The
-    // device-counter step always fuses (its top-k length is on the device).
+    // device-counter step takes the separate launches only with candidate
+    // lists (its entry count is on the device: without lists the top-k must
+    // read the whole row, which the fused kernel bounds by that count).
     const bool all_resident = csa::topk_attn_workgroups(L->batch, L->h, n_max) <= csa::device_cu_count();
-    const bool fuse = bf && (dev || ((ca.lists || N <= kFuseExactMaxN) && all_resident));
+    const bool fuse = bf && (dev ? (!ca.lists || all_resident)
+                                 : ((ca.lists || N <= kFuseExactMaxN) && all_resident));
     if (!fuse) {
         e = csa::launch_topk(ta, ca.lists ? &ca : nullptr, s);
         if (e != hipSuccess) return launched(e, "csa_decode_step/topk");

@@ -67,6 +67,10 @@ __host__ __device__ inline bool dev_completes(const DevState& s, int m, int max_
 }
 // Move the counters past the step that read them (one thread, after every
 // reader of this step is done).
+// Entries a step scores and selects from: those before it plus the block it completes.
+__host__ __device__ inline int dev_step_entries(const DevState& s, int m, int max_comp) {
+    return s.n_comp + (dev_completes(s, m, max_comp) ? 1 : 0);
+}
 __host__ __device__ inline void dev_advance(DevState* st, int m, int w, int max_comp) {
     DevState s = dev_load(st, w, max_comp);
     if (s.pos % m == m - 1) {
@@ -152,6 +156,10 @@ struct TopkArgs {
     int* idx;
     int* count;
     void* ws;
+    // decode step with device counters (one query row per sequence): n is
+    // the state's entry count after the step's own block, not the field above
+    const DevState* dev;
+    int w, m, max_comp;
 };
 // cands: per-slot candidate lists already produced (by the score kernel), or
 // nullptr (the launcher produces them itself when the rows are long).

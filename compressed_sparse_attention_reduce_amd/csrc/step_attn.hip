@@ -22,15 +22,8 @@ __host__ __device__ inline size_t topk_attn_lds_bytes() {
 }
 
 __global__ __launch_bounds__(kFinalThreads) void k_topk_attn(TopkArgs ta, CandArgs c, AttnArgs a, int n_splits) {
-    if (a.dev) {  // counters on the device: the step's view of them after its jobs
-        const DevState st = dev_load(a.dev, a.w, a.max_comp);
-        if (a.dev_pos && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *a.dev_pos = st.pos;
-        const int n = st.n_comp + (dev_completes(st, a.m, a.max_comp) ? 1 : 0);
-        ta.n = n;
-        a.n_comp = n;
-        a.swa_head = (st.swa_head + 1) % a.w;
-        a.swa_len = st.swa_len + 1 < a.w ? st.swa_len + 1 : a.w;
-    }
+    if (a.dev)  // counters on the device: the step's view of them after its jobs
+        ta.n = attn_dev_view(a, blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0);
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     FinalSmem& fs = *reinterpret_cast<FinalSmem*>(smem);
     int* sidx = reinterpret_cast<int*>(smem + sizeof(FinalSmem));  // this sequence's top-k indices

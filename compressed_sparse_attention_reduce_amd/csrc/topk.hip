@@ -49,6 +49,7 @@ constexpr int kCandPer = kCandChunk / kCandThreads;
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 __global__ __launch_bounds__(kFinalThreads) void k_topk_final(TopkArgs a, CandArgs c) {
+    if (a.dev) a.n = dev_step_entries(dev_load(a.dev, a.w, a.max_comp), a.m, a.max_comp);
     extern __shared__ __attribute__((aligned(16))) unsigned char final_smem[];
     FinalSmem& sm = *reinterpret_cast<FinalSmem*>(final_smem);
     const int row = blockIdx.x;

@@ -17,7 +17,7 @@ typedef unsigned long long u64;
 
 constexpr int kHistBits = 12;               // first radix digit over a raw score row
 constexpr int kHistBins = 1 << kHistBits;
-constexpr int kSelBits = 11;                // digits of the register-resident sorted select
+constexpr int kSelBits = 10;                // digits of the register-resident sorted select
 
 // Unique sort key of an element: order-preserving score key, then the
 // inverted index (so equal scores rank the lower index higher).

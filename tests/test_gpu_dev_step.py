@@ -267,6 +267,15 @@ def test_dev_step_fp8_keys(csa):
     _run(csa, mixed=False, overlap=0, B=2, n0=150, pos0=600, max_comp=200, steps=9, seed=8104, fp8=True)
 
 
+def test_dev_step_batched_separate_topk(csa):
+    """Batch 4 at top_k 512, window 128: 4 x 80 fused workgroups would not all
+    be resident, so the device-counter step takes one top-k launch per
+    sequence (entry count from the device state, candidate lists from the
+    scan) and the 256-thread attention; five replays from a block start, one
+    block completion."""
+    _run(csa, mixed=False, overlap=0, B=4, n0=8000, pos0=32000, max_comp=8200, steps=5, seed=8105, W=128, K=512)
+
+
 def test_dev_step_full_cache_sets_flag(csa):
     """A block completing into a full cache writes nothing, keeps n_comp and
     sets bit 0 of the flags; the step's attention is the one of a step that
