@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
 
     if (!kCands) return;
     // 4. this workgroup's best m and their bound to its candidate slot
-    block_top_m(top, drop, a.cands.m, a.cands.mw,
+    block_top_m<kWaves>(top, drop, a.cands.m, a.cands.mw,
                 a.cands.lists + (static_cast<long long>(row) * a.cands.slots + wg) * (a.cands.m + 1), cs);
 }
 

@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void k_index_score_bf16(ScoreArgs
 
     if (!kCands) return;
     // 4. this workgroup's best m and their bound to its candidate slot
-    block_top_m(top, drop, a.cands.m, a.cands.mw,
+    block_top_m<kWavesPerWg>(top, drop, a.cands.m, a.cands.mw,
                 a.cands.lists + (static_cast<long long>(row) * a.cands.slots + wg) * (a.cands.m + 1), cs);
 }
 

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kCandThreads) void k_topk_cands(TopkArgs a, CandArg
         const uint32_t key = score_key(x[u]);
         lane_insert(top, drop, key_valid(key, x[u]) ? composite(key, static_cast<uint32_t>(i)) : 0ull);
     }
-    block_top_m(top, drop, c.m, c.mw, c.lists + (static_cast<long long>(row) * c.slots + blockIdx.x) * (c.m + 1), cs);
+    block_top_m<kCandThreads / kWave>(top, drop, c.m, c.mw, c.lists + (static_cast<long long>(row) * c.slots + blockIdx.x) * (c.m + 1), cs);
 }
 
 }  // namespace
@@ -148,12 +148,13 @@ hipError_t launch_topk_rows(const TopkArgs& a, hipStream_t s) {
 }
 
 int topk_cand_m(int n, int k, int keys_per_slot) {
-    // slots hold m + 1 entries; m covers the expected share of the top k of a
-    // slot plus six standard deviations (the final kernel proves containment
-    // and falls back to the exact path if a slot held more)
+    // slots hold m + 1 entries; m covers the expected share e of the top k of
+    // a slot plus 4 sqrt(e) + 2 (Poisson tails: about one row in a thousand
+    // at 1M context has a slot that held more; the top-k proves containment
+    // and then re-reads the few slots concerned)
     if (n <= 0 || keys_per_slot <= 0) return -1;
     const double e = static_cast<double>(k) * keys_per_slot / n;
-    const int m = static_cast<int>(e + 4.0 * sqrt(e) + 3.0 + 0.999);
+    const int m = static_cast<int>(e + 4.0 * sqrt(e) + 2.0 + 0.999);
     return m + 1 <= kMaxCandM1 ? m : -1;
 }
 

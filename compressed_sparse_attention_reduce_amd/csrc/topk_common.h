@@ -153,13 +153,14 @@ struct CandSmem {
 // Workgroup candidate list from the lanes' lists: out[0..m) (global) = the m
 // largest of the composites the waves extracted (each wave its mw largest),
 // descending, zero padded; out[m] = a bound at least as large as every
-// composite of the workgroup not in out[0..m).  mw <= m < kMaxCandM1; at
-// most 16 waves.  Every thread calls it, once per kernel.
-template <int L>
+// composite of the workgroup not in out[0..m).  mw <= m < kMaxCandM1; NW
+// waves (blockDim.x == 64 NW, at most 16).  Every thread calls it, once per
+// kernel.
+template <int NW, int L>
 __device__ inline void block_top_m(u64 (&top)[L], u64 drop, int m, int mw, u64* out, CandSmem& cs) {
+    static_assert(NW >= 1 && NW <= 16, "at most 16 waves");
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
-    const int nw = blockDim.x / kWave;
     int cnt;
     const u64 bound = wave_extract_top(top, drop, mw, cs.wtop[wv], &cnt);
     if (lane == 0) {
@@ -168,11 +169,13 @@ __device__ inline void block_top_m(u64 (&top)[L], u64 drop, int m, int mw, u64* 
     }
     __syncthreads();
     // merge: an entry's rank is the number of larger entries over all lists
-    // (unique values; the zero padding never counts); reads in unrolled runs
-    // of 8 so they are in flight together
+    // (unique values; the zero padding never counts).  Every lane reads the
+    // same words (broadcasts): a run of 8 entries of every list is loaded at
+    // once, one LDS round trip per run.
     u64 maxb = 0;
     int total = 0;
-    for (int w = 0; w < nw; ++w) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
         maxb = umax64(maxb, cs.wbound[w]);
         total += cs.wcount[w];
     }
@@ -180,12 +183,17 @@ __device__ inline void block_top_m(u64 (&top)[L], u64 drop, int m, int mw, u64* 
     if (lane < cs.wcount[wv]) {
         const u64 x = cs.wtop[wv][lane];
         int rank = 0;
-        for (int w = 0; w < nw; ++w)
-            for (int j0 = 0; j0 < mw8; j0 += 8) {
-                const u64* row = cs.wtop[w] + j0;
+        for (int j0 = 0; j0 < mw8; j0 += 8) {
+            u64 r[NW][8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) rank += row[j] > x ? 1 : 0;
-            }
+            for (int w = 0; w < NW; ++w)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) r[w][j] = cs.wtop[w][j0 + j];
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) rank += r[w][j] > x ? 1 : 0;
+        }
         if (rank < m) out[rank] = x;
         else if (rank == m) out[m] = umax64(x, maxb);
     }
