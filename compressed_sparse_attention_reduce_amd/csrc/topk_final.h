@@ -341,16 +341,19 @@ __device__ bool stream_row_topk(FinalSmem& sm, const float* row, int n, int k, i
 // layout is not stated, the open slots cover more than a quarter of the row,
 // or the candidates overflow the pool.
 constexpr int kRefineMaxSlots = 2048;
-static_assert(sizeof(FinalSmem::stage) >= kRefineMaxSlots * sizeof(uint32_t), "open-slot list fits the stage");
+constexpr int kRefineMaxRuns = 2048;  // (open slot, run) pairs re-read
+static_assert(sizeof(FinalSmem::stage) >= (kRefineMaxSlots + kRefineMaxRuns) * sizeof(uint32_t),
+              "open-slot list and run starts fit the stage");
 __device__ bool refine_topk(FinalSmem& sm, const CandArgs& c, int row, const float* srow, int n, int k, int* out,
                             uint32_t& k_eff) {
-    if (!c.lists || c.run <= 0 || c.stride < c.run || c.stride % c.run != 0 || c.stride / c.run > c.slots ||
-        c.slots > kRefineMaxSlots)
+    if (!c.lists || c.run <= 0 || (c.run & (c.run - 1)) != 0 || c.stride < c.run || c.stride % c.run != 0 ||
+        c.stride / c.run > c.slots || c.slots > kRefineMaxSlots)
         return false;
     const int m1 = c.m + 1;
     const int total = c.slots * m1;
     if (total > kUnionCap) return false;
     const u64* lists = c.lists + static_cast<long long>(row) * total;
+    const int lane = threadIdx.x & (kWave - 1);
     uint32_t* hist = sm.hist;
     uint32_t* open_list = reinterpret_cast<uint32_t*>(sm.stage);
     u64 v[kUnionRegs];
@@ -359,15 +362,35 @@ __device__ bool refine_topk(FinalSmem& sm, const CandArgs& c, int row, const flo
         const int i = threadIdx.x + u * kFinalThreads;
         v[u] = i < total ? lists[i] : 0ull;
     }
+    // entry i = t + 1024 u is entry i % m1 of slot i / m1 (slot m1 entries: m listed, then the bound);
+    // the quotient and remainder advance by fixed steps (one division per thread)
+    int sl[kUnionRegs];
+    bool bnd[kUnionRegs];
+    {
+        int q = static_cast<int>(threadIdx.x) / m1;
+        int r = static_cast<int>(threadIdx.x) - q * m1;
+        const int dq = kFinalThreads / m1, dr = kFinalThreads - dq * m1;
+#pragma unroll
+        for (int u = 0; u < kUnionRegs; ++u) {
+            const bool in = static_cast<int>(threadIdx.x) + u * kFinalThreads < total;
+            sl[u] = in ? q : -1;
+            bnd[u] = in && r == c.m;
+            q += dq;
+            r += dr;
+            if (r >= m1) {
+                r -= m1;
+                ++q;
+            }
+        }
+    }
     // 1. a lower bound of the k-th largest listed key: its top 12 bits, then the next 12
     for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) hist[i] = 0;
     if (threadIdx.x == 0) { sm.n_sel = 0; sm.n_pool = 0; }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kUnionRegs; ++u) {
-        const int i = threadIdx.x + u * kFinalThreads;
         const uint32_t hi = static_cast<uint32_t>(v[u] >> 32);
-        if (i % m1 != c.m && hi) atomicAdd(&hist[hi >> 20], 1u);
+        if (!bnd[u] && hi) atomicAdd(&hist[hi >> 20], 1u);
     }
     __syncthreads();
     int tb;
@@ -379,9 +402,8 @@ __device__ bool refine_topk(FinalSmem& sm, const CandArgs& c, int row, const flo
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < kUnionRegs; ++u) {
-            const int i = threadIdx.x + u * kFinalThreads;
             const uint32_t hi = static_cast<uint32_t>(v[u] >> 32);
-            if (i % m1 != c.m && hi && static_cast<int>(hi >> 20) == tb) atomicAdd(&hist[(hi >> 8) & 0xfffu], 1u);
+            if (!bnd[u] && hi && static_cast<int>(hi >> 20) == tb) atomicAdd(&hist[(hi >> 8) & 0xfffu], 1u);
         }
         __syncthreads();
         int tb2;
@@ -397,38 +419,67 @@ __device__ bool refine_topk(FinalSmem& sm, const CandArgs& c, int row, const flo
     int unmapped = 0;                            // an open slot outside the layout
 #pragma unroll
     for (int u = 0; u < kUnionRegs; ++u) {
-        const int i = threadIdx.x + u * kFinalThreads;
-        const bool reach = i < total && i % m1 == c.m && static_cast<uint32_t>(v[u] >> 32) >= lo;
-        const bool open = reach && i / m1 < layout_slots;
+        const bool reach = bnd[u] && static_cast<uint32_t>(v[u] >> 32) >= lo;
+        const bool open = reach && sl[u] < layout_slots;
         unmapped |= reach && !open;
         const uint32_t p = wave_append_pos(open, &sm.n_pool);
         if (open) {
-            hist[i / m1] = 1u;
-            open_list[p] = static_cast<uint32_t>(i / m1);
+            hist[sl[u]] = 1u;
+            open_list[p] = static_cast<uint32_t>(sl[u]);
         }
     }
     if (__syncthreads_or(unmapped)) return false;
     const uint32_t n_open = sm.n_pool;
     const uint32_t runs = static_cast<uint32_t>((static_cast<long long>(n) + c.stride - 1) / c.stride);
-    const uint32_t per_slot = runs * static_cast<uint32_t>(c.run);
-    const long long span_ll = static_cast<long long>(n_open) * per_slot;
-    if (span_ll > n / 4 + c.run) return false;  // the streaming reads are cheaper
+    const long long n_runs_ll = static_cast<long long>(n_open) * runs;
+    const long long span_ll = n_runs_ll * c.run;
+    if (span_ll > n / 4 + c.run || n_runs_ll > kRefineMaxRuns) return false;  // the streaming reads are cheaper
+    const uint32_t n_runs = static_cast<uint32_t>(n_runs_ll);
     const uint32_t span = static_cast<uint32_t>(span_ll);
+    // the first key of every (open slot, run) pair: run q is run q % runs of open slot q / runs
+    uint32_t* run_start = open_list + kRefineMaxSlots;
+    const uint32_t run = static_cast<uint32_t>(c.run), stride = static_cast<uint32_t>(c.stride);
+    for (uint32_t q = threadIdx.x; q < n_runs; q += blockDim.x) {
+        const uint32_t o = q / runs;
+        run_start[q] = open_list[o] * run + (q - o * runs) * stride;
+    }
     // 3. candidates: listed entries at or above lo whose key no open slot covers ...
+    {
+        bool keep[kUnionRegs];
+        uint32_t cnt = 0;
 #pragma unroll
-    for (int u = 0; u < kUnionRegs; ++u) {
-        const int i = threadIdx.x + u * kFinalThreads;
-        const uint32_t hi = static_cast<uint32_t>(v[u] >> 32);
-        bool keep = i < total && i % m1 != c.m && hi >= lo;
-        if (keep) {
-            const uint32_t idx = ~static_cast<uint32_t>(v[u]);
-            keep = hist[(idx % static_cast<uint32_t>(c.stride)) / static_cast<uint32_t>(c.run)] == 0u;
+        for (int u = 0; u < kUnionRegs; ++u) {
+            const uint32_t hi = static_cast<uint32_t>(v[u] >> 32);
+            keep[u] = sl[u] >= 0 && !bnd[u] && hi >= lo;
+            if (keep[u]) {
+                const uint32_t idx = ~static_cast<uint32_t>(v[u]);
+                keep[u] = hist[(idx % static_cast<uint32_t>(c.stride)) / static_cast<uint32_t>(c.run)] == 0u;
+            }
+            cnt += keep[u] ? 1u : 0u;
         }
-        const uint32_t p = wave_append_pos(keep, &sm.n_sel);
-        if (keep && p < static_cast<uint32_t>(kUnionCap)) sm.pool[p] = v[u];
+        uint32_t pre = cnt, sum = cnt;
+#define CSA_SCAN_STEP(o)                              \
+        {                                             \
+            const uint32_t other = xor_lanes<o>(sum); \
+            if (lane & (o)) pre += other;             \
+            sum += other;                             \
+        }
+        CSA_SCAN_STEP(1) CSA_SCAN_STEP(2) CSA_SCAN_STEP(4) CSA_SCAN_STEP(8) CSA_SCAN_STEP(16) CSA_SCAN_STEP(32)
+#undef CSA_SCAN_STEP
+        uint32_t wbase = 0;
+        if (lane == 0 && sum) wbase = atomicAdd(&sm.n_sel, sum);
+        wbase = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(wbase)));
+        uint32_t off = wbase + pre - cnt;
+        if (wbase + sum <= static_cast<uint32_t>(kUnionCap)) {
+#pragma unroll
+            for (int u = 0; u < kUnionRegs; ++u)
+                if (keep[u]) sm.pool[off++] = v[u];
+        }
     }
     // ... and the open slots' keys at or above lo, read from the score row
-    const uint32_t run = static_cast<uint32_t>(c.run), stride = static_cast<uint32_t>(c.stride);
+    // (the runs are powers of two: key f of the re-read is key f % run of run f / run)
+    __syncthreads();
+    const int run_shift = __ffs(static_cast<int>(run)) - 1;
 #pragma unroll 1
     for (uint32_t base = 0; base < span; base += kStreamBatch * blockDim.x) {
         uint32_t key[kStreamBatch];
@@ -436,22 +487,31 @@ __device__ bool refine_topk(FinalSmem& sm, const CandArgs& c, int row, const flo
 #pragma unroll
         for (int u = 0; u < kStreamBatch; ++u) {
             const uint32_t f = base + u * blockDim.x + threadIdx.x;
-            int x = n;  // past the row: key 0
-            if (f < span) {
-                const uint32_t o = f / per_slot;
-                const uint32_t rest = f - o * per_slot;
-                const uint32_t j = rest / run;
-                x = static_cast<int>(open_list[o] * run + j * stride + (rest - j * run));
-            }
+            const int x = f < span ? static_cast<int>(run_start[f >> run_shift] + (f & (run - 1))) : n;  // past the row: key 0
             at_i[u] = x;
             key[u] = long_key(srow, x, n);
         }
+        // one slot reservation per wave and batch (a scan of the lanes' counts)
+        uint32_t cnt = 0;
 #pragma unroll
-        for (int u = 0; u < kStreamBatch; ++u) {
-            const bool keep = key[u] >= lo;
-            const uint32_t p = wave_append_pos(keep, &sm.n_sel);
-            if (keep && p < static_cast<uint32_t>(kUnionCap))
-                sm.pool[p] = composite(key[u], static_cast<uint32_t>(at_i[u]));
+        for (int u = 0; u < kStreamBatch; ++u) cnt += key[u] >= lo ? 1u : 0u;
+        uint32_t pre = cnt, sum = cnt;
+#define CSA_SCAN_STEP(o)                              \
+        {                                             \
+            const uint32_t other = xor_lanes<o>(sum); \
+            if (lane & (o)) pre += other;             \
+            sum += other;                             \
+        }
+        CSA_SCAN_STEP(1) CSA_SCAN_STEP(2) CSA_SCAN_STEP(4) CSA_SCAN_STEP(8) CSA_SCAN_STEP(16) CSA_SCAN_STEP(32)
+#undef CSA_SCAN_STEP
+        uint32_t wbase = 0;
+        if (lane == 0 && sum) wbase = atomicAdd(&sm.n_sel, sum);
+        wbase = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(wbase)));
+        uint32_t off = wbase + pre - cnt;
+        if (wbase + sum <= static_cast<uint32_t>(kUnionCap)) {  // else overflow: the total shows it
+#pragma unroll
+            for (int u = 0; u < kStreamBatch; ++u)
+                if (key[u] >= lo) sm.pool[off++] = composite(key[u], static_cast<uint32_t>(at_i[u]));
         }
     }
     __syncthreads();
