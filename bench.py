@@ -807,6 +807,39 @@ def time_clustered(csa, layers, shape, steps: int, warmup: int, count: int = 409
     return ms, inside
 
 
+def time_mfma_ceiling(csa, reps: int = 5, launch_mfmas: int = 6000) -> dict:
+    """The bf16 matrix rate one launch reaches with 0..3 float FMAs per
+    16x16x32 MFMA (csa_mfma_probe: four independent MFMA chains per wave),
+    at two and at four waves per SIMD; HIP events around `reps` launches
+    after one warm-up.  The ceiling of a matrix kernel whose epilogue needs
+    that much vector work per MFMA at that occupancy."""
+    import torch
+
+    sink = torch.zeros(1, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {"peak_tflops": BF16_MFMA_PEAK_TFLOPS}
+    for wps in (2, 4):
+        iters = launch_mfmas // wps  # the same work per SIMD at either occupancy
+        flop = cus * wps * 4 * iters * 4 * 16384
+        line = {"flop_per_launch": flop}
+        for valu in range(4):
+            csa.csa_mfma_probe(sink, wps, iters, valu)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                csa.csa_mfma_probe(sink, wps, iters, valu)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            tf = flop / (us * 1e-6) / 1e12
+            line[f"valu_per_mfma_{valu}"] = {"us": round(us, 2), "tflops": round(tf, 1),
+                                             "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+        out[f"waves_per_simd_{wps}"] = line
+    return out
+
+
 def time_one_layer_config(csa, name: str, reps: int):
     """A latency-sized decode workload (tiny: context 1024, float32; ctx8k:
     context 8192, bf16): one layer's csa_decode_step on the workload's seeded
@@ -1200,6 +1233,7 @@ def main() -> int:
                             **time_one_layer_config(csa, "ctx8k", max(50, args.steps)))
     if "prefill" in legs:
         res["prefill"] = time_prefill(csa, max(2, args.scan_reps // 2))
+        res["prefill"]["mfma_ceiling"] = time_mfma_ceiling(csa)
     if "hca" in legs:
         res["hca"] = time_hca(csa, args.scan_reps)
     if "batch" in legs:

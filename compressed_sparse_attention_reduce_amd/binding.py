@@ -85,6 +85,7 @@ _SIGS = {
     "csa_quantize_query_fp8": (_i, [_vp, _i, _vp, _vp, _vp, _ll, _i, _i, _vp]),
     "csa_pack_kv_mixed": (_i, [_vp, _i, _vp, _ll, _i, _i, _vp]),
     "csa_read_probe": (_i, [_vp, _ll, _vp, _vp]),
+    "csa_mfma_probe": (_i, [_vp, _i, _i, _i, _vp]),
     "csa_index_score_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _ll, _ll, _ll,
                                  _ll, _ll, _ll, _vp]),
     "csa_topk_workspace_size": (_sz, [_i, _i, _i, _i]),
@@ -228,6 +229,11 @@ def csa_quantize_query_fp8(q, w, q_codes, w_folded, stream=None) -> None:
         raise ValueError("q_codes must match q, w and w_folded be q's shape without d")
     _check(lib().csa_quantize_query_fp8(_ptr(q), _dt(q), _ptr(w), _ptr(q_codes), _ptr(w_folded), rows, h, d,
                                         _stream(stream)))
+
+
+def csa_mfma_probe(sink, waves_per_simd: int, iters: int, valu_per_mfma: int, stream=None) -> None:
+    """Matrix-core issue ceiling (calibration, not a step of the method)."""
+    _check(lib().csa_mfma_probe(_ptr(sink), int(waves_per_simd), int(iters), int(valu_per_mfma), _stream(stream)))
 
 
 def csa_read_probe(buf, sink, stream=None) -> None:

@@ -31,7 +31,54 @@ __global__ __launch_bounds__(kProbeThreads) void k_read_probe(const uint4* __res
     if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the loads; practically never taken
 }
 
+// Matrix-core issue ceiling: every wave runs four independent chains of
+// v_mfma_f32_16x16x32_bf16 (16,384 FLOP each) with kValu float FMAs on
+// independent registers between consecutive MFMAs, the ratio of vector work
+// to matrix work that a kernel's epilogue imposes.  Operands come from the
+// thread index (nothing folds); the sums reach `sink` only on a value that
+// practically never occurs, so no work is removed.
+template <int kValu>
+__global__ __launch_bounds__(kProbeThreads) void k_mfma_probe(float* __restrict__ sink, int iters) {
+    const int t = threadIdx.x + blockIdx.x * blockDim.x;
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = static_cast<__bf16>(static_cast<float>((t + e) & 7) * 0.125f);
+        b[e] = static_cast<__bf16>(static_cast<float>((t * 3 + e) & 7) * 0.0625f);
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float x[4] = {static_cast<float>(t & 15), 1.f, 2.f, 3.f};
+    const float y = 1.0000001f, z = static_cast<float>(t & 3) * 1e-7f;
+#pragma unroll 1
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < kValu; ++v) x[(c + v) & 3] = fmaf(x[(c + v) & 3], y, z);
+        }
+    }
+    float s = x[0] + x[1] + x[2] + x[3];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+    if (s == 1234567.f) sink[0] = s;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_probe(float* sink, int waves_per_simd, int iters, int valu_per_mfma, hipStream_t s) {
+    const dim3 grid(device_cu_count() * waves_per_simd), block(kProbeThreads);
+    switch (valu_per_mfma) {
+        case 0: hipLaunchKernelGGL(k_mfma_probe<0>, grid, block, 0, s, sink, iters); break;
+        case 1: hipLaunchKernelGGL(k_mfma_probe<1>, grid, block, 0, s, sink, iters); break;
+        case 2: hipLaunchKernelGGL(k_mfma_probe<2>, grid, block, 0, s, sink, iters); break;
+        case 3: hipLaunchKernelGGL(k_mfma_probe<3>, grid, block, 0, s, sink, iters); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_read_probe(const void* buf, long long bytes, unsigned* sink, hipStream_t s) {
     if (bytes < 16) return hipSuccess;

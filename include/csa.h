@@ -637,6 +637,16 @@ int csa_prefill_attn_mixed(const void *q, const unsigned char *comp_rec, int n_c
  * ------------------------------------------------------------------------ */
 int csa_read_probe(const void *buf, long long bytes, unsigned *sink, csa_stream stream);
 
+/* csa_mfma_probe: the matrix cores' issue ceiling.  waves_per_simd (1..8)
+ *   workgroups of 256 threads per compute unit; every wave runs iters
+ *   (1..2^24) rounds of four independent v_mfma_f32_16x16x32_bf16 chains,
+ *   with valu_per_mfma (0..3) float FMAs on other registers after each MFMA.
+ *   One launch performs (CUs x waves_per_simd x 4 waves) x iters x 4 x 16,384
+ *   FLOP; timed, it gives the bf16 matrix rate a kernel with that much vector
+ *   work per MFMA can reach.  sink: one float of device memory (rarely
+ *   written).  Bad arguments: CSA_ERR_INVALID_ARG. */
+int csa_mfma_probe(float *sink, int waves_per_simd, int iters, int valu_per_mfma, csa_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

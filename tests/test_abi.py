@@ -129,6 +129,17 @@ def test_fp8_entry_points_reject_bad_args(csa):
     assert lib.csa_index_score_fp8(*a) == B.CSA_ERR_INVALID_ARG
 
 
+def test_probes_reject_bad_args(csa):
+    lib, B = csa.lib(), csa.binding
+    sink = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation
+    assert lib.csa_mfma_probe(None, 1, 1, 0, None) == B.CSA_ERR_INVALID_ARG
+    assert lib.csa_mfma_probe(sink, 0, 1, 0, None) == B.CSA_ERR_INVALID_ARG
+    assert lib.csa_mfma_probe(sink, 9, 1, 0, None) == B.CSA_ERR_INVALID_ARG
+    assert lib.csa_mfma_probe(sink, 1, 0, 0, None) == B.CSA_ERR_INVALID_ARG
+    assert lib.csa_mfma_probe(sink, 1, 1, 4, None) == B.CSA_ERR_INVALID_ARG
+    assert lib.csa_read_probe(None, 64, None, None) == B.CSA_ERR_INVALID_ARG
+
+
 def test_prefill_entry_points_reject_bad_args(csa):
     lib = csa.lib()
     B = csa.binding
