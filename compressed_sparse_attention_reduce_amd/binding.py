@@ -84,8 +84,6 @@ _SIGS = {
     "csa_quantize_fp8": (_i, [_vp, _i, _vp, _vp, _ll, _i, _vp]),
     "csa_quantize_query_fp8": (_i, [_vp, _i, _vp, _vp, _vp, _ll, _i, _i, _vp]),
     "csa_pack_kv_mixed": (_i, [_vp, _i, _vp, _ll, _i, _i, _vp]),
-    "csa_read_probe": (_i, [_vp, _ll, _vp, _vp]),
-    "csa_mfma_probe": (_i, [_vp, _i, _i, _i, _vp]),
     "csa_index_score_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _ll, _ll, _ll,
                                  _ll, _ll, _ll, _vp]),
     "csa_topk_workspace_size": (_sz, [_i, _i, _i, _i]),
@@ -122,6 +120,30 @@ _SIGS = {
 }
 
 _lib = None
+
+
+_CALIB_SIGS = {
+    "csa_read_probe": (_i, [_vp, _ll, _vp, _vp]),
+    "csa_mfma_probe": (_i, [_vp, _i, _i, _i, _vp]),
+}
+CALIB_LIB_PATH = os.path.join(_PKG, "libcsa_calib.so")
+_calib = None
+
+
+def calib_lib() -> ctypes.CDLL:
+    """The calibration probes' library (include/csa_calib.h), loaded on first use."""
+    global _calib
+    if _calib is None:
+        if not os.path.exists(CALIB_LIB_PATH):
+            raise RuntimeError(f"{CALIB_LIB_PATH} is missing: build it first (python -c "
+                               "'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(CALIB_LIB_PATH)
+        for name, (res, args) in _CALIB_SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _calib = L
+    return _calib
 
 
 def lib() -> ctypes.CDLL:
@@ -231,16 +253,23 @@ def csa_quantize_query_fp8(q, w, q_codes, w_folded, stream=None) -> None:
                                         _stream(stream)))
 
 
+def _check_calib(rc: int, name: str) -> None:
+    if rc != CSA_OK:
+        raise CsaError(rc, f"{name}: bad arguments or launch failure")
+
+
 def csa_mfma_probe(sink, waves_per_simd: int, iters: int, valu_per_mfma: int, stream=None) -> None:
-    """Matrix-core issue ceiling (calibration, not a step of the method)."""
-    _check(lib().csa_mfma_probe(_ptr(sink), int(waves_per_simd), int(iters), int(valu_per_mfma), _stream(stream)))
+    """Matrix-core issue ceiling (libcsa_calib.so; not a step of the method)."""
+    _check_calib(calib_lib().csa_mfma_probe(_ptr(sink), int(waves_per_simd), int(iters), int(valu_per_mfma),
+                                            _stream(stream)), "csa_mfma_probe")
 
 
 def csa_read_probe(buf, sink, stream=None) -> None:
-    """Read every byte of the contiguous device tensor buf once (calibration)."""
+    """Read every byte of the contiguous device tensor buf once (libcsa_calib.so; calibration)."""
     if not buf.is_contiguous():
         raise ValueError("buf must be contiguous")
-    _check(lib().csa_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
+    _check_calib(calib_lib().csa_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                            _stream(stream)), "csa_read_probe")
 
 
 MIX_REC_BYTES = 592  # one mixed main-KV row: 448 E4M3 codes, 64 bf16 RoPE values, scale, pad

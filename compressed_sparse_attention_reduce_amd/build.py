@@ -1,8 +1,10 @@
 """Ahead-of-time build of libcsa.so (the C-ABI library) for gfx950.
 
 Every ``csrc/*.hip`` file is compiled with hipcc to an object in ``_build/``
-(in parallel), then linked into ``libcsa.so`` next to this file.  All device
-code is built with packed-FP32 instruction selection disabled.
+(in parallel), then linked into ``libcsa.so`` next to this file; the
+calibration probes in ``csrc/calib/`` go into ``libcsa_calib.so`` beside it
+(include/csa_calib.h).  All device code is built with packed-FP32
+instruction selection disabled.
 """
 
 from __future__ import annotations
@@ -17,6 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
+CALIB_LIB = os.path.join(PKG, "libcsa_calib.so")
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -48,18 +51,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    """Compile every HIP source and link libcsa.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
-    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 8) -> str:
+    """Compile every HIP source and link libcsa.so and libcsa_calib.so;
+    returns the path of libcsa.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    calib_dir = os.path.join(CSRC, "calib")
+    calib = sorted(os.path.join(calib_dir, f) for f in os.listdir(calib_dir) if f.endswith(".hip"))
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs) + len(calib)))) as ex:
+        objs = list(ex.map(_compile, srcs + calib))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], CALIB_LIB)
     return LIB
 
 

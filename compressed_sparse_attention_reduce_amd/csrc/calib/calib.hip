@@ -1,9 +1,11 @@
-// Calibration: a plain streaming read of a buffer, the practical HBM read
-// ceiling that the memory-bound kernels here are compared with (one launch
-// reading each byte once, as the index scan reads its key cache).  Not a
-// step of the method.
-#include "common.h"
-#include "kernels.h"
+// Calibration probes (libcsa_calib.so, include/csa_calib.h), not a step of
+// the method and not part of libcsa.so: a plain streaming read of a buffer
+// (the practical HBM read ceiling that the memory-bound kernels are compared
+// with: one launch reading each byte once, as the index scan reads its key
+// cache) and the matrix cores' issue ceiling.
+#include "csa_calib.h"
+
+#include "../common.h"
 
 namespace csa {
 
@@ -68,8 +70,17 @@ __global__ __launch_bounds__(kProbeThreads) void k_mfma_probe(float* __restrict_
 
 }  // namespace
 
+int cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return n;
+}
+
 hipError_t launch_mfma_probe(float* sink, int waves_per_simd, int iters, int valu_per_mfma, hipStream_t s) {
-    const dim3 grid(device_cu_count() * waves_per_simd), block(kProbeThreads);
+    const int cus = cu_count();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    const dim3 grid(cus * waves_per_simd), block(kProbeThreads);
     switch (valu_per_mfma) {
         case 0: hipLaunchKernelGGL(k_mfma_probe<0>, grid, block, 0, s, sink, iters); break;
         case 1: hipLaunchKernelGGL(k_mfma_probe<1>, grid, block, 0, s, sink, iters); break;
@@ -82,9 +93,32 @@ hipError_t launch_mfma_probe(float* sink, int waves_per_simd, int iters, int val
 
 hipError_t launch_read_probe(const void* buf, long long bytes, unsigned* sink, hipStream_t s) {
     if (bytes < 16) return hipSuccess;
-    hipLaunchKernelGGL(k_read_probe, dim3(2 * device_cu_count()), dim3(kProbeThreads), 0, s,
-                       static_cast<const uint4*>(buf), bytes / 16, sink);
+    const int cus = cu_count();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    hipLaunchKernelGGL(k_read_probe, dim3(2 * cus), dim3(kProbeThreads), 0, s, static_cast<const uint4*>(buf),
+                       bytes / 16, sink);
     return hipGetLastError();
 }
 
 }  // namespace csa
+
+extern "C" {
+
+int csa_read_probe(const void* buf, long long bytes, unsigned* sink, csa_stream stream) {
+    if (bytes < 0 || (bytes >= 16 && (!buf || !sink)) || (reinterpret_cast<uintptr_t>(buf) & 15) != 0)
+        return CSA_ERR_INVALID_ARG;
+    return csa::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)) == hipSuccess ? CSA_OK
+                                                                                                     : CSA_ERR_LAUNCH;
+}
+
+int csa_mfma_probe(float* sink, int waves_per_simd, int iters, int valu_per_mfma, csa_stream stream) {
+    if (!sink || waves_per_simd < 1 || waves_per_simd > 8 || iters < 1 || iters > (1 << 24) || valu_per_mfma < 0 ||
+        valu_per_mfma > 3)
+        return CSA_ERR_INVALID_ARG;
+    return csa::launch_mfma_probe(sink, waves_per_simd, iters, valu_per_mfma, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? CSA_OK
+               : CSA_ERR_LAUNCH;
+}
+
+}  // extern "C"

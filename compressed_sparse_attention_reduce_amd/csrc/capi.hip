@@ -174,23 +174,6 @@ int csa_quantize_query_fp8(const void* q, csa_dtype q_dtype, const float* w, uns
                     "csa_quantize_query_fp8");
 }
 
-int csa_read_probe(const void* buf, long long bytes, unsigned* sink, csa_stream stream) {
-    CHECK((buf && sink) || bytes < 16, "csa_read_probe: null pointer argument");
-    CHECK(bytes >= 0 && aligned16(buf), "csa_read_probe: bytes %lld / unaligned buffer", bytes);
-    return launched(csa::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)), "csa_read_probe");
-}
-
-int csa_mfma_probe(float* sink, int waves_per_simd, int iters, int valu_per_mfma, csa_stream stream) {
-    CHECK(sink, "csa_mfma_probe: null sink");
-    CHECK(waves_per_simd >= 1 && waves_per_simd <= 8 && iters >= 1 && iters <= (1 << 24) && valu_per_mfma >= 0 &&
-              valu_per_mfma <= 3,
-          "csa_mfma_probe: waves_per_simd %d (1..8), iters %d (1..2^24), valu_per_mfma %d (0..3)", waves_per_simd,
-          iters, valu_per_mfma);
-    return launched(csa::launch_mfma_probe(sink, waves_per_simd, iters, valu_per_mfma,
-                                           static_cast<hipStream_t>(stream)),
-                    "csa_mfma_probe");
-}
-
 int csa_pack_kv_mixed(const void* x, csa_dtype x_dtype, unsigned char* rec, long long rows, int d, int rope_dim,
                       csa_stream stream) {
     CHECK((x && rec) || rows == 0, "csa_pack_kv_mixed: null pointer argument");

@@ -12,9 +12,6 @@ namespace csa {
 int device_cu_count();
 
 // calibration read (calib.hip): every 16-byte piece of buf read once
-hipError_t launch_read_probe(const void* buf, long long bytes, unsigned* sink, hipStream_t s);
-// waves_per_simd x 256 threads per CU, each wave iters x 4 MFMAs of 16x16x32 bf16
-hipError_t launch_mfma_probe(float* sink, int waves_per_simd, int iters, int valu_per_mfma, hipStream_t s);
 
 constexpr int kTopkMaxK = 2048;
 

@@ -626,27 +626,6 @@ int csa_prefill_attn_mixed(const void *q, const unsigned char *comp_rec, int n_c
                            const float *sink, float scale, void *out, csa_dtype out_dtype, float *lse,
                            int t, int h, csa_stream stream);
 
-/* ------------------------------------------------------------------------
- * 8. Calibration (not a step of the method).
- *
- * csa_read_probe: read every byte of buf (device, 16-byte aligned, the first
- *   bytes / 16 * 16 of them) once with plain streaming loads, as one launch:
- *   timed over large buffers it gives the practical HBM read ceiling of one
- *   launch that memory-bound kernels can be compared with.  sink: one
- *   unsigned of device memory (rarely written).
- * ------------------------------------------------------------------------ */
-int csa_read_probe(const void *buf, long long bytes, unsigned *sink, csa_stream stream);
-
-/* csa_mfma_probe: the matrix cores' issue ceiling.  waves_per_simd (1..8)
- *   workgroups of 256 threads per compute unit; every wave runs iters
- *   (1..2^24) rounds of four independent v_mfma_f32_16x16x32_bf16 chains,
- *   with valu_per_mfma (0..3) float FMAs on other registers after each MFMA.
- *   One launch performs (CUs x waves_per_simd x 4 waves) x iters x 4 x 16,384
- *   FLOP; timed, it gives the bf16 matrix rate a kernel with that much vector
- *   work per MFMA can reach.  sink: one float of device memory (rarely
- *   written).  Bad arguments: CSA_ERR_INVALID_ARG. */
-int csa_mfma_probe(float *sink, int waves_per_simd, int iters, int valu_per_mfma, csa_stream stream);
-
 #ifdef __cplusplus
 }
 #endif

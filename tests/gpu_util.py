@@ -50,6 +50,15 @@ def rel_err(g, r) -> float:
     return float(np.abs(g - r).max() / scale)
 
 
+def assert_lse_close(g, r, abs_tol: float = 1e-2, rel_tol: float = 2e-2) -> None:
+    """Log-sum-exp of the bf16 path: the relative rule of the other outputs
+    (max |diff| / max |oracle|) and an absolute bound, both."""
+    g = np.asarray(g, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    assert rel_err(g, r) <= rel_tol, rel_err(g, r)
+    assert np.abs(g - r).max() <= abs_tol, np.abs(g - r).max()
+
+
 def assert_bf16_close(g_bits: np.ndarray, exact: np.ndarray, ulps: int = 1) -> None:
     """bf16 output within `ulps` of round-to-nearest-even(exact)."""
     g = numfmt.bf16_bits_to_f64(g_bits)

@@ -129,8 +129,20 @@ def test_fp8_entry_points_reject_bad_args(csa):
     assert lib.csa_index_score_fp8(*a) == B.CSA_ERR_INVALID_ARG
 
 
+def test_calib_symbols_are_exported_by_their_own_library(csa):
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "csa_calib.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(csa_\w+)\s*\(", text)))
+    assert names == ["csa_mfma_probe", "csa_read_probe"]
+    out = subprocess.run(["nm", "-D", "--defined-only", csa.binding.CALIB_LIB_PATH], capture_output=True, text=True)
+    exported = set(re.findall(r" T (\w+)", out.stdout))
+    assert set(names) <= exported
+    # and they are not part of the CSA library itself
+    out = subprocess.run(["nm", "-D", "--defined-only", csa.binding.LIB_PATH], capture_output=True, text=True)
+    assert not set(names) & set(re.findall(r" T (\w+)", out.stdout))
+
+
 def test_probes_reject_bad_args(csa):
-    lib, B = csa.lib(), csa.binding
+    lib, B = csa.binding.calib_lib(), csa.binding
     sink = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation
     assert lib.csa_mfma_probe(None, 1, 1, 0, None) == B.CSA_ERR_INVALID_ARG
     assert lib.csa_mfma_probe(sink, 0, 1, 0, None) == B.CSA_ERR_INVALID_ARG

@@ -16,7 +16,7 @@ import torch
 import oracle
 import synth
 from oracle import numfmt
-from tests.gpu_util import DEV, as_f64, assert_topk_gap_rule, dev_bf16, dev_f32, host_f64, rel_err
+from tests.gpu_util import assert_lse_close, DEV, as_f64, assert_topk_gap_rule, dev_bf16, dev_f32, host_f64, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -371,7 +371,7 @@ def test_prefill_attn(csa, case):
     ro, rl = _attn_ref(as_f64(qn), as_f64(comp), idx, cnt, as_f64(win), window, pos0,
                        None if sink is None else sink.astype(np.float64), scale)
     assert rel_err(host_f64(out), ro) <= 2e-2
-    assert np.abs(lse.cpu().numpy() - rl).max() <= 1e-2
+    assert_lse_close(lse.cpu().numpy(), rl)
 
 
 # ---------------------------------------------------------------------------
@@ -399,7 +399,7 @@ def test_prefill_chunk_matches_oracle_composition(csa):
     ro, rl = _attn_ref(as_f64(x["q"]), as_f64(x["comp_kv"]), gi, gc, as_f64(x["win_kv"]), W, x["pos0"],
                        x["sink"].astype(np.float64), 1.0 / np.sqrt(shape.d))
     assert rel_err(host_f64(out), ro) <= 2e-2
-    assert np.abs(lse.cpu().numpy() - rl).max() <= 1e-2
+    assert_lse_close(lse.cpu().numpy(), rl)
     same = [r for r in range(T) if (gi[r] == ref["idx"][r]).all()]
     assert len(same) >= T // 2
     assert rel_err(host_f64(out)[same], ref["out"][same]) <= 2e-2
@@ -450,7 +450,7 @@ def test_prefill_full_size_sampled(csa):
         kv = np.concatenate([comp[gi[r, :gc[r]]], np.stack(wrows)])
         o, l = oracle.sparse_attn(qh[i], kv, sink, 1.0 / np.sqrt(shape.d))
         assert rel_err(outs[i], o) <= 2e-2
-        assert np.abs(lse[r].cpu().numpy() - l).max() <= 1e-2
+        assert_lse_close(lse[r].cpu().numpy(), l)
 
 
 # ---------------------------------------------------------------------------
