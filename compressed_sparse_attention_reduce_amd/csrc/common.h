@@ -18,6 +18,9 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
+// s_waitcnt immediate: vmcnt(0), the other counters left free
+constexpr int kVmcntZero = 0x0f70;
+
 // float32 -> bfloat16 bits, round to nearest even (quiet NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
     uint32_t u = __float_as_uint(x);

@@ -127,6 +127,21 @@ __device__ inline void slice_row_update(float lz, float lc, float& mx, float& de
     acc += e * lc;
 }
 
+// One lane-swap level of slice_merge: the running sums of slice partners
+// O lanes apart combined (DPP moves, no LDS).
+template <int O>
+__device__ inline void slice_swap(float& m2, float& d2, float& a2) {
+    const float mo = xor_lanes_f32<O>(m2);
+    const float dn = xor_lanes_f32<O>(d2);
+    const float ao = xor_lanes_f32<O>(a2);
+    const float M = fmaxf(m2, mo);
+    const float f1 = m2 == -INFINITY ? 0.f : expf(m2 - M);  // an empty slice adds nothing
+    const float f2 = mo == -INFINITY ? 0.f : expf(mo - M);
+    d2 = d2 * f1 + dn * f2;
+    a2 = a2 * f1 + ao * f2;
+    m2 = M;
+}
+
 // The slices' running sums combined in LDS; the output channels written.
 __device__ inline void slice_merge(float mx, float den, float acc, void* __restrict__ out_row, bool out_bf16, int d,
                                    int ch0, int nch, float* part) {
@@ -146,17 +161,12 @@ __device__ inline void slice_merge(float mx, float den, float acc, void* __restr
         float m2 = part[s2 * nch + tc];
         float d2 = part[blockDim.x + s2 * nch + tc];
         float a2 = part[2 * blockDim.x + s2 * nch + tc];
-        for (int off = 1; off < slices; off <<= 1) {
-            const float mo = __shfl_xor(m2, off);
-            const float dn = __shfl_xor(d2, off);
-            const float ao = __shfl_xor(a2, off);
-            const float M = fmaxf(m2, mo);
-            const float f1 = m2 == -INFINITY ? 0.f : expf(m2 - M);  // an empty slice adds nothing
-            const float f2 = mo == -INFINITY ? 0.f : expf(mo - M);
-            d2 = d2 * f1 + dn * f2;
-            a2 = a2 * f1 + ao * f2;
-            m2 = M;
-        }
+        if (slices > 1) slice_swap<1>(m2, d2, a2);
+        if (slices > 2) slice_swap<2>(m2, d2, a2);
+        if (slices > 4) slice_swap<4>(m2, d2, a2);
+        if (slices > 8) slice_swap<8>(m2, d2, a2);
+        if (slices > 16) slice_swap<16>(m2, d2, a2);
+        if (slices > 32) slice_swap<32>(m2, d2, a2);
         if (s2 == 0 && ch0 + tc < d) {
             const float y = a2 / d2;
             if (out_bf16)

@@ -37,6 +37,53 @@ constexpr int kDenseRowPer = kDenseRows * kDenseMaxD / 8 / kDenseThreads; // row
 // channels of a folded block compression per workgroup, at least: 32 row
 // slices of 4 rows each for a 128-row block, merged by 16 threads
 constexpr int kFoldMinCh = 16;
+constexpr int kFoldPre = 4;  // rows of its slice a thread loads with the attention's rows (a 128-row block)
+
+// The slices' (max, denominator, weighted sum) of the folded compression
+// combined: transposed through LDS so that a channel's slices sit in
+// consecutive lanes, the channel's maximum by lane swaps, each slice rescaled
+// to it once, then the sums by lane swaps; y = sum / denominator.  Other
+// slice counts take slice_merge.  part: 3 * blockDim.x floats of LDS.
+__device__ inline void fold_merge(float mx, float den, float acc, void* __restrict__ out_row, bool out_bf16, int d,
+                                  int ch0, int nch, float* part) {
+    const int slices = blockDim.x / nch;
+    if ((slices & (slices - 1)) != 0 || slices > kWave || slices * nch != static_cast<int>(blockDim.x)) {
+        slice_merge(mx, den, acc, out_row, out_bf16, d, ch0, nch, part);
+        return;
+    }
+    part[threadIdx.x] = mx;
+    part[blockDim.x + threadIdx.x] = den;
+    part[2 * blockDim.x + threadIdx.x] = acc;
+    __syncthreads();
+    const int tc = threadIdx.x / slices;
+    const int s2 = threadIdx.x % slices;
+    const float m2 = part[s2 * nch + tc];
+    float d2 = part[blockDim.x + s2 * nch + tc];
+    float a2 = part[2 * blockDim.x + s2 * nch + tc];
+    float M = m2;
+    if (slices > 1) M = fmaxf(M, xor_lanes_f32<1>(M));
+    if (slices > 2) M = fmaxf(M, xor_lanes_f32<2>(M));
+    if (slices > 4) M = fmaxf(M, xor_lanes_f32<4>(M));
+    if (slices > 8) M = fmaxf(M, xor_lanes_f32<8>(M));
+    if (slices > 16) M = fmaxf(M, xor_lanes_f32<16>(M));
+    if (slices > 32) M = fmaxf(M, xor_lanes_f32<32>(M));
+    const float f = m2 == -INFINITY ? 0.f : expf(m2 - M);  // an empty slice adds nothing
+    d2 *= f;
+    a2 *= f;
+    if (slices > 1) { d2 += xor_lanes_f32<1>(d2); a2 += xor_lanes_f32<1>(a2); }
+    if (slices > 2) { d2 += xor_lanes_f32<2>(d2); a2 += xor_lanes_f32<2>(a2); }
+    if (slices > 4) { d2 += xor_lanes_f32<4>(d2); a2 += xor_lanes_f32<4>(a2); }
+    if (slices > 8) { d2 += xor_lanes_f32<8>(d2); a2 += xor_lanes_f32<8>(a2); }
+    if (slices > 16) { d2 += xor_lanes_f32<16>(d2); a2 += xor_lanes_f32<16>(a2); }
+    if (slices > 32) { d2 += xor_lanes_f32<32>(d2); a2 += xor_lanes_f32<32>(a2); }
+    if (s2 == 0 && ch0 + tc < d) {
+        const float y = a2 / d2;
+        if (out_bf16)
+            static_cast<uint16_t*>(out_row)[ch0 + tc] = f32_to_bf16(y);
+        else
+            static_cast<float*>(out_row)[ch0 + tc] = y;
+    }
+}
 
 __host__ __device__ inline size_t dense_lds_bytes(int d) {
     return sizeof(uint16_t) * (static_cast<size_t>(kDenseRows + kHeadGroup) * (d + 8) +
@@ -49,7 +96,7 @@ __host__ __device__ inline size_t dense_lds_bytes(int d) {
 __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, int n_splits, int prep_wgs, PrepArgs p,
                                                                     int extra_rows, int fold_ch, float* entry_f32) {
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-    __shared__ float wmax[kDenseWaves][kHeadGroup];
+    __shared__ __attribute__((aligned(16))) float wmax[kDenseWaves][kHeadGroup];
     __shared__ float wsum[kDenseWaves][kHeadGroup];
     // the step's small jobs (SWA append, compression of a completed block) in
     // their own workgroups; the rows they write are not
@@ -98,36 +145,86 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
     // A block this step completes is compressed here, fold_ch channels per
     // workgroup by the first ones (ratio-m blocks are long: one workgroup
     // alone would take longer than the attention).  Its rows are independent
-    // of the attention's, which covers the entries before the step only.
-    // With device counters the block's rows come from the ring, to which
-    // each folding workgroup first adds its channels of the token's row.
+    // of the attention's, which covers the entries before the step only, so
+    // the channels' inputs are loaded with the attention's rows and reduced
+    // after the partials are written.  With device counters the block's last
+    // row is the token's own; the others come from the ring, to which each
+    // folding workgroup adds its channels of the token's row.
     const bool fold = fold_ch > 0 && id * fold_ch < p.d && dev_done;  // uniform
-    auto fold_block = [&](float* scratch) {
-        const float* z = p.z_main + b * p.zc_main_stride_b;
-        const float* c = p.c_main + b * p.zc_main_stride_b;
-        const int ch0 = id * fold_ch;
-        const int nch = min(fold_ch, p.d - ch0);
-        if (p.dev) {
-            const long long pos = p.block * p.m + p.m - 1;  // the completing token
-            float* rz = p.dev_ring + b * p.ring_stride_b;
-            float* rc = rz + 2LL * p.m * p.d;
-            const long long slot = pos % (2 * p.m);
-            for (int j = threadIdx.x; j < nch; j += blockDim.x) {
-                rz[slot * p.d + ch0 + j] = z[ch0 + j];
-                rc[slot * p.d + ch0 + j] = c[ch0 + j];
+    const int f_ch0 = id * fold_ch;
+    const int f_nch = fold ? min(fold_ch, p.d - f_ch0) : 0;
+    int f_ch = 0, f_lo = 0, f_hi = 0;
+    float fz[kFoldPre], fb[kFoldPre], fc[kFoldPre];
+    const float* f_z = p.z_main + b * p.zc_main_stride_b;
+    const float* f_c = p.c_main + b * p.zc_main_stride_b;
+    auto fold_src = [&](int r, const float*& zr, const float*& cr) {
+        if (p.dev && r < p.m - 1) {
+            const float* rz = p.dev_ring + b * p.ring_stride_b;
+            const long long o = (p.block & 1) * static_cast<long long>(p.m) * p.d + static_cast<long long>(r) * p.d;
+            zr = rz + o;
+            cr = rz + 2LL * p.m * p.d + o;
+        } else if (p.dev) {
+            zr = f_z;
+            cr = f_c;
+        } else {
+            zr = f_z + static_cast<long long>(r) * p.d;
+            cr = f_c + static_cast<long long>(r) * p.d;
+        }
+    };
+    auto fold_load = [&]() {
+        slice_rows(p.m, p.d, f_ch0, f_nch, f_ch, f_lo, f_hi);
+#pragma unroll
+        for (int u = 0; u < kFoldPre; ++u) {
+            const int r = f_lo + u;
+            fz[u] = fb[u] = fc[u] = 0.f;
+            if (r < f_hi) {
+                const float* zr;
+                const float* cr;
+                fold_src(r, zr, cr);
+                fz[u] = zr[f_ch];
+                fb[u] = p.main_bias[static_cast<long long>(r) * p.d + f_ch];
+                fc[u] = cr[f_ch];
             }
-            __syncthreads();
-            const long long cur = (p.block & 1) * static_cast<long long>(p.m) * p.d;
-            z = rz + cur;
-            c = rc + cur;
         }
-        if (entry_f32) {
-            compress_block_slice(z, c, p.main_bias, entry_f32 + static_cast<long long>(b) * p.d, false, p.m, p.d, ch0,
-                                 nch, scratch);
-            return;
+    };
+    // every thread calls it (scratch: 3 * blockDim.x floats of LDS, free)
+    auto fold_finish = [&](float* scratch) {
+        // the loaded rows against their own maximum (one exponential per row),
+        // any further rows of a longer slice by the running form
+        float lz[kFoldPre];
+        float mx = -INFINITY, den = 0.f, acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < kFoldPre; ++u) {
+            lz[u] = fz[u] + fb[u];
+            if (f_lo + u < f_hi) mx = fmaxf(mx, lz[u]);
         }
-        char* out = static_cast<char*>(p.comp_kv) + (b * p.comp_kv_stride_b + static_cast<long long>(p.n_comp) * p.d) * p.es;
-        compress_block_slice(z, c, p.main_bias, out, p.es == 2, p.m, p.d, ch0, nch, scratch);
+#pragma unroll
+        for (int u = 0; u < kFoldPre; ++u) {
+            if (f_lo + u < f_hi) {
+                const float e = expf(lz[u] - mx);
+                den += e;
+                acc += e * fc[u];
+            }
+        }
+        for (int r = f_lo + kFoldPre; r < f_hi; ++r) {
+            const float* zr;
+            const float* cr;
+            fold_src(r, zr, cr);
+            slice_row_update(zr[f_ch] + p.main_bias[static_cast<long long>(r) * p.d + f_ch], cr[f_ch], mx, den, acc);
+        }
+        if (p.dev) {  // the token's channels into the ring (its slot in the block's half)
+            float* rz = p.dev_ring + b * p.ring_stride_b;
+            const long long o = ((p.block & 1) * static_cast<long long>(p.m) + p.m - 1) * p.d + f_ch0;
+            for (int j = threadIdx.x; j < f_nch; j += blockDim.x) {
+                rz[o + j] = f_z[f_ch0 + j];
+                rz[2LL * p.m * p.d + o + j] = f_c[f_ch0 + j];
+            }
+        }
+        void* out = entry_f32 ? static_cast<void*>(entry_f32 + static_cast<long long>(b) * p.d)
+                              : static_cast<void*>(static_cast<char*>(p.comp_kv) +
+                                                   (b * p.comp_kv_stride_b + static_cast<long long>(p.n_comp) * p.d) *
+                                                       p.es);
+        fold_merge(mx, den, acc, out, !entry_f32 && p.es == 2, p.d, f_ch0, f_nch, scratch);
     };
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
@@ -151,7 +248,10 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
             a.ws_ml[2 * (ml_base + static_cast<long long>(threadIdx.x) * n_splits) + 0] = -INFINITY;
             a.ws_ml[2 * (ml_base + static_cast<long long>(threadIdx.x) * n_splits) + 1] = 0.f;
         }
-        if (fold) fold_block(reinterpret_cast<float*>(smem));
+        if (fold) {
+            fold_load();
+            fold_finish(reinterpret_cast<float*>(smem));
+        }
         return;
     }
     // 1. the split's rows and the query group to LDS, all loads in one batch
@@ -198,10 +298,15 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
                            : swa + static_cast<long long>(swa_slot(a.swa_head, a.swa_len, j - cnt, a.w)) * d;
         };
         if (wave_rows) {
+            // one whole row per wave instruction, straight into its LDS row
+            // (no registers, no LDS stores); rows past the split's repeat its
+            // first row, whose probabilities are zero
 #pragma unroll
             for (int u = 0; u < kDenseRowPer; ++u) {
                 const int r = wvu + u * kRowStep;
-                v[u] = r < rows ? *reinterpret_cast<const uint4*>(row_of(r0 + r) + lane * 8) : make_uint4(0, 0, 0, 0);
+                __builtin_amdgcn_global_load_lds(row_of(r < rows ? r0 + r : r0) + lane * 8,
+                                                 (__attribute__((address_space(3))) void*)(tile + r * pitch), 16, 0,
+                                                 0);
             }
         } else {
 #pragma unroll
@@ -216,11 +321,8 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
         qv[u] = c < kHeadGroup * cpr ? *reinterpret_cast<const uint4*>(qg + (c / cpr) * d + (c % cpr) * 8)
                                      : make_uint4(0, 0, 0, 0);
     }
-    // the block's channels while the rows are in flight (LDS as scratch first)
-    if (fold) {
-        fold_block(reinterpret_cast<float*>(smem));
-        __syncthreads();
-    }
+    // the block's channels: loads behind the rows', reduced at the end
+    if (fold) fold_load();
     if (a.kv_mixed) {  // decode the pieces (the first use of the loaded bytes); rows past the split's are zero
 #pragma unroll
         for (int u = 0; u < kDenseRowPer; ++u)
@@ -231,9 +333,14 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
         const int c = threadIdx.x + u * kDenseThreads;
         if (c < kHeadGroup * cpr) *reinterpret_cast<uint4*>(qs + (c / cpr) * pitch + (c % cpr) * 8) = qv[u];
     }
+    const bool direct = wave_rows && !a.kv_mixed;  // the rows went straight to LDS
+    if (direct) {
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);  // this wave's row loads have landed
+    } else {
 #pragma unroll
-    for (int u = 0; u < kDenseRowPer; ++u)
-        if (pr[u] < kDenseRows) *reinterpret_cast<uint4*>(tile + pr[u] * pitch + pc[u] * 8) = v[u];
+        for (int u = 0; u < kDenseRowPer; ++u)
+            if (pr[u] < kDenseRows) *reinterpret_cast<uint4*>(tile + pr[u] * pitch + pc[u] * 8) = v[u];
+    }
     __syncthreads();
 
     // 2. S = q K^T: wave wv owns rows 16*wv .. 16*wv+15; per-head max of the wave
@@ -245,6 +352,20 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
         const uint16_t* krow = tile + my_row * pitch + 8 * lg;
         const int nks = d / 32;
         int ks = 0;
+        if (d == kDenseMaxD) {  // all k-steps unrolled, two accumulators: half the dependent chain
+            f32x4 s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k2 = 0; k2 < kDenseMaxD / 32; k2 += 2) {
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(qrow + 32 * k2),
+                                                               *reinterpret_cast<const bf16x8*>(krow + 32 * k2), sacc,
+                                                               0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(qrow + 32 * k2 + 32),
+                                                             *reinterpret_cast<const bf16x8*>(krow + 32 * k2 + 32), s1,
+                                                             0, 0, 0);
+            }
+            sacc += s1;
+            ks = nks;
+        }
         for (; ks + 4 <= nks; ks += 4) {
             bf16x8 qa[4], kb[4];
 #pragma unroll
@@ -271,12 +392,20 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
     }
     __syncthreads();
     // 3. probabilities against the split's max (finite: row 0 is valid)
+    float Mr[4];  // the split's maximum of heads 4 lg .. 4 lg + 3: one 16-byte read per wave
+    {
+        float4 m4 = *reinterpret_cast<const float4*>(&wmax[0][4 * lg]);
+#pragma unroll
+        for (int w = 1; w < kDenseWaves; ++w) {
+            const float4 o = *reinterpret_cast<const float4*>(&wmax[w][4 * lg]);
+            m4.x = fmaxf(m4.x, o.x); m4.y = fmaxf(m4.y, o.y); m4.z = fmaxf(m4.z, o.z); m4.w = fmaxf(m4.w, o.w);
+        }
+        Mr[0] = m4.x; Mr[1] = m4.y; Mr[2] = m4.z; Mr[3] = m4.w;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int hh = 4 * lg + r;
-        float M = wmax[0][hh];
-#pragma unroll
-        for (int w = 1; w < kDenseWaves; ++w) M = fmaxf(M, wmax[w][hh]);
+        const float M = Mr[r];
         const uint16_t pb = f32_to_bf16(expf(x[r] - M));
         pl[hh * kDensePPitch + my_row] = pb;
         float e = bf16_to_f32(pb);
@@ -303,6 +432,10 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
     const int ksteps = (rows + 31) / 32;  // rows past the valid ones hold zeros and p = 0
     for (int g = wv; 64 * g < d; g += kDenseWaves)
         pv_group<4>(tile, pitch, pl, kDensePPitch, ksteps, 64 * g, d, ob, static_cast<long long>(n_splits) * d);
+    if (fold) {
+        __syncthreads();  // P V's reads of the tile are over: it becomes the merge's scratch
+        fold_finish(reinterpret_cast<float*>(smem));
+    }
 }
 
 // Merge of the splits plus the step's new rows (the compressed entry of a

@@ -65,8 +65,6 @@ struct MqShape {
 };
 using Mq = MqShape<CSA_MQ_SHAPE>;
 constexpr int kMqRowsPerWg = Mq::kRows;
-// s_waitcnt immediate: vmcnt(0), the other counters left free
-constexpr int kVmcntZero = 0x0f70;
 constexpr int kMqPitch = kIdxDi + 8;  // LDS key row: 272 B, so the 16 rows of a B operand spread over the banks
 constexpr size_t kMqLds = sizeof(uint16_t) * 2 * Mq::kGroupTiles * 16 * kMqPitch;
 

@@ -291,13 +291,14 @@ def test_decode_step_ctx1m_mixed_kv_full_size(csa):
     assert_lse_close(outs["lse"][0].cpu().numpy(), rl)
 
 
-@pytest.mark.parametrize("B", [3, 5])
+@pytest.mark.parametrize("B", [3, 5, 8])
 def test_decode_step_mixed_kv_fp8_keys_batched(csa, B):
     """Several sequences, E4M3 indexer keys and mixed main KV together, a step
     that completes a block: each sequence's new records, scores, selection,
     gather_buf and output against the oracle.  Three sequences take the fused
     top-k + attention (240 workgroups, all resident on 256 compute units);
-    five take one top-k launch per sequence and the separate attention."""
+    five and eight take one top-k launch per sequence and the separate
+    attention (eight: 640 attention workgroups)."""
     shape = synth.with_(synth.SHAPES["ctx8k"], batch=B, ctx=4000, n_comp=999)
     x = synth.make_decode_inputs(shape, 7401, max_comp=1000)
     g = _g(7402)

@@ -407,6 +407,9 @@ ATTN_CASES = [
     ("gather_buf_640", 1, 64, 512, 640, [640], True, True, True),
     ("ragged_37", 1, 64, 512, 640, [37], True, True, True),
     ("batch_mixed", 4, 64, 512, 640, [640, 1, 333, 129], True, True, False),
+    # more splits than two rounds of workgroups on 256 compute units
+    ("wide_batch_ragged", 8, 64, 512, 640, [640, 1, 333, 129, 0, 500, 640, 257], True, True, False),
+    ("wide_d256", 16, 32, 256, 1000, [1000, 999, 128, 127, 1, 0, 640, 641] * 2, True, True, True),
     ("no_sink", 1, 32, 256, 96, [96], False, True, True),
     ("empty_with_sink", 1, 16, 128, 64, [0], True, True, False),
     ("empty_no_sink", 1, 16, 128, 64, [0], False, True, False),
