@@ -223,6 +223,7 @@ __device__ inline void attn_split(const AttnArgs& a, int n_splits, int split, in
     // 1. every chunk's source (top-k row of the compressed cache, SWA slot, or
     //    the plain kv rows), all loads in one unrolled batch: rows -> LDS (and
     //    gather_buf); query -> LDS
+    const bool direct = !a.kv_mixed && cpr == kWave && G::kChunks * (NT / kWave) == kR;
     uint4 v[G::kChunks];
     if (a.kv_mixed) {
         // mixed records (d = 512): one 16-byte read and the row scale per chunk, with no branch on the
@@ -264,6 +265,34 @@ __device__ inline void attn_split(const AttnArgs& a, int n_splits, int split, in
             }
             v[u] = live ? mixed_piece_value(v[u], vsc[u], cc) : make_uint4(0, 0, 0, 0);
         }
+    } else if (direct) {
+        // d = 512: piece u of wave wv is the whole row wv + u NT / 64 (lane =
+        // chunk), so one wave instruction moves a row straight into its LDS
+        // row (no registers, no LDS stores); rows past the split's are zeroed
+        const int wvu = __builtin_amdgcn_readfirstlane(wv);
+#pragma unroll
+        for (int u = 0; u < G::kChunks; ++u) {
+            const int r = wvu + u * (NT / kWave);
+            const int j = r0 + r;
+            if (r < rows) {
+                const uint16_t* src;
+                if (!a.idx && !a.dense) {
+                    src = a.kv + b * a.kv_stride_b + static_cast<long long>(j) * d;
+                } else if (j < cnt) {
+                    const int ix = __builtin_amdgcn_readfirstlane(my_idx[u]);
+                    const int ri = ix < 0 ? 0 : (ix >= a.n_comp ? a.n_comp - 1 : ix);
+                    src = a.comp_kv + b * a.comp_kv_stride_b + static_cast<long long>(ri) * d;
+                } else {
+                    src = a.swa + b * a.swa_stride_b +
+                          static_cast<long long>(swa_slot(a.swa_head, a.swa_len, j - cnt, a.w)) * d;
+                }
+                __builtin_amdgcn_global_load_lds(src + lane * 8,
+                                                 (__attribute__((address_space(3))) void*)(tile + r * pitch), 16, 0,
+                                                 0);
+            } else {
+                *reinterpret_cast<uint4*>(tile + r * pitch + lane * 8) = make_uint4(0, 0, 0, 0);
+            }
+        }
     } else {
 #pragma unroll
     for (int u = 0; u < G::kChunks; ++u) {
@@ -289,17 +318,31 @@ __device__ inline void attn_split(const AttnArgs& a, int n_splits, int split, in
         if (c < kHeadGroup * cpr) *reinterpret_cast<uint4*>(qs + (c / cpr) * pitch + (c % cpr) * 8) = qv[u];
     }
     const bool write_buf = (a.idx || a.dense) && a.gather_buf && hg == 0 && !a.kv_mixed;
+    if (direct) {
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);  // this wave's rows have landed in LDS
+    } else {
 #pragma unroll
-    for (int u = 0; u < G::kChunks; ++u) {
-        if (pr[u] < kR) {
-            const int r = pr[u];
-            const int cc = pc[u];
-            *reinterpret_cast<uint4*>(tile + r * pitch + cc * 8) = v[u];
-            if (write_buf && r < rows)
-                *reinterpret_cast<uint4*>(a.gather_buf + b * a.buf_stride_b + static_cast<long long>(r0 + r) * d + cc * 8) = v[u];
+        for (int u = 0; u < G::kChunks; ++u) {
+            if (pr[u] < kR) {
+                const int r = pr[u];
+                const int cc = pc[u];
+                *reinterpret_cast<uint4*>(tile + r * pitch + cc * 8) = v[u];
+                if (write_buf && r < rows)
+                    *reinterpret_cast<uint4*>(a.gather_buf + b * a.buf_stride_b + static_cast<long long>(r0 + r) * d +
+                                              cc * 8) = v[u];
+            }
         }
     }
     __syncthreads();
+    if (direct && write_buf) {  // the wave's own rows, from LDS to gather_buf
+#pragma unroll
+        for (int u = 0; u < G::kChunks; ++u) {
+            const int r = pr[u];
+            if (r < rows)
+                *reinterpret_cast<uint4*>(a.gather_buf + b * a.buf_stride_b + static_cast<long long>(r0 + r) * d +
+                                          pc[u] * 8) = *reinterpret_cast<const uint4*>(tile + r * pitch + pc[u] * 8);
+        }
+    }
 
     // 2. S = q K^T: wave wv < kNt owns rows 16*wv .. 16*wv+15
     const int li = lane & 15;
@@ -313,6 +356,20 @@ __device__ inline void attn_split(const AttnArgs& a, int n_splits, int split, in
         const uint16_t* krow = tile + my_row * pitch + 8 * lg;
         const int nks = d / 32;
         int ks = 0;
+        if (d == 512) {  // all k-steps unrolled, two accumulators: half the dependent chain
+            f32x4 s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k2 = 0; k2 < 16; k2 += 2) {
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(qrow + 32 * k2),
+                                                            *reinterpret_cast<const bf16x8*>(krow + 32 * k2), s, 0, 0,
+                                                            0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(qrow + 32 * k2 + 32),
+                                                             *reinterpret_cast<const bf16x8*>(krow + 32 * k2 + 32), s1,
+                                                             0, 0, 0);
+            }
+            s += s1;
+            ks = nks;
+        }
         for (; ks + 4 <= nks; ks += 4) {  // four k-steps' operands in flight at once
             bf16x8 qa[4], kb[4];
 #pragma unroll

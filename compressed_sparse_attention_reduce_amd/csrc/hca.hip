@@ -497,6 +497,21 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge_rows(AttnArgs a, i
     const int wv = threadIdx.x / kWave;
     const long long base = (static_cast<long long>(b) * a.h + hh) * n_splits;
     const float* ob = a.ws_o + base * d;
+    // this wave's splits for the workgroup's columns and the splits' (m, l),
+    // loaded first so that they are in flight with the new rows' loads; empty
+    // splits' slots hold stale bytes, selected away (never multiplied)
+    const int col2 = cb * kMergeCols + 2 * lane;
+    const bool has_col = col2 < d;
+    constexpr int kBatch = 16;
+    float2 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int sp = wv + kMergeWaves * u;
+        v[u] = (has_col && sp < n_splits) ? *reinterpret_cast<const float2*>(ob + static_cast<long long>(sp) * d + col2)
+                                          : make_float2(0.f, 0.f);
+    }
+    const float ms = lane < n_splits ? a.ws_ml[2 * (base + lane)] : -INFINITY;
+    const float ls = lane < n_splits ? a.ws_ml[2 * (base + lane) + 1] : 0.f;
     // the new rows' logits: q . x_i over the whole head, two sums at once
     // (d <= 2 * kMergeThreads)
     const uint16_t* qh = a.q + b * a.q_stride_b + static_cast<long long>(hh) * d;
@@ -588,22 +603,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge_rows(AttnArgs a, i
         red[0][wv] = d0;
         red[1][wv] = d1;
     }
-    // split weights (every wave derives them)
-    const float ms = lane < n_splits ? a.ws_ml[2 * (base + lane)] : -INFINITY;
-    const float ls = lane < n_splits ? a.ws_ml[2 * (base + lane) + 1] : 0.f;
     float M = wave_max(ls > 0.f ? ms : -INFINITY);
-    // this wave's splits for the workgroup's columns, in batches of loads;
-    // empty splits' slots hold stale bytes, selected away (never multiplied)
-    const int col2 = cb * kMergeCols + 2 * lane;
-    const bool has_col = col2 < d;
-    constexpr int kBatch = 16;
-    float2 v[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        const int sp = wv + kMergeWaves * u;
-        v[u] = (has_col && sp < n_splits) ? *reinterpret_cast<const float2*>(ob + static_cast<long long>(sp) * d + col2)
-                                          : make_float2(0.f, 0.f);
-    }
     __syncthreads();
     d0 = 0.f;
     d1 = 0.f;
