@@ -40,14 +40,15 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial_bf16(AttnArgs a, 
 
 constexpr int kMaxSplits = 256;
 constexpr int kMergeWaves = kAttnThreads / kWave;
-constexpr int kMergeCols = 2 * kWave;  // columns per workgroup: one pair per lane
-
-// One workgroup per (head, 128 columns, sequence).  Every wave derives the
+// One workgroup per (head, C * 64 columns, sequence): C = 2 while the
+// workgroups would not fill the chip twice over, else 4 (16-byte loads, half
+// the workgroups).  Every wave derives the
 // split weights itself (lane s holds split s of each group of 64, no
 // barrier); wave w sums splits w, w + 4, ... for the workgroup's columns and
 // the four partial sums meet in LDS.  Partials of empty splits (l = 0) are
 // never written: their loads read stale workspace bytes that are skipped
 // (never multiplied).
+template <int C>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __restrict__ ws_o,
                                                              const float* __restrict__ ws_ml,
                                                              const float* __restrict__ sink, int h,
@@ -58,14 +59,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
                                                              const int* dev_pos, const float* rope_cos,
                                                              const float* rope_sin, int rope_rows, DevState* adv,
                                                              int adv_m, int adv_w, int adv_max_comp) {
-    __shared__ float2 part[kMergeWaves][kWave];
+    __shared__ float4 part[kMergeWaves][kWave];
     if (dev_pos && rope_cos) {  // the inverse-RoPE row of the step's position (device counters)
         const int p = *dev_pos < rope_rows ? *dev_pos : rope_rows - 1;
         const long long row = static_cast<long long>(p) * (kMixRope / 2);
         inv_cos = rope_cos + row;
         inv_sin = rope_sin + row;
     }
-    const int col_blocks = (d + kMergeCols - 1) / kMergeCols;
+    static_assert(C == 2 || C == 4, "column pairs or quads per lane");
+    constexpr int kCols = C * kWave;
+    const int col_blocks = (d + kCols - 1) / kCols;
     const int hh = blockIdx.x / col_blocks;
     const int cb = blockIdx.x % col_blocks;
     const int b = blockIdx.y;
@@ -74,17 +77,20 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
     const long long base = (static_cast<long long>(b) * h + hh) * n_splits;
     const float* ml = ws_ml + 2 * base;
     const float* ob = ws_o + base * d;
-    const int col = cb * kMergeCols + 2 * lane;
-    const bool has_col = col < d;
+    const int col = cb * kCols + C * lane;
+    const bool has_col = col < d;  // d is a multiple of 32
+    auto load = [&](int sp) -> float4 {
+        if (!has_col || sp >= n_splits) return make_float4(0.f, 0.f, 0.f, 0.f);
+        const float* p = ob + static_cast<long long>(sp) * d + col;
+        if constexpr (C == 4) return *reinterpret_cast<const float4*>(p);
+        const float2 t = *reinterpret_cast<const float2*>(p);
+        return make_float4(t.x, t.y, 0.f, 0.f);
+    };
     // this wave's first splits' loads go first
     constexpr int kBatch = 16;
-    float2 v[kBatch];
+    float4 v[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        const int sp = wv + kMergeWaves * u;
-        v[u] = (has_col && sp < n_splits) ? *reinterpret_cast<const float2*>(ob + static_cast<long long>(sp) * d + col)
-                                          : make_float2(0.f, 0.f);
-    }
+    for (int u = 0; u < kBatch; ++u) v[u] = load(wv + kMergeWaves * u);
     constexpr int kGroups = kMaxSplits / kWave;
     float ms[kGroups], ls[kGroups];
     float M = sink ? sink[hh] : -INFINITY;
@@ -114,16 +120,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
             if (sp / kWave == g) c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cf[g]), sp % kWave));
         return c;
     };
-    float2 acc = make_float2(0.f, 0.f);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = 0; s0 < n_splits; s0 += kMergeWaves * kBatch) {
         if (s0 > 0) {
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int sp = s0 + wv + kMergeWaves * u;
-                v[u] = (has_col && sp < n_splits)
-                           ? *reinterpret_cast<const float2*>(ob + static_cast<long long>(sp) * d + col)
-                           : make_float2(0.f, 0.f);
-            }
+            for (int u = 0; u < kBatch; ++u) v[u] = load(s0 + wv + kMergeWaves * u);
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
@@ -133,6 +134,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
                 if (c != 0.f) {
                     acc.x += v[u].x * c;
                     acc.y += v[u].y * c;
+                    if constexpr (C == 4) {
+                        acc.z += v[u].z * c;
+                        acc.w += v[u].w * c;
+                    }
                 }
             }
         }
@@ -142,23 +147,40 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(const float* __rest
     if (wv != 0) return;
 #pragma unroll
     for (int w = 1; w < kMergeWaves; ++w) {
-        acc.x += part[w][lane].x;
-        acc.y += part[w][lane].y;
+        const float4 o = part[w][lane];
+        acc.x += o.x;
+        acc.y += o.y;
+        acc.z += o.z;
+        acc.w += o.w;
     }
     if (has_col) {
         // the RoPE dims rotated back at the token's position (a lane holds
-        // one (even, odd) pair)
+        // two (even, odd) pairs)
         if (inv_cos && col >= rope_start) {
             const int pr = (col - rope_start) / 2;
             rope_pair(acc.x, acc.y, inv_cos[pr], inv_sin[pr], true);
+            if constexpr (C == 4) rope_pair(acc.z, acc.w, inv_cos[pr + 1], inv_sin[pr + 1], true);
         }
         const long long o = b * out_stride_b + static_cast<long long>(hh) * d + col;
+        const float y[4] = {acc.x, acc.y, acc.z, acc.w};
         if (out_bf16) {
-            static_cast<uint16_t*>(out)[o] = f32_to_bf16(acc.x);
-            static_cast<uint16_t*>(out)[o + 1] = f32_to_bf16(acc.y);
+            uint16_t* p = static_cast<uint16_t*>(out) + o;
+            if (C == 4 && (reinterpret_cast<uintptr_t>(p) & 7) == 0) {  // one 8-byte store
+                *reinterpret_cast<uint2*>(p) =
+                    make_uint2(f32_to_bf16(y[0]) | (static_cast<uint32_t>(f32_to_bf16(y[1])) << 16),
+                               f32_to_bf16(y[2]) | (static_cast<uint32_t>(f32_to_bf16(y[3])) << 16));
+            } else {
+#pragma unroll
+                for (int e = 0; e < C; ++e) p[e] = f32_to_bf16(y[e]);
+            }
         } else {
-            static_cast<float*>(out)[o] = acc.x;
-            static_cast<float*>(out)[o + 1] = acc.y;
+            float* p = static_cast<float*>(out) + o;
+            if (C == 4 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {  // one 16-byte store
+                *reinterpret_cast<float4*>(p) = acc;
+            } else {
+#pragma unroll
+                for (int e = 0; e < C; ++e) p[e] = y[e];
+            }
         }
     }
     if (lse && cb == 0 && lane == 0)
@@ -264,12 +286,20 @@ hipError_t launch_attn_bf16(AttnArgs a, hipStream_t s) {
 }
 
 hipError_t launch_attn_merge(const AttnArgs& a, int ns, hipStream_t s) {
-    const int col_blocks = (a.d + kMergeCols - 1) / kMergeCols;
-    hipLaunchKernelGGL(k_attn_merge, dim3(a.h * col_blocks, a.batch), dim3(kAttnThreads), 0, s, a.ws_o, a.ws_ml,
-                       a.sink, a.h,
-                       a.d, ns, a.out, a.out_bf16 ? 1 : 0, a.lse, a.out_stride_b, a.inv_cos, a.inv_sin,
-                       a.d - kMixRope, a.dev_pos, a.kv_mixed ? a.rope_cos : nullptr, a.rope_sin, a.rope_rows,
-                       a.dev_adv, a.m, a.w, a.max_comp);
+    const bool quads = static_cast<long long>(a.h) * ((a.d + 2 * kWave - 1) / (2 * kWave)) * a.batch >
+                       2LL * device_cu_count();
+    const int cols = (quads ? 4 : 2) * kWave;
+    const dim3 grid(a.h * ((a.d + cols - 1) / cols), a.batch);
+    if (quads)
+        hipLaunchKernelGGL(k_attn_merge<4>, grid, dim3(kAttnThreads), 0, s, a.ws_o, a.ws_ml, a.sink, a.h, a.d, ns,
+                           a.out, a.out_bf16 ? 1 : 0, a.lse, a.out_stride_b, a.inv_cos, a.inv_sin, a.d - kMixRope,
+                           a.dev_pos, a.kv_mixed ? a.rope_cos : nullptr, a.rope_sin, a.rope_rows, a.dev_adv, a.m,
+                           a.w, a.max_comp);
+    else
+        hipLaunchKernelGGL(k_attn_merge<2>, grid, dim3(kAttnThreads), 0, s, a.ws_o, a.ws_ml, a.sink, a.h, a.d, ns,
+                           a.out, a.out_bf16 ? 1 : 0, a.lse, a.out_stride_b, a.inv_cos, a.inv_sin, a.d - kMixRope,
+                           a.dev_pos, a.kv_mixed ? a.rope_cos : nullptr, a.rope_sin, a.rope_rows, a.dev_adv, a.m,
+                           a.w, a.max_comp);
     return hipGetLastError();
 }
 
