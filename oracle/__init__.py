@@ -18,6 +18,7 @@ from .csa import (
     gather,
     hca_decode_step,
     index_score,
+    index_score_fp4,
     index_score_fp8,
     kv_norm,
     mixed_kv_row,
@@ -35,6 +36,7 @@ __all__ = [
     "rope_rotate",
     "mixed_kv_row",
     "index_score",
+    "index_score_fp4",
     "index_score_fp8",
     "topk",
     "rescored_topk",

@@ -29,6 +29,7 @@ import numpy as np
 
 __all__ = [
     "rescored_topk",
+    "index_score_fp4",
     "compress",
     "kv_norm",
     "index_score",
@@ -197,6 +198,40 @@ def index_score_fp8(q_codes, w, k_codes, k_scale, q_pos=None, ratio: int = 4) ->
     out = np.empty((T, kd.shape[0]), dtype=np.float64)
     for t in range(T):
         dots = (qd[t] @ kd.T) * ks[None, :]    # [H, N]: k_scale[s] * (q[t,h] . K[s])
+        out[t] = (w[t][:, None] * np.maximum(dots, 0.0)).sum(axis=0)
+    if q_pos is not None:
+        pos = np.asarray(q_pos, dtype=np.int64).reshape(T)
+        block_end = ratio * np.arange(kd.shape[0], dtype=np.int64) + (ratio - 1)
+        out[block_end[None, :] > pos[:, None]] = -np.inf
+    return out
+
+
+def index_score_fp4(q_codes, w, k_codes, k_scales, q_pos=None, ratio: int = 4) -> np.ndarray:
+    """The index score with an FP8 E4M3 query and FP4 E2M1 keys with E8M0
+    block scales (the FP4 indexer cache of page 1,
+    ``ARCHITECTURE_AND_MEMORY_AUDIT.md``, C4, paired with FP4 tensor-core
+    scoring; block layout per reading R30).
+
+    Key s decodes to ``e2m1(k_codes[s, j]) * 2^(k_scales[s, j // 32] - 127)``
+    (:func:`numfmt.mxfp4_decode_rows`); the query decodes to ``e4m3(q_codes)``
+    with any per-head scale already folded into ``w`` (reading R20).  So
+    ``I[t,s] = sum_h w[t,h] * ReLU(e4m3(q[t,h]) . K[s])``, computed exactly in
+    float64 from the decoded values.  ``q_codes`` ``[T, H, d]`` uint8 (E4M3),
+    ``w`` ``[T, H]``, ``k_codes`` ``[N, d]`` uint8 (one E2M1 code per
+    element), ``k_scales`` ``[N, d / 32]`` uint8 (E8M0).  Returns float64
+    ``[T, N]`` (causal mask as in :func:`index_score`).
+    """
+    from .numfmt import e4m3_decode, mxfp4_decode_rows
+
+    qd = e4m3_decode(np.asarray(q_codes, dtype=np.uint8))
+    kd = mxfp4_decode_rows(k_codes, k_scales)
+    if kd.ndim != 2:
+        raise ValueError(f"bad key shape {kd.shape}")
+    w = np.asarray(w, dtype=np.float64)
+    T = qd.shape[0]
+    out = np.empty((T, kd.shape[0]), dtype=np.float64)
+    for t in range(T):
+        dots = qd[t] @ kd.T                    # [H, N]
         out[t] = (w[t][:, None] * np.maximum(dots, 0.0)).sum(axis=0)
     if q_pos is not None:
         pos = np.asarray(q_pos, dtype=np.int64).reshape(T)
@@ -455,6 +490,11 @@ class LayerState:
     # scales [max_comp]; when set they replace idx_keys
     idx_codes: Optional[np.ndarray] = None
     idx_scales: Optional[np.ndarray] = None
+    # FP4 indexer keys (page 1, ARCHITECTURE_AND_MEMORY_AUDIT.md, C4; block
+    # layout per reading R30): with ``idx_fp4`` set, ``idx_codes`` holds one
+    # E2M1 code per element [max_comp, d_I] and ``idx_scales`` the E8M0
+    # block scales [max_comp, d_I / 32] uint8
+    idx_fp4: bool = False
     # Mixed main KV (page 2, eager_attention, "B1"): comp_kv and the SWA ring
     # hold the values of mixed rows (:func:`mixed_kv_row`); compressed entries
     # get RoPE from the comp tables at their block index, the output inverse
@@ -497,8 +537,10 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
     With E4M3 indexer keys (``L.idx_codes`` set) the compressed key is taken
     to float32 and quantised per row (:func:`numfmt.quantize_e4m3_rows`) into
     ``L.idx_codes`` / ``L.idx_scales``, and the scores are
-    :func:`index_score_fp8`.  A real-valued ``q_idx`` is quantised the same
-    way, one row per head, and each head's scale is folded into its weight
+    :func:`index_score_fp8`; with ``L.idx_fp4`` as well the key is quantised
+    by :func:`numfmt.quantize_mxfp4_rows` instead and the scores are
+    :func:`index_score_fp4` (the query stays E4M3).  A real-valued ``q_idx``
+    is quantised per row as E4M3, one row per head, and each head's scale is folded into its weight
     with one binary32 product (reading R20: ReLU(s x) = s ReLU(x) for s > 0);
     a uint8 ``q_idx`` is taken as codes whose scales ``w_idx`` already
     carries.
@@ -509,7 +551,7 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
     stored as :func:`mixed_kv_row` values, and the attention output gets the
     inverse rotation at ``pos`` (the pages' "Inverse RoPE" after the FMHA).
     """
-    from .numfmt import quantize_e4m3_rows
+    from .numfmt import quantize_e4m3_rows, quantize_mxfp4_rows
 
     m = L.m
     fp8 = L.idx_codes is not None
@@ -535,7 +577,8 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
         else:
             L.comp_kv[L.n_comp] = rnd(ym)
         if fp8:
-            codes, kscale = quantize_e4m3_rows(np.asarray(yi, dtype=np.float32)[None])
+            quant = quantize_mxfp4_rows if L.idx_fp4 else quantize_e4m3_rows
+            codes, kscale = quant(np.asarray(yi, dtype=np.float32)[None])
             L.idx_codes[L.n_comp] = codes[0]
             L.idx_scales[L.n_comp] = kscale[0]
         if not fp8 or L.fp8_rescore:
@@ -548,7 +591,8 @@ def decode_step(L: LayerState, *, q, q_idx, w_idx, kv_new, pos: int, top_k: int,
         if q_codes.dtype != np.uint8:
             q_codes, q_scale = quantize_e4m3_rows(q_codes.astype(np.float32))
             w_fold = (w_fold.astype(np.float32) * q_scale).astype(np.float32)
-        scores = index_score_fp8(q_codes[None], w_fold[None], L.idx_codes[:N], L.idx_scales[:N])[0]
+        score_fn = index_score_fp4 if L.idx_fp4 else index_score_fp8
+        scores = score_fn(q_codes[None], w_fold[None], L.idx_codes[:N], L.idx_scales[:N])[0]
     else:
         scores = index_score(np.asarray(q_idx)[None], np.asarray(w_idx)[None], L.idx_keys[:N])[0]
     if fp8 and L.fp8_rescore:
