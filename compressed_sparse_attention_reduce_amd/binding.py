@@ -25,6 +25,7 @@ CSA_ERR_WORKSPACE = -4
 CSA_F32 = 0
 CSA_BF16 = 1
 CSA_FP8_E4M3 = 2
+CSA_FP4_E2M1 = 3
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -82,6 +83,9 @@ _SIGS = {
     "csa_index_score": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _ll, _ll, _ll,
                              _ll, _ll, _vp]),
     "csa_quantize_fp8": (_i, [_vp, _i, _vp, _vp, _ll, _i, _vp]),
+    "csa_quantize_fp4": (_i, [_vp, _i, _vp, _vp, _ll, _i, _vp]),
+    "csa_index_score_fp4": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _ll, _ll, _ll, _ll, _ll, _ll,
+                                 _vp]),
     "csa_quantize_query_fp8": (_i, [_vp, _i, _vp, _vp, _vp, _ll, _i, _i, _vp]),
     "csa_pack_kv_mixed": (_i, [_vp, _i, _vp, _ll, _i, _i, _vp]),
     "csa_index_score_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _ll, _ll, _ll,
@@ -234,6 +238,22 @@ def csa_quantize_fp8(x, codes, scales, stream=None) -> None:
     if codes.shape != x.shape or scales.numel() != rows:
         raise ValueError("codes must match x and scales hold one value per row")
     _check(lib().csa_quantize_fp8(_ptr(x), _dt(x), _ptr(codes), _ptr(scales), rows, d, _stream(stream)))
+
+
+def csa_quantize_fp4(x, codes, scales, stream=None) -> None:
+    """x [..., d] float32 / bfloat16 (contiguous, d a multiple of 32) -> codes
+    [..., d / 2] uint8 packed E2M1 (element 2j in the low nibble of byte j),
+    scales [..., d / 32] uint8 E8M0."""
+    for t_, nm in ((x, "x"), (codes, "codes"), (scales, "scales")):
+        if not t_.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        raise TypeError("codes and scales must be uint8")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if codes.shape != (*x.shape[:-1], d // 2) or scales.shape != (*x.shape[:-1], d // 32):
+        raise ValueError("codes must be x's shape with d / 2, scales with d / 32")
+    _check(lib().csa_quantize_fp4(_ptr(x), _dt(x), _ptr(codes), _ptr(scales), rows, d, _stream(stream)))
 
 
 def csa_quantize_query_fp8(q, w, q_codes, w_folded, stream=None) -> None:
@@ -413,6 +433,26 @@ def csa_hca_decode_step_dev(layer: LayerDesc, io: StepIO, state, ring, ws, strea
                                          _stream(stream)))
 
 
+def csa_index_score_fp4(q, w, k, k_scales, scores, q_pos=None, ratio: int = 4, n: Optional[int] = None,
+                        stream=None) -> None:
+    """q [B, t, 64, 128] uint8 E4M3; w [B, t, 64] float32 (query scales folded in);
+    k [B, N, 64] uint8 packed E2M1; k_scales [B, N, 4] uint8 E8M0 (one per 32
+    elements); scores [B, t, ld] float32."""
+    for t_, nm in ((q, "q"), (w, "w"), (k, "k"), (k_scales, "k_scales"), (scores, "scores")):
+        _inner_contig(t_, nm)
+    if q.dtype != torch.uint8 or k.dtype != torch.uint8 or k_scales.dtype != torch.uint8:
+        raise TypeError("q, k and k_scales must be uint8")
+    if k_scales.shape[-1] != 4 or k_scales.stride(0) % 4 != 0:
+        raise ValueError("k_scales must be [B, N, 4] with a batch stride of whole words")
+    B, t, h_i, d_i = q.shape
+    n = k.shape[1] if n is None else n
+    _check(lib().csa_index_score_fp4(_ptr(q), _ptr(w), _ptr(k), _ptr(k_scales), _ptr(scores), B, t, h_i, d_i,
+                                     n, _ptr(q_pos), ratio, q.stride(0), w.stride(0),
+                                     k.stride(0) if k.shape[0] > 1 else 0,
+                                     k_scales.stride(0) // 4 if k_scales.shape[0] > 1 else 0, scores.stride(0),
+                                     scores.shape[2], _stream(stream)))
+
+
 def csa_layer_advance(layer: LayerDesc, pos: int) -> None:
     _check(lib().csa_layer_advance(ctypes.byref(layer), pos))
 
@@ -425,7 +465,9 @@ def make_layer_desc(*, comp_kv, idx_keys, swa, main_bias, idx_bias, sink, n_comp
     """Fill a LayerDesc from cache tensors: comp_kv [B, max_comp, d], idx_keys
     [B, max_comp, d_i] (None for an HCA layer, with idx_bias None, h_i and
     top_k 0), swa [B, W, d].  idx_keys of torch.uint8 are E4M3 codes, with
-    their row scales in idx_scales [B, max_comp] float32.  comp_kv and swa of
+    their row scales in idx_scales [B, max_comp] float32, or, with idx_scales
+    uint8 [B, max_comp, 4], packed E2M1 codes [B, max_comp, d_i / 2] with
+    their E8M0 block scales.  comp_kv and swa of
     torch.uint8 [B, rows, 592] are mixed main-KV records (d = 512), with
     rope = (cos, sin) and comp_rope = (cos, sin) float32 tables
     [rows, 32] of token positions and of block indices.  E4M3 keys with
@@ -439,7 +481,10 @@ def make_layer_desc(*, comp_kv, idx_keys, swa, main_bias, idx_bias, sink, n_comp
             raise ValueError("mixed KV: comp_kv / swa uint8 [B, rows, 592] and both RoPE tables")
         d = 512
     L = LayerDesc()
-    L.batch, L.h, L.d, L.h_i, L.d_i = B, h, d, h_i, (idx_keys.shape[2] if idx_keys is not None else 0)
+    fp4 = idx_keys is not None and idx_keys.dtype == torch.uint8 and idx_scales is not None and \
+        idx_scales.dtype == torch.uint8
+    L.batch, L.h, L.d, L.h_i = B, h, d, h_i
+    L.d_i = (idx_keys.shape[2] * (2 if fp4 else 1)) if idx_keys is not None else 0
     L.m, L.w, L.top_k, L.overlap = m, swa.shape[1], top_k, overlap
     L.dtype = CSA_BF16 if mixed else _dt(comp_kv)
     L.out_dtype = L.dtype if out_dtype is None else (CSA_BF16 if out_dtype == torch.bfloat16 else CSA_F32)
@@ -460,7 +505,13 @@ def make_layer_desc(*, comp_kv, idx_keys, swa, main_bias, idx_bias, sink, n_comp
     L.sink = _ptr(sink)
     L.scale = (1.0 / d ** 0.5) if scale is None else scale
     L.n_comp, L.swa_head, L.swa_len = n_comp, swa_head, swa_len
-    if idx_keys is not None and idx_keys.dtype == torch.uint8:
+    if fp4:
+        if idx_scales.shape != (B, max_comp, 4) or idx_scales.stride(1) != 4 or idx_scales.stride(2) != 1 or \
+                idx_scales.stride(0) % 4 != 0:
+            raise ValueError("E2M1 idx_keys need uint8 idx_scales [B, max_comp, 4] with whole-word rows")
+        L.idx_dtype = CSA_FP4_E2M1
+        L.idx_scales, L.idx_scales_stride_b = idx_scales.data_ptr(), idx_scales.stride(0) // 4
+    elif idx_keys is not None and idx_keys.dtype == torch.uint8:
         if idx_scales is None or idx_scales.dtype != torch.float32:
             raise ValueError("E4M3 idx_keys need float32 idx_scales [B, max_comp]")
         L.idx_dtype = CSA_FP8_E4M3

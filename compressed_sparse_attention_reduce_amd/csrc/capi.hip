@@ -143,6 +143,17 @@ int csa_quantize_fp8(const void* x, csa_dtype x_dtype, unsigned char* codes, flo
                     "csa_quantize_fp8");
 }
 
+int csa_quantize_fp4(const void* x, csa_dtype x_dtype, unsigned char* codes, unsigned char* scales, long long rows,
+                     int d, csa_stream stream) {
+    CHECK((x && codes && scales) || rows == 0, "csa_quantize_fp4: null pointer argument");
+    CHECK(x_dtype == CSA_F32 || x_dtype == CSA_BF16, "csa_quantize_fp4: x must be float32 or bfloat16");
+    CHECK(rows >= 0 && rows <= (1LL << 31) * 4, "csa_quantize_fp4: rows %lld", rows);
+    CHECK(d >= 32 && d <= 65536 && d % 32 == 0, "csa_quantize_fp4: d=%d (a multiple of 32 in 32..65536)", d);
+    return launched(csa::launch_quantize_fp4(x, x_dtype == CSA_BF16, codes, scales, rows, d,
+                                             static_cast<hipStream_t>(stream)),
+                    "csa_quantize_fp4");
+}
+
 static int check_fp8_score_args(const void* q, const float* w, const void* k, const float* k_scale, float* scores,
                                 int batch, int t, int h_i, int d_i, int n, int ratio, long long q_stride_b,
                                 long long w_stride_b, long long k_stride_b, long long ks_stride_b,
@@ -201,6 +212,20 @@ int csa_index_score_fp8(const unsigned char* q, const float* w, const unsigned c
     if (t >= csa::kMqMinRows)
         return launched(csa::launch_index_score_mq_fp8(a, -1, s), "csa_index_score_fp8");
     return launched(csa::launch_index_score_fp8(a, nullptr, s), "csa_index_score_fp8");
+}
+
+int csa_index_score_fp4(const unsigned char* q, const float* w, const unsigned char* k, const unsigned int* k_scales,
+                        float* scores, int batch, int t, int h_i, int d_i, int n, const int* q_pos, int ratio,
+                        long long q_stride_b, long long w_stride_b, long long k_stride_b, long long ks_stride_b,
+                        long long s_stride_b, long long ld_s, csa_stream stream) {
+    const float* ks = reinterpret_cast<const float*>(k_scales);  // four E8M0 bytes per key (a 32-bit word)
+    const int rc = check_fp8_score_args(q, w, k, ks, scores, batch, t, h_i, d_i, n, ratio, q_stride_b, w_stride_b,
+                                        k_stride_b, ks_stride_b, s_stride_b, ld_s, "csa_index_score_fp4");
+    if (rc != CSA_OK) return rc;
+    csa::Fp8ScoreArgs a{q, w, k, ks, scores, batch, t, n, q_pos, ratio,
+                        q_stride_b, w_stride_b, k_stride_b, ks_stride_b, s_stride_b, ld_s, csa::CandArgs{nullptr, 0, 0, 0}};
+    a.k_fp4 = 1;
+    return launched(csa::launch_index_score_fp8(a, nullptr, static_cast<hipStream_t>(stream)), "csa_index_score_fp4");
 }
 
 size_t csa_topk_workspace_size(int batch, int t, int n, int k) {
@@ -326,7 +351,7 @@ static size_t step_topk_bytes(const csa_layer_desc* L) {
 
 // the two-stage E4M3 selection's list of exact candidates (one per sequence)
 static size_t step_rescore_bytes(const csa_layer_desc* L) {
-    if (L->idx_dtype != CSA_FP8_E4M3 || L->idx_rescore <= 0) return 0;
+    if ((L->idx_dtype != CSA_FP8_E4M3 && L->idx_dtype != CSA_FP4_E2M1) || L->idx_rescore <= 0) return 0;
     return align256(static_cast<size_t>(L->batch) * (static_cast<size_t>(L->idx_rescore) + 1) *
                     sizeof(unsigned long long));
 }
@@ -395,15 +420,17 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
         return fail(CSA_ERR_WORKSPACE, "csa_decode_step: workspace %zu < %zu bytes", ws_bytes,
                     csa_decode_step_workspace_size(L));
     const int N = dev ? L->max_comp : L->n_comp + (completes ? 1 : 0);
-    // E4M3 indexer keys: bfloat16 everything else, the FP8 score kernel
-    const bool fp8 = L->idx_dtype == CSA_FP8_E4M3;
+    // E4M3 or E2M1 indexer keys: bfloat16 everything else, the FP8 score
+    // kernel (its E2M1 form for FP4 keys); below `fp8` covers both
+    const bool fp4 = L->idx_dtype == CSA_FP4_E2M1;
+    const bool fp8 = L->idx_dtype == CSA_FP8_E4M3 || fp4;
     if (fp8 && L->dtype != CSA_BF16)
-        return fail(CSA_ERR_UNSUPPORTED, "csa_decode_step: E4M3 indexer keys need bfloat16 caches");
+        return fail(CSA_ERR_UNSUPPORTED, "csa_decode_step: E4M3 / E2M1 indexer keys need bfloat16 caches");
     // the two-stage E4M3 selection: the k_cand best by E4M3 score, rescored from bfloat16 keys
     const bool rescore = fp8 && L->idx_rescore > 0;
     if (L->idx_rescore != 0) {
         if (!fp8)
-            return fail(CSA_ERR_UNSUPPORTED, "csa_decode_step: idx_rescore needs E4M3 indexer keys");
+            return fail(CSA_ERR_UNSUPPORTED, "csa_decode_step: idx_rescore needs E4M3 or E2M1 indexer keys");
         if (dev)
             return fail(CSA_ERR_UNSUPPORTED, "csa_decode_step_dev: the two-stage E4M3 selection needs host counters");
         CHECK(L->idx_rescore >= L->top_k && L->idx_rescore <= csa::kTopkMaxK,
@@ -496,6 +523,7 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
     pa.idx_keys = L->idx_keys;
     pa.idx_keys_stride_b = L->idx_keys_stride_b;
     pa.idx_fp8 = fp8 ? 1 : 0;
+    pa.idx_fp4 = fp4 ? 1 : 0;
     pa.idx_scales = fp8 ? L->idx_scales : nullptr;
     pa.idx_scales_stride_b = fp8 ? L->idx_scales_stride_b : 0;
     pa.idx_keys_exact = rescore ? static_cast<uint16_t*>(L->idx_keys_exact) : nullptr;
@@ -558,7 +586,7 @@ static int decode_step(const csa_layer_desc* L, const csa_step_io* io, void* ws,
                                    static_cast<const uint8_t*>(L->idx_keys), L->idx_scales, io->scores,
                                    L->batch, 1, n_scan, nullptr, L->m, 2 * io->q_idx_stride_b, io->w_stride_b,
                                    L->idx_keys_stride_b, L->idx_scales_stride_b, io->scores_stride_b, N, ca, dev,
-                                   static_cast<const uint16_t*>(io->q_idx), io->q_idx_stride_b};
+                                   static_cast<const uint16_t*>(io->q_idx), io->q_idx_stride_b, fp4 ? 1 : 0};
         e = csa::launch_index_score_fp8(fa, &pa, s);
     } else {
         e = bf ? csa::launch_index_score_bf16(sa, &pa, s) : csa::launch_index_score_f32(sa, s);

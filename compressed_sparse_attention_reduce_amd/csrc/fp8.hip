@@ -21,6 +21,23 @@
 //   and key whatever order it takes k slots in; the key's scale multiplies
 //   the head sum (s > 0: sum_h w ReLU(s x) = s sum_h w ReLU(x)); a ring of 8
 //   tiles per wave keeps as many bytes in flight as the bf16 kernel's 4.
+//
+// FP4 keys (the FP4 indexer cache the pages plan, page 1,
+// ARCHITECTURE_AND_MEMORY_AUDIT.md, C4, paired with FP4 tensor-core
+// scoring): a key row is 64 bytes of E2M1 codes (element 2 j in the low
+// nibble of byte j) and four E8M0 scales, one per 32 elements.
+//   k_quantize_fp4: one wave per 128 elements of a row, lane l taking
+//     elements 2 l and 2 l + 1 (a 32-element block is 16 lanes): the block's
+//     E8M0 exponent from its maximum by lane swaps, the elements scaled by
+//     it (exact) and rounded to E2M1.
+//   k_index_score_fp8<kCands, true>: the same scan with E4M3 query (unit
+//     scales) against E2M1 keys (format code 4) on the same instruction, the
+//     key's block scale as the per-lane B scale: for this shape an E2M1
+//     operand gives lane (li, lg) elements 32 lg .. 32 lg + 31 of its key
+//     (the 16 bytes at 16 lg, so block lg and its scale), while an E4M3
+//     operand gives it elements 16 lg .. 16 lg + 15 in bytes 0-15 and 64 +
+//     16 lg .. in bytes 16-31 (measured on gfx950), so the query operand is
+//     taken in that order.  No multiply after the head sum.
 #include "common.h"
 #include "fp8_codec.h"
 #include "kernels.h"
@@ -57,6 +74,39 @@ __global__ __launch_bounds__(kQuantThreads) void k_quantize_fp8(const void* __re
     if (lane == 0) {
         if (w_out) w_out[row] = w_in[row] * scale;
         else scales[row] = scale;
+    }
+}
+
+// FP4 E2M1 with E8M0 block scales: rows [rows][d] (d a multiple of 32) to
+// packed codes [rows][d / 2] and scales [rows][d / 32], one wave per row,
+// 128 elements per pass.
+__global__ __launch_bounds__(kQuantThreads) void k_quantize_fp4(const void* __restrict__ x, int x_bf16,
+                                                                uint8_t* __restrict__ codes,
+                                                                uint8_t* __restrict__ scales, long long rows, int d) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long row = static_cast<long long>(blockIdx.x) * kQuantRowsPerWg + threadIdx.x / kWave;
+    if (row >= rows) return;  // wave-uniform
+    auto get = [&](int j) -> float {
+        const long long o = row * d + j;
+        return x_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(x)[o]) : static_cast<const float*>(x)[o];
+    };
+    for (int base = 0; base < d; base += 2 * kWave) {
+        const int j = base + 2 * lane;
+        const bool live = j < d;  // whole 16-lane blocks (d is a multiple of 32)
+        const float x0 = live ? get(j) : 0.f;
+        const float x1 = live ? get(j + 1) : 0.f;
+        float amax = fmaxf(fabsf(x0), fabsf(x1));
+        amax = fmaxf(amax, xor_lanes_f32<1>(amax));
+        amax = fmaxf(amax, xor_lanes_f32<2>(amax));
+        amax = fmaxf(amax, xor_lanes_f32<4>(amax));
+        amax = fmaxf(amax, xor_lanes_f32<8>(amax));
+        const int xe = mx_block_exp(amax);
+        const uint32_t c0 = e2m1_encode_rne(__builtin_ldexpf(x0, -xe));
+        const uint32_t c1 = e2m1_encode_rne(__builtin_ldexpf(x1, -xe));
+        if (live) {
+            codes[row * (d / 2) + j / 2] = static_cast<uint8_t>(c0 | (c1 << 4));
+            if ((lane & 15) == 0) scales[row * (d / 32) + j / 32] = static_cast<uint8_t>(xe + 127);
+        }
     }
 }
 
@@ -142,7 +192,7 @@ __device__ inline float score_one_key_fp8(const Fp8ScoreArgs& a, int b, int tt, 
     return tot;
 }
 
-template <bool kCands>
+template <bool kCands, bool kFp4>
 __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a, int tiles_per_row, PrepArgs p,
                                                                  int prep_wgs) {
     // the query staging area doubles as the LDS of the decode step's small jobs
@@ -200,14 +250,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
     const int gw = wg * kWaves + wv;
     const int n_mine = gw < tiles_per_row ? (tiles_per_row - gw + waves_per_row - 1) / waves_per_row : 0;
 
-    const uint8_t* kbase = a.k + b * a.k_stride_b + 32 * lg;
+    // FP8: 32 code bytes of the key and its float scale; FP4: the 16 bytes of
+    // block lg and that block's E8M0 scale (as a float's bits)
+    constexpr int kKeyBytes = kFp4 ? kDi / 2 : kDi;
+    const uint8_t* kbase = a.k + b * a.k_stride_b + (kFp4 ? 16 : 32) * lg;
     const float* sbase = a.k_scale + b * a.ks_stride_b;
     auto load_tile = [&](int j, uint4* dst, float& ks) {
         const int key = j < n_mine ? min((gw + j * waves_per_row) * kTileKeys + li, n - 1) : n - 1;
-        const uint8_t* src = kbase + static_cast<long long>(key) * kDi;
+        const uint8_t* src = kbase + static_cast<long long>(key) * kKeyBytes;
         dst[0] = *reinterpret_cast<const uint4*>(src);
-        dst[1] = *reinterpret_cast<const uint4*>(src + 16);
-        ks = sbase[key];
+        if constexpr (kFp4) {
+            dst[1] = make_uint4(0, 0, 0, 0);
+            ks = __uint_as_float((__float_as_uint(sbase[key]) >> (8 * lg)) & 0xffu);
+        } else {
+            dst[1] = *reinterpret_cast<const uint4*>(src + 16);
+            ks = sbase[key];
+        }
     };
 
     // 1. query (8 KB of codes: two 16-byte pieces per thread; or 16 KB of
@@ -275,9 +333,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
     i32x8 qa[kMTiles];
 #pragma unroll
     for (int mt = 0; mt < kMTiles; ++mt) {
-        const uint8_t* qp = qs + (16 * mt + li) * kQPitch + 32 * lg;
+        // against E4M3 keys the same 32 bytes as the key's; against E2M1 keys
+        // the bytes of elements 16 lg .. and 64 + 16 lg .. (the instruction's
+        // E4M3 operand order for this shape)
+        const uint8_t* qp = qs + (16 * mt + li) * kQPitch + (kFp4 ? 16 : 32) * lg;
         const uint4 lo = *reinterpret_cast<const uint4*>(qp);
-        const uint4 hi = *reinterpret_cast<const uint4*>(qp + 16);
+        const uint4 hi = *reinterpret_cast<const uint4*>(qp + (kFp4 ? 64 : 16));
         qa[mt] = i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
                        static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
     }
@@ -310,15 +371,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
         const i32x8 kv = {static_cast<int>(kb[i][0].x), static_cast<int>(kb[i][0].y), static_cast<int>(kb[i][0].z),
                           static_cast<int>(kb[i][0].w), static_cast<int>(kb[i][1].x), static_cast<int>(kb[i][1].y),
                           static_cast<int>(kb[i][1].z), static_cast<int>(kb[i][1].w)};
-#pragma unroll
-        for (int mt = 0; mt < kMTiles; ++mt)
-            acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kv, acc[mt], 0, 0, 0, kUnitScale, 0,
-                                                                       kUnitScale);
         const float ks = ksc[i];
+#pragma unroll
+        for (int mt = 0; mt < kMTiles; ++mt) {
+            if constexpr (kFp4)  // B: E2M1 (format 4) with the key block's E8M0 scale
+                acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    qa[mt], kv, acc[mt], 0, 4, 0, kUnitScale, 0, static_cast<int>(__float_as_uint(ks)));
+            else
+                acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kv, acc[mt], 0, 0, 0, kUnitScale,
+                                                                           0, kUnitScale);
+        }
         if (refill) load_tile(j + kRing, kb[i], ksc[i]);
         // accumulator register r of M tile mt <-> head 16*mt + 4*lg + r, key li;
-        // the key's scale applied once after the head sum (ks > 0)
-        const float part = tile_head_sum(acc, wr) * ks;
+        // an E4M3 key's scale applied once after the head sum (ks > 0)
+        const float part = kFp4 ? tile_head_sum(acc, wr) : tile_head_sum(acc, wr) * ks;
         const int key = (gw + j * waves_per_row) * kTileKeys + li;
         const bool live = j < n_mine && key < n;
         float sc = part;
@@ -350,6 +416,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_index_score_fp8(Fp8ScoreArgs a,
 }
 
 }  // namespace
+
+hipError_t launch_quantize_fp4(const void* x, bool x_bf16, uint8_t* codes, uint8_t* scales, long long rows, int d,
+                               hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    if (d < 32 || d % 32 != 0) return hipErrorInvalidValue;
+    const long long wgs = (rows + kQuantRowsPerWg - 1) / kQuantRowsPerWg;
+    hipLaunchKernelGGL(k_quantize_fp4, dim3(static_cast<unsigned>(wgs)), dim3(kQuantThreads), 0, s, x,
+                       x_bf16 ? 1 : 0, codes, scales, rows, d);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize_fp8(const void* x, bool x_bf16, uint8_t* codes, float* scales, long long rows, int d,
                                hipStream_t s, const float* w_in, float* w_out) {
@@ -388,14 +464,17 @@ hipError_t launch_index_score_fp8(const Fp8ScoreArgs& a, const PrepArgs* fold, h
     }
     const int wgs = index_score_fp8_wgs(rows, a.n, prep_wgs);
     const int new_slot = fold && p.completes ? 1 : 0;
-    if (a.cands.lists && a.cands.slots == wgs + new_slot && (a.n == 0 || index_score_fp8_keys_per_wg(rows, a.n, prep_wgs) > 0))
-        hipLaunchKernelGGL(k_index_score_fp8<true>, dim3(prep_wgs + wgs, rows), dim3(kThreads), 0, s, a, tiles, p,
-                           prep_wgs);
-    else if (!a.cands.lists)
-        hipLaunchKernelGGL(k_index_score_fp8<false>, dim3(prep_wgs + wgs, rows), dim3(kThreads), 0, s, a, tiles, p,
-                           prep_wgs);
-    else
+    const bool lists = a.cands.lists != nullptr;
+    if (lists && !(a.cands.slots == wgs + new_slot && (a.n == 0 || index_score_fp8_keys_per_wg(rows, a.n, prep_wgs) > 0)))
         return hipErrorInvalidValue;  // candidate slots that do not match the grid
+    const dim3 grid(prep_wgs + wgs, rows);
+    if (a.k_fp4) {
+        if (lists) hipLaunchKernelGGL((k_index_score_fp8<true, true>), grid, dim3(kThreads), 0, s, a, tiles, p, prep_wgs);
+        else hipLaunchKernelGGL((k_index_score_fp8<false, true>), grid, dim3(kThreads), 0, s, a, tiles, p, prep_wgs);
+    } else {
+        if (lists) hipLaunchKernelGGL((k_index_score_fp8<true, false>), grid, dim3(kThreads), 0, s, a, tiles, p, prep_wgs);
+        else hipLaunchKernelGGL((k_index_score_fp8<false, false>), grid, dim3(kThreads), 0, s, a, tiles, p, prep_wgs);
+    }
     return hipGetLastError();
 }
 

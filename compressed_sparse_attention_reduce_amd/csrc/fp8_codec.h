@@ -1,6 +1,9 @@
 // OCP FP8 E4M3 codes (bias 7, subnormals, NaN at S.1111.111, +-448 largest):
 // the encoder of the per-row quantiser and an exact decoder, shared by the
-// FP8 scan and the decode step's key compressor.
+// FP8 scan and the decode step's key compressor.  Also FP4 E2M1 elements
+// with E8M0 block scales (the OCP microscaling element and scale formats:
+// magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; a scale is 2^(s - 127)), which
+// gfx950's scaled matrix instructions read.
 #pragma once
 
 #include "common.h"
@@ -81,6 +84,41 @@ __device__ inline float e4m3_decode(uint32_t c) {
     const uint32_t m = c & 7u;
     const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : static_cast<float>(m) * 0.001953125f;
     return (c & 0x80u) ? -mag : mag;
+}
+
+// E8M0 exponent X of a 32-element block whose largest magnitude is amax
+// (finite, >= 0): the smallest X with amax <= 6 * 2^X, clamped to [-127,
+// 127]; 0 for an all-zero block.  With amax = 1.f * 2^E (normal binary32),
+// 6 * 2^X = 1.5 * 2^(X + 2), so X = E - 2 when 1.f <= 1.5, else E - 1; a
+// subnormal amax (below 2^-126 <= 6 * 2^-127) takes the clamp.
+__device__ inline int mx_block_exp(float amax) {
+    if (!(amax > 0.f)) return 0;
+    const uint32_t u = __float_as_uint(amax);
+    const int e = static_cast<int>((u >> 23) & 0xffu);
+    if (e == 0) return -127;
+    const int x = e - 127 - 2 + ((u & 0x7fffffu) > 0x400000u ? 1 : 0);
+    return x < -127 ? -127 : x;
+}
+
+// E2M1 code of y (|y| <= 6 after the block scale): round to nearest, ties
+// to the even code, saturating at 6; a zero result is code 0 whatever y's
+// sign.  The thresholds are the midpoints between neighbouring magnitudes,
+// strict where the lower neighbour's code is even.
+__device__ inline uint32_t e2m1_encode_rne(float y) {
+    const float a = fabsf(y);
+    const uint32_t c = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
+                       static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
+                       static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
+                       static_cast<uint32_t>(a > 5.0f);
+    return (y < 0.f && c != 0u) ? (c | 8u) : c;
+}
+
+// The exact value of an E2M1 code (low 4 bits of c).
+__device__ inline float e2m1_decode(uint32_t c) {
+    const uint32_t e = (c >> 1) & 3u;
+    const uint32_t m = c & 1u;
+    const float mag = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * static_cast<float>(m);
+    return (c & 8u) ? -mag : mag;
 }
 
 }  // namespace

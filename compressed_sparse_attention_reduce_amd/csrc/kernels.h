@@ -118,6 +118,10 @@ hipError_t launch_index_score_f32(const ScoreArgs& a, hipStream_t s);
 // w_in[r] * scale_r replaces scales[r] (the scale folded into the weight)
 hipError_t launch_quantize_fp8(const void* x, bool x_bf16, uint8_t* codes, float* scales, long long rows, int d,
                                hipStream_t s, const float* w_in = nullptr, float* w_out = nullptr);
+// FP4 E2M1 rows with one E8M0 scale per 32 elements (d a multiple of 32):
+// packed codes [rows][d / 2], scales [rows][d / 32]
+hipError_t launch_quantize_fp4(const void* x, bool x_bf16, uint8_t* codes, uint8_t* scales, long long rows, int d,
+                               hipStream_t s);
 struct Fp8ScoreArgs {
     const uint8_t* q;      // [B][t][64][128] E4M3
     const float* w;        // [B][t][64], query scales folded in (unless q_raw)
@@ -137,6 +141,11 @@ struct Fp8ScoreArgs {
     // row as csa_quantize_fp8 does and multiplies w by the row's scale
     const uint16_t* q_raw;
     long long q_raw_stride_b;
+    // non-zero: FP4 keys — k holds packed E2M1 rows (element 2j in the low
+    // nibble of byte j of the 64-byte row, stride k_stride_b bytes) and
+    // k_scale 32-bit words, byte j the E8M0 scale of elements 32 j .. 32 j +
+    // 31 (stride ks_stride_b words)
+    int k_fp4;
 };
 // Scan workgroups per row and keys per scan workgroup of the FP8 scan.
 int index_score_fp8_wgs(int rows, int n, int extra);
@@ -313,6 +322,8 @@ struct PrepArgs {
     int batch, es, d, d_i, m, overlap, completes, n_comp;
     int main_wgs;  // > 1: the main block is compressed in that many channel slices (roles 1 .. main_wgs)
     int idx_fp8;   // the indexer keys are E4M3 codes with per-row scales (role 2 quantises the new key)
+    int idx_fp4;   // the indexer keys are packed E2M1 codes, idx_scales 32-bit words of four E8M0
+                   // block scales (role 2 quantises the new key; idx_fp8 is set too)
     float* idx_scales;
     long long idx_scales_stride_b;
     uint16_t* idx_keys_exact;  // E4M3 keys: also the bfloat16 key here (nullable)

@@ -78,6 +78,40 @@ __device__ inline void step_prep_role_at(const PrepArgs& a, int role, int b, flo
         compress_block(z, c, a.idx_bias, a.idx_norm, key, false, a.m, a.d_i, a.overlap != 0, a.block, ybuf, red,
                        nullptr, prev_idx);
         __syncthreads();
+        if (a.idx_fp4) {
+            // FP4 keys (d_i = 128): quantised like csa_quantize_fp4 by the
+            // first wave, lane l taking elements 2 l, 2 l + 1 (a 32-element
+            // block is 16 lanes); `key` is left holding the decoded values
+            // (code times block scale) and key[a.d_i] = 1
+            if (a.idx_keys_exact) {  // the key in bfloat16 too (the bfloat16 step's rounding)
+                uint16_t* ex = a.idx_keys_exact + b * a.idx_keys_exact_stride_b + static_cast<long long>(a.n_comp) * a.d_i;
+                for (int j = threadIdx.x; j < a.d_i; j += blockDim.x) ex[j] = f32_to_bf16(key[j]);
+            }
+            __syncthreads();  // every thread has read key before the first wave rewrites it
+            if (threadIdx.x < kWave) {
+                const int l = threadIdx.x;
+                const float x0 = key[2 * l], x1 = key[2 * l + 1];
+                float amax = fmaxf(fabsf(x0), fabsf(x1));
+                amax = fmaxf(amax, xor_lanes_f32<1>(amax));
+                amax = fmaxf(amax, xor_lanes_f32<2>(amax));
+                amax = fmaxf(amax, xor_lanes_f32<4>(amax));
+                amax = fmaxf(amax, xor_lanes_f32<8>(amax));
+                const int xe = mx_block_exp(amax);
+                const uint32_t c0 = e2m1_encode_rne(__builtin_ldexpf(x0, -xe));
+                const uint32_t c1 = e2m1_encode_rne(__builtin_ldexpf(x1, -xe));
+                uint8_t* codes = static_cast<uint8_t*>(a.idx_keys) + b * a.idx_keys_stride_b +
+                                 static_cast<long long>(a.n_comp) * (a.d_i / 2);
+                codes[l] = static_cast<uint8_t>(c0 | (c1 << 4));
+                if ((l & 15) == 0)
+                    reinterpret_cast<uint8_t*>(a.idx_scales + b * a.idx_scales_stride_b + a.n_comp)[l >> 4] =
+                        static_cast<uint8_t>(xe + 127);
+                key[2 * l] = __builtin_ldexpf(e2m1_decode(c0), xe);
+                key[2 * l + 1] = __builtin_ldexpf(e2m1_decode(c1), xe);
+                if (l == 0) key[a.d_i] = 1.0f;
+            }
+            __syncthreads();
+            return;
+        }
         float amax = 0.f;
         for (int j = threadIdx.x; j < a.d_i; j += blockDim.x) amax = fmaxf(amax, fabsf(key[j]));
         amax = wave_max(amax);

@@ -61,9 +61,10 @@ typedef enum {
     CSA_ERR_WORKSPACE = -4
 } csa_status;
 
-/* CSA_FP8_E4M3 (OCP E4M3 codes, one byte per element) is accepted only where
- * an entry point says so. */
-typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 } csa_dtype;
+/* CSA_FP8_E4M3 (OCP E4M3 codes, one byte per element) and CSA_FP4_E2M1
+ * (E2M1 codes, two per byte, with E8M0 block scales: section 2d) are
+ * accepted only where an entry point says so. */
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_FP4_E2M1 = 3 } csa_dtype;
 
 typedef void *csa_stream; /* hipStream_t */
 
@@ -171,6 +172,53 @@ int csa_quantize_query_fp8(const void *q, csa_dtype q_dtype, const float *w, uns
 int csa_index_score_fp8(const unsigned char *q, const float *w, const unsigned char *k,
                         const float *k_scale, float *scores, int batch, int t, int h_i, int d_i,
                         int n, const int *q_pos, int ratio, long long q_stride_b,
+                        long long w_stride_b, long long k_stride_b, long long ks_stride_b,
+                        long long s_stride_b, long long ld_s, csa_stream stream);
+
+/* ------------------------------------------------------------------------
+ * 2d. FP4 E2M1 indexer keys with E8M0 block scales.
+ *
+ * Source: page 1, ARCHITECTURE_AND_MEMORY_AUDIT.md, C4 "Optional: Quantize
+ * indexer KV to FP4" (an FP4 indexer cache, paired with an FP4 tensor-core
+ * scoring kernel, never one without the other).  The pages fix no block
+ * layout; here the keys use the formats gfx950's scaled matrix instructions
+ * read: E2M1 elements (sign, 2 exponent bits with bias 1, 1 mantissa bit:
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) and one E8M0 scale (2^(s - 127))
+ * per 32 consecutive elements; the query stays E4M3 (section 2b).
+ *
+ * csa_quantize_fp4: x [rows][d] float32 or bfloat16 (x_dtype), contiguous ->
+ *   codes [rows][d / 2] bytes (element 2j in the low nibble of byte j,
+ *   element 2j + 1 in the high nibble) and scales [rows][d / 32] E8M0 bytes.
+ *   A block's scale is 2^X with X the smallest integer such that the
+ *   block's largest magnitude is at most 6 * 2^X (so nothing saturates),
+ *   clamped to [-127, 127], X = 0 for an all-zero block; each element is
+ *   multiplied by 2^-X (exact) and rounded to the nearest E2M1 magnitude,
+ *   ties to the even code, its sign kept unless it rounds to zero (code 0).
+ *   NaN inputs are out of contract.  Limits: d a multiple of 32, 32 <= d
+ *   <= 65536.
+ *
+ * csa_index_score_fp4:
+ *   I[t,s] = sum_h w[t,h] * ReLU(e4m3(q[t,h]) . K[s]),
+ *   K[s][j] = e2m1(code[s][j]) * 2^(scale[s][j / 32] - 127).
+ *   q:        [B][t][h_i][d_i] uint8 E4M3 codes, stride_b = q_stride_b bytes
+ *             (csa_quantize_query_fp8 makes them and the folded weights).
+ *   w:        [B][t][h_i] float32, stride_b = w_stride_b, query scales folded in.
+ *   k:        [B][n][d_i / 2] packed codes, stride_b = k_stride_b bytes.
+ *   k_scales: [B][n] 32-bit words, byte j of word s the scale of elements
+ *             32 j .. 32 j + 31 of key s (d_i / 32 = 4 bytes), stride_b =
+ *             ks_stride_b words.
+ *   scores:   [B][t][ld_s] float32, stride_b = s_stride_b; columns 0..n-1.
+ *   q_pos, ratio: the causal form, as for csa_index_score.
+ * Supported: h_i = 64, d_i = 128; q, k, w 16-byte aligned and strides that
+ * keep them so.  Products of E4M3 and E2M1 values are exact; the matrix
+ * core sums in float32 (so the scores agree with the exact sum to float32
+ * rounding of partial sums).
+ * ------------------------------------------------------------------------ */
+int csa_quantize_fp4(const void *x, csa_dtype x_dtype, unsigned char *codes, unsigned char *scales,
+                     long long rows, int d, csa_stream stream);
+int csa_index_score_fp4(const unsigned char *q, const float *w, const unsigned char *k,
+                        const unsigned int *k_scales, float *scores, int batch, int t, int h_i,
+                        int d_i, int n, const int *q_pos, int ratio, long long q_stride_b,
                         long long w_stride_b, long long k_stride_b, long long ks_stride_b,
                         long long s_stride_b, long long ld_s, csa_stream stream);
 
@@ -288,6 +336,14 @@ int csa_sparse_attn(const void *q, const void *kv, const int *n_valid, const flo
  * selection must keep 99% of the exact top-512), which per-row E4M3 alone
  * misses on crowded scores (93.6% on the 1M-context workload).  Host
  * counters only (csa_decode_step_dev: CSA_ERR_UNSUPPORTED).
+ * With E2M1 indexer keys (idx_dtype = CSA_FP4_E2M1, section 2d; same
+ * conditions as E4M3 keys) step b stores the compressed key as
+ * csa_quantize_fp4 would (packed codes into idx_keys[n_comp], its four
+ * E8M0 scales into the 32-bit word idx_scales[n_comp]) and step c scores as
+ * csa_index_score_fp4 does, with the query quantised as for E4M3 keys;
+ * idx_rescore works as for E4M3 keys (E2M1 keys alone keep about 82% of the
+ * exact top-512 on the 1M-context workload; the 2048 best by E2M1 score,
+ * rescored, keep all of it).
  * It does NOT update the host integers: afterwards the caller sets
  * swa_head = (swa_head + 1) % w, swa_len = min(swa_len + 1, w) and, if a block
  * completed, n_comp += 1 (csa_layer_advance does exactly this).
@@ -323,6 +379,9 @@ typedef struct csa_layer_desc {
      * value: keys stored as `dtype`. */
     csa_dtype idx_dtype;
     float *idx_scales; long long idx_scales_stride_b;
+    /* (idx_dtype = CSA_FP4_E2M1, section 2d: idx_keys [B][max_comp][d_i / 2]
+     * packed E2M1 codes (stride in bytes); idx_scales [B][max_comp] 32-bit
+     * words of four E8M0 block scales (stride in words); d_i = 128) */
     /* Mixed main KV (section 6c; appended: zero keeps comp_kv / swa rows of
      * `dtype`): kv_dtype = CSA_FP8_E4M3 makes every comp_kv and swa row a
      * 592-byte record (csa_pack_kv_mixed), comp_kv_stride_b and swa_stride_b
@@ -334,8 +393,8 @@ typedef struct csa_layer_desc {
     int rope_dim;
     const float *rope_cos, *rope_sin; int rope_rows;
     const float *comp_rope_cos, *comp_rope_sin; int comp_rope_rows;
-    /* Recall-restored E4M3 keys (section 2c; appended: zero = off): with
-     * idx_dtype = CSA_FP8_E4M3 and idx_rescore = k_cand (top_k <= k_cand <=
+    /* Recall-restored E4M3 or E2M1 keys (section 2c; appended: zero = off): with
+     * idx_dtype = CSA_FP8_E4M3 or CSA_FP4_E2M1 and idx_rescore = k_cand (top_k <= k_cand <=
      * 2048) the layer also keeps its keys as bfloat16 in idx_keys_exact
      * [B][max_comp][d_i] (stride idx_keys_exact_stride_b elements, 16-byte
      * aligned rows). */

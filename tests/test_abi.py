@@ -129,6 +129,30 @@ def test_fp8_entry_points_reject_bad_args(csa):
     assert lib.csa_index_score_fp8(*a) == B.CSA_ERR_INVALID_ARG
 
 
+def test_fp4_entry_points_reject_bad_args(csa):
+    lib = csa.lib()
+    B = csa.binding
+    q = [FAKE, B.CSA_F32, FAKE, FAKE, 10, 128, None]
+    a = list(q); a[1] = B.CSA_FP4_E2M1          # input must be float32 or bf16
+    assert lib.csa_quantize_fp4(*a) == B.CSA_ERR_INVALID_ARG
+    for d in (0, 16, 48, 100):                  # whole 32-element blocks only
+        a = list(q); a[5] = d
+        assert lib.csa_quantize_fp4(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(q); a[3] = None                    # no scales
+    assert lib.csa_quantize_fp4(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(q); a[0] = None; a[2] = None; a[3] = None; a[4] = 0   # nothing to do
+    assert lib.csa_quantize_fp4(*a) == B.CSA_OK
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 128, 1000, None, 4, 0, 0, 0, 0, 0, 1000, None]
+    a = list(base); a[8] = 64
+    assert lib.csa_index_score_fp4(*a) == B.CSA_ERR_UNSUPPORTED
+    a = list(base); a[3] = None                 # no block scales
+    assert lib.csa_index_score_fp4(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(base); a[17] = 999                 # ld_s < n
+    assert lib.csa_index_score_fp4(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(base); a[2] = FAKE + 8             # misaligned keys
+    assert lib.csa_index_score_fp4(*a) == B.CSA_ERR_INVALID_ARG
+
+
 def test_calib_symbols_are_exported_by_their_own_library(csa):
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "csa_calib.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(csa_\w+)\s*\(", text)))
@@ -347,6 +371,31 @@ def test_decode_step_fp8_keys_validation(csa):
     assert call(L) == B.CSA_ERR_INVALID_ARG
     # a zero-filled descriptor keeps keys of the cache dtype
     assert _desc(csa).idx_dtype == csa.CSA_F32 and _desc(csa).idx_scales is None
+
+
+def test_decode_step_fp4_keys_validation(csa):
+    """E2M1 indexer keys: the E4M3 step's rules (bfloat16 caches, a 64 x 128
+    indexer, block scales given)."""
+    B = csa.binding
+    lib = csa.lib()
+    L = _desc(csa, idx_dtype=csa.CSA_FP4_E2M1)
+    io = _io(csa, pos=3999)
+
+    def call(layer):
+        need = csa.csa_decode_step_workspace_size(layer)
+        return lib.csa_decode_step(ctypes.byref(layer), ctypes.byref(io), FAKE, need, None)
+
+    assert call(L) == B.CSA_ERR_INVALID_ARG      # idx_scales missing
+    L.idx_scales = FAKE
+    L.d_i = 64
+    assert call(L) == B.CSA_ERR_UNSUPPORTED
+    L.d_i = 128
+    L.dtype = csa.CSA_F32
+    assert call(L) == B.CSA_ERR_UNSUPPORTED
+    assert "bfloat16" in csa.csa_last_error()
+    L.dtype = csa.CSA_BF16
+    L.idx_rescore = L.top_k - 1                  # a first stage smaller than top_k
+    assert call(L) == B.CSA_ERR_INVALID_ARG
 
 
 def test_mixed_kv_validation(csa):
