@@ -96,3 +96,17 @@ def assert_topk_gap_rule(gpu_idx: np.ndarray, gpu_count: int, oracle_scores: np.
     diff = set(sel.tolist()) ^ ref
     for i in diff:
         assert abs(s[i] - sk) <= tol, f"index {i} score {s[i]} vs s_k {sk}"
+
+
+def assert_fp4_key_close(codes_packed, scales, y):
+    """A key the GPU quantised from its own float32 compressor output, next
+    to the oracle's float64 key y: each block's exponent within one of the
+    oracle's rule applied to y, each element within the largest E2M1 half
+    gap (2^X) of y plus float32 slack."""
+    c = numfmt.unpack_e2m1(np.asarray(codes_packed, dtype=np.uint8)[None])
+    s = np.asarray(scales, dtype=np.uint8)[None]
+    dec = numfmt.mxfp4_decode_rows(c, s)[0]
+    _, rs = numfmt.quantize_mxfp4_rows(np.asarray(y, dtype=np.float32)[None])
+    assert np.abs(s.astype(np.int64) - rs.astype(np.int64)).max() <= 1
+    X = np.repeat(np.ldexp(1.0, s[0].astype(np.int64) - 127), 32)
+    assert (np.abs(dec - y) <= X + 1e-5 * np.abs(y).max()).all()

@@ -15,8 +15,8 @@ import torch
 import oracle
 import synth
 from oracle import numfmt
-from tests.gpu_util import (DEV, assert_bf16_close, assert_topk_gap_rule, dev_bf16, dev_f32, host_bits, host_f64,
-                            rel_err)
+from tests.gpu_util import (DEV, assert_bf16_close, assert_fp4_key_close, assert_topk_gap_rule, dev_bf16, dev_f32,
+                            host_bits, host_f64, rel_err)
 from tests.test_gpu_mixed_kv import _assert_entry_close, decode_records, oracle_records, record_of
 from tests.test_gpu_parity import _assert_e4m3_key_close
 
@@ -42,7 +42,8 @@ def _tables_np(rows, offset, base):
     return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
 
 
-def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64, fp8=False):
+def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64, fp8=False, fp4=False):
+    fp8 = fp8 or fp4  # fp4: E2M1 keys, the E4M3 step's paths otherwise
     g = _g(seed)
     D, Di, H = 512, 128, 64
     m = 4
@@ -61,12 +62,21 @@ def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64, 
     rope = tuple(dev_f32(t) for t in rope_np) if mixed else None
     comp_rope = tuple(dev_f32(t) for t in comp_rope_np) if mixed else None
 
-    if fp8:
+    if fp4:
+        c4, s4 = numfmt.quantize_mxfp4_rows(f(keys_bits).reshape(-1, Di).astype(np.float32))
+        kc0 = numfmt.pack_e2m1(c4).reshape(B, max_comp, Di // 2)
+        ks0 = s4.reshape(B, max_comp, Di // 32)
+        oc0 = c4.reshape(B, max_comp, Di)              # the oracle's codes, one per element
+    elif fp8:
         kc0, ks0 = numfmt.quantize_e4m3_rows(f(keys_bits).reshape(-1, Di).astype(np.float32))
         kc0, ks0 = kc0.reshape(B, max_comp, Di), ks0.reshape(B, max_comp)
+        oc0 = kc0
 
     def caches():
-        keys = (torch.from_numpy(kc0.copy()).to(DEV), dev_f32(ks0)) if fp8 else dev_bf16(keys_bits)
+        if fp4:
+            keys = (torch.from_numpy(kc0.copy()).to(DEV), torch.from_numpy(ks0.copy()).to(DEV))
+        else:
+            keys = (torch.from_numpy(kc0.copy()).to(DEV), dev_f32(ks0)) if fp8 else dev_bf16(keys_bits)
         if mixed:
             comp = torch.empty(B, max_comp, REC, dtype=torch.uint8, device=DEV)
             swa = torch.empty(B, W, REC, dtype=torch.uint8, device=DEV)
@@ -106,7 +116,7 @@ def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64, 
             swa=oracle.SwaRing(swa_val.copy(), pos0 % W, min(pos0, W)), main_bias=mb_np.astype(np.float64),
             idx_bias=ib_np.astype(np.float64), sink=sink_np.astype(np.float64), overlap=bool(overlap),
             round_cache=numfmt.bf16_round_f64,
-            idx_codes=kc0[b].copy() if fp8 else None, idx_scales=ks0[b].copy() if fp8 else None,
+            idx_codes=oc0[b].copy() if fp8 else None, idx_scales=ks0[b].copy() if fp8 else None, idx_fp4=fp4,
             kv_mixed=mixed, rope_dim=ROPE,
             rope_cos=rope_np[0].astype(np.float64) if mixed else None,
             rope_sin=rope_np[1].astype(np.float64) if mixed else None,
@@ -198,16 +208,21 @@ def _run(csa, *, mixed, overlap, B, n0, pos0, max_comp, steps, seed, W=8, K=64, 
                     _assert_entry_close(cd[b, nb].cpu().numpy(), ost.comp_kv[nb])
                 else:
                     assert_bf16_close(host_bits(cd[b, nb]), ym)
-                if fp8:
+                if fp4:
+                    assert_fp4_key_close(kd[0][b, nb].cpu().numpy(), kd[1][b, nb].cpu().numpy(), yi)
+                elif fp8:
                     _assert_e4m3_key_close(kd[0][b, nb].cpu().numpy(), float(kd[1][b, nb]), yi)
                 else:
                     assert_bf16_close(host_bits(kd[b, nb]), yi)
             ost.comp_kv[:N] = decode_records(cd[b, :N].cpu().numpy()) if mixed else host_f64(cd[b, :N])
             if fp8:
-                ost.idx_codes[:N], ost.idx_scales[:N] = kd[0][b, :N].cpu().numpy(), kd[1][b, :N].cpu().numpy()
+                gcodes = kd[0][b, :N].cpu().numpy()
+                ost.idx_codes[:N] = numfmt.unpack_e2m1(gcodes) if fp4 else gcodes
+                ost.idx_scales[:N] = kd[1][b, :N].cpu().numpy()
                 qc, qs = numfmt.quantize_e4m3_rows(f(x["q_idx"][b]).astype(np.float32))
                 w8 = (x["w_idx"][b] * qs).astype(np.float32)
-                ref_s = oracle.index_score_fp8(qc[None], w8[None], ost.idx_codes[:N], ost.idx_scales[:N])[0]
+                score_fn = oracle.index_score_fp4 if fp4 else oracle.index_score_fp8
+                ref_s = score_fn(qc[None], w8[None], ost.idx_codes[:N], ost.idx_scales[:N])[0]
             else:
                 ost.idx_keys[:N] = host_f64(kd[b, :N])
                 ref_s = oracle.index_score(f(x["q_idx"][b])[None], x["w_idx"][b][None], ost.idx_keys[:N])[0]
@@ -265,6 +280,12 @@ def test_dev_step_overlap_and_mixed_kv(csa):
 def test_dev_step_fp8_keys(csa):
     """E4M3 indexer keys (the new key quantised in the step), batch 2."""
     _run(csa, mixed=False, overlap=0, B=2, n0=150, pos0=600, max_comp=200, steps=9, seed=8104, fp8=True)
+
+
+def test_dev_step_fp4_keys(csa):
+    """E2M1 indexer keys with E8M0 block scales (the new key quantised in the
+    step), batch 2."""
+    _run(csa, mixed=False, overlap=0, B=2, n0=150, pos0=600, max_comp=200, steps=9, seed=8105, fp4=True)
 
 
 def test_dev_step_batched_separate_topk(csa):

@@ -15,8 +15,8 @@ import torch
 import oracle
 import synth
 from oracle import numfmt
-from tests.gpu_util import (DEV, assert_bf16_close, assert_topk_gap_rule, dev_bf16, dev_f32, host_bits, host_f64,
-                            rel_err)
+from tests.gpu_util import (DEV, assert_bf16_close, assert_fp4_key_close, assert_topk_gap_rule, dev_bf16, dev_f32,
+                            host_bits, host_f64, rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -197,20 +197,6 @@ def _fp8_query(qi, wi):
     return qc.reshape(qi.shape), (wi * qs.reshape(wi.shape)).astype(np.float32)
 
 
-def _assert_fp4_key_close(codes_packed, scales, y):
-    """A key the GPU quantised from its own float32 compressor output, next
-    to the oracle's float64 key y: each block's exponent within one of the
-    oracle's rule applied to y, each element within the largest E2M1 half
-    gap (2^X) of y plus float32 slack."""
-    c = numfmt.unpack_e2m1(np.asarray(codes_packed, dtype=np.uint8)[None])
-    s = np.asarray(scales, dtype=np.uint8)[None]
-    dec = numfmt.mxfp4_decode_rows(c, s)[0]
-    _, rs = numfmt.quantize_mxfp4_rows(np.asarray(y, dtype=np.float32)[None])
-    assert np.abs(s.astype(np.int64) - rs.astype(np.int64)).max() <= 1
-    X = np.repeat(np.ldexp(1.0, s[0].astype(np.int64) - 127), 32)
-    assert (np.abs(dec - y) <= X + 1e-5 * np.abs(y).max()).all()
-
-
 def _fp4_rescored_layer(csa, x, B, max_comp, K, kc):
     f = numfmt.bf16_bits_to_f64
     c0, s0 = numfmt.quantize_mxfp4_rows(f(x["idx_keys"]).reshape(-1, 128).astype(np.float32))
@@ -298,7 +284,7 @@ def test_decode_steps_in_sequence_fp4_rescored(csa, B):
             np.testing.assert_array_equal(numfmt.unpack_e2m1(codes[b, :n0].cpu().numpy()), ost.idx_codes[:n0])
             if completes:
                 yi = oracle.compress(zi[b], ci[b], x["idx_bias"], 4)[0]
-                _assert_fp4_key_close(codes[b, n0].cpu().numpy(), scales[b, n0].cpu().numpy(), yi)
+                assert_fp4_key_close(codes[b, n0].cpu().numpy(), scales[b, n0].cpu().numpy(), yi)
                 assert_bf16_close(host_bits(exact_keys[b, n0]), yi)
                 assert_bf16_close(host_bits(comp[b, n0]), oracle.compress(zm[b], cm[b], x["main_bias"], 4)[0])
             ost.comp_kv[:N] = host_f64(comp[b, :N])
