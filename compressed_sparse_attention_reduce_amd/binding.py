@@ -115,6 +115,9 @@ _SIGS = {
     "csa_index_topk": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _ll, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_topk_fp8": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _ll, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_topk_fp8_rescored_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "csa_index_topk_fp4": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _ll, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "csa_index_topk_fp4_rescored": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _ll, _i, _i, _i, _vp, _vp, _vp, _sz,
+                                         _vp]),
     "csa_index_topk_fp8_rescored": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _ll, _i, _i, _i, _vp, _vp, _vp, _sz,
                                          _vp]),
     "csa_prefill_attn": (_i, [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _ll, _vp, _f, _vp, _i, _vp, _i, _i, _i,
@@ -609,6 +612,51 @@ def csa_index_topk_fp8_rescored(q, w, k8, k_scale, k16, idx, count, ws, k_cand: 
     t, h_i, d_i = q.shape
     n = k8.shape[0] if n is None else n
     _check(lib().csa_index_topk_fp8_rescored(_ptr(q), _ptr(w), _ptr(k8), _ptr(k_scale), _ptr(k16), t, h_i, d_i, n,
+                                             pos0, ratio, idx.shape[1], k_cand, _ptr(idx), _ptr(count), _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def _fp4_keys(k, k_scales, nm):
+    if not k.is_contiguous() or not k_scales.is_contiguous():
+        raise ValueError(f"{nm} and k_scales must be contiguous")
+    if k.dtype != torch.uint8 or k_scales.dtype != torch.uint8 or k.shape[-1] != 64 or \
+            k_scales.shape != (*k.shape[:-1], 4):
+        raise TypeError(f"{nm} must be uint8 [N, 64] packed E2M1, k_scales uint8 [N, 4] E8M0")
+
+
+def csa_index_topk_fp4(q, w, k, k_scales, idx, count, ws, pos0: int = -1, ratio: int = 4,
+                       n: Optional[int] = None, stream=None) -> None:
+    """q [t, 64, 128] uint8 E4M3; w [t, 64] float32 (query scales folded in);
+    k [N, 64] uint8 packed E2M1 and k_scales [N, 4] uint8 E8M0 (first n
+    rows); idx, count, pos0 as for csa_index_topk."""
+    for t_, nm in ((q, "q"), (w, "w"), (idx, "idx")):
+        if not t_.is_contiguous():
+            raise ValueError(f"{nm}: must be contiguous")
+    _fp4_keys(k, k_scales, "k")
+    if q.dtype != torch.uint8:
+        raise TypeError("q must hold uint8 E4M3 codes")
+    t, h_i, d_i = q.shape
+    n = k.shape[0] if n is None else n
+    _check(lib().csa_index_topk_fp4(_ptr(q), _ptr(w), _ptr(k), _ptr(k_scales), t, h_i, d_i, n, pos0, ratio,
+                                    idx.shape[1], _ptr(idx), _ptr(count), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)))
+
+
+def csa_index_topk_fp4_rescored(q, w, k4, k_scales, k16, idx, count, ws, k_cand: int, pos0: int = -1,
+                                ratio: int = 4, n: Optional[int] = None, stream=None) -> None:
+    """q [t, 64, 128] bf16; w [t, 64] float32 (plain weights); k4 [N, 64]
+    uint8 packed E2M1, k_scales [N, 4] uint8 E8M0 and k16 [N, 128] bf16 (the
+    same keys); idx [t, top_k] int32; count [t] int32 or None; ws of
+    csa_index_topk_fp8_rescored_workspace_size bytes."""
+    for t_, nm in ((q, "q"), (w, "w"), (k16, "k16"), (idx, "idx")):
+        if not t_.is_contiguous():
+            raise ValueError(f"{nm}: must be contiguous")
+    _fp4_keys(k4, k_scales, "k4")
+    if q.dtype != torch.bfloat16 or k16.dtype != torch.bfloat16:
+        raise TypeError("q and k16 must be bfloat16")
+    t, h_i, d_i = q.shape
+    n = k4.shape[0] if n is None else n
+    _check(lib().csa_index_topk_fp4_rescored(_ptr(q), _ptr(w), _ptr(k4), _ptr(k_scales), _ptr(k16), t, h_i, d_i, n,
                                              pos0, ratio, idx.shape[1], k_cand, _ptr(idx), _ptr(count), _ptr(ws),
                                              ws.numel() * ws.element_size(), _stream(stream)))
 

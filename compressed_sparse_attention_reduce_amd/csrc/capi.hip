@@ -225,7 +225,10 @@ int csa_index_score_fp4(const unsigned char* q, const float* w, const unsigned c
     csa::Fp8ScoreArgs a{q, w, k, ks, scores, batch, t, n, q_pos, ratio,
                         q_stride_b, w_stride_b, k_stride_b, ks_stride_b, s_stride_b, ld_s, csa::CandArgs{nullptr, 0, 0, 0}};
     a.k_fp4 = 1;
-    return launched(csa::launch_index_score_fp8(a, nullptr, static_cast<hipStream_t>(stream)), "csa_index_score_fp4");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (t >= csa::kMqMinRows)
+        return launched(csa::launch_index_score_mq_fp8(a, -1, s), "csa_index_score_fp4");
+    return launched(csa::launch_index_score_fp8(a, nullptr, s), "csa_index_score_fp4");
 }
 
 size_t csa_topk_workspace_size(int batch, int t, int n, int k) {
@@ -1001,20 +1004,21 @@ int csa_index_topk(const void* q, const float* w, const void* k, int t, int h_i,
     return launched(csa::launch_index_topk(a, static_cast<hipStream_t>(stream)), "csa_index_topk");
 }
 
-int csa_index_topk_fp8(const unsigned char* q, const float* w, const unsigned char* k, const float* k_scale, int t,
-                       int h_i, int d_i, int n, long long pos0, int ratio, int top_k, int* idx, int* count,
-                       void* ws, size_t ws_bytes, csa_stream stream) {
-    CHECK(q && w && idx && ws && ((k && k_scale) || n == 0), "csa_index_topk_fp8: null pointer argument");
-    CHECK(t >= 1 && n >= 0, "csa_index_topk_fp8: t %d n %d", t, n);
-    CHECK(ratio >= 1, "csa_index_topk_fp8: ratio %d", ratio);
-    CHECK(top_k >= 1 && top_k <= csa::kTopkMaxK, "csa_index_topk_fp8: top_k=%d out of 1..%d", top_k,
-          csa::kTopkMaxK);
+// csa_index_topk_fp8 and csa_index_topk_fp4: E4M3 query codes against E4M3
+// keys with row scales, or E2M1 keys with E8M0 block scales (fp4)
+static int index_topk_lowp(const unsigned char* q, const float* w, const unsigned char* k, const float* k_scale,
+                           bool fp4, int t, int h_i, int d_i, int n, long long pos0, int ratio, int top_k, int* idx,
+                           int* count, void* ws, size_t ws_bytes, csa_stream stream, const char* who) {
+    CHECK(q && w && idx && ws && ((k && k_scale) || n == 0), "%s: null pointer argument", who);
+    CHECK(t >= 1 && n >= 0, "%s: t %d n %d", who, t, n);
+    CHECK(ratio >= 1, "%s: ratio %d", who, ratio);
+    CHECK(top_k >= 1 && top_k <= csa::kTopkMaxK, "%s: top_k=%d out of 1..%d", who, top_k, csa::kTopkMaxK);
     if (h_i != 64 || d_i != 128)
-        return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk_fp8: needs h_i=64, d_i=128 (got %d, %d)", h_i, d_i);
+        return fail(CSA_ERR_UNSUPPORTED, "%s: needs h_i=64, d_i=128 (got %d, %d)", who, h_i, d_i);
     CHECK(aligned16(q) && aligned16(w) && aligned16(ws) && (n == 0 || aligned16(k)),
-          "csa_index_topk_fp8: q, w, k and ws must be 16-byte aligned");
+          "%s: q, w, k and ws must be 16-byte aligned", who);
     if (ws_bytes < csa_index_topk_workspace_size(t, n, top_k))
-        return fail(CSA_ERR_WORKSPACE, "csa_index_topk_fp8: workspace %zu < %zu bytes", ws_bytes,
+        return fail(CSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes,
                     csa_index_topk_workspace_size(t, n, top_k));
     csa::IndexTopkArgs a{};
     a.w = w;
@@ -1028,10 +1032,25 @@ int csa_index_topk_fp8(const unsigned char* q, const float* w, const unsigned ch
     a.ws = ws;
     a.q8 = q;
     a.k8 = k;
-    // a non-null scale pointer selects the E4M3 scan (no key is read when n = 0)
+    // a non-null scale pointer selects the low-precision scan (no key is read when n = 0)
     static const float kNoKeys = 1.f;
     a.k_scale = n > 0 ? k_scale : &kNoKeys;
-    return launched(csa::launch_index_topk(a, static_cast<hipStream_t>(stream)), "csa_index_topk_fp8");
+    a.k_fp4 = fp4 ? 1 : 0;
+    return launched(csa::launch_index_topk(a, static_cast<hipStream_t>(stream)), who);
+}
+
+int csa_index_topk_fp8(const unsigned char* q, const float* w, const unsigned char* k, const float* k_scale, int t,
+                       int h_i, int d_i, int n, long long pos0, int ratio, int top_k, int* idx, int* count,
+                       void* ws, size_t ws_bytes, csa_stream stream) {
+    return index_topk_lowp(q, w, k, k_scale, false, t, h_i, d_i, n, pos0, ratio, top_k, idx, count, ws, ws_bytes,
+                           stream, "csa_index_topk_fp8");
+}
+
+int csa_index_topk_fp4(const unsigned char* q, const float* w, const unsigned char* k, const unsigned int* k_scales,
+                       int t, int h_i, int d_i, int n, long long pos0, int ratio, int top_k, int* idx, int* count,
+                       void* ws, size_t ws_bytes, csa_stream stream) {
+    return index_topk_lowp(q, w, k, reinterpret_cast<const float*>(k_scales), true, t, h_i, d_i, n, pos0, ratio,
+                           top_k, idx, count, ws, ws_bytes, stream, "csa_index_topk_fp4");
 }
 
 // workspace of the two-stage E4M3 selection of a chunk: query codes, folded
@@ -1052,23 +1071,23 @@ size_t csa_index_topk_fp8_rescored_workspace_size(int t, int n, int top_k, int k
     return rescored_parts(t, n, k_cand, off);
 }
 
-int csa_index_topk_fp8_rescored(const void* q, const float* w, const unsigned char* k8, const float* k_scale,
-                                const void* k16, int t, int h_i, int d_i, int n, long long pos0, int ratio, int top_k,
-                                int k_cand, int* idx, int* count, void* ws, size_t ws_bytes, csa_stream stream) {
-    CHECK(q && w && idx && ws && ((k8 && k_scale && k16) || n == 0), "csa_index_topk_fp8_rescored: null pointer argument");
-    CHECK(t >= 1 && n >= 0, "csa_index_topk_fp8_rescored: t %d n %d", t, n);
-    CHECK(ratio >= 1, "csa_index_topk_fp8_rescored: ratio %d", ratio);
+// csa_index_topk_fp8_rescored and csa_index_topk_fp4_rescored
+static int index_topk_lowp_rescored(const void* q, const float* w, const unsigned char* k8, const float* k_scale,
+                                    bool fp4, const void* k16, int t, int h_i, int d_i, int n, long long pos0,
+                                    int ratio, int top_k, int k_cand, int* idx, int* count, void* ws,
+                                    size_t ws_bytes, csa_stream stream, const char* who) {
+    CHECK(q && w && idx && ws && ((k8 && k_scale && k16) || n == 0), "%s: null pointer argument", who);
+    CHECK(t >= 1 && n >= 0, "%s: t %d n %d", who, t, n);
+    CHECK(ratio >= 1, "%s: ratio %d", who, ratio);
     CHECK(top_k >= 1 && k_cand >= top_k && k_cand <= csa::kTopkMaxK,
-          "csa_index_topk_fp8_rescored: top_k %d / k_cand %d (need 1 <= top_k <= k_cand <= %d)", top_k, k_cand,
-          csa::kTopkMaxK);
+          "%s: top_k %d / k_cand %d (need 1 <= top_k <= k_cand <= %d)", who, top_k, k_cand, csa::kTopkMaxK);
     if (h_i != 64 || d_i != 128)
-        return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk_fp8_rescored: needs h_i=64, d_i=128 (got %d, %d)", h_i, d_i);
+        return fail(CSA_ERR_UNSUPPORTED, "%s: needs h_i=64, d_i=128 (got %d, %d)", who, h_i, d_i);
     CHECK(aligned16(q) && aligned16(w) && aligned16(ws) && (n == 0 || (aligned16(k8) && aligned16(k16))),
-          "csa_index_topk_fp8_rescored: q, w, keys and ws must be 16-byte aligned");
+          "%s: q, w, keys and ws must be 16-byte aligned", who);
     size_t off[5];
     const size_t need = rescored_parts(t, n, k_cand, off);
-    if (ws_bytes < need)
-        return fail(CSA_ERR_WORKSPACE, "csa_index_topk_fp8_rescored: workspace %zu < %zu bytes", ws_bytes, need);
+    if (ws_bytes < need) return fail(CSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     char* base = static_cast<char*>(ws);
     auto* qc = reinterpret_cast<uint8_t*>(base + off[0]);
@@ -1077,8 +1096,8 @@ int csa_index_topk_fp8_rescored(const void* q, const float* w, const unsigned ch
     auto* ccount = reinterpret_cast<int*>(base + off[3]);
     // 1. the query's codes and folded weights
     hipError_t e = csa::launch_quantize_fp8(q, true, qc, nullptr, static_cast<long long>(t) * 64, 128, s, w, wf);
-    if (e != hipSuccess) return launched(e, "csa_index_topk_fp8_rescored/quantise");
-    // 2. the k_cand best by E4M3 score per query
+    if (e != hipSuccess) return launched(e, who);
+    // 2. the k_cand best by low-precision score per query
     csa::IndexTopkArgs a{};
     a.w = wf;
     a.t = t;
@@ -1093,12 +1112,28 @@ int csa_index_topk_fp8_rescored(const void* q, const float* w, const unsigned ch
     a.k8 = k8;
     static const float kNoKeys = 1.f;
     a.k_scale = n > 0 ? k_scale : &kNoKeys;
+    a.k_fp4 = fp4 ? 1 : 0;
     e = csa::launch_index_topk(a, s);
-    if (e != hipSuccess) return launched(e, "csa_index_topk_fp8_rescored/first stage");
+    if (e != hipSuccess) return launched(e, who);
     // 3. their exact scores and the top_k of them
     const csa::RescoreRowsArgs r{static_cast<const uint16_t*>(q), w, static_cast<const uint16_t*>(k16), n, cand, ccount,
                                  k_cand, t, top_k, idx, count};
-    return launched(csa::launch_rescore_rows(r, s), "csa_index_topk_fp8_rescored");
+    return launched(csa::launch_rescore_rows(r, s), who);
+}
+
+int csa_index_topk_fp8_rescored(const void* q, const float* w, const unsigned char* k8, const float* k_scale,
+                                const void* k16, int t, int h_i, int d_i, int n, long long pos0, int ratio, int top_k,
+                                int k_cand, int* idx, int* count, void* ws, size_t ws_bytes, csa_stream stream) {
+    return index_topk_lowp_rescored(q, w, k8, k_scale, false, k16, t, h_i, d_i, n, pos0, ratio, top_k, k_cand, idx,
+                                    count, ws, ws_bytes, stream, "csa_index_topk_fp8_rescored");
+}
+
+int csa_index_topk_fp4_rescored(const void* q, const float* w, const unsigned char* k4, const unsigned int* k_scales,
+                                const void* k16, int t, int h_i, int d_i, int n, long long pos0, int ratio, int top_k,
+                                int k_cand, int* idx, int* count, void* ws, size_t ws_bytes, csa_stream stream) {
+    return index_topk_lowp_rescored(q, w, k4, reinterpret_cast<const float*>(k_scales), true, k16, t, h_i, d_i, n,
+                                    pos0, ratio, top_k, k_cand, idx, count, ws, ws_bytes, stream,
+                                    "csa_index_topk_fp4_rescored");
 }
 
 int csa_prefill_attn(const void* q, const void* comp_kv, int n_comp, const int* idx, const int* count, int k,

@@ -29,6 +29,9 @@ struct IndexTopkArgs {
     const uint8_t* q8;
     const uint8_t* k8;
     const float* k_scale;
+    // with k_fp4: k8 [n][64] packed E2M1 codes, k_scale four E8M0 bytes per
+    // key (one 32-bit word each)
+    int k_fp4;
 };
 size_t index_topk_workspace_bytes(int t, int n, int top_k);
 hipError_t launch_index_topk(const IndexTopkArgs& a, hipStream_t s);

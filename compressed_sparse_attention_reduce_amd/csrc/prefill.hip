@@ -575,6 +575,7 @@ hipError_t launch_index_topk(const IndexTopkArgs& a, hipStream_t s) {
             fa.w = a.w + static_cast<long long>(r0) * kIdxHeads;
             fa.k = a.k8;
             fa.k_scale = a.k_scale;
+            fa.k_fp4 = a.k_fp4;
             fa.scores = sc;
             fa.batch = 1;
             fa.t = rows;

@@ -634,6 +634,16 @@ int csa_hca_decode_step_dev(const csa_layer_desc *layer, const csa_step_io *io, 
  *   ws: csa_index_topk_fp8_rescored_workspace_size(t, n, top_k, k_cand)
  *   bytes, 16-byte aligned.
  *
+ * csa_index_topk_fp4 / csa_index_topk_fp4_rescored: the same two calls over
+ *   FP4 keys (section 2d; page 1, ARCHITECTURE_AND_MEMORY_AUDIT.md, C4):
+ *   k / k4 [n][64] packed E2M1 codes and k_scales [n] 32-bit words of four
+ *   E8M0 block scales, as csa_quantize_fp4 writes them (its [n][4] bytes);
+ *   scores as csa_index_score_fp4 computes them.  Query, outputs, limits
+ *   and workspace sizes as their E4M3 forms (the rescored one sizes its
+ *   workspace with csa_index_topk_fp8_rescored_workspace_size).  FP4 keys
+ *   alone keep about 81% of the exact top-512 at 250,000 keys; the
+ *   two-stage form restores it with k_cand = 4 top_k.
+ *
  * csa_prefill_attn: per query row r, one softmax (scale, then the sink in the
  *   denominator only) over comp_kv[idx[r][0 .. count[r])] followed by its
  *   window rows.  q: [t][h][d] bf16; comp_kv: [n_comp][d] bf16; idx/count as
@@ -663,6 +673,14 @@ int csa_index_topk_fp8_rescored(const void *q, const float *w, const unsigned ch
                                 const void *k16, int t, int h_i, int d_i, int n, long long pos0, int ratio,
                                 int top_k, int k_cand, int *idx, int *count, void *ws, size_t ws_bytes,
                                 csa_stream stream);
+int csa_index_topk_fp4(const unsigned char *q, const float *w, const unsigned char *k,
+                       const unsigned int *k_scales, int t, int h_i, int d_i, int n, long long pos0,
+                       int ratio, int top_k, int *idx, int *count, void *ws, size_t ws_bytes,
+                       csa_stream stream);
+int csa_index_topk_fp4_rescored(const void *q, const float *w, const unsigned char *k4,
+                                const unsigned int *k_scales, const void *k16, int t, int h_i, int d_i,
+                                int n, long long pos0, int ratio, int top_k, int k_cand, int *idx,
+                                int *count, void *ws, size_t ws_bytes, csa_stream stream);
 int csa_prefill_attn(const void *q, const void *comp_kv, int n_comp, const int *idx,
                      const int *count, int k, const void *win_kv, int window, long long pos0,
                      const float *sink, float scale, void *out, csa_dtype out_dtype, float *lse,

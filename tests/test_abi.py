@@ -151,6 +151,21 @@ def test_fp4_entry_points_reject_bad_args(csa):
     assert lib.csa_index_score_fp4(*a) == B.CSA_ERR_INVALID_ARG
     a = list(base); a[2] = FAKE + 8             # misaligned keys
     assert lib.csa_index_score_fp4(*a) == B.CSA_ERR_INVALID_ARG
+    # the chunk selections over FP4 keys: the E4M3 forms' rules
+    tk = [FAKE, FAKE, FAKE, FAKE, 16, 64, 128, 1000, 0, 4, 64, FAKE, FAKE, FAKE, 1 << 30, None]
+    a = list(tk); a[3] = None                   # no block scales
+    assert lib.csa_index_topk_fp4(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(tk); a[5] = 32
+    assert lib.csa_index_topk_fp4(*a) == B.CSA_ERR_UNSUPPORTED
+    a = list(tk); a[14] = 16                    # short workspace
+    assert lib.csa_index_topk_fp4(*a) == B.CSA_ERR_WORKSPACE
+    rs = [FAKE, FAKE, FAKE, FAKE, FAKE, 16, 64, 128, 1000, 0, 4, 64, 256, FAKE, FAKE, FAKE, 1 << 30, None]
+    a = list(rs); a[4] = None                   # no bfloat16 keys
+    assert lib.csa_index_topk_fp4_rescored(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(rs); a[12] = 32                    # k_cand < top_k
+    assert lib.csa_index_topk_fp4_rescored(*a) == B.CSA_ERR_INVALID_ARG
+    a = list(rs); a[16] = 16
+    assert lib.csa_index_topk_fp4_rescored(*a) == B.CSA_ERR_WORKSPACE
 
 
 def test_calib_symbols_are_exported_by_their_own_library(csa):
