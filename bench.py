@@ -549,6 +549,46 @@ def time_prefill(csa, reps: int):
     stream.synchronize()
     score8_us = e0.elapsed_time(e1) * 1e3 / launches
     tflops8 = flop / (score8_us * 1e-6) / 1e12
+
+    # the FP4-key variant (E2M1, an E8M0 scale per 32 elements): the same
+    # E4M3 query codes, keys quantised once outside the timed region; the
+    # two-stage form takes the 2048 best by FP4 score
+    k4 = torch.empty(N, 64, dtype=torch.uint8, device="cuda")
+    s4 = torch.empty(N, 4, dtype=torch.uint8, device="cuda")
+    csa.csa_quantize_fp4(x["idx_keys"], k4, s4)
+    del kc, ks
+    torch.cuda.synchronize()
+
+    def topk4():
+        csa.csa_quantize_query_fp8(x["q_idx"], x["w_idx"], qc, w8)
+        csa.csa_index_topk_fp4(qc, w8, k4, s4, idx, cnt, ws, pos0=x["pos0"])
+
+    topk4_ms = timed(topk4, reps)
+    kcand4 = 4 * k
+    ws_r = torch.empty(csa.csa_index_topk_fp8_rescored_workspace_size(T, N, k, kcand4), dtype=torch.uint8,
+                       device="cuda")
+
+    def topk4r():
+        csa.csa_index_topk_fp4_rescored(x["q_idx"], x["w_idx"], k4, s4, x["idx_keys"], idx, cnt, ws_r, kcand4,
+                                        pos0=x["pos0"])
+
+    topk4r_ms = timed(topk4r, reps)
+    del ws_r
+    g4 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g4, stream=stream):
+            for r0 in range(0, T, rows):
+                csa.csa_index_score_fp4(qc[None, r0:r0 + rows], w8[None, r0:r0 + rows], k4[None], s4[None], sc,
+                                        q_pos=pos[:, r0:r0 + rows], stream=stream)
+        g4.replay()
+        stream.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            g4.replay()
+        e1.record(stream)
+    stream.synchronize()
+    score4_us = e0.elapsed_time(e1) * 1e3 / launches
+    tflops4 = flop / (score4_us * 1e-6) / 1e12
     return {
         "workload": "prefill chunk: 2048 queries at positions 260096..262143 against 65536 compressed "
                     "blocks (causal), indexer 64x128 bf16, top_k 512, main attention 64 heads x 512 bf16 "
@@ -586,6 +626,26 @@ def time_prefill(csa, reps: int):
                 "peak": FP8_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s",
                 "frac": round(tflops8 / FP8_MFMA_PEAK_TFLOPS, 4),
+            },
+        },
+        "fp4_keys": {
+            "index_topk_ms": round(topk4_ms, 4),
+            "chunk_ms": round(topk4_ms + attn_ms, 4),
+            "queries_per_s": round(T / ((topk4_ms + attn_ms) * 1e-3), 1),
+            "rescored_index_topk_ms": round(topk4r_ms, 4),
+            "rescored_chunk_ms": round(topk4r_ms + attn_ms, 4),
+            "rescored_note": "query quantised, the best 2048 by E2M1-key score per query, then the top-512 of "
+                             "those by exact score from the bf16 keys",
+            "score_kernel": {
+                "kernel": "k_index_score_mq_fp8<true> (E4M3 query x E2M1 keys)",
+                "bound": "mfma",
+                "rows_per_launch": rows,
+                "avg_launch_us": round(score4_us, 2),
+                "achieved": round(tflops4, 1),
+                "peak": FP8_MFMA_PEAK_TFLOPS,
+                "peak_note": "one operand E4M3: the instruction runs at the fp8 rate, so the fp8 peak",
+                "unit": "TFLOP/s",
+                "frac": round(tflops4 / FP8_MFMA_PEAK_TFLOPS, 4),
             },
         },
     }
