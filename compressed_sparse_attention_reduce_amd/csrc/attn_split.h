@@ -81,11 +81,15 @@ __device__ inline int swa_slot(int head, int len, int i, int w) {
 // them into the B operands of P MFMAs (dword j: rows 2j and 2j + 1 of one
 // column), so P MFMAs share 8 reads instead of taking 8 two-byte reads each.
 // Accumulator t holds column c_base + P li + t; each head's P values leave as
-// one store of P floats to ob[head * ob_head_stride + column].  Columns at or
-// past d (a last, partial group) read column 0 and store nothing.
-template <int P>
+// one store of P values of type Out to ob[head * ob_head_stride + column]:
+// float32, or bfloat16 rounded to nearest even (Out = uint16_t, the HCA
+// step's partials: half the bytes written here and read by its merge, a
+// relative rounding of 2^-9 per partial on an output that is itself
+// bfloat16).  Columns at or past d (a last, partial group) read column 0 and
+// store nothing.
+template <int P, typename Out = float>
 __device__ inline void pv_group(const uint16_t* tile, int pitch, const uint16_t* pl, int ppitch, int ksteps,
-                                int c_base, int d, float* ob, long long ob_head_stride) {
+                                int c_base, int d, Out* ob, long long ob_head_stride) {
     static_assert(P == 2 || P == 4, "two or four columns per lane");
     using Piece = typename std::conditional<P == 2, uint32_t, uint2>::type;
     const int lane = threadIdx.x & (kWave - 1);
@@ -126,11 +130,24 @@ __device__ inline void pv_group(const uint16_t* tile, int pitch, const uint16_t*
     if (!cv) return;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        float* dst = ob + static_cast<long long>(4 * lg + r) * ob_head_stride + cp;
-        if constexpr (P == 2)
-            *reinterpret_cast<float2*>(dst) = make_float2(o[0][r], o[1][r]);
-        else
-            *reinterpret_cast<float4*>(dst) = make_float4(o[0][r], o[1][r], o[2][r], o[3][r]);
+        Out* dst = ob + static_cast<long long>(4 * lg + r) * ob_head_stride + cp;
+        if constexpr (std::is_same<Out, float>::value) {
+            if constexpr (P == 2)
+                *reinterpret_cast<float2*>(dst) = make_float2(o[0][r], o[1][r]);
+            else
+                *reinterpret_cast<float4*>(dst) = make_float4(o[0][r], o[1][r], o[2][r], o[3][r]);
+        } else {
+            static_assert(std::is_same<Out, uint16_t>::value, "float32 or bfloat16 partials");
+            const uint32_t w0 =
+                static_cast<uint32_t>(f32_to_bf16(o[0][r])) | (static_cast<uint32_t>(f32_to_bf16(o[1][r])) << 16);
+            if constexpr (P == 2) {
+                *reinterpret_cast<uint32_t*>(dst) = w0;
+            } else {
+                const uint32_t w1 =
+                    static_cast<uint32_t>(f32_to_bf16(o[2][r])) | (static_cast<uint32_t>(f32_to_bf16(o[3][r])) << 16);
+                *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+            }
+        }
     }
 }
 

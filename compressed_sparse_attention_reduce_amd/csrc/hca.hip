@@ -10,7 +10,9 @@
 // at once (one round of loads, eight waves: one 16-row tile of S = q K^T
 // each, then four 16-column tiles of O = P V each, both on
 // v_mfma_f32_16x16x32_bf16), so the partials are a quarter of the row bytes
-// of 32-row splits, and k_attn_merge_rows merges them.  The four head groups
+// of 32-row splits, and k_attn_merge_rows merges them.  The partial outputs
+// are stored in bfloat16 (the (max, sum) pairs in float32), halving what the
+// attention writes and the merge reads again.  The four head groups
 // of a split run on one XCD (consecutive workgroup ids go to consecutive
 // XCDs), so the rows come from HBM once and from that XCD's L2 for the other
 // three groups.  One workgroup per split and head group and nothing else
@@ -427,11 +429,11 @@ __global__ __launch_bounds__(kDenseThreads) void k_attn_dense_bf16(AttnArgs a, i
     }
     // 4. O = P V: M = 16 heads, K = the split's rows in 32-row steps, N = d in
     //    groups of 64 columns, one per wave
-    float* ob = a.ws_o + (static_cast<long long>(b) * a.h + hg * kHeadGroup) * n_splits * d +
-                static_cast<long long>(split) * d;
+    uint16_t* ob = reinterpret_cast<uint16_t*>(a.ws_o) + (static_cast<long long>(b) * a.h + hg * kHeadGroup) * n_splits * d +
+                   static_cast<long long>(split) * d;
     const int ksteps = (rows + 31) / 32;  // rows past the valid ones hold zeros and p = 0
     for (int g = wv; 64 * g < d; g += kDenseWaves)
-        pv_group<4>(tile, pitch, pl, kDensePPitch, ksteps, 64 * g, d, ob, static_cast<long long>(n_splits) * d);
+        pv_group<4, uint16_t>(tile, pitch, pl, kDensePPitch, ksteps, 64 * g, d, ob, static_cast<long long>(n_splits) * d);
     if (fold) {
         __syncthreads();  // P V's reads of the tile are over: it becomes the merge's scratch
         fold_finish(reinterpret_cast<float*>(smem));
@@ -496,7 +498,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge_rows(AttnArgs a, i
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const long long base = (static_cast<long long>(b) * a.h + hh) * n_splits;
-    const float* ob = a.ws_o + base * d;
+    const uint16_t* ob = reinterpret_cast<const uint16_t*>(a.ws_o) + base * d;
     // this wave's splits for the workgroup's columns and the splits' (m, l),
     // loaded first so that they are in flight with the new rows' loads; empty
     // splits' slots hold stale bytes, selected away (never multiplied)
@@ -507,8 +509,9 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge_rows(AttnArgs a, i
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
         const int sp = wv + kMergeWaves * u;
-        v[u] = (has_col && sp < n_splits) ? *reinterpret_cast<const float2*>(ob + static_cast<long long>(sp) * d + col2)
-                                          : make_float2(0.f, 0.f);
+        const uint32_t w = (has_col && sp < n_splits) ? *reinterpret_cast<const uint32_t*>(ob + static_cast<long long>(sp) * d + col2)
+                                                      : 0u;
+        v[u] = make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
     }
     const float ms = lane < n_splits ? a.ws_ml[2 * (base + lane)] : -INFINITY;
     const float ls = lane < n_splits ? a.ws_ml[2 * (base + lane) + 1] : 0.f;
