@@ -1273,7 +1273,7 @@ def main() -> int:
             "frac": round(fp4_gbs / HBM_PEAK_GBS, 4),
             "decode_steps_per_s": round(1e3 / fp4_step_ms, 2),
             "decode_ms_per_step": round(fp4_step_ms, 5),
-            "decode_note": "FP4 keys alone reach top-512 recall 0.81 against the float64 indexer",
+            "decode_note": "FP4 keys alone reach top-512 recall about 0.8 against the float64 indexer",
             "rescored": {
                 "workload": "the E2M1 step with the two-stage selection: the top-512 by exact score (bf16 keys "
                             "kept as well) of the best 2048 by E2M1 score; top-512 recall 1.0",

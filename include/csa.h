@@ -341,7 +341,7 @@ int csa_sparse_attn(const void *q, const void *kv, const int *n_valid, const flo
  * csa_quantize_fp4 would (packed codes into idx_keys[n_comp], its four
  * E8M0 scales into the 32-bit word idx_scales[n_comp]) and step c scores as
  * csa_index_score_fp4 does, with the query quantised as for E4M3 keys;
- * idx_rescore works as for E4M3 keys (E2M1 keys alone keep about 82% of the
+ * idx_rescore works as for E4M3 keys (E2M1 keys alone keep about 80% of the
  * exact top-512 on the 1M-context workload; the 2048 best by E2M1 score,
  * rescored, keep all of it).
  * It does NOT update the host integers: afterwards the caller sets
@@ -641,7 +641,7 @@ int csa_hca_decode_step_dev(const csa_layer_desc *layer, const csa_step_io *io, 
  *   scores as csa_index_score_fp4 computes them.  Query, outputs, limits
  *   and workspace sizes as their E4M3 forms (the rescored one sizes its
  *   workspace with csa_index_topk_fp8_rescored_workspace_size).  FP4 keys
- *   alone keep about 81% of the exact top-512 at 250,000 keys; the
+ *   alone keep about 80% of the exact top-512 at 250,000 keys; the
  *   two-stage form restores it with k_cand = 4 top_k.
  *
  * csa_prefill_attn: per query row r, one softmax (scale, then the sink in the
