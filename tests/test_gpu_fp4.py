@@ -398,3 +398,81 @@ def test_decode_step_ctx1m_fp4_rescored_full_size_recall(csa):
     sel = host_f64(x["comp_kv"][0, torch.from_numpy(gi).to(DEV).long()])
     np.testing.assert_array_equal(host_f64(outs["gather_buf"][0, :gc]), sel)
     assert int(outs["n_valid"][0]) == gc + W
+
+
+def test_decode_steps_fp4_from_first_token(csa):
+    """From token 0 over FP4 keys (an empty compressed cache, the first block
+    completing at token 3, the window filling and wrapping), batch 2, plain
+    selection: every step's new key, scores, selection, gather and attention
+    against the oracle, the GPU's new entries adopted as in the other
+    sequences."""
+    B, H, D, Di, W, K, m, max_comp, steps = 2, 64, 512, 128, 8, 4, 4, 16, 11
+    g = _g(5500)
+    f = numfmt.bf16_bits_to_f64
+    comp = torch.zeros(B, max_comp, D, dtype=torch.bfloat16, device=DEV)
+    codes = torch.zeros(B, max_comp, Di // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.zeros(B, max_comp, Di // 32, dtype=torch.uint8, device=DEV)
+    swa = torch.zeros(B, W, D, dtype=torch.bfloat16, device=DEV)
+    mb = g.standard_normal((m, D), dtype=np.float32) * np.float32(0.1)
+    ib = g.standard_normal((m, Di), dtype=np.float32) * np.float32(0.1)
+    sink = g.standard_normal(H, dtype=np.float32)
+    L = csa.make_layer_desc(comp_kv=comp, idx_keys=codes, idx_scales=scales, swa=swa, main_bias=dev_f32(mb),
+                            idx_bias=dev_f32(ib), sink=dev_f32(sink), n_comp=0, swa_head=0, swa_len=0, h=H, h_i=64,
+                            top_k=K)
+    assert L.idx_dtype == csa.CSA_FP4_E2M1
+    osts = [oracle.LayerState(comp_kv=np.zeros((max_comp, D)), idx_keys=np.zeros((max_comp, Di)), n_comp=0,
+                              swa=oracle.SwaRing(np.zeros((W, D))), main_bias=mb.astype(np.float64),
+                              idx_bias=ib.astype(np.float64), sink=sink.astype(np.float64),
+                              round_cache=numfmt.bf16_round_f64, idx_codes=np.zeros((max_comp, Di), np.uint8),
+                              idx_scales=np.zeros((max_comp, Di // 32), np.uint8), idx_fp4=True) for _ in range(B)]
+    ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+    for pos in range(steps):
+        q = synth.to_bf16_bits(g.standard_normal((B, H, D), dtype=np.float32))
+        qi = synth.to_bf16_bits(g.standard_normal((B, 64, Di), dtype=np.float32) / np.float32(np.sqrt(Di)))
+        wi = g.standard_normal((B, 64), dtype=np.float32)
+        kvn = synth.to_bf16_bits(g.standard_normal((B, D), dtype=np.float32))
+        zm, cm = g.standard_normal((2, B, m, D), dtype=np.float32)
+        zi, ci = g.standard_normal((2, B, m, Di), dtype=np.float32)
+        outs = dict(scores=torch.full((B, max_comp), 9.0, device=DEV),
+                    topk_idx=torch.full((B, K), -7, dtype=torch.int32, device=DEV),
+                    topk_count=torch.full((B,), -7, dtype=torch.int32, device=DEV),
+                    gather_buf=torch.zeros(B, K + W, D, dtype=torch.bfloat16, device=DEV),
+                    n_valid=torch.full((B,), -7, dtype=torch.int32, device=DEV),
+                    out=torch.empty(B, H, D, dtype=torch.bfloat16, device=DEV), lse=torch.empty(B, H, device=DEV))
+        io = csa.make_step_io(pos=pos, q=dev_bf16(q), q_idx=dev_bf16(qi), w_idx=dev_f32(wi), kv_new=dev_bf16(kvn),
+                              z_main=dev_f32(zm), c_main=dev_f32(cm), z_idx=dev_f32(zi), c_idx=dev_f32(ci), **outs)
+        print(f"fp4-key step from the first token, pos={pos}", flush=True)
+        csa.csa_decode_step(L, io, ws)
+        csa.csa_layer_advance(L, pos)
+        torch.cuda.synchronize()
+        for b in range(B):
+            ost = osts[b]
+            n0 = ost.n_comp
+            oracle.decode_step(ost, q=f(q[b]), q_idx=f(qi[b]), w_idx=wi[b], kv_new=f(kvn[b]), pos=pos, top_k=K,
+                               z_main=zm[b], c_main=cm[b], z_idx=zi[b], c_idx=ci[b], scale=1 / np.sqrt(D))
+            N = ost.n_comp
+            assert (L.n_comp, L.swa_head, L.swa_len) == (N, ost.swa.head, ost.swa.length)
+            if N > n0:
+                yi = oracle.compress(zi[b], ci[b], ib.astype(np.float64), m)[0]
+                assert_fp4_key_close(codes[b, n0].cpu().numpy(), scales[b, n0].cpu().numpy(), yi)
+                assert_bf16_close(host_bits(comp[b, n0]), oracle.compress(zm[b], cm[b], mb.astype(np.float64), m)[0])
+            ost.comp_kv[:N] = host_f64(comp[b, :N])
+            ost.idx_codes[:N] = numfmt.unpack_e2m1(codes[b, :N].cpu().numpy())
+            ost.idx_scales[:N] = scales[b, :N].cpu().numpy()
+            gi, gc = outs["topk_idx"][b].cpu().numpy(), int(outs["topk_count"][b])
+            if N:
+                qc, w8 = _fp8_query(f(qi[b:b + 1]).astype(np.float32), wi[b:b + 1])
+                ref_s = oracle.index_score_fp4(qc, w8, ost.idx_codes[:N], ost.idx_scales[:N])[0]
+                got_s = outs["scores"][b, :N].cpu().numpy().astype(np.float64)
+                assert rel_err(got_s, ref_s) <= 1e-4
+                np.testing.assert_array_equal(gi, oracle.topk(got_s[None], K)[0][0])
+                assert_topk_gap_rule(gi, gc, ref_s, K)
+            else:
+                assert gc == 0 and (gi == -1).all()
+            rows, n_valid = oracle.gather(ost.comp_kv[:N], gi, gc, ost.swa.rows, ost.swa.head, ost.swa.length)
+            assert int(outs["n_valid"][b]) == n_valid
+            np.testing.assert_array_equal(host_f64(outs["gather_buf"][b, :n_valid]), rows)
+            ro, rl = oracle.sparse_attn(f(q[b]), rows, ost.sink, 1 / np.sqrt(D))
+            assert rel_err(host_f64(outs["out"][b]), ro) <= 2e-2
+            assert rel_err(outs["lse"][b].cpu().numpy(), rl) <= 2e-2
+    assert L.n_comp == 2
