@@ -166,7 +166,7 @@ static int check_fp8_score_args(const void* q, const float* w, const void* k, co
               s_stride_b >= 0,
           "%s: bad strides", who);
     if (h_i != 64 || d_i != 128)
-        return fail(CSA_ERR_UNSUPPORTED, "%s: E4M3 keys need h_i=64, d_i=128 (got %d, %d)", who, h_i, d_i);
+        return fail(CSA_ERR_UNSUPPORTED, "%s: E4M3 and E2M1 keys need h_i=64, d_i=128 (got %d, %d)", who, h_i, d_i);
     CHECK(aligned16(q) && aligned16(k) && aligned16(w), "%s: q, k, w must be 16-byte aligned", who);
     CHECK(q_stride_b % 16 == 0 && k_stride_b % 16 == 0 && w_stride_b % 4 == 0,
           "%s: batch strides must keep 16-byte alignment", who);
