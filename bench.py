@@ -150,6 +150,76 @@ def time_step_scan(csa, layers, reps: int):
     return e0.elapsed_time(e1) / n, n
 
 
+def time_queue_probe(csa, n_bufs: int = 5) -> dict:
+    """When a row that every workgroup reads arrives while the workgroups'
+    own loads fill the memory system: csa_queue_probe (the pattern of the
+    index scan's first loads: one shared 16 KB row, then a ring of 16 KB key
+    tiles per workgroup), per-workgroup wall-clock stamps of the last of
+    several runs over rotating buffers (n_bufs x 64 MB, more than the
+    last-level cache).  Times in us from the first workgroup's start."""
+    import numpy as np
+    import torch
+
+    wgs = csa.csa_probe_workgroups()
+    tile = 16384
+    row = torch.ones(tile // 4, dtype=torch.float32, device="cuda")
+    bufs = [torch.ones(wgs * 8 * tile // 4, dtype=torch.float32, device="cuda") for _ in range(n_bufs)]
+    stamps = torch.zeros(wgs, 4, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {"workgroups": wgs, "row_bytes": tile, "tile_bytes_per_workgroup": tile}
+    for tiles in (0, 4, 8):
+        for r in range(2 * n_bufs):
+            csa.csa_queue_probe(row, bufs[r % n_bufs] if tiles else None, tiles, stamps, sink)
+        torch.cuda.synchronize()
+        st = stamps.cpu().numpy()
+        t0 = st[:, 0].min()
+        row_us = (st[:, 1] - t0) / 100.0
+        all_us = (st[:, 2] - t0) / 100.0
+        pct = lambda a, p: round(float(np.percentile(a, p)), 2)  # noqa: E731
+        out[f"tiles_{tiles}"] = {
+            "in_flight_mb": round(wgs * tiles * tile / 2 ** 20, 1),
+            "row_arrival_us": {"p10": pct(row_us, 10), "p50": pct(row_us, 50), "p90": pct(row_us, 90),
+                               "max": round(float(row_us.max()), 2)},
+            "all_arrived_us_max": round(float(all_us.max()), 2),
+        }
+    del bufs
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_handoff_probe(csa, reps: int = 200) -> dict:
+    """What handing every workgroup's results to a last workgroup inside one
+    launch costs (csa_handoff_probe: a release fence per workgroup, a ticket,
+    an acquire fence and the last workgroup's reads), against the same
+    launch without it, at the grid of the decode step's attention (80
+    workgroups) and of its scan (512)."""
+    import numpy as np
+    import torch
+
+    data = torch.zeros(512 * 256, dtype=torch.float32, device="cuda")
+    counter = torch.zeros(1, dtype=torch.int32, device="cuda")
+    outb = torch.zeros(256, dtype=torch.float32, device="cuda")
+    res = {}
+    for wgs in (80, 512):
+        t = {}
+        for handoff in (False, True):
+            for _ in range(10):
+                csa.csa_handoff_probe(data, counter, outb, wgs, handoff)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                csa.csa_handoff_probe(data, counter, outb, wgs, handoff)
+            e1.record()
+            torch.cuda.synchronize()
+            t[handoff] = e0.elapsed_time(e1) * 1e3 / reps
+        want = np.arange(wgs).sum() + wgs * 0.5 * np.arange(256)
+        assert np.allclose(outb.cpu().numpy(), want, rtol=1e-5), "hand-off probe read stale data"
+        res[f"workgroups_{wgs}"] = {"plain_us": round(t[False], 2), "handoff_us": round(t[True], 2),
+                                    "extra_us": round(t[True] - t[False], 2)}
+    return res
+
+
 def time_steady_read(csa, reps: int, gib: int = 1):
     """Sustained HBM read rate: csa_read_probe (plain streaming loads) over a
     `gib` GiB buffer in one launch, graph-replayed; separates the per-launch
@@ -1239,6 +1309,7 @@ def main() -> int:
     }
     sr_us, sr_bytes = time_steady_read(csa, max(3, args.scan_reps // 2))
     res["roofline"]["steady_read_gbps_1gib"] = round(sr_bytes / (sr_us * 1e-6) / 1e9, 1)
+    res["calib"] = {"queue_probe": time_queue_probe(csa), "handoff_probe": time_handoff_probe(csa)}
 
     if "fp8" in legs:
         fp8_ms, fp8_bytes, fp8_step_ms, rescored_ms = time_fp8(csa, layers, shape, args.scan_reps,

@@ -132,6 +132,9 @@ _lib = None
 _CALIB_SIGS = {
     "csa_read_probe": (_i, [_vp, _ll, _vp, _vp]),
     "csa_mfma_probe": (_i, [_vp, _i, _i, _i, _vp]),
+    "csa_probe_workgroups": (_i, []),
+    "csa_queue_probe": (_i, [_vp, _vp, _ll, _i, _vp, _ll, _vp, _vp]),
+    "csa_handoff_probe": (_i, [_vp, _ll, _vp, _vp, _i, _i, _vp]),
 }
 CALIB_LIB_PATH = os.path.join(_PKG, "libcsa_calib.so")
 _calib = None
@@ -293,6 +296,27 @@ def csa_read_probe(buf, sink, stream=None) -> None:
         raise ValueError("buf must be contiguous")
     _check_calib(calib_lib().csa_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                             _stream(stream)), "csa_read_probe")
+
+
+def csa_probe_workgroups() -> int:
+    return int(calib_lib().csa_probe_workgroups())
+
+
+def csa_queue_probe(row, buf, tiles: int, stamps, sink, stream=None) -> None:
+    """Shared-row arrival behind every workgroup's own loads (libcsa_calib.so;
+    calibration): row 16 KB, buf the workgroups' slices (or None for tiles 0),
+    stamps int64 [csa_probe_workgroups(), 4]."""
+    nbytes = buf.numel() * buf.element_size() if buf is not None else 0
+    _check_calib(calib_lib().csa_queue_probe(_ptr(row), _ptr(buf), nbytes, int(tiles), _ptr(stamps), stamps.numel(),
+                                             _ptr(sink), _stream(stream)), "csa_queue_probe")
+
+
+def csa_handoff_probe(data, counter, out, wgs: int, handoff: bool, stream=None) -> None:
+    """Workgroup results handed to the last workgroup inside one launch, or
+    not (libcsa_calib.so; calibration): data float32 [>= 256 wgs], counter
+    int32 [1] (zero before the first launch), out float32 [256]."""
+    _check_calib(calib_lib().csa_handoff_probe(_ptr(data), data.numel(), _ptr(counter), _ptr(out), int(wgs),
+                                               1 if handoff else 0, _stream(stream)), "csa_handoff_probe")
 
 
 MIX_REC_BYTES = 592  # one mixed main-KV row: 448 E4M3 codes, 64 bf16 RoPE values, scale, pad

@@ -171,7 +171,8 @@ def test_fp4_entry_points_reject_bad_args(csa):
 def test_calib_symbols_are_exported_by_their_own_library(csa):
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "csa_calib.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(csa_\w+)\s*\(", text)))
-    assert names == ["csa_mfma_probe", "csa_read_probe"]
+    assert names == ["csa_handoff_probe", "csa_mfma_probe", "csa_probe_workgroups", "csa_queue_probe",
+                     "csa_read_probe"]
     out = subprocess.run(["nm", "-D", "--defined-only", csa.binding.CALIB_LIB_PATH], capture_output=True, text=True)
     exported = set(re.findall(r" T (\w+)", out.stdout))
     assert set(names) <= exported
@@ -189,6 +190,16 @@ def test_probes_reject_bad_args(csa):
     assert lib.csa_mfma_probe(sink, 1, 0, 0, None) == B.CSA_ERR_INVALID_ARG
     assert lib.csa_mfma_probe(sink, 1, 1, 4, None) == B.CSA_ERR_INVALID_ARG
     assert lib.csa_read_probe(None, 64, None, None) == B.CSA_ERR_INVALID_ARG
+    # queue probe: no row, a ring depth it does not build, a misaligned row, no slices to read
+    assert lib.csa_queue_probe(None, sink, 1 << 30, 4, sink, 1 << 20, sink, None) == B.CSA_ERR_INVALID_ARG
+    assert lib.csa_queue_probe(sink, sink, 1 << 30, 3, sink, 1 << 20, sink, None) == B.CSA_ERR_INVALID_ARG
+    assert lib.csa_queue_probe(ctypes.c_void_p(24), sink, 1 << 30, 4, sink, 1 << 20, sink, None) == \
+        B.CSA_ERR_INVALID_ARG
+    assert lib.csa_queue_probe(sink, None, 0, 4, sink, 1 << 20, sink, None) == B.CSA_ERR_INVALID_ARG
+    # hand-off probe: no counter, no workgroups, too few floats for the grid
+    assert lib.csa_handoff_probe(sink, 1 << 20, None, sink, 80, 1, None) == B.CSA_ERR_INVALID_ARG
+    assert lib.csa_handoff_probe(sink, 1 << 20, sink, sink, 0, 1, None) == B.CSA_ERR_INVALID_ARG
+    assert lib.csa_handoff_probe(sink, 255 * 80, sink, sink, 80, 1, None) == B.CSA_ERR_INVALID_ARG
 
 
 def test_prefill_entry_points_reject_bad_args(csa):
