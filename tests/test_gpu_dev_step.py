@@ -288,6 +288,13 @@ def test_dev_step_fp4_keys(csa):
     _run(csa, mixed=False, overlap=0, B=2, n0=150, pos0=600, max_comp=200, steps=9, seed=8105, fp4=True)
 
 
+def test_dev_step_fp4_keys_overlap_and_mixed_kv(csa):
+    """E2M1 indexer keys with the overlapped compressor and mixed main KV,
+    from the first token (the new key quantised from the overlapped block's
+    compression), batch 2."""
+    _run(csa, mixed=True, overlap=1, B=2, n0=0, pos0=0, max_comp=16, steps=13, seed=8106, fp4=True)
+
+
 def test_dev_step_batched_separate_topk(csa):
     """Batch 4 at top_k 512, window 128: 4 x 80 fused workgroups would not all
     be resident, so the device-counter step takes one top-k launch per
