@@ -476,3 +476,77 @@ def test_decode_steps_fp4_from_first_token(csa):
             assert rel_err(host_f64(outs["out"][b]), ro) <= 2e-2
             assert rel_err(outs["lse"][b].cpu().numpy(), rl) <= 2e-2
     assert L.n_comp == 2
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_decode_step_batch128k_lowp_keys_full_size(csa, fmt):
+    """The batched 128K workload (8 sequences x 32,768 entries) with E4M3 or
+    E2M1 indexer keys (quantised by the oracle), one decode step with plain
+    selection: at this size each scan wave hands on 10 candidates (the
+    threshold-search extraction).  Per sequence: the new key, every score
+    against the oracle's, the top-k exact on the GPU's scores and by the gap
+    rule on the oracle's, gather and attention against the oracle."""
+    shape = synth.SHAPES["batch128k"]
+    x = synth.make_decode_inputs(shape, 5600 if fmt == "e2m1" else 5601)
+    B, K, W, D, Di, N0 = shape.batch, shape.top_k, shape.w, shape.d, shape.d_i, x["n_comp"]
+    f = numfmt.bf16_bits_to_f64
+    kf = f(x["idx_keys"]).reshape(-1, Di).astype(np.float32)
+    if fmt == "e2m1":
+        c, sc = numfmt.quantize_mxfp4_rows(kf)
+        codes = torch.from_numpy(numfmt.pack_e2m1(c).reshape(B, -1, Di // 2)).to(DEV)
+        scales = torch.from_numpy(sc.reshape(B, -1, Di // 32)).to(DEV)
+    else:
+        c, sc = numfmt.quantize_e4m3_rows(kf)
+        codes = torch.from_numpy(c.reshape(B, -1, Di)).to(DEV)
+        scales = dev_f32(sc.reshape(B, -1))
+    comp, swa = dev_bf16(x["comp_kv"]), dev_bf16(x["swa"])
+    L = csa.make_layer_desc(comp_kv=comp, idx_keys=codes, idx_scales=scales, swa=swa,
+                            main_bias=dev_f32(x["main_bias"]), idx_bias=dev_f32(x["idx_bias"]),
+                            sink=dev_f32(x["sink"]), n_comp=N0, swa_head=x["swa_head"], swa_len=x["swa_len"],
+                            h=shape.h, h_i=shape.h_i, top_k=K)
+    assert L.idx_dtype == (csa.CSA_FP4_E2M1 if fmt == "e2m1" else csa.CSA_FP8_E4M3)
+    outs = dict(scores=torch.empty(B, shape.max_comp, device=DEV),
+                topk_idx=torch.empty(B, K, dtype=torch.int32, device=DEV),
+                topk_count=torch.empty(B, dtype=torch.int32, device=DEV),
+                gather_buf=torch.zeros(B, K + W, D, dtype=torch.bfloat16, device=DEV),
+                n_valid=torch.empty(B, dtype=torch.int32, device=DEV),
+                out=torch.empty(B, shape.h, D, dtype=torch.bfloat16, device=DEV),
+                lse=torch.empty(B, shape.h, device=DEV))
+    io = csa.make_step_io(pos=x["pos"], q=dev_bf16(x["q"]), q_idx=dev_bf16(x["q_idx"]), w_idx=dev_f32(x["w_idx"]),
+                          kv_new=dev_bf16(x["kv_new"]), z_main=dev_f32(x["z_main"]), c_main=dev_f32(x["c_main"]),
+                          z_idx=dev_f32(x["z_idx"]), c_idx=dev_f32(x["c_idx"]), **outs)
+    ws = torch.empty(csa.csa_decode_step_workspace_size(L), dtype=torch.uint8, device=DEV)
+    print(f"batch128k step over {fmt} keys", flush=True)
+    csa.csa_decode_step(L, io, ws)
+    torch.cuda.synchronize()
+    completes = x["pos"] % 4 == 3
+    N = N0 + (1 if completes else 0)
+    for b in range(B):
+        if completes:  # the new key within rounding of the oracle's, then the GPU's adopted
+            yi = oracle.compress(x["z_idx"][b], x["c_idx"][b], x["idx_bias"], 4)[-1]
+            if fmt == "e2m1":
+                assert_fp4_key_close(codes[b, N0].cpu().numpy(), scales[b, N0].cpu().numpy(), yi)
+            else:
+                got = numfmt.e4m3_decode(codes[b, N0].cpu().numpy()) * float(scales[b, N0])
+                y = np.asarray(yi, np.float32).astype(np.float64)
+                assert (np.abs(got - y) <= np.maximum(np.abs(y) * 2.0 ** -4, np.abs(y).max() / 448 * 2.0 ** -10)
+                        + 1e-5 * np.abs(y).max()).all()
+        qc, w8 = _fp8_query(f(x["q_idx"][b:b + 1]).astype(np.float32), x["w_idx"][b:b + 1])
+        if fmt == "e2m1":
+            ref_s = oracle.index_score_fp4(qc, w8, numfmt.unpack_e2m1(codes[b, :N].cpu().numpy()),
+                                           scales[b, :N].cpu().numpy())[0]
+        else:
+            ref_s = oracle.index_score_fp8(qc, w8, codes[b, :N].cpu().numpy(), scales[b, :N].cpu().numpy())[0]
+        got_s = outs["scores"][b, :N].cpu().numpy().astype(np.float64)
+        assert rel_err(got_s, ref_s) <= 1e-4
+        gi, gc = outs["topk_idx"][b].cpu().numpy(), int(outs["topk_count"][b])
+        np.testing.assert_array_equal(gi, oracle.topk(got_s[None], K)[0][0])
+        assert_topk_gap_rule(gi, gc, ref_s, K)
+        comp_b = host_f64(comp[b, :N])
+        swa_b = host_f64(swa[b])
+        rows, n_valid = oracle.gather(comp_b, gi, gc, swa_b, (x["swa_head"] + 1) % W, min(x["swa_len"] + 1, W))
+        assert int(outs["n_valid"][b]) == n_valid
+        np.testing.assert_array_equal(host_f64(outs["gather_buf"][b, :n_valid]), rows)
+        ro, rl = oracle.sparse_attn(f(x["q"][b]), rows, x["sink"], 1 / np.sqrt(D))
+        assert rel_err(host_f64(outs["out"][b]), ro) <= 2e-2
+        assert rel_err(outs["lse"][b].cpu().numpy(), rl) <= 2e-2
