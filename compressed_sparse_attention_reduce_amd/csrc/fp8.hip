@@ -19,8 +19,9 @@
 //   lane loads 32 contiguous bytes of its key row and supplies the same 32
 //   bytes of its query row, so the instruction pairs the same byte of query
 //   and key whatever order it takes k slots in; the key's scale multiplies
-//   the head sum (s > 0: sum_h w ReLU(s x) = s sum_h w ReLU(x)); a ring of 8
-//   tiles per wave keeps as many bytes in flight as the bf16 kernel's 4.
+//   the head sum (s > 0: sum_h w ReLU(s x) = s sum_h w ReLU(x)); a ring of 4
+//   tiles per wave (half the bf16 kernel's bytes in flight, so the query
+//   arrives sooner behind them).
 //
 // FP4 keys (the FP4 indexer cache the pages plan, page 1,
 // ARCHITECTURE_AND_MEMORY_AUDIT.md, C4, paired with FP4 tensor-core
@@ -118,7 +119,12 @@ constexpr int kTileKeys = 16;
 constexpr int kHeads = 64;
 constexpr int kDi = 128;            // key bytes (one per element)
 constexpr int kMTiles = kHeads / 16;
-constexpr int kRing = 8;            // key tiles in flight per wave
+// key tiles in flight per wave: 4 rather than 8, so that the query, which
+// every workgroup reads first, is not queued behind 32 MB of key loads at
+// 1M context (8 tiles: scan 10.6 us, decode step 1040 steps/s; 4 tiles:
+// 9.4 us, 1131 steps/s; csa_queue_probe shows the shared row's arrival
+// growing with the bytes in flight)
+constexpr int kRing = 4;
 constexpr int kQPitch = kDi + 16;   // LDS row pitch of the staged query (bytes)
 
 constexpr int kLaneTop = 4;         // composites a lane keeps (candidate lists)
