@@ -34,7 +34,7 @@ namespace csa {
 
 namespace {
 
-constexpr int kScoreThreads = 256;  // two workgroups per CU: one's tail overlaps the other's stream
+constexpr int kScoreThreads = 256;  // four waves; one workgroup per CU in the grid (index_score_bf16_wgs)
 constexpr int kWavesPerWg = kScoreThreads / kWave;
 static_assert(kWavesPerWg == kScoreWavesPerWg, "waves per workgroup as the host assumes");
 constexpr int kTileKeys = 16;
@@ -308,8 +308,11 @@ __global__ __launch_bounds__(kScoreF32Threads) void k_index_score_f32(ScoreArgs 
 
 int index_score_bf16_wgs(int rows, int n, int extra) {
     const int tiles = (n + kTileKeys - 1) / kTileKeys;
-    // two workgroups per CU in all, the extra ones included
-    const int target = 2 * device_cu_count();
+    // one workgroup per CU in all, the extra ones included: with the ring
+    // of 4 tiles per wave that is 16 MB of key loads in flight at 1M
+    // context, so the query every workgroup reads first is not queued behind
+    // 32 MB (two per CU: scan 16.6 us, step 1010 steps/s; one: 16.1 us, 1039)
+    const int target = device_cu_count();
     int wgs = (target + rows - 1) / rows - extra;
     // at least kRing tiles per wave where the row is long enough
     const int max_wgs = (tiles + kWavesPerWg * kRing - 1) / (kWavesPerWg * kRing);
